@@ -1,0 +1,316 @@
+// dla_abi.cpp -- host side of the C ABI declared in include/dla.h: argument
+// checks, workspace carving, launch configuration, status codes.  Every check
+// runs before anything is enqueued; the library allocates nothing and never
+// synchronises.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "dla.h"
+#include "dla_internal.h"
+
+using namespace dla;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+dla_status fail(dla_status s, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+dla_status ok()
+{
+    g_err[0] = '\0';
+    return DLA_OK;
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Shape check shared by every entry point.  Returns DLA_OK or a status and message.
+dla_status check_shape(int32_t B, int32_t H, int32_t C, int32_t dk, int32_t dv)
+{
+    if (B < 1 || H < 1) return fail(DLA_ERR_ARG, "B and H must be >= 1 (got %d, %d)", B, H);
+    if (static_cast<int64_t>(B) * H > (1 << 24)) return fail(DLA_ERR_ARG, "B*H too large");
+    if (C < 1 || C > DLA_MAX_C) return fail(DLA_ERR_ARG, "C must be in [1, %d] (got %d)", DLA_MAX_C, C);
+    if (dk != 64 && dk != 128) return fail(DLA_ERR_UNSUPPORTED, "d_k must be 64 or 128 (got %d)", dk);
+    if (dv < 16 || dv % 16 != 0 || dv > 4096)
+        return fail(DLA_ERR_UNSUPPORTED, "d_v must be a multiple of 16 in [16, 4096] (got %d)", dv);
+    return DLA_OK;
+}
+
+struct Sizes {
+    uint64_t s, qs, flag, tile_cnt, tile_sum, seg_t, seg_P, seg_q0, nseg, events, chunk_ev, shadow;
+    uint64_t total;
+};
+
+Sizes workspace_sizes(int64_t BH, int64_t T, int64_t C, int64_t dk, int64_t dv)
+{
+    const int64_t NT = (T + kScoreTile - 1) / kScoreTile;
+    const int64_t NCH = (T + kChunk - 1) / kChunk;
+    Sizes z;
+    z.s = align_up(4ull * BH * T, 256);
+    z.qs = align_up(8ull * BH * T, 256);
+    z.flag = align_up(1ull * BH * T, 256);
+    z.tile_cnt = align_up(4ull * BH * NT, 256);
+    z.tile_sum = align_up(8ull * BH * NT, 256);
+    z.seg_t = align_up(4ull * BH * (T + 1), 256);
+    z.seg_P = align_up(8ull * BH * (T + 1), 256);
+    z.seg_q0 = align_up(8ull * BH * T, 256);
+    z.nseg = align_up(4ull * BH, 256);
+    z.events = align_up(8ull * BH * T, 256);
+    z.chunk_ev = align_up(4ull * BH * (NCH + 1), 256);
+    z.shadow = align_up(2ull * BH * C * dv * dk, 256);
+    z.total = z.s + z.qs + z.flag + z.tile_cnt + z.tile_sum + z.seg_t + z.seg_P + z.seg_q0 + z.nseg +
+              z.events + z.chunk_ev + z.shadow;
+    return z;
+}
+
+Workspace carve(void *base, const Sizes &z)
+{
+    uint8_t *p = static_cast<uint8_t *>(base);
+    Workspace w;
+    w.s = reinterpret_cast<float *>(p); p += z.s;
+    w.qs = reinterpret_cast<int64_t *>(p); p += z.qs;
+    w.flag = p; p += z.flag;
+    w.tile_cnt = reinterpret_cast<int32_t *>(p); p += z.tile_cnt;
+    w.tile_sum = reinterpret_cast<int64_t *>(p); p += z.tile_sum;
+    w.seg_t = reinterpret_cast<int32_t *>(p); p += z.seg_t;
+    w.seg_P = reinterpret_cast<int64_t *>(p); p += z.seg_P;
+    w.seg_q0 = reinterpret_cast<int64_t *>(p); p += z.seg_q0;
+    w.nseg = reinterpret_cast<int32_t *>(p); p += z.nseg;
+    w.events = reinterpret_cast<int2 *>(p); p += z.events;
+    w.chunk_ev = reinterpret_cast<int32_t *>(p); p += z.chunk_ev;
+    w.shadow = p;
+    return w;
+}
+
+uint64_t states_bytes(int64_t BH, int64_t C, int64_t dk, int64_t dv) { return 4ull * BH * C * dv * dk; }
+
+dla_status check_cache(const dla_cache *c)
+{
+    if (!c) return fail(DLA_ERR_ARG, "cache is NULL");
+    dla_status s = check_shape(c->B, c->H, c->C, c->d_k, c->d_v);
+    if (s != DLA_OK) return s;
+    if (!c->base || !aligned(c->base, 256)) return fail(DLA_ERR_ARG, "cache base is NULL or not 256-byte aligned");
+    if (c->bytes < dla_cache_bytes(c->B, c->H, c->C, c->d_k, c->d_v))
+        return fail(DLA_ERR_ARG, "cache buffer too small (%llu bytes)", static_cast<unsigned long long>(c->bytes));
+    return DLA_OK;
+}
+
+CacheGeom geom(const dla_cache *c)
+{
+    CacheGeom g;
+    g.B = c->B; g.H = c->H; g.C = c->C; g.dk = c->d_k; g.dv = c->d_v;
+    g.meta_stride = meta_stride_bytes(c->d_k);
+    return g;
+}
+
+dla_status hip_status(hipError_t e, const char *what)
+{
+    if (e == hipSuccess) return ok();
+    return fail(DLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int choose_dvt(int64_t BH, int dv)
+{
+    const char *env = std::getenv("DLA_PREFILL_DVT");
+    if (env) {
+        const int v = std::atoi(env);
+        if ((v == 16 || v == 32) && dv % v == 0) return v;
+    }
+    if (dv % 32 != 0) return 16;
+    // prefer the wider slice when it still gives about one block per compute unit
+    return BH * (dv / 32) >= 200 ? 32 : 16;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t dla_abi_version(void) { return DLA_ABI_VERSION; }
+
+uint64_t dla_cache_bytes(int32_t B, int32_t H, int32_t C, int32_t d_k, int32_t d_v)
+{
+    char saved[sizeof(g_err)];
+    std::memcpy(saved, g_err, sizeof(g_err));
+    const bool bad = check_shape(B, H, C, d_k, d_v) != DLA_OK;
+    std::memcpy(g_err, saved, sizeof(g_err));
+    if (bad) return 0;
+    const int64_t BH = static_cast<int64_t>(B) * H;
+    return align_up(states_bytes(BH, C, d_k, d_v), 256) + BH * meta_stride_bytes(d_k);
+}
+
+dla_status dla_cache_layout(int32_t B, int32_t H, int32_t C, int32_t d_k, int32_t d_v, dla_cache_layout_t *out)
+{
+    dla_status s = check_shape(B, H, C, d_k, d_v);
+    if (s != DLA_OK) return s;
+    if (!out) return fail(DLA_ERR_ARG, "out is NULL");
+    const int64_t BH = static_cast<int64_t>(B) * H;
+    out->states_offset = 0;
+    out->meta_offset = align_up(states_bytes(BH, C, d_k, d_v), 256);
+    out->meta_stride = meta_stride_bytes(d_k);
+    out->off_m = kOffM;
+    out->off_has_prev = kOffHasPrev;
+    out->off_s_prev = kOffSPrev;
+    out->off_t_seen = kOffTSeen;
+    out->off_order = kOffOrder;
+    out->off_info = kOffInfo;
+    out->off_count = kOffCount;
+    out->off_start = kOffStart;
+    out->off_k_prev = kOffKprev;
+    return ok();
+}
+
+dla_status dla_cache_init(dla_cache *cache, void *base, uint64_t bytes, int32_t B, int32_t H, int32_t C,
+                          int32_t d_k, int32_t d_v, const dla_cache_preload *preload, void *stream)
+{
+    if (!cache) return fail(DLA_ERR_ARG, "cache is NULL");
+    dla_status s = check_shape(B, H, C, d_k, d_v);
+    if (s != DLA_OK) return s;
+    if (!base || !aligned(base, 256)) return fail(DLA_ERR_ARG, "base is NULL or not 256-byte aligned");
+    if (bytes < dla_cache_bytes(B, H, C, d_k, d_v))
+        return fail(DLA_ERR_ARG, "buffer of %llu bytes is smaller than dla_cache_bytes",
+                    static_cast<unsigned long long>(bytes));
+    PreloadArgs pre = {0, nullptr, nullptr, nullptr, nullptr, 0};
+    if (preload) {
+        if (preload->m0 < 0 || preload->m0 > C) return fail(DLA_ERR_ARG, "preload m0 must be in [0, C]");
+        if (preload->t_seen < 0) return fail(DLA_ERR_ARG, "preload t_seen must be >= 0");
+        if (preload->m0 > 0) {
+            if (!preload->states || !preload->info || !preload->count || !preload->start)
+                return fail(DLA_ERR_ARG, "preload pointers must be non-NULL when m0 > 0");
+            if (!aligned(preload->states, 16) || !aligned(preload->info, 8) || !aligned(preload->count, 4) ||
+                !aligned(preload->start, 8))
+                return fail(DLA_ERR_ARG, "preload pointers misaligned");
+        }
+        pre.m0 = preload->m0;
+        pre.states = preload->states;
+        pre.info = preload->info;
+        pre.count = preload->count;
+        pre.start = preload->start;
+        pre.t_seen = preload->t_seen;
+    }
+    cache->B = B; cache->H = H; cache->C = C; cache->d_k = d_k; cache->d_v = d_v;
+    cache->reserved = 0;
+    cache->base = base;
+    cache->bytes = bytes;
+    const CacheGeom g = geom(cache);
+    const int64_t BH = static_cast<int64_t>(B) * H;
+    uint8_t *b8 = static_cast<uint8_t *>(base);
+    float *states = reinterpret_cast<float *>(b8);
+    uint8_t *meta = b8 + align_up(states_bytes(BH, C, d_k, d_v), 256);
+    return hip_status(launch_cache_init(states, meta, g, pre, static_cast<hipStream_t>(stream)),
+                      "cache init launch");
+}
+
+uint64_t dla_prefill_workspace_bytes(int32_t B, int32_t H, int32_t T, int32_t C, int32_t d_k, int32_t d_v)
+{
+    char saved[sizeof(g_err)];
+    std::memcpy(saved, g_err, sizeof(g_err));
+    const bool bad = check_shape(B, H, C, d_k, d_v) != DLA_OK || T < 1 || T > (1 << 24);
+    std::memcpy(g_err, saved, sizeof(g_err));
+    if (bad) return 0;
+    return workspace_sizes(static_cast<int64_t>(B) * H, T, C, d_k, d_v).total;
+}
+
+dla_status dla_prefill(const void *q, const void *k, const void *v, const void *lam, void *o, int32_t T,
+                       float tau, dla_dtype io, const dla_cache *cache, void *workspace,
+                       uint64_t workspace_bytes, const dla_schedule_out *sched, void *stream)
+{
+    dla_status s = check_cache(cache);
+    if (s != DLA_OK) return s;
+    if (!q || !k || !v || !lam || !o) return fail(DLA_ERR_ARG, "q, k, v, lam and o must be non-NULL");
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(lam, 16) || !aligned(o, 16))
+        return fail(DLA_ERR_ARG, "q, k, v, lam and o must be 16-byte aligned");
+    if (T < 1 || T > (1 << 24)) return fail(DLA_ERR_ARG, "T must be in [1, 2^24] (got %d)", T);
+    if (io != DLA_F32 && io != DLA_BF16) return fail(DLA_ERR_ARG, "unknown io dtype %d", static_cast<int>(io));
+    if (io == DLA_F32 && cache->d_k != 64)
+        return fail(DLA_ERR_UNSUPPORTED, "float32 prefill supports d_k = 64 only");
+    if (tau != tau) return fail(DLA_ERR_ARG, "tau is NaN");
+    const int64_t BH = static_cast<int64_t>(cache->B) * cache->H;
+    const Sizes z = workspace_sizes(BH, T, cache->C, cache->d_k, cache->d_v);
+    if (!workspace || !aligned(workspace, 256)) return fail(DLA_ERR_WORKSPACE, "workspace NULL or not 256-byte aligned");
+    if (workspace_bytes < z.total)
+        return fail(DLA_ERR_WORKSPACE, "workspace of %llu bytes, %llu needed",
+                    static_cast<unsigned long long>(workspace_bytes), static_cast<unsigned long long>(z.total));
+    PrefillArgs a;
+    a.q = q; a.k = k; a.v = v; a.lam = lam; a.o = o;
+    a.T = T;
+    a.tau = tau;
+    a.io_bf16 = io == DLA_BF16;
+    a.dvt = choose_dvt(BH, cache->d_v);
+    if (prefill_smem_bytes(a.io_bf16, cache->d_k, a.dvt) > 160 * 1024)
+        return fail(DLA_ERR_UNSUPPORTED, "shape needs more LDS than a compute unit has");
+    a.g = geom(cache);
+    uint8_t *b8 = static_cast<uint8_t *>(cache->base);
+    a.states = reinterpret_cast<float *>(b8);
+    a.meta = b8 + align_up(states_bytes(BH, cache->C, cache->d_k, cache->d_v), 256);
+    a.ws = carve(workspace, z);
+    if (sched) a.sched = *sched;
+    else std::memset(&a.sched, 0, sizeof(a.sched));
+    // schedule fields the prefill kernels never fill are ignored; s and boundary
+    // are copied from the workspace afterwards
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = launch_prefill(a, st);
+    if (e != hipSuccess) return hip_status(e, "prefill launch");
+    if (sched && sched->s) {
+        e = hipMemcpyAsync(sched->s, a.ws.s, 4ull * BH * T, hipMemcpyDeviceToDevice, st);
+        if (e != hipSuccess) return hip_status(e, "schedule copy");
+    }
+    if (sched && sched->boundary) {
+        e = hipMemcpyAsync(sched->boundary, a.ws.flag, 1ull * BH * T, hipMemcpyDeviceToDevice, st);
+        if (e != hipSuccess) return hip_status(e, "schedule copy");
+    }
+    return ok();
+}
+
+dla_status dla_decode_step(const void *q, const void *k, const void *v, const void *lam, void *o, float tau,
+                           dla_dtype io, const dla_cache *cache, const dla_schedule_out *sched, void *stream)
+{
+    dla_status s = check_cache(cache);
+    if (s != DLA_OK) return s;
+    if (!q || !k || !v || !lam || !o) return fail(DLA_ERR_ARG, "q, k, v, lam and o must be non-NULL");
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(lam, 16) || !aligned(o, 16))
+        return fail(DLA_ERR_ARG, "q, k, v, lam and o must be 16-byte aligned");
+    if (io != DLA_F32 && io != DLA_BF16) return fail(DLA_ERR_ARG, "unknown io dtype %d", static_cast<int>(io));
+    if (cache->d_k != cache->d_v) return fail(DLA_ERR_UNSUPPORTED, "decode needs d_k == d_v");
+    if (tau != tau) return fail(DLA_ERR_ARG, "tau is NaN");
+    DecodeArgs a;
+    a.q = q; a.k = k; a.v = v; a.lam = lam; a.o = o;
+    a.tau = tau;
+    a.io_bf16 = io == DLA_BF16;
+    a.g = geom(cache);
+    const int64_t BH = static_cast<int64_t>(cache->B) * cache->H;
+    uint8_t *b8 = static_cast<uint8_t *>(cache->base);
+    a.states = reinterpret_cast<float *>(b8);
+    a.meta = b8 + align_up(states_bytes(BH, cache->C, cache->d_k, cache->d_v), 256);
+    a.sched.s = sched ? sched->s : nullptr;
+    a.sched.boundary = sched ? sched->boundary : nullptr;
+    a.sched.m_t = sched ? sched->m_t : nullptr;
+    a.sched.ev_i = sched ? sched->ev_i : nullptr;
+    return hip_status(launch_decode(a, static_cast<hipStream_t>(stream)), "decode launch");
+}
+
+const char *dla_status_str(dla_status s)
+{
+    switch (s) {
+    case DLA_OK: return "ok";
+    case DLA_ERR_ARG: return "invalid argument";
+    case DLA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case DLA_ERR_WORKSPACE: return "workspace missing or too small";
+    case DLA_ERR_HIP: return "HIP error";
+    }
+    return "unknown status";
+}
+
+const char *dla_last_error(void) { return g_err; }
+
+}  // extern "C"

@@ -1,0 +1,108 @@
+// dla_internal.h -- definitions shared by the host ABI and the kernels of
+// libdla (cache metadata layout, workspace carving, launcher signatures).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "dla.h"
+
+namespace dla {
+
+constexpr int kChunk = DLA_CHUNK;   // tokens per prefill chunk (mask width)
+constexpr int kMaxC = DLA_MAX_C;    // lanes of the greedy wave = largest capacity
+constexpr int kScoreTile = 256;     // tokens per block of the score/compaction passes
+
+// Per-stream metadata record (see dla.h for the meaning of each field).
+struct MetaHead {
+    int32_t m;
+    int32_t has_prev;
+    float s_prev;
+    int32_t pad0;
+    int64_t t_seen;
+    int64_t pad1;
+};
+static_assert(sizeof(MetaHead) == 32, "metadata head is 32 bytes");
+constexpr uint32_t kOffM = 0;
+constexpr uint32_t kOffHasPrev = 4;
+constexpr uint32_t kOffSPrev = 8;
+constexpr uint32_t kOffTSeen = 16;
+constexpr uint32_t kOffOrder = 32;                     // uint8[64]
+constexpr uint32_t kOffInfo = kOffOrder + 64;          // int64[64]
+constexpr uint32_t kOffCount = kOffInfo + 8 * 64;      // int32[64]
+constexpr uint32_t kOffStart = kOffCount + 4 * 64;     // int64[64]
+constexpr uint32_t kOffKprev = kOffStart + 8 * 64;     // float[d_k]
+
+inline uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
+inline uint64_t meta_stride_bytes(int dk) { return align_up(kOffKprev + 4ull * dk, 256); }
+
+struct CacheGeom {
+    int B, H, C, dk, dv;
+    size_t meta_stride;
+};
+
+struct PreloadArgs {
+    int m0;
+    const float *states;
+    const int64_t *info;
+    const int32_t *count;
+    const int64_t *start;
+    int64_t t_seen;
+};
+
+// Prefill workspace, carved from one caller buffer (see carve_workspace).
+struct Workspace {
+    float *s;            // [BH][T] token information
+    int64_t *qs;         // [BH][T] information, 2^-32 fixed point
+    uint8_t *flag;       // [BH][T] boundary flags
+    int32_t *tile_cnt;   // [BH][NT]
+    int64_t *tile_sum;   // [BH][NT]
+    int32_t *seg_t;      // [BH][T+1] boundary tokens (+ sentinel T)
+    int64_t *seg_P;      // [BH][T+1] information before each boundary (+ total)
+    int64_t *seg_q0;     // [BH][T] information of each boundary token
+    int32_t *nseg;       // [BH]
+    int2 *events;        // [BH][T] (token, state merged away or -1)
+    int32_t *chunk_ev;   // [BH][NCH+1] first event of each chunk
+    void *shadow;        // [BH][C][dv][dk] bf16 copy of the states (bf16 io)
+};
+
+struct PrefillArgs {
+    const void *q, *k, *v, *lam;
+    void *o;
+    int T;
+    float tau;
+    int io_bf16;
+    int dvt;
+    CacheGeom g;
+    float *states;
+    uint8_t *meta;
+    Workspace ws;
+    dla_schedule_out sched;
+};
+
+struct DecodeSched {
+    float *s;
+    uint8_t *boundary;
+    int32_t *m_t;
+    int32_t *ev_i;
+};
+
+struct DecodeArgs {
+    const void *q, *k, *v, *lam;
+    void *o;
+    float tau;
+    int io_bf16;
+    CacheGeom g;
+    float *states;
+    uint8_t *meta;
+    DecodeSched sched;
+};
+
+hipError_t launch_cache_init(float *states, uint8_t *meta, const CacheGeom &g, const PreloadArgs &pre,
+                             hipStream_t stream);
+hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+size_t prefill_smem_bytes(int io_bf16, int dk, int dvt);
+
+}  // namespace dla

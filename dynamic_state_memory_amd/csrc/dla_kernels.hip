@@ -1,0 +1,1123 @@
+// dla_kernels.hip -- gfx950 kernels of the Dynamic Linear Attention (DLA)
+// layer forward pass: token score, boundary compaction, greedy capacity scan,
+// chunked MFMA prefill, streaming decode step, cache initialisation.
+//
+// Method (reading notes "Dynamic Linear Attention | Chlience Paper Archive"):
+//   section 5.1  per-token state v k^T; a low-information token joins the
+//                current state, otherwise it opens a new one;
+//   section 5.2  at most C states, chronological; when over capacity the
+//                adjacent pair with the least information is merged
+//                (S_i += S_{i+1}, counts and information summed);
+//   section 5.3  o_t = sum_i lam_{t,i} S_i q_t over the bounded cache;
+//   section 1    the state already holds token t when o_t is read.
+// ai-feeds.com summary "Dynamic Linear Attention", method section: the
+// information signal may be the feature change of the key, two consecutive
+// low-information tokens merge, and a merged state keeps its original
+// timestamp.  The fixed choices (cosine score, summed-information key,
+// slot-indexed lam) are listed in include/dla.h.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dla_internal.h"
+
+namespace dla {
+
+// ---------------------------------------------------------------- helpers
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ float to_f(float x) { return x; }
+__device__ __forceinline__ float to_f(__bf16 x) { return static_cast<float>(x); }
+template <typename T> __device__ __forceinline__ T from_f(float x);
+template <> __device__ __forceinline__ float from_f<float>(float x) { return x; }
+template <> __device__ __forceinline__ __bf16 from_f<__bf16>(float x) { return static_cast<__bf16>(x); }
+
+// k >> s for s in [0, 64]; a shift by 64 gives 0.
+__device__ __forceinline__ uint64_t shr64(uint64_t x, int s) { return s >= 64 ? 0ull : (x >> s); }
+__device__ __forceinline__ uint64_t low_bits(int n) { return n >= 64 ? ~0ull : ((1ull << n) - 1ull); }
+
+// The 2^-32 fixed-point value of a float information score (round half even).
+__device__ __forceinline__ int64_t fixed_point(float s) {
+    return __double2ll_rn(static_cast<double>(s) * 4294967296.0);
+}
+
+// 1 - cos from double-precision dot and squared norms, rounded once to float.
+__device__ __forceinline__ float cosine_distance(double d, double a, double b) {
+    const double ab = a * b;
+    if (ab == 0.0) return 1.0f;
+    return static_cast<float>(1.0 - d / sqrt(ab));
+}
+
+// Eight consecutive elements, the per-lane operand of one 16x16x32 MFMA step.
+template <typename T> struct Frag;
+template <> struct Frag<__bf16> { bf16x8 v; };
+template <> struct Frag<float> { float v[8]; };
+
+__device__ __forceinline__ void load_frag(Frag<__bf16> &f, const __bf16 *p) {
+    f.v = *reinterpret_cast<const bf16x8 *>(p);
+}
+__device__ __forceinline__ void load_frag(Frag<float> &f, const float *p) {
+    const float4 a = reinterpret_cast<const float4 *>(p)[0];
+    const float4 b = reinterpret_cast<const float4 *>(p)[1];
+    f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
+    f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
+}
+__device__ __forceinline__ void zero_frag(Frag<__bf16> &f) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f.v[e] = static_cast<__bf16>(0.0f);
+}
+__device__ __forceinline__ void zero_frag(Frag<float> &f) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f.v[e] = 0.0f;
+}
+// Zero the elements whose index (base + e) lies outside [lo, hi).
+__device__ __forceinline__ void mask_frag(Frag<__bf16> &f, int base, int lo, int hi) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        if (base + e < lo || base + e >= hi) f.v[e] = static_cast<__bf16>(0.0f);
+}
+__device__ __forceinline__ void mask_frag(Frag<float> &f, int base, int lo, int hi) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        if (base + e < lo || base + e >= hi) f.v[e] = 0.0f;
+}
+
+// acc(16x16) += A(16x32) * B(32x16).  Lane l holds A row (l % 16) and B
+// column (l % 16) at reduction indices 8*(l/16) + e, e = 0..7; A and B use the
+// same index map, so the product sums every reduction index exactly once.
+// The accumulator holds D[4*(l/16) + r][l % 16], r = 0..3.
+__device__ __forceinline__ void mma32(floatx4 &acc, const Frag<__bf16> &a, const Frag<__bf16> &b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma32(floatx4 &acc, const Frag<float> &a, const Frag<float> &b) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[e], b.v[e], acc, 0, 0, 0);
+}
+
+template <typename T> __device__ __forceinline__ T wave_sum(T x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+    return x;
+}
+
+__device__ __forceinline__ int64_t wave_min_i64(int64_t x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        const int64_t y = __shfl_xor(x, off);
+        x = y < x ? y : x;
+    }
+    return x;
+}
+
+// Inclusive scan over a 64-lane wave.
+template <typename T> __device__ __forceinline__ T wave_incl_scan(T x, int lane) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const T y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+    }
+    return x;
+}
+
+// ------------------------------------------------------------ cache init
+
+// One block per stream: metadata reset, optional preload of the first m0 states.
+__global__ __launch_bounds__(256) void k_cache_init(float *__restrict__ states,
+                                                     uint8_t *__restrict__ meta_base,
+                                                     CacheGeom g, PreloadArgs pre)
+{
+    const int bh = blockIdx.x;
+    const int tid = threadIdx.x;
+    uint8_t *meta = meta_base + static_cast<size_t>(bh) * g.meta_stride;
+    MetaHead *head = reinterpret_cast<MetaHead *>(meta);
+    uint8_t *order = meta + kOffOrder;
+    int64_t *info = reinterpret_cast<int64_t *>(meta + kOffInfo);
+    int32_t *count = reinterpret_cast<int32_t *>(meta + kOffCount);
+    int64_t *start = reinterpret_cast<int64_t *>(meta + kOffStart);
+    float *kprev = reinterpret_cast<float *>(meta + kOffKprev);
+    const int m0 = pre.m0;
+    if (tid == 0) {
+        head->m = m0;
+        head->has_prev = 0;
+        head->s_prev = 1.0f;
+        head->pad0 = 0;
+        head->t_seen = pre.t_seen;
+        head->pad1 = 0;
+    }
+    if (tid < kMaxC) {
+        order[tid] = static_cast<uint8_t>(tid);
+        const bool live = tid < m0;
+        info[tid] = live ? pre.info[static_cast<size_t>(bh) * m0 + tid] : 0;
+        count[tid] = live ? pre.count[static_cast<size_t>(bh) * m0 + tid] : 0;
+        start[tid] = live ? pre.start[static_cast<size_t>(bh) * m0 + tid] : 0;
+    }
+    for (int i = tid; i < g.dk; i += blockDim.x) kprev[i] = 0.0f;
+    if (m0 > 0) {
+        const size_t n4 = static_cast<size_t>(m0) * g.dv * g.dk / 4;
+        const float4 *src = reinterpret_cast<const float4 *>(pre.states) + bh * n4;
+        float4 *dst = reinterpret_cast<float4 *>(states) +
+                      static_cast<size_t>(bh) * g.C * g.dv * g.dk / 4;
+        for (size_t i = tid; i < n4; i += blockDim.x) dst[i] = src[i];
+    }
+}
+
+// ------------------------------------------------------------ token score
+
+// Grid (tiles of 256 tokens, streams).  s_t = 1 - cos(k_t, k_{t-1}) from
+// double sums; boundary b_t = empty cache or not (s_t < tau and s_{t-1} < tau);
+// per-tile boundary count and information sum for the compaction pass.
+template <typename TIO, int DK>
+__global__ __launch_bounds__(256) void k_score(const TIO *__restrict__ K, int T, float tau,
+                                               float *__restrict__ s_out,
+                                               int64_t *__restrict__ qs_out,
+                                               uint8_t *__restrict__ flag_out,
+                                               int32_t *__restrict__ tile_cnt,
+                                               int64_t *__restrict__ tile_sum, int NT)
+{
+    constexpr int G = DK / 8;        // lanes per token, 8 elements each
+    constexpr int TPW = 64 / G;      // tokens per wave pass
+    __shared__ float s_lds[kScoreTile + 1];
+    __shared__ int32_t red_c[4];
+    __shared__ int64_t red_q[4];
+    const int bh = blockIdx.y, tile = blockIdx.x;
+    const int t0 = tile * kScoreTile;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int gi = lane / G, gl = lane % G;
+    const TIO *Kb = K + static_cast<size_t>(bh) * T * DK;
+
+    // j indexes tokens t0 - 1 .. t0 + 255
+    for (int base = wave * TPW; base < kScoreTile + 1; base += 4 * TPW) {
+        const int j = base + gi;
+        const int t = t0 - 1 + j;
+        const bool valid = j < kScoreTile + 1 && t >= 0 && t < T;
+        double d = 0.0, a = 0.0, b = 0.0;
+        if (valid && t > 0) {
+            const TIO *kt = Kb + static_cast<size_t>(t) * DK + gl * 8;
+            const TIO *kp = kt - DK;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const double x = to_f(kt[e]);
+                const double y = to_f(kp[e]);
+                d += x * y;
+                a += x * x;
+                b += y * y;
+            }
+        }
+#pragma unroll
+        for (int off = G / 2; off > 0; off >>= 1) {
+            d += __shfl_xor(d, off);
+            a += __shfl_xor(a, off);
+            b += __shfl_xor(b, off);
+        }
+        if (valid && gl == 0) s_lds[j] = (t == 0) ? 1.0f : cosine_distance(d, a, b);
+    }
+    __syncthreads();
+
+    const int t = t0 + tid;
+    int32_t c = 0;
+    int64_t q = 0;
+    if (t < T) {
+        const float s = s_lds[tid + 1];
+        const float sp = (t == 0) ? 1.0f : s_lds[tid];
+        const int bnd = (t == 0) || !((s < tau) && (sp < tau));
+        q = fixed_point(s);
+        const size_t row = static_cast<size_t>(bh) * T + t;
+        s_out[row] = s;
+        qs_out[row] = q;
+        flag_out[row] = static_cast<uint8_t>(bnd);
+        c = bnd;
+    }
+    c = wave_sum(c);
+    q = wave_sum(q);
+    if (lane == 0) { red_c[wave] = c; red_q[wave] = q; }
+    __syncthreads();
+    if (tid == 0) {
+        tile_cnt[static_cast<size_t>(bh) * NT + tile] = red_c[0] + red_c[1] + red_c[2] + red_c[3];
+        tile_sum[static_cast<size_t>(bh) * NT + tile] = red_q[0] + red_q[1] + red_q[2] + red_q[3];
+    }
+}
+
+// ------------------------------------------------------ boundary compaction
+
+// Grid (tiles, streams).  Lists every boundary token j of a stream with the
+// exclusive prefix of information before it, so that the greedy scan sees
+// whole segments (a boundary and the low tokens after it).
+__global__ __launch_bounds__(256) void k_compact(int T, int NT, const uint8_t *__restrict__ flag,
+                                                 const int64_t *__restrict__ qs,
+                                                 const int32_t *__restrict__ tile_cnt,
+                                                 const int64_t *__restrict__ tile_sum,
+                                                 int32_t *__restrict__ seg_t,
+                                                 int64_t *__restrict__ seg_P,
+                                                 int64_t *__restrict__ seg_q0,
+                                                 int32_t *__restrict__ nseg,
+                                                 int32_t *__restrict__ seg_id_out)
+{
+    __shared__ int32_t wc[4];
+    __shared__ int64_t wq[4];
+    __shared__ int32_t base_c_s;
+    __shared__ int64_t base_q_s;
+    const int bh = blockIdx.y, tile = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+    int32_t c = 0;
+    int64_t p = 0;
+    for (int i = tid; i < tile; i += 256) {
+        c += tile_cnt[static_cast<size_t>(bh) * NT + i];
+        p += tile_sum[static_cast<size_t>(bh) * NT + i];
+    }
+    c = wave_sum(c);
+    p = wave_sum(p);
+    if (lane == 0) { wc[wave] = c; wq[wave] = p; }
+    __syncthreads();
+    if (tid == 0) {
+        base_c_s = wc[0] + wc[1] + wc[2] + wc[3];
+        base_q_s = wq[0] + wq[1] + wq[2] + wq[3];
+    }
+    __syncthreads();
+    const int32_t base_c = base_c_s;
+    const int64_t base_q = base_q_s;
+
+    const int t = tile * kScoreTile + tid;
+    const size_t row = static_cast<size_t>(bh) * T + t;
+    const int32_t f = (t < T) ? flag[row] : 0;
+    const int64_t q = (t < T) ? qs[row] : 0;
+    const int32_t fi = wave_incl_scan(f, lane);
+    const int64_t qi = wave_incl_scan(q, lane);
+    __syncthreads();
+    if (lane == 63) { wc[wave] = fi; wq[wave] = qi; }
+    __syncthreads();
+    int32_t off_c = 0;
+    int64_t off_q = 0;
+    for (int w = 0; w < wave; ++w) { off_c += wc[w]; off_q += wq[w]; }
+    const int32_t ex_c = base_c + off_c + fi - f;
+    const int64_t ex_q = base_q + off_q + qi - q;
+    const size_t sbase = static_cast<size_t>(bh) * (T + 1);
+    if (t < T && f) {
+        seg_t[sbase + ex_c] = t;
+        seg_P[sbase + ex_c] = ex_q;
+        seg_q0[static_cast<size_t>(bh) * T + ex_c] = q;
+    }
+    if (seg_id_out && t < T) seg_id_out[row] = ex_c + f - 1;
+    if (tile == NT - 1 && tid == 255) {
+        // totals of the whole stream: sentinel entry after the last segment
+        const int32_t tot_c = ex_c + f;
+        const int64_t tot_q = ex_q + q;
+        nseg[bh] = tot_c;
+        seg_t[sbase + tot_c] = T;
+        seg_P[sbase + tot_c] = tot_q;
+    }
+}
+
+// ----------------------------------------------------- greedy capacity scan
+
+// One wave per stream; lane i holds live state i (oldest first).  Walks the
+// segments in order: the boundary token is appended as a new state; if that
+// leaves C+1 states the adjacent pair with the smallest summed information
+// is merged (earliest pair on ties, the earlier start kept); the rest of the
+// segment joins the most recent state.  Emits one event per boundary for the
+// prefill kernel: (token, identity of the state merged away or -1), where the
+// identity is its index among the states alive at its chunk's start, or
+// 64 + its start offset within the chunk when it was opened in that chunk.
+__global__ __launch_bounds__(64) void k_greedy(int T, int C, int NCH,
+                                               const int32_t *__restrict__ seg_t,
+                                               const int64_t *__restrict__ seg_P,
+                                               const int64_t *__restrict__ seg_q0,
+                                               const int32_t *__restrict__ nseg_arr,
+                                               int2 *__restrict__ events,
+                                               int32_t *__restrict__ chunk_ev,
+                                               const float *__restrict__ s_all,
+                                               uint8_t *__restrict__ meta_base, size_t meta_stride,
+                                               int32_t *__restrict__ ev_t_out,
+                                               int32_t *__restrict__ ev_i_out,
+                                               int32_t *__restrict__ n_ev_out)
+{
+    const int bh = blockIdx.x;
+    const int lane = threadIdx.x;
+    const size_t sbase = static_cast<size_t>(bh) * (T + 1);
+    const int nseg = nseg_arr[bh];
+    int64_t I = 0;
+    int32_t n = 0, st = 0, oi = -1;
+    int m = 0, cur_chunk = -1, nev = 0, nmerge = 0;
+
+    for (int b0 = 0; b0 < nseg; b0 += 64) {
+        const int j = b0 + lane;
+        int32_t tj = 0, tn = 0;
+        int64_t Pj = 0, Pn = 0, q0 = 0;
+        if (j < nseg) {
+            tj = seg_t[sbase + j];
+            tn = seg_t[sbase + j + 1];
+            Pj = seg_P[sbase + j];
+            Pn = seg_P[sbase + j + 1];
+            q0 = seg_q0[static_cast<size_t>(bh) * T + j];
+        }
+        const int cnt = min(64, nseg - b0);
+        for (int jj = 0; jj < cnt; ++jj) {
+            const int t = __shfl(tj, jj);
+            const int tnext = __shfl(tn, jj);
+            const int64_t qj = __shfl(q0, jj);
+            const int64_t remI = __shfl(Pn, jj) - __shfl(Pj, jj) - qj;
+            const int remn = tnext - t - 1;
+            const int c = t / kChunk;
+            if (c != cur_chunk) {
+                for (int kk = cur_chunk + 1 + lane; kk <= c; kk += 64)
+                    chunk_ev[static_cast<size_t>(bh) * (NCH + 1) + kk] = nev;
+                oi = lane < m ? lane : -1;
+                cur_chunk = c;
+            }
+            int dead = -1, istar = -1;
+            if (m < C) {
+                if (lane == m) { I = qj; n = 1; st = t; oi = -1; }
+                ++m;
+            } else {
+                const int64_t I_nx = __shfl_down(I, 1);
+                const int32_t n_nx = __shfl_down(n, 1);
+                const int32_t st_nx = __shfl_down(st, 1);
+                const int32_t oi_nx = __shfl_down(oi, 1);
+                const bool inside = lane + 1 < m;
+                const int64_t pI = inside ? I_nx : qj;
+                const int32_t pn = inside ? n_nx : 1;
+                const int32_t pst = inside ? st_nx : t;
+                const int32_t poi = inside ? oi_nx : -1;
+                const int64_t key = lane < m ? I + pI : INT64_MAX;
+                const int64_t kmin = wave_min_i64(key);
+                const uint64_t hit = __ballot(key == kmin);
+                istar = __ffsll(static_cast<unsigned long long>(hit)) - 1;
+                const int32_t d_oi = __shfl(poi, istar);
+                const int32_t d_st = __shfl(pst, istar);
+                dead = d_oi >= 0 ? d_oi : 64 + (d_st - cur_chunk * kChunk);
+                if (lane == istar) { I += pI; n += pn; }
+                else if (lane > istar && lane < m) { I = pI; n = pn; st = pst; oi = poi; }
+            }
+            if (lane == 0) {
+                events[static_cast<size_t>(bh) * T + nev] = make_int2(t, dead);
+                if (ev_t_out && istar >= 0) {
+                    ev_t_out[static_cast<size_t>(bh) * T + nmerge] = t;
+                    ev_i_out[static_cast<size_t>(bh) * T + nmerge] = istar;
+                }
+            }
+            ++nev;
+            if (istar >= 0) ++nmerge;
+            if (lane == m - 1) { I += remI; n += remn; }
+        }
+    }
+    for (int kk = cur_chunk + 1 + lane; kk <= NCH; kk += 64)
+        chunk_ev[static_cast<size_t>(bh) * (NCH + 1) + kk] = nev;
+    if (n_ev_out && lane == 0) n_ev_out[bh] = nmerge;
+
+    uint8_t *meta = meta_base + static_cast<size_t>(bh) * meta_stride;
+    MetaHead *head = reinterpret_cast<MetaHead *>(meta);
+    int64_t *info = reinterpret_cast<int64_t *>(meta + kOffInfo);
+    int32_t *count = reinterpret_cast<int32_t *>(meta + kOffCount);
+    int64_t *start = reinterpret_cast<int64_t *>(meta + kOffStart);
+    info[lane] = lane < m ? I : 0;
+    count[lane] = lane < m ? n : 0;
+    start[lane] = lane < m ? static_cast<int64_t>(st) : 0;
+    if (lane == 0) {
+        head->m = m;
+        head->has_prev = 1;
+        head->s_prev = s_all[static_cast<size_t>(bh) * T + T - 1];
+        head->pad0 = 0;
+        head->t_seen = T;
+        head->pad1 = 0;
+    }
+}
+
+// Copies the last key of every stream into its cache metadata (float).
+template <typename TIO>
+__global__ void k_store_kprev(const TIO *__restrict__ K, int T, int dk, uint8_t *__restrict__ meta_base,
+                              size_t meta_stride)
+{
+    const int bh = blockIdx.x;
+    float *kp = reinterpret_cast<float *>(meta_base + static_cast<size_t>(bh) * meta_stride + kOffKprev);
+    const TIO *src = K + (static_cast<size_t>(bh) * T + T - 1) * dk;
+    for (int i = threadIdx.x; i < dk; i += blockDim.x) kp[i] = to_f(src[i]);
+}
+
+// ------------------------------------------------------------ prefill
+
+template <typename TIO, int DK, int DVT>
+struct PrefillSmem {
+    static constexpr int PAD = 16 / sizeof(TIO);
+    TIO q[kChunk][DK + PAD];
+    TIO k[kChunk][DK + PAD];
+    TIO kt[DK][kChunk + PAD];
+    TIO vt[DVT][kChunk + PAD];
+    TIO pw[kChunk][kChunk + PAD];
+    float lam[kChunk][kMaxC];
+    float wold[kMaxC][kChunk];
+    float ored[4][kChunk][DVT];
+    uint64_t om[kChunk];
+    uint64_t nm[kChunk];
+    int32_t order[kMaxC];
+    int32_t new_order[kMaxC];
+    int32_t merge_dst[kMaxC];
+    int32_t merge_src[kMaxC];
+    int32_t grp_lo[kChunk + 1];
+    int32_t grp_hi[kChunk + 1];
+    int32_t grp_slot[kChunk + 1];
+    int32_t grp_add[kChunk + 1];
+    int32_t changed[kMaxC + kChunk + 1];
+    int32_t n_merge, n_grp, n_changed, m_new;
+};
+
+// One block (4 waves) per (stream, d_v tile of DVT columns); sweeps the
+// stream's chunks of 64 tokens in order.  Per chunk:
+//   1. token masks from the chunk's events: bit i of om_t = state i of the
+//      chunk start still live at t, bit p of nm_t = state opened at chunk
+//      position p still live at t;
+//   2. inter-chunk read: O[t] = sum_i lam_t[slot_t(i)] S_i q_t over the states
+//      live at the chunk start (states merged during the chunk share the
+//      weight of the state they joined); each wave takes every 4th state;
+//   3. intra-chunk product: O += ((Q K^T) o W) V with W[t][s] =
+//      lam_t[#{live chunk starts > s}] for s <= t;
+//   4. o store; then chunk-end update: old merges S_a += S_b, every group of
+//      chunk tokens adds (or sets) V_g^T K_g into its final state, and the
+//      bf16 copies used as MFMA operands are refreshed.
+// States are fp32 in the cache; TS is the type the read streams (a bf16 copy
+// in the workspace for bf16 io, the fp32 state itself for fp32 io).
+template <typename TIO, int DK, int DVT>
+__global__ __launch_bounds__(256, 1) void k_prefill(
+    const TIO *__restrict__ Q, const TIO *__restrict__ K, const TIO *__restrict__ V,
+    const TIO *__restrict__ LAM, TIO *__restrict__ O, int T, int C, int DV, int nblk_dv,
+    float *__restrict__ states, TIO *__restrict__ shadow,
+    const int2 *__restrict__ events, const int32_t *__restrict__ chunk_ev,
+    uint8_t *__restrict__ meta_base, size_t meta_stride, int32_t *__restrict__ m_t_out)
+{
+    constexpr int KS = DK / 32;     // reduction steps over d_k
+    constexpr int NTV = DVT / 16;   // 16-wide tiles over the d_v slice
+    constexpr int MT = kChunk / 16; // 16-row tiles over the chunk
+    constexpr int EPV = 16 / sizeof(TIO);
+    typedef PrefillSmem<TIO, DK, DVT> Smem;
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    Smem &S = *reinterpret_cast<Smem *>(smem_raw);
+
+    // blocks of one stream are given consecutive ids on one XCD when possible
+    const int nblk = gridDim.x;
+    int lin = blockIdx.x;
+    if ((nblk & 7) == 0) lin = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
+    const int bh = lin / nblk_dv;
+    const int dv0 = (lin % nblk_dv) * DVT;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lr = lane & 15, lg = lane >> 4;
+    const int NCH = (T + kChunk - 1) / kChunk;
+    const size_t tok0 = static_cast<size_t>(bh) * T;
+    // a state's d_v slice for this block starts at state(p) + dv0*DK
+    float *st_base = states + static_cast<size_t>(bh) * C * DV * DK + static_cast<size_t>(dv0) * DK;
+    const TIO *rd_base;
+    if constexpr (sizeof(TIO) == 2)
+        rd_base = shadow + static_cast<size_t>(bh) * C * DV * DK + static_cast<size_t>(dv0) * DK;
+    else
+        rd_base = reinterpret_cast<const TIO *>(st_base);
+    const size_t slot_stride = static_cast<size_t>(DV) * DK;
+
+    int m0 = 0;
+    if (tid < kMaxC) S.order[tid] = tid;
+
+    for (int ch = 0; ch < NCH; ++ch) {
+        const int c0 = ch * kChunk;
+        const int nvalid = min(kChunk, T - c0);
+        __syncthreads();
+        // ---- 1. load the chunk and build token masks
+        for (int idx = tid; idx < kChunk * DK / EPV; idx += 256) {
+            const int r = idx / (DK / EPV), cv = (idx % (DK / EPV)) * EPV;
+            uint4 qv = make_uint4(0, 0, 0, 0), kv = qv;
+            if (r < nvalid) {
+                const size_t off = (tok0 + c0 + r) * DK + cv;
+                qv = *reinterpret_cast<const uint4 *>(Q + off);
+                kv = *reinterpret_cast<const uint4 *>(K + off);
+            }
+            *reinterpret_cast<uint4 *>(&S.q[r][cv]) = qv;
+            *reinterpret_cast<uint4 *>(&S.k[r][cv]) = kv;
+            const TIO *ke = reinterpret_cast<const TIO *>(&kv);
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) S.kt[cv + e][r] = ke[e];
+        }
+        for (int idx = tid; idx < kChunk * DVT / EPV; idx += 256) {
+            const int r = idx / (DVT / EPV), cv = (idx % (DVT / EPV)) * EPV;
+            uint4 vv = make_uint4(0, 0, 0, 0);
+            if (r < nvalid) vv = *reinterpret_cast<const uint4 *>(V + (tok0 + c0 + r) * DV + dv0 + cv);
+            const TIO *ve = reinterpret_cast<const TIO *>(&vv);
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) S.vt[cv + e][r] = ve[e];
+        }
+        for (int idx = tid; idx < kChunk * C; idx += 256) {
+            const int r = idx / C, j = idx % C;
+            S.lam[r][j] = r < nvalid ? to_f(LAM[(tok0 + c0 + r) * C + j]) : 0.0f;
+        }
+        if (tid < kChunk) {
+            const int e0 = chunk_ev[static_cast<size_t>(bh) * (NCH + 1) + ch];
+            const int e1 = chunk_ev[static_cast<size_t>(bh) * (NCH + 1) + ch + 1];
+            uint64_t om = low_bits(m0), nm = 0;
+            for (int e = e0; e < e1; ++e) {
+                const int2 ev = events[tok0 + e];
+                const int pos = ev.x - c0;
+                if (tid >= pos) {
+                    nm |= 1ull << pos;
+                    if (ev.y >= 64) nm &= ~(1ull << (ev.y - 64));
+                    else if (ev.y >= 0) om &= ~(1ull << ev.y);
+                }
+            }
+            S.om[tid] = om;
+            S.nm[tid] = nm;
+            if (m_t_out && dv0 == 0 && tid < nvalid)
+                m_t_out[tok0 + c0 + tid] = __popcll(om) + __popcll(nm);
+        }
+        __syncthreads();
+        for (int idx = tid; idx < m0 * kChunk; idx += 256) {
+            const int i = idx / kChunk, t = idx % kChunk;
+            const int slot = __popcll(shr64(S.om[t], i + 1)) + __popcll(S.nm[t]);
+            S.wold[i][t] = S.lam[t][slot];
+        }
+        // Q fragments of the whole chunk (A operand of the inter-chunk read)
+        Frag<TIO> qf[MT][KS];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) load_frag(qf[mt][ks], &S.q[16 * mt + lr][32 * ks + 8 * lg]);
+        __syncthreads();
+
+        // ---- 2. inter-chunk read over the states live at the chunk start
+        floatx4 Oi[MT][NTV];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < NTV; ++nt) Oi[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+        {
+            Frag<TIO> bc[KS][NTV], bn[KS][NTV];
+            int i = wave;
+            if (i < m0) {
+                const TIO *sp = rd_base + S.order[i] * slot_stride;
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                    for (int nt = 0; nt < NTV; ++nt)
+                        load_frag(bc[ks][nt], sp + (16 * nt + lr) * DK + 32 * ks + 8 * lg);
+            }
+            for (; i < m0; i += 4) {
+                if (i + 4 < m0) {
+                    const TIO *sp = rd_base + S.order[i + 4] * slot_stride;
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                        for (int nt = 0; nt < NTV; ++nt)
+                            load_frag(bn[ks][nt], sp + (16 * nt + lr) * DK + 32 * ks + 8 * lg);
+                }
+                floatx4 P[MT][NTV];
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int nt = 0; nt < NTV; ++nt) P[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                        for (int nt = 0; nt < NTV; ++nt) mma32(P[mt][nt], qf[mt][ks], bc[ks][nt]);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    const float4 w = *reinterpret_cast<const float4 *>(&S.wold[i][16 * mt + 4 * lg]);
+#pragma unroll
+                    for (int nt = 0; nt < NTV; ++nt) {
+                        Oi[mt][nt][0] += w.x * P[mt][nt][0];
+                        Oi[mt][nt][1] += w.y * P[mt][nt][1];
+                        Oi[mt][nt][2] += w.z * P[mt][nt][2];
+                        Oi[mt][nt][3] += w.w * P[mt][nt][3];
+                    }
+                }
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                    for (int nt = 0; nt < NTV; ++nt) bc[ks][nt] = bn[ks][nt];
+            }
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < NTV; ++nt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) S.ored[wave][16 * mt + 4 * lg + r][16 * nt + lr] = Oi[mt][nt][r];
+
+        // ---- 3. intra-chunk slot-weighted causal product (wave w: rows 16w..16w+15)
+        {
+            const int w = wave;
+            Frag<TIO> qa[KS];
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) load_frag(qa[ks], &S.q[16 * w + lr][32 * ks + 8 * lg]);
+#pragma unroll
+            for (int nt = 0; nt < MT; ++nt) {
+                floatx4 A = floatx4{0.f, 0.f, 0.f, 0.f};
+                if (nt <= w) {
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) {
+                        Frag<TIO> kb;
+                        load_frag(kb, &S.k[16 * nt + lr][32 * ks + 8 * lg]);
+                        mma32(A, qa[ks], kb);
+                    }
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = 16 * w + 4 * lg + r;
+                    const int s = 16 * nt + lr;
+                    float val = 0.0f;
+                    if (s <= t) {
+                        const int slot = __popcll(shr64(S.nm[t], s + 1));
+                        val = A[r] * S.lam[t][slot];
+                    }
+                    S.pw[t][s] = from_f<TIO>(val);
+                }
+            }
+        }
+        __syncthreads();
+        {
+            const int w = wave;
+            floatx4 Oa[NTV];
+#pragma unroll
+            for (int nt = 0; nt < NTV; ++nt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = 16 * w + 4 * lg + r, col = 16 * nt + lr;
+                    Oa[nt][r] = S.ored[0][t][col] + S.ored[1][t][col] + S.ored[2][t][col] + S.ored[3][t][col];
+                }
+#pragma unroll
+            for (int ks = 0; ks < kChunk / 32; ++ks) {
+                if (32 * ks <= 16 * w + 15) {
+                    Frag<TIO> a;
+                    load_frag(a, &S.pw[16 * w + lr][32 * ks + 8 * lg]);
+#pragma unroll
+                    for (int nt = 0; nt < NTV; ++nt) {
+                        Frag<TIO> b;
+                        load_frag(b, &S.vt[16 * nt + lr][32 * ks + 8 * lg]);
+                        mma32(Oa[nt], a, b);
+                    }
+                }
+            }
+            // ---- 4a. output
+#pragma unroll
+            for (int nt = 0; nt < NTV; ++nt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = 16 * w + 4 * lg + r;
+                    if (t < nvalid) O[(tok0 + c0 + t) * DV + dv0 + 16 * nt + lr] = from_f<TIO>(Oa[nt][r]);
+                }
+        }
+
+        // ---- 4b. chunk-end state update
+        if (tid == 0) {
+            const int tl = nvalid - 1;
+            const uint64_t oa = S.om[tl], na = S.nm[tl];
+            uint64_t used = 0;
+            int nold = 0, last_old = -1, nmg = 0, tgt = -1;
+            for (int i = 0; i < m0; ++i) {
+                if ((oa >> i) & 1ull) {
+                    S.new_order[nold++] = S.order[i];
+                    used |= 1ull << S.order[i];
+                    last_old = i;
+                    tgt = i;
+                } else if (tgt >= 0) {   // old state 0 is never merged away
+                    S.merge_dst[nmg] = S.order[tgt];
+                    S.merge_src[nmg] = S.order[i];
+                    ++nmg;
+                }
+            }
+            int ng = 0, mnew = nold, nch = 0;
+            for (int i = 0; i < nmg; ++i) S.changed[nch++] = S.merge_dst[i];
+            const int first_new = na ? __ffsll(static_cast<unsigned long long>(na)) - 1 : nvalid;
+            if (first_new > 0 && last_old >= 0) {
+                S.grp_lo[ng] = 0; S.grp_hi[ng] = first_new;
+                S.grp_slot[ng] = S.order[last_old]; S.grp_add[ng] = 1;
+                S.changed[nch++] = S.order[last_old];
+                ++ng;
+            }
+            uint64_t rest = na;
+            while (rest) {
+                const int p = __ffsll(static_cast<unsigned long long>(rest)) - 1;
+                rest &= rest - 1;
+                const int q = rest ? __ffsll(static_cast<unsigned long long>(rest)) - 1 : nvalid;
+                const int slot = __ffsll(static_cast<unsigned long long>(~used)) - 1;
+                if (slot < 0 || slot >= C) break;   // cannot happen: at most C states live
+                used |= 1ull << slot;
+                S.new_order[mnew++] = slot;
+                S.grp_lo[ng] = p; S.grp_hi[ng] = q; S.grp_slot[ng] = slot; S.grp_add[ng] = 0;
+                S.changed[nch++] = slot;
+                ++ng;
+            }
+            S.n_merge = nmg;
+            S.n_grp = ng;
+            S.n_changed = nch;
+            S.m_new = mnew;
+        }
+        __syncthreads();
+        // merges of states that were live at the chunk start (fp32, in place)
+        for (int g = 0; g < S.n_merge; ++g) {
+            float4 *dst = reinterpret_cast<float4 *>(st_base + S.merge_dst[g] * slot_stride);
+            const float4 *src = reinterpret_cast<const float4 *>(st_base + S.merge_src[g] * slot_stride);
+            for (int idx = tid; idx < DVT * DK / 4; idx += 256) {
+                float4 a = dst[idx];
+                const float4 b = src[idx];
+                a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+                dst[idx] = a;
+            }
+        }
+        __syncthreads();
+        // V_g^T K_g of every group of chunk tokens into its final state
+        for (int g = 0; g < S.n_grp; ++g) {
+            const int lo = S.grp_lo[g], hi = S.grp_hi[g];
+            float *dst = st_base + S.grp_slot[g] * slot_stride;
+            const bool add = S.grp_add[g] != 0;
+            for (int tile = wave; tile < NTV * (DK / 16); tile += 4) {
+                const int mt = tile % NTV, nt = tile / NTV;
+                floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < kChunk / 32; ++ks) {
+                    const int base = 32 * ks + 8 * lg;
+                    if (32 * ks < hi && 32 * ks + 32 > lo) {
+                        Frag<TIO> a, b;
+                        load_frag(a, &S.vt[16 * mt + lr][base]);
+                        mask_frag(a, base, lo, hi);
+                        load_frag(b, &S.kt[16 * nt + lr][base]);
+                        mma32(acc, a, b);
+                    }
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float *p = dst + (16 * mt + 4 * lg + r) * DK + 16 * nt + lr;
+                    *p = add ? (*p + acc[r]) : acc[r];
+                }
+            }
+        }
+        __syncthreads();
+        if constexpr (sizeof(TIO) == 2) {
+            for (int c = 0; c < S.n_changed; ++c) {
+                const int slot = S.changed[c];
+                const float *src = st_base + slot * slot_stride;
+                TIO *dst = shadow + static_cast<size_t>(bh) * C * DV * DK + slot * slot_stride +
+                           static_cast<size_t>(dv0) * DK;
+                for (int idx = tid; idx < DVT * DK / 8; idx += 256) {
+                    const float4 a = reinterpret_cast<const float4 *>(src)[2 * idx];
+                    const float4 b = reinterpret_cast<const float4 *>(src)[2 * idx + 1];
+                    bf16x8 o;
+                    o[0] = static_cast<__bf16>(a.x); o[1] = static_cast<__bf16>(a.y);
+                    o[2] = static_cast<__bf16>(a.z); o[3] = static_cast<__bf16>(a.w);
+                    o[4] = static_cast<__bf16>(b.x); o[5] = static_cast<__bf16>(b.y);
+                    o[6] = static_cast<__bf16>(b.z); o[7] = static_cast<__bf16>(b.w);
+                    reinterpret_cast<bf16x8 *>(dst)[idx] = o;
+                }
+            }
+        }
+        __syncthreads();
+        if (tid < kMaxC) S.order[tid] = tid < S.m_new ? S.new_order[tid] : 0;
+        m0 = S.m_new;
+    }
+    __syncthreads();
+    if (dv0 == 0 && tid < kMaxC) {
+        uint8_t *order = meta_base + static_cast<size_t>(bh) * meta_stride + kOffOrder;
+        order[tid] = static_cast<uint8_t>(tid < m0 ? S.order[tid] : 0xFF);
+    }
+}
+
+// ------------------------------------------------------------ decode step
+
+// One block per stream.  Wave 0 runs the scalar step (score, boundary,
+// greedy merge on the metadata); then every thread streams the live states
+// once: o = sum_i lam[slot(i)] S_i q + lam[0] v (k . q), adding v k^T into
+// the most recent state, or writing the new state v k^T into a free slot,
+// and applying a capacity merge S_a += S_b while the data passes through.
+template <typename TIO, int D>
+__global__ __launch_bounds__(256) void k_decode(const TIO *__restrict__ Qg, const TIO *__restrict__ Kg,
+                                                const TIO *__restrict__ Vg, const TIO *__restrict__ Lg,
+                                                TIO *__restrict__ Og, float tau, int C,
+                                                float *__restrict__ states, uint8_t *__restrict__ meta_base,
+                                                size_t meta_stride, DecodeSched sched)
+{
+    constexpr int G = D / 4;          // threads per state row (float4 each)
+    constexpr int R = 256 / G;        // rows per pass
+    constexpr int P = D / R;          // passes per state
+    __shared__ float qs[D], ks[D], vs[D], kp[D], lw[kMaxC];
+    __shared__ float wlog[kMaxC];
+    __shared__ int32_t order_s[kMaxC];
+    __shared__ double red[4][4];
+    __shared__ float orow[D];
+    __shared__ int32_t ctl[8];        // mode, add_slot, set_slot, merge_i, m, ...
+    __shared__ float sc_kq;
+
+    const int bh = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    uint8_t *meta = meta_base + static_cast<size_t>(bh) * meta_stride;
+    MetaHead *head = reinterpret_cast<MetaHead *>(meta);
+    uint8_t *order = meta + kOffOrder;
+    int64_t *info = reinterpret_cast<int64_t *>(meta + kOffInfo);
+    int32_t *count = reinterpret_cast<int32_t *>(meta + kOffCount);
+    int64_t *start = reinterpret_cast<int64_t *>(meta + kOffStart);
+    float *kprev = reinterpret_cast<float *>(meta + kOffKprev);
+
+    if (tid < D) {
+        qs[tid] = to_f(Qg[static_cast<size_t>(bh) * D + tid]);
+        ks[tid] = to_f(Kg[static_cast<size_t>(bh) * D + tid]);
+        vs[tid] = to_f(Vg[static_cast<size_t>(bh) * D + tid]);
+        kp[tid] = kprev[tid];
+    }
+    if (tid < C) lw[tid] = to_f(Lg[static_cast<size_t>(bh) * C + tid]);
+    __syncthreads();
+    {
+        double d = 0.0, a = 0.0, b = 0.0, kq = 0.0;
+        if (tid < D) {
+            const double x = ks[tid], y = kp[tid];
+            d = x * y; a = x * x; b = y * y;
+            kq = x * static_cast<double>(qs[tid]);
+        }
+        d = wave_sum(d); a = wave_sum(a); b = wave_sum(b); kq = wave_sum(kq);
+        if (lane == 0) { red[wave][0] = d; red[wave][1] = a; red[wave][2] = b; red[wave][3] = kq; }
+    }
+    __syncthreads();
+    if (wave == 0) {
+        const double d = red[0][0] + red[1][0] + red[2][0] + red[3][0];
+        const double a = red[0][1] + red[1][1] + red[2][1] + red[3][1];
+        const double b = red[0][2] + red[1][2] + red[2][2] + red[3][2];
+        const double kq = red[0][3] + red[1][3] + red[2][3] + red[3][3];
+        const int m = head->m;
+        const int has_prev = head->has_prev;
+        const float s_prev = head->s_prev;
+        const int64_t t_seen = head->t_seen;
+        const float s = has_prev ? cosine_distance(d, a, b) : 1.0f;
+        const int bnd = (m == 0) || !((s < tau) && (s_prev < tau));
+        const int64_t qv = fixed_point(s);
+        int64_t I = lane < m ? info[lane] : 0;
+        int32_t n = lane < m ? count[lane] : 0;
+        int64_t stt = lane < m ? start[lane] : 0;
+        int32_t ord = lane < m ? static_cast<int32_t>(order[lane]) : 0;
+        uint64_t usedmask = 0;
+        for (int i = 0; i < m; ++i) usedmask |= 1ull << __shfl(ord, i);
+        int mode, add_slot = -1, set_slot = -1, merge_i = -1, m_new = m, post_slot = 0;
+        if (!bnd) {
+            mode = 0;                                  // join the most recent state
+            add_slot = __shfl(ord, m - 1);
+            post_slot = m - 1 - lane;
+            if (lane == m - 1) { I += qv; n += 1; }
+        } else if (m < C) {
+            mode = 1;                                  // open a state in a free slot
+            set_slot = __ffsll(static_cast<unsigned long long>(~usedmask)) - 1;
+            post_slot = m - lane;
+            if (lane == m) { I = qv; n = 1; stt = t_seen; ord = set_slot; }
+            m_new = m + 1;
+        } else {
+            const int64_t I_nx = __shfl_down(I, 1);
+            const bool inside = lane + 1 < m;
+            const int64_t pI = inside ? I_nx : qv;
+            const int64_t key = lane < m ? I + pI : INT64_MAX;
+            const int64_t kmin = wave_min_i64(key);
+            merge_i = __ffsll(static_cast<unsigned long long>(__ballot(key == kmin))) - 1;
+            post_slot = m - 1 - (lane <= merge_i ? lane : lane - 1);
+            if (merge_i == m - 1) {
+                mode = 3;                              // the new token joins the most recent state
+                add_slot = __shfl(ord, m - 1);
+                if (lane == m - 1) { I += qv; n += 1; }
+            } else {
+                mode = 2;                              // merge (i, i+1), new state into the freed slot
+                const int32_t freed = __shfl(ord, merge_i + 1);
+                set_slot = freed;
+                const int32_t n_nx = __shfl_down(n, 1);
+                const int64_t st_nx = __shfl_down(stt, 1);
+                const int32_t ord_nx = __shfl_down(ord, 1);
+                if (lane == merge_i) { I += I_nx; n += n_nx; }
+                else if (lane > merge_i && lane < m - 1) { I = I_nx; n = n_nx; stt = st_nx; ord = ord_nx; }
+                else if (lane == m - 1) { I = qv; n = 1; stt = t_seen; ord = freed; }
+            }
+        }
+        if (lane < m) {
+            wlog[lane] = lw[post_slot];
+            order_s[lane] = static_cast<int32_t>(order[lane]);
+        }
+        if (lane == 0) {
+            ctl[0] = mode; ctl[1] = add_slot; ctl[2] = set_slot; ctl[3] = merge_i; ctl[4] = m;
+            sc_kq = static_cast<float>(kq) * lw[0];
+        }
+        // new metadata
+        if (lane < kMaxC) {
+            info[lane] = lane < m_new ? I : 0;
+            count[lane] = lane < m_new ? n : 0;
+            start[lane] = lane < m_new ? stt : 0;
+            order[lane] = static_cast<uint8_t>(lane < m_new ? ord : 0xFF);
+        }
+        if (lane == 0) {
+            head->m = m_new;
+            head->has_prev = 1;
+            head->s_prev = s;
+            head->t_seen = t_seen + 1;
+            if (sched.s) sched.s[bh] = s;
+            if (sched.boundary) sched.boundary[bh] = static_cast<uint8_t>(bnd);
+            if (sched.m_t) sched.m_t[bh] = m_new;
+            if (sched.ev_i) sched.ev_i[bh] = merge_i;
+        }
+    }
+    __syncthreads();
+    if (tid < D) kprev[tid] = ks[tid];
+    const int mode = ctl[0], add_slot = ctl[1], set_slot = ctl[2], merge_i = ctl[3], m = ctl[4];
+    const int col = (tid % G) * 4, row0 = tid / G;
+    const float4 q4 = *reinterpret_cast<const float4 *>(&qs[col]);
+    const float4 k4 = *reinterpret_cast<const float4 *>(&ks[col]);
+    float acc[P];
+#pragma unroll
+    for (int j = 0; j < P; ++j) acc[j] = 0.0f;
+    float *sb = states + static_cast<size_t>(bh) * C * D * D;
+    for (int i = 0; i < m; ++i) {
+        const int p = order_s[i];
+        const float w = wlog[i];
+        float4 *sp = reinterpret_cast<float4 *>(sb + static_cast<size_t>(p) * D * D);
+        float4 x[P];
+#pragma unroll
+        for (int j = 0; j < P; ++j) x[j] = sp[((row0 + R * j) * D + col) / 4];
+#pragma unroll
+        for (int j = 0; j < P; ++j)
+            acc[j] += w * (x[j].x * q4.x + x[j].y * q4.y + x[j].z * q4.z + x[j].w * q4.w);
+        if (p == add_slot) {
+#pragma unroll
+            for (int j = 0; j < P; ++j) {
+                const float vr = vs[row0 + R * j];
+                float4 y = x[j];
+                y.x += vr * k4.x; y.y += vr * k4.y; y.z += vr * k4.z; y.w += vr * k4.w;
+                sp[((row0 + R * j) * D + col) / 4] = y;
+            }
+        }
+        if (mode == 2 && i == merge_i + 1) {
+            float4 *dp = reinterpret_cast<float4 *>(sb + static_cast<size_t>(order_s[merge_i]) * D * D);
+#pragma unroll
+            for (int j = 0; j < P; ++j) {
+                const int idx = ((row0 + R * j) * D + col) / 4;
+                float4 a = dp[idx];
+                a.x += x[j].x; a.y += x[j].y; a.z += x[j].z; a.w += x[j].w;
+                dp[idx] = a;
+            }
+        }
+    }
+    if (set_slot >= 0) {
+        float4 *sp = reinterpret_cast<float4 *>(sb + static_cast<size_t>(set_slot) * D * D);
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+            const float vr = vs[row0 + R * j];
+            sp[((row0 + R * j) * D + col) / 4] = make_float4(vr * k4.x, vr * k4.y, vr * k4.z, vr * k4.w);
+        }
+    }
+    (void)mode;
+#pragma unroll
+    for (int j = 0; j < P; ++j) {
+        float x = acc[j];
+#pragma unroll
+        for (int off = G / 2; off > 0; off >>= 1) x += __shfl_xor(x, off);
+        if (tid % G == 0) orow[row0 + R * j] = x;
+    }
+    __syncthreads();
+    if (tid < D) Og[static_cast<size_t>(bh) * D + tid] = from_f<TIO>(orow[tid] + sc_kq * vs[tid]);
+}
+
+// ------------------------------------------------------------ launchers
+
+hipError_t launch_cache_init(float *states, uint8_t *meta, const CacheGeom &g, const PreloadArgs &pre,
+                             hipStream_t stream)
+{
+    hipLaunchKernelGGL(k_cache_init, dim3(g.B * g.H), dim3(256), 0, stream, states, meta, g, pre);
+    return hipGetLastError();
+}
+
+template <typename TIO, int DK>
+static hipError_t prefill_schedule(const PrefillArgs &a, hipStream_t stream)
+{
+    const int BH = a.g.B * a.g.H, T = a.T;
+    const int NT = (T + kScoreTile - 1) / kScoreTile;
+    const int NCH = (T + kChunk - 1) / kChunk;
+    const TIO *K = static_cast<const TIO *>(a.k);
+    hipLaunchKernelGGL((k_score<TIO, DK>), dim3(NT, BH), dim3(256), 0, stream, K, T, a.tau, a.ws.s,
+                       a.ws.qs, a.ws.flag, a.ws.tile_cnt, a.ws.tile_sum, NT);
+    hipLaunchKernelGGL(k_compact, dim3(NT, BH), dim3(256), 0, stream, T, NT, a.ws.flag, a.ws.qs,
+                       a.ws.tile_cnt, a.ws.tile_sum, a.ws.seg_t, a.ws.seg_P, a.ws.seg_q0, a.ws.nseg,
+                       a.sched.seg_id);
+    hipLaunchKernelGGL(k_greedy, dim3(BH), dim3(64), 0, stream, T, a.g.C, NCH, a.ws.seg_t, a.ws.seg_P,
+                       a.ws.seg_q0, a.ws.nseg, a.ws.events, a.ws.chunk_ev, a.ws.s, a.meta, a.g.meta_stride,
+                       a.sched.ev_t, a.sched.ev_i, a.sched.n_ev);
+    hipLaunchKernelGGL((k_store_kprev<TIO>), dim3(BH), dim3(128), 0, stream, K, T, DK, a.meta,
+                       a.g.meta_stride);
+    return hipGetLastError();
+}
+
+template <typename TIO, int DK, int DVT>
+static hipError_t prefill_main(const PrefillArgs &a, hipStream_t stream)
+{
+    const int BH = a.g.B * a.g.H;
+    const int nblk_dv = a.g.dv / DVT;
+    const size_t smem = sizeof(PrefillSmem<TIO, DK, DVT>);
+    static bool attr_set = false;   // idempotent; a race only repeats the same call
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_prefill<TIO, DK, DVT>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           static_cast<int>(smem));
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    hipLaunchKernelGGL((k_prefill<TIO, DK, DVT>), dim3(BH * nblk_dv), dim3(256), smem, stream,
+                       static_cast<const TIO *>(a.q), static_cast<const TIO *>(a.k),
+                       static_cast<const TIO *>(a.v), static_cast<const TIO *>(a.lam),
+                       static_cast<TIO *>(a.o), a.T, a.g.C, a.g.dv, nblk_dv, a.states,
+                       static_cast<TIO *>(a.ws.shadow), a.ws.events, a.ws.chunk_ev, a.meta,
+                       a.g.meta_stride, a.sched.m_t);
+    return hipGetLastError();
+}
+
+template <typename TIO>
+static hipError_t prefill_typed(const PrefillArgs &a, hipStream_t stream)
+{
+    hipError_t e;
+    if (a.g.dk == 64) {
+        e = prefill_schedule<TIO, 64>(a, stream);
+        if (e != hipSuccess) return e;
+        if (a.dvt == 32) return prefill_main<TIO, 64, 32>(a, stream);
+        return prefill_main<TIO, 64, 16>(a, stream);
+    }
+    if constexpr (sizeof(TIO) == 2) {
+        e = prefill_schedule<TIO, 128>(a, stream);
+        if (e != hipSuccess) return e;
+        if (a.dvt == 32) return prefill_main<TIO, 128, 32>(a, stream);
+        return prefill_main<TIO, 128, 16>(a, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream)
+{
+    if (a.io_bf16) return prefill_typed<__bf16>(a, stream);
+    return prefill_typed<float>(a, stream);
+}
+
+template <typename TIO>
+static hipError_t decode_typed(const DecodeArgs &a, hipStream_t stream)
+{
+    const int BH = a.g.B * a.g.H;
+    const TIO *q = static_cast<const TIO *>(a.q), *k = static_cast<const TIO *>(a.k);
+    const TIO *v = static_cast<const TIO *>(a.v), *l = static_cast<const TIO *>(a.lam);
+    TIO *o = static_cast<TIO *>(a.o);
+    if (a.g.dk == 128)
+        hipLaunchKernelGGL((k_decode<TIO, 128>), dim3(BH), dim3(256), 0, stream, q, k, v, l, o, a.tau,
+                           a.g.C, a.states, a.meta, a.g.meta_stride, a.sched);
+    else
+        hipLaunchKernelGGL((k_decode<TIO, 64>), dim3(BH), dim3(256), 0, stream, q, k, v, l, o, a.tau,
+                           a.g.C, a.states, a.meta, a.g.meta_stride, a.sched);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream)
+{
+    if (a.io_bf16) return decode_typed<__bf16>(a, stream);
+    return decode_typed<float>(a, stream);
+}
+
+size_t prefill_smem_bytes(int io_bf16, int dk, int dvt)
+{
+    if (io_bf16) {
+        if (dk == 64) return dvt == 32 ? sizeof(PrefillSmem<__bf16, 64, 32>) : sizeof(PrefillSmem<__bf16, 64, 16>);
+        return dvt == 32 ? sizeof(PrefillSmem<__bf16, 128, 32>) : sizeof(PrefillSmem<__bf16, 128, 16>);
+    }
+    return dvt == 32 ? sizeof(PrefillSmem<float, 64, 32>) : sizeof(PrefillSmem<float, 64, 16>);
+}
+
+}  // namespace dla

@@ -1,0 +1,201 @@
+/*
+ * dla.h -- C ABI of the Dynamic Linear Attention (DLA) layer forward pass on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The layer is multi-state linear attention over a fixed-capacity,
+ * chronologically ordered cache of outer-product states S = sum v_s k_s^T
+ * (d_v x d_k), read as o_t = sum_j lam_t[j] S_(j) q_t with slot j the j-th
+ * most recent state.  Sources (reading notes "Dynamic Linear Attention |
+ * Chlience Paper Archive"): section 5.1 builds the per-token state and either
+ * merges it into the current state or opens a new one; section 5.2 keeps at
+ * most C states and greedily merges an adjacent pair when the cache is over
+ * capacity; section 5.3 reads the bounded cache with query-dependent weights;
+ * section 1 gives the single-state recurrence whose state includes token t
+ * when o_t is read.  The ai-feeds.com summary "Dynamic Linear Attention"
+ * (method section) adds that the layer consumes an online token stream, that
+ * two consecutive low-information tokens are merged, that a merged state
+ * keeps the original timestamp, and that the updated state set is handed on
+ * to decoding.
+ *
+ * Fixed choices (the pages leave them open):
+ *   - token information s_t = 1 - cos(k_t, k_{t-1}), float, s = 1 without a
+ *     previous key or with a zero-norm key (dot and norms summed in double,
+ *     rounded once to float);
+ *   - token t opens a new state unless s_t < tau and s_{t-1} < tau;
+ *     an empty cache always opens one;
+ *   - information sums are int64 multiples of 2^-32 (exact);
+ *   - after an append that leaves C+1 states, the adjacent pair with the
+ *     smallest summed information is merged (earliest pair on ties); the
+ *     merged state keeps the earlier start;
+ *   - o_t is read after the update and any merge;
+ *   - lam is indexed by cache slot, slot 0 = most recent state.
+ *
+ * Conventions for every entry point
+ *   - Pointers named as device pointers must point to device memory the
+ *     caller allocated; the library never allocates, frees or synchronises.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued
+ *     on it and the call returns at once; buffers must stay alive until the
+ *     stream work completes.  A cache must not be used on two streams at once.
+ *   - All argument checks run on the host before anything is enqueued; on any
+ *     error status nothing was enqueued.  dla_last_error() then describes the
+ *     problem (thread-local string).
+ *   - Tensors are row-major and contiguous; every device pointer must be
+ *     16-byte aligned.
+ *   - NaN or Inf inputs are outside the contract.
+ */
+#ifndef DLA_H
+#define DLA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DLA_ABI_VERSION 1
+#define DLA_MAX_C 64        /* largest supported cache capacity */
+#define DLA_CHUNK 64        /* tokens per prefill chunk */
+
+typedef enum dla_status {
+    DLA_OK = 0,
+    DLA_ERR_ARG = 1,          /* bad pointer, size, alignment or mismatch */
+    DLA_ERR_UNSUPPORTED = 2,  /* valid request outside what this build supports */
+    DLA_ERR_WORKSPACE = 3,    /* workspace missing or too small */
+    DLA_ERR_HIP = 4           /* a HIP launch failed; see dla_last_error() */
+} dla_status;
+
+typedef enum dla_dtype {
+    DLA_F32 = 0,   /* float32 inputs and outputs */
+    DLA_BF16 = 1   /* bfloat16 inputs and outputs */
+} dla_dtype;
+
+/*
+ * Cache: caller-owned device memory holding, for every stream (b, h), up to
+ * C fp32 states in physical slots plus the stream's metadata.  The struct is
+ * a plain view; dla_cache_init fills it.
+ *
+ * Buffer layout (offsets from dla_cache_layout):
+ *   states  at states_offset: [B*H][C][d_v][d_k] float32, physical slots;
+ *   meta    at meta_offset + bh * meta_stride, per stream:
+ *     int32  m            live states (0..C)
+ *     int32  has_prev     1 once the stream has seen a key
+ *     float  s_prev       information of the last token (1 if none)
+ *     int64  t_seen       tokens consumed so far (state starts are counted on it)
+ *     uint8  order[64]    physical slot of live state i, i = 0 oldest
+ *     int64  info[64]     summed information of live state i, units of 2^-32
+ *     int32  count[64]    tokens in live state i
+ *     int64  start[64]    index of the first token of live state i
+ *     float  k_prev[d_k]  last key seen
+ * A checkpoint of a stream is a copy of this buffer.
+ */
+typedef struct dla_cache {
+    int32_t B, H, C, d_k, d_v;
+    int32_t reserved;
+    void *base;        /* device pointer */
+    uint64_t bytes;
+} dla_cache;
+
+typedef struct dla_cache_layout_t {
+    uint64_t states_offset;
+    uint64_t meta_offset;
+    uint64_t meta_stride;
+    uint32_t off_m, off_has_prev, off_s_prev, off_t_seen;
+    uint32_t off_order, off_info, off_count, off_start, off_k_prev;
+} dla_cache_layout_t;
+
+/* Optional starting content of a cache (device pointers, oldest state first). */
+typedef struct dla_cache_preload {
+    int32_t m0;               /* live states per stream, 0..C */
+    int32_t reserved;
+    const float *states;      /* [B*H][m0][d_v][d_k] float32 */
+    const int64_t *info;      /* [B*H][m0] summed information, units of 2^-32 */
+    const int32_t *count;     /* [B*H][m0] tokens per state */
+    const int64_t *start;     /* [B*H][m0] first token of each state */
+    int64_t t_seen;           /* tokens every stream has already consumed */
+} dla_cache_preload;
+
+/*
+ * Optional schedule export (device pointers, any may be NULL).
+ * Prefill (T tokens per stream):
+ *   s [B*H][T]        token information
+ *   boundary [B*H][T] 1 if the token opened a state
+ *   seg_id [B*H][T]   states opened so far in this call, minus one
+ *   m_t [B*H][T]      live states after the token
+ *   ev_t, ev_i [B*H][T], n_ev [B*H]: the capacity merges in order: token and
+ *                     chronological index of the earlier state of the pair
+ * Decode step: s, boundary, m_t and ev_i are [B*H] (ev_i = -1 without a
+ * merge); seg_id, ev_t and n_ev are ignored.
+ */
+typedef struct dla_schedule_out {
+    float *s;
+    uint8_t *boundary;
+    int32_t *seg_id;
+    int32_t *m_t;
+    int32_t *ev_t;
+    int32_t *ev_i;
+    int32_t *n_ev;
+} dla_schedule_out;
+
+/* Version of this ABI (DLA_ABI_VERSION). */
+int32_t dla_abi_version(void);
+
+/* Bytes of a cache for the given shape; 0 if the shape is invalid. */
+uint64_t dla_cache_bytes(int32_t B, int32_t H, int32_t C, int32_t d_k, int32_t d_v);
+
+/* Offsets of the cache buffer's parts (see dla_cache).  DLA_ERR_ARG on a bad shape. */
+dla_status dla_cache_layout(int32_t B, int32_t H, int32_t C, int32_t d_k, int32_t d_v,
+                            dla_cache_layout_t *out);
+
+/*
+ * Make `base` (device, >= dla_cache_bytes bytes, 256-byte aligned) an empty
+ * cache, or one holding `preload` (may be NULL), and fill *cache.
+ * Supported: C in [1, 64], d_k in {64, 128}, d_v a positive multiple of 16.
+ * A preloaded stream has no previous key, so its next token has s = 1.
+ */
+dla_status dla_cache_init(dla_cache *cache, void *base, uint64_t bytes, int32_t B,
+                          int32_t H, int32_t C, int32_t d_k, int32_t d_v,
+                          const dla_cache_preload *preload, void *stream);
+
+/* Workspace bytes dla_prefill needs for this shape; 0 if the shape is invalid. */
+uint64_t dla_prefill_workspace_bytes(int32_t B, int32_t H, int32_t T, int32_t C,
+                                     int32_t d_k, int32_t d_v);
+
+/*
+ * Prefill: consume T tokens of every stream, starting each stream afresh
+ * (whatever the cache held is discarded), write o for every token and leave
+ * the final states and metadata in the cache, ready for dla_decode_step.
+ *   q, k    [B*H][T][d_k]   io dtype, device
+ *   v, o    [B*H][T][d_v]   io dtype, device
+ *   lam     [B*H][T][C]     io dtype, device; lam[.][t][j] weights slot j
+ *   tau     boundary threshold
+ *   io      DLA_F32 (d_k = 64 only) or DLA_BF16 (d_k in {64, 128})
+ *   workspace  device, >= dla_prefill_workspace_bytes, 256-byte aligned;
+ *              scratch owned by the call until the stream work completes
+ *   sched   optional schedule export, may be NULL
+ * T must be in [1, 2^24].
+ */
+dla_status dla_prefill(const void *q, const void *k, const void *v, const void *lam,
+                       void *o, int32_t T, float tau, dla_dtype io, const dla_cache *cache,
+                       void *workspace, uint64_t workspace_bytes,
+                       const dla_schedule_out *sched, void *stream);
+
+/*
+ * Decode step: consume one token of every stream on top of the cache and
+ * write o.  q, k [B*H][d_k]; v, o [B*H][d_v]; lam [B*H][C]; io dtype, device.
+ * Supported: d_k = d_v = 128 or d_k = d_v = 64, any io dtype.
+ */
+dla_status dla_decode_step(const void *q, const void *k, const void *v, const void *lam,
+                           void *o, float tau, dla_dtype io, const dla_cache *cache,
+                           const dla_schedule_out *sched, void *stream);
+
+/* Static text for a status code. */
+const char *dla_status_str(dla_status s);
+
+/* Detail of the last non-OK status returned on this thread ("" if none). */
+const char *dla_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DLA_H */

@@ -1,0 +1,105 @@
+"""The C-ABI library loads, exports what include/dla.h declares, and rejects bad
+arguments on the host before anything is enqueued (no GPU needed)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import dynamic_state_memory_amd as dla
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "dla.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dla_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = dla.load()
+    names = _declared()
+    assert {"dla_prefill", "dla_decode_step", "dla_cache_init"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert dla.dla_abi_version() == 1
+
+
+def test_sizes_and_layout():
+    assert dla.dla_cache_bytes(1, 1, 8, 64, 64) > 8 * 64 * 64 * 4
+    assert dla.dla_cache_bytes(1, 1, 0, 64, 64) == 0
+    assert dla.dla_cache_bytes(1, 1, 65, 64, 64) == 0
+    assert dla.dla_cache_bytes(1, 1, 8, 96, 64) == 0
+    assert dla.dla_cache_bytes(1, 1, 8, 64, 24) == 0
+    L = dla.dla_cache_layout(2, 3, 32, 128, 256)
+    assert L.meta_offset >= 6 * 32 * 128 * 256 * 4 and L.meta_offset % 256 == 0
+    assert L.meta_stride % 256 == 0 and L.off_k_prev + 4 * 128 <= L.meta_stride
+    assert dla.dla_cache_bytes(2, 3, 32, 128, 256) == L.meta_offset + 6 * L.meta_stride
+    ws = dla.dla_prefill_workspace_bytes(2, 16, 32768, 32, 128, 256)
+    assert ws > 32 * 32768 * 8
+    assert dla.dla_prefill_workspace_bytes(2, 16, 0, 32, 128, 256) == 0
+    assert dla.dla_status_str(3) == "workspace missing or too small"
+
+
+def _cache(B=1, H=1, C_=8, dk=64, dv=64, base=0x10000):
+    c = dla.dla_cache()
+    c.B, c.H, c.C, c.d_k, c.d_v = B, H, C_, dk, dv
+    c.base = base
+    c.bytes = dla.dla_cache_bytes(B, H, C_, dk, dv)
+    return c
+
+
+def test_bad_arguments_are_rejected_on_the_host():
+    # fake, aligned device addresses: validation must fail before any use
+    p = 0x100000
+    c = _cache()
+    ws = dla.dla_prefill_workspace_bytes(1, 1, 100, 8, 64, 64)
+    ok_args = dict(q=p, k=p, v=p, lam=p, o=p, T=100, tau=0.3, io=dla.DLA_F32, cache=c,
+                   workspace=p, workspace_bytes=ws, sched=None, stream=None)
+
+    def call(**kw):
+        a = dict(ok_args)
+        a.update(kw)
+        return dla.dla_prefill(a["q"], a["k"], a["v"], a["lam"], a["o"], a["T"], a["tau"], a["io"],
+                               a["cache"], a["workspace"], a["workspace_bytes"], a["sched"],
+                               a["stream"])
+
+    assert call(q=None) == dla.DLA_ERR_ARG and "non-NULL" in dla.dla_last_error()
+    assert call(k=p + 4) == dla.DLA_ERR_ARG and "aligned" in dla.dla_last_error()
+    assert call(T=0) == dla.DLA_ERR_ARG
+    assert call(T=(1 << 24) + 1) == dla.DLA_ERR_ARG
+    assert call(io=7) == dla.DLA_ERR_ARG
+    assert call(tau=float("nan")) == dla.DLA_ERR_ARG
+    assert call(workspace_bytes=ws - 1) == dla.DLA_ERR_WORKSPACE
+    assert call(workspace=None) == dla.DLA_ERR_WORKSPACE
+    assert call(cache=_cache(C_=0)) == dla.DLA_ERR_ARG
+    assert call(cache=_cache(base=0)) == dla.DLA_ERR_ARG
+    assert call(cache=_cache(base=0x10010)) == dla.DLA_ERR_ARG
+    c_small = _cache()
+    c_small.bytes -= 1
+    assert call(cache=c_small) == dla.DLA_ERR_ARG
+    assert call(cache=_cache(dk=128, dv=64), io=dla.DLA_F32,
+                workspace_bytes=dla.dla_prefill_workspace_bytes(1, 1, 100, 8, 128, 64)) \
+        == dla.DLA_ERR_UNSUPPORTED
+    # decode
+    assert dla.dla_decode_step(p, p, p, p, None, 0.3, dla.DLA_BF16, c, None, None) == dla.DLA_ERR_ARG
+    assert dla.dla_decode_step(p, p, p, p, p, 0.3, dla.DLA_BF16, _cache(dk=64, dv=128), None, None) \
+        == dla.DLA_ERR_UNSUPPORTED
+    # cache init
+    cc = dla.dla_cache()
+    assert dla.dla_cache_init(cc, 0, 1 << 20, 1, 1, 8, 64, 64, None, None) == dla.DLA_ERR_ARG
+    assert dla.dla_cache_init(cc, p, 16, 1, 1, 8, 64, 64, None, None) == dla.DLA_ERR_ARG
+    pre = dla.dla_cache_preload(9, 0, p, p, p, p, 0)
+    assert dla.dla_cache_init(cc, p, 1 << 30, 1, 1, 8, 64, 64, pre, None) == dla.DLA_ERR_ARG
+    pre = dla.dla_cache_preload(2, 0, None, p, p, p, 0)
+    assert dla.dla_cache_init(cc, p, 1 << 30, 1, 1, 8, 64, 64, pre, None) == dla.DLA_ERR_ARG
+
+
+def test_gpu_package_never_imports_the_oracle():
+    pkg = os.path.join(ROOT, "dynamic_state_memory_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                txt = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in txt.lower(), f

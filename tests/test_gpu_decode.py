@@ -1,0 +1,146 @@
+"""GPU parity of dla_decode_step: stream equivalence with prefill and the
+oracle, and the batched-decode workload in its full launch configuration."""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from tests.gpu_common import (TOL, compare_outputs, gpu_prefill, oracle_threads, say,
+                              torch_mod)
+from tests.helpers import mat_rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+def _decode_steps(cache, q, k, v, lam, tau, io, B, H):
+    """Run q.shape[1] decode steps; inputs [S, steps, d] numpy.  Returns o and per-step schedule."""
+    torch = torch_mod()
+    import dynamic_state_memory_amd as dla
+    dev = torch.device("cuda:0")
+    dt = torch.bfloat16 if io == "bf16" else torch.float32
+    S, n = k.shape[:2]
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(np.swapaxes(a, 0, 1))).to(dev).to(dt)
+
+    tq, tk, tv, tl = up(q), up(k), up(v), up(lam)
+    BH = B * H
+    sched = dict(s=torch.empty(n, BH, dtype=torch.float32, device=dev),
+                 boundary=torch.empty(n, BH, dtype=torch.uint8, device=dev),
+                 m_t=torch.empty(n, BH, dtype=torch.int32, device=dev),
+                 ev_i=torch.empty(n, BH, dtype=torch.int32, device=dev))
+    o = torch.empty(n, BH, v.shape[2], dtype=dt, device=dev)
+    for j in range(n):
+        dla.decode_step(tq[j].view(B, H, -1), tk[j].view(B, H, -1), tv[j].view(B, H, -1),
+                        tl[j].view(B, H, -1), tau, cache, o=o[j].view(B, H, -1),
+                        sched={kk: vv[j] for kk, vv in sched.items()})
+    torch.cuda.synchronize()
+    out = o.float().cpu().numpy().swapaxes(0, 1)
+    return out, {kk: vv.cpu().numpy().swapaxes(0, 1) for kk, vv in sched.items()}
+
+
+def _merge_log(r, S, n):
+    """Oracle merges as a per-step array (-1 = none)."""
+    ev = np.full((S, n), -1, np.int32)
+    for i in range(S):
+        for t, e in r["events"][i]:
+            ev[i, t] = e
+    return ev
+
+
+@pytest.mark.parametrize("name,io,T,j,means", [
+    ("tiny_fp32", "f32", 512, 100, None),
+    ("long_t131k_bf16", "bf16", 1500, 300, (20,)),
+])
+def test_prefill_then_decode_equals_one_prefill(name, io, T, j, means):
+    torch = torch_mod()
+    import dynamic_state_memory_amd as dla
+    cfg = workloads.CONFIGS[name]
+    if means is not None:
+        cfg = dataclasses.replace(cfg, seg_means=means)
+    streams = [0] if cfg.B * cfg.H == 1 else [0, 1, 2]
+    d = workloads.prefill_inputs(cfg, streams=streams, T=T)
+    S = len(streams)
+    say(f"decode equivalence {name}: prefill {T - j} + {j} steps")
+    r = oracle.run(d["q"], d["k"], d["v"], d["lam"], cfg.C, cfg.tau, nthreads=oracle_threads())
+    # prefill of the first T - j tokens
+    dev = torch.device("cuda:0")
+    dt = torch.bfloat16 if io == "bf16" else torch.float32
+    cache = dla.Cache(1, S, cfg.C, cfg.dk, cfg.dv, device=dev)
+
+    def up(a, d_):
+        return torch.from_numpy(np.ascontiguousarray(a[:, :T - j])).to(dev).to(dt).reshape(1, S, T - j, d_)
+
+    o1 = dla.prefill(up(d["q"], cfg.dk), up(d["k"], cfg.dk), up(d["v"], cfg.dv), up(d["lam"], cfg.C),
+                     cfg.tau, cache)
+    torch.cuda.synchronize()
+    o1 = o1.float().cpu().numpy().reshape(S, T - j, cfg.dv)
+    o2, sc = _decode_steps(cache, d["q"][:, T - j:], d["k"][:, T - j:], d["v"][:, T - j:],
+                           d["lam"][:, T - j:], cfg.tau, io, 1, S)
+    compare_outputs(o1, r["o"][:, :T - j], TOL[io], "prefill part")
+    compare_outputs(o2, r["o"][:, T - j:], TOL[io], "decode part")
+    assert np.array_equal(sc["s"].view(np.uint32), r["s"][:, T - j:].view(np.uint32))
+    assert np.array_equal(sc["boundary"], r["b"][:, T - j:])
+    assert np.array_equal(sc["m_t"], r["m_t"][:, T - j:])
+    assert np.array_equal(sc["ev_i"], _merge_log(r, S, T)[:, T - j:])
+    fin = cache.read()
+    assert np.array_equal(fin["m"], r["fin_m"])
+    for i in range(S):
+        m = int(r["fin_m"][i])
+        assert np.array_equal(fin["start"][i, :m], r["fin_start"][i, :m])
+        assert np.array_equal(fin["info"][i, :m], r["fin_I"][i, :m])
+        assert mat_rel_err(fin["S"][i, :m], r["fin_S"][i, :m]) <= 1e-4
+    say(f"decode equivalence {name}: ok")
+
+
+def _decode_workload(n_unique, steps, B, H):
+    """The batched-decode workload: n_unique distinct caches tiled over B*H."""
+    d = workloads.decode_inputs(caches=range(n_unique), steps=steps)
+    BH = B * H
+    idx = np.arange(BH) % n_unique
+    return d, idx
+
+
+@pytest.mark.parametrize("B,H,n_unique,steps", [(1, 32, 32, 400), (256, 16, 32, 40)])
+def test_batched_decode_workload(B, H, n_unique, steps):
+    """Full caches preloaded; steps of fresh tokens.  The full launch
+    configuration (B=256, H=16) tiles 32 distinct caches over the 4096 streams,
+    so every stream is checked against the oracle."""
+    torch = torch_mod()
+    import dynamic_state_memory_amd as dla
+    d, idx = _decode_workload(n_unique, steps, B, H)
+    cfg = d["cfg"]
+    C, dk, dv = cfg.C, cfg.dk, cfg.dv
+    S = n_unique
+    say(f"batched decode B={B} H={H} unique={S} steps={steps}: oracle")
+    init = dict(m=np.full(S, C, np.int32), S=d["states"], I=d["info"], n=d["count"], start=d["start"],
+                has_prev=np.zeros(S, np.int32), s_prev=np.ones(S, np.float32),
+                k_prev=np.zeros((S, dk), np.float32), t_seen=np.full(S, d["t_seen"], np.int64))
+    r = oracle.run(d["q"], d["k"], d["v"], d["lam"], C, cfg.tau, init=init, nthreads=oracle_threads())
+    dev = torch.device("cuda:0")
+    say(f"batched decode B={B} H={H}: GPU")
+    ti = torch.from_numpy(idx).to(dev)
+    pre = dict(m0=C, states=torch.from_numpy(d["states"]).to(dev)[ti],
+               info=torch.from_numpy(d["info"]).to(dev)[ti],
+               count=torch.from_numpy(d["count"]).to(dev)[ti],
+               start=torch.from_numpy(d["start"]).to(dev)[ti], t_seen=d["t_seen"])
+    cache = dla.Cache(B, H, C, dk, dv, device=dev, preload=pre)
+    del pre
+    o, sc = _decode_steps(cache, d["q"][idx], d["k"][idx], d["v"][idx], d["lam"][idx], cfg.tau,
+                          "bf16", B, H)
+    compare_outputs(o, r["o"][idx], TOL["bf16"], "decode outputs")
+    assert np.array_equal(sc["s"].view(np.uint32), r["s"][idx].view(np.uint32))
+    assert np.array_equal(sc["boundary"], r["b"][idx])
+    assert np.array_equal(sc["m_t"], r["m_t"][idx])
+    assert np.array_equal(sc["ev_i"], _merge_log(r, S, steps)[idx])
+    # the first step has no previous key: s = 1 opens a state and forces a merge
+    assert np.all(sc["s"][:, 0] == 1.0) and np.all(sc["ev_i"][:, 0] >= 0)
+    if B * H <= 64:
+        fin = cache.read()
+        for i in range(B * H):
+            m = int(r["fin_m"][idx[i]])
+            assert np.array_equal(fin["start"][i, :m], r["fin_start"][idx[i], :m])
+            assert mat_rel_err(fin["S"][i, :m], r["fin_S"][idx[i], :m]) <= 1e-4
+    say(f"batched decode B={B} H={H}: ok, merges/stream {r['n_ev'].mean():.1f}")

@@ -1,0 +1,148 @@
+"""GPU parity of dla_prefill against the oracle (schedule bit-exact, outputs
+within 1e-4 for fp32 and 2e-2 for bf16 inputs, final states within 1e-4)."""
+import dataclasses
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from tests.gpu_common import (TOL, compare_outputs, compare_schedule, compare_states, gpu_prefill,
+                              oracle_threads, say, torch_mod)
+from tests.helpers import keys_for_scores, row_rel_err
+
+pytestmark = pytest.mark.gpu
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "schedule_cases.json")
+
+
+def _full_check(d, C, tau, io, label, B=None, H=None):
+    say(f"prefill {label}: S={d['k'].shape[0]} T={d['k'].shape[1]} dk={d['k'].shape[2]} "
+        f"dv={d['v'].shape[2]} C={C} tau={tau} io={io}")
+    o, sc, fin = gpu_prefill(d["q"], d["k"], d["v"], d["lam"], C, tau, io, B=B, H=H)
+    r = oracle.run(d["q"], d["k"], d["v"], d["lam"], C, tau, nthreads=oracle_threads())
+    compare_schedule(r, sc, fin, label)
+    compare_states(r, fin, label=label)
+    err = compare_outputs(o, r["o"], TOL[io], label)
+    say(f"prefill {label}: ok, max row rel err {err:.2e}, merges {int(r['n_ev'].sum())}")
+    return r
+
+
+def test_tiny_fp32_workload():
+    torch_mod()
+    d = workloads.prefill_inputs("tiny_fp32")
+    cfg = d["cfg"]
+    r = _full_check(d, cfg.C, cfg.tau, "f32", "tiny_fp32")
+    assert r["n_ev"].sum() > 0
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_hand_derived_schedules(io):
+    torch_mod()
+    cases = json.load(open(GOLDEN))["cases"]
+    for case in cases:
+        s_des = case["s_after_first"]
+        T = len(s_des) + 1
+        k = keys_for_scores(s_des, dk=64)[None]
+        rng = np.random.default_rng(3)
+        q = workloads.round_bf16(rng.standard_normal((1, T, 64)).astype(np.float32) / 8)
+        v = workloads.round_bf16(rng.standard_normal((1, T, 16)).astype(np.float32) / 4)
+        lam = workloads.round_bf16(rng.uniform(0.1, 1, (1, T, case["C"])).astype(np.float32))
+        d = dict(q=q, k=k, v=v, lam=lam)
+        r = _full_check(d, case["C"], case["tau"], io, f"golden {case['name']} {io}")
+        e = case["expect"]
+        assert r["b"][0].tolist() == e["boundary"]
+
+
+REDUCED = [
+    # (workload, streams, T, segment means override)
+    ("mamba2_780m_bf16", [0, 1, 2], 1000, None),
+    ("mamba2_780m_bf16", [5, 6], 2100, (20,)),
+    ("gdn_1p3b_t32k_bf16", [0, 1], 3000, None),
+    ("gdn_1p3b_t32k_bf16", [2, 3], 2500, (12, 90)),
+    ("long_t131k_bf16", [0, 1], 4099, (16,)),
+    ("long_t131k_bf16", [3], 700, None),
+]
+
+
+@pytest.mark.parametrize("name,streams,T,means", REDUCED)
+def test_reduced_bf16_workloads(name, streams, T, means):
+    torch_mod()
+    cfg = workloads.CONFIGS[name]
+    if means is not None:
+        cfg = dataclasses.replace(cfg, seg_means=means)
+    d = workloads.prefill_inputs(cfg, streams=streams, T=T)
+    r = _full_check(d, cfg.C, cfg.tau, "bf16", f"{name} T={T} means={cfg.seg_means}")
+    if means is not None:
+        assert r["n_ev"].min() > 0
+
+
+def test_literal_noise_reading_every_token_opens():
+    torch_mod()
+    cfg = workloads.CONFIGS["gdn_1p3b_t32k_bf16"]
+    d = workloads.prefill_inputs(cfg, reading="literal", streams=[0, 1], T=777)
+    r = _full_check(d, cfg.C, cfg.tau, "bf16", "literal reading")
+    assert r["b"].mean() > 0.99 and r["n_ev"].min() >= 777 - cfg.C - 5
+
+
+@pytest.mark.parametrize("tau,C", [(-1.0, 64), (-1.0, 5), (3.0, 8), (0.3, 1), (0.9, 63)])
+def test_threshold_and_capacity_extremes(tau, C):
+    torch_mod()
+    cfg = dataclasses.replace(workloads.CONFIGS["long_t131k_bf16"], C=C, seg_means=(10,))
+    d = workloads.prefill_inputs(cfg, streams=[0, 1], T=300)
+    _full_check(d, C, tau, "bf16", f"tau={tau} C={C}")
+
+
+def test_lambda_one_is_causal_linear_attention():
+    torch = torch_mod()
+    cfg = dataclasses.replace(workloads.CONFIGS["mamba2_780m_bf16"], seg_means=(30,))
+    d = workloads.prefill_inputs(cfg, streams=[0], T=500)
+    d["lam"] = np.ones_like(d["lam"])
+    say("prefill lambda=1")
+    o, _, fin = gpu_prefill(d["q"], d["k"], d["v"], d["lam"], cfg.C, cfg.tau, "bf16")
+    Q, K, V = (d[x][0].astype(np.float64) for x in ("q", "k", "v"))
+    ref = np.tril(Q @ K.T) @ V
+    assert row_rel_err(o[0], ref) <= TOL["bf16"]
+    # the final states sum to the whole prefix
+    tot = fin["S"][0, :int(fin["m"][0])].astype(np.float64).sum(0)
+    assert np.abs(tot - V.T @ K).max() <= 1e-4 * np.abs(V.T @ K).max()
+    del torch
+
+
+def test_runs_are_bitwise_deterministic():
+    torch_mod()
+    cfg = dataclasses.replace(workloads.CONFIGS["gdn_1p3b_t32k_bf16"], seg_means=(16, 200))
+    d = workloads.prefill_inputs(cfg, streams=[0, 1], T=1500)
+    say("prefill determinism")
+    outs, sc, fin = gpu_prefill(d["q"], d["k"], d["v"], d["lam"], cfg.C, cfg.tau, "bf16", repeats=2)
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+
+
+FULL = ["mamba2_780m_bf16", "gdn_1p3b_t32k_bf16", "long_t131k_bf16"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_workload_sampled(name):
+    """Full workload in the benchmark's launch configuration: whole schedule and
+    final cache bit-exact / 1e-4, outputs at sampled tokens within 2e-2."""
+    torch_mod()
+    cfg = workloads.CONFIGS[name]
+    say(f"full-size {name}: generating inputs")
+    d = workloads.prefill_inputs(cfg)
+    S, T = d["k"].shape[:2]
+    rng = np.random.default_rng(99)
+    want = np.zeros((S, T), bool)
+    for i in range(S):
+        want[i, rng.choice(T, 24, replace=False)] = True
+        want[i, [0, 63, 64, T - 1]] = True
+    say(f"full-size {name}: GPU prefill")
+    o, sc, fin = gpu_prefill(d["q"], d["k"], d["v"], d["lam"], cfg.C, cfg.tau, "bf16", B=cfg.B, H=cfg.H)
+    say(f"full-size {name}: oracle ({oracle_threads()} threads)")
+    r = oracle.run(d["q"], d["k"], d["v"], d["lam"], cfg.C, cfg.tau, want=want,
+                   nthreads=oracle_threads())
+    compare_schedule(r, sc, fin, name)
+    compare_states(r, fin, label=name)
+    err = compare_outputs(o, r["o"], TOL["bf16"], name, mask=want)
+    say(f"full-size {name}: ok, sampled max row rel err {err:.2e}, merges/stream "
+        f"{r['n_ev'].mean():.1f}, boundaries/stream {r['b'].sum(1).mean():.1f}")

@@ -1,0 +1,305 @@
+#!/usr/bin/env python3
+"""Throughput of the DLA layer forward pass on one MI355X.
+
+Headline (the JSON line's value): prefill tokens/s of the Gated-DeltaNet-1.3B
+shaped layer at T = 32768 (B=2, H=16, d_k=128, d_v=256, C=32, tau=0.3, bf16),
+one step = one dla_prefill call over the whole batch (score, boundaries,
+greedy capacity merges, chunked MFMA read/update).  Inputs are synthetic
+(seeded piecewise-regime keys) and resident in HBM before timing starts.
+
+Also reported on the same line:
+  roofline      the chunk kernel's algorithmic flops (sum over token-heads of
+                2 (m_t + 1) d_k d_v, m_t from the run's own schedule) per
+                launch over its HIP-event-timed duration, against the dense
+                bf16 MFMA peak;
+  decode        batched decode (B=256, H=16, d=128, C=32 full fp32 caches):
+                steps/s over a loop of dla_decode_step calls and the decode
+                kernel's algorithmic HBM bytes per launch over its duration,
+                against the HBM peak;
+  cpu_baseline  the CPU oracle on a bounded sample of the prefill workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "DLA prefill tokens/s at T=32K; decode steps/s at B=256; % MFMA / HBM peak"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def prefill_bench(args, torch, dla, workloads):
+    cfg = workloads.CONFIGS[args.workload]
+    B, H, T, dk, dv, C = cfg.B, cfg.H, cfg.T, cfg.dk, cfg.dv, cfg.C
+    BH = B * H
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    d = workloads.prefill_inputs(cfg, reading=args.reading)
+    log(f"prefill inputs {args.workload} ({args.reading}) generated in {time.time() - t0:.1f}s")
+    dt = torch.bfloat16 if cfg.io == "bf16" else torch.float32
+
+    def up(a, dd):
+        return torch.from_numpy(a).to(dev).to(dt).view(B, H, T, dd)
+
+    q, k, v, lam = up(d["q"], dk), up(d["k"], dk), up(d["v"], dv), up(d["lam"], C)
+    sample = None
+    if not args.no_cpu:
+        S = min(BH, args.cpu_streams)
+        sample = {x: d[x][:S].copy() for x in ("q", "k", "v", "lam")}
+    del d
+    cache = dla.Cache(B, H, C, dk, dv, device=dev)
+    ws = dla.prefill_workspace(B, H, T, C, dk, dv, dev)
+    o = torch.empty(B, H, T, dv, dtype=dt, device=dev)
+    # one untimed call exporting the schedule: m_t gives the algorithmic flops
+    m_t = torch.empty(BH, T, dtype=torch.int32, device=dev)
+    bnd = torch.empty(BH, T, dtype=torch.uint8, device=dev)
+    n_ev = torch.empty(BH, dtype=torch.int32, device=dev)
+    dla.prefill(q, k, v, lam, cfg.tau, cache, o=o, workspace=ws,
+                sched=dict(m_t=m_t, boundary=bnd, n_ev=n_ev))
+    torch.cuda.synchronize()
+    m_sum = int(m_t.sum(dtype=torch.int64).item())
+    flops = 2.0 * (m_sum + BH * T) * dk * dv
+    stats = dict(mean_live_states=m_sum / (BH * T),
+                 boundaries_per_stream=float(bnd.sum(dtype=torch.int64).item()) / BH,
+                 merges_per_stream=float(n_ev.sum(dtype=torch.int64).item()) / BH)
+    for _ in range(args.warmup):
+        dla.prefill(q, k, v, lam, cfg.tau, cache, o=o, workspace=ws)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for a, b in evs:          # materialise the event handles
+        a.record()
+        b.record()
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for a, b in evs:
+        dla.dla_set_prefill_events(a.cuda_event, b.cuda_event)
+        dla.prefill(q, k, v, lam, cfg.tau, cache, o=o, workspace=ws)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    dla.dla_set_prefill_events(None, None)
+    kern_ms = [a.elapsed_time(b) for a, b in evs]
+    kern_avg = sum(kern_ms) / len(kern_ms)
+    ms_per_step = wall * 1e3 / args.steps
+    tokens = B * T
+    achieved = flops / (kern_avg * 1e-3) / 1e12
+    res = dict(
+        value=tokens / (ms_per_step * 1e-3), ms_per_step=ms_per_step,
+        config=dict(workload=f"{args.workload} prefill", B=B, H=H, T=T, d_k=dk, d_v=dv, C=C,
+                    tau=cfg.tau, io=cfg.io, keys=f"piecewise-regime, {args.reading} noise",
+                    segment_means=list(cfg.seg_means)),
+        roofline=dict(bound="mfma", achieved=achieved, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                      frac=achieved / PEAK_BF16_TFLOPS, traffic=None,
+                      kernel="k_prefill", kernel_ms=kern_avg, algorithmic_flop_per_launch=flops),
+        schedule=stats,
+        token_heads_per_s=BH * T / (ms_per_step * 1e-3),
+    )
+    log(f"prefill: {ms_per_step:.3f} ms/step, chunk kernel {kern_avg:.3f} ms, "
+        f"{achieved:.1f} TFLOP/s algorithmic ({100 * achieved / PEAK_BF16_TFLOPS:.1f}% of bf16 peak), "
+        f"mean live states {stats['mean_live_states']:.2f}")
+    del q, k, v, lam, o, ws, cache
+    torch.cuda.empty_cache()
+    return res, sample, cfg
+
+
+def decode_inputs_device(torch, cfg, steps, dev):
+    """The batched-decode workload drawn on the device with torch's seeded
+    generator (same recipe as workloads.decode_inputs, different generator)."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(cfg.seed)
+    BH, C, dk, dv, n0 = cfg.B * cfg.H, cfg.C, cfg.dk, cfg.dv, cfg.init_tokens
+    bf = torch.bfloat16
+    states = torch.empty(BH, C, dv, dk, dtype=torch.float32, device=dev)
+    step = 128
+    for c0 in range(0, BH, step):
+        n = min(step, BH - c0)
+        U = (torch.randn(n * C, dv, n0, generator=g, device=dev) / math.sqrt(dv)).to(bf).float()
+        W = (torch.randn(n * C, n0, dk, generator=g, device=dev) / math.sqrt(dk)).to(bf).float()
+        states[c0:c0 + n] = torch.bmm(U, W.contiguous()).view(n, C, dv, dk)
+    e = torch.empty(BH, C, dtype=torch.float64, device=dev).exponential_(1.0, generator=g)
+    info = torch.round(e * 2.0 ** 32).to(torch.int64)
+    count = torch.full((BH, C), n0, dtype=torch.int32, device=dev)
+    start = (torch.arange(C, device=dev, dtype=torch.int64) * n0).expand(BH, C).contiguous()
+    # keys: a new regime starts at each step with probability 1/mean (Geometric lengths)
+    mu = cfg.seg_means[0]
+    newseg = torch.rand(BH, steps, generator=g, device=dev) < (1.0 / mu)
+    seg = torch.cumsum(newseg.to(torch.int32), 1)
+    nseg = int(seg.max().item()) + 1
+    cent = torch.randn(BH, nseg, dk, generator=g, device=dev)
+    cent = cent / cent.norm(dim=2, keepdim=True)
+    K = torch.empty(steps, BH, dk, dtype=bf, device=dev)
+    Q = torch.empty(steps, BH, dk, dtype=bf, device=dev)
+    V = torch.empty(steps, BH, dv, dtype=bf, device=dev)
+    L = torch.empty(steps, BH, C, dtype=bf, device=dev)
+    for s0 in range(0, steps, 256):
+        n = min(256, steps - s0)
+        sg = seg[:, s0:s0 + n].long()
+        kk = torch.gather(cent, 1, sg.unsqueeze(2).expand(BH, n, dk)) + \
+            (0.2 / math.sqrt(dk)) * torch.randn(BH, n, dk, generator=g, device=dev)
+        K[s0:s0 + n] = kk.transpose(0, 1).to(bf)
+        Q[s0:s0 + n] = (torch.randn(n, BH, dk, generator=g, device=dev) / math.sqrt(dk)).to(bf)
+        V[s0:s0 + n] = (torch.randn(n, BH, dv, generator=g, device=dev) / math.sqrt(dv)).to(bf)
+        L[s0:s0 + n] = torch.sigmoid(torch.randn(n, BH, C, generator=g, device=dev)).to(bf)
+    return dict(states=states, info=info, count=count, start=start, t_seen=C * n0,
+                q=Q, k=K, v=V, lam=L)
+
+
+def decode_bench(args, torch, dla, workloads):
+    cfg = workloads.CONFIGS[args.decode_workload]
+    B, H, C, dk, dv = cfg.B, cfg.H, cfg.C, cfg.dk, cfg.dv
+    BH = B * H
+    dev = torch.device("cuda:0")
+    S, W = args.decode_steps, args.decode_warmup
+    t0 = time.time()
+    d = decode_inputs_device(torch, cfg, S + W, dev)
+    cache = dla.Cache(B, H, C, dk, dv, device=dev,
+                      preload=dict(m0=C, states=d["states"], info=d["info"], count=d["count"],
+                                   start=d["start"], t_seen=d["t_seen"]))
+    del d["states"]
+    torch.cuda.synchronize()
+    log(f"decode inputs generated in {time.time() - t0:.1f}s")
+    o = torch.empty(B, H, dv, dtype=torch.bfloat16, device=dev)
+    bnd = torch.empty(S + W, BH, dtype=torch.uint8, device=dev)
+    evi = torch.empty(S + W, BH, dtype=torch.int32, device=dev)
+    mt = torch.empty(S + W, BH, dtype=torch.int32, device=dev)
+
+    def step(j):
+        dla.decode_step(d["q"][j].view(B, H, dk), d["k"][j].view(B, H, dk), d["v"][j].view(B, H, dv),
+                        d["lam"][j].view(B, H, C), cfg.tau, cache, o=o,
+                        sched=dict(boundary=bnd[j], ev_i=evi[j], m_t=mt[j]))
+
+    for j in range(W):
+        step(j)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(S)]
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for i, (a, b) in enumerate(evs):
+        a.record()
+        step(W + i)
+        b.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    kern = [a.elapsed_time(b) for a, b in evs]
+    kern_avg = sum(kern) / S
+    # algorithmic bytes: every live state read once; states written (1, or 2
+    # for a merge away from the newest pair); q, k, v, lam in, o out (bf16);
+    # the stream's metadata read and written
+    b_ = bnd[W:].to(torch.int64)
+    e_ = evi[W:].to(torch.int64)
+    m_prev = torch.cat([mt[W - 1:W] if W > 0 else torch.full((1, BH), C, dtype=torch.int32, device=dev),
+                        mt[W:-1]], 0).to(torch.int64)
+    writes = torch.where((b_ == 1) & (e_ >= 0) & (e_ < m_prev - 1), 2, 1)
+    st_bytes = dk * dv * 4
+    meta_rw = 2 * (32 + 64 + 20 * m_prev + 4 * dk)
+    io_bytes = 2 * (2 * dk + dv + C + dv)
+    total = (m_prev * st_bytes + writes * st_bytes + meta_rw + io_bytes).sum().item()
+    bytes_per_step = total / S
+    achieved = bytes_per_step / (kern_avg * 1e-3) / 1e9
+    res = dict(
+        workload=f"{args.decode_workload}", B=B, H=H, d_k=dk, d_v=dv, C=C, steps=S, warmup=W,
+        steps_per_s=S / wall, ms_per_step=wall * 1e3 / S, tokens_per_s=BH * S / wall,
+        boundaries_per_stream=float(b_.sum().item()) / BH,
+        merges_per_stream=float((e_ >= 0).sum().item()) / BH,
+        roofline=dict(bound="hbm", achieved=achieved, peak=PEAK_HBM_GBS, unit="GB/s",
+                      frac=achieved / PEAK_HBM_GBS, traffic=None, kernel="k_decode",
+                      kernel_ms=kern_avg, algorithmic_bytes_per_launch=bytes_per_step),
+        inputs="drawn on the device with torch's seeded generator, same recipe",
+    )
+    log(f"decode: {res['steps_per_s']:.1f} steps/s, kernel {kern_avg:.3f} ms, "
+        f"{achieved:.0f} GB/s algorithmic ({100 * achieved / PEAK_HBM_GBS:.1f}% of HBM peak)")
+    return res
+
+
+def cpu_baseline(args, sample, cfg):
+    """The oracle as it stands on S streams x the first Ts tokens; Ts doubles
+    from 512 until one run takes a third of the time budget, and that run is
+    reported."""
+    import oracle
+    S = sample["k"].shape[0]
+    cores = min(S, os.cpu_count() or 1)
+    Ts = 512
+    while True:
+        t0 = time.perf_counter()
+        oracle.run(*(sample[x][:, :Ts] for x in ("q", "k", "v", "lam")), cfg.C, cfg.tau,
+                   final_states=False, nthreads=cores)
+        dt = time.perf_counter() - t0
+        if dt >= args.cpu_seconds / 3 or Ts >= cfg.T:
+            break
+        Ts = min(cfg.T, 2 * Ts)
+    # a token of the layer is d_k x d_v work in each of the H heads
+    val = S * Ts / dt / cfg.H
+    log(f"cpu oracle: {S} streams x {Ts} tokens in {dt:.1f}s on {cores} threads")
+    return dict(value=val, unit="tokens/s", cores=cores, kind="oracle",
+                sample=f"{S} of {cfg.B * cfg.H} streams x first {Ts} of {cfg.T} tokens of the "
+                       f"prefill workload (schedule, states and every output, float64), "
+                       f"{dt:.1f} s; value = stream-tokens/s / H",
+                host_cpu=_cpu_model())
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="gdn_1p3b_t32k_bf16")
+    ap.add_argument("--reading", default="relative", choices=["relative", "literal"])
+    ap.add_argument("--decode-workload", default="decode_b256_bf16")
+    ap.add_argument("--decode-steps", type=int, default=4096)
+    ap.add_argument("--decode-warmup", type=int, default=8)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-streams", type=int, default=16)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures the layer on one GPU only (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE {world}): streams shard over GPUs with no communication, so a "
+              f"multi-GPU figure is N independent copies of this one.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import dynamic_state_memory_amd as dla
+    import workloads
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dla.load()
+    pre, sample, cfg = prefill_bench(args, torch, dla, workloads)
+    dec = None if args.no_decode else decode_bench(args, torch, dla, workloads)
+    cpu = None if args.no_cpu else cpu_baseline(args, sample, cfg)
+    out = {
+        "metric": METRIC, "value": pre["value"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": pre["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic", "config": pre["config"], "roofline": pre["roofline"],
+        "cpu_baseline": cpu, "decode": dec, "schedule": pre["schedule"],
+        "token_heads_per_s": pre["token_heads_per_s"],
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -17,7 +17,8 @@ __all__ = [
     "DLA_OK", "DLA_F32", "DLA_BF16", "DLAError", "lib_path", "load",
     "dla_abi_version", "dla_cache_bytes", "dla_cache_layout", "dla_cache_init",
     "dla_prefill_workspace_bytes", "dla_prefill", "dla_decode_step",
-    "dla_status_str", "dla_last_error", "Cache", "prefill", "decode_step",
+    "dla_status_str", "dla_last_error", "dla_set_prefill_events", "Cache", "prefill",
+    "decode_step",
     "prefill_workspace", "DLA_MAX_C", "DLA_CHUNK",
 ]
 
@@ -75,6 +76,11 @@ def load():
     global _lib
     if _lib is not None:
         return _lib
+    try:
+        # load torch's HIP runtime first so that the library binds to the same one
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     if not os.path.exists(_LIB):
         raise RuntimeError(f"{_LIB} is missing: build it with `python __graft_entry__.py build` "
                            "or dynamic_state_memory_amd/build.py")
@@ -97,6 +103,8 @@ def load():
     lib.dla_decode_step.restype = C.c_int
     lib.dla_decode_step.argtypes = [vp, vp, vp, vp, vp, f32, C.c_int, C.POINTER(dla_cache),
                                     C.POINTER(dla_schedule_out), vp]
+    lib.dla_set_prefill_events.restype = C.c_int
+    lib.dla_set_prefill_events.argtypes = [vp, vp]
     lib.dla_status_str.restype = C.c_char_p
     lib.dla_status_str.argtypes = [C.c_int]
     lib.dla_last_error.restype = C.c_char_p
@@ -142,6 +150,10 @@ def dla_decode_step(q, k, v, lam, o, tau, io, cache: dla_cache,
                     sched: dla_schedule_out | None, stream) -> int:
     return load().dla_decode_step(q, k, v, lam, o, tau, io, C.byref(cache),
                                   C.byref(sched) if sched is not None else None, stream)
+
+
+def dla_set_prefill_events(before, after) -> int:
+    return load().dla_set_prefill_events(before, after)
 
 
 def dla_status_str(s: int) -> str:

@@ -17,6 +17,7 @@ using namespace dla;
 namespace {
 
 thread_local char g_err[512] = "";
+thread_local hipEvent_t g_ev_before = nullptr, g_ev_after = nullptr;
 
 dla_status fail(dla_status s, const char *fmt, ...)
 {
@@ -235,6 +236,8 @@ dla_status dla_prefill(const void *q, const void *k, const void *v, const void *
     if (io == DLA_F32 && cache->d_k != 64)
         return fail(DLA_ERR_UNSUPPORTED, "float32 prefill supports d_k = 64 only");
     if (tau != tau) return fail(DLA_ERR_ARG, "tau is NaN");
+    if (sched && ((sched->ev_t == nullptr) != (sched->ev_i == nullptr)))
+        return fail(DLA_ERR_ARG, "schedule export: ev_t and ev_i go together");
     const int64_t BH = static_cast<int64_t>(cache->B) * cache->H;
     const Sizes z = workspace_sizes(BH, T, cache->C, cache->d_k, cache->d_v);
     if (!workspace || !aligned(workspace, 256)) return fail(DLA_ERR_WORKSPACE, "workspace NULL or not 256-byte aligned");
@@ -254,6 +257,8 @@ dla_status dla_prefill(const void *q, const void *k, const void *v, const void *
     a.states = reinterpret_cast<float *>(b8);
     a.meta = b8 + align_up(states_bytes(BH, cache->C, cache->d_k, cache->d_v), 256);
     a.ws = carve(workspace, z);
+    a.ev_before = g_ev_before;
+    a.ev_after = g_ev_after;
     if (sched) a.sched = *sched;
     else std::memset(&a.sched, 0, sizeof(a.sched));
     // schedule fields the prefill kernels never fill are ignored; s and boundary
@@ -297,6 +302,15 @@ dla_status dla_decode_step(const void *q, const void *k, const void *v, const vo
     a.sched.m_t = sched ? sched->m_t : nullptr;
     a.sched.ev_i = sched ? sched->ev_i : nullptr;
     return hip_status(launch_decode(a, static_cast<hipStream_t>(stream)), "decode launch");
+}
+
+dla_status dla_set_prefill_events(void *before, void *after)
+{
+    if ((before == nullptr) != (after == nullptr))
+        return fail(DLA_ERR_ARG, "pass both events or neither");
+    g_ev_before = static_cast<hipEvent_t>(before);
+    g_ev_after = static_cast<hipEvent_t>(after);
+    return ok();
 }
 
 const char *dla_status_str(dla_status s)

@@ -79,6 +79,7 @@ struct PrefillArgs {
     uint8_t *meta;
     Workspace ws;
     dla_schedule_out sched;
+    hipEvent_t ev_before, ev_after;   // optional, recorded around the chunk kernel
 };
 
 struct DecodeSched {

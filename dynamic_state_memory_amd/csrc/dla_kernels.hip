@@ -26,6 +26,7 @@ namespace dla {
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ float to_f(float x) { return x; }
 __device__ __forceinline__ float to_f(__bf16 x) { return static_cast<float>(x); }
@@ -52,10 +53,21 @@ __device__ __forceinline__ float cosine_distance(double d, double a, double b) {
 // Eight consecutive elements, the per-lane operand of one 16x16x32 MFMA step.
 template <typename T> struct Frag;
 template <> struct Frag<__bf16> { bf16x8 v; };
+template <> struct Frag<_Float16> { f16x8 v; };
 template <> struct Frag<float> { float v[8]; };
+
+// Operand type of the inter-chunk read: bf16 inputs are read against an fp16
+// copy of the states (11-bit significands, normalised per state by a power of
+// two), fp32 inputs against the fp32 states themselves.
+template <typename TIO> struct ReadT;
+template <> struct ReadT<__bf16> { typedef _Float16 type; };
+template <> struct ReadT<float> { typedef float type; };
 
 __device__ __forceinline__ void load_frag(Frag<__bf16> &f, const __bf16 *p) {
     f.v = *reinterpret_cast<const bf16x8 *>(p);
+}
+__device__ __forceinline__ void load_frag(Frag<_Float16> &f, const _Float16 *p) {
+    f.v = *reinterpret_cast<const f16x8 *>(p);
 }
 __device__ __forceinline__ void load_frag(Frag<float> &f, const float *p) {
     const float4 a = reinterpret_cast<const float4 *>(p)[0];
@@ -90,6 +102,9 @@ __device__ __forceinline__ void mask_frag(Frag<float> &f, int base, int lo, int 
 __device__ __forceinline__ void mma32(floatx4 &acc, const Frag<__bf16> &a, const Frag<__bf16> &b) {
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, acc, 0, 0, 0);
 }
+__device__ __forceinline__ void mma32(floatx4 &acc, const Frag<_Float16> &a, const Frag<_Float16> &b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a.v, b.v, acc, 0, 0, 0);
+}
 __device__ __forceinline__ void mma32(floatx4 &acc, const Frag<float> &a, const Frag<float> &b) {
 #pragma unroll
     for (int e = 0; e < 8; ++e)
@@ -101,6 +116,26 @@ template <typename T> __device__ __forceinline__ T wave_sum(T x) {
     for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
     return x;
 }
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+    return x;
+}
+
+// Exponent e with max * 2^-e in [2^14, 2^15): the largest magnitude then uses
+// the top of fp16's range; 0 for an all-zero block.
+__device__ __forceinline__ int f16_exponent(float maxabs) {
+    return maxabs > 0.0f ? ilogbf(maxabs) - 14 : 0;
+}
+
+// The query chunk's A fragment of the inter-chunk read: fp16, scaled by 2^-e.
+__device__ __forceinline__ void read_frag_from(Frag<_Float16> &f, const __bf16 *p, int e) {
+    const bf16x8 x = *reinterpret_cast<const bf16x8 *>(p);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f.v[j] = static_cast<_Float16>(ldexpf(static_cast<float>(x[j]), -e));
+}
+__device__ __forceinline__ void read_frag_from(Frag<float> &f, const float *p, int) { load_frag(f, p); }
 
 __device__ __forceinline__ int64_t wave_min_i64(int64_t x) {
 #pragma unroll
@@ -459,7 +494,9 @@ struct PrefillSmem {
     int32_t grp_slot[kChunk + 1];
     int32_t grp_add[kChunk + 1];
     int32_t changed[kMaxC + kChunk + 1];
-    int32_t n_merge, n_grp, n_changed, m_new;
+    int32_t shexp[kMaxC];         // power-of-two exponent of each fp16 state copy
+    float red[4];
+    int32_t n_merge, n_grp, n_changed, m_new, qexp;
 };
 
 // One block (4 waves) per (stream, d_v tile of DVT columns); sweeps the
@@ -474,14 +511,17 @@ struct PrefillSmem {
 //      lam_t[#{live chunk starts > s}] for s <= t;
 //   4. o store; then chunk-end update: old merges S_a += S_b, every group of
 //      chunk tokens adds (or sets) V_g^T K_g into its final state, and the
-//      bf16 copies used as MFMA operands are refreshed.
-// States are fp32 in the cache; TS is the type the read streams (a bf16 copy
-// in the workspace for bf16 io, the fp32 state itself for fp32 io).
+//      operand copies of the changed states are refreshed.
+// States are fp32 in the cache.  With bf16 inputs the read streams an fp16
+// copy of each state, normalised by a power of two kept in LDS, against the
+// query chunk scaled by a power of two; both exponents are folded into the
+// read weights.  The intra-chunk product and the state updates multiply the
+// exact bf16 inputs (fp32 accumulation).  With fp32 inputs everything is fp32.
 template <typename TIO, int DK, int DVT>
 __global__ __launch_bounds__(256, 1) void k_prefill(
     const TIO *__restrict__ Q, const TIO *__restrict__ K, const TIO *__restrict__ V,
     const TIO *__restrict__ LAM, TIO *__restrict__ O, int T, int C, int DV, int nblk_dv,
-    float *__restrict__ states, TIO *__restrict__ shadow,
+    float *__restrict__ states, typename ReadT<TIO>::type *__restrict__ shadow,
     const int2 *__restrict__ events, const int32_t *__restrict__ chunk_ev,
     uint8_t *__restrict__ meta_base, size_t meta_stride, int32_t *__restrict__ m_t_out)
 {
@@ -489,6 +529,8 @@ __global__ __launch_bounds__(256, 1) void k_prefill(
     constexpr int NTV = DVT / 16;   // 16-wide tiles over the d_v slice
     constexpr int MT = kChunk / 16; // 16-row tiles over the chunk
     constexpr int EPV = 16 / sizeof(TIO);
+    constexpr bool kHalfRead = sizeof(TIO) == 2;
+    typedef typename ReadT<TIO>::type RT;
     typedef PrefillSmem<TIO, DK, DVT> Smem;
     extern __shared__ __align__(16) unsigned char smem_raw[];
     Smem &S = *reinterpret_cast<Smem *>(smem_raw);
@@ -506,21 +548,22 @@ __global__ __launch_bounds__(256, 1) void k_prefill(
     const size_t tok0 = static_cast<size_t>(bh) * T;
     // a state's d_v slice for this block starts at state(p) + dv0*DK
     float *st_base = states + static_cast<size_t>(bh) * C * DV * DK + static_cast<size_t>(dv0) * DK;
-    const TIO *rd_base;
-    if constexpr (sizeof(TIO) == 2)
+    const RT *rd_base;
+    if constexpr (kHalfRead)
         rd_base = shadow + static_cast<size_t>(bh) * C * DV * DK + static_cast<size_t>(dv0) * DK;
     else
-        rd_base = reinterpret_cast<const TIO *>(st_base);
+        rd_base = reinterpret_cast<const RT *>(st_base);
     const size_t slot_stride = static_cast<size_t>(DV) * DK;
 
     int m0 = 0;
-    if (tid < kMaxC) S.order[tid] = tid;
+    if (tid < kMaxC) { S.order[tid] = tid; S.shexp[tid] = 0; }
 
     for (int ch = 0; ch < NCH; ++ch) {
         const int c0 = ch * kChunk;
         const int nvalid = min(kChunk, T - c0);
         __syncthreads();
         // ---- 1. load the chunk and build token masks
+        float qmax = 0.0f;
         for (int idx = tid; idx < kChunk * DK / EPV; idx += 256) {
             const int r = idx / (DK / EPV), cv = (idx % (DK / EPV)) * EPV;
             uint4 qv = make_uint4(0, 0, 0, 0), kv = qv;
@@ -531,6 +574,9 @@ __global__ __launch_bounds__(256, 1) void k_prefill(
             }
             *reinterpret_cast<uint4 *>(&S.q[r][cv]) = qv;
             *reinterpret_cast<uint4 *>(&S.k[r][cv]) = kv;
+            const TIO *qe = reinterpret_cast<const TIO *>(&qv);
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) qmax = fmaxf(qmax, fabsf(to_f(qe[e])));
             const TIO *ke = reinterpret_cast<const TIO *>(&kv);
 #pragma unroll
             for (int e = 0; e < EPV; ++e) S.kt[cv + e][r] = ke[e];
@@ -565,18 +611,22 @@ __global__ __launch_bounds__(256, 1) void k_prefill(
             if (m_t_out && dv0 == 0 && tid < nvalid)
                 m_t_out[tok0 + c0 + tid] = __popcll(om) + __popcll(nm);
         }
+        qmax = wave_max(qmax);
+        if (lane == 0) S.red[wave] = qmax;
         __syncthreads();
+        const int qexp = kHalfRead ? f16_exponent(fmaxf(fmaxf(S.red[0], S.red[1]), fmaxf(S.red[2], S.red[3]))) : 0;
         for (int idx = tid; idx < m0 * kChunk; idx += 256) {
             const int i = idx / kChunk, t = idx % kChunk;
             const int slot = __popcll(shr64(S.om[t], i + 1)) + __popcll(S.nm[t]);
-            S.wold[i][t] = S.lam[t][slot];
+            const float w = S.lam[t][slot];
+            S.wold[i][t] = kHalfRead ? ldexpf(w, S.shexp[S.order[i]] + qexp) : w;
         }
         // Q fragments of the whole chunk (A operand of the inter-chunk read)
-        Frag<TIO> qf[MT][KS];
+        Frag<RT> qf[MT][KS];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) load_frag(qf[mt][ks], &S.q[16 * mt + lr][32 * ks + 8 * lg]);
+            for (int ks = 0; ks < KS; ++ks) read_frag_from(qf[mt][ks], &S.q[16 * mt + lr][32 * ks + 8 * lg], qexp);
         __syncthreads();
 
         // ---- 2. inter-chunk read over the states live at the chunk start
@@ -586,10 +636,10 @@ __global__ __launch_bounds__(256, 1) void k_prefill(
 #pragma unroll
             for (int nt = 0; nt < NTV; ++nt) Oi[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
         {
-            Frag<TIO> bc[KS][NTV], bn[KS][NTV];
+            Frag<RT> bc[KS][NTV], bn[KS][NTV];
             int i = wave;
             if (i < m0) {
-                const TIO *sp = rd_base + S.order[i] * slot_stride;
+                const RT *sp = rd_base + S.order[i] * slot_stride;
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
@@ -598,7 +648,7 @@ __global__ __launch_bounds__(256, 1) void k_prefill(
             }
             for (; i < m0; i += 4) {
                 if (i + 4 < m0) {
-                    const TIO *sp = rd_base + S.order[i + 4] * slot_stride;
+                    const RT *sp = rd_base + S.order[i + 4] * slot_stride;
 #pragma unroll
                     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
@@ -789,22 +839,34 @@ __global__ __launch_bounds__(256, 1) void k_prefill(
             }
         }
         __syncthreads();
-        if constexpr (sizeof(TIO) == 2) {
+        if constexpr (kHalfRead) {
+            // fp16 operand copies of the changed states, normalised per state
             for (int c = 0; c < S.n_changed; ++c) {
                 const int slot = S.changed[c];
-                const float *src = st_base + slot * slot_stride;
-                TIO *dst = shadow + static_cast<size_t>(bh) * C * DV * DK + slot * slot_stride +
-                           static_cast<size_t>(dv0) * DK;
-                for (int idx = tid; idx < DVT * DK / 8; idx += 256) {
-                    const float4 a = reinterpret_cast<const float4 *>(src)[2 * idx];
-                    const float4 b = reinterpret_cast<const float4 *>(src)[2 * idx + 1];
-                    bf16x8 o;
-                    o[0] = static_cast<__bf16>(a.x); o[1] = static_cast<__bf16>(a.y);
-                    o[2] = static_cast<__bf16>(a.z); o[3] = static_cast<__bf16>(a.w);
-                    o[4] = static_cast<__bf16>(b.x); o[5] = static_cast<__bf16>(b.y);
-                    o[6] = static_cast<__bf16>(b.z); o[7] = static_cast<__bf16>(b.w);
-                    reinterpret_cast<bf16x8 *>(dst)[idx] = o;
+                const float4 *src = reinterpret_cast<const float4 *>(st_base + slot * slot_stride);
+                float mx = 0.0f;
+                for (int idx = tid; idx < DVT * DK / 4; idx += 256) {
+                    const float4 a = src[idx];
+                    mx = fmaxf(mx, fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))));
                 }
+                mx = wave_max(mx);
+                __syncthreads();
+                if (lane == 0) S.red[wave] = mx;
+                __syncthreads();
+                const int e = f16_exponent(fmaxf(fmaxf(S.red[0], S.red[1]), fmaxf(S.red[2], S.red[3])));
+                RT *dst = shadow + static_cast<size_t>(bh) * C * DV * DK + slot * slot_stride +
+                          static_cast<size_t>(dv0) * DK;
+                for (int idx = tid; idx < DVT * DK / 8; idx += 256) {
+                    const float4 a = src[2 * idx];
+                    const float4 b = src[2 * idx + 1];
+                    f16x8 o;
+                    o[0] = static_cast<_Float16>(ldexpf(a.x, -e)); o[1] = static_cast<_Float16>(ldexpf(a.y, -e));
+                    o[2] = static_cast<_Float16>(ldexpf(a.z, -e)); o[3] = static_cast<_Float16>(ldexpf(a.w, -e));
+                    o[4] = static_cast<_Float16>(ldexpf(b.x, -e)); o[5] = static_cast<_Float16>(ldexpf(b.y, -e));
+                    o[6] = static_cast<_Float16>(ldexpf(b.z, -e)); o[7] = static_cast<_Float16>(ldexpf(b.w, -e));
+                    reinterpret_cast<f16x8 *>(dst)[idx] = o;
+                }
+                if (tid == 0) S.shexp[slot] = e;
             }
         }
         __syncthreads();
@@ -1055,13 +1117,19 @@ static hipError_t prefill_main(const PrefillArgs &a, hipStream_t stream)
         if (e != hipSuccess) return e;
         attr_set = true;
     }
+    if (a.ev_before) {
+        hipError_t e = hipEventRecord(a.ev_before, stream);
+        if (e != hipSuccess) return e;
+    }
     hipLaunchKernelGGL((k_prefill<TIO, DK, DVT>), dim3(BH * nblk_dv), dim3(256), smem, stream,
                        static_cast<const TIO *>(a.q), static_cast<const TIO *>(a.k),
                        static_cast<const TIO *>(a.v), static_cast<const TIO *>(a.lam),
                        static_cast<TIO *>(a.o), a.T, a.g.C, a.g.dv, nblk_dv, a.states,
-                       static_cast<TIO *>(a.ws.shadow), a.ws.events, a.ws.chunk_ev, a.meta,
+                       static_cast<typename ReadT<TIO>::type *>(a.ws.shadow), a.ws.events, a.ws.chunk_ev, a.meta,
                        a.g.meta_stride, a.sched.m_t);
-    return hipGetLastError();
+    hipError_t e = hipGetLastError();
+    if (e == hipSuccess && a.ev_after) e = hipEventRecord(a.ev_after, stream);
+    return e;
 }
 
 template <typename TIO>

@@ -123,6 +123,7 @@ typedef struct dla_cache_preload {
  *   m_t [B*H][T]      live states after the token
  *   ev_t, ev_i [B*H][T], n_ev [B*H]: the capacity merges in order: token and
  *                     chronological index of the earlier state of the pair
+ *                     (ev_t and ev_i are given together or not at all)
  * Decode step: s, boundary, m_t and ev_i are [B*H] (ev_i = -1 without a
  * merge); seg_id, ev_t and n_ev are ignored.
  */
@@ -187,6 +188,15 @@ dla_status dla_prefill(const void *q, const void *k, const void *v, const void *
 dla_status dla_decode_step(const void *q, const void *k, const void *v, const void *lam,
                            void *o, float tau, dla_dtype io, const dla_cache *cache,
                            const dla_schedule_out *sched, void *stream);
+
+/*
+ * Benchmark hook.  While set, every dla_prefill call made on this thread
+ * records the event `before` right before its chunk kernel (the MFMA
+ * prefill sweep, after the schedule kernels) and `after` right after it, on
+ * the call's stream.  Both are hipEvent_t handles owned by the caller; pass
+ * NULL, NULL to stop.  DLA_ERR_ARG if exactly one is NULL.
+ */
+dla_status dla_set_prefill_events(void *before, void *after);
 
 /* Static text for a status code. */
 const char *dla_status_str(dla_status s);

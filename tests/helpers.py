@@ -55,3 +55,15 @@ def mat_rel_err(got, ref) -> float:
     den = np.abs(r).max(1)
     den = np.where(den == 0, 1.0, den)
     return float((num / den).max()) if len(num) else 0.0
+
+
+def assert_close_to_sum(got, ref, ref_abs, rtol=1e-12):
+    """|got - ref| <= rtol * max over the row of ref_abs, where ref_abs is the
+    same sum taken over absolute values (a bound on the rounding error of any
+    summation order, whatever the cancellation)."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    scale = np.asarray(ref_abs, np.float64).reshape(-1, got.shape[-1]).max(1)
+    err = np.abs(got - ref).reshape(-1, got.shape[-1]).max(1)
+    bad = err > rtol * np.maximum(scale, 1e-300)
+    assert not bad.any(), f"rows {np.flatnonzero(bad)[:5]}: err {err[bad][:5]} scale {scale[bad][:5]}"

@@ -9,7 +9,7 @@ from hypothesis import given, settings, strategies as st
 from scipy.spatial.distance import cosine as scipy_cosine
 
 import oracle
-from tests.helpers import keys_for_scores, mat_rel_err, row_rel_err
+from tests.helpers import assert_close_to_sum, keys_for_scores, mat_rel_err, row_rel_err
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "schedule_cases.json")
 
@@ -125,7 +125,8 @@ def test_oracle_equals_brute_force_and_greedy(T, dk, dv, C, tau, seg, seed):
     oracle.check_schedule(r["s"][0], tau, C, r["b"][0], r["events"][0], r["m_t"][0])
     sets = oracle.start_sets(T, r["b"][0], r["events"][0])
     bf = oracle.brute_force(q[0], k[0], v[0], lam[0], sets)
-    assert row_rel_err(r["o"][0], bf) < 1e-12
+    bf_abs = oracle.brute_force(np.abs(q[0]), np.abs(k[0]), np.abs(v[0]), np.abs(lam[0]), sets)
+    assert_close_to_sum(r["o"][0], bf, bf_abs, 1e-12)
     # invariants of the final cache
     m = int(r["fin_m"][0])
     starts = r["fin_start"][0, :m]

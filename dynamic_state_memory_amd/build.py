@@ -7,7 +7,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = [os.path.join(PKG, "csrc", "dla_kernels.hip"), os.path.join(PKG, "csrc", "dla_abi.cpp")]
+SRC = [os.path.join(PKG, "csrc", f) for f in ("dla_kernels.hip", "dla_prefill_rs.hip", "dla_abi.cpp")]
 OUT = os.path.join(PKG, "_build", "libdla.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = os.environ.get("DLA_OFFLOAD_ARCH", "gfx950")

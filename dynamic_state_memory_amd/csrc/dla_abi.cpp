@@ -50,6 +50,7 @@ dla_status check_shape(int32_t B, int32_t H, int32_t C, int32_t dk, int32_t dv)
 
 struct Sizes {
     uint64_t s, qs, flag, tile_cnt, tile_sum, seg_t, seg_P, seg_q0, nseg, events, chunk_ev, shadow;
+    uint64_t q16f, qexp, lamT, pwf, ktf;
     uint64_t total;
 };
 
@@ -70,8 +71,13 @@ Sizes workspace_sizes(int64_t BH, int64_t T, int64_t C, int64_t dk, int64_t dv)
     z.events = align_up(8ull * BH * T, 256);
     z.chunk_ev = align_up(4ull * BH * (NCH + 1), 256);
     z.shadow = align_up(2ull * BH * C * dv * dk, 256);
+    z.q16f = align_up(2ull * BH * NCH * kChunk * dk, 256);
+    z.qexp = align_up(4ull * BH * NCH, 256);
+    z.lamT = align_up(4ull * BH * NCH * kPrepCmax * kChunk, 256);
+    z.pwf = align_up(2ull * BH * NCH * kChunk * kChunk, 256);
+    z.ktf = align_up(2ull * BH * NCH * kChunk * dk, 256);
     z.total = z.s + z.qs + z.flag + z.tile_cnt + z.tile_sum + z.seg_t + z.seg_P + z.seg_q0 + z.nseg +
-              z.events + z.chunk_ev + z.shadow;
+              z.events + z.chunk_ev + z.shadow + z.q16f + z.qexp + z.lamT + z.pwf + z.ktf;
     return z;
 }
 
@@ -90,7 +96,12 @@ Workspace carve(void *base, const Sizes &z)
     w.nseg = reinterpret_cast<int32_t *>(p); p += z.nseg;
     w.events = reinterpret_cast<int2 *>(p); p += z.events;
     w.chunk_ev = reinterpret_cast<int32_t *>(p); p += z.chunk_ev;
-    w.shadow = p;
+    w.shadow = p; p += z.shadow;
+    w.q16f = p; p += z.q16f;
+    w.qexp = reinterpret_cast<int32_t *>(p); p += z.qexp;
+    w.lamT = reinterpret_cast<float *>(p); p += z.lamT;
+    w.pwf = p; p += z.pwf;
+    w.ktf = p;
     return w;
 }
 
@@ -250,7 +261,14 @@ dla_status dla_prefill(const void *q, const void *k, const void *v, const void *
     a.tau = tau;
     a.io_bf16 = io == DLA_BF16;
     a.dvt = choose_dvt(BH, cache->d_v);
-    if (prefill_smem_bytes(a.io_bf16, cache->d_k, a.dvt) > 160 * 1024)
+    // bf16 inputs with C <= 32 keep the state stack in registers; the
+    // streamed kernel covers the rest (DLA_PREFILL_PATH=streamed forces it)
+    const char *path = std::getenv("DLA_PREFILL_PATH");
+    a.register_resident = a.io_bf16 && cache->C <= 32 && !(path && std::strcmp(path, "streamed") == 0);
+    if (a.register_resident) a.dvt = prefill_rs_dvt(cache->d_k, cache->C, a.dvt);
+    const size_t lds = a.register_resident ? prefill_rs_smem_bytes(cache->d_k, a.dvt, cache->C)
+                                           : prefill_smem_bytes(a.io_bf16, cache->d_k, a.dvt);
+    if (lds > 160 * 1024)
         return fail(DLA_ERR_UNSUPPORTED, "shape needs more LDS than a compute unit has");
     a.g = geom(cache);
     uint8_t *b8 = static_cast<uint8_t *>(cache->base);

@@ -1,0 +1,153 @@
+// dla_device.h -- device helpers shared by the libdla kernels: MFMA operand
+// fragments, wave reductions, fixed-point and fp16 scaling helpers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dla {
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ float to_f(float x) { return x; }
+__device__ __forceinline__ float to_f(__bf16 x) { return static_cast<float>(x); }
+template <typename T> __device__ __forceinline__ T from_f(float x);
+template <> __device__ __forceinline__ float from_f<float>(float x) { return x; }
+template <> __device__ __forceinline__ __bf16 from_f<__bf16>(float x) { return static_cast<__bf16>(x); }
+
+// k >> s for s in [0, 64]; a shift by 64 gives 0.
+__device__ __forceinline__ uint64_t shr64(uint64_t x, int s) { return s >= 64 ? 0ull : (x >> s); }
+__device__ __forceinline__ uint64_t low_bits(int n) { return n >= 64 ? ~0ull : ((1ull << n) - 1ull); }
+
+// The 2^-32 fixed-point value of a float information score (round half even).
+__device__ __forceinline__ int64_t fixed_point(float s) {
+    return __double2ll_rn(static_cast<double>(s) * 4294967296.0);
+}
+
+// 1 - cos from double-precision dot and squared norms, rounded once to float.
+__device__ __forceinline__ float cosine_distance(double d, double a, double b) {
+    const double ab = a * b;
+    if (ab == 0.0) return 1.0f;
+    return static_cast<float>(1.0 - d / sqrt(ab));
+}
+
+// Eight consecutive elements, the per-lane operand of one 16x16x32 MFMA step.
+template <typename T> struct Frag;
+template <> struct Frag<__bf16> { bf16x8 v; };
+template <> struct Frag<_Float16> { f16x8 v; };
+template <> struct Frag<float> { float v[8]; };
+
+// Operand type of the inter-chunk read: bf16 inputs are read against an fp16
+// copy of the states (11-bit significands, normalised per state by a power of
+// two), fp32 inputs against the fp32 states themselves.
+template <typename TIO> struct ReadT;
+template <> struct ReadT<__bf16> { typedef _Float16 type; };
+template <> struct ReadT<float> { typedef float type; };
+
+__device__ __forceinline__ void load_frag(Frag<__bf16> &f, const __bf16 *p) {
+    f.v = *reinterpret_cast<const bf16x8 *>(p);
+}
+__device__ __forceinline__ void load_frag(Frag<_Float16> &f, const _Float16 *p) {
+    f.v = *reinterpret_cast<const f16x8 *>(p);
+}
+__device__ __forceinline__ void load_frag(Frag<float> &f, const float *p) {
+    const float4 a = reinterpret_cast<const float4 *>(p)[0];
+    const float4 b = reinterpret_cast<const float4 *>(p)[1];
+    f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
+    f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
+}
+__device__ __forceinline__ void zero_frag(Frag<__bf16> &f) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f.v[e] = static_cast<__bf16>(0.0f);
+}
+__device__ __forceinline__ void zero_frag(Frag<_Float16> &f) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f.v[e] = static_cast<_Float16>(0.0f);
+}
+__device__ __forceinline__ void zero_frag(Frag<float> &f) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f.v[e] = 0.0f;
+}
+// Zero the elements whose index (base + e) lies outside [lo, hi).
+__device__ __forceinline__ void mask_frag(Frag<__bf16> &f, int base, int lo, int hi) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        if (base + e < lo || base + e >= hi) f.v[e] = static_cast<__bf16>(0.0f);
+}
+__device__ __forceinline__ void mask_frag(Frag<float> &f, int base, int lo, int hi) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        if (base + e < lo || base + e >= hi) f.v[e] = 0.0f;
+}
+
+// acc(16x16) += A(16x32) * B(32x16).  Lane l holds A row (l % 16) and B
+// column (l % 16) at reduction indices 8*(l/16) + e, e = 0..7; A and B use the
+// same index map, so the product sums every reduction index exactly once.
+// The accumulator holds D[4*(l/16) + r][l % 16], r = 0..3.
+__device__ __forceinline__ void mma32(floatx4 &acc, const Frag<__bf16> &a, const Frag<__bf16> &b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma32(floatx4 &acc, const Frag<_Float16> &a, const Frag<_Float16> &b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a.v, b.v, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma32(floatx4 &acc, const Frag<float> &a, const Frag<float> &b) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[e], b.v[e], acc, 0, 0, 0);
+}
+
+// Workgroup barrier that orders LDS only: waits for this wave's LDS traffic,
+// not for its global loads and stores, so prefetches stay in flight across it.
+// Use __syncthreads() where waves exchange data through global memory.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <typename T> __device__ __forceinline__ T wave_sum(T x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+    return x;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+    return x;
+}
+
+// Exponent e with max * 2^-e in [2^14, 2^15): the largest magnitude then uses
+// the top of fp16's range; 0 for an all-zero block.
+__device__ __forceinline__ int f16_exponent(float maxabs) {
+    return maxabs > 0.0f ? ilogbf(maxabs) - 14 : 0;
+}
+
+// The query chunk's A fragment of the inter-chunk read: fp16, scaled by 2^-e.
+__device__ __forceinline__ void read_frag_from(Frag<_Float16> &f, const __bf16 *p, int e) {
+    const bf16x8 x = *reinterpret_cast<const bf16x8 *>(p);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f.v[j] = static_cast<_Float16>(ldexpf(static_cast<float>(x[j]), -e));
+}
+__device__ __forceinline__ void read_frag_from(Frag<float> &f, const float *p, int) { load_frag(f, p); }
+
+__device__ __forceinline__ int64_t wave_min_i64(int64_t x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        const int64_t y = __shfl_xor(x, off);
+        x = y < x ? y : x;
+    }
+    return x;
+}
+
+// Inclusive scan over a 64-lane wave.
+template <typename T> __device__ __forceinline__ T wave_incl_scan(T x, int lane) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const T y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+    }
+    return x;
+}
+
+}  // namespace dla

@@ -64,8 +64,15 @@ struct Workspace {
     int32_t *nseg;       // [BH]
     int2 *events;        // [BH][T] (token, state merged away or -1)
     int32_t *chunk_ev;   // [BH][NCH+1] first event of each chunk
-    void *shadow;        // [BH][C][dv][dk] bf16 copy of the states (bf16 io)
+    void *shadow;        // [BH][C][dv][dk] fp16 copy of the states (bf16 io)
+    // per-chunk operands built by the chunk pre-pass (register-resident path)
+    void *q16f;          // [BH][NCH][4][DK/32][64][8] fp16 query fragments
+    int32_t *qexp;       // [BH][NCH] power-of-two exponent of each chunk's fp16 query
+    float *lamT;         // [BH][NCH][CMAX][64] lam of the chunk, slot-major
+    void *pwf;           // [BH][NCH][4][2][64][8] bf16 fragments of (Q K^T) o W
+    void *ktf;           // [BH][NCH][DK/16][2][64][8] bf16 fragments of K^T
 };
+constexpr int kPrepCmax = 32;   // lam slots kept per chunk by the pre-pass
 
 struct PrefillArgs {
     const void *q, *k, *v, *lam;
@@ -80,6 +87,7 @@ struct PrefillArgs {
     Workspace ws;
     dla_schedule_out sched;
     hipEvent_t ev_before, ev_after;   // optional, recorded around the chunk kernel
+    int register_resident;            // 1: k_prefill_rs, 0: k_prefill (states streamed)
 };
 
 struct DecodeSched {
@@ -105,5 +113,8 @@ hipError_t launch_cache_init(float *states, uint8_t *meta, const CacheGeom &g, c
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 size_t prefill_smem_bytes(int io_bf16, int dk, int dvt);
+hipError_t launch_prefill_rs(const PrefillArgs &a, hipStream_t stream);
+size_t prefill_rs_smem_bytes(int dk, int dvt, int C);
+int prefill_rs_dvt(int dk, int C, int dvt_wanted);
 
 }  // namespace dla

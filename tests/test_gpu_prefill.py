@@ -66,8 +66,19 @@ REDUCED = [
 ]
 
 
+@pytest.fixture(params=["register", "streamed"])
+def prefill_path(request, monkeypatch):
+    """Both prefill kernels: states held in registers (the default for bf16
+    inputs and C <= 32) and states streamed from the cache."""
+    if request.param == "streamed":
+        monkeypatch.setenv("DLA_PREFILL_PATH", "streamed")
+    else:
+        monkeypatch.delenv("DLA_PREFILL_PATH", raising=False)
+    return request.param
+
+
 @pytest.mark.parametrize("name,streams,T,means", REDUCED)
-def test_reduced_bf16_workloads(name, streams, T, means):
+def test_reduced_bf16_workloads(name, streams, T, means, prefill_path):
     torch_mod()
     cfg = workloads.CONFIGS[name]
     if means is not None:
@@ -78,7 +89,7 @@ def test_reduced_bf16_workloads(name, streams, T, means):
         assert r["n_ev"].min() > 0
 
 
-def test_literal_noise_reading_every_token_opens():
+def test_literal_noise_reading_every_token_opens(prefill_path):
     torch_mod()
     cfg = workloads.CONFIGS["gdn_1p3b_t32k_bf16"]
     d = workloads.prefill_inputs(cfg, reading="literal", streams=[0, 1], T=777)
@@ -86,7 +97,8 @@ def test_literal_noise_reading_every_token_opens():
     assert r["b"].mean() > 0.99 and r["n_ev"].min() >= 777 - cfg.C - 5
 
 
-@pytest.mark.parametrize("tau,C", [(-1.0, 64), (-1.0, 5), (3.0, 8), (0.3, 1), (0.9, 63)])
+@pytest.mark.parametrize("tau,C", [(-1.0, 64), (-1.0, 5), (3.0, 8), (0.3, 1), (0.9, 63), (-1.0, 32),
+                                   (0.3, 17)])
 def test_threshold_and_capacity_extremes(tau, C):
     torch_mod()
     cfg = dataclasses.replace(workloads.CONFIGS["long_t131k_bf16"], C=C, seg_means=(10,))

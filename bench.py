@@ -17,10 +17,18 @@ Also reported on the same line:
                 kernel's algorithmic HBM bytes per launch over its duration,
                 against the HBM peak;
   cpu_baseline  the CPU oracle on a bounded sample of the prefill workload.
+
+roofline.traffic is the kernel's HBM bytes per launch from the hardware
+counters FETCH_SIZE and WRITE_SIZE (two rocprofv3 --pmc passes over this
+script with --copy-probe-mib, each scaled by what the counter reads for a plain
+device copy of known size), read from the counter summary committed under
+profiles/.  It is null when that summary is missing or was taken on kernel
+sources other than the ones built now (sha256 over the files it names).
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -38,6 +46,45 @@ PEAK_HBM_GBS = 8000.0
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def measured_traffic(summary: str, kernel: str):
+    """HBM bytes per launch of `kernel` from a committed counter summary
+    (key: value lines), or None when it is absent, names another kernel, or
+    its kernel sources no longer hash to what it recorded."""
+    path = os.path.join(ROOT, "profiles", summary)
+    try:
+        kv = {}
+        for line in open(path):
+            if ":" in line and not line.startswith("#"):
+                key, val = line.split(":", 1)
+                kv[key.strip()] = val.strip()
+        if kv.get("kernel") != kernel:
+            return None
+        h = hashlib.sha256()
+        for f in kv["sources"].split():
+            h.update(open(os.path.join(ROOT, f), "rb").read())
+        if h.hexdigest() != kv["sources_sha256"]:
+            return None
+        return float(kv["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def copy_probe(torch, mib):
+    """A plain device-to-device copy of mib MiB, three times: the counter
+    passes scale FETCH_SIZE and WRITE_SIZE by what they read for it."""
+    if mib <= 0:
+        return
+    n = mib * (1 << 20)
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copy probe: 3 x {n} bytes")
+    del src, dst
+    torch.cuda.empty_cache()
 
 
 def prefill_bench(args, torch, dla, workloads):
@@ -94,14 +141,16 @@ def prefill_bench(args, torch, dla, workloads):
     ms_per_step = wall * 1e3 / args.steps
     tokens = B * T
     achieved = flops / (kern_avg * 1e-3) / 1e12
+    kernel = dla.dla_prefill_kernel(dla.DLA_BF16 if cfg.io == "bf16" else dla.DLA_F32, B, H, C, dk, dv)
+    traffic = measured_traffic(f"{_kernel_file(kernel)}_{args.workload}_hbm_traffic.txt", kernel)
     res = dict(
         value=tokens / (ms_per_step * 1e-3), ms_per_step=ms_per_step,
         config=dict(workload=f"{args.workload} prefill", B=B, H=H, T=T, d_k=dk, d_v=dv, C=C,
                     tau=cfg.tau, io=cfg.io, keys=f"piecewise-regime, {args.reading} noise",
                     segment_means=list(cfg.seg_means)),
         roofline=dict(bound="mfma", achieved=achieved, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                      frac=achieved / PEAK_BF16_TFLOPS, traffic=None,
-                      kernel="k_prefill", kernel_ms=kern_avg, algorithmic_flop_per_launch=flops),
+                      frac=achieved / PEAK_BF16_TFLOPS, traffic=traffic,
+                      kernel=kernel, kernel_ms=kern_avg, algorithmic_flop_per_launch=flops),
         schedule=stats,
         token_heads_per_s=BH * T / (ms_per_step * 1e-3),
     )
@@ -212,13 +261,21 @@ def decode_bench(args, torch, dla, workloads):
         boundaries_per_stream=float(b_.sum().item()) / BH,
         merges_per_stream=float((e_ >= 0).sum().item()) / BH,
         roofline=dict(bound="hbm", achieved=achieved, peak=PEAK_HBM_GBS, unit="GB/s",
-                      frac=achieved / PEAK_HBM_GBS, traffic=None, kernel="k_decode",
+                      frac=achieved / PEAK_HBM_GBS,
+                      traffic=measured_traffic(f"k_decode_{args.decode_workload}_hbm_traffic.txt",
+                                               "k_decode"),
+                      kernel="k_decode",
                       kernel_ms=kern_avg, algorithmic_bytes_per_launch=bytes_per_step),
         inputs="drawn on the device with torch's seeded generator, same recipe",
     )
     log(f"decode: {res['steps_per_s']:.1f} steps/s, kernel {kern_avg:.3f} ms, "
         f"{achieved:.0f} GB/s algorithmic ({100 * achieved / PEAK_HBM_GBS:.1f}% of HBM peak)")
     return res
+
+
+def _kernel_file(kernel: str) -> str:
+    """k_prefill_rs<128,16,8> -> k_prefill_rs_128_16_8 (a file-name form)."""
+    return kernel.replace("<", "_").replace(">", "").replace(",", "_")
 
 
 def cpu_baseline(args, sample, cfg):
@@ -271,6 +328,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--cpu-streams", type=int, default=16)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after the prefill, copy this many MiB three times (counter calibration)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -288,6 +347,7 @@ def main():
         sys.exit(1)
     dla.load()
     pre, sample, cfg = prefill_bench(args, torch, dla, workloads)
+    copy_probe(torch, args.copy_probe_mib)
     dec = None if args.no_decode else decode_bench(args, torch, dla, workloads)
     cpu = None if args.no_cpu else cpu_baseline(args, sample, cfg)
     out = {

@@ -105,6 +105,8 @@ def load():
                                     C.POINTER(dla_schedule_out), vp]
     lib.dla_set_prefill_events.restype = C.c_int
     lib.dla_set_prefill_events.argtypes = [vp, vp]
+    lib.dla_prefill_kernel.restype = C.c_char_p
+    lib.dla_prefill_kernel.argtypes = [C.c_int] + [i32] * 5
     lib.dla_status_str.restype = C.c_char_p
     lib.dla_status_str.argtypes = [C.c_int]
     lib.dla_last_error.restype = C.c_char_p
@@ -154,6 +156,11 @@ def dla_decode_step(q, k, v, lam, o, tau, io, cache: dla_cache,
 
 def dla_set_prefill_events(before, after) -> int:
     return load().dla_set_prefill_events(before, after)
+
+
+def dla_prefill_kernel(io, B, H, C_, d_k, d_v) -> str | None:
+    r = load().dla_prefill_kernel(io, B, H, C_, d_k, d_v)
+    return r.decode() if r is not None else None
 
 
 def dla_status_str(s: int) -> str:

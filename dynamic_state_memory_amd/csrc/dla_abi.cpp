@@ -144,6 +144,37 @@ int choose_dvt(int64_t BH, int dv)
     return BH * (dv / 32) >= 200 ? 32 : 16;
 }
 
+// Which chunk kernel a prefill of this shape runs, with its value-column
+// slice width and LDS need.  bf16 inputs with C <= 32 keep the state stack in
+// registers; the streamed kernel covers the rest (DLA_PREFILL_PATH=streamed
+// forces it).
+struct PrefillPlan {
+    int register_resident;
+    int dvt;
+    size_t lds;
+    char name[48];
+};
+
+PrefillPlan plan_prefill(bool io_bf16, int64_t BH, int C, int dk, int dv)
+{
+    PrefillPlan p;
+    p.dvt = choose_dvt(BH, dv);
+    const char *path = std::getenv("DLA_PREFILL_PATH");
+    p.register_resident = io_bf16 && C <= 32 && !(path && std::strcmp(path, "streamed") == 0);
+    if (p.register_resident) {
+        p.dvt = prefill_rs_dvt(dk, C, p.dvt);
+        p.lds = prefill_rs_smem_bytes(dk, p.dvt, C);
+        const int spw = C <= 8 ? 2 : C <= 16 ? 4 : 8;
+        std::snprintf(p.name, sizeof(p.name), "k_prefill_rs<%d,%d,%d>", dk, p.dvt, spw);
+    } else {
+        p.lds = prefill_smem_bytes(io_bf16, dk, p.dvt);
+        std::snprintf(p.name, sizeof(p.name), "k_prefill<%s,%d,%d>", io_bf16 ? "bf16" : "f32", dk, p.dvt);
+    }
+    return p;
+}
+
+thread_local char g_kernel_name[48];
+
 }  // namespace
 
 extern "C" {
@@ -260,15 +291,10 @@ dla_status dla_prefill(const void *q, const void *k, const void *v, const void *
     a.T = T;
     a.tau = tau;
     a.io_bf16 = io == DLA_BF16;
-    a.dvt = choose_dvt(BH, cache->d_v);
-    // bf16 inputs with C <= 32 keep the state stack in registers; the
-    // streamed kernel covers the rest (DLA_PREFILL_PATH=streamed forces it)
-    const char *path = std::getenv("DLA_PREFILL_PATH");
-    a.register_resident = a.io_bf16 && cache->C <= 32 && !(path && std::strcmp(path, "streamed") == 0);
-    if (a.register_resident) a.dvt = prefill_rs_dvt(cache->d_k, cache->C, a.dvt);
-    const size_t lds = a.register_resident ? prefill_rs_smem_bytes(cache->d_k, a.dvt, cache->C)
-                                           : prefill_smem_bytes(a.io_bf16, cache->d_k, a.dvt);
-    if (lds > 160 * 1024)
+    const PrefillPlan plan = plan_prefill(a.io_bf16, BH, cache->C, cache->d_k, cache->d_v);
+    a.dvt = plan.dvt;
+    a.register_resident = plan.register_resident;
+    if (plan.lds > 160 * 1024)
         return fail(DLA_ERR_UNSUPPORTED, "shape needs more LDS than a compute unit has");
     a.g = geom(cache);
     uint8_t *b8 = static_cast<uint8_t *>(cache->base);
@@ -293,6 +319,18 @@ dla_status dla_prefill(const void *q, const void *k, const void *v, const void *
         if (e != hipSuccess) return hip_status(e, "schedule copy");
     }
     return ok();
+}
+
+const char *dla_prefill_kernel(dla_dtype io, int32_t B, int32_t H, int32_t C, int32_t d_k, int32_t d_v)
+{
+    char saved[sizeof(g_err)];
+    std::memcpy(saved, g_err, sizeof(g_err));
+    const bool bad = check_shape(B, H, C, d_k, d_v) != DLA_OK || (io != DLA_F32 && io != DLA_BF16);
+    std::memcpy(g_err, saved, sizeof(g_err));
+    if (bad) return nullptr;
+    const PrefillPlan p = plan_prefill(io == DLA_BF16, static_cast<int64_t>(B) * H, C, d_k, d_v);
+    std::memcpy(g_kernel_name, p.name, sizeof(g_kernel_name));
+    return g_kernel_name;
 }
 
 dla_status dla_decode_step(const void *q, const void *k, const void *v, const void *lam, void *o, float tau,

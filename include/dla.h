@@ -181,6 +181,16 @@ dla_status dla_prefill(const void *q, const void *k, const void *v, const void *
                        const dla_schedule_out *sched, void *stream);
 
 /*
+ * Name of the chunk kernel (the MFMA sweep after the schedule kernels) that
+ * dla_prefill launches for this shape and io dtype under the current
+ * environment, e.g. "k_prefill_rs<128,16,8>" (template arguments d_k, value
+ * columns per block, state slots per wave).  For profilers and benchmarks.
+ * The string is thread-local and valid until the next call on this thread;
+ * NULL for a shape dla_prefill would reject.
+ */
+const char *dla_prefill_kernel(dla_dtype io, int32_t B, int32_t H, int32_t C, int32_t d_k, int32_t d_v);
+
+/*
  * Decode step: consume one token of every stream on top of the cache and
  * write o.  q, k [B*H][d_k]; v, o [B*H][d_v]; lam [B*H][C]; io dtype, device.
  * Supported: d_k = d_v = 128 or d_k = d_v = 64, any io dtype.

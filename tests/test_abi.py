@@ -42,6 +42,18 @@ def test_sizes_and_layout():
     assert dla.dla_status_str(3) == "workspace missing or too small"
 
 
+def test_prefill_kernel_choice(monkeypatch):
+    monkeypatch.delenv("DLA_PREFILL_PATH", raising=False)
+    monkeypatch.delenv("DLA_PREFILL_DVT", raising=False)
+    assert dla.dla_prefill_kernel(dla.DLA_BF16, 2, 16, 32, 128, 256) == "k_prefill_rs<128,16,8>"
+    assert dla.dla_prefill_kernel(dla.DLA_BF16, 4, 24, 16, 128, 64) == "k_prefill_rs<128,16,4>"
+    assert dla.dla_prefill_kernel(dla.DLA_F32, 1, 1, 8, 64, 64) == "k_prefill<f32,64,16>"
+    assert dla.dla_prefill_kernel(dla.DLA_BF16, 1, 1, 48, 64, 64) == "k_prefill<bf16,64,16>"
+    assert dla.dla_prefill_kernel(dla.DLA_BF16, 1, 1, 8, 96, 64) is None
+    monkeypatch.setenv("DLA_PREFILL_PATH", "streamed")
+    assert dla.dla_prefill_kernel(dla.DLA_BF16, 2, 16, 32, 128, 256) == "k_prefill<bf16,128,32>"
+
+
 def _cache(B=1, H=1, C_=8, dk=64, dv=64, base=0x10000):
     c = dla.dla_cache()
     c.B, c.H, c.C, c.d_k, c.d_v = B, H, C_, dk, dv

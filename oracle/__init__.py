@@ -25,17 +25,28 @@ _OUT = os.path.join(_HERE, "_build", "libdla_oracle.so")
 _lib = None
 
 
-def build(force: bool = True) -> str:
-    """Compile the C oracle (gcc, -O2, no floating-point contraction)."""
-    if not force and os.path.exists(_OUT):
-        return _OUT
-    os.makedirs(os.path.dirname(_OUT), exist_ok=True)
-    tmp = _OUT + ".tmp"
+def build(force: bool = True, src: str = _SRC, out: str = _OUT) -> str:
+    """Compile the C oracle (gcc, -O2, no floating-point contraction).
+
+    ``src``/``out`` let a test compile a modified copy of the source (the
+    planted-mistake tests); the default builds the oracle itself."""
+    if not force and os.path.exists(out):
+        return out
+    os.makedirs(os.path.dirname(out), exist_ok=True)
+    tmp = out + ".tmp"
     cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
-           "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"]
+           "-fPIC", "-shared", "-o", tmp, src, "-lm"]
     subprocess.run(cmd, check=True)
-    os.replace(tmp, _OUT)
-    return _OUT
+    os.replace(tmp, out)
+    return out
+
+
+def load_library(path: str):
+    """A ctypes handle on a compiled oracle library (for ``run(..., lib=)``)."""
+    lib = C.CDLL(path)
+    lib.dlao_run.argtypes = [C.POINTER(_Args)]
+    lib.dlao_run.restype = C.c_int
+    return lib
 
 
 def _load():
@@ -43,10 +54,7 @@ def _load():
     if _lib is None:
         if not os.path.exists(_OUT) or os.path.getmtime(_OUT) < os.path.getmtime(_SRC):
             build()
-        lib = C.CDLL(_OUT)
-        lib.dlao_run.argtypes = [C.POINTER(_Args)]
-        lib.dlao_run.restype = C.c_int
-        _lib = lib
+        _lib = load_library(_OUT)
     return _lib
 
 
@@ -79,13 +87,14 @@ def _c(a, dt):
 
 def run(q, k, v, lam, C_: int, tau: float, init: dict | None = None,
         want=None, outputs: bool = True, final_states: bool = True,
-        nthreads: int | None = None) -> dict:
+        nthreads: int | None = None, lib=None) -> dict:
     """Run the oracle on float32 inputs q,k [S,T,dk], v [S,T,dv], lam [S,T,C].
 
     ``init``: optional starting cache, dict with m [S], S [S,C,dv,dk] (float64
     or float32), I [S,C] int64, n [S,C] int32, start [S,C] int64, has_prev [S],
     s_prev [S], k_prev [S,dk], t_seen [S].
     ``want``: optional bool mask [S,T] of the outputs to compute (others are 0).
+    ``lib``: a handle from ``load_library`` (default: the oracle itself).
     """
     q, k, v, lam = (_c(a, np.float32) for a in (q, k, v, lam))
     S_, T, dk = k.shape
@@ -139,7 +148,7 @@ def run(q, k, v, lam, C_: int, tau: float, init: dict | None = None,
     out("fin_k_prev", (S_, dk), np.float32, "fin_k_prev")
     out("fin_t_seen", (S_,), np.int64, "fin_t_seen")
     a.nthreads = int(nthreads or os.environ.get("DLA_ORACLE_THREADS", 0) or os.cpu_count() or 1)
-    rc = _load().dlao_run(C.byref(a))
+    rc = (lib or _load()).dlao_run(C.byref(a))
     if rc != 0:
         raise RuntimeError(f"dlao_run failed with code {rc}")
     res["events"] = [list(zip(res["ev_t"][i, :res["n_ev"][i]].tolist(),

@@ -38,37 +38,49 @@ def _regime_keys(T, dk, seg, seed, noise=0.2):
 
 # ---------------------------------------------------------------- token score
 
-def _s_pair(k0, k1):
+# Every pin is a function with an optional ``lib`` (a handle from
+# oracle.load_library); the tests below call them on the oracle itself, and
+# test_oracle_mutants.py calls them on copies with a planted mistake.
+
+def _s_pair(k0, k1, lib=None):
     k = np.stack([k0, k1]).astype(np.float32)[None]
     T, dk = 2, k.shape[2]
     q = np.zeros((1, T, dk), np.float32)
     v = np.zeros((1, T, 1), np.float32)
     lam = np.ones((1, T, 2), np.float32)
-    r = oracle.run(q, k, v, lam, 2, 0.3, outputs=False)
+    r = oracle.run(q, k, v, lam, 2, 0.3, outputs=False, lib=lib)
     return r["s"][0]
 
 
-def test_score_closed_forms():
+def pin_score_closed_forms(lib=None):
     rng = np.random.default_rng(0)
     for dk in (2, 64, 128):
         k0 = rng.standard_normal(dk).astype(np.float32)
         # token 0 has no previous key: s_0 = 1
-        assert _s_pair(k0, k0)[0] == np.float32(1.0)
+        assert _s_pair(k0, k0, lib)[0] == np.float32(1.0)
         # parallel keys (positive multiple): s ~ 0
-        assert abs(_s_pair(k0, (2.5 * k0).astype(np.float32))[1]) <= 1e-6
+        assert abs(_s_pair(k0, (2.5 * k0).astype(np.float32), lib)[1]) <= 1e-6
         # antiparallel: s = 2 exactly
-        assert _s_pair(k0, -k0)[1] == np.float32(2.0)
+        assert _s_pair(k0, -k0, lib)[1] == np.float32(2.0)
         # orthogonal: s = 1 exactly
         e0 = np.zeros(dk, np.float32); e0[0] = 3.0
         e1 = np.zeros(dk, np.float32); e1[1] = -0.5
-        assert _s_pair(e0, e1)[1] == np.float32(1.0)
+        assert _s_pair(e0, e1, lib)[1] == np.float32(1.0)
         # zero key: s = 1
-        assert _s_pair(k0, np.zeros(dk, np.float32))[1] == np.float32(1.0)
+        assert _s_pair(k0, np.zeros(dk, np.float32), lib)[1] == np.float32(1.0)
         # invariant to scaling either key by a power of two (exact)
         k1 = rng.standard_normal(dk).astype(np.float32)
-        s = _s_pair(k0, k1)[1]
-        assert _s_pair((4 * k0).astype(np.float32), k1)[1] == s
-        assert _s_pair(k0, (0.125 * k1).astype(np.float32))[1] == s
+        s = _s_pair(k0, k1, lib)[1]
+        assert _s_pair((4 * k0).astype(np.float32), k1, lib)[1] == s
+        assert _s_pair(k0, (0.125 * k1).astype(np.float32), lib)[1] == s
+        # not symmetric in its failure modes: a generic pair against scipy
+        k2 = (k0 + 0.7 * rng.standard_normal(dk)).astype(np.float32)
+        ref = scipy_cosine(k2.astype(np.float64), k0.astype(np.float64))
+        assert abs(float(_s_pair(k0, k2, lib)[1]) - ref) <= 1e-6
+
+
+def test_score_closed_forms():
+    pin_score_closed_forms()
 
 
 def test_score_matches_library_cosine_distance():
@@ -89,15 +101,14 @@ def _golden():
         return json.load(f)["cases"]
 
 
-@pytest.mark.parametrize("case", _golden(), ids=lambda c: c["name"])
-def test_hand_derived_schedules(case):
+def pin_hand_derived_schedule(case, lib=None):
     s_des = case["s_after_first"]
     T = len(s_des) + 1
     e = case["expect"]
     assert len(e["boundary"]) == T and len(e["m_t"]) == T
     k = keys_for_scores(s_des)[None]
     q, _, v, lam = _rand(T, k.shape[2], 4, case["C"], seed=7)
-    r = oracle.run(q, k, v, lam, case["C"], case["tau"])
+    r = oracle.run(q, k, v, lam, case["C"], case["tau"], lib=lib)
     assert r["s"][0].tolist() == [1.0] + [float(x) for x in s_des]
     assert r["b"][0].tolist() == e["boundary"]
     assert r["m_t"][0].tolist() == e["m_t"]
@@ -112,6 +123,11 @@ def test_hand_derived_schedules(case):
     assert row_rel_err(r["o"][0], bf) < 1e-12
 
 
+@pytest.mark.parametrize("case", _golden(), ids=lambda c: c["name"])
+def test_hand_derived_schedules(case):
+    pin_hand_derived_schedule(case)
+
+
 # ----------------------------------------------------- brute force / checker
 
 @settings(max_examples=60, deadline=None)
@@ -119,9 +135,13 @@ def test_hand_derived_schedules(case):
        C=st.integers(1, 6), tau=st.sampled_from([-1.0, 0.3, 0.9, 3.0]),
        seg=st.sampled_from([2, 8, 1000]), seed=st.integers(0, 2**31 - 1))
 def test_oracle_equals_brute_force_and_greedy(T, dk, dv, C, tau, seg, seed):
+    pin_brute_force_and_greedy(T, dk, dv, C, tau, seg, seed)
+
+
+def pin_brute_force_and_greedy(T, dk, dv, C, tau, seg, seed, lib=None):
     q, _, v, lam = _rand(T, dk, dv, C, seed)
     k = _regime_keys(T, dk, seg, seed + 1)[None]
-    r = oracle.run(q, k, v, lam, C, tau)
+    r = oracle.run(q, k, v, lam, C, tau, lib=lib)
     oracle.check_schedule(r["s"][0], tau, C, r["b"][0], r["events"][0], r["m_t"][0])
     sets = oracle.start_sets(T, r["b"][0], r["events"][0])
     bf = oracle.brute_force(q[0], k[0], v[0], lam[0], sets)
@@ -168,11 +188,15 @@ def test_checker_catches_planted_mistakes():
 
 @pytest.mark.parametrize("tau,C", [(0.3, 3), (-1.0, 2), (3.0, 5), (0.9, 1)])
 def test_lambda_one_gives_causal_linear_attention(tau, C):
+    pin_lambda_one(tau, C)
+
+
+def pin_lambda_one(tau, C, lib=None):
     T, dk, dv = 200, 16, 12
     q, _, v, _ = _rand(T, dk, dv, C, 3)
     k = _regime_keys(T, dk, 20, 4)[None]
     lam = np.ones((1, T, C), np.float32)
-    r = oracle.run(q, k, v, lam, C, tau)
+    r = oracle.run(q, k, v, lam, C, tau, lib=lib)
     Q, K, V = (a[0].astype(np.float64) for a in (q, k, v))
     ref = np.tril(Q @ K.T) @ V          # textbook causal linear attention
     assert row_rel_err(r["o"][0], ref) < 1e-12
@@ -180,10 +204,14 @@ def test_lambda_one_gives_causal_linear_attention(tau, C):
 
 @pytest.mark.parametrize("tau", [0.3, -1.0, 3.0])
 def test_single_state_reduces_to_linear_attention(tau):
+    pin_single_state(tau)
+
+
+def pin_single_state(tau, lib=None):
     T, dk, dv = 150, 8, 8
     q, _, v, lam = _rand(T, dk, dv, 1, 5)
     k = _regime_keys(T, dk, 10, 6)[None]
-    r = oracle.run(q, k, v, lam, 1, tau)
+    r = oracle.run(q, k, v, lam, 1, tau, lib=lib)
     assert np.all(r["m_t"][0] == 1)
     Q, K, V = (a[0].astype(np.float64) for a in (q, k, v))
     ref = lam[0, :, :1].astype(np.float64) * (np.tril(Q @ K.T) @ V)
@@ -191,9 +219,13 @@ def test_single_state_reduces_to_linear_attention(tau):
 
 
 def test_every_token_own_state_is_dense_slot_weighted_product():
+    pin_dense_slot_weighted()
+
+
+def pin_dense_slot_weighted(lib=None):
     T, dk, dv = 40, 8, 5
     q, k, v, lam = _rand(T, dk, dv, T, 8)
-    r = oracle.run(q, k, v, lam, T, -1.0)
+    r = oracle.run(q, k, v, lam, T, -1.0, lib=lib)
     assert np.all(r["b"][0] == 1) and r["n_ev"][0] == 0
     Q, K, V, L = (a[0].astype(np.float64) for a in (q, k, v, lam))
     t = np.arange(T)
@@ -201,16 +233,20 @@ def test_every_token_own_state_is_dense_slot_weighted_product():
     assert row_rel_err(r["o"][0], (W * (Q @ K.T)) @ V) < 1e-12
     # one-hot lambda on slot 0 isolates the token's own state: (q_t . k_t) v_t
     lam1 = np.zeros_like(lam); lam1[..., 0] = 1
-    r1 = oracle.run(q, k, v, lam1, T, -1.0)
+    r1 = oracle.run(q, k, v, lam1, T, -1.0, lib=lib)
     assert row_rel_err(r1["o"][0], np.sum(Q * K, 1)[:, None] * V) < 1e-12
 
 
 def test_states_always_sum_to_the_prefix():
+    pin_prefix_sum()
+
+
+def pin_prefix_sum(lib=None):
     T, dk, dv, C = 400, 16, 8, 4
     q, _, v, lam = _rand(T, dk, dv, C, 9)
     k = _regime_keys(T, dk, 5, 10)[None]
     for Tp in (1, 17, 400):
-        r = oracle.run(q[:, :Tp], k[:, :Tp], v[:, :Tp], lam[:, :Tp], C, 0.3)
+        r = oracle.run(q[:, :Tp], k[:, :Tp], v[:, :Tp], lam[:, :Tp], C, 0.3, lib=lib)
         tot = r["fin_S"][0].sum(0)
         ref = v[0, :Tp].astype(np.float64).T @ k[0, :Tp].astype(np.float64)
         assert mat_rel_err(tot, ref) < 1e-12

@@ -218,16 +218,26 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
 
 // ------------------------------------------------------------ the sweep
 
-template <int DK, int DVT, int CMAX>
-struct RsSmem {
-    _Float16 qf[kChunk / 16][DK / 32][64][8];   // query fragments of the chunk
-    float lamT[CMAX][kChunk];                    // lam of the chunk, slot-major
+// The chunk operands k_chunk_prep wrote, one 64-token chunk, copied verbatim
+// into LDS by the global->LDS loads (each 16-byte piece lands at the same
+// offset it has in the global chunk).
+template <int DK, int CMAX>
+struct RsStage {
+    _Float16 qf[kChunk / 16][DK / 32][64][8];   // query fragments (permuted reduction order)
+    float lamT[CMAX][kChunk];                    // lam, slot-major
     __bf16 pwf[kChunk / 16][2][64][8];           // fragments of (Q K^T) o W
     __bf16 ktf[DK / 16][2][64][8];               // fragments of K^T
-    __bf16 vt[DVT][kChunk + 8];                  // V slice, transposed
-    float W[CMAX][kChunk];      // closed-state read weights, by physical slot
-    float wact[kChunk];         // active-state read weight
-    float ored[4][kChunk][DVT];
+};
+
+// Everything else the sweep keeps in LDS.  The two stages are separate
+// __shared__ variables so that the compiler can tell that the in-flight loads
+// into one stage never touch the other (no wait before reading the current one).
+template <int DK, int DVT, int CMAX>
+struct RsSmem {
+    __bf16 vt[DVT][kChunk + 8];                  // V slice of the chunk, transposed
+    float W[CMAX][kChunk];      // closed-state read weights by physical slot (owner wave's rows)
+    float wact[4][kChunk];      // active-state read weights, one row per wave
+    floatx4 ored[4][kChunk / 16][DVT / 16][64];  // partial reads: wave, row tile, column tile, lane
     uint64_t om[kChunk];
     uint64_t nm[kChunk];
     int32_t order[kMaxC];
@@ -247,137 +257,157 @@ struct RsSmem {
 };
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void glb_void_t;
 
-// One chunk's operands in registers, loaded a chunk ahead of their use.
-template <int DK, int DVT, int CMAX>
-struct ChunkRegs {
-    static constexpr int NQ = kChunk * DK * 2 / 16 / 256;     // 16-byte pieces per thread
-    static constexpr int NL = (CMAX * kChunk * 4 / 16 + 255) / 256;
-    static constexpr int NP = kChunk * kChunk * 2 / 16 / 256;
-    static constexpr int NK = kChunk * DK * 2 / 16 / 256;
-    u32x4 q[NQ], l[NL], p[NP], k[NK];
-    u32x4 v;                    // 64 rows x DVT bf16 (DVT <= 32)
-    int qexp, e0, e1;
-};
-
-template <int DK, int DVT, int CMAX>
-__device__ __forceinline__ void load_chunk(ChunkRegs<DK, DVT, CMAX> &R, const __bf16 *V, const _Float16 *q16f,
-                                           const int32_t *qexp, const float *lamT, const __bf16 *pwf,
-                                           const __bf16 *ktf, const int32_t *chunk_ev, int bh, int NCH,
-                                           int T, int DV, int dv0, int ch, int tid)
+// One 16-byte piece per lane from global memory straight into LDS: lane l's
+// piece lands at lds_wave + 16 l (lds_wave is the same for the whole wave).
+__device__ __forceinline__ void load_to_lds16(const void *g, void *lds_wave)
 {
-    typedef ChunkRegs<DK, DVT, CMAX> R_t;
-    const size_t cb = static_cast<size_t>(bh) * NCH + ch;
+    __builtin_amdgcn_global_load_lds((glb_void_t *)(g), (lds_void_t *)(lds_wave),
+                                     16, 0, 0);
+}
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Issue the loads of chunk ch's operands into stage X (wave w moves pieces
+// 64 w + 256 j of every array).
+template <int DK, int CMAX>
+__device__ __forceinline__ void stage_chunk(RsStage<DK, CMAX> &X, const _Float16 *q16f, const float *lamT,
+                                            const __bf16 *pwf, const __bf16 *ktf, size_t cb, int tid, int wave)
+{
     const u32x4 *qs = reinterpret_cast<const u32x4 *>(q16f) + cb * (kChunk * DK * 2 / 16);
     const u32x4 *ls = reinterpret_cast<const u32x4 *>(lamT) + cb * (kPrepCmax * kChunk * 4 / 16);
     const u32x4 *ps = reinterpret_cast<const u32x4 *>(pwf) + cb * (kChunk * kChunk * 2 / 16);
     const u32x4 *ks = reinterpret_cast<const u32x4 *>(ktf) + cb * (kChunk * DK * 2 / 16);
+    u32x4 *qd = reinterpret_cast<u32x4 *>(&X.qf[0][0][0][0]);
+    u32x4 *ld = reinterpret_cast<u32x4 *>(&X.lamT[0][0]);
+    u32x4 *pd = reinterpret_cast<u32x4 *>(&X.pwf[0][0][0][0]);
+    u32x4 *kd = reinterpret_cast<u32x4 *>(&X.ktf[0][0][0][0]);
 #pragma unroll
-    for (int j = 0; j < R_t::NQ; ++j) R.q[j] = qs[tid + 256 * j];
+    for (int j = 0; j < kChunk * DK * 2 / 16 / 256; ++j) load_to_lds16(qs + tid + 256 * j, qd + 64 * wave + 256 * j);
+    constexpr int NL = CMAX * kChunk * 4 / 16;   // 128, 256 or 512 pieces
 #pragma unroll
-    for (int j = 0; j < R_t::NL; ++j) {
-        const int idx = tid + 256 * j;
-        R.l[j] = idx < CMAX * kChunk / 4 ? ls[idx] : u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int j = 0; j < (NL + 255) / 256; ++j)
+        if (64 * wave + 256 * j < NL) load_to_lds16(ls + tid + 256 * j, ld + 64 * wave + 256 * j);
 #pragma unroll
-    for (int j = 0; j < R_t::NP; ++j) R.p[j] = ps[tid + 256 * j];
+    for (int j = 0; j < kChunk * kChunk * 2 / 16 / 256; ++j) load_to_lds16(ps + tid + 256 * j, pd + 64 * wave + 256 * j);
 #pragma unroll
-    for (int j = 0; j < R_t::NK; ++j) R.k[j] = ks[tid + 256 * j];
-    const int c0 = ch * kChunk;
-    const int nvalid = min(kChunk, T - c0);
-    const int r = tid & (kChunk - 1), cv = (tid / kChunk) * 8;
-    R.v = u32x4{0u, 0u, 0u, 0u};
-    if (tid < kChunk * DVT / 8 && r < nvalid)
-        R.v = *reinterpret_cast<const u32x4 *>(V + (static_cast<size_t>(bh) * T + c0 + r) * DV + dv0 + cv);
-    R.qexp = qexp[cb];
-    R.e0 = chunk_ev[static_cast<size_t>(bh) * (NCH + 1) + ch];
-    R.e1 = chunk_ev[static_cast<size_t>(bh) * (NCH + 1) + ch + 1];
+    for (int j = 0; j < kChunk * DK * 2 / 16 / 256; ++j) load_to_lds16(ks + tid + 256 * j, kd + 64 * wave + 256 * j);
 }
 
+// What one block carries from chunk to chunk (registers after inlining).
 template <int DK, int DVT, int SPW>
-__global__ __launch_bounds__(256, 1) void k_prefill_rs(
-    const __bf16 *__restrict__ V, __bf16 *__restrict__ O, int T, int C, int DV, int nblk_dv,
-    float *__restrict__ states, _Float16 *__restrict__ shadow, const int2 *__restrict__ events,
-    const int32_t *__restrict__ chunk_ev, const _Float16 *__restrict__ q16f, const int32_t *__restrict__ qexp_g,
-    const float *__restrict__ lamT_g, const __bf16 *__restrict__ pwf_g, const __bf16 *__restrict__ ktf_g,
-    uint8_t *__restrict__ meta_base, size_t meta_stride, int32_t *__restrict__ m_t_out)
+struct RsCarry {
+    Frag<_Float16> stk[SPW][DK / 32][DVT / 16];  // closed states of the wave's slots (fp16, normalised)
+    floatx4 am[DVT / 16][2];                     // active state, d_k rows 32w..32w+31 (fp32)
+    Frag<_Float16> af[DVT / 16];                 // its fp16 operand copy
+    floatx4 Oprev[DVT / 16];                     // previous chunk's outputs, stored one chunk late
+    // read-weight source of the wave's slots p = 4r + wave in a chunk without
+    // events: lam row m0 - 1 - (chronological index), times 2^(state
+    // exponent); 0 for a slot without a closed state (uniform, refreshed after
+    // every chunk with events)
+    int jrow[SPW];
+    float wsc[SPW];
+    u32x4 vnext;                                 // next chunk's V piece
+    int2 evnext;                                 // next chunk's event of this thread
+    int ea;                                      // exponent of this wave's active-state operand
+    int m0, act;                                 // live states, the active state's slot (uniform)
+    int e0n, e1n, qexpn;                         // next chunk's event range and query exponent
+    int prev_c0, prev_nvalid;
+    uint32_t closed;                             // physical slots of the closed states (uniform)
+    bool refresh_w;
+};
+
+// Per-block constants of the sweep.
+struct RsParams {
+    const __bf16 *V;
+    __bf16 *O;
+    int T, C, DV;
+    const int2 *events;
+    const _Float16 *q16f;
+    const int32_t *qexp_g;
+    const float *lamT_g;
+    const __bf16 *pwf_g, *ktf_g;
+    int32_t *m_t_out;
+    int bh, dv0, tid, lane, wave, lr, lg, NCH, vr, vc;
+    bool v_mover;
+    size_t tok0, slot_stride;
+    float *st_base;
+    _Float16 *sh_base;
+    const int32_t *cev;
+};
+
+// One chunk of the sweep: its operands are in X, the next chunk's go into Xn.
+template <int DK, int DVT, int SPW>
+__device__ __forceinline__ void rs_chunk(const int ch, RsStage<DK, 4 * SPW> &X, RsStage<DK, 4 * SPW> &Xn,
+                                         RsSmem<DK, DVT, 4 * SPW> &S, const RsParams &A, RsCarry<DK, DVT, SPW> &c)
 {
     constexpr int KS = DK / 32;
     constexpr int NTV = DVT / 16;
     constexpr int MT = kChunk / 16;
     constexpr int CMAX = 4 * SPW;
-    static_assert(KS <= 4, "the active state gives each wave at most one 32-row block of d_k");
-    typedef RsSmem<DK, DVT, CMAX> Smem;
-    typedef ChunkRegs<DK, DVT, CMAX> Regs;
-    extern __shared__ __align__(16) unsigned char smem_raw[];
-    Smem &S = *reinterpret_cast<Smem *>(smem_raw);
-
-    const int nblk = gridDim.x;
-    int lin = blockIdx.x;
-    if ((nblk & 7) == 0) lin = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
-    const int bh = lin / nblk_dv;
-    const int dv0 = (lin % nblk_dv) * DVT;
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int lr = lane & 15, lg = lane >> 4;
-    const int NCH = (T + kChunk - 1) / kChunk;
-    const size_t tok0 = static_cast<size_t>(bh) * T;
-    const size_t slot_stride = static_cast<size_t>(DV) * DK;
-    float *st_base = states + static_cast<size_t>(bh) * C * DV * DK + static_cast<size_t>(dv0) * DK;
-    _Float16 *sh_base = shadow + static_cast<size_t>(bh) * C * DV * DK + static_cast<size_t>(dv0) * DK;
-
-    Frag<_Float16> stk[SPW][KS][NTV];
-    floatx4 am[NTV][2];
-    Frag<_Float16> af[NTV];
-#pragma unroll
-    for (int r = 0; r < SPW; ++r)
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-            for (int nt = 0; nt < NTV; ++nt) zero_frag(stk[r][ks][nt]);
-#pragma unroll
-    for (int nt = 0; nt < NTV; ++nt) {
-        am[nt][0] = floatx4{0.f, 0.f, 0.f, 0.f};
-        am[nt][1] = floatx4{0.f, 0.f, 0.f, 0.f};
-        zero_frag(af[nt]);
-    }
-    int ea = 0;           // exponent of this wave's active-state operand
-    int m0 = 0, act = -1; // live states and the active state's slot (uniform)
-    uint32_t closed = 0;  // physical slots of the closed states (uniform)
-    if (tid < kMaxC) { S.order[tid] = tid; S.shexp[tid] = 0; }
-
-    Regs pre;
-    load_chunk(pre, V, q16f, qexp_g, lamT_g, pwf_g, ktf_g, chunk_ev, bh, NCH, T, DV, dv0, 0, tid);
-    floatx4 Oprev[NTV];           // the previous chunk's outputs, stored one iteration late
-    int prev_c0 = 0, prev_nvalid = 0;
-    for (int ch = 0; ch < NCH; ++ch) {
+    const __bf16 *V = A.V;
+    __bf16 *O = A.O;
+    const int T = A.T, C = A.C, DV = A.DV;
+    const int2 *events = A.events;
+    const _Float16 *q16f = A.q16f;
+    const int32_t *qexp_g = A.qexp_g;
+    const float *lamT_g = A.lamT_g;
+    const __bf16 *pwf_g = A.pwf_g, *ktf_g = A.ktf_g;
+    int32_t *m_t_out = A.m_t_out;
+    const int bh = A.bh, dv0 = A.dv0, tid = A.tid, lane = A.lane, wave = A.wave, lr = A.lr, lg = A.lg;
+    const int NCH = A.NCH, vr = A.vr, vc = A.vc;
+    const bool v_mover = A.v_mover;
+    const size_t tok0 = A.tok0, slot_stride = A.slot_stride;
+    float *st_base = A.st_base;
+    _Float16 *sh_base = A.sh_base;
+    const int32_t *cev = A.cev;
+    auto &stk = c.stk;
+    auto &am = c.am;
+    auto &af = c.af;
+    auto &Oprev = c.Oprev;
+    auto &jrow = c.jrow;
+    auto &wsc = c.wsc;
+    u32x4 &vnext = c.vnext;
+    int2 &evnext = c.evnext;
+    int &ea = c.ea, &m0 = c.m0, &act = c.act, &e0n = c.e0n, &e1n = c.e1n, &qexpn = c.qexpn;
+    int &prev_c0 = c.prev_c0, &prev_nvalid = c.prev_nvalid;
+    uint32_t &closed = c.closed;
+    bool &refresh_w = c.refresh_w;
         const int c0 = ch * kChunk;
         const int nvalid = min(kChunk, T - c0);
-        const int e0 = pre.e0, nev = pre.e1 - pre.e0;
+        const int nev = e1n - e0n;
         const bool has_ev = nev > 0;
-        const int qexp = pre.qexp;
-        lds_barrier();
-        // ---- the chunk's operands into LDS, the next chunk's into registers
-#pragma unroll
-        for (int j = 0; j < Regs::NQ; ++j) reinterpret_cast<u32x4 *>(&S.qf[0][0][0][0])[tid + 256 * j] = pre.q[j];
-#pragma unroll
-        for (int j = 0; j < Regs::NL; ++j) {
-            const int idx = tid + 256 * j;
-            if (idx < CMAX * kChunk / 4) reinterpret_cast<u32x4 *>(&S.lamT[0][0])[idx] = pre.l[j];
+        const int qexp = qexpn;
+        const u32x4 vcur = vnext;
+        const int2 evcur = evnext;
+        // chunk ch's operands have landed (every wave's share) and every wave
+        // is done with chunk ch - 1
+        wait_vmem();
+        __syncthreads();
+        // ---- chunk ch + 1: operands into the other stage, V and events into registers
+        if (ch + 1 < NCH) {
+            const size_t cbn = static_cast<size_t>(bh) * NCH + ch + 1;
+            stage_chunk<DK, CMAX>(Xn, q16f, lamT_g, pwf_g, ktf_g, cbn, tid, wave);
+            e0n = cev[ch + 1];
+            e1n = cev[ch + 2];
+            qexpn = qexp_g[cbn];
+            const int c0n = c0 + kChunk;
+            vnext = u32x4{0u, 0u, 0u, 0u};
+            if (v_mover && vr < min(kChunk, T - c0n))
+                vnext = *reinterpret_cast<const u32x4 *>(V + (tok0 + c0n + vr) * DV + dv0 + vc);
+            evnext = make_int2(0, 0);
+            if (tid < e1n - e0n) evnext = events[tok0 + e0n + tid];
         }
+        // ---- this chunk's V (transposed) and events into LDS
+        if (v_mover) {
+            const __bf16 *ve = reinterpret_cast<const __bf16 *>(&vcur);
 #pragma unroll
-        for (int j = 0; j < Regs::NP; ++j) reinterpret_cast<u32x4 *>(&S.pwf[0][0][0][0])[tid + 256 * j] = pre.p[j];
-#pragma unroll
-        for (int j = 0; j < Regs::NK; ++j) reinterpret_cast<u32x4 *>(&S.ktf[0][0][0][0])[tid + 256 * j] = pre.k[j];
-        if (tid < kChunk * DVT / 8) {
-            const int r = tid & (kChunk - 1), cv = (tid / kChunk) * 8;
-            const __bf16 *ve = reinterpret_cast<const __bf16 *>(&pre.v);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) S.vt[cv + e][r] = ve[e];
+            for (int e = 0; e < 8; ++e) S.vt[vc + e][vr] = ve[e];
         }
-        if (tid < nev) S.evs[tid] = events[tok0 + e0 + tid];
-        if (ch + 1 < NCH)
-            load_chunk(pre, V, q16f, qexp_g, lamT_g, pwf_g, ktf_g, chunk_ev, bh, NCH, T, DV, dv0, ch + 1, tid);
+        if (tid < nev) S.evs[tid] = evcur;
+        // ---- the previous chunk's outputs
         if (ch > 0) {
 #pragma unroll
             for (int nt = 0; nt < NTV; ++nt)
@@ -388,10 +418,21 @@ __global__ __launch_bounds__(256, 1) void k_prefill_rs(
                         O[(tok0 + prev_c0 + t) * DV + dv0 + 16 * nt + lr] = static_cast<__bf16>(Oprev[nt][r]);
                 }
         }
-        lds_barrier();
+        if (refresh_w) {
+#pragma unroll
+            for (int r = 0; r < SPW; ++r) {
+                const int p = 4 * r + wave;
+                const bool live = (closed >> p) & 1u;
+                jrow[r] = live ? __builtin_amdgcn_readfirstlane(m0 - 1 - S.inv[p]) : 0;
+                wsc[r] = live ? ldexpf(1.0f, __builtin_amdgcn_readfirstlane(S.shexp[p])) : 0.0f;
+            }
+            refresh_w = false;
+        }
+        const float qsc = ldexpf(1.0f, qexp);
         if (has_ev) {
-            // token masks: bit i of om_t = state i of the chunk start live after
-            // token t, bit p of nm_t = state opened at chunk position p live
+            // token masks (wave 0, which also wrote the events): bit i of om_t
+            // = state i of the chunk start live after token t, bit p of nm_t =
+            // state opened at chunk position p live after token t
             if (tid < kChunk) {
                 uint64_t om = low_bits(m0), nm = 0;
                 for (int e = 0; e < nev; ++e) {
@@ -409,27 +450,28 @@ __global__ __launch_bounds__(256, 1) void k_prefill_rs(
                     m_t_out[tok0 + c0 + tid] = __popcll(om) + __popcll(nm);
             }
             lds_barrier();
-        } else if (m_t_out && dv0 == 0 && tid < nvalid) {
-            m_t_out[tok0 + c0 + tid] = m0;
-        }
-        // read weights of every physical slot (0 unless it holds a closed
-        // state) and of the active state, with the operand exponents folded in;
-        // without events a closed state's slot is j = m0 - 1 - i for all tokens
+            // read weights per token: thread (wave, lane) fills rows p = 4r +
+            // wave for token lane, so each wave reads only rows it wrote
 #pragma unroll
-        for (int j = 0; j < CMAX * kChunk / 256; ++j) {
-            const int idx = tid + 256 * j;
-            const int p = idx / kChunk, t = idx & (kChunk - 1);
-            float w = 0.0f;
-            if ((closed >> p) & 1u) {
-                const int i = S.inv[p];
-                const int slot = has_ev ? __popcll(shr64(S.om[t], i + 1)) + __popcll(S.nm[t]) : m0 - 1 - i;
-                w = ldexpf(S.lamT[slot][t], S.shexp[p] + qexp);
+            for (int r = 0; r < SPW; ++r) {
+                const int p = 4 * r + wave;
+                if ((closed >> p) & 1u) {
+                    const int i = S.inv[p];
+                    const int slot = __popcll(shr64(S.om[lane], i + 1)) + __popcll(S.nm[lane]);
+                    S.W[p][lane] = ldexpf(X.lamT[slot][lane], S.shexp[p] + qexp);
+                }
             }
-            S.W[p][t] = w;
+            S.wact[wave][lane] = ldexpf(X.lamT[__popcll(S.nm[lane])][lane], qexp + ea);
+        } else {
+            if (m_t_out && dv0 == 0 && tid < nvalid) m_t_out[tok0 + c0 + tid] = m0;
+            // a closed state's slot is the same for every token of the chunk
+#pragma unroll
+            for (int r = 0; r < SPW; ++r) {
+                const int p = 4 * r + wave;
+                if ((closed >> p) & 1u) S.W[p][lane] = X.lamT[jrow[r]][lane] * (wsc[r] * qsc);
+            }
+            S.wact[wave][lane] = X.lamT[0][lane] * ldexpf(qsc, ea);
         }
-        if (m0 > 0 && tid < kChunk)
-            S.wact[tid] = ldexpf(S.lamT[has_ev ? __popcll(S.nm[tid]) : 0][tid], qexp);
-        lds_barrier();
 
         // ---- inter-chunk read: closed states from registers, then the active state
         floatx4 Oi[MT][NTV];
@@ -442,12 +484,12 @@ __global__ __launch_bounds__(256, 1) void k_prefill_rs(
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) load_frag(qf[mt][ks], S.qf[mt][ks][lane]);
-            // every slot of the wave, live or not: a slot without a closed
-            // state has weight 0 and finite (zero or stale) operands
+                for (int ks = 0; ks < KS; ++ks) load_frag(qf[mt][ks], X.qf[mt][ks][lane]);
+            // the wave's slots that hold a closed state (a uniform branch)
 #pragma unroll
             for (int r = 0; r < SPW; ++r) {
                 const int p = 4 * r + wave;
+                if (!((closed >> p) & 1u)) continue;
                 floatx4 P[MT][NTV];
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt)
@@ -473,21 +515,19 @@ __global__ __launch_bounds__(256, 1) void k_prefill_rs(
             }
             if (act >= 0 && wave < KS) {
                 // d_k rows 32w..32w+31 of the active state live in wave w
-                const float sc = ldexpf(1.0f, ea);
-                const float *wrow = &S.wact[0];
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) {
                     Frag<_Float16> qa;
-                    load_frag(qa, S.qf[mt][wave][lane]);
-                    const float4 w = *reinterpret_cast<const float4 *>(wrow + 16 * mt + 4 * lg);
+                    load_frag(qa, X.qf[mt][wave][lane]);
+                    const float4 w = *reinterpret_cast<const float4 *>(&S.wact[wave][16 * mt + 4 * lg]);
 #pragma unroll
                     for (int nt = 0; nt < NTV; ++nt) {
                         floatx4 P = floatx4{0.f, 0.f, 0.f, 0.f};
                         mma32(P, qa, af[nt]);
-                        Oi[mt][nt][0] += (sc * w.x) * P[0];
-                        Oi[mt][nt][1] += (sc * w.y) * P[1];
-                        Oi[mt][nt][2] += (sc * w.z) * P[2];
-                        Oi[mt][nt][3] += (sc * w.w) * P[3];
+                        Oi[mt][nt][0] += w.x * P[0];
+                        Oi[mt][nt][1] += w.y * P[1];
+                        Oi[mt][nt][2] += w.z * P[2];
+                        Oi[mt][nt][3] += w.w * P[3];
                     }
                 }
             }
@@ -495,25 +535,22 @@ __global__ __launch_bounds__(256, 1) void k_prefill_rs(
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int nt = 0; nt < NTV; ++nt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) S.ored[wave][16 * mt + 4 * lg + r][16 * nt + lr] = Oi[mt][nt][r];
+            for (int nt = 0; nt < NTV; ++nt) S.ored[wave][mt][nt][lane] = Oi[mt][nt];
         lds_barrier();
         // ---- reduce the waves' partial reads, add P V (wave w: rows 16w..16w+15)
         {
             const int w = wave;
 #pragma unroll
-            for (int nt = 0; nt < NTV; ++nt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t = 16 * w + 4 * lg + r, col = 16 * nt + lr;
-                    Oprev[nt][r] = S.ored[0][t][col] + S.ored[1][t][col] + S.ored[2][t][col] + S.ored[3][t][col];
-                }
+            for (int nt = 0; nt < NTV; ++nt) {
+                const floatx4 a = S.ored[0][w][nt][lane], b = S.ored[1][w][nt][lane];
+                const floatx4 c = S.ored[2][w][nt][lane], d = S.ored[3][w][nt][lane];
+                Oprev[nt] = (a + b) + (c + d);
+            }
 #pragma unroll
             for (int ks = 0; ks < kChunk / 32; ++ks) {
                 if (32 * ks <= 16 * w + 15) {
                     Frag<__bf16> a;
-                    load_frag(a, S.pwf[w][ks][lane]);
+                    load_frag(a, X.pwf[w][ks][lane]);
 #pragma unroll
                     for (int nt = 0; nt < NTV; ++nt) {
                         Frag<__bf16> b;
@@ -535,7 +572,7 @@ __global__ __launch_bounds__(256, 1) void k_prefill_rs(
 #pragma unroll
                     for (int h = 0; h < 2; ++h) {
                         Frag<__bf16> a;
-                        load_frag(a, S.ktf[2 * wave + h][kk][lane]);
+                        load_frag(a, X.ktf[2 * wave + h][kk][lane]);
 #pragma unroll
                         for (int nt = 0; nt < NTV; ++nt) {
                             Frag<__bf16> b;
@@ -545,7 +582,7 @@ __global__ __launch_bounds__(256, 1) void k_prefill_rs(
                     }
                 ea = refresh_active<NTV>(am, af);
             }
-            continue;
+            return;
         }
 
         // chunk with events: general update in the fp32 cache
@@ -633,7 +670,7 @@ __global__ __launch_bounds__(256, 1) void k_prefill_rs(
                         Frag<__bf16> a, b;
                         load_frag(a, &S.vt[16 * mt + lr][base]);
                         mask_frag(a, base, lo, hi);
-                        load_frag(b, S.ktf[nt][ks][lane]);
+                        load_frag(b, X.ktf[nt][ks][lane]);
                         mma32(acc, a, b);
                     }
                 }
@@ -713,7 +750,98 @@ __global__ __launch_bounds__(256, 1) void k_prefill_rs(
         m0 = mnew;
         act = an;
         closed = cl;
+        refresh_w = true;
+}
+
+template <int DK, int DVT, int SPW>
+__global__ __launch_bounds__(256, 1) void k_prefill_rs(
+    const __bf16 *__restrict__ V, __bf16 *__restrict__ O, int T, int C, int DV, int nblk_dv,
+    float *__restrict__ states, _Float16 *__restrict__ shadow, const int2 *__restrict__ events,
+    const int32_t *__restrict__ chunk_ev, const _Float16 *__restrict__ q16f, const int32_t *__restrict__ qexp_g,
+    const float *__restrict__ lamT_g, const __bf16 *__restrict__ pwf_g, const __bf16 *__restrict__ ktf_g,
+    uint8_t *__restrict__ meta_base, size_t meta_stride, int32_t *__restrict__ m_t_out)
+{
+    constexpr int KS = DK / 32;
+    constexpr int NTV = DVT / 16;
+    constexpr int CMAX = 4 * SPW;
+    static_assert(KS <= 4, "the active state gives each wave at most one 32-row block of d_k");
+    static_assert(DVT <= 32, "one 16-byte V piece per thread covers at most 32 columns");
+    __shared__ RsStage<DK, CMAX> st0, st1;        // chunk ch in st0 when ch is even
+    __shared__ RsSmem<DK, DVT, CMAX> S;
+
+    const int nblk = gridDim.x;
+    int lin = blockIdx.x;
+    if ((nblk & 7) == 0) lin = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
+    RsParams A;
+    A.V = V; A.O = O; A.T = T; A.C = C; A.DV = DV;
+    A.events = events; A.q16f = q16f; A.qexp_g = qexp_g; A.lamT_g = lamT_g; A.pwf_g = pwf_g; A.ktf_g = ktf_g;
+    A.m_t_out = m_t_out;
+    A.bh = lin / nblk_dv;
+    A.dv0 = (lin % nblk_dv) * DVT;
+    A.tid = threadIdx.x;
+    A.lane = A.tid & 63;
+    A.wave = __builtin_amdgcn_readfirstlane(A.tid >> 6);
+    A.lr = A.lane & 15;
+    A.lg = A.lane >> 4;
+    A.NCH = (T + kChunk - 1) / kChunk;
+    // thread tid < 8 DVT moves V piece (token tid % 64, columns 8 (tid / 64) ..)
+    A.vr = A.tid & (kChunk - 1);
+    A.vc = (A.tid / kChunk) * 8;
+    A.v_mover = A.tid < kChunk * DVT / 8;
+    A.tok0 = static_cast<size_t>(A.bh) * T;
+    A.slot_stride = static_cast<size_t>(DV) * DK;
+    A.st_base = states + static_cast<size_t>(A.bh) * C * DV * DK + static_cast<size_t>(A.dv0) * DK;
+    A.sh_base = shadow + static_cast<size_t>(A.bh) * C * DV * DK + static_cast<size_t>(A.dv0) * DK;
+    A.cev = chunk_ev + static_cast<size_t>(A.bh) * (A.NCH + 1);
+    const int tid = A.tid, wave = A.wave, lr = A.lr, lg = A.lg, NCH = A.NCH;
+
+    RsCarry<DK, DVT, SPW> c;
+#pragma unroll
+    for (int r = 0; r < SPW; ++r)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int nt = 0; nt < NTV; ++nt) zero_frag(c.stk[r][ks][nt]);
+#pragma unroll
+    for (int nt = 0; nt < NTV; ++nt) {
+        c.am[nt][0] = floatx4{0.f, 0.f, 0.f, 0.f};
+        c.am[nt][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+        zero_frag(c.af[nt]);
+        c.Oprev[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
+#pragma unroll
+    for (int r = 0; r < SPW; ++r) { c.jrow[r] = 0; c.wsc[r] = 0.0f; }
+    c.ea = 0;
+    c.m0 = 0;
+    c.act = -1;
+    c.closed = 0;
+    c.refresh_w = false;
+    c.prev_c0 = 0;
+    c.prev_nvalid = 0;
+    if (tid < kMaxC) { S.order[tid] = tid; S.shexp[tid] = 0; }
+
+    // chunk 0: operands into stage 0, V and events into registers
+    stage_chunk<DK, CMAX>(st0, q16f, lamT_g, pwf_g, ktf_g, static_cast<size_t>(A.bh) * NCH, tid, wave);
+    c.vnext = u32x4{0u, 0u, 0u, 0u};
+    if (A.v_mover && A.vr < min(kChunk, T))
+        c.vnext = *reinterpret_cast<const u32x4 *>(V + (A.tok0 + A.vr) * DV + A.dv0 + A.vc);
+    c.e0n = A.cev[0];
+    c.e1n = A.cev[1];
+    c.qexpn = qexp_g[static_cast<size_t>(A.bh) * NCH];
+    c.evnext = make_int2(0, 0);
+    if (tid < c.e1n - c.e0n) c.evnext = events[A.tok0 + c.e0n + tid];
+
+    for (int ch = 0; ch < NCH; ch += 2) {
+        rs_chunk<DK, DVT, SPW>(ch, st0, st1, S, A, c);
+        if (ch + 1 < NCH) rs_chunk<DK, DVT, SPW>(ch + 1, st1, st0, S, A, c);
+    }
+
+    const size_t tok0 = A.tok0, slot_stride = A.slot_stride;
+    const int dv0 = A.dv0, bh = A.bh;
+    float *st_base = A.st_base;
+    const int prev_c0 = c.prev_c0, prev_nvalid = c.prev_nvalid, act = c.act, m0 = c.m0;
+    auto &Oprev = c.Oprev;
+    auto &am = c.am;
 #pragma unroll
     for (int nt = 0; nt < NTV; ++nt)
 #pragma unroll
@@ -744,14 +872,6 @@ static hipError_t launch_rs(const PrefillArgs &a, hipStream_t stream)
 {
     const int BH = a.g.B * a.g.H;
     const int nblk_dv = a.g.dv / DVT;
-    const size_t smem = sizeof(RsSmem<DK, DVT, 4 * SPW>);
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_prefill_rs<DK, DVT, SPW>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
     const int NCH = (a.T + kChunk - 1) / kChunk;
     hipLaunchKernelGGL((k_chunk_prep<DK>), dim3(NCH, BH), dim3(256), 0, stream,
                        static_cast<const __bf16 *>(a.q), static_cast<const __bf16 *>(a.k),
@@ -764,7 +884,7 @@ static hipError_t launch_rs(const PrefillArgs &a, hipStream_t stream)
         hipError_t e = hipEventRecord(a.ev_before, stream);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((k_prefill_rs<DK, DVT, SPW>), dim3(BH * nblk_dv), dim3(256), smem, stream,
+    hipLaunchKernelGGL((k_prefill_rs<DK, DVT, SPW>), dim3(BH * nblk_dv), dim3(256), 0, stream,
                        static_cast<const __bf16 *>(a.v), static_cast<__bf16 *>(a.o), a.T, a.g.C, a.g.dv,
                        nblk_dv, a.states, static_cast<_Float16 *>(a.ws.shadow), a.ws.events, a.ws.chunk_ev,
                        static_cast<const _Float16 *>(a.ws.q16f), a.ws.qexp, a.ws.lamT,
@@ -795,18 +915,18 @@ hipError_t launch_prefill_rs(const PrefillArgs &a, hipStream_t stream)
                                                                : launch_rs<64, 16, 8>(a, stream);
 }
 
+template <int DK, int DVT, int CMAX>
+constexpr size_t rs_lds_bytes() { return 2 * sizeof(RsStage<DK, CMAX>) + sizeof(RsSmem<DK, DVT, CMAX>); }
+
 size_t prefill_rs_smem_bytes(int dk, int dvt, int C)
 {
     const int cmax = C <= 8 ? 8 : (C <= 16 ? 16 : 32);
-    size_t b = 0;
     if (dk == 128) {
-        if (dvt == 32) b = cmax == 8 ? sizeof(RsSmem<128, 32, 8>) : cmax == 16 ? sizeof(RsSmem<128, 32, 16>) : sizeof(RsSmem<128, 32, 32>);
-        else b = cmax == 8 ? sizeof(RsSmem<128, 16, 8>) : cmax == 16 ? sizeof(RsSmem<128, 16, 16>) : sizeof(RsSmem<128, 16, 32>);
-    } else {
-        if (dvt == 32) b = cmax == 8 ? sizeof(RsSmem<64, 32, 8>) : cmax == 16 ? sizeof(RsSmem<64, 32, 16>) : sizeof(RsSmem<64, 32, 32>);
-        else b = cmax == 8 ? sizeof(RsSmem<64, 16, 8>) : cmax == 16 ? sizeof(RsSmem<64, 16, 16>) : sizeof(RsSmem<64, 16, 32>);
+        if (dvt == 32) return cmax == 8 ? rs_lds_bytes<128, 32, 8>() : cmax == 16 ? rs_lds_bytes<128, 32, 16>() : rs_lds_bytes<128, 32, 32>();
+        return cmax == 8 ? rs_lds_bytes<128, 16, 8>() : cmax == 16 ? rs_lds_bytes<128, 16, 16>() : rs_lds_bytes<128, 16, 32>();
     }
-    return b;
+    if (dvt == 32) return cmax == 8 ? rs_lds_bytes<64, 32, 8>() : cmax == 16 ? rs_lds_bytes<64, 32, 16>() : rs_lds_bytes<64, 32, 32>();
+    return cmax == 8 ? rs_lds_bytes<64, 16, 8>() : cmax == 16 ? rs_lds_bytes<64, 16, 16>() : rs_lds_bytes<64, 16, 32>();
 }
 
 }  // namespace dla

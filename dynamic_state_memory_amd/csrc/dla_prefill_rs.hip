@@ -36,6 +36,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "dla_device.h"
 #include "dla_internal.h"
 
@@ -218,6 +220,10 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
 
 // ------------------------------------------------------------ the sweep
 
+constexpr int kRsWaves = 8;                    // waves per sweep block (two per SIMD)
+constexpr int kRsThreads = 64 * kRsWaves;
+constexpr int kRsActWave0 = 4;                 // waves 4.. hold the active state, 0..3 reduce
+
 // The chunk operands k_chunk_prep wrote, one 64-token chunk, copied verbatim
 // into LDS by the global->LDS loads (each 16-byte piece lands at the same
 // offset it has in the global chunk).
@@ -236,8 +242,8 @@ template <int DK, int DVT, int CMAX>
 struct RsSmem {
     __bf16 vt[DVT][kChunk + 8];                  // V slice of the chunk, transposed
     float W[CMAX][kChunk];      // closed-state read weights by physical slot (owner wave's rows)
-    float wact[4][kChunk];      // active-state read weights, one row per wave
-    floatx4 ored[4][kChunk / 16][DVT / 16][64];  // partial reads: wave, row tile, column tile, lane
+    float wact[DK / 32][kChunk];  // active-state read weights, one row per active wave
+    floatx4 ored[kRsWaves][kChunk / 16][DVT / 16][64];  // partial reads: wave, row tile, column tile, lane
     uint64_t om[kChunk];
     uint64_t nm[kChunk];
     int32_t order[kMaxC];
@@ -252,7 +258,7 @@ struct RsSmem {
     int32_t shexp[kMaxC];
     int32_t inv[kMaxC];         // chronological index of the state in each physical slot
     int2 evs[kChunk];           // the chunk's events (at most one per token)
-    float red[4];
+    float red[kRsWaves];
     int32_t n_merge, n_grp, n_changed, m_new, act_new;
 };
 
@@ -264,46 +270,55 @@ typedef __attribute__((address_space(1))) const void glb_void_t;
 // piece lands at lds_wave + 16 l (lds_wave is the same for the whole wave).
 __device__ __forceinline__ void load_to_lds16(const void *g, void *lds_wave)
 {
-    __builtin_amdgcn_global_load_lds((glb_void_t *)(g), (lds_void_t *)(lds_wave),
-                                     16, 0, 0);
+    __builtin_amdgcn_global_load_lds((glb_void_t *)(g), (lds_void_t *)(lds_wave), 16, 0, 0);
 }
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Issue the loads of chunk ch's operands into stage X (wave w moves pieces
-// 64 w + 256 j of every array).
+// base (the same for the whole wave) plus a per-lane byte offset: the form
+// the global instructions take as an SGPR base and a 32-bit VGPR offset
+template <typename P>
+__device__ __forceinline__ P *at_bytes(P *base, uint32_t off)
+{
+    typedef typename std::conditional<std::is_const<P>::value, const char, char>::type B;
+    return reinterpret_cast<P *>(reinterpret_cast<B *>(base) + off);
+}
+
+// Pieces j of an array of N 16-byte pieces: thread tid moves piece tid + NT j
+// (wave w's instruction fills pieces 64 w + NT j .. + 63).
+template <int N>
+__device__ __forceinline__ void stage_array(const u32x4 *src, u32x4 *dst, int tid, int wave)
+{
+#pragma unroll
+    for (int j = 0; j < (N + kRsThreads - 1) / kRsThreads; ++j)
+        if (N % kRsThreads == 0 || 64 * wave + kRsThreads * j < N)
+            load_to_lds16(at_bytes(src + kRsThreads * j, 16u * tid), dst + 64 * wave + kRsThreads * j);
+}
+
+// Issue the loads of chunk cb's operands into stage X.
 template <int DK, int CMAX>
 __device__ __forceinline__ void stage_chunk(RsStage<DK, CMAX> &X, const _Float16 *q16f, const float *lamT,
                                             const __bf16 *pwf, const __bf16 *ktf, size_t cb, int tid, int wave)
 {
-    const u32x4 *qs = reinterpret_cast<const u32x4 *>(q16f) + cb * (kChunk * DK * 2 / 16);
-    const u32x4 *ls = reinterpret_cast<const u32x4 *>(lamT) + cb * (kPrepCmax * kChunk * 4 / 16);
-    const u32x4 *ps = reinterpret_cast<const u32x4 *>(pwf) + cb * (kChunk * kChunk * 2 / 16);
-    const u32x4 *ks = reinterpret_cast<const u32x4 *>(ktf) + cb * (kChunk * DK * 2 / 16);
-    u32x4 *qd = reinterpret_cast<u32x4 *>(&X.qf[0][0][0][0]);
-    u32x4 *ld = reinterpret_cast<u32x4 *>(&X.lamT[0][0]);
-    u32x4 *pd = reinterpret_cast<u32x4 *>(&X.pwf[0][0][0][0]);
-    u32x4 *kd = reinterpret_cast<u32x4 *>(&X.ktf[0][0][0][0]);
-#pragma unroll
-    for (int j = 0; j < kChunk * DK * 2 / 16 / 256; ++j) load_to_lds16(qs + tid + 256 * j, qd + 64 * wave + 256 * j);
-    constexpr int NL = CMAX * kChunk * 4 / 16;   // 128, 256 or 512 pieces
-#pragma unroll
-    for (int j = 0; j < (NL + 255) / 256; ++j)
-        if (64 * wave + 256 * j < NL) load_to_lds16(ls + tid + 256 * j, ld + 64 * wave + 256 * j);
-#pragma unroll
-    for (int j = 0; j < kChunk * kChunk * 2 / 16 / 256; ++j) load_to_lds16(ps + tid + 256 * j, pd + 64 * wave + 256 * j);
-#pragma unroll
-    for (int j = 0; j < kChunk * DK * 2 / 16 / 256; ++j) load_to_lds16(ks + tid + 256 * j, kd + 64 * wave + 256 * j);
+    constexpr int NQ = kChunk * DK * 2 / 16, NL = CMAX * kChunk * 4 / 16, NP = kChunk * kChunk * 2 / 16;
+    stage_array<NQ>(reinterpret_cast<const u32x4 *>(q16f) + cb * NQ, reinterpret_cast<u32x4 *>(&X.qf[0][0][0][0]),
+                    tid, wave);
+    stage_array<NL>(reinterpret_cast<const u32x4 *>(lamT) + cb * (kPrepCmax * kChunk * 4 / 16),
+                    reinterpret_cast<u32x4 *>(&X.lamT[0][0]), tid, wave);
+    stage_array<NP>(reinterpret_cast<const u32x4 *>(pwf) + cb * NP, reinterpret_cast<u32x4 *>(&X.pwf[0][0][0][0]),
+                    tid, wave);
+    stage_array<NQ>(reinterpret_cast<const u32x4 *>(ktf) + cb * NQ, reinterpret_cast<u32x4 *>(&X.ktf[0][0][0][0]),
+                    tid, wave);
 }
 
 // What one block carries from chunk to chunk (registers after inlining).
 template <int DK, int DVT, int SPW>
 struct RsCarry {
     Frag<_Float16> stk[SPW][DK / 32][DVT / 16];  // closed states of the wave's slots (fp16, normalised)
-    floatx4 am[DVT / 16][2];                     // active state, d_k rows 32w..32w+31 (fp32)
+    floatx4 am[DVT / 16][2];                     // active state, d_k rows 32 kb .. 32 kb + 31 (fp32)
     Frag<_Float16> af[DVT / 16];                 // its fp16 operand copy
     floatx4 Oprev[DVT / 16];                     // previous chunk's outputs, stored one chunk late
-    // read-weight source of the wave's slots p = 4r + wave in a chunk without
+    // read-weight source of the wave's slots p = 8 r + wave in a chunk without
     // events: lam row m0 - 1 - (chronological index), times 2^(state
     // exponent); 0 for a slot without a closed state (uniform, refreshed after
     // every chunk with events)
@@ -331,6 +346,8 @@ struct RsParams {
     const __bf16 *pwf_g, *ktf_g;
     int32_t *m_t_out;
     int bh, dv0, tid, lane, wave, lr, lg, NCH, vr, vc;
+    uint32_t v_off;             // byte offset of this thread's V piece within a chunk's rows
+    uint32_t o_off;             // byte offset of this lane's first output within a chunk (reducing waves)
     bool v_mover;
     size_t tok0, slot_stride;
     float *st_base;
@@ -339,422 +356,431 @@ struct RsParams {
 };
 
 // One chunk of the sweep: its operands are in X, the next chunk's go into Xn.
+//
+// Work split over the 8 waves: wave w owns the physical slots p = 8 r + w
+// (closed states in registers); waves 4 .. 4 + d_k/32 - 1 hold d_k rows
+// 32 (w - 4) .. + 31 of the active state; after the partial reads are
+// exchanged, waves 0..3 reduce rows 16 w .. 16 w + 15 and add P V while the
+// active-state waves add V^T K to it.
 template <int DK, int DVT, int SPW>
-__device__ __forceinline__ void rs_chunk(const int ch, RsStage<DK, 4 * SPW> &X, RsStage<DK, 4 * SPW> &Xn,
-                                         RsSmem<DK, DVT, 4 * SPW> &S, const RsParams &A, RsCarry<DK, DVT, SPW> &c)
+__device__ __forceinline__ void rs_chunk(const int ch, RsStage<DK, kRsWaves * SPW> &X,
+                                         RsStage<DK, kRsWaves * SPW> &Xn, RsSmem<DK, DVT, kRsWaves * SPW> &S,
+                                         const RsParams &A, RsCarry<DK, DVT, SPW> &c)
 {
     constexpr int KS = DK / 32;
     constexpr int NTV = DVT / 16;
     constexpr int MT = kChunk / 16;
-    constexpr int CMAX = 4 * SPW;
-    const __bf16 *V = A.V;
+    constexpr int NW = kRsWaves;
+    constexpr int NT = kRsThreads;
+    constexpr int AW = kRsActWave0;
+    constexpr int CMAX = NW * SPW;
     __bf16 *O = A.O;
     const int T = A.T, C = A.C, DV = A.DV;
-    const int2 *events = A.events;
-    const _Float16 *q16f = A.q16f;
-    const int32_t *qexp_g = A.qexp_g;
-    const float *lamT_g = A.lamT_g;
-    const __bf16 *pwf_g = A.pwf_g, *ktf_g = A.ktf_g;
-    int32_t *m_t_out = A.m_t_out;
     const int bh = A.bh, dv0 = A.dv0, tid = A.tid, lane = A.lane, wave = A.wave, lr = A.lr, lg = A.lg;
     const int NCH = A.NCH, vr = A.vr, vc = A.vc;
-    const bool v_mover = A.v_mover;
     const size_t tok0 = A.tok0, slot_stride = A.slot_stride;
     float *st_base = A.st_base;
     _Float16 *sh_base = A.sh_base;
-    const int32_t *cev = A.cev;
+    int32_t *m_t_out = A.m_t_out;
     auto &stk = c.stk;
     auto &am = c.am;
     auto &af = c.af;
     auto &Oprev = c.Oprev;
-    auto &jrow = c.jrow;
-    auto &wsc = c.wsc;
-    u32x4 &vnext = c.vnext;
-    int2 &evnext = c.evnext;
-    int &ea = c.ea, &m0 = c.m0, &act = c.act, &e0n = c.e0n, &e1n = c.e1n, &qexpn = c.qexpn;
-    int &prev_c0 = c.prev_c0, &prev_nvalid = c.prev_nvalid;
-    uint32_t &closed = c.closed;
-    bool &refresh_w = c.refresh_w;
-        const int c0 = ch * kChunk;
-        const int nvalid = min(kChunk, T - c0);
-        const int nev = e1n - e0n;
-        const bool has_ev = nev > 0;
-        const int qexp = qexpn;
-        const u32x4 vcur = vnext;
-        const int2 evcur = evnext;
-        // chunk ch's operands have landed (every wave's share) and every wave
-        // is done with chunk ch - 1
-        wait_vmem();
-        __syncthreads();
-        // ---- chunk ch + 1: operands into the other stage, V and events into registers
-        if (ch + 1 < NCH) {
-            const size_t cbn = static_cast<size_t>(bh) * NCH + ch + 1;
-            stage_chunk<DK, CMAX>(Xn, q16f, lamT_g, pwf_g, ktf_g, cbn, tid, wave);
-            e0n = cev[ch + 1];
-            e1n = cev[ch + 2];
-            qexpn = qexp_g[cbn];
-            const int c0n = c0 + kChunk;
-            vnext = u32x4{0u, 0u, 0u, 0u};
-            if (v_mover && vr < min(kChunk, T - c0n))
-                vnext = *reinterpret_cast<const u32x4 *>(V + (tok0 + c0n + vr) * DV + dv0 + vc);
-            evnext = make_int2(0, 0);
-            if (tid < e1n - e0n) evnext = events[tok0 + e0n + tid];
-        }
-        // ---- this chunk's V (transposed) and events into LDS
-        if (v_mover) {
-            const __bf16 *ve = reinterpret_cast<const __bf16 *>(&vcur);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) S.vt[vc + e][vr] = ve[e];
-        }
-        if (tid < nev) S.evs[tid] = evcur;
-        // ---- the previous chunk's outputs
-        if (ch > 0) {
-#pragma unroll
-            for (int nt = 0; nt < NTV; ++nt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t = 16 * wave + 4 * lg + r;
-                    if (t < prev_nvalid)
-                        O[(tok0 + prev_c0 + t) * DV + dv0 + 16 * nt + lr] = static_cast<__bf16>(Oprev[nt][r]);
-                }
-        }
-        if (refresh_w) {
-#pragma unroll
-            for (int r = 0; r < SPW; ++r) {
-                const int p = 4 * r + wave;
-                const bool live = (closed >> p) & 1u;
-                jrow[r] = live ? __builtin_amdgcn_readfirstlane(m0 - 1 - S.inv[p]) : 0;
-                wsc[r] = live ? ldexpf(1.0f, __builtin_amdgcn_readfirstlane(S.shexp[p])) : 0.0f;
-            }
-            refresh_w = false;
-        }
-        const float qsc = ldexpf(1.0f, qexp);
-        if (has_ev) {
-            // token masks (wave 0, which also wrote the events): bit i of om_t
-            // = state i of the chunk start live after token t, bit p of nm_t =
-            // state opened at chunk position p live after token t
-            if (tid < kChunk) {
-                uint64_t om = low_bits(m0), nm = 0;
-                for (int e = 0; e < nev; ++e) {
-                    const int2 ev = S.evs[e];
-                    const int pos = ev.x - c0;
-                    if (tid >= pos) {
-                        nm |= 1ull << pos;
-                        if (ev.y >= 64) nm &= ~(1ull << (ev.y - 64));
-                        else if (ev.y >= 0) om &= ~(1ull << ev.y);
-                    }
-                }
-                S.om[tid] = om;
-                S.nm[tid] = nm;
-                if (m_t_out && dv0 == 0 && tid < nvalid)
-                    m_t_out[tok0 + c0 + tid] = __popcll(om) + __popcll(nm);
-            }
-            lds_barrier();
-            // read weights per token: thread (wave, lane) fills rows p = 4r +
-            // wave for token lane, so each wave reads only rows it wrote
-#pragma unroll
-            for (int r = 0; r < SPW; ++r) {
-                const int p = 4 * r + wave;
-                if ((closed >> p) & 1u) {
-                    const int i = S.inv[p];
-                    const int slot = __popcll(shr64(S.om[lane], i + 1)) + __popcll(S.nm[lane]);
-                    S.W[p][lane] = ldexpf(X.lamT[slot][lane], S.shexp[p] + qexp);
-                }
-            }
-            S.wact[wave][lane] = ldexpf(X.lamT[__popcll(S.nm[lane])][lane], qexp + ea);
-        } else {
-            if (m_t_out && dv0 == 0 && tid < nvalid) m_t_out[tok0 + c0 + tid] = m0;
-            // a closed state's slot is the same for every token of the chunk
-#pragma unroll
-            for (int r = 0; r < SPW; ++r) {
-                const int p = 4 * r + wave;
-                if ((closed >> p) & 1u) S.W[p][lane] = X.lamT[jrow[r]][lane] * (wsc[r] * qsc);
-            }
-            S.wact[wave][lane] = X.lamT[0][lane] * ldexpf(qsc, ea);
-        }
+    const bool act_wave = wave >= AW && wave < AW + KS;
+    const int kb = wave - AW;                    // the active wave's d_k block
 
-        // ---- inter-chunk read: closed states from registers, then the active state
-        floatx4 Oi[MT][NTV];
+    const int c0 = ch * kChunk;
+    const int nvalid = min(kChunk, T - c0);
+    const int nev = c.e1n - c.e0n;
+    const bool has_ev = nev > 0;
+    const int qexp = c.qexpn;
+    const u32x4 vcur = c.vnext;
+    const int2 evcur = c.evnext;
+    // chunk ch's operands have landed (every wave's share) and every wave is
+    // done with chunk ch - 1
+    wait_vmem();
+    __syncthreads();
+    // ---- chunk ch + 1: operands into the other stage, V and events into registers
+    if (ch + 1 < NCH) {
+        const size_t cbn = static_cast<size_t>(bh) * NCH + ch + 1;
+        stage_chunk<DK, CMAX>(Xn, A.q16f, A.lamT_g, A.pwf_g, A.ktf_g, cbn, tid, wave);
+        c.e0n = A.cev[ch + 1];
+        c.e1n = A.cev[ch + 2];
+        c.qexpn = A.qexp_g[cbn];
+        const int c0n = c0 + kChunk;
+        c.vnext = u32x4{0u, 0u, 0u, 0u};
+        if (A.v_mover && vr < min(kChunk, T - c0n))
+            c.vnext = *at_bytes(reinterpret_cast<const u32x4 *>(A.V + (tok0 + c0n) * DV + dv0), A.v_off);
+        c.evnext = make_int2(0, 0);
+        if (tid < c.e1n - c.e0n) c.evnext = *at_bytes(A.events + tok0 + c.e0n, 8u * tid);
+    }
+    // ---- this chunk's V (transposed) and events into LDS
+    if (A.v_mover) {
+        const __bf16 *ve = reinterpret_cast<const __bf16 *>(&vcur);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+        for (int e = 0; e < 8; ++e) S.vt[vc + e][vr] = ve[e];
+    }
+    if (tid < nev) S.evs[tid] = evcur;
+    // ---- the previous chunk's outputs (reducing waves)
+    if (ch > 0 && wave < MT) {
+        __bf16 *ob = O + (tok0 + c.prev_c0) * DV + dv0;
 #pragma unroll
-            for (int nt = 0; nt < NTV; ++nt) Oi[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
-        {
-            Frag<_Float16> qf[MT][KS];
+        for (int nt = 0; nt < NTV; ++nt)
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * wave + 4 * lg + r;
+                if (t < c.prev_nvalid) *at_bytes(ob + r * DV + 16 * nt, A.o_off) = static_cast<__bf16>(Oprev[nt][r]);
+            }
+    }
+    if (c.refresh_w) {
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) load_frag(qf[mt][ks], X.qf[mt][ks][lane]);
+        for (int r = 0; r < SPW; ++r) {
+            const int p = NW * r + wave;
+            const bool live = (c.closed >> p) & 1u;
+            c.jrow[r] = live ? __builtin_amdgcn_readfirstlane(c.m0 - 1 - S.inv[p]) : 0;
+            c.wsc[r] = live ? ldexpf(1.0f, __builtin_amdgcn_readfirstlane(S.shexp[p])) : 0.0f;
+        }
+        c.refresh_w = false;
+    }
+    const float qsc = ldexpf(1.0f, qexp);
+    if (has_ev) {
+        // token masks (wave 0, which also wrote the events): bit i of om_t =
+        // state i of the chunk start live after token t, bit p of nm_t =
+        // state opened at chunk position p live after token t
+        if (tid < kChunk) {
+            uint64_t om = low_bits(c.m0), nm = 0;
+            for (int e = 0; e < nev; ++e) {
+                const int2 ev = S.evs[e];
+                const int pos = ev.x - c0;
+                if (tid >= pos) {
+                    nm |= 1ull << pos;
+                    if (ev.y >= 64) nm &= ~(1ull << (ev.y - 64));
+                    else if (ev.y >= 0) om &= ~(1ull << ev.y);
+                }
+            }
+            S.om[tid] = om;
+            S.nm[tid] = nm;
+            if (m_t_out && dv0 == 0 && tid < nvalid) m_t_out[tok0 + c0 + tid] = __popcll(om) + __popcll(nm);
+        }
+        lds_barrier();
+        // read weights per token: thread (wave, lane) fills the rows of the
+        // wave's slots for token lane, so each wave reads only rows it wrote
+#pragma unroll
+        for (int r = 0; r < SPW; ++r) {
+            const int p = NW * r + wave;
+            if ((c.closed >> p) & 1u) {
+                const int i = S.inv[p];
+                const int slot = __popcll(shr64(S.om[lane], i + 1)) + __popcll(S.nm[lane]);
+                S.W[p][lane] = ldexpf(X.lamT[slot][lane], S.shexp[p] + qexp);
+            }
+        }
+        if (act_wave) S.wact[kb][lane] = ldexpf(X.lamT[__popcll(S.nm[lane])][lane], qexp + c.ea);
+    } else {
+        if (m_t_out && dv0 == 0 && tid < nvalid) m_t_out[tok0 + c0 + tid] = c.m0;
+        // a closed state's slot is the same for every token of the chunk
+#pragma unroll
+        for (int r = 0; r < SPW; ++r) {
+            const int p = NW * r + wave;
+            if ((c.closed >> p) & 1u) S.W[p][lane] = X.lamT[c.jrow[r]][lane] * (c.wsc[r] * qsc);
+        }
+        if (act_wave) S.wact[kb][lane] = X.lamT[0][lane] * ldexpf(qsc, c.ea);
+    }
+
+    // ---- inter-chunk read: closed states from registers, then the active state
+    floatx4 Oi[MT][NTV];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NTV; ++nt) Oi[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    uint32_t mine = 0;          // which of the wave's slots hold a closed state (uniform)
+#pragma unroll
+    for (int r = 0; r < SPW; ++r) mine |= ((c.closed >> (NW * r + wave)) & 1u) << r;
+    if (mine != 0u) {
+        // two halves of the chunk's tokens (row tiles 2 hf, 2 hf + 1) keep
+        // half of the query fragments live at a time
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            Frag<_Float16> qf[2][KS];
+#pragma unroll
+            for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) load_frag(qf[m2][ks], X.qf[2 * hf + m2][ks][lane]);
             // the wave's slots that hold a closed state (a uniform branch)
 #pragma unroll
             for (int r = 0; r < SPW; ++r) {
-                const int p = 4 * r + wave;
-                if (!((closed >> p) & 1u)) continue;
-                floatx4 P[MT][NTV];
+                const int p = NW * r + wave;
+                if (!((mine >> r) & 1u)) continue;
+                floatx4 P[2][NTV];
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
+                for (int m2 = 0; m2 < 2; ++m2)
 #pragma unroll
-                    for (int nt = 0; nt < NTV; ++nt) P[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+                    for (int nt = 0; nt < NTV; ++nt) P[m2][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-                    for (int mt = 0; mt < MT; ++mt)
+                    for (int m2 = 0; m2 < 2; ++m2)
 #pragma unroll
-                        for (int nt = 0; nt < NTV; ++nt) mma32(P[mt][nt], qf[mt][ks], stk[r][ks][nt]);
+                        for (int nt = 0; nt < NTV; ++nt) mma32(P[m2][nt], qf[m2][ks], stk[r][ks][nt]);
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
+                for (int m2 = 0; m2 < 2; ++m2) {
+                    const int mt = 2 * hf + m2;
                     const float4 w = *reinterpret_cast<const float4 *>(&S.W[p][16 * mt + 4 * lg]);
 #pragma unroll
                     for (int nt = 0; nt < NTV; ++nt) {
-                        Oi[mt][nt][0] += w.x * P[mt][nt][0];
-                        Oi[mt][nt][1] += w.y * P[mt][nt][1];
-                        Oi[mt][nt][2] += w.z * P[mt][nt][2];
-                        Oi[mt][nt][3] += w.w * P[mt][nt][3];
-                    }
-                }
-            }
-            if (act >= 0 && wave < KS) {
-                // d_k rows 32w..32w+31 of the active state live in wave w
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
-                    Frag<_Float16> qa;
-                    load_frag(qa, X.qf[mt][wave][lane]);
-                    const float4 w = *reinterpret_cast<const float4 *>(&S.wact[wave][16 * mt + 4 * lg]);
-#pragma unroll
-                    for (int nt = 0; nt < NTV; ++nt) {
-                        floatx4 P = floatx4{0.f, 0.f, 0.f, 0.f};
-                        mma32(P, qa, af[nt]);
-                        Oi[mt][nt][0] += w.x * P[0];
-                        Oi[mt][nt][1] += w.y * P[1];
-                        Oi[mt][nt][2] += w.z * P[2];
-                        Oi[mt][nt][3] += w.w * P[3];
+                        Oi[mt][nt][0] += w.x * P[m2][nt][0];
+                        Oi[mt][nt][1] += w.y * P[m2][nt][1];
+                        Oi[mt][nt][2] += w.z * P[m2][nt][2];
+                        Oi[mt][nt][3] += w.w * P[m2][nt][3];
                     }
                 }
             }
         }
+    }
+    if (c.act >= 0 && act_wave) {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int nt = 0; nt < NTV; ++nt) S.ored[wave][mt][nt][lane] = Oi[mt][nt];
-        lds_barrier();
-        // ---- reduce the waves' partial reads, add P V (wave w: rows 16w..16w+15)
-        {
-            const int w = wave;
+        for (int mt = 0; mt < MT; ++mt) {
+            Frag<_Float16> qa;
+            load_frag(qa, X.qf[mt][kb][lane]);
+            const float4 w = *reinterpret_cast<const float4 *>(&S.wact[kb][16 * mt + 4 * lg]);
 #pragma unroll
             for (int nt = 0; nt < NTV; ++nt) {
-                const floatx4 a = S.ored[0][w][nt][lane], b = S.ored[1][w][nt][lane];
-                const floatx4 c = S.ored[2][w][nt][lane], d = S.ored[3][w][nt][lane];
-                Oprev[nt] = (a + b) + (c + d);
+                floatx4 P = floatx4{0.f, 0.f, 0.f, 0.f};
+                mma32(P, qa, af[nt]);
+                Oi[mt][nt][0] += w.x * P[0];
+                Oi[mt][nt][1] += w.y * P[1];
+                Oi[mt][nt][2] += w.z * P[2];
+                Oi[mt][nt][3] += w.w * P[3];
             }
+        }
+    }
 #pragma unroll
-            for (int ks = 0; ks < kChunk / 32; ++ks) {
-                if (32 * ks <= 16 * w + 15) {
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NTV; ++nt) S.ored[wave][mt][nt][lane] = Oi[mt][nt];
+    lds_barrier();
+    // ---- reducing waves: sum the partial reads of rows 16 w .., add P V
+    if (wave < MT) {
+        const int w = wave;
+#pragma unroll
+        for (int nt = 0; nt < NTV; ++nt) {
+            floatx4 sum = S.ored[0][w][nt][lane];
+#pragma unroll
+            for (int u = 1; u < NW; ++u) sum += S.ored[u][w][nt][lane];
+            Oprev[nt] = sum;
+        }
+#pragma unroll
+        for (int ks = 0; ks < kChunk / 32; ++ks) {
+            if (32 * ks <= 16 * w + 15) {
+                Frag<__bf16> a;
+                load_frag(a, X.pwf[w][ks][lane]);
+#pragma unroll
+                for (int nt = 0; nt < NTV; ++nt) {
+                    Frag<__bf16> b;
+                    load_frag(b, &S.vt[16 * nt + lr][32 * ks + 8 * lg]);
+                    mma32(Oprev[nt], a, b);
+                }
+            }
+        }
+    }
+    c.prev_c0 = c0;
+    c.prev_nvalid = nvalid;
+
+    // ---- chunk-end update
+    if (!has_ev) {
+        // every token of the chunk joins the active state: V_c^T K_c into its registers
+        if (act_wave) {
+#pragma unroll
+            for (int kk = 0; kk < kChunk / 32; ++kk)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
                     Frag<__bf16> a;
-                    load_frag(a, X.pwf[w][ks][lane]);
+                    load_frag(a, X.ktf[2 * kb + h][kk][lane]);
 #pragma unroll
                     for (int nt = 0; nt < NTV; ++nt) {
                         Frag<__bf16> b;
-                        load_frag(b, &S.vt[16 * nt + lr][32 * ks + 8 * lg]);
-                        mma32(Oprev[nt], a, b);
+                        load_frag(b, &S.vt[16 * nt + lr][32 * kk + 8 * lg]);
+                        mma32(am[nt][h], a, b);
                     }
                 }
-            }
-            prev_c0 = c0;
-            prev_nvalid = nvalid;
+            c.ea = refresh_active<NTV>(am, af);
         }
+        return;
+    }
 
-        // ---- chunk-end update
-        if (!has_ev) {
-            // every token of the chunk joins the active state: V_c^T K_c into its registers
-            if (wave < KS) {
-#pragma unroll
-                for (int kk = 0; kk < kChunk / 32; ++kk)
-#pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        Frag<__bf16> a;
-                        load_frag(a, X.ktf[2 * wave + h][kk][lane]);
-#pragma unroll
-                        for (int nt = 0; nt < NTV; ++nt) {
-                            Frag<__bf16> b;
-                            load_frag(b, &S.vt[16 * nt + lr][32 * kk + 8 * lg]);
-                            mma32(am[nt][h], a, b);
-                        }
-                    }
-                ea = refresh_active<NTV>(am, af);
+    // chunk with events: general update in the fp32 cache
+    const int m0 = c.m0, act = c.act;
+    if (tid == 0) {
+        const int tl = nvalid - 1;
+        const uint64_t oa = S.om[tl], na = S.nm[tl];
+        uint64_t used = 0;
+        int nold = 0, last_old = -1, nmg = 0, tgt = -1;
+        for (int i = 0; i < m0; ++i) {
+            if ((oa >> i) & 1ull) {
+                S.new_order[nold++] = S.order[i];
+                used |= 1ull << S.order[i];
+                last_old = i;
+                tgt = i;
+            } else if (tgt >= 0) {
+                S.merge_dst[nmg] = S.order[tgt];
+                S.merge_src[nmg] = S.order[i];
+                ++nmg;
             }
-            return;
         }
-
-        // chunk with events: general update in the fp32 cache
-        if (tid == 0) {
-            const int tl = nvalid - 1;
-            const uint64_t oa = S.om[tl], na = S.nm[tl];
-            uint64_t used = 0;
-            int nold = 0, last_old = -1, nmg = 0, tgt = -1;
-            for (int i = 0; i < m0; ++i) {
-                if ((oa >> i) & 1ull) {
-                    S.new_order[nold++] = S.order[i];
-                    used |= 1ull << S.order[i];
-                    last_old = i;
-                    tgt = i;
-                } else if (tgt >= 0) {
-                    S.merge_dst[nmg] = S.order[tgt];
-                    S.merge_src[nmg] = S.order[i];
-                    ++nmg;
+        int ng = 0, mnew = nold, nch = 0;
+        for (int i = 0; i < nmg; ++i) S.changed[nch++] = S.merge_dst[i];
+        const int first_new = na ? __ffsll(static_cast<unsigned long long>(na)) - 1 : nvalid;
+        if (first_new > 0 && last_old >= 0) {
+            S.grp_lo[ng] = 0; S.grp_hi[ng] = first_new;
+            S.grp_slot[ng] = S.order[last_old]; S.grp_add[ng] = 1;
+            S.changed[nch++] = S.order[last_old];
+            ++ng;
+        }
+        uint64_t rest = na;
+        while (rest) {
+            const int p = __ffsll(static_cast<unsigned long long>(rest)) - 1;
+            rest &= rest - 1;
+            const int q = rest ? __ffsll(static_cast<unsigned long long>(rest)) - 1 : nvalid;
+            const int slot = __ffsll(static_cast<unsigned long long>(~used)) - 1;
+            if (slot < 0 || slot >= C) break;   // cannot happen: at most C states live
+            used |= 1ull << slot;
+            S.new_order[mnew++] = slot;
+            S.grp_lo[ng] = p; S.grp_hi[ng] = q; S.grp_slot[ng] = slot; S.grp_add[ng] = 0;
+            S.changed[nch++] = slot;
+            ++ng;
+        }
+        const int an = mnew > 0 ? S.new_order[mnew - 1] : -1;
+        // the previous active state, if it is now closed, needs an operand copy
+        if (act >= 0 && m0 > 0 && ((oa >> (m0 - 1)) & 1ull) && act != an) S.changed[nch++] = act;
+        S.n_merge = nmg;
+        S.n_grp = ng;
+        S.n_changed = nch;
+        S.m_new = mnew;
+        S.act_new = an;
+    }
+    // flush the active state's accumulators to its fp32 state in the cache
+    if (act >= 0 && act_wave) {
+        float *dst = st_base + act * slot_stride;
+#pragma unroll
+        for (int nt = 0; nt < NTV; ++nt)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                *reinterpret_cast<float4 *>(dst + (16 * nt + lr) * DK + 32 * kb + 16 * h + 4 * lg) =
+                    make_float4(am[nt][h][0], am[nt][h][1], am[nt][h][2], am[nt][h][3]);
+    }
+    __syncthreads();
+    for (int g = 0; g < S.n_merge; ++g) {
+        float4 *dst = reinterpret_cast<float4 *>(st_base + S.merge_dst[g] * slot_stride);
+        const float4 *src = reinterpret_cast<const float4 *>(st_base + S.merge_src[g] * slot_stride);
+        for (int idx = tid; idx < DVT * DK / 4; idx += NT) {
+            float4 a = dst[idx];
+            const float4 b = src[idx];
+            a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+            dst[idx] = a;
+        }
+    }
+    __syncthreads();
+    for (int g = 0; g < S.n_grp; ++g) {
+        const int lo = S.grp_lo[g], hi = S.grp_hi[g];
+        float *dst = st_base + S.grp_slot[g] * slot_stride;
+        const bool add = S.grp_add[g] != 0;
+        for (int tile = wave; tile < NTV * (DK / 16); tile += NW) {
+            const int mt = tile % NTV, nt = tile / NTV;
+            floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < kChunk / 32; ++ks) {
+                const int base = 32 * ks + 8 * lg;
+                if (32 * ks < hi && 32 * ks + 32 > lo) {
+                    Frag<__bf16> a, b;
+                    load_frag(a, &S.vt[16 * mt + lr][base]);
+                    mask_frag(a, base, lo, hi);
+                    load_frag(b, X.ktf[nt][ks][lane]);
+                    mma32(acc, a, b);
                 }
             }
-            int ng = 0, mnew = nold, nch = 0;
-            for (int i = 0; i < nmg; ++i) S.changed[nch++] = S.merge_dst[i];
-            const int first_new = na ? __ffsll(static_cast<unsigned long long>(na)) - 1 : nvalid;
-            if (first_new > 0 && last_old >= 0) {
-                S.grp_lo[ng] = 0; S.grp_hi[ng] = first_new;
-                S.grp_slot[ng] = S.order[last_old]; S.grp_add[ng] = 1;
-                S.changed[nch++] = S.order[last_old];
-                ++ng;
-            }
-            uint64_t rest = na;
-            while (rest) {
-                const int p = __ffsll(static_cast<unsigned long long>(rest)) - 1;
-                rest &= rest - 1;
-                const int q = rest ? __ffsll(static_cast<unsigned long long>(rest)) - 1 : nvalid;
-                const int slot = __ffsll(static_cast<unsigned long long>(~used)) - 1;
-                if (slot < 0 || slot >= C) break;   // cannot happen: at most C states live
-                used |= 1ull << slot;
-                S.new_order[mnew++] = slot;
-                S.grp_lo[ng] = p; S.grp_hi[ng] = q; S.grp_slot[ng] = slot; S.grp_add[ng] = 0;
-                S.changed[nch++] = slot;
-                ++ng;
-            }
-            const int an = mnew > 0 ? S.new_order[mnew - 1] : -1;
-            // the previous active state, if it is now closed, needs an operand copy
-            if (act >= 0 && m0 > 0 && ((oa >> (m0 - 1)) & 1ull) && act != an) S.changed[nch++] = act;
-            S.n_merge = nmg;
-            S.n_grp = ng;
-            S.n_changed = nch;
-            S.m_new = mnew;
-            S.act_new = an;
-        }
-        // flush the active state's accumulators to its fp32 state in the cache
-        if (act >= 0 && wave < KS) {
-            float *dst = st_base + act * slot_stride;
 #pragma unroll
-            for (int nt = 0; nt < NTV; ++nt)
-#pragma unroll
-                for (int h = 0; h < 2; ++h)
-                    *reinterpret_cast<float4 *>(dst + (16 * nt + lr) * DK + 32 * wave + 16 * h + 4 * lg) =
-                        make_float4(am[nt][h][0], am[nt][h][1], am[nt][h][2], am[nt][h][3]);
+            for (int r = 0; r < 4; ++r) {
+                float *p = dst + (16 * mt + 4 * lg + r) * DK + 16 * nt + lr;
+                *p = add ? (*p + acc[r]) : acc[r];
+            }
         }
+    }
+    __syncthreads();
+    const int an = S.act_new;
+    // normalised fp16 copies of the changed closed states
+    for (int cc = 0; cc < S.n_changed; ++cc) {
+        const int slot = S.changed[cc];
+        if (slot == an) continue;
+        const float4 *src = reinterpret_cast<const float4 *>(st_base + slot * slot_stride);
+        float mx = 0.0f;
+        for (int idx = tid; idx < DVT * DK / 4; idx += NT) {
+            const float4 a = src[idx];
+            mx = fmaxf(mx, fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))));
+        }
+        mx = wave_max(mx);
         __syncthreads();
-        for (int g = 0; g < S.n_merge; ++g) {
-            float4 *dst = reinterpret_cast<float4 *>(st_base + S.merge_dst[g] * slot_stride);
-            const float4 *src = reinterpret_cast<const float4 *>(st_base + S.merge_src[g] * slot_stride);
-            for (int idx = tid; idx < DVT * DK / 4; idx += 256) {
-                float4 a = dst[idx];
-                const float4 b = src[idx];
-                a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
-                dst[idx] = a;
-            }
-        }
+        if (lane == 0) S.red[wave] = mx;
         __syncthreads();
-        for (int g = 0; g < S.n_grp; ++g) {
-            const int lo = S.grp_lo[g], hi = S.grp_hi[g];
-            float *dst = st_base + S.grp_slot[g] * slot_stride;
-            const bool add = S.grp_add[g] != 0;
-            for (int tile = wave; tile < NTV * (DK / 16); tile += 4) {
-                const int mt = tile % NTV, nt = tile / NTV;
-                floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+        float all = S.red[0];
 #pragma unroll
-                for (int ks = 0; ks < kChunk / 32; ++ks) {
-                    const int base = 32 * ks + 8 * lg;
-                    if (32 * ks < hi && 32 * ks + 32 > lo) {
-                        Frag<__bf16> a, b;
-                        load_frag(a, &S.vt[16 * mt + lr][base]);
-                        mask_frag(a, base, lo, hi);
-                        load_frag(b, X.ktf[nt][ks][lane]);
-                        mma32(acc, a, b);
-                    }
-                }
+        for (int u = 1; u < NW; ++u) all = fmaxf(all, S.red[u]);
+        const int e = f16_exponent(all);
+        _Float16 *dst = sh_base + slot * slot_stride;
+        for (int idx = tid; idx < DVT * DK / 8; idx += NT) {
+            const float4 a = src[2 * idx];
+            const float4 b = src[2 * idx + 1];
+            f16x8 o;
+            o[0] = static_cast<_Float16>(ldexpf(a.x, -e)); o[1] = static_cast<_Float16>(ldexpf(a.y, -e));
+            o[2] = static_cast<_Float16>(ldexpf(a.z, -e)); o[3] = static_cast<_Float16>(ldexpf(a.w, -e));
+            o[4] = static_cast<_Float16>(ldexpf(b.x, -e)); o[5] = static_cast<_Float16>(ldexpf(b.y, -e));
+            o[6] = static_cast<_Float16>(ldexpf(b.z, -e)); o[7] = static_cast<_Float16>(ldexpf(b.w, -e));
+            reinterpret_cast<f16x8 *>(dst)[idx] = o;
+        }
+        if (tid == 0) S.shexp[slot] = e;
+    }
+    __syncthreads();
+    // owner waves reload the register copies of the changed closed states
+    for (int cc = 0; cc < S.n_changed; ++cc) {
+        const int slot = S.changed[cc];
+        if (slot == an || (slot % NW) != wave) continue;
+        const _Float16 *src = sh_base + slot * slot_stride;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    float *p = dst + (16 * mt + 4 * lg + r) * DK + 16 * nt + lr;
-                    *p = add ? (*p + acc[r]) : acc[r];
-                }
+        for (int r = 0; r < SPW; ++r) {
+            if (slot / NW == r) {
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                    for (int nt = 0; nt < NTV; ++nt)
+                        perm_frag_f16(stk[r][ks][nt], src + (16 * nt + lr) * DK, 32 * ks + 4 * lg);
             }
         }
-        __syncthreads();
-        const int an = S.act_new;
-        // normalised fp16 copies of the changed closed states
-        for (int c = 0; c < S.n_changed; ++c) {
-            const int slot = S.changed[c];
-            if (slot == an) continue;
-            const float4 *src = reinterpret_cast<const float4 *>(st_base + slot * slot_stride);
-            float mx = 0.0f;
-            for (int idx = tid; idx < DVT * DK / 4; idx += 256) {
-                const float4 a = src[idx];
-                mx = fmaxf(mx, fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))));
+    }
+    // the new active state into the accumulators
+    if (an >= 0 && act_wave) {
+        const float *src = st_base + an * slot_stride;
+#pragma unroll
+        for (int nt = 0; nt < NTV; ++nt)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const float4 a = *reinterpret_cast<const float4 *>(src + (16 * nt + lr) * DK + 32 * kb + 16 * h +
+                                                                  4 * lg);
+                am[nt][h] = floatx4{a.x, a.y, a.z, a.w};
             }
-            mx = wave_max(mx);
-            __syncthreads();
-            if (lane == 0) S.red[wave] = mx;
-            __syncthreads();
-            const int e = f16_exponent(fmaxf(fmaxf(S.red[0], S.red[1]), fmaxf(S.red[2], S.red[3])));
-            _Float16 *dst = sh_base + slot * slot_stride;
-            for (int idx = tid; idx < DVT * DK / 8; idx += 256) {
-                const float4 a = src[2 * idx];
-                const float4 b = src[2 * idx + 1];
-                f16x8 o;
-                o[0] = static_cast<_Float16>(ldexpf(a.x, -e)); o[1] = static_cast<_Float16>(ldexpf(a.y, -e));
-                o[2] = static_cast<_Float16>(ldexpf(a.z, -e)); o[3] = static_cast<_Float16>(ldexpf(a.w, -e));
-                o[4] = static_cast<_Float16>(ldexpf(b.x, -e)); o[5] = static_cast<_Float16>(ldexpf(b.y, -e));
-                o[6] = static_cast<_Float16>(ldexpf(b.z, -e)); o[7] = static_cast<_Float16>(ldexpf(b.w, -e));
-                reinterpret_cast<f16x8 *>(dst)[idx] = o;
-            }
-            if (tid == 0) S.shexp[slot] = e;
-        }
-        __syncthreads();
-        // owner waves reload the register copies of the changed closed states
-        for (int c = 0; c < S.n_changed; ++c) {
-            const int slot = S.changed[c];
-            if (slot == an || (slot & 3) != wave) continue;
-            const _Float16 *src = sh_base + slot * slot_stride;
-#pragma unroll
-            for (int r = 0; r < SPW; ++r) {
-                if ((slot >> 2) == r) {
-#pragma unroll
-                    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-                        for (int nt = 0; nt < NTV; ++nt)
-                            perm_frag_f16(stk[r][ks][nt], src + (16 * nt + lr) * DK, 32 * ks + 4 * lg);
-                }
-            }
-        }
-        // the new active state into the accumulators
-        if (an >= 0 && wave < KS) {
-            const float *src = st_base + an * slot_stride;
-#pragma unroll
-            for (int nt = 0; nt < NTV; ++nt)
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const float4 a = *reinterpret_cast<const float4 *>(src + (16 * nt + lr) * DK + 32 * wave +
-                                                                      16 * h + 4 * lg);
-                    am[nt][h] = floatx4{a.x, a.y, a.z, a.w};
-                }
-            ea = refresh_active<NTV>(am, af);
-        }
-        const int mnew = S.m_new;
-        uint32_t cl = 0;
-        for (int i = 0; i + 1 < mnew; ++i) cl |= 1u << S.new_order[i];
-        __syncthreads();
-        if (tid < kMaxC) S.order[tid] = tid < mnew ? S.new_order[tid] : 0;
-        if (tid < mnew) S.inv[S.new_order[tid]] = tid;
-        m0 = mnew;
-        act = an;
-        closed = cl;
-        refresh_w = true;
+        c.ea = refresh_active<NTV>(am, af);
+    }
+    const int mnew = S.m_new;
+    uint32_t cl = 0;
+    for (int i = 0; i + 1 < mnew; ++i) cl |= 1u << S.new_order[i];
+    __syncthreads();
+    if (tid < kMaxC) S.order[tid] = tid < mnew ? S.new_order[tid] : 0;
+    if (tid < mnew) S.inv[S.new_order[tid]] = tid;
+    c.m0 = mnew;
+    c.act = an;
+    c.closed = cl;
+    c.refresh_w = true;
 }
 
 template <int DK, int DVT, int SPW>
-__global__ __launch_bounds__(256, 1) void k_prefill_rs(
+__global__ __launch_bounds__(kRsThreads, 1) void k_prefill_rs(
     const __bf16 *__restrict__ V, __bf16 *__restrict__ O, int T, int C, int DV, int nblk_dv,
     float *__restrict__ states, _Float16 *__restrict__ shadow, const int2 *__restrict__ events,
     const int32_t *__restrict__ chunk_ev, const _Float16 *__restrict__ q16f, const int32_t *__restrict__ qexp_g,
@@ -763,9 +789,9 @@ __global__ __launch_bounds__(256, 1) void k_prefill_rs(
 {
     constexpr int KS = DK / 32;
     constexpr int NTV = DVT / 16;
-    constexpr int CMAX = 4 * SPW;
-    static_assert(KS <= 4, "the active state gives each wave at most one 32-row block of d_k");
-    static_assert(DVT <= 32, "one 16-byte V piece per thread covers at most 32 columns");
+    constexpr int CMAX = kRsWaves * SPW;
+    static_assert(KS <= kRsWaves - kRsActWave0, "one wave per 32-row block of the active state");
+    static_assert(kChunk * DVT / 8 <= kRsThreads, "one 16-byte V piece per thread");
     __shared__ RsStage<DK, CMAX> st0, st1;        // chunk ch in st0 when ch is even
     __shared__ RsSmem<DK, DVT, CMAX> S;
 
@@ -788,6 +814,8 @@ __global__ __launch_bounds__(256, 1) void k_prefill_rs(
     A.vr = A.tid & (kChunk - 1);
     A.vc = (A.tid / kChunk) * 8;
     A.v_mover = A.tid < kChunk * DVT / 8;
+    A.v_off = 2u * static_cast<uint32_t>(A.vr * DV + A.vc);
+    A.o_off = 2u * static_cast<uint32_t>((16 * (A.wave & 3) + 4 * A.lg) * DV + A.lr);
     A.tok0 = static_cast<size_t>(A.bh) * T;
     A.slot_stride = static_cast<size_t>(DV) * DK;
     A.st_base = states + static_cast<size_t>(A.bh) * C * DV * DK + static_cast<size_t>(A.dv0) * DK;
@@ -836,34 +864,33 @@ __global__ __launch_bounds__(256, 1) void k_prefill_rs(
         if (ch + 1 < NCH) rs_chunk<DK, DVT, SPW>(ch + 1, st1, st0, S, A, c);
     }
 
-    const size_t tok0 = A.tok0, slot_stride = A.slot_stride;
-    const int dv0 = A.dv0, bh = A.bh;
-    float *st_base = A.st_base;
-    const int prev_c0 = c.prev_c0, prev_nvalid = c.prev_nvalid, act = c.act, m0 = c.m0;
-    auto &Oprev = c.Oprev;
-    auto &am = c.am;
+    // the last chunk's outputs
+    const size_t tok0 = A.tok0;
+    if (wave < kChunk / 16) {
 #pragma unroll
-    for (int nt = 0; nt < NTV; ++nt)
+        for (int nt = 0; nt < NTV; ++nt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = 16 * wave + 4 * lg + r;
-            if (t < prev_nvalid)
-                O[(tok0 + prev_c0 + t) * DV + dv0 + 16 * nt + lr] = static_cast<__bf16>(Oprev[nt][r]);
-        }
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * wave + 4 * lg + r;
+                if (t < c.prev_nvalid)
+                    O[(tok0 + c.prev_c0 + t) * DV + A.dv0 + 16 * nt + lr] = static_cast<__bf16>(c.Oprev[nt][r]);
+            }
+    }
     // the active state's accumulators are the last state of the final cache
-    if (act >= 0 && wave < KS) {
-        float *dst = st_base + act * slot_stride;
+    const int kb = wave - kRsActWave0;
+    if (c.act >= 0 && kb >= 0 && kb < KS) {
+        float *dst = A.st_base + c.act * A.slot_stride;
 #pragma unroll
         for (int nt = 0; nt < NTV; ++nt)
 #pragma unroll
             for (int h = 0; h < 2; ++h)
-                *reinterpret_cast<float4 *>(dst + (16 * nt + lr) * DK + 32 * wave + 16 * h + 4 * lg) =
-                    make_float4(am[nt][h][0], am[nt][h][1], am[nt][h][2], am[nt][h][3]);
+                *reinterpret_cast<float4 *>(dst + (16 * nt + lr) * DK + 32 * kb + 16 * h + 4 * lg) =
+                    make_float4(c.am[nt][h][0], c.am[nt][h][1], c.am[nt][h][2], c.am[nt][h][3]);
     }
     __syncthreads();
-    if (dv0 == 0 && tid < kMaxC) {
-        uint8_t *order = meta_base + static_cast<size_t>(bh) * meta_stride + kOffOrder;
-        order[tid] = static_cast<uint8_t>(tid < m0 ? S.order[tid] : 0xFF);
+    if (A.dv0 == 0 && tid < kMaxC) {
+        uint8_t *order = meta_base + static_cast<size_t>(A.bh) * meta_stride + kOffOrder;
+        order[tid] = static_cast<uint8_t>(tid < c.m0 ? S.order[tid] : 0xFF);
     }
 }
 
@@ -884,7 +911,7 @@ static hipError_t launch_rs(const PrefillArgs &a, hipStream_t stream)
         hipError_t e = hipEventRecord(a.ev_before, stream);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((k_prefill_rs<DK, DVT, SPW>), dim3(BH * nblk_dv), dim3(256), 0, stream,
+    hipLaunchKernelGGL((k_prefill_rs<DK, DVT, SPW>), dim3(BH * nblk_dv), dim3(kRsThreads), 0, stream,
                        static_cast<const __bf16 *>(a.v), static_cast<__bf16 *>(a.o), a.T, a.g.C, a.g.dv,
                        nblk_dv, a.states, static_cast<_Float16 *>(a.ws.shadow), a.ws.events, a.ws.chunk_ev,
                        static_cast<const _Float16 *>(a.ws.q16f), a.ws.qexp, a.ws.lamT,
@@ -895,37 +922,28 @@ static hipError_t launch_rs(const PrefillArgs &a, hipStream_t stream)
     return e;
 }
 
-// Register budget: with d_k = 128 and more than 16 states the stack of a
-// 32-column slice does not fit beside the working set (the compiler spills),
-// so that case always uses 16-column slices.
-int prefill_rs_dvt(int dk, int C, int dvt_wanted) { return (dk == 128 && C > 16) ? 16 : dvt_wanted; }
+// The register-resident sweep works on 16-column slices of d_v (8 waves, two
+// per SIMD, each holding C/8 states of the slice).
+int prefill_rs_dvt(int, int, int) { return 16; }
 
 hipError_t launch_prefill_rs(const PrefillArgs &a, hipStream_t stream)
 {
     const int C = a.g.C;
-    if (a.g.dk == 128) {
-        if (C > 16) return launch_rs<128, 16, 8>(a, stream);
-        if (a.dvt == 32) return C <= 8 ? launch_rs<128, 32, 2>(a, stream) : launch_rs<128, 32, 4>(a, stream);
-        return C <= 8 ? launch_rs<128, 16, 2>(a, stream) : launch_rs<128, 16, 4>(a, stream);
-    }
-    if (a.dvt == 32)
-        return C <= 8 ? launch_rs<64, 32, 2>(a, stream) : C <= 16 ? launch_rs<64, 32, 4>(a, stream)
-                                                                 : launch_rs<64, 32, 8>(a, stream);
-    return C <= 8 ? launch_rs<64, 16, 2>(a, stream) : C <= 16 ? launch_rs<64, 16, 4>(a, stream)
-                                                               : launch_rs<64, 16, 8>(a, stream);
+    if (a.g.dk == 128)
+        return C <= 8 ? launch_rs<128, 16, 1>(a, stream) : C <= 16 ? launch_rs<128, 16, 2>(a, stream)
+                                                               : launch_rs<128, 16, 4>(a, stream);
+    return C <= 8 ? launch_rs<64, 16, 1>(a, stream) : C <= 16 ? launch_rs<64, 16, 2>(a, stream)
+                                                             : launch_rs<64, 16, 4>(a, stream);
 }
 
 template <int DK, int DVT, int CMAX>
 constexpr size_t rs_lds_bytes() { return 2 * sizeof(RsStage<DK, CMAX>) + sizeof(RsSmem<DK, DVT, CMAX>); }
 
-size_t prefill_rs_smem_bytes(int dk, int dvt, int C)
+size_t prefill_rs_smem_bytes(int dk, int, int C)
 {
     const int cmax = C <= 8 ? 8 : (C <= 16 ? 16 : 32);
-    if (dk == 128) {
-        if (dvt == 32) return cmax == 8 ? rs_lds_bytes<128, 32, 8>() : cmax == 16 ? rs_lds_bytes<128, 32, 16>() : rs_lds_bytes<128, 32, 32>();
-        return cmax == 8 ? rs_lds_bytes<128, 16, 8>() : cmax == 16 ? rs_lds_bytes<128, 16, 16>() : rs_lds_bytes<128, 16, 32>();
-    }
-    if (dvt == 32) return cmax == 8 ? rs_lds_bytes<64, 32, 8>() : cmax == 16 ? rs_lds_bytes<64, 32, 16>() : rs_lds_bytes<64, 32, 32>();
+    if (dk == 128) return cmax == 8 ? rs_lds_bytes<128, 16, 8>() : cmax == 16 ? rs_lds_bytes<128, 16, 16>()
+                                                                             : rs_lds_bytes<128, 16, 32>();
     return cmax == 8 ? rs_lds_bytes<64, 16, 8>() : cmax == 16 ? rs_lds_bytes<64, 16, 16>() : rs_lds_bytes<64, 16, 32>();
 }
 

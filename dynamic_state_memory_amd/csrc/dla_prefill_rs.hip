@@ -295,20 +295,37 @@ __device__ __forceinline__ void stage_array(const u32x4 *src, u32x4 *dst, int ti
             load_to_lds16(at_bytes(src + kRsThreads * j, 16u * tid), dst + 64 * wave + kRsThreads * j);
 }
 
-// Issue the loads of chunk cb's operands into stage X.
+// Issue the loads of chunk cb's operands into stage X, in three groups so
+// that a caller can spread them over the chunk (the per-CU rate of these
+// loads is far below what a burst of all of them asks for): group 0 lam and
+// the weighted scores, groups 1 and 2 one half each of the query and key
+// fragments.
+template <int DK, int CMAX>
+__device__ __forceinline__ void stage_group(int grp, RsStage<DK, CMAX> &X, const _Float16 *q16f, const float *lamT,
+                                            const __bf16 *pwf, const __bf16 *ktf, size_t cb, int tid, int wave)
+{
+    constexpr int NQ = kChunk * DK * 2 / 16, NL = CMAX * kChunk * 4 / 16, NP = kChunk * kChunk * 2 / 16;
+    constexpr int NQ2 = NQ / 2;
+    if (grp == 0) {
+        stage_array<NL>(reinterpret_cast<const u32x4 *>(lamT) + cb * (kPrepCmax * kChunk * 4 / 16),
+                        reinterpret_cast<u32x4 *>(&X.lamT[0][0]), tid, wave);
+        stage_array<NP>(reinterpret_cast<const u32x4 *>(pwf) + cb * NP, reinterpret_cast<u32x4 *>(&X.pwf[0][0][0][0]),
+                        tid, wave);
+    } else {
+        const int h = (grp - 1) * NQ2;
+        stage_array<NQ2>(reinterpret_cast<const u32x4 *>(q16f) + cb * NQ + h,
+                         reinterpret_cast<u32x4 *>(&X.qf[0][0][0][0]) + h, tid, wave);
+        stage_array<NQ2>(reinterpret_cast<const u32x4 *>(ktf) + cb * NQ + h,
+                         reinterpret_cast<u32x4 *>(&X.ktf[0][0][0][0]) + h, tid, wave);
+    }
+}
+
 template <int DK, int CMAX>
 __device__ __forceinline__ void stage_chunk(RsStage<DK, CMAX> &X, const _Float16 *q16f, const float *lamT,
                                             const __bf16 *pwf, const __bf16 *ktf, size_t cb, int tid, int wave)
 {
-    constexpr int NQ = kChunk * DK * 2 / 16, NL = CMAX * kChunk * 4 / 16, NP = kChunk * kChunk * 2 / 16;
-    stage_array<NQ>(reinterpret_cast<const u32x4 *>(q16f) + cb * NQ, reinterpret_cast<u32x4 *>(&X.qf[0][0][0][0]),
-                    tid, wave);
-    stage_array<NL>(reinterpret_cast<const u32x4 *>(lamT) + cb * (kPrepCmax * kChunk * 4 / 16),
-                    reinterpret_cast<u32x4 *>(&X.lamT[0][0]), tid, wave);
-    stage_array<NP>(reinterpret_cast<const u32x4 *>(pwf) + cb * NP, reinterpret_cast<u32x4 *>(&X.pwf[0][0][0][0]),
-                    tid, wave);
-    stage_array<NQ>(reinterpret_cast<const u32x4 *>(ktf) + cb * NQ, reinterpret_cast<u32x4 *>(&X.ktf[0][0][0][0]),
-                    tid, wave);
+#pragma unroll
+    for (int g = 0; g < 3; ++g) stage_group<DK, CMAX>(g, X, q16f, lamT, pwf, ktf, cb, tid, wave);
 }
 
 // What one block carries from chunk to chunk (registers after inlining).
@@ -328,7 +345,8 @@ struct RsCarry {
     int2 evnext;                                 // next chunk's event of this thread
     int ea;                                      // exponent of this wave's active-state operand
     int m0, act;                                 // live states, the active state's slot (uniform)
-    int e0n, e1n, qexpn;                         // next chunk's event range and query exponent
+    int eA, eB, eC;                              // event offsets of chunks ch, ch + 1, ch + 2 (at chunk ch)
+    int qexpn;                                   // next chunk's query exponent
     int prev_c0, prev_nvalid;
     uint32_t closed;                             // physical slots of the closed states (uniform)
     bool refresh_w;
@@ -391,29 +409,31 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStage<DK, kRsWaves * SP
 
     const int c0 = ch * kChunk;
     const int nvalid = min(kChunk, T - c0);
-    const int nev = c.e1n - c.e0n;
+    const int nev = c.eB - c.eA;
     const bool has_ev = nev > 0;
     const int qexp = c.qexpn;
     const u32x4 vcur = c.vnext;
     const int2 evcur = c.evnext;
+    const bool more = ch + 1 < NCH;
+    const size_t cbn = static_cast<size_t>(bh) * NCH + ch + 1;
     // chunk ch's operands have landed (every wave's share) and every wave is
     // done with chunk ch - 1
     wait_vmem();
     __syncthreads();
-    // ---- chunk ch + 1: operands into the other stage, V and events into registers
-    if (ch + 1 < NCH) {
-        const size_t cbn = static_cast<size_t>(bh) * NCH + ch + 1;
-        stage_chunk<DK, CMAX>(Xn, A.q16f, A.lamT_g, A.pwf_g, A.ktf_g, cbn, tid, wave);
-        c.e0n = A.cev[ch + 1];
-        c.e1n = A.cev[ch + 2];
+    // ---- chunk ch + 1: first operand group into the other stage, V, events
+    // and the query exponent into registers (the event range is already known)
+    if (more) {
+        stage_group<DK, CMAX>(0, Xn, A.q16f, A.lamT_g, A.pwf_g, A.ktf_g, cbn, tid, wave);
         c.qexpn = A.qexp_g[cbn];
         const int c0n = c0 + kChunk;
         c.vnext = u32x4{0u, 0u, 0u, 0u};
         if (A.v_mover && vr < min(kChunk, T - c0n))
             c.vnext = *at_bytes(reinterpret_cast<const u32x4 *>(A.V + (tok0 + c0n) * DV + dv0), A.v_off);
         c.evnext = make_int2(0, 0);
-        if (tid < c.e1n - c.e0n) c.evnext = *at_bytes(A.events + tok0 + c.e0n, 8u * tid);
+        if (tid < c.eC - c.eB) c.evnext = *at_bytes(A.events + tok0 + c.eB, 8u * tid);
     }
+    // event offset of chunk ch + 3 (used two chunks from now)
+    const int eD = ch + 3 <= NCH ? A.cev[ch + 3] : c.eC;
     // ---- this chunk's V (transposed) and events into LDS
     if (A.v_mover) {
         const __bf16 *ve = reinterpret_cast<const __bf16 *>(&vcur);
@@ -465,24 +485,23 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStage<DK, kRsWaves * SP
         lds_barrier();
         // read weights per token: thread (wave, lane) fills the rows of the
         // wave's slots for token lane, so each wave reads only rows it wrote
+        // (a row of a slot without a closed state gets 0 and is never read)
+        const uint64_t om_t = S.om[lane], nm_t = S.nm[lane];
 #pragma unroll
         for (int r = 0; r < SPW; ++r) {
             const int p = NW * r + wave;
-            if ((c.closed >> p) & 1u) {
-                const int i = S.inv[p];
-                const int slot = __popcll(shr64(S.om[lane], i + 1)) + __popcll(S.nm[lane]);
-                S.W[p][lane] = ldexpf(X.lamT[slot][lane], S.shexp[p] + qexp);
-            }
+            const bool live = (c.closed >> p) & 1u;
+            const int slot = live ? __popcll(shr64(om_t, S.inv[p] + 1)) + __popcll(nm_t) : 0;
+            const float w = ldexpf(X.lamT[slot][lane], S.shexp[p] + qexp);
+            S.W[p][lane] = live ? w : 0.0f;
         }
         if (act_wave) S.wact[kb][lane] = ldexpf(X.lamT[__popcll(S.nm[lane])][lane], qexp + c.ea);
     } else {
         if (m_t_out && dv0 == 0 && tid < nvalid) m_t_out[tok0 + c0 + tid] = c.m0;
         // a closed state's slot is the same for every token of the chunk
+        // (wsc is 0 for a slot without a closed state)
 #pragma unroll
-        for (int r = 0; r < SPW; ++r) {
-            const int p = NW * r + wave;
-            if ((c.closed >> p) & 1u) S.W[p][lane] = X.lamT[c.jrow[r]][lane] * (c.wsc[r] * qsc);
-        }
+        for (int r = 0; r < SPW; ++r) S.W[NW * r + wave][lane] = X.lamT[c.jrow[r]][lane] * (c.wsc[r] * qsc);
         if (act_wave) S.wact[kb][lane] = X.lamT[0][lane] * ldexpf(qsc, c.ea);
     }
 
@@ -495,11 +514,13 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStage<DK, kRsWaves * SP
     uint32_t mine = 0;          // which of the wave's slots hold a closed state (uniform)
 #pragma unroll
     for (int r = 0; r < SPW; ++r) mine |= ((c.closed >> (NW * r + wave)) & 1u) << r;
-    if (mine != 0u) {
-        // two halves of the chunk's tokens (row tiles 2 hf, 2 hf + 1) keep
-        // half of the query fragments live at a time
+    // two halves of the chunk's tokens (row tiles 2 hf, 2 hf + 1) keep half of
+    // the query fragments live at a time; each half first issues one more
+    // group of the next chunk's operand loads
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
+    for (int hf = 0; hf < 2; ++hf) {
+        if (more) stage_group<DK, CMAX>(1 + hf, Xn, A.q16f, A.lamT_g, A.pwf_g, A.ktf_g, cbn, tid, wave);
+        if (mine != 0u) {
             Frag<_Float16> qf[2][KS];
 #pragma unroll
             for (int m2 = 0; m2 < 2; ++m2)
@@ -604,6 +625,9 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStage<DK, kRsWaves * SP
                 }
             c.ea = refresh_active<NTV>(am, af);
         }
+        c.eA = c.eB;
+        c.eB = c.eC;
+        c.eC = eD;
         return;
     }
 
@@ -777,6 +801,9 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStage<DK, kRsWaves * SP
     c.act = an;
     c.closed = cl;
     c.refresh_w = true;
+    c.eA = c.eB;
+    c.eB = c.eC;
+    c.eC = eD;
 }
 
 template <int DK, int DVT, int SPW>
@@ -853,11 +880,12 @@ __global__ __launch_bounds__(kRsThreads, 1) void k_prefill_rs(
     c.vnext = u32x4{0u, 0u, 0u, 0u};
     if (A.v_mover && A.vr < min(kChunk, T))
         c.vnext = *reinterpret_cast<const u32x4 *>(V + (A.tok0 + A.vr) * DV + A.dv0 + A.vc);
-    c.e0n = A.cev[0];
-    c.e1n = A.cev[1];
+    c.eA = A.cev[0];
+    c.eB = A.cev[1];
+    c.eC = NCH >= 2 ? A.cev[2] : c.eB;
     c.qexpn = qexp_g[static_cast<size_t>(A.bh) * NCH];
     c.evnext = make_int2(0, 0);
-    if (tid < c.e1n - c.e0n) c.evnext = events[A.tok0 + c.e0n + tid];
+    if (tid < c.eB - c.eA) c.evnext = events[A.tok0 + c.eA + tid];
 
     for (int ch = 0; ch < NCH; ch += 2) {
         rs_chunk<DK, DVT, SPW>(ch, st0, st1, S, A, c);

@@ -50,7 +50,7 @@ dla_status check_shape(int32_t B, int32_t H, int32_t C, int32_t dk, int32_t dv)
 
 struct Sizes {
     uint64_t s, qs, flag, tile_cnt, tile_sum, seg_t, seg_P, seg_q0, nseg, events, chunk_ev, shadow;
-    uint64_t q16f, qexp, lamT, pwf, ktf;
+    uint64_t rec, qexp;
     uint64_t total;
 };
 
@@ -71,13 +71,10 @@ Sizes workspace_sizes(int64_t BH, int64_t T, int64_t C, int64_t dk, int64_t dv)
     z.events = align_up(8ull * BH * T, 256);
     z.chunk_ev = align_up(4ull * BH * (NCH + 1), 256);
     z.shadow = align_up(2ull * BH * C * dv * dk, 256);
-    z.q16f = align_up(2ull * BH * NCH * kChunk * dk, 256);
+    z.rec = align_up(static_cast<uint64_t>(BH) * NCH * rs_record_bytes(dk), 256);
     z.qexp = align_up(4ull * BH * NCH, 256);
-    z.lamT = align_up(4ull * BH * NCH * kPrepCmax * kChunk, 256);
-    z.pwf = align_up(2ull * BH * NCH * kChunk * kChunk, 256);
-    z.ktf = align_up(2ull * BH * NCH * kChunk * dk, 256);
     z.total = z.s + z.qs + z.flag + z.tile_cnt + z.tile_sum + z.seg_t + z.seg_P + z.seg_q0 + z.nseg +
-              z.events + z.chunk_ev + z.shadow + z.q16f + z.qexp + z.lamT + z.pwf + z.ktf;
+              z.events + z.chunk_ev + z.shadow + z.rec + z.qexp;
     return z;
 }
 
@@ -97,11 +94,9 @@ Workspace carve(void *base, const Sizes &z)
     w.events = reinterpret_cast<int2 *>(p); p += z.events;
     w.chunk_ev = reinterpret_cast<int32_t *>(p); p += z.chunk_ev;
     w.shadow = p; p += z.shadow;
-    w.q16f = p; p += z.q16f;
+    w.rec = p; p += z.rec;
     w.qexp = reinterpret_cast<int32_t *>(p); p += z.qexp;
-    w.lamT = reinterpret_cast<float *>(p); p += z.lamT;
-    w.pwf = p; p += z.pwf;
-    w.ktf = p;
+    (void)p;
     return w;
 }
 
@@ -164,7 +159,7 @@ PrefillPlan plan_prefill(bool io_bf16, int64_t BH, int C, int dk, int dv)
     if (p.register_resident) {
         p.dvt = prefill_rs_dvt(dk, C, p.dvt);
         p.lds = prefill_rs_smem_bytes(dk, p.dvt, C);
-        const int spw = C <= 8 ? 1 : C <= 16 ? 2 : 4;   // states per wave (8 waves)
+        const int spw = C <= 8 ? 2 : C <= 16 ? 4 : 8;   // states per wave (4 waves)
         std::snprintf(p.name, sizeof(p.name), "k_prefill_rs<%d,%d,%d>", dk, p.dvt, spw);
     } else {
         p.lds = prefill_smem_bytes(io_bf16, dk, p.dvt);

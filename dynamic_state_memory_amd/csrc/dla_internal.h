@@ -66,13 +66,20 @@ struct Workspace {
     int32_t *chunk_ev;   // [BH][NCH+1] first event of each chunk
     void *shadow;        // [BH][C][dv][dk] fp16 copy of the states (bf16 io)
     // per-chunk operands built by the chunk pre-pass (register-resident path)
-    void *q16f;          // [BH][NCH][4][DK/32][64][8] fp16 query fragments
+    // [BH][NCH] chunk records of the register-resident prefill, each
+    // rs_record_bytes(d_k) long: fp16 query fragments [4][DK/32][64][8],
+    // bf16 lam [32][64] (slot-major), bf16 fragments of (Q K^T) o W
+    // [4][2][64][8], bf16 fragments of K^T [DK/16][2][64][8]
+    void *rec;
     int32_t *qexp;       // [BH][NCH] power-of-two exponent of each chunk's fp16 query
-    float *lamT;         // [BH][NCH][CMAX][64] lam of the chunk, slot-major
-    void *pwf;           // [BH][NCH][4][2][64][8] bf16 fragments of (Q K^T) o W
-    void *ktf;           // [BH][NCH][DK/16][2][64][8] bf16 fragments of K^T
 };
 constexpr int kPrepCmax = 32;   // lam slots kept per chunk by the pre-pass
+// chunk record of the register-resident prefill: query fragments, lam,
+// weighted-score fragments, key fragments (bytes; each part a multiple of 16)
+constexpr size_t rs_rec_q_bytes(int dk) { return 2ull * 64 * dk; }
+constexpr size_t rs_rec_a_bytes(int dk) { return rs_rec_q_bytes(dk) + 2ull * 32 * 64; }
+constexpr size_t rs_rec_b_bytes(int dk) { return 2ull * 64 * 64 + 2ull * 64 * dk; }
+constexpr size_t rs_record_bytes(int dk) { return rs_rec_a_bytes(dk) + rs_rec_b_bytes(dk); }
 
 struct PrefillArgs {
     const void *q, *k, *v, *lam;

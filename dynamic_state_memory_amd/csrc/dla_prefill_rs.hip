@@ -84,8 +84,8 @@ __device__ __forceinline__ int refresh_active(const floatx4 (&am)[NTV][2], Frag<
 template <int DK>
 __global__ __launch_bounds__(256) void k_chunk_prep(
     const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, const __bf16 *__restrict__ LAM, int T, int C,
-    const int2 *__restrict__ events, const int32_t *__restrict__ chunk_ev, _Float16 *__restrict__ q16f,
-    int32_t *__restrict__ qexp_out, float *__restrict__ lamT, __bf16 *__restrict__ pwf, __bf16 *__restrict__ ktf)
+    const int2 *__restrict__ events, const int32_t *__restrict__ chunk_ev, uint8_t *__restrict__ rec,
+    int32_t *__restrict__ qexp_out)
 {
     constexpr int KS = DK / 32;
     __shared__ __align__(16) __bf16 q[kChunk][DK + 8];
@@ -102,6 +102,12 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
     const size_t tok0 = static_cast<size_t>(bh) * T;
     const size_t cb = static_cast<size_t>(bh) * NCH + ch;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // this chunk's record: query fragments, lam, weighted-score fragments, key fragments
+    uint8_t *rb = rec + cb * rs_record_bytes(DK);
+    f16x8 *q16f = reinterpret_cast<f16x8 *>(rb);
+    __bf16 *lamT = reinterpret_cast<__bf16 *>(rb + rs_rec_q_bytes(DK));
+    bf16x8 *pwf = reinterpret_cast<bf16x8 *>(rb + rs_rec_a_bytes(DK));
+    bf16x8 *ktf = reinterpret_cast<bf16x8 *>(rb + rs_rec_a_bytes(DK) + 2 * kChunk * kChunk);
     const int lr = lane & 15, lg = lane >> 4;
 
     float qmax = 0.0f;
@@ -161,13 +167,13 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
             h[e] = static_cast<_Float16>(ldexpf(static_cast<float>(row[cc + e]), -qexp));
             h[4 + e] = static_cast<_Float16>(ldexpf(static_cast<float>(row[cc + 16 + e]), -qexp));
         }
-        reinterpret_cast<f16x8 *>(q16f)[cb * 4 * KS * 64 + f] = h;
+        q16f[f] = h;
     }
     // lam, slot-major
 #pragma unroll
     for (int j = 0; j < kPrepCmax / 4; ++j) {
         const int idx = tid + 256 * j;
-        lamT[cb * kPrepCmax * kChunk + idx] = lam[idx & (kChunk - 1)][idx / kChunk];
+        lamT[idx] = static_cast<__bf16>(lam[idx & (kChunk - 1)][idx / kChunk]);
     }
     // K^T fragments: d_k rows of a 16-tile, 8 consecutive tokens per lane
 #pragma unroll
@@ -178,7 +184,7 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
         bf16x8 h;
 #pragma unroll
         for (int e = 0; e < 8; ++e) h[e] = k[t0 + e][dk];
-        reinterpret_cast<bf16x8 *>(ktf)[cb * (DK / 16) * 2 * 64 + f] = h;
+        ktf[f] = h;
     }
     __syncthreads();
     // P = (Q K^T) o W on the causal triangle (wave w: rows 16w..16w+15)
@@ -213,31 +219,37 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
     for (int j = 0; j < 2; ++j) {
         const int f = tid + 256 * j;                   // (mt, ks2, lane)
         const int l = f & 63, ks2 = (f >> 6) & 1, mt = f >> 7;
-        reinterpret_cast<bf16x8 *>(pwf)[cb * 8 * 64 + f] =
-            *reinterpret_cast<const bf16x8 *>(&pw[16 * mt + (l & 15)][32 * ks2 + 8 * (l >> 4)]);
+        pwf[f] = *reinterpret_cast<const bf16x8 *>(&pw[16 * mt + (l & 15)][32 * ks2 + 8 * (l >> 4)]);
     }
 }
 
 // ------------------------------------------------------------ the sweep
 
-constexpr int kRsWaves = 8;                    // waves per sweep block (two per SIMD)
+constexpr int kRsWaves = 4;                    // waves per sweep block; two blocks share a CU
 constexpr int kRsThreads = 64 * kRsWaves;
-constexpr int kRsActWave0 = 4;                 // waves 4.. hold the active state, 0..3 reduce
 
-// The chunk operands k_chunk_prep wrote, one 64-token chunk, copied verbatim
-// into LDS by the global->LDS loads (each 16-byte piece lands at the same
-// offset it has in the global chunk).
-template <int DK, int CMAX>
-struct RsStage {
+// A chunk's operands written by k_chunk_prep, copied verbatim into LDS by
+// global->LDS loads (each 16-byte piece lands at the offset it has in the
+// global chunk).  Part A is read from the chunk start to the end of the
+// inter-chunk read, part B from then on, so part A of the next chunk is
+// loaded while part B is in use and the other way round (one buffer each).
+template <int DK>
+struct RsStageA {
     _Float16 qf[kChunk / 16][DK / 32][64][8];   // query fragments (permuted reduction order)
-    float lamT[CMAX][kChunk];                    // lam, slot-major
+    __bf16 lamT[kPrepCmax][kChunk];              // lam, slot-major
+};
+template <int DK>
+struct RsStageB {
     __bf16 pwf[kChunk / 16][2][64][8];           // fragments of (Q K^T) o W
     __bf16 ktf[DK / 16][2][64][8];               // fragments of K^T
 };
+static_assert(sizeof(RsStageA<128>) == rs_rec_a_bytes(128) && sizeof(RsStageB<128>) == rs_rec_b_bytes(128) &&
+                  sizeof(RsStageA<64>) == rs_rec_a_bytes(64) && sizeof(RsStageB<64>) == rs_rec_b_bytes(64),
+              "the LDS stages mirror the two parts of a chunk record");
 
-// Everything else the sweep keeps in LDS.  The two stages are separate
-// __shared__ variables so that the compiler can tell that the in-flight loads
-// into one stage never touch the other (no wait before reading the current one).
+// Everything else the sweep keeps in LDS.  The stages are separate __shared__
+// variables so that the compiler can tell that loads in flight into one never
+// touch the other.
 template <int DK, int DVT, int CMAX>
 struct RsSmem {
     __bf16 vt[DVT][kChunk + 8];                  // V slice of the chunk, transposed
@@ -258,8 +270,14 @@ struct RsSmem {
     int32_t shexp[kMaxC];
     int32_t inv[kMaxC];         // chronological index of the state in each physical slot
     int2 evs[kChunk];           // the chunk's events (at most one per token)
+    // read-weight source of physical slot p in a chunk without events: lam
+    // row m0 - 1 - (chronological index) and 2^(state exponent); 0 for a slot
+    // without a closed state (rewritten after every chunk with events)
+    int32_t jrow[CMAX];
+    float wsc[CMAX];
     float red[kRsWaves];
     int32_t n_merge, n_grp, n_changed, m_new, act_new;
+    uint32_t reload;            // physical slots whose closed-state operands must be reloaded
 };
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -292,40 +310,23 @@ __device__ __forceinline__ void stage_array(const u32x4 *src, u32x4 *dst, int ti
 #pragma unroll
     for (int j = 0; j < (N + kRsThreads - 1) / kRsThreads; ++j)
         if (N % kRsThreads == 0 || 64 * wave + kRsThreads * j < N)
-            load_to_lds16(at_bytes(src + kRsThreads * j, 16u * tid), dst + 64 * wave + kRsThreads * j);
+            load_to_lds16(at_bytes(src + 64 * wave + kRsThreads * j, 16u * (tid & 63)), dst + 64 * wave + kRsThreads * j);
 }
 
-// Issue the loads of chunk cb's operands into stage X, in three groups so
-// that a caller can spread them over the chunk (the per-CU rate of these
-// loads is far below what a burst of all of them asks for): group 0 lam and
-// the weighted scores, groups 1 and 2 one half each of the query and key
-// fragments.
-template <int DK, int CMAX>
-__device__ __forceinline__ void stage_group(int grp, RsStage<DK, CMAX> &X, const _Float16 *q16f, const float *lamT,
-                                            const __bf16 *pwf, const __bf16 *ktf, size_t cb, int tid, int wave)
+// part A / part B of chunk record cb into the stages
+template <int DK>
+__device__ __forceinline__ void stage_a(RsStageA<DK> &X, const uint8_t *rec, size_t cb, int tid, int wave)
 {
-    constexpr int NQ = kChunk * DK * 2 / 16, NL = CMAX * kChunk * 4 / 16, NP = kChunk * kChunk * 2 / 16;
-    constexpr int NQ2 = NQ / 2;
-    if (grp == 0) {
-        stage_array<NL>(reinterpret_cast<const u32x4 *>(lamT) + cb * (kPrepCmax * kChunk * 4 / 16),
-                        reinterpret_cast<u32x4 *>(&X.lamT[0][0]), tid, wave);
-        stage_array<NP>(reinterpret_cast<const u32x4 *>(pwf) + cb * NP, reinterpret_cast<u32x4 *>(&X.pwf[0][0][0][0]),
-                        tid, wave);
-    } else {
-        const int h = (grp - 1) * NQ2;
-        stage_array<NQ2>(reinterpret_cast<const u32x4 *>(q16f) + cb * NQ + h,
-                         reinterpret_cast<u32x4 *>(&X.qf[0][0][0][0]) + h, tid, wave);
-        stage_array<NQ2>(reinterpret_cast<const u32x4 *>(ktf) + cb * NQ + h,
-                         reinterpret_cast<u32x4 *>(&X.ktf[0][0][0][0]) + h, tid, wave);
-    }
+    stage_array<rs_rec_a_bytes(DK) / 16>(reinterpret_cast<const u32x4 *>(rec + cb * rs_record_bytes(DK)),
+                                         reinterpret_cast<u32x4 *>(&X), tid, wave);
 }
 
-template <int DK, int CMAX>
-__device__ __forceinline__ void stage_chunk(RsStage<DK, CMAX> &X, const _Float16 *q16f, const float *lamT,
-                                            const __bf16 *pwf, const __bf16 *ktf, size_t cb, int tid, int wave)
+template <int DK>
+__device__ __forceinline__ void stage_b(RsStageB<DK> &Y, const uint8_t *rec, size_t cb, int tid, int wave)
 {
-#pragma unroll
-    for (int g = 0; g < 3; ++g) stage_group<DK, CMAX>(g, X, q16f, lamT, pwf, ktf, cb, tid, wave);
+    stage_array<rs_rec_b_bytes(DK) / 16>(
+        reinterpret_cast<const u32x4 *>(rec + cb * rs_record_bytes(DK) + rs_rec_a_bytes(DK)),
+        reinterpret_cast<u32x4 *>(&Y), tid, wave);
 }
 
 // What one block carries from chunk to chunk (registers after inlining).
@@ -334,20 +335,12 @@ struct RsCarry {
     Frag<_Float16> stk[SPW][DK / 32][DVT / 16];  // closed states of the wave's slots (fp16, normalised)
     floatx4 am[DVT / 16][2];                     // active state, d_k rows 32 kb .. 32 kb + 31 (fp32)
     Frag<_Float16> af[DVT / 16];                 // its fp16 operand copy
-    floatx4 Oprev[DVT / 16];                     // previous chunk's outputs, stored one chunk late
-    // read-weight source of the wave's slots p = 8 r + wave in a chunk without
-    // events: lam row m0 - 1 - (chronological index), times 2^(state
-    // exponent); 0 for a slot without a closed state (uniform, refreshed after
-    // every chunk with events)
-    int jrow[SPW];
-    float wsc[SPW];
     u32x4 vnext;                                 // next chunk's V piece
     int2 evnext;                                 // next chunk's event of this thread
     int ea;                                      // exponent of this wave's active-state operand
     int m0, act;                                 // live states, the active state's slot (uniform)
     int eA, eB, eC;                              // event offsets of chunks ch, ch + 1, ch + 2 (at chunk ch)
     int qexpn;                                   // next chunk's query exponent
-    int prev_c0, prev_nvalid;
     uint32_t closed;                             // physical slots of the closed states (uniform)
     bool refresh_w;
 };
@@ -358,14 +351,12 @@ struct RsParams {
     __bf16 *O;
     int T, C, DV;
     const int2 *events;
-    const _Float16 *q16f;
+    const uint8_t *rec;         // chunk records
     const int32_t *qexp_g;
-    const float *lamT_g;
-    const __bf16 *pwf_g, *ktf_g;
     int32_t *m_t_out;
     int bh, dv0, tid, lane, wave, lr, lg, NCH, vr, vc;
     uint32_t v_off;             // byte offset of this thread's V piece within a chunk's rows
-    uint32_t o_off;             // byte offset of this lane's first output within a chunk (reducing waves)
+    uint32_t o_off;             // byte offset of this lane's first output within a chunk
     bool v_mover;
     size_t tok0, slot_stride;
     float *st_base;
@@ -373,25 +364,27 @@ struct RsParams {
     const int32_t *cev;
 };
 
-// One chunk of the sweep: its operands are in X, the next chunk's go into Xn.
+// One chunk of the sweep: its part A operands are in X, its part B operands
+// are loaded into Y at its start; part A of the next chunk goes into X once
+// the inter-chunk read is done.
 //
-// Work split over the 8 waves: wave w owns the physical slots p = 8 r + w
-// (closed states in registers); waves 4 .. 4 + d_k/32 - 1 hold d_k rows
-// 32 (w - 4) .. + 31 of the active state; after the partial reads are
-// exchanged, waves 0..3 reduce rows 16 w .. 16 w + 15 and add P V while the
-// active-state waves add V^T K to it.
+// Work split over the 4 waves: wave w owns the physical slots p = 4 r + w
+// (closed states in registers), holds d_k rows 32 (w - AW) .. + 31 of the
+// active state (d_k = 128: every wave), and reduces and stores the outputs of
+// tokens 16 w .. 16 w + 15.
 template <int DK, int DVT, int SPW>
-__device__ __forceinline__ void rs_chunk(const int ch, RsStage<DK, kRsWaves * SPW> &X,
-                                         RsStage<DK, kRsWaves * SPW> &Xn, RsSmem<DK, DVT, kRsWaves * SPW> &S,
-                                         const RsParams &A, RsCarry<DK, DVT, SPW> &c)
+__device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB<DK> &Y,
+                                         RsSmem<DK, DVT, kRsWaves * SPW> &S, const RsParams &A,
+                                         RsCarry<DK, DVT, SPW> &c)
 {
     constexpr int KS = DK / 32;
     constexpr int NTV = DVT / 16;
     constexpr int MT = kChunk / 16;
     constexpr int NW = kRsWaves;
     constexpr int NT = kRsThreads;
-    constexpr int AW = kRsActWave0;
+    constexpr int AW = NW - KS;                  // first wave holding rows of the active state
     constexpr int CMAX = NW * SPW;
+    static_assert(MT == NW, "one 16-token row tile per wave");
     __bf16 *O = A.O;
     const int T = A.T, C = A.C, DV = A.DV;
     const int bh = A.bh, dv0 = A.dv0, tid = A.tid, lane = A.lane, wave = A.wave, lr = A.lr, lg = A.lg;
@@ -403,9 +396,9 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStage<DK, kRsWaves * SP
     auto &stk = c.stk;
     auto &am = c.am;
     auto &af = c.af;
-    auto &Oprev = c.Oprev;
-    const bool act_wave = wave >= AW && wave < AW + KS;
-    const int kb = wave - AW;                    // the active wave's d_k block
+    floatx4 Oprev[NTV];                          // this chunk's outputs (rows 16 wave ..)
+    const bool act_wave = wave >= AW;
+    const int kb = wave - AW;                    // the active wave's 32-row d_k block
 
     const int c0 = ch * kChunk;
     const int nvalid = min(kChunk, T - c0);
@@ -415,23 +408,13 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStage<DK, kRsWaves * SP
     const u32x4 vcur = c.vnext;
     const int2 evcur = c.evnext;
     const bool more = ch + 1 < NCH;
-    const size_t cbn = static_cast<size_t>(bh) * NCH + ch + 1;
-    // chunk ch's operands have landed (every wave's share) and every wave is
-    // done with chunk ch - 1
+    const size_t cb = static_cast<size_t>(bh) * NCH + ch;
+    // part A of chunk ch has landed (every wave's share) and every wave is
+    // done with chunk ch - 1 (so part B may be overwritten)
     wait_vmem();
     __syncthreads();
-    // ---- chunk ch + 1: first operand group into the other stage, V, events
-    // and the query exponent into registers (the event range is already known)
-    if (more) {
-        stage_group<DK, CMAX>(0, Xn, A.q16f, A.lamT_g, A.pwf_g, A.ktf_g, cbn, tid, wave);
-        c.qexpn = A.qexp_g[cbn];
-        const int c0n = c0 + kChunk;
-        c.vnext = u32x4{0u, 0u, 0u, 0u};
-        if (A.v_mover && vr < min(kChunk, T - c0n))
-            c.vnext = *at_bytes(reinterpret_cast<const u32x4 *>(A.V + (tok0 + c0n) * DV + dv0), A.v_off);
-        c.evnext = make_int2(0, 0);
-        if (tid < c.eC - c.eB) c.evnext = *at_bytes(A.events + tok0 + c.eB, 8u * tid);
-    }
+    // ---- part B of this chunk
+    stage_b<DK>(Y, A.rec, cb, tid, wave);
     // event offset of chunk ch + 3 (used two chunks from now)
     const int eD = ch + 3 <= NCH ? A.cev[ch + 3] : c.eC;
     // ---- this chunk's V (transposed) and events into LDS
@@ -441,26 +424,14 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStage<DK, kRsWaves * SP
         for (int e = 0; e < 8; ++e) S.vt[vc + e][vr] = ve[e];
     }
     if (tid < nev) S.evs[tid] = evcur;
-    // ---- the previous chunk's outputs (reducing waves)
-    if (ch > 0 && wave < MT) {
-        __bf16 *ob = O + (tok0 + c.prev_c0) * DV + dv0;
-#pragma unroll
-        for (int nt = 0; nt < NTV; ++nt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 16 * wave + 4 * lg + r;
-                if (t < c.prev_nvalid) *at_bytes(ob + r * DV + 16 * nt, A.o_off) = static_cast<__bf16>(Oprev[nt][r]);
-            }
-    }
     if (c.refresh_w) {
-#pragma unroll
-        for (int r = 0; r < SPW; ++r) {
-            const int p = NW * r + wave;
-            const bool live = (c.closed >> p) & 1u;
-            c.jrow[r] = live ? __builtin_amdgcn_readfirstlane(c.m0 - 1 - S.inv[p]) : 0;
-            c.wsc[r] = live ? ldexpf(1.0f, __builtin_amdgcn_readfirstlane(S.shexp[p])) : 0.0f;
+        if (tid < CMAX) {
+            const bool live = (c.closed >> tid) & 1u;
+            S.jrow[tid] = live ? c.m0 - 1 - S.inv[tid] : 0;
+            S.wsc[tid] = live ? ldexpf(1.0f, S.shexp[tid]) : 0.0f;
         }
         c.refresh_w = false;
+        lds_barrier();
     }
     const float qsc = ldexpf(1.0f, qexp);
     if (has_ev) {
@@ -492,17 +463,21 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStage<DK, kRsWaves * SP
             const int p = NW * r + wave;
             const bool live = (c.closed >> p) & 1u;
             const int slot = live ? __popcll(shr64(om_t, S.inv[p] + 1)) + __popcll(nm_t) : 0;
-            const float w = ldexpf(X.lamT[slot][lane], S.shexp[p] + qexp);
+            const float w = ldexpf(static_cast<float>(X.lamT[slot][lane]), S.shexp[p] + qexp);
             S.W[p][lane] = live ? w : 0.0f;
         }
-        if (act_wave) S.wact[kb][lane] = ldexpf(X.lamT[__popcll(S.nm[lane])][lane], qexp + c.ea);
+        if (act_wave)
+            S.wact[kb][lane] = ldexpf(static_cast<float>(X.lamT[__popcll(nm_t)][lane]), qexp + c.ea);
     } else {
         if (m_t_out && dv0 == 0 && tid < nvalid) m_t_out[tok0 + c0 + tid] = c.m0;
         // a closed state's slot is the same for every token of the chunk
         // (wsc is 0 for a slot without a closed state)
 #pragma unroll
-        for (int r = 0; r < SPW; ++r) S.W[NW * r + wave][lane] = X.lamT[c.jrow[r]][lane] * (c.wsc[r] * qsc);
-        if (act_wave) S.wact[kb][lane] = X.lamT[0][lane] * ldexpf(qsc, c.ea);
+        for (int r = 0; r < SPW; ++r) {
+            const int p = NW * r + wave;
+            S.W[p][lane] = static_cast<float>(X.lamT[S.jrow[p]][lane]) * (S.wsc[p] * qsc);
+        }
+        if (act_wave) S.wact[kb][lane] = static_cast<float>(X.lamT[0][lane]) * ldexpf(qsc, c.ea);
     }
 
     // ---- inter-chunk read: closed states from registers, then the active state
@@ -514,45 +489,41 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStage<DK, kRsWaves * SP
     uint32_t mine = 0;          // which of the wave's slots hold a closed state (uniform)
 #pragma unroll
     for (int r = 0; r < SPW; ++r) mine |= ((c.closed >> (NW * r + wave)) & 1u) << r;
-    // two halves of the chunk's tokens (row tiles 2 hf, 2 hf + 1) keep half of
-    // the query fragments live at a time; each half first issues one more
-    // group of the next chunk's operand loads
+    // one 16-token row tile at a time keeps a quarter of the query fragments
+    // live; the wave's slots go in pairs (two independent product chains),
+    // a pair is skipped when neither slot holds a closed state (a slot without
+    // one has weight 0 and finite operands)
+    static_assert(SPW % 2 == 0, "slots are read in pairs");
+    if (mine != 0u) {
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-        if (more) stage_group<DK, CMAX>(1 + hf, Xn, A.q16f, A.lamT_g, A.pwf_g, A.ktf_g, cbn, tid, wave);
-        if (mine != 0u) {
-            Frag<_Float16> qf[2][KS];
+        for (int mt = 0; mt < MT; ++mt) {
+            Frag<_Float16> qf[KS];
 #pragma unroll
-            for (int m2 = 0; m2 < 2; ++m2)
+            for (int ks = 0; ks < KS; ++ks) load_frag(qf[ks], X.qf[mt][ks][lane]);
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) load_frag(qf[m2][ks], X.qf[2 * hf + m2][ks][lane]);
-            // the wave's slots that hold a closed state (a uniform branch)
+            for (int r2 = 0; r2 < SPW; r2 += 2) {
+                if (!((mine >> r2) & 3u)) continue;
+                floatx4 P0[NTV], P1[NTV];
 #pragma unroll
-            for (int r = 0; r < SPW; ++r) {
-                const int p = NW * r + wave;
-                if (!((mine >> r) & 1u)) continue;
-                floatx4 P[2][NTV];
-#pragma unroll
-                for (int m2 = 0; m2 < 2; ++m2)
-#pragma unroll
-                    for (int nt = 0; nt < NTV; ++nt) P[m2][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+                for (int nt = 0; nt < NTV; ++nt) {
+                    P0[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+                    P1[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+                }
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-                    for (int m2 = 0; m2 < 2; ++m2)
-#pragma unroll
-                        for (int nt = 0; nt < NTV; ++nt) mma32(P[m2][nt], qf[m2][ks], stk[r][ks][nt]);
-#pragma unroll
-                for (int m2 = 0; m2 < 2; ++m2) {
-                    const int mt = 2 * hf + m2;
-                    const float4 w = *reinterpret_cast<const float4 *>(&S.W[p][16 * mt + 4 * lg]);
-#pragma unroll
                     for (int nt = 0; nt < NTV; ++nt) {
-                        Oi[mt][nt][0] += w.x * P[m2][nt][0];
-                        Oi[mt][nt][1] += w.y * P[m2][nt][1];
-                        Oi[mt][nt][2] += w.z * P[m2][nt][2];
-                        Oi[mt][nt][3] += w.w * P[m2][nt][3];
+                        mma32(P0[nt], qf[ks], stk[r2][ks][nt]);
+                        mma32(P1[nt], qf[ks], stk[r2 + 1][ks][nt]);
                     }
+                const float4 w0 = *reinterpret_cast<const float4 *>(&S.W[NW * r2 + wave][16 * mt + 4 * lg]);
+                const float4 w1 = *reinterpret_cast<const float4 *>(&S.W[NW * (r2 + 1) + wave][16 * mt + 4 * lg]);
+#pragma unroll
+                for (int nt = 0; nt < NTV; ++nt) {
+                    Oi[mt][nt][0] += w0.x * P0[nt][0] + w1.x * P1[nt][0];
+                    Oi[mt][nt][1] += w0.y * P0[nt][1] + w1.y * P1[nt][1];
+                    Oi[mt][nt][2] += w0.z * P0[nt][2] + w1.z * P1[nt][2];
+                    Oi[mt][nt][3] += w0.w * P0[nt][3] + w1.w * P1[nt][3];
                 }
             }
         }
@@ -578,9 +549,22 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStage<DK, kRsWaves * SP
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int nt = 0; nt < NTV; ++nt) S.ored[wave][mt][nt][lane] = Oi[mt][nt];
-    lds_barrier();
-    // ---- reducing waves: sum the partial reads of rows 16 w .., add P V
-    if (wave < MT) {
+    // part B has landed and every wave is done with part A
+    wait_vmem();
+    __syncthreads();
+    // ---- part A of the next chunk; its V, events and query exponent into registers
+    if (more) {
+        stage_a<DK>(X, A.rec, cb + 1, tid, wave);
+        c.qexpn = A.qexp_g[cb + 1];
+        const int c0n = c0 + kChunk;
+        c.vnext = u32x4{0u, 0u, 0u, 0u};
+        if (A.v_mover && vr < min(kChunk, T - c0n))
+            c.vnext = *at_bytes(reinterpret_cast<const u32x4 *>(A.V + (tok0 + c0n) * DV + dv0), A.v_off);
+        c.evnext = make_int2(0, 0);
+        if (tid < c.eC - c.eB) c.evnext = *at_bytes(A.events + tok0 + c.eB, 8u * tid);
+    }
+    // ---- reduce the partial reads of rows 16 w .., add P V
+    {
         const int w = wave;
 #pragma unroll
         for (int nt = 0; nt < NTV; ++nt) {
@@ -593,7 +577,7 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStage<DK, kRsWaves * SP
         for (int ks = 0; ks < kChunk / 32; ++ks) {
             if (32 * ks <= 16 * w + 15) {
                 Frag<__bf16> a;
-                load_frag(a, X.pwf[w][ks][lane]);
+                load_frag(a, Y.pwf[w][ks][lane]);
 #pragma unroll
                 for (int nt = 0; nt < NTV; ++nt) {
                     Frag<__bf16> b;
@@ -602,9 +586,15 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStage<DK, kRsWaves * SP
                 }
             }
         }
+        __bf16 *ob = O + (tok0 + c0) * DV + dv0;
+#pragma unroll
+        for (int nt = 0; nt < NTV; ++nt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * w + 4 * lg + r;
+                if (t < nvalid) *at_bytes(ob + r * DV + 16 * nt, A.o_off) = static_cast<__bf16>(Oprev[nt][r]);
+            }
     }
-    c.prev_c0 = c0;
-    c.prev_nvalid = nvalid;
 
     // ---- chunk-end update
     if (!has_ev) {
@@ -615,7 +605,7 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStage<DK, kRsWaves * SP
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     Frag<__bf16> a;
-                    load_frag(a, X.ktf[2 * kb + h][kk][lane]);
+                    load_frag(a, Y.ktf[2 * kb + h][kk][lane]);
 #pragma unroll
                     for (int nt = 0; nt < NTV; ++nt) {
                         Frag<__bf16> b;
@@ -675,6 +665,10 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStage<DK, kRsWaves * SP
         const int an = mnew > 0 ? S.new_order[mnew - 1] : -1;
         // the previous active state, if it is now closed, needs an operand copy
         if (act >= 0 && m0 > 0 && ((oa >> (m0 - 1)) & 1ull) && act != an) S.changed[nch++] = act;
+        uint32_t rl = 0;
+        for (int i = 0; i < nch; ++i)
+            if (S.changed[i] != an) rl |= 1u << S.changed[i];
+        S.reload = rl;
         S.n_merge = nmg;
         S.n_grp = ng;
         S.n_changed = nch;
@@ -717,7 +711,7 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStage<DK, kRsWaves * SP
                     Frag<__bf16> a, b;
                     load_frag(a, &S.vt[16 * mt + lr][base]);
                     mask_frag(a, base, lo, hi);
-                    load_frag(b, X.ktf[nt][ks][lane]);
+                    load_frag(b, Y.ktf[nt][ks][lane]);
                     mma32(acc, a, b);
                 }
             }
@@ -763,19 +757,17 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStage<DK, kRsWaves * SP
     }
     __syncthreads();
     // owner waves reload the register copies of the changed closed states
-    for (int cc = 0; cc < S.n_changed; ++cc) {
-        const int slot = S.changed[cc];
-        if (slot == an || (slot % NW) != wave) continue;
-        const _Float16 *src = sh_base + slot * slot_stride;
+    const uint32_t reload = __builtin_amdgcn_readfirstlane(S.reload);
 #pragma unroll
-        for (int r = 0; r < SPW; ++r) {
-            if (slot / NW == r) {
+    for (int r = 0; r < SPW; ++r) {
+        const int slot = NW * r + wave;
+        if ((reload >> slot) & 1u) {
+            const _Float16 *src = sh_base + slot * slot_stride;
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
+            for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-                    for (int nt = 0; nt < NTV; ++nt)
-                        perm_frag_f16(stk[r][ks][nt], src + (16 * nt + lr) * DK, 32 * ks + 4 * lg);
-            }
+                for (int nt = 0; nt < NTV; ++nt)
+                    perm_frag_f16(stk[r][ks][nt], src + (16 * nt + lr) * DK, 32 * ks + 4 * lg);
         }
     }
     // the new active state into the accumulators
@@ -807,19 +799,19 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStage<DK, kRsWaves * SP
 }
 
 template <int DK, int DVT, int SPW>
-__global__ __launch_bounds__(kRsThreads, 1) void k_prefill_rs(
+__global__ __launch_bounds__(kRsThreads, 2) void k_prefill_rs(
     const __bf16 *__restrict__ V, __bf16 *__restrict__ O, int T, int C, int DV, int nblk_dv,
     float *__restrict__ states, _Float16 *__restrict__ shadow, const int2 *__restrict__ events,
-    const int32_t *__restrict__ chunk_ev, const _Float16 *__restrict__ q16f, const int32_t *__restrict__ qexp_g,
-    const float *__restrict__ lamT_g, const __bf16 *__restrict__ pwf_g, const __bf16 *__restrict__ ktf_g,
+    const int32_t *__restrict__ chunk_ev, const uint8_t *__restrict__ rec, const int32_t *__restrict__ qexp_g,
     uint8_t *__restrict__ meta_base, size_t meta_stride, int32_t *__restrict__ m_t_out)
 {
     constexpr int KS = DK / 32;
     constexpr int NTV = DVT / 16;
     constexpr int CMAX = kRsWaves * SPW;
-    static_assert(KS <= kRsWaves - kRsActWave0, "one wave per 32-row block of the active state");
+    static_assert(KS <= kRsWaves, "one wave per 32-row block of the active state");
     static_assert(kChunk * DVT / 8 <= kRsThreads, "one 16-byte V piece per thread");
-    __shared__ RsStage<DK, CMAX> st0, st1;        // chunk ch in st0 when ch is even
+    __shared__ RsStageA<DK> stA;
+    __shared__ RsStageB<DK> stB;
     __shared__ RsSmem<DK, DVT, CMAX> S;
 
     const int nblk = gridDim.x;
@@ -827,7 +819,7 @@ __global__ __launch_bounds__(kRsThreads, 1) void k_prefill_rs(
     if ((nblk & 7) == 0) lin = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
     RsParams A;
     A.V = V; A.O = O; A.T = T; A.C = C; A.DV = DV;
-    A.events = events; A.q16f = q16f; A.qexp_g = qexp_g; A.lamT_g = lamT_g; A.pwf_g = pwf_g; A.ktf_g = ktf_g;
+    A.events = events; A.rec = rec; A.qexp_g = qexp_g;
     A.m_t_out = m_t_out;
     A.bh = lin / nblk_dv;
     A.dv0 = (lin % nblk_dv) * DVT;
@@ -842,7 +834,7 @@ __global__ __launch_bounds__(kRsThreads, 1) void k_prefill_rs(
     A.vc = (A.tid / kChunk) * 8;
     A.v_mover = A.tid < kChunk * DVT / 8;
     A.v_off = 2u * static_cast<uint32_t>(A.vr * DV + A.vc);
-    A.o_off = 2u * static_cast<uint32_t>((16 * (A.wave & 3) + 4 * A.lg) * DV + A.lr);
+    A.o_off = 2u * static_cast<uint32_t>((16 * A.wave + 4 * A.lg) * DV + A.lr);
     A.tok0 = static_cast<size_t>(A.bh) * T;
     A.slot_stride = static_cast<size_t>(DV) * DK;
     A.st_base = states + static_cast<size_t>(A.bh) * C * DV * DK + static_cast<size_t>(A.dv0) * DK;
@@ -862,21 +854,17 @@ __global__ __launch_bounds__(kRsThreads, 1) void k_prefill_rs(
         c.am[nt][0] = floatx4{0.f, 0.f, 0.f, 0.f};
         c.am[nt][1] = floatx4{0.f, 0.f, 0.f, 0.f};
         zero_frag(c.af[nt]);
-        c.Oprev[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
-#pragma unroll
-    for (int r = 0; r < SPW; ++r) { c.jrow[r] = 0; c.wsc[r] = 0.0f; }
+    if (tid < CMAX) { S.jrow[tid] = 0; S.wsc[tid] = 0.0f; }
     c.ea = 0;
     c.m0 = 0;
     c.act = -1;
     c.closed = 0;
     c.refresh_w = false;
-    c.prev_c0 = 0;
-    c.prev_nvalid = 0;
     if (tid < kMaxC) { S.order[tid] = tid; S.shexp[tid] = 0; }
 
-    // chunk 0: operands into stage 0, V and events into registers
-    stage_chunk<DK, CMAX>(st0, q16f, lamT_g, pwf_g, ktf_g, static_cast<size_t>(A.bh) * NCH, tid, wave);
+    // chunk 0: part A into LDS, V and events into registers
+    stage_a<DK>(stA, rec, static_cast<size_t>(A.bh) * NCH, tid, wave);
     c.vnext = u32x4{0u, 0u, 0u, 0u};
     if (A.v_mover && A.vr < min(kChunk, T))
         c.vnext = *reinterpret_cast<const u32x4 *>(V + (A.tok0 + A.vr) * DV + A.dv0 + A.vc);
@@ -887,26 +875,11 @@ __global__ __launch_bounds__(kRsThreads, 1) void k_prefill_rs(
     c.evnext = make_int2(0, 0);
     if (tid < c.eB - c.eA) c.evnext = events[A.tok0 + c.eA + tid];
 
-    for (int ch = 0; ch < NCH; ch += 2) {
-        rs_chunk<DK, DVT, SPW>(ch, st0, st1, S, A, c);
-        if (ch + 1 < NCH) rs_chunk<DK, DVT, SPW>(ch + 1, st1, st0, S, A, c);
-    }
+    for (int ch = 0; ch < NCH; ++ch) rs_chunk<DK, DVT, SPW>(ch, stA, stB, S, A, c);
 
-    // the last chunk's outputs
-    const size_t tok0 = A.tok0;
-    if (wave < kChunk / 16) {
-#pragma unroll
-        for (int nt = 0; nt < NTV; ++nt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 16 * wave + 4 * lg + r;
-                if (t < c.prev_nvalid)
-                    O[(tok0 + c.prev_c0 + t) * DV + A.dv0 + 16 * nt + lr] = static_cast<__bf16>(c.Oprev[nt][r]);
-            }
-    }
     // the active state's accumulators are the last state of the final cache
-    const int kb = wave - kRsActWave0;
-    if (c.act >= 0 && kb >= 0 && kb < KS) {
+    const int kb = wave - (kRsWaves - KS);
+    if (c.act >= 0 && kb >= 0) {
         float *dst = A.st_base + c.act * A.slot_stride;
 #pragma unroll
         for (int nt = 0; nt < NTV; ++nt)
@@ -931,8 +904,7 @@ static hipError_t launch_rs(const PrefillArgs &a, hipStream_t stream)
     hipLaunchKernelGGL((k_chunk_prep<DK>), dim3(NCH, BH), dim3(256), 0, stream,
                        static_cast<const __bf16 *>(a.q), static_cast<const __bf16 *>(a.k),
                        static_cast<const __bf16 *>(a.lam), a.T, a.g.C, a.ws.events, a.ws.chunk_ev,
-                       static_cast<_Float16 *>(a.ws.q16f), a.ws.qexp, a.ws.lamT,
-                       static_cast<__bf16 *>(a.ws.pwf), static_cast<__bf16 *>(a.ws.ktf));
+                       static_cast<uint8_t *>(a.ws.rec), a.ws.qexp);
     hipError_t e0 = hipGetLastError();
     if (e0 != hipSuccess) return e0;
     if (a.ev_before) {
@@ -942,30 +914,31 @@ static hipError_t launch_rs(const PrefillArgs &a, hipStream_t stream)
     hipLaunchKernelGGL((k_prefill_rs<DK, DVT, SPW>), dim3(BH * nblk_dv), dim3(kRsThreads), 0, stream,
                        static_cast<const __bf16 *>(a.v), static_cast<__bf16 *>(a.o), a.T, a.g.C, a.g.dv,
                        nblk_dv, a.states, static_cast<_Float16 *>(a.ws.shadow), a.ws.events, a.ws.chunk_ev,
-                       static_cast<const _Float16 *>(a.ws.q16f), a.ws.qexp, a.ws.lamT,
-                       static_cast<const __bf16 *>(a.ws.pwf), static_cast<const __bf16 *>(a.ws.ktf), a.meta,
-                       a.g.meta_stride, a.sched.m_t);
+                       static_cast<const uint8_t *>(a.ws.rec), a.ws.qexp, a.meta, a.g.meta_stride, a.sched.m_t);
     hipError_t e = hipGetLastError();
     if (e == hipSuccess && a.ev_after) e = hipEventRecord(a.ev_after, stream);
     return e;
 }
 
-// The register-resident sweep works on 16-column slices of d_v (8 waves, two
-// per SIMD, each holding C/8 states of the slice).
+// The register-resident sweep works on 16-column slices of d_v (4 waves, each
+// holding C/4 states of the slice; two blocks share a compute unit).
 int prefill_rs_dvt(int, int, int) { return 16; }
 
 hipError_t launch_prefill_rs(const PrefillArgs &a, hipStream_t stream)
 {
     const int C = a.g.C;
     if (a.g.dk == 128)
-        return C <= 8 ? launch_rs<128, 16, 1>(a, stream) : C <= 16 ? launch_rs<128, 16, 2>(a, stream)
-                                                               : launch_rs<128, 16, 4>(a, stream);
-    return C <= 8 ? launch_rs<64, 16, 1>(a, stream) : C <= 16 ? launch_rs<64, 16, 2>(a, stream)
-                                                             : launch_rs<64, 16, 4>(a, stream);
+        return C <= 8 ? launch_rs<128, 16, 2>(a, stream) : C <= 16 ? launch_rs<128, 16, 4>(a, stream)
+                                                               : launch_rs<128, 16, 8>(a, stream);
+    return C <= 8 ? launch_rs<64, 16, 2>(a, stream) : C <= 16 ? launch_rs<64, 16, 4>(a, stream)
+                                                             : launch_rs<64, 16, 8>(a, stream);
 }
 
 template <int DK, int DVT, int CMAX>
-constexpr size_t rs_lds_bytes() { return 2 * sizeof(RsStage<DK, CMAX>) + sizeof(RsSmem<DK, DVT, CMAX>); }
+constexpr size_t rs_lds_bytes()
+{
+    return sizeof(RsStageA<DK>) + sizeof(RsStageB<DK>) + sizeof(RsSmem<DK, DVT, CMAX>);
+}
 
 size_t prefill_rs_smem_bytes(int dk, int, int C)
 {

@@ -45,8 +45,8 @@ def test_sizes_and_layout():
 def test_prefill_kernel_choice(monkeypatch):
     monkeypatch.delenv("DLA_PREFILL_PATH", raising=False)
     monkeypatch.delenv("DLA_PREFILL_DVT", raising=False)
-    assert dla.dla_prefill_kernel(dla.DLA_BF16, 2, 16, 32, 128, 256) == "k_prefill_rs<128,16,4>"
-    assert dla.dla_prefill_kernel(dla.DLA_BF16, 4, 24, 16, 128, 64) == "k_prefill_rs<128,16,2>"
+    assert dla.dla_prefill_kernel(dla.DLA_BF16, 2, 16, 32, 128, 256) == "k_prefill_rs<128,16,8>"
+    assert dla.dla_prefill_kernel(dla.DLA_BF16, 4, 24, 16, 128, 64) == "k_prefill_rs<128,16,4>"
     assert dla.dla_prefill_kernel(dla.DLA_F32, 1, 1, 8, 64, 64) == "k_prefill<f32,64,16>"
     assert dla.dla_prefill_kernel(dla.DLA_BF16, 1, 1, 48, 64, 64) == "k_prefill<bf16,64,16>"
     assert dla.dla_prefill_kernel(dla.DLA_BF16, 1, 1, 8, 96, 64) is None

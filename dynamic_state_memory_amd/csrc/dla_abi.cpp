@@ -159,7 +159,7 @@ PrefillPlan plan_prefill(bool io_bf16, int64_t BH, int C, int dk, int dv)
     if (p.register_resident) {
         p.dvt = prefill_rs_dvt(dk, C, p.dvt);
         p.lds = prefill_rs_smem_bytes(dk, p.dvt, C);
-        const int spw = C <= 8 ? 2 : C <= 16 ? 4 : 8;   // states per wave (4 waves)
+        const int spw = prefill_rs_spw(C);
         std::snprintf(p.name, sizeof(p.name), "k_prefill_rs<%d,%d,%d>", dk, p.dvt, spw);
     } else {
         p.lds = prefill_smem_bytes(io_bf16, dk, p.dvt);

@@ -123,5 +123,6 @@ size_t prefill_smem_bytes(int io_bf16, int dk, int dvt);
 hipError_t launch_prefill_rs(const PrefillArgs &a, hipStream_t stream);
 size_t prefill_rs_smem_bytes(int dk, int dvt, int C);
 int prefill_rs_dvt(int dk, int C, int dvt_wanted);
+int prefill_rs_spw(int C);      // closed-state slots per wave of the register-resident sweep
 
 }  // namespace dla

@@ -810,6 +810,7 @@ __global__ __launch_bounds__(kRsThreads, 2) void k_prefill_rs(
     constexpr int CMAX = kRsWaves * SPW;
     static_assert(KS <= kRsWaves, "one wave per 32-row block of the active state");
     static_assert(kChunk * DVT / 8 <= kRsThreads, "one 16-byte V piece per thread");
+    static_assert(CMAX <= kPrepCmax, "a chunk record holds lam for 32 slots");
     __shared__ RsStageA<DK> stA;
     __shared__ RsStageB<DK> stB;
     __shared__ RsSmem<DK, DVT, CMAX> S;
@@ -921,17 +922,25 @@ static hipError_t launch_rs(const PrefillArgs &a, hipStream_t stream)
 }
 
 // The register-resident sweep works on 16-column slices of d_v (4 waves, each
-// holding C/4 states of the slice; two blocks share a compute unit).
+// holding C/4 states of the slice, C rounded up to 8, 16 or 32; two blocks
+// share a compute unit).
 int prefill_rs_dvt(int, int, int) { return 16; }
+
+int prefill_rs_spw(int C) { return (C <= 8 ? 8 : C <= 16 ? 16 : 32) / kRsWaves; }
+
+template <int DK>
+static hipError_t launch_rs_dk(const PrefillArgs &a, hipStream_t stream)
+{
+    switch (prefill_rs_spw(a.g.C)) {
+    case 2: return launch_rs<DK, 16, 2>(a, stream);
+    case 4: return launch_rs<DK, 16, 4>(a, stream);
+    default: return launch_rs<DK, 16, 8>(a, stream);
+    }
+}
 
 hipError_t launch_prefill_rs(const PrefillArgs &a, hipStream_t stream)
 {
-    const int C = a.g.C;
-    if (a.g.dk == 128)
-        return C <= 8 ? launch_rs<128, 16, 2>(a, stream) : C <= 16 ? launch_rs<128, 16, 4>(a, stream)
-                                                               : launch_rs<128, 16, 8>(a, stream);
-    return C <= 8 ? launch_rs<64, 16, 2>(a, stream) : C <= 16 ? launch_rs<64, 16, 4>(a, stream)
-                                                             : launch_rs<64, 16, 8>(a, stream);
+    return a.g.dk == 128 ? launch_rs_dk<128>(a, stream) : launch_rs_dk<64>(a, stream);
 }
 
 template <int DK, int DVT, int CMAX>

@@ -253,20 +253,22 @@ static_assert(sizeof(RsStageA<128>) == rs_rec_a_bytes(128) && sizeof(RsStageB<12
 template <int DK, int DVT, int CMAX>
 struct RsSmem {
     __bf16 vt[DVT][kChunk + 8];                  // V slice of the chunk, transposed
-    float W[CMAX][kChunk];      // closed-state read weights by physical slot (owner wave's rows)
+    // closed-state read weights by physical slot (owner wave's rows); in a
+    // chunk with events, after the read, the active state passes through it
+    float W[CMAX < 32 ? 32 : CMAX][kChunk];
     float wact[DK / 32][kChunk];  // active-state read weights, one row per active wave
     floatx4 ored[kRsWaves][kChunk / 16][DVT / 16][64];  // partial reads: wave, row tile, column tile, lane
     uint64_t om[kChunk];
     uint64_t nm[kChunk];
     int32_t order[kMaxC];
     int32_t new_order[kMaxC];
-    int32_t merge_dst[kMaxC];
-    int32_t merge_src[kMaxC];
-    int32_t grp_lo[kChunk + 1];
-    int32_t grp_hi[kChunk + 1];
-    int32_t grp_slot[kChunk + 1];
-    int32_t grp_add[kChunk + 1];
-    int32_t changed[kMaxC + kChunk + 2];
+    // per physical slot, what a chunk with events does to the state in it:
+    // its new value is (own value if jbase) + (values of the slots in jsrc,
+    // merged into it) + (V^T K of the chunk tokens [jlo, jhi))
+    int32_t jbase[kMaxC];
+    uint32_t jsrc[kMaxC];
+    int32_t jlo[kMaxC];
+    int32_t jhi[kMaxC];
     int32_t shexp[kMaxC];
     int32_t inv[kMaxC];         // chronological index of the state in each physical slot
     int2 evs[kChunk];           // the chunk's events (at most one per token)
@@ -275,9 +277,8 @@ struct RsSmem {
     // without a closed state (rewritten after every chunk with events)
     int32_t jrow[CMAX];
     float wsc[CMAX];
-    float red[kRsWaves];
-    int32_t n_merge, n_grp, n_changed, m_new, act_new;
-    uint32_t reload;            // physical slots whose closed-state operands must be reloaded
+    uint32_t jobs;              // slots whose new value an owner wave builds
+    int32_t m_new, act_new, an_case;
 };
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -360,7 +361,6 @@ struct RsParams {
     bool v_mover;
     size_t tok0, slot_stride;
     float *st_base;
-    _Float16 *sh_base;
     const int32_t *cev;
 };
 
@@ -381,17 +381,15 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
     constexpr int NTV = DVT / 16;
     constexpr int MT = kChunk / 16;
     constexpr int NW = kRsWaves;
-    constexpr int NT = kRsThreads;
     constexpr int AW = NW - KS;                  // first wave holding rows of the active state
     constexpr int CMAX = NW * SPW;
     static_assert(MT == NW, "one 16-token row tile per wave");
     __bf16 *O = A.O;
-    const int T = A.T, C = A.C, DV = A.DV;
+    const int T = A.T, DV = A.DV;
     const int bh = A.bh, dv0 = A.dv0, tid = A.tid, lane = A.lane, wave = A.wave, lr = A.lr, lg = A.lg;
     const int NCH = A.NCH, vr = A.vr, vc = A.vc;
     const size_t tok0 = A.tok0, slot_stride = A.slot_stride;
     float *st_base = A.st_base;
-    _Float16 *sh_base = A.sh_base;
     int32_t *m_t_out = A.m_t_out;
     auto &stk = c.stk;
     auto &am = c.am;
@@ -621,166 +619,250 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
         return;
     }
 
-    // chunk with events: general update in the fp32 cache
+    // ---- chunk with events.  The bookkeeping (one thread) turns the chunk's
+    // merges and new starts into per-slot jobs; the active-state waves pass
+    // the active state to LDS; then the wave owning each changed closed slot
+    // builds its new fp32 value in registers (old values + merged-in values +
+    // V^T K of its tokens), writes it to the cache and converts it into its
+    // fp16 operand copy, and the active-state waves form the new active state.
     const int m0 = c.m0, act = c.act;
+    // the active state (d_k rows in 16-row tiles) passes through the read
+    // weights, which no wave reads after the inter-chunk read; a new active
+    // state built by an owner wave (rare) through the partial reads, which it
+    // writes only after the barrier that follows every wave's reduce
+    floatx4 *actbuf = reinterpret_cast<floatx4 *>(&S.W[0][0]);     // [DK / 16][NTV][64]
+    floatx4 *anbuf = &S.ored[0][0][0][0];                           // [DK / 16][NTV][64]
+    static_assert((DK / 16) * NTV * 64 * sizeof(floatx4) <= sizeof(S.W), "the active state fits the weight table");
+    static_assert((DK / 16) * NTV * 64 <= NW * MT * NTV * 64, "a state slice fits the partial-read buffer");
     if (tid == 0) {
         const int tl = nvalid - 1;
         const uint64_t oa = S.om[tl], na = S.nm[tl];
-        uint64_t used = 0;
-        int nold = 0, last_old = -1, nmg = 0, tgt = -1;
+        uint32_t used = 0, jobs = 0;
+        int nold = 0, last_old = -1, tgt = -1;
         for (int i = 0; i < m0; ++i) {
+            const int p = S.order[i];
             if ((oa >> i) & 1ull) {
-                S.new_order[nold++] = S.order[i];
-                used |= 1ull << S.order[i];
+                S.new_order[nold++] = p;
+                used |= 1u << p;
                 last_old = i;
-                tgt = i;
-            } else if (tgt >= 0) {
-                S.merge_dst[nmg] = S.order[tgt];
-                S.merge_src[nmg] = S.order[i];
-                ++nmg;
+                tgt = p;
+                S.jbase[p] = 1;
+                S.jsrc[p] = 0;
+                S.jlo[p] = 0;
+                S.jhi[p] = 0;
+            } else {
+                // a state merged away joins the nearest older live state (the
+                // oldest state is never merged away, so tgt >= 0)
+                S.jsrc[tgt] |= 1u << p;
+                jobs |= 1u << tgt;
             }
         }
-        int ng = 0, mnew = nold, nch = 0;
-        for (int i = 0; i < nmg; ++i) S.changed[nch++] = S.merge_dst[i];
         const int first_new = na ? __ffsll(static_cast<unsigned long long>(na)) - 1 : nvalid;
         if (first_new > 0 && last_old >= 0) {
-            S.grp_lo[ng] = 0; S.grp_hi[ng] = first_new;
-            S.grp_slot[ng] = S.order[last_old]; S.grp_add[ng] = 1;
-            S.changed[nch++] = S.order[last_old];
-            ++ng;
+            // the chunk's tokens before its first new state join the last old state
+            const int p = S.order[last_old];
+            S.jlo[p] = 0;
+            S.jhi[p] = first_new;
+            jobs |= 1u << p;
         }
+        int mnew = nold;
         uint64_t rest = na;
         while (rest) {
-            const int p = __ffsll(static_cast<unsigned long long>(rest)) - 1;
+            const int pos = __ffsll(static_cast<unsigned long long>(rest)) - 1;
             rest &= rest - 1;
             const int q = rest ? __ffsll(static_cast<unsigned long long>(rest)) - 1 : nvalid;
-            const int slot = __ffsll(static_cast<unsigned long long>(~used)) - 1;
-            if (slot < 0 || slot >= C) break;   // cannot happen: at most C states live
-            used |= 1ull << slot;
+            const int slot = __ffs(~used) - 1;          // lowest free slot (at most C states live)
+            used |= 1u << slot;
             S.new_order[mnew++] = slot;
-            S.grp_lo[ng] = p; S.grp_hi[ng] = q; S.grp_slot[ng] = slot; S.grp_add[ng] = 0;
-            S.changed[nch++] = slot;
-            ++ng;
+            S.jbase[slot] = 0;
+            S.jsrc[slot] = 0;
+            S.jlo[slot] = pos;
+            S.jhi[slot] = q;
+            jobs |= 1u << slot;
         }
-        const int an = mnew > 0 ? S.new_order[mnew - 1] : -1;
-        // the previous active state, if it is now closed, needs an operand copy
-        if (act >= 0 && m0 > 0 && ((oa >> (m0 - 1)) & 1ull) && act != an) S.changed[nch++] = act;
-        uint32_t rl = 0;
-        for (int i = 0; i < nch; ++i)
-            if (S.changed[i] != an) rl |= 1u << S.changed[i];
-        S.reload = rl;
-        S.n_merge = nmg;
-        S.n_grp = ng;
-        S.n_changed = nch;
+        const int an = S.new_order[mnew - 1];
+        // the previous active state, still live but no longer the most recent, closes
+        if (act >= 0 && act != an && ((oa >> (m0 - 1)) & 1ull)) jobs |= 1u << act;
+        // the new active state: 0 = the same state (tokens added), 1 = a new
+        // state (set from its tokens; it may sit in the slot of the previous
+        // active state when that one was merged away), 2 = an older state
+        // (built by its owner)
+        const int an_case = S.jbase[an] == 0 ? 1 : (an == act ? 0 : 2);
+        if (an_case != 2) jobs &= ~(1u << an);
+        S.jobs = jobs;
         S.m_new = mnew;
         S.act_new = an;
+        S.an_case = an_case;
     }
-    // flush the active state's accumulators to its fp32 state in the cache
     if (act >= 0 && act_wave) {
-        float *dst = st_base + act * slot_stride;
 #pragma unroll
         for (int nt = 0; nt < NTV; ++nt)
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
-                *reinterpret_cast<float4 *>(dst + (16 * nt + lr) * DK + 32 * kb + 16 * h + 4 * lg) =
-                    make_float4(am[nt][h][0], am[nt][h][1], am[nt][h][2], am[nt][h][3]);
+            for (int h = 0; h < 2; ++h) actbuf[((2 * kb + h) * NTV + nt) * 64 + lane] = am[nt][h];
     }
     __syncthreads();
-    for (int g = 0; g < S.n_merge; ++g) {
-        float4 *dst = reinterpret_cast<float4 *>(st_base + S.merge_dst[g] * slot_stride);
-        const float4 *src = reinterpret_cast<const float4 *>(st_base + S.merge_src[g] * slot_stride);
-        for (int idx = tid; idx < DVT * DK / 4; idx += NT) {
-            float4 a = dst[idx];
-            const float4 b = src[idx];
-            a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
-            dst[idx] = a;
-        }
-    }
-    __syncthreads();
-    for (int g = 0; g < S.n_grp; ++g) {
-        const int lo = S.grp_lo[g], hi = S.grp_hi[g];
-        float *dst = st_base + S.grp_slot[g] * slot_stride;
-        const bool add = S.grp_add[g] != 0;
-        for (int tile = wave; tile < NTV * (DK / 16); tile += NW) {
-            const int mt = tile % NTV, nt = tile / NTV;
-            floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+    const int an = S.act_new, an_case = S.an_case;
+    uint32_t mine_jobs = 0;     // the wave's slots with a job (uniform)
+    {
+        const uint32_t jobs = __builtin_amdgcn_readfirstlane(S.jobs);
 #pragma unroll
-            for (int ks = 0; ks < kChunk / 32; ++ks) {
-                const int base = 32 * ks + 8 * lg;
-                if (32 * ks < hi && 32 * ks + 32 > lo) {
-                    Frag<__bf16> a, b;
-                    load_frag(a, &S.vt[16 * mt + lr][base]);
-                    mask_frag(a, base, lo, hi);
-                    load_frag(b, Y.ktf[nt][ks][lane]);
-                    mma32(acc, a, b);
+        for (int r = 0; r < SPW; ++r) mine_jobs |= ((jobs >> (NW * r + wave)) & 1u) << r;
+    }
+#pragma unroll
+    for (int r = 0; r < SPW; ++r) {
+        if (!((mine_jobs >> r) & 1u)) continue;
+        const int p = NW * r + wave;
+        // the new value in d_k tiles (rows 16 kt + 4 lg + e, column 16 nt + lr)
+        floatx4 acc[DK / 16][NTV];
+        const int jbase = __builtin_amdgcn_readfirstlane(S.jbase[p]);
+        const uint32_t jsrc = __builtin_amdgcn_readfirstlane(S.jsrc[p]);
+        const int lo = __builtin_amdgcn_readfirstlane(S.jlo[p]), hi = __builtin_amdgcn_readfirstlane(S.jhi[p]);
+        const uint32_t parts = (jbase ? 1u << p : 0u) | jsrc;
+#pragma unroll
+        for (int kt = 0; kt < DK / 16; ++kt)
+#pragma unroll
+            for (int nt = 0; nt < NTV; ++nt) acc[kt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (uint32_t pm = parts; pm; pm &= pm - 1) {
+            const int q = __builtin_ctz(pm);
+            if (q == act) {
+#pragma unroll
+                for (int kt = 0; kt < DK / 16; ++kt)
+#pragma unroll
+                    for (int nt = 0; nt < NTV; ++nt) acc[kt][nt] += actbuf[(kt * NTV + nt) * 64 + lane];
+            } else {
+                const float *src = st_base + q * slot_stride;
+#pragma unroll
+                for (int kt = 0; kt < DK / 16; ++kt)
+#pragma unroll
+                    for (int nt = 0; nt < NTV; ++nt) {
+                        const float4 v = *reinterpret_cast<const float4 *>(src + (16 * nt + lr) * DK + 16 * kt + 4 * lg);
+                        acc[kt][nt] += floatx4{v.x, v.y, v.z, v.w};
+                    }
+            }
+        }
+        if (hi > lo) {
+#pragma unroll
+            for (int kk = 0; kk < kChunk / 32; ++kk) {
+                if (32 * kk >= hi || 32 * kk + 32 <= lo) continue;
+                Frag<__bf16> b[NTV];
+#pragma unroll
+                for (int nt = 0; nt < NTV; ++nt) load_frag(b[nt], &S.vt[16 * nt + lr][32 * kk + 8 * lg]);
+#pragma unroll
+                for (int kt = 0; kt < DK / 16; ++kt) {
+                    Frag<__bf16> a;
+                    load_frag(a, Y.ktf[kt][kk][lane]);
+                    mask_frag(a, 32 * kk + 8 * lg, lo, hi);
+#pragma unroll
+                    for (int nt = 0; nt < NTV; ++nt) mma32(acc[kt][nt], a, b[nt]);
+                }
+            }
+        }
+        if (p == an) {
+            // an older state becomes the active one: hand it to the active-state waves
+#pragma unroll
+            for (int kt = 0; kt < DK / 16; ++kt)
+#pragma unroll
+                for (int nt = 0; nt < NTV; ++nt) anbuf[(kt * NTV + nt) * 64 + lane] = acc[kt][nt];
+            continue;
+        }
+        // fp32 value into the cache (a new state's slot may be the slot of a
+        // state merged away in this chunk, which another wave may still be
+        // reading: new states are written after the next barrier), normalised
+        // fp16 copy into the registers
+        float *dst = st_base + p * slot_stride;
+        float mx = 0.0f;
+#pragma unroll
+        for (int kt = 0; kt < DK / 16; ++kt)
+#pragma unroll
+            for (int nt = 0; nt < NTV; ++nt) {
+                const floatx4 v = acc[kt][nt];
+                if (jbase)
+                    *reinterpret_cast<float4 *>(dst + (16 * nt + lr) * DK + 16 * kt + 4 * lg) =
+                        make_float4(v[0], v[1], v[2], v[3]);
+                mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
+            }
+        const int e = f16_exponent(wave_max(mx));
+        if (lane == 0) S.shexp[p] = e;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int nt = 0; nt < NTV; ++nt)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    stk[r][ks][nt].v[j] = static_cast<_Float16>(ldexpf(acc[2 * ks][nt][j], -e));
+                    stk[r][ks][nt].v[4 + j] = static_cast<_Float16>(ldexpf(acc[2 * ks + 1][nt][j], -e));
+                }
+    }
+    // every merged-in value has been read (and anbuf written by the owner of an)
+    __syncthreads();
+    // new closed states: their fp32 values into the cache (recomputed from their tokens)
+#pragma unroll
+    for (int r = 0; r < SPW; ++r) {
+        if (!((mine_jobs >> r) & 1u)) continue;
+        const int p = NW * r + wave;
+        if (p == an || S.jbase[p]) continue;
+        const int lo = __builtin_amdgcn_readfirstlane(S.jlo[p]), hi = __builtin_amdgcn_readfirstlane(S.jhi[p]);
+        floatx4 acc[DK / 16][NTV];
+#pragma unroll
+        for (int kt = 0; kt < DK / 16; ++kt)
+#pragma unroll
+            for (int nt = 0; nt < NTV; ++nt) acc[kt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < kChunk / 32; ++kk) {
+            if (32 * kk >= hi || 32 * kk + 32 <= lo) continue;
+            Frag<__bf16> b[NTV];
+#pragma unroll
+            for (int nt = 0; nt < NTV; ++nt) load_frag(b[nt], &S.vt[16 * nt + lr][32 * kk + 8 * lg]);
+#pragma unroll
+            for (int kt = 0; kt < DK / 16; ++kt) {
+                Frag<__bf16> a;
+                load_frag(a, Y.ktf[kt][kk][lane]);
+                mask_frag(a, 32 * kk + 8 * lg, lo, hi);
+#pragma unroll
+                for (int nt = 0; nt < NTV; ++nt) mma32(acc[kt][nt], a, b[nt]);
+            }
+        }
+        float *dst = st_base + p * slot_stride;
+#pragma unroll
+        for (int kt = 0; kt < DK / 16; ++kt)
+#pragma unroll
+            for (int nt = 0; nt < NTV; ++nt)
+                *reinterpret_cast<float4 *>(dst + (16 * nt + lr) * DK + 16 * kt + 4 * lg) =
+                    make_float4(acc[kt][nt][0], acc[kt][nt][1], acc[kt][nt][2], acc[kt][nt][3]);
+    }
+    // the new active state into the accumulators
+    if (act_wave) {
+        if (an_case == 2) {
+#pragma unroll
+            for (int nt = 0; nt < NTV; ++nt)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) am[nt][h] = anbuf[((2 * kb + h) * NTV + nt) * 64 + lane];
+        } else {
+            const int lo = S.jlo[an], hi = S.jhi[an];
+            if (an_case == 1) {
+#pragma unroll
+                for (int nt = 0; nt < NTV; ++nt) {
+                    am[nt][0] = floatx4{0.f, 0.f, 0.f, 0.f};
+                    am[nt][1] = floatx4{0.f, 0.f, 0.f, 0.f};
                 }
             }
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float *p = dst + (16 * mt + 4 * lg + r) * DK + 16 * nt + lr;
-                *p = add ? (*p + acc[r]) : acc[r];
+            for (int kk = 0; kk < kChunk / 32; ++kk) {
+                if (32 * kk >= hi || 32 * kk + 32 <= lo) continue;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    Frag<__bf16> a;
+                    load_frag(a, Y.ktf[2 * kb + h][kk][lane]);
+                    mask_frag(a, 32 * kk + 8 * lg, lo, hi);
+#pragma unroll
+                    for (int nt = 0; nt < NTV; ++nt) {
+                        Frag<__bf16> b;
+                        load_frag(b, &S.vt[16 * nt + lr][32 * kk + 8 * lg]);
+                        mma32(am[nt][h], a, b);
+                    }
+                }
             }
         }
-    }
-    __syncthreads();
-    const int an = S.act_new;
-    // normalised fp16 copies of the changed closed states
-    for (int cc = 0; cc < S.n_changed; ++cc) {
-        const int slot = S.changed[cc];
-        if (slot == an) continue;
-        const float4 *src = reinterpret_cast<const float4 *>(st_base + slot * slot_stride);
-        float mx = 0.0f;
-        for (int idx = tid; idx < DVT * DK / 4; idx += NT) {
-            const float4 a = src[idx];
-            mx = fmaxf(mx, fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))));
-        }
-        mx = wave_max(mx);
-        __syncthreads();
-        if (lane == 0) S.red[wave] = mx;
-        __syncthreads();
-        float all = S.red[0];
-#pragma unroll
-        for (int u = 1; u < NW; ++u) all = fmaxf(all, S.red[u]);
-        const int e = f16_exponent(all);
-        _Float16 *dst = sh_base + slot * slot_stride;
-        for (int idx = tid; idx < DVT * DK / 8; idx += NT) {
-            const float4 a = src[2 * idx];
-            const float4 b = src[2 * idx + 1];
-            f16x8 o;
-            o[0] = static_cast<_Float16>(ldexpf(a.x, -e)); o[1] = static_cast<_Float16>(ldexpf(a.y, -e));
-            o[2] = static_cast<_Float16>(ldexpf(a.z, -e)); o[3] = static_cast<_Float16>(ldexpf(a.w, -e));
-            o[4] = static_cast<_Float16>(ldexpf(b.x, -e)); o[5] = static_cast<_Float16>(ldexpf(b.y, -e));
-            o[6] = static_cast<_Float16>(ldexpf(b.z, -e)); o[7] = static_cast<_Float16>(ldexpf(b.w, -e));
-            reinterpret_cast<f16x8 *>(dst)[idx] = o;
-        }
-        if (tid == 0) S.shexp[slot] = e;
-    }
-    __syncthreads();
-    // owner waves reload the register copies of the changed closed states
-    const uint32_t reload = __builtin_amdgcn_readfirstlane(S.reload);
-#pragma unroll
-    for (int r = 0; r < SPW; ++r) {
-        const int slot = NW * r + wave;
-        if ((reload >> slot) & 1u) {
-            const _Float16 *src = sh_base + slot * slot_stride;
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-                for (int nt = 0; nt < NTV; ++nt)
-                    perm_frag_f16(stk[r][ks][nt], src + (16 * nt + lr) * DK, 32 * ks + 4 * lg);
-        }
-    }
-    // the new active state into the accumulators
-    if (an >= 0 && act_wave) {
-        const float *src = st_base + an * slot_stride;
-#pragma unroll
-        for (int nt = 0; nt < NTV; ++nt)
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const float4 a = *reinterpret_cast<const float4 *>(src + (16 * nt + lr) * DK + 32 * kb + 16 * h +
-                                                                  4 * lg);
-                am[nt][h] = floatx4{a.x, a.y, a.z, a.w};
-            }
         c.ea = refresh_active<NTV>(am, af);
     }
     const int mnew = S.m_new;
@@ -801,7 +883,7 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
 template <int DK, int DVT, int SPW>
 __global__ __launch_bounds__(kRsThreads, 2) void k_prefill_rs(
     const __bf16 *__restrict__ V, __bf16 *__restrict__ O, int T, int C, int DV, int nblk_dv,
-    float *__restrict__ states, _Float16 *__restrict__ shadow, const int2 *__restrict__ events,
+    float *__restrict__ states, const int2 *__restrict__ events,
     const int32_t *__restrict__ chunk_ev, const uint8_t *__restrict__ rec, const int32_t *__restrict__ qexp_g,
     uint8_t *__restrict__ meta_base, size_t meta_stride, int32_t *__restrict__ m_t_out)
 {
@@ -839,7 +921,6 @@ __global__ __launch_bounds__(kRsThreads, 2) void k_prefill_rs(
     A.tok0 = static_cast<size_t>(A.bh) * T;
     A.slot_stride = static_cast<size_t>(DV) * DK;
     A.st_base = states + static_cast<size_t>(A.bh) * C * DV * DK + static_cast<size_t>(A.dv0) * DK;
-    A.sh_base = shadow + static_cast<size_t>(A.bh) * C * DV * DK + static_cast<size_t>(A.dv0) * DK;
     A.cev = chunk_ev + static_cast<size_t>(A.bh) * (A.NCH + 1);
     const int tid = A.tid, wave = A.wave, lr = A.lr, lg = A.lg, NCH = A.NCH;
 
@@ -914,8 +995,7 @@ static hipError_t launch_rs(const PrefillArgs &a, hipStream_t stream)
     }
     hipLaunchKernelGGL((k_prefill_rs<DK, DVT, SPW>), dim3(BH * nblk_dv), dim3(kRsThreads), 0, stream,
                        static_cast<const __bf16 *>(a.v), static_cast<__bf16 *>(a.o), a.T, a.g.C, a.g.dv,
-                       nblk_dv, a.states, static_cast<_Float16 *>(a.ws.shadow), a.ws.events, a.ws.chunk_ev,
-                       static_cast<const uint8_t *>(a.ws.rec), a.ws.qexp, a.meta, a.g.meta_stride, a.sched.m_t);
+                       nblk_dv, a.states, a.ws.events, a.ws.chunk_ev, static_cast<const uint8_t *>(a.ws.rec), a.ws.qexp, a.meta, a.g.meta_stride, a.sched.m_t);
     hipError_t e = hipGetLastError();
     if (e == hipSuccess && a.ev_after) e = hipEventRecord(a.ev_after, stream);
     return e;

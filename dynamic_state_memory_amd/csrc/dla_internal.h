@@ -68,13 +68,15 @@ struct Workspace {
     // per-chunk operands built by the chunk pre-pass (register-resident path)
     // [BH][NCH] chunk records of the register-resident prefill, each
     // rs_record_bytes(d_k) long: fp16 query fragments [4][DK/32][64][8],
-    // bf16 lam [32][64] (slot-major), bf16 fragments of (Q K^T) o W
-    // [4][2][64][8], bf16 fragments of K^T [DK/16][2][64][8]
+    // bf16 read weights [32][64] (row i: lam_t of the slot that the state
+    // with chronological index i at the chunk start is read with at token t),
+    // bf16 fragments of (Q K^T) o W [4][2][64][8], bf16 fragments of K^T
+    // [DK/16][2][64][8]
     void *rec;
     int32_t *qexp;       // [BH][NCH] power-of-two exponent of each chunk's fp16 query
 };
-constexpr int kPrepCmax = 32;   // lam slots kept per chunk by the pre-pass
-// chunk record of the register-resident prefill: query fragments, lam,
+constexpr int kPrepCmax = 32;   // read-weight rows kept per chunk by the pre-pass
+// chunk record of the register-resident prefill: query fragments, read weights,
 // weighted-score fragments, key fragments (bytes; each part a multiple of 16)
 constexpr size_t rs_rec_q_bytes(int dk) { return 2ull * 64 * dk; }
 constexpr size_t rs_rec_a_bytes(int dk) { return rs_rec_q_bytes(dk) + 2ull * 32 * 64; }

@@ -11,10 +11,12 @@
 // Two kernels:
 //   k_chunk_prep  one block per (stream, 64-token chunk), all chunks in
 //                 parallel: the operands of the chunk that do not depend on
-//                 the state, in MFMA-fragment order -- the query as fp16
-//                 scaled by a power of two, lam transposed, K transposed, and
-//                 the intra-chunk slot-weighted causal product
-//                 P = (Q K^T) o W, W[t][s] = lam_t[#live chunk starts > s].
+//                 the state values, in MFMA-fragment order -- the query as
+//                 fp16 scaled by a power of two, the read weight of every
+//                 state live at the chunk start for every token (from the
+//                 schedule alone), K transposed, and the intra-chunk
+//                 slot-weighted causal product P = (Q K^T) o W,
+//                 W[t][s] = lam_t[#live chunk starts > s].
 //   k_prefill_rs  one block (4 waves) per (stream, d_v slice of DVT columns)
 //                 sweeping the stream's chunks in order.  It keeps every
 //                 closed state (all but the most recent) of the slice as fp16
@@ -24,10 +26,11 @@
 //                 recent ("active") state as fp32 MFMA accumulators (d_k rows
 //                 32w..32w+31 in wave w) plus an fp16 operand copy.  A chunk
 //                 without events touches no state memory: read, P V, then
-//                 V_c^T K_c accumulated into the active state's registers.  A
-//                 chunk with events flushes the active state to the fp32 cache,
-//                 runs the general update there (merges, per-group V_g^T K_g)
-//                 and reloads the register copies of the states it changed.
+//                 V_c^T K_c accumulated into the active state's registers.  In
+//                 a chunk with events the wave owning each changed slot builds
+//                 its new fp32 value in registers (own value, merged-in
+//                 values, V_g^T K_g of its tokens), writes it to the fp32 cache
+//                 and converts it into its register copy.
 //
 // Operand order of the read: the reduction index d_k of a 32-wide step is
 // split over lane groups g = lane / 16 as {4g..4g+3, 16+4g..16+4g+3}, the
@@ -85,13 +88,14 @@ template <int DK>
 __global__ __launch_bounds__(256) void k_chunk_prep(
     const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, const __bf16 *__restrict__ LAM, int T, int C,
     const int2 *__restrict__ events, const int32_t *__restrict__ chunk_ev, uint8_t *__restrict__ rec,
-    int32_t *__restrict__ qexp_out)
+    int32_t *__restrict__ qexp_out, int32_t *__restrict__ m_t_out)
 {
     constexpr int KS = DK / 32;
     __shared__ __align__(16) __bf16 q[kChunk][DK + 8];
     __shared__ __align__(16) __bf16 k[kChunk][DK + 8];
     __shared__ __align__(16) __bf16 pw[kChunk][kChunk + 8];
     __shared__ float lam[kChunk][kPrepCmax + 1];
+    __shared__ uint64_t om[kChunk];
     __shared__ uint64_t nm[kChunk];
     __shared__ int2 evs[kChunk];
     __shared__ float red[4];
@@ -102,10 +106,10 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
     const size_t tok0 = static_cast<size_t>(bh) * T;
     const size_t cb = static_cast<size_t>(bh) * NCH + ch;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    // this chunk's record: query fragments, lam, weighted-score fragments, key fragments
+    // this chunk's record: query fragments, read weights, weighted-score fragments, key fragments
     uint8_t *rb = rec + cb * rs_record_bytes(DK);
     f16x8 *q16f = reinterpret_cast<f16x8 *>(rb);
-    __bf16 *lamT = reinterpret_cast<__bf16 *>(rb + rs_rec_q_bytes(DK));
+    __bf16 *wrow = reinterpret_cast<__bf16 *>(rb + rs_rec_q_bytes(DK));
     bf16x8 *pwf = reinterpret_cast<bf16x8 *>(rb + rs_rec_a_bytes(DK));
     bf16x8 *ktf = reinterpret_cast<bf16x8 *>(rb + rs_rec_a_bytes(DK) + 2 * kChunk * kChunk);
     const int lr = lane & 15, lg = lane >> 4;
@@ -135,6 +139,9 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
     }
     const int e0 = chunk_ev[static_cast<size_t>(bh) * (NCH + 1) + ch];
     const int nev = chunk_ev[static_cast<size_t>(bh) * (NCH + 1) + ch + 1] - e0;
+    // states live at the chunk start: the cache starts empty, every boundary
+    // opens a state and a merge keeps the count at C
+    const int m0 = min(C, e0);
     if (tid < nev) evs[tid] = events[tok0 + e0 + tid];
     qmax = wave_max(qmax);
     if (lane == 0) red[wave] = qmax;
@@ -142,17 +149,22 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
     const int qexp = f16_exponent(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
     if (tid == 0) qexp_out[cb] = qexp;
     if (tid < kChunk) {
-        // bit p: the state opened at chunk position p is live after token tid
-        uint64_t m = 0;
+        // bit i of o: the state with chronological index i at the chunk start
+        // is live after token tid; bit p of m: the state opened at chunk
+        // position p is live after token tid
+        uint64_t o = low_bits(m0), m = 0;
         for (int e = 0; e < nev; ++e) {
             const int2 ev = evs[e];
             const int pos = ev.x - c0;
             if (tid >= pos) {
                 m |= 1ull << pos;
                 if (ev.y >= 64) m &= ~(1ull << (ev.y - 64));
+                else if (ev.y >= 0) o &= ~(1ull << ev.y);
             }
         }
+        om[tid] = o;
         nm[tid] = m;
+        if (m_t_out && tid < nvalid) m_t_out[tok0 + c0 + tid] = __popcll(o) + __popcll(m);
     }
     // fp16 query fragments (permuted reduction order)
 #pragma unroll
@@ -168,12 +180,6 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
             h[4 + e] = static_cast<_Float16>(ldexpf(static_cast<float>(row[cc + 16 + e]), -qexp));
         }
         q16f[f] = h;
-    }
-    // lam, slot-major
-#pragma unroll
-    for (int j = 0; j < kPrepCmax / 4; ++j) {
-        const int idx = tid + 256 * j;
-        lamT[idx] = static_cast<__bf16>(lam[idx & (kChunk - 1)][idx / kChunk]);
     }
     // K^T fragments: d_k rows of a 16-tile, 8 consecutive tokens per lane
 #pragma unroll
@@ -221,6 +227,18 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
         const int l = f & 63, ks2 = (f >> 6) & 1, mt = f >> 7;
         pwf[f] = *reinterpret_cast<const bf16x8 *>(&pw[16 * mt + (l & 15)][32 * ks2 + 8 * (l >> 4)]);
     }
+    // read weights by chronological index: a state live at the chunk start is
+    // read at token t with the slot of the nearest older state still live
+    // (itself, or the state it was merged into), i.e. after every live state
+    // that is more recent, old or new; 0 for rows without a state
+#pragma unroll
+    for (int j = 0; j < kPrepCmax / 4; ++j) {
+        const int idx = tid + 256 * j;
+        const int t = idx & (kChunk - 1), i = idx / kChunk;
+        float w = 0.0f;
+        if (i < m0) w = lam[t][__popcll(shr64(om[t], i + 1)) + __popcll(nm[t])];
+        wrow[idx] = static_cast<__bf16>(w);
+    }
 }
 
 // ------------------------------------------------------------ the sweep
@@ -236,7 +254,7 @@ constexpr int kRsThreads = 64 * kRsWaves;
 template <int DK>
 struct RsStageA {
     _Float16 qf[kChunk / 16][DK / 32][64][8];   // query fragments (permuted reduction order)
-    __bf16 lamT[kPrepCmax][kChunk];              // lam, slot-major
+    __bf16 wr[kPrepCmax][kChunk];                // read weights by chronological index of the state
 };
 template <int DK>
 struct RsStageB {
@@ -258,9 +276,7 @@ struct RsSmem {
     float W[CMAX < 32 ? 32 : CMAX][kChunk];
     float wact[DK / 32][kChunk];  // active-state read weights, one row per active wave
     floatx4 ored[kRsWaves][kChunk / 16][DVT / 16][64];  // partial reads: wave, row tile, column tile, lane
-    uint64_t om[kChunk];
-    uint64_t nm[kChunk];
-    int32_t order[kMaxC];
+    int32_t order[kMaxC];       // physical slot of each live state, oldest first
     int32_t new_order[kMaxC];
     // per physical slot, what a chunk with events does to the state in it:
     // its new value is (own value if jbase) + (values of the slots in jsrc,
@@ -270,14 +286,14 @@ struct RsSmem {
     int32_t jlo[kMaxC];
     int32_t jhi[kMaxC];
     int32_t shexp[kMaxC];
-    int32_t inv[kMaxC];         // chronological index of the state in each physical slot
-    int2 evs[kChunk];           // the chunk's events (at most one per token)
-    // read-weight source of physical slot p in a chunk without events: lam
-    // row m0 - 1 - (chronological index) and 2^(state exponent); 0 for a slot
-    // without a closed state (rewritten after every chunk with events)
+    // read weights of physical slot p: row jrow[p] of the chunk's weight table
+    // (the chronological index of its state) times wsc[p] = 2^(state
+    // exponent); 0 for a slot without a closed state (rewritten after every
+    // chunk with events)
     int32_t jrow[CMAX];
     float wsc[CMAX];
     uint32_t jobs;              // slots whose new value an owner wave builds
+    uint32_t closed_new;        // slots of the closed states after the chunk
     int32_t m_new, act_new, an_case;
 };
 
@@ -343,7 +359,6 @@ struct RsCarry {
     int eA, eB, eC;                              // event offsets of chunks ch, ch + 1, ch + 2 (at chunk ch)
     int qexpn;                                   // next chunk's query exponent
     uint32_t closed;                             // physical slots of the closed states (uniform)
-    bool refresh_w;
 };
 
 // Per-block constants of the sweep.
@@ -354,7 +369,6 @@ struct RsParams {
     const int2 *events;
     const uint8_t *rec;         // chunk records
     const int32_t *qexp_g;
-    int32_t *m_t_out;
     int bh, dv0, tid, lane, wave, lr, lg, NCH, vr, vc;
     uint32_t v_off;             // byte offset of this thread's V piece within a chunk's rows
     uint32_t o_off;             // byte offset of this lane's first output within a chunk
@@ -390,7 +404,6 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
     const int NCH = A.NCH, vr = A.vr, vc = A.vc;
     const size_t tok0 = A.tok0, slot_stride = A.slot_stride;
     float *st_base = A.st_base;
-    int32_t *m_t_out = A.m_t_out;
     auto &stk = c.stk;
     auto &am = c.am;
     auto &af = c.af;
@@ -421,63 +434,17 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
 #pragma unroll
         for (int e = 0; e < 8; ++e) S.vt[vc + e][vr] = ve[e];
     }
-    if (tid < nev) S.evs[tid] = evcur;
-    if (c.refresh_w) {
-        if (tid < CMAX) {
-            const bool live = (c.closed >> tid) & 1u;
-            S.jrow[tid] = live ? c.m0 - 1 - S.inv[tid] : 0;
-            S.wsc[tid] = live ? ldexpf(1.0f, S.shexp[tid]) : 0.0f;
-        }
-        c.refresh_w = false;
-        lds_barrier();
-    }
+    // read weights: closed states by slot, from the row of their
+    // chronological index (wsc is 0 for a slot without a closed state); the
+    // active state is the most recent one (each wave writes and reads only
+    // its own rows)
     const float qsc = ldexpf(1.0f, qexp);
-    if (has_ev) {
-        // token masks (wave 0, which also wrote the events): bit i of om_t =
-        // state i of the chunk start live after token t, bit p of nm_t =
-        // state opened at chunk position p live after token t
-        if (tid < kChunk) {
-            uint64_t om = low_bits(c.m0), nm = 0;
-            for (int e = 0; e < nev; ++e) {
-                const int2 ev = S.evs[e];
-                const int pos = ev.x - c0;
-                if (tid >= pos) {
-                    nm |= 1ull << pos;
-                    if (ev.y >= 64) nm &= ~(1ull << (ev.y - 64));
-                    else if (ev.y >= 0) om &= ~(1ull << ev.y);
-                }
-            }
-            S.om[tid] = om;
-            S.nm[tid] = nm;
-            if (m_t_out && dv0 == 0 && tid < nvalid) m_t_out[tok0 + c0 + tid] = __popcll(om) + __popcll(nm);
-        }
-        lds_barrier();
-        // read weights per token: thread (wave, lane) fills the rows of the
-        // wave's slots for token lane, so each wave reads only rows it wrote
-        // (a row of a slot without a closed state gets 0 and is never read)
-        const uint64_t om_t = S.om[lane], nm_t = S.nm[lane];
 #pragma unroll
-        for (int r = 0; r < SPW; ++r) {
-            const int p = NW * r + wave;
-            const bool live = (c.closed >> p) & 1u;
-            const int slot = live ? __popcll(shr64(om_t, S.inv[p] + 1)) + __popcll(nm_t) : 0;
-            const float w = ldexpf(static_cast<float>(X.lamT[slot][lane]), S.shexp[p] + qexp);
-            S.W[p][lane] = live ? w : 0.0f;
-        }
-        if (act_wave)
-            S.wact[kb][lane] = ldexpf(static_cast<float>(X.lamT[__popcll(nm_t)][lane]), qexp + c.ea);
-    } else {
-        if (m_t_out && dv0 == 0 && tid < nvalid) m_t_out[tok0 + c0 + tid] = c.m0;
-        // a closed state's slot is the same for every token of the chunk
-        // (wsc is 0 for a slot without a closed state)
-#pragma unroll
-        for (int r = 0; r < SPW; ++r) {
-            const int p = NW * r + wave;
-            S.W[p][lane] = static_cast<float>(X.lamT[S.jrow[p]][lane]) * (S.wsc[p] * qsc);
-        }
-        if (act_wave) S.wact[kb][lane] = static_cast<float>(X.lamT[0][lane]) * ldexpf(qsc, c.ea);
+    for (int r = 0; r < SPW; ++r) {
+        const int p = NW * r + wave;
+        S.W[p][lane] = static_cast<float>(X.wr[S.jrow[p]][lane]) * (S.wsc[p] * qsc);
     }
-
+    if (act_wave) S.wact[kb][lane] = static_cast<float>(X.wr[c.m0 > 0 ? c.m0 - 1 : 0][lane]) * ldexpf(qsc, c.ea);
     // ---- inter-chunk read: closed states from registers, then the active state
     floatx4 Oi[MT][NTV];
 #pragma unroll
@@ -634,65 +601,88 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
     floatx4 *anbuf = &S.ored[0][0][0][0];                           // [DK / 16][NTV][64]
     static_assert((DK / 16) * NTV * 64 * sizeof(floatx4) <= sizeof(S.W), "the active state fits the weight table");
     static_assert((DK / 16) * NTV * 64 <= NW * MT * NTV * 64, "a state slice fits the partial-read buffer");
-    if (tid == 0) {
-        const int tl = nvalid - 1;
-        const uint64_t oa = S.om[tl], na = S.nm[tl];
-        uint32_t used = 0, jobs = 0;
-        int nold = 0, last_old = -1, tgt = -1;
-        for (int i = 0; i < m0; ++i) {
-            const int p = S.order[i];
-            if ((oa >> i) & 1ull) {
-                S.new_order[nold++] = p;
-                used |= 1u << p;
-                last_old = i;
-                tgt = p;
-                S.jbase[p] = 1;
-                S.jsrc[p] = 0;
-                S.jlo[p] = 0;
-                S.jhi[p] = 0;
-            } else {
-                // a state merged away joins the nearest older live state (the
-                // oldest state is never merged away, so tgt >= 0)
-                S.jsrc[tgt] |= 1u << p;
-                jobs |= 1u << tgt;
+    if (wave == 0) {
+        // the chunk's events are in the registers of lanes 0 .. nev - 1: the
+        // live states at its end (bit i of oa: old state i, bit p of na: the
+        // state opened at chunk position p) and the slots the old ones keep
+        uint64_t oa = low_bits(m0), na = 0;
+        uint32_t used = c.closed | (act >= 0 ? 1u << act : 0u);
+        for (int e = 0; e < nev; ++e) {
+            const int pos = __builtin_amdgcn_readlane(evcur.x, e) - c0;
+            const int d = __builtin_amdgcn_readlane(evcur.y, e);
+            na |= 1ull << pos;
+            if (d >= 64) {
+                na &= ~(1ull << (d - 64));
+            } else if (d >= 0) {
+                oa &= ~(1ull << d);
+                used &= ~(1u << S.order[d]);
             }
         }
-        const int first_new = na ? __ffsll(static_cast<unsigned long long>(na)) - 1 : nvalid;
-        if (first_new > 0 && last_old >= 0) {
-            // the chunk's tokens before its first new state join the last old state
-            const int p = S.order[last_old];
+        // old states still live keep their value and their order (lane i: old state i)
+        if (lane < m0 && ((oa >> lane) & 1ull)) {
+            const int p = S.order[lane];
+            S.new_order[__popcll(oa & low_bits(lane))] = p;
+            S.jbase[p] = 1;
+            S.jsrc[p] = 0;
             S.jlo[p] = 0;
-            S.jhi[p] = first_new;
-            jobs |= 1u << p;
+            S.jhi[p] = 0;
         }
-        int mnew = nold;
-        uint64_t rest = na;
-        while (rest) {
-            const int pos = __ffsll(static_cast<unsigned long long>(rest)) - 1;
+        uint32_t jobs = 0;
+        // a state merged away joins the nearest older live state (the oldest
+        // state is never merged away) and is no longer read
+        for (uint64_t dead = low_bits(m0) & ~oa; dead; dead &= dead - 1) {
+            const int i = __builtin_ctzll(dead);
+            const uint64_t older = oa & low_bits(i);
+            const int tp = S.order[older ? 63 - __builtin_clzll(older) : 0];
+            const int dp = S.order[i];
+            if (lane == 0) {
+                S.jsrc[tp] |= 1u << dp;
+                S.jrow[dp] = 0;
+                S.wsc[dp] = 0.0f;
+            }
+            jobs |= 1u << tp;
+        }
+        const int nold = __popcll(oa);
+        const int last_p = nold ? S.order[63 - __builtin_clzll(oa)] : -1;
+        const int first_new = na ? __builtin_ctzll(na) : nvalid;
+        if (first_new > 0 && nold > 0) {
+            // the chunk's tokens before its first new state join the last old state
+            if (lane == 0) S.jhi[last_p] = first_new;
+            jobs |= 1u << last_p;
+        }
+        int mnew = nold, an = last_p;
+        for (uint64_t rest = na; rest;) {
+            const int pos = __builtin_ctzll(rest);
             rest &= rest - 1;
-            const int q = rest ? __ffsll(static_cast<unsigned long long>(rest)) - 1 : nvalid;
-            const int slot = __ffs(~used) - 1;          // lowest free slot (at most C states live)
+            const int q = rest ? __builtin_ctzll(rest) : nvalid;
+            const int slot = __builtin_ctz(~used);        // lowest free slot (at most C states live)
             used |= 1u << slot;
-            S.new_order[mnew++] = slot;
-            S.jbase[slot] = 0;
-            S.jsrc[slot] = 0;
-            S.jlo[slot] = pos;
-            S.jhi[slot] = q;
+            if (lane == 0) {
+                S.new_order[mnew] = slot;
+                S.jbase[slot] = 0;
+                S.jsrc[slot] = 0;
+                S.jlo[slot] = pos;
+                S.jhi[slot] = q;
+            }
+            ++mnew;
+            an = slot;
             jobs |= 1u << slot;
         }
-        const int an = S.new_order[mnew - 1];
         // the previous active state, still live but no longer the most recent, closes
         if (act >= 0 && act != an && ((oa >> (m0 - 1)) & 1ull)) jobs |= 1u << act;
         // the new active state: 0 = the same state (tokens added), 1 = a new
         // state (set from its tokens; it may sit in the slot of the previous
         // active state when that one was merged away), 2 = an older state
         // (built by its owner)
-        const int an_case = S.jbase[an] == 0 ? 1 : (an == act ? 0 : 2);
+        const int an_case = na ? 1 : (an == act ? 0 : 2);
         if (an_case != 2) jobs &= ~(1u << an);
-        S.jobs = jobs;
-        S.m_new = mnew;
-        S.act_new = an;
-        S.an_case = an_case;
+        if (lane == 0) {
+            S.jobs = jobs;
+            S.closed_new = used & ~(1u << an);
+            S.m_new = mnew;
+            S.act_new = an;
+            S.an_case = an_case;
+        }
     }
     if (act >= 0 && act_wave) {
 #pragma unroll
@@ -700,7 +690,11 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
 #pragma unroll
             for (int h = 0; h < 2; ++h) actbuf[((2 * kb + h) * NTV + nt) * 64 + lane] = am[nt][h];
     }
-    __syncthreads();
+    // LDS-only barriers from here on: the loads in flight (next chunk's
+    // operands) and the stores of this chunk drain behind them; a state's
+    // fp32 value written here is read by another wave only in a later chunk,
+    // after the chunk-start barrier that waits for every wave's stores
+    lds_barrier();
     const int an = S.act_new, an_case = S.an_case;
     uint32_t mine_jobs = 0;     // the wave's slots with a job (uniform)
     {
@@ -793,8 +787,9 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
                     stk[r][ks][nt].v[4 + j] = static_cast<_Float16>(ldexpf(acc[2 * ks + 1][nt][j], -e));
                 }
     }
-    // every merged-in value has been read (and anbuf written by the owner of an)
-    __syncthreads();
+    // every merged-in value has been read (the loads have returned, their
+    // values are used) and anbuf is written by the owner of an
+    lds_barrier();
     // new closed states: their fp32 values into the cache (recomputed from their tokens)
 #pragma unroll
     for (int r = 0; r < SPW; ++r) {
@@ -865,16 +860,21 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
         }
         c.ea = refresh_active<NTV>(am, af);
     }
-    const int mnew = S.m_new;
-    uint32_t cl = 0;
-    for (int i = 0; i + 1 < mnew; ++i) cl |= 1u << S.new_order[i];
-    __syncthreads();
-    if (tid < kMaxC) S.order[tid] = tid < mnew ? S.new_order[tid] : 0;
-    if (tid < mnew) S.inv[S.new_order[tid]] = tid;
+    const int mnew = __builtin_amdgcn_readfirstlane(S.m_new);
+    const uint32_t cl = __builtin_amdgcn_readfirstlane(S.closed_new);
+    lds_barrier();
+    // the new order; read weights of the closed states from the next chunk on
+    // (their exponents are final; the slots merged away were cleared)
+    if (tid < mnew) {
+        const int p = S.new_order[tid];
+        S.order[tid] = p;
+        const bool closed = tid + 1 < mnew;
+        S.jrow[p] = closed ? tid : 0;
+        S.wsc[p] = closed ? ldexpf(1.0f, S.shexp[p]) : 0.0f;
+    }
     c.m0 = mnew;
     c.act = an;
     c.closed = cl;
-    c.refresh_w = true;
     c.eA = c.eB;
     c.eB = c.eC;
     c.eC = eD;
@@ -885,7 +885,7 @@ __global__ __launch_bounds__(kRsThreads, 2) void k_prefill_rs(
     const __bf16 *__restrict__ V, __bf16 *__restrict__ O, int T, int C, int DV, int nblk_dv,
     float *__restrict__ states, const int2 *__restrict__ events,
     const int32_t *__restrict__ chunk_ev, const uint8_t *__restrict__ rec, const int32_t *__restrict__ qexp_g,
-    uint8_t *__restrict__ meta_base, size_t meta_stride, int32_t *__restrict__ m_t_out)
+    uint8_t *__restrict__ meta_base, size_t meta_stride)
 {
     constexpr int KS = DK / 32;
     constexpr int NTV = DVT / 16;
@@ -903,7 +903,6 @@ __global__ __launch_bounds__(kRsThreads, 2) void k_prefill_rs(
     RsParams A;
     A.V = V; A.O = O; A.T = T; A.C = C; A.DV = DV;
     A.events = events; A.rec = rec; A.qexp_g = qexp_g;
-    A.m_t_out = m_t_out;
     A.bh = lin / nblk_dv;
     A.dv0 = (lin % nblk_dv) * DVT;
     A.tid = threadIdx.x;
@@ -942,7 +941,6 @@ __global__ __launch_bounds__(kRsThreads, 2) void k_prefill_rs(
     c.m0 = 0;
     c.act = -1;
     c.closed = 0;
-    c.refresh_w = false;
     if (tid < kMaxC) { S.order[tid] = tid; S.shexp[tid] = 0; }
 
     // chunk 0: part A into LDS, V and events into registers
@@ -986,7 +984,7 @@ static hipError_t launch_rs(const PrefillArgs &a, hipStream_t stream)
     hipLaunchKernelGGL((k_chunk_prep<DK>), dim3(NCH, BH), dim3(256), 0, stream,
                        static_cast<const __bf16 *>(a.q), static_cast<const __bf16 *>(a.k),
                        static_cast<const __bf16 *>(a.lam), a.T, a.g.C, a.ws.events, a.ws.chunk_ev,
-                       static_cast<uint8_t *>(a.ws.rec), a.ws.qexp);
+                       static_cast<uint8_t *>(a.ws.rec), a.ws.qexp, a.sched.m_t);
     hipError_t e0 = hipGetLastError();
     if (e0 != hipSuccess) return e0;
     if (a.ev_before) {
@@ -995,7 +993,7 @@ static hipError_t launch_rs(const PrefillArgs &a, hipStream_t stream)
     }
     hipLaunchKernelGGL((k_prefill_rs<DK, DVT, SPW>), dim3(BH * nblk_dv), dim3(kRsThreads), 0, stream,
                        static_cast<const __bf16 *>(a.v), static_cast<__bf16 *>(a.o), a.T, a.g.C, a.g.dv,
-                       nblk_dv, a.states, a.ws.events, a.ws.chunk_ev, static_cast<const uint8_t *>(a.ws.rec), a.ws.qexp, a.meta, a.g.meta_stride, a.sched.m_t);
+                       nblk_dv, a.states, a.ws.events, a.ws.chunk_ev, static_cast<const uint8_t *>(a.ws.rec), a.ws.qexp, a.meta, a.g.meta_stride);
     hipError_t e = hipGetLastError();
     if (e == hipSuccess && a.ev_after) e = hipEventRecord(a.ev_after, stream);
     return e;

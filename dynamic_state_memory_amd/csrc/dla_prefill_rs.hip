@@ -455,9 +455,11 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
 #pragma unroll
     for (int r = 0; r < SPW; ++r) mine |= ((c.closed >> (NW * r + wave)) & 1u) << r;
     // one 16-token row tile at a time keeps a quarter of the query fragments
-    // live; the wave's slots go in pairs (two independent product chains),
-    // a pair is skipped when neither slot holds a closed state (a slot without
-    // one has weight 0 and finite operands)
+    // live; the wave's slots go in pairs (two independent product chains)
+    // and every slot is read (a slot without a closed state has weight 0 and
+    // finite operands): with no branch between them the products of one pair
+    // overlap the weighting of the previous one, and the slowest blocks (full
+    // caches) have every slot live anyway
     static_assert(SPW % 2 == 0, "slots are read in pairs");
     if (mine != 0u) {
 #pragma unroll
@@ -467,7 +469,6 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
             for (int ks = 0; ks < KS; ++ks) load_frag(qf[ks], X.qf[mt][ks][lane]);
 #pragma unroll
             for (int r2 = 0; r2 < SPW; r2 += 2) {
-                if (!((mine >> r2) & 3u)) continue;
                 floatx4 P0[NTV], P1[NTV];
 #pragma unroll
                 for (int nt = 0; nt < NTV; ++nt) {
@@ -485,10 +486,10 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
                 const float4 w1 = *reinterpret_cast<const float4 *>(&S.W[NW * (r2 + 1) + wave][16 * mt + 4 * lg]);
 #pragma unroll
                 for (int nt = 0; nt < NTV; ++nt) {
-                    Oi[mt][nt][0] += w0.x * P0[nt][0] + w1.x * P1[nt][0];
-                    Oi[mt][nt][1] += w0.y * P0[nt][1] + w1.y * P1[nt][1];
-                    Oi[mt][nt][2] += w0.z * P0[nt][2] + w1.z * P1[nt][2];
-                    Oi[mt][nt][3] += w0.w * P0[nt][3] + w1.w * P1[nt][3];
+                    Oi[mt][nt][0] = fmaf(w1.x, P1[nt][0], fmaf(w0.x, P0[nt][0], Oi[mt][nt][0]));
+                    Oi[mt][nt][1] = fmaf(w1.y, P1[nt][1], fmaf(w0.y, P0[nt][1], Oi[mt][nt][1]));
+                    Oi[mt][nt][2] = fmaf(w1.z, P1[nt][2], fmaf(w0.z, P0[nt][2], Oi[mt][nt][2]));
+                    Oi[mt][nt][3] = fmaf(w1.w, P1[nt][3], fmaf(w0.w, P0[nt][3], Oi[mt][nt][3]));
                 }
             }
         }
@@ -503,10 +504,10 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
             for (int nt = 0; nt < NTV; ++nt) {
                 floatx4 P = floatx4{0.f, 0.f, 0.f, 0.f};
                 mma32(P, qa, af[nt]);
-                Oi[mt][nt][0] += w.x * P[0];
-                Oi[mt][nt][1] += w.y * P[1];
-                Oi[mt][nt][2] += w.z * P[2];
-                Oi[mt][nt][3] += w.w * P[3];
+                Oi[mt][nt][0] = fmaf(w.x, P[0], Oi[mt][nt][0]);
+                Oi[mt][nt][1] = fmaf(w.y, P[1], Oi[mt][nt][1]);
+                Oi[mt][nt][2] = fmaf(w.z, P[2], Oi[mt][nt][2]);
+                Oi[mt][nt][3] = fmaf(w.w, P[3], Oi[mt][nt][3]);
             }
         }
     }

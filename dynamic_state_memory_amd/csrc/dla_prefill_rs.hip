@@ -346,6 +346,54 @@ __device__ __forceinline__ void stage_b(RsStageB<DK> &Y, const uint8_t *rec, siz
         reinterpret_cast<u32x4 *>(&Y), tid, wave);
 }
 
+// The closed-state part of the inter-chunk read over the wave's first NP slot
+// pairs: one 16-token row tile at a time (a quarter of the query fragments
+// live), two independent product chains per pair, each product weighted per
+// token with the slot's read weights (row NW r + wave of W).  Straight-line
+// code: the products of one pair overlap the weighting of the previous one.
+template <int DK, int DVT, int SPW, int NP>
+__device__ __forceinline__ void rs_read_closed(floatx4 (&Oi)[kChunk / 16][DVT / 16],
+                                               const Frag<_Float16> (&stk)[SPW][DK / 32][DVT / 16],
+                                               const RsStageA<DK> &X, const float (*W)[kChunk], int wave, int lane,
+                                               int lg)
+{
+    constexpr int KS = DK / 32;
+    constexpr int NTV = DVT / 16;
+    constexpr int NW = kRsWaves;
+    static_assert(2 * NP <= SPW, "pairs of the wave's slots");
+#pragma unroll
+    for (int mt = 0; mt < kChunk / 16; ++mt) {
+        Frag<_Float16> qf[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) load_frag(qf[ks], X.qf[mt][ks][lane]);
+#pragma unroll
+        for (int r2 = 0; r2 < 2 * NP; r2 += 2) {
+            floatx4 P0[NTV], P1[NTV];
+#pragma unroll
+            for (int nt = 0; nt < NTV; ++nt) {
+                P0[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+                P1[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int nt = 0; nt < NTV; ++nt) {
+                    mma32(P0[nt], qf[ks], stk[r2][ks][nt]);
+                    mma32(P1[nt], qf[ks], stk[r2 + 1][ks][nt]);
+                }
+            const float4 w0 = *reinterpret_cast<const float4 *>(&W[NW * r2 + wave][16 * mt + 4 * lg]);
+            const float4 w1 = *reinterpret_cast<const float4 *>(&W[NW * (r2 + 1) + wave][16 * mt + 4 * lg]);
+#pragma unroll
+            for (int nt = 0; nt < NTV; ++nt) {
+                Oi[mt][nt][0] = fmaf(w1.x, P1[nt][0], fmaf(w0.x, P0[nt][0], Oi[mt][nt][0]));
+                Oi[mt][nt][1] = fmaf(w1.y, P1[nt][1], fmaf(w0.y, P0[nt][1], Oi[mt][nt][1]));
+                Oi[mt][nt][2] = fmaf(w1.z, P1[nt][2], fmaf(w0.z, P0[nt][2], Oi[mt][nt][2]));
+                Oi[mt][nt][3] = fmaf(w1.w, P1[nt][3], fmaf(w0.w, P0[nt][3], Oi[mt][nt][3]));
+            }
+        }
+    }
+}
+
 // What one block carries from chunk to chunk (registers after inlining).
 template <int DK, int DVT, int SPW>
 struct RsCarry {
@@ -451,48 +499,21 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int nt = 0; nt < NTV; ++nt) Oi[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    // the wave's slot pairs up to the last one holding a closed state (slots
+    // are taken lowest-free, so the live ones gather at the low end; a slot
+    // without a closed state inside the range has weight 0 and finite
+    // operands): one uniform branch per chunk picks a straight-line read
     uint32_t mine = 0;          // which of the wave's slots hold a closed state (uniform)
 #pragma unroll
     for (int r = 0; r < SPW; ++r) mine |= ((c.closed >> (NW * r + wave)) & 1u) << r;
-    // one 16-token row tile at a time keeps a quarter of the query fragments
-    // live; the wave's slots go in pairs (two independent product chains)
-    // and every slot is read (a slot without a closed state has weight 0 and
-    // finite operands): with no branch between them the products of one pair
-    // overlap the weighting of the previous one, and the slowest blocks (full
-    // caches) have every slot live anyway
-    static_assert(SPW % 2 == 0, "slots are read in pairs");
-    if (mine != 0u) {
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            Frag<_Float16> qf[KS];
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) load_frag(qf[ks], X.qf[mt][ks][lane]);
-#pragma unroll
-            for (int r2 = 0; r2 < SPW; r2 += 2) {
-                floatx4 P0[NTV], P1[NTV];
-#pragma unroll
-                for (int nt = 0; nt < NTV; ++nt) {
-                    P0[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
-                    P1[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
-                }
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-                    for (int nt = 0; nt < NTV; ++nt) {
-                        mma32(P0[nt], qf[ks], stk[r2][ks][nt]);
-                        mma32(P1[nt], qf[ks], stk[r2 + 1][ks][nt]);
-                    }
-                const float4 w0 = *reinterpret_cast<const float4 *>(&S.W[NW * r2 + wave][16 * mt + 4 * lg]);
-                const float4 w1 = *reinterpret_cast<const float4 *>(&S.W[NW * (r2 + 1) + wave][16 * mt + 4 * lg]);
-#pragma unroll
-                for (int nt = 0; nt < NTV; ++nt) {
-                    Oi[mt][nt][0] = fmaf(w1.x, P1[nt][0], fmaf(w0.x, P0[nt][0], Oi[mt][nt][0]));
-                    Oi[mt][nt][1] = fmaf(w1.y, P1[nt][1], fmaf(w0.y, P0[nt][1], Oi[mt][nt][1]));
-                    Oi[mt][nt][2] = fmaf(w1.z, P1[nt][2], fmaf(w0.z, P0[nt][2], Oi[mt][nt][2]));
-                    Oi[mt][nt][3] = fmaf(w1.w, P1[nt][3], fmaf(w0.w, P0[nt][3], Oi[mt][nt][3]));
-                }
-            }
-        }
+    static_assert(SPW % 2 == 0 && SPW <= 8, "slots are read in pairs");
+    const int npair = mine ? (33 - __builtin_clz(mine)) / 2 : 0;
+    switch (npair) {
+    case 0: break;
+    case 1: rs_read_closed<DK, DVT, SPW, 1>(Oi, stk, X, S.W, wave, lane, lg); break;
+    case 2: rs_read_closed<DK, DVT, SPW, (SPW >= 4 ? 2 : 1)>(Oi, stk, X, S.W, wave, lane, lg); break;
+    case 3: rs_read_closed<DK, DVT, SPW, (SPW >= 6 ? 3 : 1)>(Oi, stk, X, S.W, wave, lane, lg); break;
+    default: rs_read_closed<DK, DVT, SPW, SPW / 2>(Oi, stk, X, S.W, wave, lane, lg); break;
     }
     if (c.act >= 0 && act_wave) {
 #pragma unroll

@@ -311,11 +311,16 @@ __device__ __forceinline__ void load_to_lds16(const void *g, void *lds_wave)
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // base (the same for the whole wave) plus a per-lane byte offset: the form
-// the global instructions take as an SGPR base and a 32-bit VGPR offset
+// the global instructions take as an SGPR base and a 32-bit VGPR offset.  The
+// empty asm makes the offset opaque at each use, so that the compiler does
+// not hoist base + offset out of the chunk loop as a 64-bit per-lane address
+// (with the register file full it would spill it and reload it from scratch
+// on every chunk).
 template <typename P>
 __device__ __forceinline__ P *at_bytes(P *base, uint32_t off)
 {
     typedef typename std::conditional<std::is_const<P>::value, const char, char>::type B;
+    asm volatile("" : "+v"(off));
     return reinterpret_cast<P *>(reinterpret_cast<B *>(base) + off);
 }
 
@@ -409,6 +414,25 @@ struct RsCarry {
     uint32_t closed;                             // physical slots of the closed states (uniform)
 };
 
+// Per-lane byte offsets, recomputed at each use from an opaque copy of the
+// thread index (kept live anyway) rather than held, or spilled, across chunks:
+// thread tid's V piece (token tid % 64, columns 8 (tid / 64) ..) within a
+// chunk's rows, and lane (lr, lg) of wave w's first output (token 16 w + 4 lg,
+// column lr) within a chunk.
+__device__ __forceinline__ uint32_t v_offset(int tid, int DV)
+{
+    uint32_t t = static_cast<uint32_t>(tid);
+    asm volatile("" : "+v"(t));
+    return 2u * ((t & (kChunk - 1)) * static_cast<uint32_t>(DV) + (t / kChunk) * 8u);
+}
+__device__ __forceinline__ uint32_t o_offset(int tid, int DV)
+{
+    uint32_t t = static_cast<uint32_t>(tid);
+    asm volatile("" : "+v"(t));
+    const uint32_t w = t >> 6, l = t & 63;
+    return 2u * ((16u * w + 4u * (l >> 4)) * static_cast<uint32_t>(DV) + (l & 15u));
+}
+
 // Per-block constants of the sweep.
 struct RsParams {
     const __bf16 *V;
@@ -418,8 +442,6 @@ struct RsParams {
     const uint8_t *rec;         // chunk records
     const int32_t *qexp_g;
     int bh, dv0, tid, lane, wave, lr, lg, NCH, vr, vc;
-    uint32_t v_off;             // byte offset of this thread's V piece within a chunk's rows
-    uint32_t o_off;             // byte offset of this lane's first output within a chunk
     bool v_mover;
     size_t tok0, slot_stride;
     float *st_base;
@@ -486,13 +508,23 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
     // chronological index (wsc is 0 for a slot without a closed state); the
     // active state is the most recent one (each wave writes and reads only
     // its own rows)
+    // (every load before the first store: the stores into S.W could alias the
+    // row indices and scales as far as the compiler knows, so interleaving
+    // them would serialise the loads)
     const float qsc = ldexpf(1.0f, qexp);
+    int wrow[SPW];
+    float wscl[SPW], wv[SPW];
 #pragma unroll
     for (int r = 0; r < SPW; ++r) {
-        const int p = NW * r + wave;
-        S.W[p][lane] = static_cast<float>(X.wr[S.jrow[p]][lane]) * (S.wsc[p] * qsc);
+        wrow[r] = S.jrow[NW * r + wave];
+        wscl[r] = S.wsc[NW * r + wave];
     }
-    if (act_wave) S.wact[kb][lane] = static_cast<float>(X.wr[c.m0 > 0 ? c.m0 - 1 : 0][lane]) * ldexpf(qsc, c.ea);
+#pragma unroll
+    for (int r = 0; r < SPW; ++r) wv[r] = static_cast<float>(X.wr[wrow[r]][lane]) * (wscl[r] * qsc);
+    const float wa = static_cast<float>(X.wr[c.m0 > 0 ? c.m0 - 1 : 0][lane]) * ldexpf(qsc, c.ea);
+#pragma unroll
+    for (int r = 0; r < SPW; ++r) S.W[NW * r + wave][lane] = wv[r];
+    if (act_wave) S.wact[kb][lane] = wa;
     // ---- inter-chunk read: closed states from registers, then the active state
     floatx4 Oi[MT][NTV];
 #pragma unroll
@@ -546,7 +578,7 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
         const int c0n = c0 + kChunk;
         c.vnext = u32x4{0u, 0u, 0u, 0u};
         if (A.v_mover && vr < min(kChunk, T - c0n))
-            c.vnext = *at_bytes(reinterpret_cast<const u32x4 *>(A.V + (tok0 + c0n) * DV + dv0), A.v_off);
+            c.vnext = *at_bytes(reinterpret_cast<const u32x4 *>(A.V + (tok0 + c0n) * DV + dv0), v_offset(tid, DV));
         c.evnext = make_int2(0, 0);
         if (tid < c.eC - c.eB) c.evnext = *at_bytes(A.events + tok0 + c.eB, 8u * tid);
     }
@@ -579,7 +611,7 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = 16 * w + 4 * lg + r;
-                if (t < nvalid) *at_bytes(ob + r * DV + 16 * nt, A.o_off) = static_cast<__bf16>(Oprev[nt][r]);
+                if (t < nvalid) *at_bytes(ob + r * DV + 16 * nt, o_offset(tid, DV)) = static_cast<__bf16>(Oprev[nt][r]);
             }
     }
 
@@ -937,8 +969,6 @@ __global__ __launch_bounds__(kRsThreads, 2) void k_prefill_rs(
     A.vr = A.tid & (kChunk - 1);
     A.vc = (A.tid / kChunk) * 8;
     A.v_mover = A.tid < kChunk * DVT / 8;
-    A.v_off = 2u * static_cast<uint32_t>(A.vr * DV + A.vc);
-    A.o_off = 2u * static_cast<uint32_t>((16 * A.wave + 4 * A.lg) * DV + A.lr);
     A.tok0 = static_cast<size_t>(A.bh) * T;
     A.slot_stride = static_cast<size_t>(DV) * DK;
     A.st_base = states + static_cast<size_t>(A.bh) * C * DV * DK + static_cast<size_t>(A.dv0) * DK;

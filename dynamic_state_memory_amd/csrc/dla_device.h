@@ -105,16 +105,65 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Cross-lane moves within a row of 16 lanes (DPP): lane l reads lane l ^ 1,
+// l ^ 2, (l & ~7) + 7 - (l & 7) and (l & ~15) + 15 - (l & 15).  Every source
+// lane lies in the same row, so no lane reads outside its row.
+template <int CTRL> __device__ __forceinline__ uint32_t dpp32(uint32_t x) {
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141; // row_half_mirror
+constexpr int kDppMirror = 0x140;     // row_mirror
+
+template <int CTRL> __device__ __forceinline__ float dpp_move(float x) {
+    return __builtin_bit_cast(float, dpp32<CTRL>(__builtin_bit_cast(uint32_t, x)));
+}
+template <int CTRL> __device__ __forceinline__ int32_t dpp_move(int32_t x) {
+    return static_cast<int32_t>(dpp32<CTRL>(static_cast<uint32_t>(x)));
+}
+template <int CTRL> __device__ __forceinline__ uint64_t dpp_move64(uint64_t x) {
+    const uint32_t lo = dpp32<CTRL>(static_cast<uint32_t>(x));
+    const uint32_t hi = dpp32<CTRL>(static_cast<uint32_t>(x >> 32));
+    return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+template <int CTRL> __device__ __forceinline__ double dpp_move(double x) {
+    return __builtin_bit_cast(double, dpp_move64<CTRL>(__builtin_bit_cast(uint64_t, x)));
+}
+template <int CTRL> __device__ __forceinline__ int64_t dpp_move(int64_t x) {
+    return static_cast<int64_t>(dpp_move64<CTRL>(static_cast<uint64_t>(x)));
+}
+
+template <typename T> __device__ __forceinline__ T readlane_any(T x, int l) {
+    if constexpr (sizeof(T) == 8) {
+        const uint64_t u = __builtin_bit_cast(uint64_t, x);
+        const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(u)), l);
+        const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(u >> 32)), l);
+        return __builtin_bit_cast(T, (static_cast<uint64_t>(hi) << 32) | lo);
+    } else {
+        return __builtin_bit_cast(T, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+    }
+}
+
+// Sum / maximum over the 64 lanes of a wave, returned in every lane: four
+// DPP steps reduce each row of 16 lanes, then the four row results are
+// combined from lanes 0, 16, 32, 48.  The whole wave must be active.
+// (Summation order: pairs, quads, halves, rows, then rows 0 + 1 + 2 + 3;
+// sums of exactly representable terms, as in the score, are order-free.)
 template <typename T> __device__ __forceinline__ T wave_sum(T x) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
-    return x;
+    x += dpp_move<kDppXor1>(x);
+    x += dpp_move<kDppXor2>(x);
+    x += dpp_move<kDppHalfMirror>(x);
+    x += dpp_move<kDppMirror>(x);
+    return (readlane_any(x, 0) + readlane_any(x, 16)) + (readlane_any(x, 32) + readlane_any(x, 48));
 }
 
 __device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
-    return x;
+    x = fmaxf(x, dpp_move<kDppXor1>(x));
+    x = fmaxf(x, dpp_move<kDppXor2>(x));
+    x = fmaxf(x, dpp_move<kDppHalfMirror>(x));
+    x = fmaxf(x, dpp_move<kDppMirror>(x));
+    return fmaxf(fmaxf(readlane_any(x, 0), readlane_any(x, 16)), fmaxf(readlane_any(x, 32), readlane_any(x, 48)));
 }
 
 // Exponent e with max * 2^-e in [2^14, 2^15): the largest magnitude then uses

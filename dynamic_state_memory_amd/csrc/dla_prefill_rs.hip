@@ -466,7 +466,6 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
     constexpr int MT = kChunk / 16;
     constexpr int NW = kRsWaves;
     constexpr int AW = NW - KS;                  // first wave holding rows of the active state
-    constexpr int CMAX = NW * SPW;
     static_assert(MT == NW, "one 16-token row tile per wave");
     __bf16 *O = A.O;
     const int T = A.T, DV = A.DV;

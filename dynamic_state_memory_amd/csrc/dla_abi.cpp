@@ -50,7 +50,7 @@ dla_status check_shape(int32_t B, int32_t H, int32_t C, int32_t dk, int32_t dv)
 
 struct Sizes {
     uint64_t s, qs, flag, tile_cnt, tile_sum, seg_t, seg_P, seg_q0, nseg, events, chunk_ev, shadow;
-    uint64_t rec, qexp;
+    uint64_t rec;
     uint64_t total;
 };
 
@@ -72,9 +72,8 @@ Sizes workspace_sizes(int64_t BH, int64_t T, int64_t C, int64_t dk, int64_t dv)
     z.chunk_ev = align_up(4ull * BH * (NCH + 1), 256);
     z.shadow = align_up(2ull * BH * C * dv * dk, 256);
     z.rec = align_up(static_cast<uint64_t>(BH) * NCH * rs_record_bytes(dk), 256);
-    z.qexp = align_up(4ull * BH * NCH, 256);
     z.total = z.s + z.qs + z.flag + z.tile_cnt + z.tile_sum + z.seg_t + z.seg_P + z.seg_q0 + z.nseg +
-              z.events + z.chunk_ev + z.shadow + z.rec + z.qexp;
+              z.events + z.chunk_ev + z.shadow + z.rec;
     return z;
 }
 
@@ -95,7 +94,6 @@ Workspace carve(void *base, const Sizes &z)
     w.chunk_ev = reinterpret_cast<int32_t *>(p); p += z.chunk_ev;
     w.shadow = p; p += z.shadow;
     w.rec = p; p += z.rec;
-    w.qexp = reinterpret_cast<int32_t *>(p); p += z.qexp;
     (void)p;
     return w;
 }

@@ -69,11 +69,10 @@ struct Workspace {
     // [BH][NCH] chunk records of the register-resident prefill, each
     // rs_record_bytes(d_k) long: fp16 query fragments [4][DK/32][64][8],
     // bf16 read weights [32][64] (row i: lam_t of the slot that the state
-    // with chronological index i at the chunk start is read with at token t),
-    // bf16 fragments of (Q K^T) o W [4][2][64][8], bf16 fragments of K^T
-    // [DK/16][2][64][8]
+    // with chronological index i at the chunk start is read with at token t,
+    // times 2^e for the query scaling 2^-e of the fragments), bf16 fragments
+    // of (Q K^T) o W [4][2][64][8], bf16 fragments of K^T [DK/16][2][64][8]
     void *rec;
-    int32_t *qexp;       // [BH][NCH] power-of-two exponent of each chunk's fp16 query
 };
 constexpr int kPrepCmax = 32;   // read-weight rows kept per chunk by the pre-pass
 // chunk record of the register-resident prefill: query fragments, read weights,

@@ -88,7 +88,7 @@ template <int DK>
 __global__ __launch_bounds__(256) void k_chunk_prep(
     const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, const __bf16 *__restrict__ LAM, int T, int C,
     const int2 *__restrict__ events, const int32_t *__restrict__ chunk_ev, uint8_t *__restrict__ rec,
-    int32_t *__restrict__ qexp_out, int32_t *__restrict__ m_t_out)
+    int32_t *__restrict__ m_t_out)
 {
     constexpr int KS = DK / 32;
     __shared__ __align__(16) __bf16 q[kChunk][DK + 8];
@@ -147,7 +147,6 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
     if (lane == 0) red[wave] = qmax;
     __syncthreads();
     const int qexp = f16_exponent(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
-    if (tid == 0) qexp_out[cb] = qexp;
     if (tid < kChunk) {
         // bit i of o: the state with chronological index i at the chunk start
         // is live after token tid; bit p of m: the state opened at chunk
@@ -230,13 +229,14 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
     // read weights by chronological index: a state live at the chunk start is
     // read at token t with the slot of the nearest older state still live
     // (itself, or the state it was merged into), i.e. after every live state
-    // that is more recent, old or new; 0 for rows without a state
+    // that is more recent, old or new; 0 for rows without a state.  They
+    // carry the factor 2^qexp that undoes the query scaling (exact in bf16).
 #pragma unroll
     for (int j = 0; j < kPrepCmax / 4; ++j) {
         const int idx = tid + 256 * j;
         const int t = idx & (kChunk - 1), i = idx / kChunk;
         float w = 0.0f;
-        if (i < m0) w = lam[t][__popcll(shr64(om[t], i + 1)) + __popcll(nm[t])];
+        if (i < m0) w = ldexpf(lam[t][__popcll(shr64(om[t], i + 1)) + __popcll(nm[t])], qexp);
         wrow[idx] = static_cast<__bf16>(w);
     }
 }
@@ -292,6 +292,7 @@ struct RsSmem {
     // chunk with events)
     int32_t jrow[CMAX];
     float wsc[CMAX];
+    int32_t nev;                // events of the chunk
     uint32_t jobs;              // slots whose new value an owner wave builds
     uint32_t closed_new;        // slots of the closed states after the chunk
     int32_t m_new, act_new, an_case;
@@ -406,11 +407,10 @@ struct RsCarry {
     floatx4 am[DVT / 16][2];                     // active state, d_k rows 32 kb .. 32 kb + 31 (fp32)
     Frag<_Float16> af[DVT / 16];                 // its fp16 operand copy
     u32x4 vnext;                                 // next chunk's V piece
-    int2 evnext;                                 // next chunk's event of this thread
+    int2 evnext;                                 // event lane of the next chunk's window (wave 0)
     int ea;                                      // exponent of this wave's active-state operand
     int m0, act;                                 // live states, the active state's slot (uniform)
-    int eA, eB, eC;                              // event offsets of chunks ch, ch + 1, ch + 2 (at chunk ch)
-    int qexpn;                                   // next chunk's query exponent
+    int ewin;                                    // index of this chunk's first event in the stream
     uint32_t closed;                             // physical slots of the closed states (uniform)
 };
 
@@ -439,13 +439,12 @@ struct RsParams {
     __bf16 *O;
     int T, C, DV;
     const int2 *events;
+    int evtot;                  // events of the stream
     const uint8_t *rec;         // chunk records
-    const int32_t *qexp_g;
     int bh, dv0, tid, lane, wave, lr, lg, NCH, vr, vc;
     bool v_mover;
     size_t tok0, slot_stride;
     float *st_base;
-    const int32_t *cev;
 };
 
 // One chunk of the sweep: its part A operands are in X, its part B operands
@@ -482,9 +481,6 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
 
     const int c0 = ch * kChunk;
     const int nvalid = min(kChunk, T - c0);
-    const int nev = c.eB - c.eA;
-    const bool has_ev = nev > 0;
-    const int qexp = c.qexpn;
     const u32x4 vcur = c.vnext;
     const int2 evcur = c.evnext;
     const bool more = ch + 1 < NCH;
@@ -495,8 +491,12 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
     __syncthreads();
     // ---- part B of this chunk
     stage_b<DK>(Y, A.rec, cb, tid, wave);
-    // event offset of chunk ch + 3 (used two chunks from now)
-    const int eD = ch + 3 <= NCH ? A.cev[ch + 3] : c.eC;
+    // the chunk's events: the lanes of wave 0's window (the next 64 events of
+    // the stream, at most 64 per chunk) whose token lies in the chunk
+    if (wave == 0) {
+        const int n = __popcll(__ballot(evcur.x < c0 + kChunk));
+        if (lane == 0) S.nev = n;
+    }
     // ---- this chunk's V (transposed) and events into LDS
     if (A.v_mover) {
         const __bf16 *ve = reinterpret_cast<const __bf16 *>(&vcur);
@@ -510,7 +510,6 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
     // (every load before the first store: the stores into S.W could alias the
     // row indices and scales as far as the compiler knows, so interleaving
     // them would serialise the loads)
-    const float qsc = ldexpf(1.0f, qexp);
     int wrow[SPW];
     float wscl[SPW], wv[SPW];
 #pragma unroll
@@ -519,8 +518,8 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
         wscl[r] = S.wsc[NW * r + wave];
     }
 #pragma unroll
-    for (int r = 0; r < SPW; ++r) wv[r] = static_cast<float>(X.wr[wrow[r]][lane]) * (wscl[r] * qsc);
-    const float wa = static_cast<float>(X.wr[c.m0 > 0 ? c.m0 - 1 : 0][lane]) * ldexpf(qsc, c.ea);
+    for (int r = 0; r < SPW; ++r) wv[r] = static_cast<float>(X.wr[wrow[r]][lane]) * wscl[r];
+    const float wa = ldexpf(static_cast<float>(X.wr[c.m0 > 0 ? c.m0 - 1 : 0][lane]), c.ea);
 #pragma unroll
     for (int r = 0; r < SPW; ++r) S.W[NW * r + wave][lane] = wv[r];
     if (act_wave) S.wact[kb][lane] = wa;
@@ -570,16 +569,20 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
     // part B has landed and every wave is done with part A
     wait_vmem();
     __syncthreads();
+    const int nev = __builtin_amdgcn_readfirstlane(S.nev);
+    const bool has_ev = nev > 0;
     // ---- part A of the next chunk; its V, events and query exponent into registers
     if (more) {
         stage_a<DK>(X, A.rec, cb + 1, tid, wave);
-        c.qexpn = A.qexp_g[cb + 1];
         const int c0n = c0 + kChunk;
         c.vnext = u32x4{0u, 0u, 0u, 0u};
         if (A.v_mover && vr < min(kChunk, T - c0n))
             c.vnext = *at_bytes(reinterpret_cast<const u32x4 *>(A.V + (tok0 + c0n) * DV + dv0), v_offset(tid, DV));
-        c.evnext = make_int2(0, 0);
-        if (tid < c.eC - c.eB) c.evnext = *at_bytes(A.events + tok0 + c.eB, 8u * tid);
+        // wave 0: the window of the next chunk (past the stream's last event a
+        // lane holds a token no chunk reaches)
+        c.evnext = make_int2(0x7fffffff, -1);
+        const int en = c.ewin + nev;
+        if (wave == 0 && en + lane < A.evtot) c.evnext = *at_bytes(A.events + tok0 + en, 8u * lane);
     }
     // ---- reduce the partial reads of rows 16 w .., add P V
     {
@@ -633,9 +636,7 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
                 }
             c.ea = refresh_active<NTV>(am, af);
         }
-        c.eA = c.eB;
-        c.eB = c.eC;
-        c.eC = eD;
+        c.ewin += nev;
         return;
     }
 
@@ -928,16 +929,14 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
     c.m0 = mnew;
     c.act = an;
     c.closed = cl;
-    c.eA = c.eB;
-    c.eB = c.eC;
-    c.eC = eD;
+    c.ewin += nev;
 }
 
 template <int DK, int DVT, int SPW>
 __global__ __launch_bounds__(kRsThreads, 2) void k_prefill_rs(
     const __bf16 *__restrict__ V, __bf16 *__restrict__ O, int T, int C, int DV, int nblk_dv,
     float *__restrict__ states, const int2 *__restrict__ events,
-    const int32_t *__restrict__ chunk_ev, const uint8_t *__restrict__ rec, const int32_t *__restrict__ qexp_g,
+    const int32_t *__restrict__ chunk_ev, const uint8_t *__restrict__ rec,
     uint8_t *__restrict__ meta_base, size_t meta_stride)
 {
     constexpr int KS = DK / 32;
@@ -955,7 +954,7 @@ __global__ __launch_bounds__(kRsThreads, 2) void k_prefill_rs(
     if ((nblk & 7) == 0) lin = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
     RsParams A;
     A.V = V; A.O = O; A.T = T; A.C = C; A.DV = DV;
-    A.events = events; A.rec = rec; A.qexp_g = qexp_g;
+    A.events = events; A.rec = rec;
     A.bh = lin / nblk_dv;
     A.dv0 = (lin % nblk_dv) * DVT;
     A.tid = threadIdx.x;
@@ -971,7 +970,7 @@ __global__ __launch_bounds__(kRsThreads, 2) void k_prefill_rs(
     A.tok0 = static_cast<size_t>(A.bh) * T;
     A.slot_stride = static_cast<size_t>(DV) * DK;
     A.st_base = states + static_cast<size_t>(A.bh) * C * DV * DK + static_cast<size_t>(A.dv0) * DK;
-    A.cev = chunk_ev + static_cast<size_t>(A.bh) * (A.NCH + 1);
+    A.evtot = chunk_ev[static_cast<size_t>(A.bh) * (A.NCH + 1) + A.NCH];
     const int tid = A.tid, wave = A.wave, lr = A.lr, lg = A.lg, NCH = A.NCH;
 
     RsCarry<DK, DVT, SPW> c;
@@ -999,12 +998,10 @@ __global__ __launch_bounds__(kRsThreads, 2) void k_prefill_rs(
     c.vnext = u32x4{0u, 0u, 0u, 0u};
     if (A.v_mover && A.vr < min(kChunk, T))
         c.vnext = *reinterpret_cast<const u32x4 *>(V + (A.tok0 + A.vr) * DV + A.dv0 + A.vc);
-    c.eA = A.cev[0];
-    c.eB = A.cev[1];
-    c.eC = NCH >= 2 ? A.cev[2] : c.eB;
-    c.qexpn = qexp_g[static_cast<size_t>(A.bh) * NCH];
-    c.evnext = make_int2(0, 0);
-    if (tid < c.eB - c.eA) c.evnext = events[A.tok0 + c.eA + tid];
+    // wave 0: the window of chunk 0 (the stream's first 64 events)
+    c.ewin = 0;
+    c.evnext = make_int2(0x7fffffff, -1);
+    if (wave == 0 && A.lane < A.evtot) c.evnext = events[A.tok0 + A.lane];
 
     for (int ch = 0; ch < NCH; ++ch) rs_chunk<DK, DVT, SPW>(ch, stA, stB, S, A, c);
 
@@ -1035,7 +1032,7 @@ static hipError_t launch_rs(const PrefillArgs &a, hipStream_t stream)
     hipLaunchKernelGGL((k_chunk_prep<DK>), dim3(NCH, BH), dim3(256), 0, stream,
                        static_cast<const __bf16 *>(a.q), static_cast<const __bf16 *>(a.k),
                        static_cast<const __bf16 *>(a.lam), a.T, a.g.C, a.ws.events, a.ws.chunk_ev,
-                       static_cast<uint8_t *>(a.ws.rec), a.ws.qexp, a.sched.m_t);
+                       static_cast<uint8_t *>(a.ws.rec), a.sched.m_t);
     hipError_t e0 = hipGetLastError();
     if (e0 != hipSuccess) return e0;
     if (a.ev_before) {
@@ -1044,7 +1041,7 @@ static hipError_t launch_rs(const PrefillArgs &a, hipStream_t stream)
     }
     hipLaunchKernelGGL((k_prefill_rs<DK, DVT, SPW>), dim3(BH * nblk_dv), dim3(kRsThreads), 0, stream,
                        static_cast<const __bf16 *>(a.v), static_cast<__bf16 *>(a.o), a.T, a.g.C, a.g.dv,
-                       nblk_dv, a.states, a.ws.events, a.ws.chunk_ev, static_cast<const uint8_t *>(a.ws.rec), a.ws.qexp, a.meta, a.g.meta_stride);
+                       nblk_dv, a.states, a.ws.events, a.ws.chunk_ev, static_cast<const uint8_t *>(a.ws.rec), a.meta, a.g.meta_stride);
     hipError_t e = hipGetLastError();
     if (e == hipSuccess && a.ev_after) e = hipEventRecord(a.ev_after, stream);
     return e;

@@ -608,13 +608,20 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
             }
         }
         __bf16 *ob = O + (tok0 + c0) * DV + dv0;
+        const uint32_t oo = o_offset(tid, DV);
+        if (nvalid == kChunk) {
 #pragma unroll
-        for (int nt = 0; nt < NTV; ++nt)
+            for (int nt = 0; nt < NTV; ++nt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 16 * w + 4 * lg + r;
-                if (t < nvalid) *at_bytes(ob + r * DV + 16 * nt, o_offset(tid, DV)) = static_cast<__bf16>(Oprev[nt][r]);
-            }
+                for (int r = 0; r < 4; ++r) *at_bytes(ob + r * DV + 16 * nt, oo) = static_cast<__bf16>(Oprev[nt][r]);
+        } else {
+#pragma unroll
+            for (int nt = 0; nt < NTV; ++nt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (16 * w + 4 * lg + r < nvalid)
+                        *at_bytes(ob + r * DV + 16 * nt, oo) = static_cast<__bf16>(Oprev[nt][r]);
+        }
     }
 
     // ---- chunk-end update

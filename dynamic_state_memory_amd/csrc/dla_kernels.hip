@@ -754,6 +754,8 @@ __global__ __launch_bounds__(256, 1) void k_prefill(
 // once: o = sum_i lam[slot(i)] S_i q + lam[0] v (k . q), adding v k^T into
 // the most recent state, or writing the new state v k^T into a free slot,
 // and applying a capacity merge S_a += S_b while the data passes through.
+// The states are read and written with nontemporal hints: a step touches
+// each of them once, so they should not displace other data in the caches.
 template <typename TIO, int D>
 __global__ __launch_bounds__(256) void k_decode(const TIO *__restrict__ Qg, const TIO *__restrict__ Kg,
                                                 const TIO *__restrict__ Vg, const TIO *__restrict__ Lg,
@@ -897,7 +899,10 @@ __global__ __launch_bounds__(256) void k_decode(const TIO *__restrict__ Qg, cons
         float4 *sp = reinterpret_cast<float4 *>(sb + static_cast<size_t>(p) * D * D);
         float4 x[P];
 #pragma unroll
-        for (int j = 0; j < P; ++j) x[j] = sp[((row0 + R * j) * D + col) / 4];
+        for (int j = 0; j < P; ++j) {
+            const floatx4 t = __builtin_nontemporal_load(reinterpret_cast<const floatx4 *>(sp) + ((row0 + R * j) * D + col) / 4);
+            x[j] = make_float4(t[0], t[1], t[2], t[3]);
+        }
 #pragma unroll
         for (int j = 0; j < P; ++j)
             acc[j] += w * (x[j].x * q4.x + x[j].y * q4.y + x[j].z * q4.z + x[j].w * q4.w);
@@ -907,7 +912,8 @@ __global__ __launch_bounds__(256) void k_decode(const TIO *__restrict__ Qg, cons
                 const float vr = vs[row0 + R * j];
                 float4 y = x[j];
                 y.x += vr * k4.x; y.y += vr * k4.y; y.z += vr * k4.z; y.w += vr * k4.w;
-                sp[((row0 + R * j) * D + col) / 4] = y;
+                __builtin_nontemporal_store(floatx4{y.x, y.y, y.z, y.w},
+                                            reinterpret_cast<floatx4 *>(sp) + ((row0 + R * j) * D + col) / 4);
             }
         }
         if (mode == 2 && i == merge_i + 1) {
@@ -917,7 +923,7 @@ __global__ __launch_bounds__(256) void k_decode(const TIO *__restrict__ Qg, cons
                 const int idx = ((row0 + R * j) * D + col) / 4;
                 float4 a = dp[idx];
                 a.x += x[j].x; a.y += x[j].y; a.z += x[j].z; a.w += x[j].w;
-                dp[idx] = a;
+                __builtin_nontemporal_store(floatx4{a.x, a.y, a.z, a.w}, reinterpret_cast<floatx4 *>(dp) + idx);
             }
         }
     }
@@ -926,7 +932,8 @@ __global__ __launch_bounds__(256) void k_decode(const TIO *__restrict__ Qg, cons
 #pragma unroll
         for (int j = 0; j < P; ++j) {
             const float vr = vs[row0 + R * j];
-            sp[((row0 + R * j) * D + col) / 4] = make_float4(vr * k4.x, vr * k4.y, vr * k4.z, vr * k4.w);
+            __builtin_nontemporal_store(floatx4{vr * k4.x, vr * k4.y, vr * k4.z, vr * k4.w},
+                                        reinterpret_cast<floatx4 *>(sp) + ((row0 + R * j) * D + col) / 4);
         }
     }
     (void)mode;

@@ -106,7 +106,9 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
     const size_t tok0 = static_cast<size_t>(bh) * T;
     const size_t cb = static_cast<size_t>(bh) * NCH + ch;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    // this chunk's record: query fragments, read weights, weighted-score fragments, key fragments
+    // this chunk's record: query fragments, read weights, weighted-score
+    // fragments, key fragments (written with nontemporal hints: the sweep
+    // reads a record only after many others have been written)
     uint8_t *rb = rec + cb * rs_record_bytes(DK);
     f16x8 *q16f = reinterpret_cast<f16x8 *>(rb);
     __bf16 *wrow = reinterpret_cast<__bf16 *>(rb + rs_rec_q_bytes(DK));
@@ -178,7 +180,7 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
             h[e] = static_cast<_Float16>(ldexpf(static_cast<float>(row[cc + e]), -qexp));
             h[4 + e] = static_cast<_Float16>(ldexpf(static_cast<float>(row[cc + 16 + e]), -qexp));
         }
-        q16f[f] = h;
+        __builtin_nontemporal_store(h, &q16f[f]);
     }
     // K^T fragments: d_k rows of a 16-tile, 8 consecutive tokens per lane
 #pragma unroll
@@ -189,7 +191,7 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
         bf16x8 h;
 #pragma unroll
         for (int e = 0; e < 8; ++e) h[e] = k[t0 + e][dk];
-        ktf[f] = h;
+        __builtin_nontemporal_store(h, &ktf[f]);
     }
     __syncthreads();
     // P = (Q K^T) o W on the causal triangle (wave w: rows 16w..16w+15)
@@ -224,7 +226,7 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
     for (int j = 0; j < 2; ++j) {
         const int f = tid + 256 * j;                   // (mt, ks2, lane)
         const int l = f & 63, ks2 = (f >> 6) & 1, mt = f >> 7;
-        pwf[f] = *reinterpret_cast<const bf16x8 *>(&pw[16 * mt + (l & 15)][32 * ks2 + 8 * (l >> 4)]);
+        __builtin_nontemporal_store(*reinterpret_cast<const bf16x8 *>(&pw[16 * mt + (l & 15)][32 * ks2 + 8 * (l >> 4)]), &pwf[f]);
     }
     // read weights by chronological index: a state live at the chunk start is
     // read at token t with the slot of the nearest older state still live

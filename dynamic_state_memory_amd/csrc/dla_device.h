@@ -145,6 +145,17 @@ template <typename T> __device__ __forceinline__ T readlane_any(T x, int l) {
     }
 }
 
+// Sum over aligned groups of G lanes (G = 8 or 16), in every lane of the
+// group: DPP steps within the group only.
+template <int G, typename T> __device__ __forceinline__ T group_sum_dpp(T x) {
+    static_assert(G == 8 || G == 16, "groups of 8 or 16 lanes");
+    x += dpp_move<kDppXor1>(x);
+    x += dpp_move<kDppXor2>(x);
+    x += dpp_move<kDppHalfMirror>(x);
+    if constexpr (G == 16) x += dpp_move<kDppMirror>(x);
+    return x;
+}
+
 // Sum / maximum over the 64 lanes of a wave, returned in every lane: four
 // DPP steps reduce each row of 16 lanes, then the four row results are
 // combined from lanes 0, 16, 32, 48.  The whole wave must be active.
@@ -180,13 +191,16 @@ __device__ __forceinline__ void read_frag_from(Frag<_Float16> &f, const __bf16 *
 }
 __device__ __forceinline__ void read_frag_from(Frag<float> &f, const float *p, int) { load_frag(f, p); }
 
+__device__ __forceinline__ int64_t min_i64(int64_t a, int64_t b) { return b < a ? b : a; }
+
+// Minimum over the 64 lanes of a wave, in every lane (DPP row steps, then the
+// four row results; the whole wave must be active).
 __device__ __forceinline__ int64_t wave_min_i64(int64_t x) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-        const int64_t y = __shfl_xor(x, off);
-        x = y < x ? y : x;
-    }
-    return x;
+    x = min_i64(x, dpp_move<kDppXor1>(x));
+    x = min_i64(x, dpp_move<kDppXor2>(x));
+    x = min_i64(x, dpp_move<kDppHalfMirror>(x));
+    x = min_i64(x, dpp_move<kDppMirror>(x));
+    return min_i64(min_i64(readlane_any(x, 0), readlane_any(x, 16)), min_i64(readlane_any(x, 32), readlane_any(x, 48)));
 }
 
 // Inclusive scan over a 64-lane wave.

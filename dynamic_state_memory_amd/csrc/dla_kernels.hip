@@ -107,12 +107,9 @@ __global__ __launch_bounds__(256) void k_score(const TIO *__restrict__ K, int T,
                 b += y * y;
             }
         }
-#pragma unroll
-        for (int off = G / 2; off > 0; off >>= 1) {
-            d += __shfl_xor(d, off);
-            a += __shfl_xor(a, off);
-            b += __shfl_xor(b, off);
-        }
+        d = group_sum_dpp<G>(d);
+        a = group_sum_dpp<G>(a);
+        b = group_sum_dpp<G>(b);
         if (valid && gl == 0) s_lds[j] = (t == 0) ? 1.0f : cosine_distance(d, a, b);
     }
     __syncthreads();
@@ -256,10 +253,11 @@ __global__ __launch_bounds__(64) void k_greedy(int T, int C, int NCH,
         }
         const int cnt = min(64, nseg - b0);
         for (int jj = 0; jj < cnt; ++jj) {
-            const int t = __shfl(tj, jj);
-            const int tnext = __shfl(tn, jj);
-            const int64_t qj = __shfl(q0, jj);
-            const int64_t remI = __shfl(Pn, jj) - __shfl(Pj, jj) - qj;
+            // segment jj of this batch, broadcast from its lane (jj is uniform)
+            const int t = readlane_any(tj, jj);
+            const int tnext = readlane_any(tn, jj);
+            const int64_t qj = readlane_any(q0, jj);
+            const int64_t remI = readlane_any(Pn, jj) - readlane_any(Pj, jj) - qj;
             const int remn = tnext - t - 1;
             const int c = t / kChunk;
             if (c != cur_chunk) {
@@ -286,8 +284,8 @@ __global__ __launch_bounds__(64) void k_greedy(int T, int C, int NCH,
                 const int64_t kmin = wave_min_i64(key);
                 const uint64_t hit = __ballot(key == kmin);
                 istar = __ffsll(static_cast<unsigned long long>(hit)) - 1;
-                const int32_t d_oi = __shfl(poi, istar);
-                const int32_t d_st = __shfl(pst, istar);
+                const int32_t d_oi = readlane_any(poi, istar);
+                const int32_t d_st = readlane_any(pst, istar);
                 dead = d_oi >= 0 ? d_oi : 64 + (d_st - cur_chunk * kChunk);
                 if (lane == istar) { I += pI; n += pn; }
                 else if (lane > istar && lane < m) { I = pI; n = pn; st = pst; oi = poi; }

@@ -91,10 +91,15 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
     int32_t *__restrict__ m_t_out)
 {
     constexpr int KS = DK / 32;
+    // 40 KB of LDS: four blocks per compute unit.  The weighted scores P
+    // reuse the query rows (wave w writes P rows 16w.. only after it has read
+    // its own query rows, and every other query read ends at a barrier
+    // before), and lam is kept in its bf16 input precision.
     __shared__ __align__(16) __bf16 q[kChunk][DK + 8];
     __shared__ __align__(16) __bf16 k[kChunk][DK + 8];
-    __shared__ __align__(16) __bf16 pw[kChunk][kChunk + 8];
-    __shared__ float lam[kChunk][kPrepCmax + 1];
+    __shared__ __bf16 lam[kChunk][kPrepCmax + 2];
+    static_assert(DK >= kChunk, "the weighted-score rows fit the query rows");
+    __bf16 (*pw)[DK + 8] = q;
     __shared__ uint64_t om[kChunk];
     __shared__ uint64_t nm[kChunk];
     __shared__ int2 evs[kChunk];
@@ -137,7 +142,7 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
     for (int j = 0; j < kPrepCmax / 4; ++j) {
         const int idx = tid + 256 * j;
         const int r = idx & (kChunk - 1), c = idx / kChunk;
-        lam[r][c] = (c < C && r < nvalid) ? static_cast<float>(LAM[(tok0 + c0 + r) * C + c]) : 0.0f;
+        lam[r][c] = (c < C && r < nvalid) ? LAM[(tok0 + c0 + r) * C + c] : static_cast<__bf16>(0.0f);
     }
     const int e0 = chunk_ev[static_cast<size_t>(bh) * (NCH + 1) + ch];
     const int nev = chunk_ev[static_cast<size_t>(bh) * (NCH + 1) + ch + 1] - e0;
@@ -216,7 +221,7 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
                 const int t = 16 * w + 4 * lg + r;
                 const int s = 16 * nt + lr;
                 float val = 0.0f;
-                if (s <= t) val = A[r] * lam[t][__popcll(shr64(nm[t], s + 1))];
+                if (s <= t) val = A[r] * static_cast<float>(lam[t][__popcll(shr64(nm[t], s + 1))]);
                 pw[t][s] = static_cast<__bf16>(val);
             }
         }
@@ -238,7 +243,7 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
         const int idx = tid + 256 * j;
         const int t = idx & (kChunk - 1), i = idx / kChunk;
         float w = 0.0f;
-        if (i < m0) w = ldexpf(lam[t][__popcll(shr64(om[t], i + 1)) + __popcll(nm[t])], qexp);
+        if (i < m0) w = ldexpf(static_cast<float>(lam[t][__popcll(shr64(om[t], i + 1)) + __popcll(nm[t])]), qexp);
         wrow[idx] = static_cast<__bf16>(w);
     }
 }

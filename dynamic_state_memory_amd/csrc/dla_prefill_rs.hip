@@ -587,6 +587,8 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
             c.vnext = *at_bytes(reinterpret_cast<const u32x4 *>(A.V + (tok0 + c0n) * DV + dv0), v_offset(tid, DV));
         // wave 0: the window of the next chunk (past the stream's last event a
         // lane holds a token no chunk reaches)
+        // (the sentinel is the destination's old value: a select on the loaded
+        // value would wait for the load here)
         c.evnext = make_int2(0x7fffffff, -1);
         const int en = c.ewin + nev;
         if (wave == 0 && en + lane < A.evtot) c.evnext = *at_bytes(A.events + tok0 + en, 8u * lane);
@@ -689,7 +691,9 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
         // old states still live keep their value and their order (lane i: old state i)
         if (lane < m0 && ((oa >> lane) & 1ull)) {
             const int p = S.order[lane];
-            S.new_order[__popcll(oa & low_bits(lane))] = p;
+            // (position: the live old states in lower lanes, counted by mbcnt)
+            S.new_order[__builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(oa >> 32),
+                                                  __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(oa), 0u))] = p;
             S.jbase[p] = 1;
             S.jsrc[p] = 0;
             S.jlo[p] = 0;

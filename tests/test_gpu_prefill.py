@@ -89,6 +89,17 @@ def test_reduced_bf16_workloads(name, streams, T, means, prefill_path):
         assert r["n_ev"].min() > 0
 
 
+@pytest.mark.parametrize("C", [8, 16, 32])
+def test_dk64_bf16_many_chunks(C, prefill_path):
+    """d_k = 64 in bf16 over many chunks: a ragged last chunk (1000 tokens),
+    frequent boundaries and merges, two 16-column slices of d_v."""
+    torch_mod()
+    cfg = dataclasses.replace(workloads.CONFIGS["mamba2_780m_bf16"], dk=64, dv=32, C=C, seg_means=(12,))
+    d = workloads.prefill_inputs(cfg, streams=[0, 1], T=1000)
+    r = _full_check(d, C, cfg.tau, "bf16", f"dk64 C={C}")
+    assert r["n_ev"].min() > 0
+
+
 def test_literal_noise_reading_every_token_opens(prefill_path):
     torch_mod()
     cfg = workloads.CONFIGS["gdn_1p3b_t32k_bf16"]

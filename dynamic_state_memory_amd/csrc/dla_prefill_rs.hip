@@ -244,7 +244,7 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
         const int t = idx & (kChunk - 1), i = idx / kChunk;
         float w = 0.0f;
         if (i < m0) w = ldexpf(static_cast<float>(lam[t][__popcll(shr64(om[t], i + 1)) + __popcll(nm[t])]), qexp);
-        wrow[idx] = static_cast<__bf16>(w);
+        wrow[i * kChunk + (t % 16) * (kChunk / 16) + t / 16] = static_cast<__bf16>(w);
     }
 }
 
@@ -261,7 +261,10 @@ constexpr int kRsThreads = 64 * kRsWaves;
 template <int DK>
 struct RsStageA {
     _Float16 qf[kChunk / 16][DK / 32][64][8];   // query fragments (permuted reduction order)
-    __bf16 wr[kPrepCmax][kChunk];                // read weights by chronological index of the state
+    // read weights by chronological index of the state; within a row, the
+    // weight of token t sits at 4 (t % 16) + t / 16 (a lane's four row tiles
+    // side by side)
+    __bf16 wr[kPrepCmax][kChunk];
 };
 template <int DK>
 struct RsStageB {
@@ -281,7 +284,6 @@ struct RsSmem {
     // closed-state read weights by physical slot (owner wave's rows); in a
     // chunk with events, after the read, the active state passes through it
     float W[CMAX < 32 ? 32 : CMAX][kChunk];
-    float wact[DK / 32][kChunk];  // active-state read weights, one row per active wave
     floatx4 ored[kRsWaves][kChunk / 16][DVT / 16][64];  // partial reads: wave, row tile, column tile, lane
     int32_t order[kMaxC];       // physical slot of each live state, oldest first
     int32_t new_order[kMaxC];
@@ -306,6 +308,7 @@ struct RsSmem {
 };
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) const void glb_void_t;
 
@@ -364,11 +367,15 @@ __device__ __forceinline__ void stage_b(RsStageB<DK> &Y, const uint8_t *rec, siz
 // live), two independent product chains per pair, each product weighted per
 // token with the slot's read weights (row NW r + wave of W).  Straight-line
 // code: the products of one pair overlap the weighting of the previous one.
+// The products are formed transposed, state fragment times query fragment
+// (the two operand layouts of the 16x16x32 product are the same), so lane
+// (lr, lg) holds token lr of the tile, columns 4 lg .. 4 lg + 3: its weight
+// is one number per slot and tile.
 template <int DK, int DVT, int SPW, int NP>
 __device__ __forceinline__ void rs_read_closed(floatx4 (&Oi)[kChunk / 16][DVT / 16],
                                                const Frag<_Float16> (&stk)[SPW][DK / 32][DVT / 16],
                                                const RsStageA<DK> &X, const float (*W)[kChunk], int wave, int lane,
-                                               int lg)
+                                               int lr)
 {
     constexpr int KS = DK / 32;
     constexpr int NTV = DVT / 16;
@@ -391,18 +398,15 @@ __device__ __forceinline__ void rs_read_closed(floatx4 (&Oi)[kChunk / 16][DVT / 
             for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
                 for (int nt = 0; nt < NTV; ++nt) {
-                    mma32(P0[nt], qf[ks], stk[r2][ks][nt]);
-                    mma32(P1[nt], qf[ks], stk[r2 + 1][ks][nt]);
+                    mma32(P0[nt], stk[r2][ks][nt], qf[ks]);
+                    mma32(P1[nt], stk[r2 + 1][ks][nt], qf[ks]);
                 }
-            const float4 w0 = *reinterpret_cast<const float4 *>(&W[NW * r2 + wave][16 * mt + 4 * lg]);
-            const float4 w1 = *reinterpret_cast<const float4 *>(&W[NW * (r2 + 1) + wave][16 * mt + 4 * lg]);
+            const float w0 = W[NW * r2 + wave][(kChunk / 16) * lr + mt];
+            const float w1 = W[NW * (r2 + 1) + wave][(kChunk / 16) * lr + mt];
 #pragma unroll
-            for (int nt = 0; nt < NTV; ++nt) {
-                Oi[mt][nt][0] = fmaf(w1.x, P1[nt][0], fmaf(w0.x, P0[nt][0], Oi[mt][nt][0]));
-                Oi[mt][nt][1] = fmaf(w1.y, P1[nt][1], fmaf(w0.y, P0[nt][1], Oi[mt][nt][1]));
-                Oi[mt][nt][2] = fmaf(w1.z, P1[nt][2], fmaf(w0.z, P0[nt][2], Oi[mt][nt][2]));
-                Oi[mt][nt][3] = fmaf(w1.w, P1[nt][3], fmaf(w0.w, P0[nt][3], Oi[mt][nt][3]));
-            }
+            for (int nt = 0; nt < NTV; ++nt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) Oi[mt][nt][i] = fmaf(w1, P1[nt][i], fmaf(w0, P0[nt][i], Oi[mt][nt][i]));
         }
     }
 }
@@ -424,8 +428,8 @@ struct RsCarry {
 // Per-lane byte offsets, recomputed at each use from an opaque copy of the
 // thread index (kept live anyway) rather than held, or spilled, across chunks:
 // thread tid's V piece (token tid % 64, columns 8 (tid / 64) ..) within a
-// chunk's rows, and lane (lr, lg) of wave w's first output (token 16 w + 4 lg,
-// column lr) within a chunk.
+// chunk's rows, and lane (lr, lg) of wave w's output piece (token 16 w + lr,
+// columns 4 lg .. 4 lg + 3) within a chunk.
 __device__ __forceinline__ uint32_t v_offset(int tid, int DV)
 {
     uint32_t t = static_cast<uint32_t>(tid);
@@ -437,7 +441,7 @@ __device__ __forceinline__ uint32_t o_offset(int tid, int DV)
     uint32_t t = static_cast<uint32_t>(tid);
     asm volatile("" : "+v"(t));
     const uint32_t w = t >> 6, l = t & 63;
-    return 2u * ((16u * w + 4u * (l >> 4)) * static_cast<uint32_t>(DV) + (l & 15u));
+    return 2u * ((16u * w + (l & 15u)) * static_cast<uint32_t>(DV) + 4u * (l >> 4));
 }
 
 // Per-block constants of the sweep.
@@ -526,10 +530,8 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
     }
 #pragma unroll
     for (int r = 0; r < SPW; ++r) wv[r] = static_cast<float>(X.wr[wrow[r]][lane]) * wscl[r];
-    const float wa = ldexpf(static_cast<float>(X.wr[c.m0 > 0 ? c.m0 - 1 : 0][lane]), c.ea);
 #pragma unroll
     for (int r = 0; r < SPW; ++r) S.W[NW * r + wave][lane] = wv[r];
-    if (act_wave) S.wact[kb][lane] = wa;
     // ---- inter-chunk read: closed states from registers, then the active state
     floatx4 Oi[MT][NTV];
 #pragma unroll
@@ -545,27 +547,36 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
     for (int r = 0; r < SPW; ++r) mine |= ((c.closed >> (NW * r + wave)) & 1u) << r;
     static_assert(SPW % 2 == 0 && SPW <= 8, "slots are read in pairs");
     const int npair = mine ? (33 - __builtin_clz(mine)) / 2 : 0;
+    // (the two blocks on a compute unit share its SIMDs: the closed-state
+    // read, a long run of independent products, issues at the lowest wave
+    // priority, everything else at a higher one, so that one block's short
+    // dependent phases take the issue slots they need while the other block
+    // reads and the products fill the rest)
+    __builtin_amdgcn_s_setprio(0);
     switch (npair) {
     case 0: break;
-    case 1: rs_read_closed<DK, DVT, SPW, 1>(Oi, stk, X, S.W, wave, lane, lg); break;
-    case 2: rs_read_closed<DK, DVT, SPW, (SPW >= 4 ? 2 : 1)>(Oi, stk, X, S.W, wave, lane, lg); break;
-    case 3: rs_read_closed<DK, DVT, SPW, (SPW >= 6 ? 3 : 1)>(Oi, stk, X, S.W, wave, lane, lg); break;
-    default: rs_read_closed<DK, DVT, SPW, SPW / 2>(Oi, stk, X, S.W, wave, lane, lg); break;
+    case 1: rs_read_closed<DK, DVT, SPW, 1>(Oi, stk, X, S.W, wave, lane, lr); break;
+    case 2: rs_read_closed<DK, DVT, SPW, (SPW >= 4 ? 2 : 1)>(Oi, stk, X, S.W, wave, lane, lr); break;
+    case 3: rs_read_closed<DK, DVT, SPW, (SPW >= 6 ? 3 : 1)>(Oi, stk, X, S.W, wave, lane, lr); break;
+    default: rs_read_closed<DK, DVT, SPW, SPW / 2>(Oi, stk, X, S.W, wave, lane, lr); break;
     }
+    __builtin_amdgcn_s_setprio(2);
     if (c.act >= 0 && act_wave) {
+        // the most recent state's weights of token 16 mt + lr, times 2^ea
+        const uint2 wb = *reinterpret_cast<const uint2 *>(&X.wr[c.m0 > 0 ? c.m0 - 1 : 0][(kChunk / 16) * lr]);
+        const float wa[4] = {ldexpf(__uint_as_float(wb.x << 16), c.ea), ldexpf(__uint_as_float(wb.x & 0xffff0000u), c.ea),
+                             ldexpf(__uint_as_float(wb.y << 16), c.ea), ldexpf(__uint_as_float(wb.y & 0xffff0000u), c.ea)};
+        static_assert(MT == 4, "one weight per row tile in the lane's 8 bytes");
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
             Frag<_Float16> qa;
             load_frag(qa, X.qf[mt][kb][lane]);
-            const float4 w = *reinterpret_cast<const float4 *>(&S.wact[kb][16 * mt + 4 * lg]);
 #pragma unroll
             for (int nt = 0; nt < NTV; ++nt) {
                 floatx4 P = floatx4{0.f, 0.f, 0.f, 0.f};
-                mma32(P, qa, af[nt]);
-                Oi[mt][nt][0] = fmaf(w.x, P[0], Oi[mt][nt][0]);
-                Oi[mt][nt][1] = fmaf(w.y, P[1], Oi[mt][nt][1]);
-                Oi[mt][nt][2] = fmaf(w.z, P[2], Oi[mt][nt][2]);
-                Oi[mt][nt][3] = fmaf(w.w, P[3], Oi[mt][nt][3]);
+                mma32(P, af[nt], qa);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) Oi[mt][nt][i] = fmaf(wa[mt], P[i], Oi[mt][nt][i]);
             }
         }
     }
@@ -612,24 +623,19 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
                 for (int nt = 0; nt < NTV; ++nt) {
                     Frag<__bf16> b;
                     load_frag(b, &S.vt[16 * nt + lr][32 * ks + 8 * lg]);
-                    mma32(Oprev[nt], a, b);
+                    mma32(Oprev[nt], b, a);
                 }
             }
         }
         __bf16 *ob = O + (tok0 + c0) * DV + dv0;
         const uint32_t oo = o_offset(tid, DV);
-        if (nvalid == kChunk) {
+        if (nvalid == kChunk || 16 * w + lr < nvalid) {
 #pragma unroll
-            for (int nt = 0; nt < NTV; ++nt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) *at_bytes(ob + r * DV + 16 * nt, oo) = static_cast<__bf16>(Oprev[nt][r]);
-        } else {
-#pragma unroll
-            for (int nt = 0; nt < NTV; ++nt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (16 * w + 4 * lg + r < nvalid)
-                        *at_bytes(ob + r * DV + 16 * nt, oo) = static_cast<__bf16>(Oprev[nt][r]);
+            for (int nt = 0; nt < NTV; ++nt) {
+                const bf16x4 h = {static_cast<__bf16>(Oprev[nt][0]), static_cast<__bf16>(Oprev[nt][1]),
+                                  static_cast<__bf16>(Oprev[nt][2]), static_cast<__bf16>(Oprev[nt][3])};
+                *at_bytes(reinterpret_cast<bf16x4 *>(ob + 16 * nt), oo) = h;
+            }
         }
     }
 

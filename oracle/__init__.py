@@ -73,8 +73,11 @@ class _Args(C.Structure):
         ("ev_t", _p), ("ev_i", _p), ("n_ev", _p),
         ("fin_m", _p), ("fin_S", _p), ("fin_I", _p), ("fin_n", _p), ("fin_start", _p),
         ("fin_has_prev", _p), ("fin_s_prev", _p), ("fin_k_prev", _p),
-        ("fin_t_seen", _p), ("nthreads", C.c_int32),
+        ("fin_t_seen", _p), ("nthreads", C.c_int32), ("merge_rule", C.c_int32),
     ]
+
+
+MERGE_RULES = {"sum": 0, "density": 1}
 
 
 def _ptr(a):
@@ -87,8 +90,11 @@ def _c(a, dt):
 
 def run(q, k, v, lam, C_: int, tau: float, init: dict | None = None,
         want=None, outputs: bool = True, final_states: bool = True,
-        nthreads: int | None = None, lib=None) -> dict:
+        nthreads: int | None = None, lib=None, merge_rule: str = "sum") -> dict:
     """Run the oracle on float32 inputs q,k [S,T,dk], v [S,T,dv], lam [S,T,C].
+
+    ``merge_rule``: "sum" merges the adjacent pair of smallest summed
+    information, "density" the pair of lowest (I_i + I_{i+1}) / (n_i + n_{i+1}).
 
     ``init``: optional starting cache, dict with m [S], S [S,C,dv,dk] (float64
     or float32), I [S,C] int64, n [S,C] int32, start [S,C] int64, has_prev [S],
@@ -148,6 +154,7 @@ def run(q, k, v, lam, C_: int, tau: float, init: dict | None = None,
     out("fin_k_prev", (S_, dk), np.float32, "fin_k_prev")
     out("fin_t_seen", (S_,), np.int64, "fin_t_seen")
     a.nthreads = int(nthreads or os.environ.get("DLA_ORACLE_THREADS", 0) or os.cpu_count() or 1)
+    a.merge_rule = MERGE_RULES[merge_rule]
     rc = (lib or _load()).dlao_run(C.byref(a))
     if rc != 0:
         raise RuntimeError(f"dlao_run failed with code {rc}")
@@ -210,24 +217,31 @@ def brute_force(q, k, v, lam, sets, rows=None) -> np.ndarray:
 
 
 def check_schedule(s, tau: float, C_: int, boundaries, events, m_t=None,
-                   init=None) -> None:
+                   init=None, merge_rule: str = "sum") -> None:
     """Assert that a schedule is exactly what the greedy rule produces from s.
 
     Re-derives from the float32 token information ``s`` alone: every boundary
     (two-consecutive-low rule, s == tau counts as high), the moment of every
     merge (right after an append that exceeds C states, never otherwise), and
-    every merged pair: summed information of each live state is recomputed
-    from the token ranges it covers, and the merged pair must be the earliest
-    adjacent pair of minimal summed information.  ``init`` (optional) is a
-    starting cache: dict with starts (list, oldest first, relative to this
-    call's token 0), infos (int64 list) and s_prev (float) / has_prev.
+    every merged pair: summed information and token count of each live state
+    are recomputed from the token ranges it covers, and the merged pair must
+    be the earliest adjacent pair of minimal summed information ("sum") or of
+    minimal information density, (I_i + I_{i+1}) / (n_i + n_{i+1}) as an exact
+    fraction ("density").  ``init`` (optional) is a starting cache: dict with
+    starts (list, oldest first, relative to this call's token 0), infos (int64
+    list), counts (int list; needed by "density") and s_prev (float) /
+    has_prev.
     """
+    from fractions import Fraction
     s = np.asarray(s, np.float32)
     T = len(s)
     qs = fixed_point(s)
     tau32 = np.float32(tau)
     starts = [] if init is None else list(init["starts"])
     base_info = {} if init is None else dict(zip(init["starts"], init["infos"]))
+    base_count = {} if init is None or "counts" not in init else dict(zip(init["starts"], init["counts"]))
+    assert merge_rule in ("sum", "density")
+    assert merge_rule == "sum" or init is None or "counts" in init
     prev = np.float32(1.0) if init is None else np.float32(init["s_prev"])
     ev = {}
     for t, i in events:
@@ -242,6 +256,11 @@ def check_schedule(s, tau: float, C_: int, boundaries, events, m_t=None,
         tot = int(qs[lo:b_end].sum()) if b_end > lo else 0
         return tot + sum(int(x) for p, x in base_info.items() if a <= p < b_end)
 
+    def count(a, b_end):
+        # tokens of [a, b_end) in this call plus those a starting state held
+        lo = max(a, 0)
+        return max(b_end - lo, 0) + sum(int(x) for p, x in base_count.items() if a <= p < b_end)
+
     for t in range(T):
         low = (s[t] < tau32) and (prev < tau32)
         expect_b = (len(starts) == 0) or (not low)
@@ -252,7 +271,11 @@ def check_schedule(s, tau: float, C_: int, boundaries, events, m_t=None,
                 assert t in ev, f"cache exceeds C after token {t} but no merge logged"
                 ends = starts[1:] + [t + 1]
                 I = [info(a, e) for a, e in zip(starts, ends)]
-                keys = [I[i] + I[i + 1] for i in range(len(I) - 1)]
+                if merge_rule == "sum":
+                    keys = [I[i] + I[i + 1] for i in range(len(I) - 1)]
+                else:
+                    n = [count(a, e) for a, e in zip(starts, ends)]
+                    keys = [Fraction(I[i] + I[i + 1], n[i] + n[i + 1]) for i in range(len(I) - 1)]
                 best = min(range(len(keys)), key=lambda i: (keys[i], i))
                 assert ev[t] == best, f"token {t}: merged pair {ev[t]}, greedy gives {best}"
                 del starts[best + 1]

@@ -30,7 +30,11 @@
  *   - right after a state is appended, if the cache holds C+1 states, the
  *     adjacent pair (i, i+1) with the smallest summed information
  *     I_i + I_{i+1} is merged (the earliest pair on ties); the merged state
- *     keeps the start of state i;
+ *     keeps the start of state i.  With merge_rule = 1 the pair is instead
+ *     the one of lowest information density (I_i + I_{i+1}) / (n_i + n_{i+1}),
+ *     n the token counts: the criterion written in section 5.2 of the
+ *     reading notes; fractions are compared exactly by cross-multiplication,
+ *     the earliest pair again winning ties;
  *   - the read uses the cache after the update and any merge:
  *     o_t = sum_j lam[t][j] * S_(m-1-j) q_t, slot j = j-th most recent state;
  *   - the per-token state is v_t k_t^T (S is d_v x d_k, o = S q).
@@ -76,6 +80,7 @@ typedef struct {
     float *fin_k_prev;              /* [BH][dk] */
     int64_t *fin_t_seen;            /* [BH] */
     int32_t nthreads;
+    int32_t merge_rule;             /* 0: smallest summed information; 1: lowest density */
 } dlao_args;
 
 /* s_t = 1 - cos(k_t, k_prev), rounded once to float. */
@@ -141,12 +146,23 @@ static void run_stream(const dlao_args *A, int bh, double *S, int64_t *I,
             ++m;
             ++nseg;
             if (m > C) {
-                /* 4. capacity merge: adjacent pair with the smallest summed information */
+                /* 4. capacity merge: the adjacent pair with the smallest summed
+                 * information, or (merge_rule 1) the lowest information density
+                 * (I_i + I_{i+1}) / (n_i + n_{i+1}); a / b < c / d is decided as
+                 * a d < c b in 128-bit integers, so the comparison is exact */
                 int best = 0;
-                int64_t bestkey = I[0] + I[1];
-                for (int i = 1; i + 1 < m; ++i) {
-                    int64_t key = I[i] + I[i + 1];
-                    if (key < bestkey) { bestkey = key; best = i; }
+                if (A->merge_rule == 1) {
+                    __int128 bnum = (__int128)(I[0] + I[1]), bden = (__int128)n[0] + n[1];
+                    for (int i = 1; i + 1 < m; ++i) {
+                        const __int128 num = (__int128)(I[i] + I[i + 1]), den = (__int128)n[i] + n[i + 1];
+                        if (num * bden < bnum * den) { bnum = num; bden = den; best = i; }
+                    }
+                } else {
+                    int64_t bestkey = I[0] + I[1];
+                    for (int i = 1; i + 1 < m; ++i) {
+                        int64_t key = I[i] + I[i + 1];
+                        if (key < bestkey) { bestkey = key; best = i; }
+                    }
                 }
                 double *Sa = S + (size_t)best * SS, *Sb = Sa + SS;
                 for (size_t e = 0; e < SS; ++e) Sa[e] += Sb[e];
@@ -228,6 +244,7 @@ int dlao_run(const dlao_args *A)
                       !A->init_has_prev || !A->init_s_prev || !A->init_k_prev ||
                       !A->init_t_seen)) return -1;
     if (A->ev_t && (!A->ev_i || !A->n_ev)) return -1;
+    if (A->merge_rule != 0 && A->merge_rule != 1) return -1;
     if (A->init_m)
         for (int bh = 0; bh < A->BH; ++bh)
             if (A->init_m[bh] < 0 || A->init_m[bh] > A->C) return -1;

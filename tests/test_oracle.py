@@ -108,7 +108,8 @@ def pin_hand_derived_schedule(case, lib=None):
     assert len(e["boundary"]) == T and len(e["m_t"]) == T
     k = keys_for_scores(s_des)[None]
     q, _, v, lam = _rand(T, k.shape[2], 4, case["C"], seed=7)
-    r = oracle.run(q, k, v, lam, case["C"], case["tau"], lib=lib)
+    rule = case.get("merge_rule", "sum")
+    r = oracle.run(q, k, v, lam, case["C"], case["tau"], lib=lib, merge_rule=rule)
     assert r["s"][0].tolist() == [1.0] + [float(x) for x in s_des]
     assert r["b"][0].tolist() == e["boundary"]
     assert r["m_t"][0].tolist() == e["m_t"]
@@ -121,6 +122,9 @@ def pin_hand_derived_schedule(case, lib=None):
     sets = oracle.start_sets(T, r["b"][0], r["events"][0])
     bf = oracle.brute_force(q[0], k[0], v[0], lam[0], sets)
     assert row_rel_err(r["o"][0], bf) < 1e-12
+    # the independent checker re-derives the same merges under the case's rule
+    oracle.check_schedule(r["s"][0], case["tau"], case["C"], r["b"][0], r["events"][0], r["m_t"][0],
+                          merge_rule=rule)
 
 
 @pytest.mark.parametrize("case", _golden(), ids=lambda c: c["name"])
@@ -138,11 +142,19 @@ def test_oracle_equals_brute_force_and_greedy(T, dk, dv, C, tau, seg, seed):
     pin_brute_force_and_greedy(T, dk, dv, C, tau, seg, seed)
 
 
-def pin_brute_force_and_greedy(T, dk, dv, C, tau, seg, seed, lib=None):
+@settings(max_examples=40, deadline=None)
+@given(T=st.integers(1, 90), dk=st.sampled_from([2, 4, 8]), dv=st.sampled_from([1, 3]),
+       C=st.integers(1, 6), tau=st.sampled_from([-1.0, 0.3, 0.9]),
+       seg=st.sampled_from([2, 8, 30]), seed=st.integers(0, 2**31 - 1))
+def test_density_rule_equals_brute_force_and_greedy(T, dk, dv, C, tau, seg, seed):
+    pin_brute_force_and_greedy(T, dk, dv, C, tau, seg, seed, merge_rule="density")
+
+
+def pin_brute_force_and_greedy(T, dk, dv, C, tau, seg, seed, lib=None, merge_rule="sum"):
     q, _, v, lam = _rand(T, dk, dv, C, seed)
     k = _regime_keys(T, dk, seg, seed + 1)[None]
-    r = oracle.run(q, k, v, lam, C, tau, lib=lib)
-    oracle.check_schedule(r["s"][0], tau, C, r["b"][0], r["events"][0], r["m_t"][0])
+    r = oracle.run(q, k, v, lam, C, tau, lib=lib, merge_rule=merge_rule)
+    oracle.check_schedule(r["s"][0], tau, C, r["b"][0], r["events"][0], r["m_t"][0], merge_rule=merge_rule)
     sets = oracle.start_sets(T, r["b"][0], r["events"][0])
     bf = oracle.brute_force(q[0], k[0], v[0], lam[0], sets)
     bf_abs = oracle.brute_force(np.abs(q[0]), np.abs(k[0]), np.abs(v[0]), np.abs(lam[0]), sets)
@@ -182,6 +194,23 @@ def test_checker_catches_planted_mistakes():
     b[i] = 1                                 # a boundary invented
     with pytest.raises(AssertionError):
         oracle.check_schedule(r["s"][0], tau, C, b, ev)
+
+
+def test_rules_differ_and_checker_tells_them_apart():
+    """On regime-structured keys the two merge rules give different
+    schedules, and the checker rejects each schedule under the other rule."""
+    T, C, tau = 400, 4, 0.3
+    q, _, v, lam = _rand(T, 8, 2, C, 21)
+    k = _regime_keys(T, 8, 10, 22)[None]
+    rs = oracle.run(q, k, v, lam, C, tau, merge_rule="sum")
+    rd = oracle.run(q, k, v, lam, C, tau, merge_rule="density")
+    assert rs["b"][0].tolist() == rd["b"][0].tolist()     # the boundary rule is shared
+    assert rs["events"][0] != rd["events"][0]
+    oracle.check_schedule(rd["s"][0], tau, C, rd["b"][0], rd["events"][0], merge_rule="density")
+    with pytest.raises(AssertionError):
+        oracle.check_schedule(rd["s"][0], tau, C, rd["b"][0], rd["events"][0], merge_rule="sum")
+    with pytest.raises(AssertionError):
+        oracle.check_schedule(rs["s"][0], tau, C, rs["b"][0], rs["events"][0], merge_rule="density")
 
 
 # ------------------------------------------------------------- special cases

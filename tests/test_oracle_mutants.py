@@ -65,6 +65,16 @@ MUTANTS = [
      "ot[r] += w * acc;", "ot[r] += acc;"),
     ("start counted from one",
      "st[m] = t_seen;", "st[m] = t_seen + 1;"),
+    ("density ties go to the latest pair",
+     "if (num * bden < bnum * den)", "if (num * bden <= bnum * den)"),
+    ("density compares the numerators only",
+     "if (num * bden < bnum * den)", "if (num < bnum)"),
+    ("density cross-multiplied the wrong way",
+     "if (num * bden < bnum * den)", "if (num * den < bnum * bden)"),
+    ("density counts one state of the pair",
+     "den = (__int128)n[i] + n[i + 1];", "den = (__int128)n[i];"),
+    ("density rule ignored",
+     "if (A->merge_rule == 1) {", "if (0) {"),
 ]
 
 
@@ -76,6 +86,9 @@ def _battery():
     for args in [(70, 4, 3, 3, 0.3, 8, 1), (60, 8, 8, 2, 0.3, 2, 2), (50, 2, 1, 4, 0.9, 1000, 3),
                  (64, 8, 3, 5, -1.0, 8, 4), (40, 4, 8, 1, 3.0, 2, 5), (70, 8, 8, 6, 0.3, 8, 6)]:
         out.append((f"brute force {args}", lambda lib, a=args: P.pin_brute_force_and_greedy(*a, lib=lib)))
+    for args in [(90, 4, 3, 3, 0.3, 8, 7), (80, 8, 2, 4, 0.3, 30, 8), (60, 4, 1, 2, -1.0, 2, 9)]:
+        out.append((f"density brute force {args}",
+                    lambda lib, a=args: P.pin_brute_force_and_greedy(*a, lib=lib, merge_rule="density")))
     for tau, C in [(0.3, 3), (-1.0, 2)]:
         out.append((f"lambda one {tau} {C}", lambda lib, t=tau, c=C: P.pin_lambda_one(t, c, lib)))
     out.append(("single state", lambda lib: P.pin_single_state(0.3, lib)))

@@ -16,7 +16,11 @@ Also reported on the same line:
                 steps/s over a loop of dla_decode_step calls and the decode
                 kernel's algorithmic HBM bytes per launch over its duration,
                 against the HBM peak;
-  cpu_baseline  the CPU oracle on a bounded sample of the prefill workload.
+  cpu_baseline  the CPU oracle on a bounded sample of the prefill workload;
+  prefill_density_merge_rule
+                the same prefill with the capacity merges choosing the pair
+                of lowest information density instead of smallest summed
+                information (--no-density skips it).
 
 roofline.traffic is the kernel's HBM bytes per launch from the hardware
 counters FETCH_SIZE and WRITE_SIZE (two rocprofv3 --pmc passes over this
@@ -106,41 +110,56 @@ def prefill_bench(args, torch, dla, workloads):
         S = min(BH, args.cpu_streams)
         sample = {x: d[x][:S].copy() for x in ("q", "k", "v", "lam")}
     del d
-    cache = dla.Cache(B, H, C, dk, dv, device=dev)
     ws = dla.prefill_workspace(B, H, T, C, dk, dv, dev)
     o = torch.empty(B, H, T, dv, dtype=dt, device=dev)
-    # one untimed call exporting the schedule: m_t gives the algorithmic flops
-    m_t = torch.empty(BH, T, dtype=torch.int32, device=dev)
-    bnd = torch.empty(BH, T, dtype=torch.uint8, device=dev)
-    n_ev = torch.empty(BH, dtype=torch.int32, device=dev)
-    dla.prefill(q, k, v, lam, cfg.tau, cache, o=o, workspace=ws,
-                sched=dict(m_t=m_t, boundary=bnd, n_ev=n_ev))
-    torch.cuda.synchronize()
-    m_sum = int(m_t.sum(dtype=torch.int64).item())
-    flops = 2.0 * (m_sum + BH * T) * dk * dv
-    stats = dict(mean_live_states=m_sum / (BH * T),
-                 boundaries_per_stream=float(bnd.sum(dtype=torch.int64).item()) / BH,
-                 merges_per_stream=float(n_ev.sum(dtype=torch.int64).item()) / BH)
-    for _ in range(args.warmup):
-        dla.prefill(q, k, v, lam, cfg.tau, cache, o=o, workspace=ws)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    for a, b in evs:          # materialise the event handles
-        a.record()
-        b.record()
-    torch.cuda.synchronize()
-    w0 = time.perf_counter()
-    for a, b in evs:
-        dla.dla_set_prefill_events(a.cuda_event, b.cuda_event)
-        dla.prefill(q, k, v, lam, cfg.tau, cache, o=o, workspace=ws)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    dla.dla_set_prefill_events(None, None)
-    kern_ms = [a.elapsed_time(b) for a, b in evs]
-    kern_avg = sum(kern_ms) / len(kern_ms)
-    ms_per_step = wall * 1e3 / args.steps
+
+    def timed(rule):
+        """One untimed call exporting the schedule (m_t gives the algorithmic
+        flops), the warmup, then args.steps timed calls: wall time per step and
+        the chunk kernel's HIP-event time."""
+        cache = dla.Cache(B, H, C, dk, dv, device=dev, merge_rule=rule)
+        m_t = torch.empty(BH, T, dtype=torch.int32, device=dev)
+        bnd = torch.empty(BH, T, dtype=torch.uint8, device=dev)
+        n_ev = torch.empty(BH, dtype=torch.int32, device=dev)
+        dla.prefill(q, k, v, lam, cfg.tau, cache, o=o, workspace=ws,
+                    sched=dict(m_t=m_t, boundary=bnd, n_ev=n_ev))
+        torch.cuda.synchronize()
+        m_sum = int(m_t.sum(dtype=torch.int64).item())
+        flops = 2.0 * (m_sum + BH * T) * dk * dv
+        stats = dict(mean_live_states=m_sum / (BH * T),
+                     boundaries_per_stream=float(bnd.sum(dtype=torch.int64).item()) / BH,
+                     merges_per_stream=float(n_ev.sum(dtype=torch.int64).item()) / BH)
+        for _ in range(args.warmup):
+            dla.prefill(q, k, v, lam, cfg.tau, cache, o=o, workspace=ws)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for a, b in evs:          # materialise the event handles
+            a.record()
+            b.record()
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
+        for a, b in evs:
+            dla.dla_set_prefill_events(a.cuda_event, b.cuda_event)
+            dla.prefill(q, k, v, lam, cfg.tau, cache, o=o, workspace=ws)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - w0
+        dla.dla_set_prefill_events(None, None)
+        kern_ms = [a.elapsed_time(b) for a, b in evs]
+        return wall * 1e3 / args.steps, sum(kern_ms) / len(kern_ms), flops, stats
+
+    ms_per_step, kern_avg, flops, stats = timed("sum")
     tokens = B * T
     achieved = flops / (kern_avg * 1e-3) / 1e12
+    density = None
+    if not args.no_density:
+        d_ms, d_kern, d_flops, d_stats = timed("density")
+        d_ach = d_flops / (d_kern * 1e-3) / 1e12
+        density = dict(merge_rule="density", value=tokens / (d_ms * 1e-3), unit="tokens/s",
+                       ms_per_step=d_ms, kernel_ms=d_kern, achieved=d_ach, unit_achieved="TFLOP/s",
+                       frac=d_ach / PEAK_BF16_TFLOPS, algorithmic_flop_per_launch=d_flops, schedule=d_stats)
+        log(f"prefill, density merge rule: {d_ms:.3f} ms/step, chunk kernel {d_kern:.3f} ms, "
+            f"{100 * d_ach / PEAK_BF16_TFLOPS:.1f}% of bf16 peak, mean live states "
+            f"{d_stats['mean_live_states']:.2f}, merges/stream {d_stats['merges_per_stream']:.1f}")
     kernel = dla.dla_prefill_kernel(dla.DLA_BF16 if cfg.io == "bf16" else dla.DLA_F32, B, H, C, dk, dv)
     traffic = measured_traffic(f"{_kernel_file(kernel)}_{args.workload}_hbm_traffic.txt", kernel)
     res = dict(
@@ -153,11 +172,12 @@ def prefill_bench(args, torch, dla, workloads):
                       kernel=kernel, kernel_ms=kern_avg, algorithmic_flop_per_launch=flops),
         schedule=stats,
         token_heads_per_s=BH * T / (ms_per_step * 1e-3),
+        density_rule=density,
     )
     log(f"prefill: {ms_per_step:.3f} ms/step, chunk kernel {kern_avg:.3f} ms, "
         f"{achieved:.1f} TFLOP/s algorithmic ({100 * achieved / PEAK_BF16_TFLOPS:.1f}% of bf16 peak), "
         f"mean live states {stats['mean_live_states']:.2f}")
-    del q, k, v, lam, o, ws, cache
+    del q, k, v, lam, o, ws
     torch.cuda.empty_cache()
     return res, sample, cfg
 
@@ -326,6 +346,8 @@ def main():
     ap.add_argument("--decode-warmup", type=int, default=8)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-density", action="store_true",
+                    help="skip the second prefill measurement under the information-density merge rule")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--cpu-streams", type=int, default=16)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -357,6 +379,7 @@ def main():
         "data": "synthetic", "config": pre["config"], "roofline": pre["roofline"],
         "cpu_baseline": cpu, "decode": dec, "schedule": pre["schedule"],
         "token_heads_per_s": pre["token_heads_per_s"],
+        "prefill_density_merge_rule": pre["density_rule"],
     }
     print(json.dumps(out), flush=True)
 

@@ -24,6 +24,8 @@ __all__ = [
 
 DLA_OK, DLA_ERR_ARG, DLA_ERR_UNSUPPORTED, DLA_ERR_WORKSPACE, DLA_ERR_HIP = 0, 1, 2, 3, 4
 DLA_F32, DLA_BF16 = 0, 1
+DLA_MERGE_SUM, DLA_MERGE_DENSITY = 0, 1
+MERGE_RULES = {"sum": DLA_MERGE_SUM, "density": DLA_MERGE_DENSITY}
 DLA_MAX_C = 64
 DLA_CHUNK = 64
 
@@ -43,7 +45,7 @@ _STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace", 4: 
 
 class dla_cache(C.Structure):
     _fields_ = [("B", C.c_int32), ("H", C.c_int32), ("C", C.c_int32), ("d_k", C.c_int32),
-                ("d_v", C.c_int32), ("reserved", C.c_int32), ("base", C.c_void_p),
+                ("d_v", C.c_int32), ("merge_rule", C.c_int32), ("base", C.c_void_p),
                 ("bytes", C.c_uint64)]
 
 
@@ -95,6 +97,8 @@ def load():
     lib.dla_cache_init.restype = C.c_int
     lib.dla_cache_init.argtypes = [C.POINTER(dla_cache), vp, u64] + [i32] * 5 + \
         [C.POINTER(dla_cache_preload), vp]
+    lib.dla_cache_set_merge_rule.restype = C.c_int
+    lib.dla_cache_set_merge_rule.argtypes = [C.POINTER(dla_cache), i32]
     lib.dla_prefill_workspace_bytes.restype = u64
     lib.dla_prefill_workspace_bytes.argtypes = [i32] * 6
     lib.dla_prefill.restype = C.c_int
@@ -135,6 +139,10 @@ def dla_cache_init(cache: dla_cache, base: int, nbytes: int, B, H, C_, d_k, d_v,
                    preload: dla_cache_preload | None, stream: int) -> int:
     return load().dla_cache_init(C.byref(cache), base, nbytes, B, H, C_, d_k, d_v,
                                  C.byref(preload) if preload is not None else None, stream)
+
+
+def dla_cache_set_merge_rule(cache: dla_cache, rule: int) -> int:
+    return _check(load().dla_cache_set_merge_rule(C.byref(cache), rule))
 
 
 def dla_prefill_workspace_bytes(B, H, T, C_, d_k, d_v) -> int:
@@ -210,9 +218,13 @@ def _stream(device):
 
 
 class Cache:
-    """A device cache for B*H streams (torch uint8 buffer + dla_cache view)."""
+    """A device cache for B*H streams (torch uint8 buffer + dla_cache view).
 
-    def __init__(self, B, H, C_, d_k, d_v, device="cuda", preload: dict | None = None):
+    ``merge_rule``: "sum" (smallest summed information, the default) or
+    "density" (lowest information density) for the capacity merges."""
+
+    def __init__(self, B, H, C_, d_k, d_v, device="cuda", preload: dict | None = None,
+                 merge_rule: str = "sum"):
         torch = _torch()
         nbytes = dla_cache_bytes(B, H, C_, d_k, d_v)
         if nbytes == 0:
@@ -234,6 +246,9 @@ class Cache:
                                     sta.data_ptr(), int(preload.get("t_seen", 0)))
         _check(dla_cache_init(self.view, self.buf.data_ptr(), nbytes, B, H, C_, d_k, d_v, pre,
                               _stream(self.buf.device)))
+        if merge_rule not in MERGE_RULES:
+            raise DLAError(DLA_ERR_ARG, f"unknown merge rule {merge_rule!r}")
+        dla_cache_set_merge_rule(self.view, MERGE_RULES[merge_rule])
 
     @property
     def device(self):

@@ -108,6 +108,8 @@ dla_status check_cache(const dla_cache *c)
     if (!c->base || !aligned(c->base, 256)) return fail(DLA_ERR_ARG, "cache base is NULL or not 256-byte aligned");
     if (c->bytes < dla_cache_bytes(c->B, c->H, c->C, c->d_k, c->d_v))
         return fail(DLA_ERR_ARG, "cache buffer too small (%llu bytes)", static_cast<unsigned long long>(c->bytes));
+    if (c->merge_rule != DLA_MERGE_SUM && c->merge_rule != DLA_MERGE_DENSITY)
+        return fail(DLA_ERR_ARG, "unknown merge rule %d", c->merge_rule);
     return DLA_OK;
 }
 
@@ -235,7 +237,7 @@ dla_status dla_cache_init(dla_cache *cache, void *base, uint64_t bytes, int32_t 
         pre.t_seen = preload->t_seen;
     }
     cache->B = B; cache->H = H; cache->C = C; cache->d_k = d_k; cache->d_v = d_v;
-    cache->reserved = 0;
+    cache->merge_rule = DLA_MERGE_SUM;
     cache->base = base;
     cache->bytes = bytes;
     const CacheGeom g = geom(cache);
@@ -245,6 +247,15 @@ dla_status dla_cache_init(dla_cache *cache, void *base, uint64_t bytes, int32_t 
     uint8_t *meta = b8 + align_up(states_bytes(BH, C, d_k, d_v), 256);
     return hip_status(launch_cache_init(states, meta, g, pre, static_cast<hipStream_t>(stream)),
                       "cache init launch");
+}
+
+dla_status dla_cache_set_merge_rule(dla_cache *cache, int32_t rule)
+{
+    if (!cache) return fail(DLA_ERR_ARG, "cache is NULL");
+    if (rule != DLA_MERGE_SUM && rule != DLA_MERGE_DENSITY)
+        return fail(DLA_ERR_ARG, "unknown merge rule %d", rule);
+    cache->merge_rule = rule;
+    return ok();
 }
 
 uint64_t dla_prefill_workspace_bytes(int32_t B, int32_t H, int32_t T, int32_t C, int32_t d_k, int32_t d_v)
@@ -284,6 +295,7 @@ dla_status dla_prefill(const void *q, const void *k, const void *v, const void *
     a.T = T;
     a.tau = tau;
     a.io_bf16 = io == DLA_BF16;
+    a.merge_rule = cache->merge_rule;
     const PrefillPlan plan = plan_prefill(a.io_bf16, BH, cache->C, cache->d_k, cache->d_v);
     a.dvt = plan.dvt;
     a.register_resident = plan.register_resident;
@@ -341,6 +353,7 @@ dla_status dla_decode_step(const void *q, const void *k, const void *v, const vo
     a.q = q; a.k = k; a.v = v; a.lam = lam; a.o = o;
     a.tau = tau;
     a.io_bf16 = io == DLA_BF16;
+    a.merge_rule = cache->merge_rule;
     a.g = geom(cache);
     const int64_t BH = static_cast<int64_t>(cache->B) * cache->H;
     uint8_t *b8 = static_cast<uint8_t *>(cache->base);

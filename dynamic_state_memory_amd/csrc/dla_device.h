@@ -193,6 +193,31 @@ __device__ __forceinline__ void read_frag_from(Frag<float> &f, const float *p, i
 
 __device__ __forceinline__ int64_t min_i64(int64_t a, int64_t b) { return b < a ? b : a; }
 
+// Lane holding the smallest of the fractions num / den (num >= 0, den >= 1)
+// over the lanes with ok set, the lowest such lane on ties; the same in every
+// lane (64 if no lane is ok).  a / b < c / d is decided as a d < c b in
+// 128-bit integers, so the comparison is exact.  A butterfly over the 64
+// lanes; the whole wave must be active.
+__device__ __forceinline__ int wave_argmin_frac(int64_t num, int64_t den, bool ok)
+{
+    int idx = ok ? static_cast<int>(__lane_id()) : 64;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int64_t n2 = __shfl_xor(num, off);
+        const int64_t d2 = __shfl_xor(den, off);
+        const int i2 = __shfl_xor(idx, off);
+        const __int128 lhs = static_cast<__int128>(n2) * den;   // n2 / d2 < num / den  <=>  lhs < rhs
+        const __int128 rhs = static_cast<__int128>(num) * d2;
+        const bool take = i2 < 64 && (idx == 64 || lhs < rhs || (lhs == rhs && i2 < idx));
+        if (take) {
+            num = n2;
+            den = d2;
+            idx = i2;
+        }
+    }
+    return __builtin_amdgcn_readfirstlane(idx);
+}
+
 // Minimum over the 64 lanes of a wave, in every lane (DPP row steps, then the
 // four row results; the whole wave must be active).
 __device__ __forceinline__ int64_t wave_min_i64(int64_t x) {

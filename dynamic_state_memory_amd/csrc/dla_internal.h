@@ -88,6 +88,7 @@ struct PrefillArgs {
     int T;
     float tau;
     int io_bf16;
+    int merge_rule;                   // DLA_MERGE_SUM or DLA_MERGE_DENSITY
     int dvt;
     CacheGeom g;
     float *states;
@@ -110,6 +111,7 @@ struct DecodeArgs {
     void *o;
     float tau;
     int io_bf16;
+    int merge_rule;                   // DLA_MERGE_SUM or DLA_MERGE_DENSITY
     CacheGeom g;
     float *states;
     uint8_t *meta;

@@ -230,7 +230,7 @@ __global__ __launch_bounds__(64) void k_greedy(int T, int C, int NCH,
                                                uint8_t *__restrict__ meta_base, size_t meta_stride,
                                                int32_t *__restrict__ ev_t_out,
                                                int32_t *__restrict__ ev_i_out,
-                                               int32_t *__restrict__ n_ev_out)
+                                               int32_t *__restrict__ n_ev_out, int merge_rule)
 {
     const int bh = blockIdx.x;
     const int lane = threadIdx.x;
@@ -280,10 +280,15 @@ __global__ __launch_bounds__(64) void k_greedy(int T, int C, int NCH,
                 const int32_t pn = inside ? n_nx : 1;
                 const int32_t pst = inside ? st_nx : t;
                 const int32_t poi = inside ? oi_nx : -1;
-                const int64_t key = lane < m ? I + pI : INT64_MAX;
-                const int64_t kmin = wave_min_i64(key);
-                const uint64_t hit = __ballot(key == kmin);
-                istar = __ffsll(static_cast<unsigned long long>(hit)) - 1;
+                if (merge_rule == DLA_MERGE_DENSITY) {
+                    // lowest information density (I_i + I_{i+1}) / (n_i + n_{i+1})
+                    istar = wave_argmin_frac(I + pI, static_cast<int64_t>(n) + pn, lane < m);
+                } else {
+                    const int64_t key = lane < m ? I + pI : INT64_MAX;
+                    const int64_t kmin = wave_min_i64(key);
+                    const uint64_t hit = __ballot(key == kmin);
+                    istar = __ffsll(static_cast<unsigned long long>(hit)) - 1;
+                }
                 const int32_t d_oi = readlane_any(poi, istar);
                 const int32_t d_st = readlane_any(pst, istar);
                 dead = d_oi >= 0 ? d_oi : 64 + (d_st - cur_chunk * kChunk);
@@ -759,7 +764,7 @@ __global__ __launch_bounds__(256) void k_decode(const TIO *__restrict__ Qg, cons
                                                 const TIO *__restrict__ Vg, const TIO *__restrict__ Lg,
                                                 TIO *__restrict__ Og, float tau, int C,
                                                 float *__restrict__ states, uint8_t *__restrict__ meta_base,
-                                                size_t meta_stride, DecodeSched sched)
+                                                size_t meta_stride, DecodeSched sched, int merge_rule)
 {
     constexpr int G = D / 4;          // threads per state row (float4 each)
     constexpr int R = 256 / G;        // rows per pass
@@ -835,9 +840,16 @@ __global__ __launch_bounds__(256) void k_decode(const TIO *__restrict__ Qg, cons
             const int64_t I_nx = __shfl_down(I, 1);
             const bool inside = lane + 1 < m;
             const int64_t pI = inside ? I_nx : qv;
-            const int64_t key = lane < m ? I + pI : INT64_MAX;
-            const int64_t kmin = wave_min_i64(key);
-            merge_i = __ffsll(static_cast<unsigned long long>(__ballot(key == kmin))) - 1;
+            if (merge_rule == DLA_MERGE_DENSITY) {
+                // lowest information density (I_i + I_{i+1}) / (n_i + n_{i+1})
+                const int32_t n_down = __shfl_down(n, 1);
+                const int64_t pn = inside ? n_down : 1;
+                merge_i = wave_argmin_frac(I + pI, static_cast<int64_t>(n) + pn, lane < m);
+            } else {
+                const int64_t key = lane < m ? I + pI : INT64_MAX;
+                const int64_t kmin = wave_min_i64(key);
+                merge_i = __ffsll(static_cast<unsigned long long>(__ballot(key == kmin))) - 1;
+            }
             post_slot = m - 1 - (lane <= merge_i ? lane : lane - 1);
             if (merge_i == m - 1) {
                 mode = 3;                              // the new token joins the most recent state
@@ -969,7 +981,7 @@ static hipError_t prefill_schedule(const PrefillArgs &a, hipStream_t stream)
                        a.sched.seg_id);
     hipLaunchKernelGGL(k_greedy, dim3(BH), dim3(64), 0, stream, T, a.g.C, NCH, a.ws.seg_t, a.ws.seg_P,
                        a.ws.seg_q0, a.ws.nseg, a.ws.events, a.ws.chunk_ev, a.ws.s, a.meta, a.g.meta_stride,
-                       a.sched.ev_t, a.sched.ev_i, a.sched.n_ev);
+                       a.sched.ev_t, a.sched.ev_i, a.sched.n_ev, a.merge_rule);
     hipLaunchKernelGGL((k_store_kprev<TIO>), dim3(BH), dim3(128), 0, stream, K, T, DK, a.meta,
                        a.g.meta_stride);
     return hipGetLastError();
@@ -1047,10 +1059,10 @@ static hipError_t decode_typed(const DecodeArgs &a, hipStream_t stream)
     TIO *o = static_cast<TIO *>(a.o);
     if (a.g.dk == 128)
         hipLaunchKernelGGL((k_decode<TIO, 128>), dim3(BH), dim3(256), 0, stream, q, k, v, l, o, a.tau,
-                           a.g.C, a.states, a.meta, a.g.meta_stride, a.sched);
+                           a.g.C, a.states, a.meta, a.g.meta_stride, a.sched, a.merge_rule);
     else
         hipLaunchKernelGGL((k_decode<TIO, 64>), dim3(BH), dim3(256), 0, stream, q, k, v, l, o, a.tau,
-                           a.g.C, a.states, a.meta, a.g.meta_stride, a.sched);
+                           a.g.C, a.states, a.meta, a.g.meta_stride, a.sched, a.merge_rule);
     return hipGetLastError();
 }
 

@@ -26,7 +26,11 @@
  *   - information sums are int64 multiples of 2^-32 (exact);
  *   - after an append that leaves C+1 states, the adjacent pair with the
  *     smallest summed information is merged (earliest pair on ties); the
- *     merged state keeps the earlier start;
+ *     merged state keeps the earlier start.  A cache set to
+ *     DLA_MERGE_DENSITY merges instead the pair of lowest information
+ *     density (I_i + I_{i+1}) / (n_i + n_{i+1}), n the token counts: the
+ *     criterion the reading notes write in section 5.2, compared exactly,
+ *     earliest pair on ties;
  *   - o_t is read after the update and any merge;
  *   - lam is indexed by cache slot, slot 0 = most recent state.
  *
@@ -52,7 +56,7 @@
 extern "C" {
 #endif
 
-#define DLA_ABI_VERSION 1
+#define DLA_ABI_VERSION 2
 #define DLA_MAX_C 64        /* largest supported cache capacity */
 #define DLA_CHUNK 64        /* tokens per prefill chunk */
 
@@ -68,6 +72,12 @@ typedef enum dla_dtype {
     DLA_F32 = 0,   /* float32 inputs and outputs */
     DLA_BF16 = 1   /* bfloat16 inputs and outputs */
 } dla_dtype;
+
+/* Which adjacent pair a capacity merge joins. */
+typedef enum dla_merge_rule {
+    DLA_MERGE_SUM = 0,       /* smallest summed information I_i + I_{i+1} (the default) */
+    DLA_MERGE_DENSITY = 1    /* lowest information density (I_i + I_{i+1}) / (n_i + n_{i+1}) */
+} dla_merge_rule;
 
 /*
  * Cache: caller-owned device memory holding, for every stream (b, h), up to
@@ -90,8 +100,8 @@ typedef enum dla_dtype {
  */
 typedef struct dla_cache {
     int32_t B, H, C, d_k, d_v;
-    int32_t reserved;
-    void *base;        /* device pointer */
+    int32_t merge_rule;  /* a dla_merge_rule; dla_cache_init sets DLA_MERGE_SUM */
+    void *base;          /* device pointer */
     uint64_t bytes;
 } dla_cache;
 
@@ -156,6 +166,17 @@ dla_status dla_cache_layout(int32_t B, int32_t H, int32_t C, int32_t d_k, int32_
 dla_status dla_cache_init(dla_cache *cache, void *base, uint64_t bytes, int32_t B,
                           int32_t H, int32_t C, int32_t d_k, int32_t d_v,
                           const dla_cache_preload *preload, void *stream);
+
+/*
+ * Merge rule of the cache's streams from the next prefill or decode call on:
+ * DLA_MERGE_SUM or DLA_MERGE_DENSITY (reading notes "Dynamic Linear Attention
+ * | Chlience Paper Archive", section 5.2: the pair of lowest information
+ * density is merged).  Host only: it sets cache->merge_rule, which a caller
+ * may also set directly; prefill and decode reject any other value with
+ * DLA_ERR_ARG.  DLA_ERR_ARG for a NULL cache or an unknown rule (the cache is
+ * then unchanged).
+ */
+dla_status dla_cache_set_merge_rule(dla_cache *cache, int32_t rule);
 
 /* Workspace bytes dla_prefill needs for this shape; 0 if the shape is invalid. */
 uint64_t dla_prefill_workspace_bytes(int32_t B, int32_t H, int32_t T, int32_t C,

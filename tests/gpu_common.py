@@ -30,7 +30,7 @@ def oracle_threads() -> int:
     return min(os.cpu_count() or 1, 16)
 
 
-def gpu_prefill(q, k, v, lam, C, tau, io, B=None, H=None, repeats=1):
+def gpu_prefill(q, k, v, lam, C, tau, io, B=None, H=None, repeats=1, merge_rule="sum"):
     """q,k [S,T,dk] ... float32 numpy (already bf16-valued for bf16).  Returns
     o (float32 numpy [S,T,dv]), schedule dict, final cache dict."""
     torch = torch_mod()
@@ -54,7 +54,7 @@ def gpu_prefill(q, k, v, lam, C, tau, io, B=None, H=None, repeats=1):
                  ev_t=torch.empty(BH, T, dtype=torch.int32, device=dev),
                  ev_i=torch.empty(BH, T, dtype=torch.int32, device=dev),
                  n_ev=torch.empty(BH, dtype=torch.int32, device=dev))
-    cache = dla.Cache(B, H, C, dk, dv, device=dev)
+    cache = dla.Cache(B, H, C, dk, dv, device=dev, merge_rule=merge_rule)
     ws = dla.prefill_workspace(B, H, T, C, dk, dv, dev)
     outs = []
     for _ in range(repeats):

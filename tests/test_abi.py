@@ -23,7 +23,7 @@ def test_library_exports_every_declared_symbol():
     assert {"dla_prefill", "dla_decode_step", "dla_cache_init"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert dla.dla_abi_version() == 1
+    assert dla.dla_abi_version() == 2
 
 
 def test_sizes_and_layout():
@@ -106,6 +106,25 @@ def test_bad_arguments_are_rejected_on_the_host():
     assert dla.dla_cache_init(cc, p, 1 << 30, 1, 1, 8, 64, 64, pre, None) == dla.DLA_ERR_ARG
     pre = dla.dla_cache_preload(2, 0, None, p, p, p, 0)
     assert dla.dla_cache_init(cc, p, 1 << 30, 1, 1, 8, 64, 64, pre, None) == dla.DLA_ERR_ARG
+
+
+def test_merge_rule_is_validated_on_the_host():
+    p = 0x100000
+    # the view's layout: the rule sits where the header puts it
+    assert C.sizeof(dla.dla_cache) == 40 and dla.dla_cache.merge_rule.offset == 20
+    c = _cache()
+    assert c.merge_rule == dla.DLA_MERGE_SUM
+    assert dla.load().dla_cache_set_merge_rule(C.byref(c), 2) == dla.DLA_ERR_ARG
+    assert "merge rule" in dla.dla_last_error() and c.merge_rule == dla.DLA_MERGE_SUM
+    assert dla.load().dla_cache_set_merge_rule(None, 1) == dla.DLA_ERR_ARG
+    dla.dla_cache_set_merge_rule(c, dla.DLA_MERGE_DENSITY)
+    assert c.merge_rule == dla.DLA_MERGE_DENSITY
+    # a rule set directly in the view is checked by prefill and decode
+    c.merge_rule = 5
+    ws = dla.dla_prefill_workspace_bytes(1, 1, 100, 8, 64, 64)
+    assert dla.dla_prefill(p, p, p, p, p, 100, 0.3, dla.DLA_F32, c, p, ws, None, None) == dla.DLA_ERR_ARG
+    assert "merge rule" in dla.dla_last_error()
+    assert dla.dla_decode_step(p, p, p, p, p, 0.3, dla.DLA_BF16, c, None, None) == dla.DLA_ERR_ARG
 
 
 def test_gpu_package_never_imports_the_oracle():

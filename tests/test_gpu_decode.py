@@ -50,11 +50,13 @@ def _merge_log(r, S, n):
     return ev
 
 
-@pytest.mark.parametrize("name,io,T,j,means", [
-    ("tiny_fp32", "f32", 512, 100, None),
-    ("long_t131k_bf16", "bf16", 1500, 300, (20,)),
+@pytest.mark.parametrize("name,io,T,j,means,rule", [
+    ("tiny_fp32", "f32", 512, 100, None, "sum"),
+    ("long_t131k_bf16", "bf16", 1500, 300, (20,), "sum"),
+    ("long_t131k_bf16", "bf16", 1500, 300, (20,), "density"),
+    ("tiny_fp32", "f32", 512, 100, None, "density"),
 ])
-def test_prefill_then_decode_equals_one_prefill(name, io, T, j, means):
+def test_prefill_then_decode_equals_one_prefill(name, io, T, j, means, rule):
     torch = torch_mod()
     import dynamic_state_memory_amd as dla
     cfg = workloads.CONFIGS[name]
@@ -63,12 +65,12 @@ def test_prefill_then_decode_equals_one_prefill(name, io, T, j, means):
     streams = [0] if cfg.B * cfg.H == 1 else [0, 1, 2]
     d = workloads.prefill_inputs(cfg, streams=streams, T=T)
     S = len(streams)
-    say(f"decode equivalence {name}: prefill {T - j} + {j} steps")
-    r = oracle.run(d["q"], d["k"], d["v"], d["lam"], cfg.C, cfg.tau, nthreads=oracle_threads())
+    say(f"decode equivalence {name} ({rule} rule): prefill {T - j} + {j} steps")
+    r = oracle.run(d["q"], d["k"], d["v"], d["lam"], cfg.C, cfg.tau, nthreads=oracle_threads(), merge_rule=rule)
     # prefill of the first T - j tokens
     dev = torch.device("cuda:0")
     dt = torch.bfloat16 if io == "bf16" else torch.float32
-    cache = dla.Cache(1, S, cfg.C, cfg.dk, cfg.dv, device=dev)
+    cache = dla.Cache(1, S, cfg.C, cfg.dk, cfg.dv, device=dev, merge_rule=rule)
 
     def up(a, d_):
         return torch.from_numpy(np.ascontiguousarray(a[:, :T - j])).to(dev).to(dt).reshape(1, S, T - j, d_)
@@ -103,8 +105,9 @@ def _decode_workload(n_unique, steps, B, H):
     return d, idx
 
 
-@pytest.mark.parametrize("B,H,n_unique,steps", [(1, 32, 32, 400), (256, 16, 32, 40)])
-def test_batched_decode_workload(B, H, n_unique, steps):
+@pytest.mark.parametrize("B,H,n_unique,steps,rule", [(1, 32, 32, 400, "sum"), (256, 16, 32, 40, "sum"),
+                                                    (1, 32, 32, 400, "density")])
+def test_batched_decode_workload(B, H, n_unique, steps, rule):
     """Full caches preloaded; steps of fresh tokens.  The full launch
     configuration (B=256, H=16) tiles 32 distinct caches over the 4096 streams,
     so every stream is checked against the oracle."""
@@ -114,11 +117,16 @@ def test_batched_decode_workload(B, H, n_unique, steps):
     cfg = d["cfg"]
     C, dk, dv = cfg.C, cfg.dk, cfg.dv
     S = n_unique
-    say(f"batched decode B={B} H={H} unique={S} steps={steps}: oracle")
+    say(f"batched decode B={B} H={H} unique={S} steps={steps} ({rule} rule): oracle")
     init = dict(m=np.full(S, C, np.int32), S=d["states"], I=d["info"], n=d["count"], start=d["start"],
                 has_prev=np.zeros(S, np.int32), s_prev=np.ones(S, np.float32),
                 k_prev=np.zeros((S, dk), np.float32), t_seen=np.full(S, d["t_seen"], np.int64))
-    r = oracle.run(d["q"], d["k"], d["v"], d["lam"], C, cfg.tau, init=init, nthreads=oracle_threads())
+    r = oracle.run(d["q"], d["k"], d["v"], d["lam"], C, cfg.tau, init=init, nthreads=oracle_threads(),
+                   merge_rule=rule)
+    if rule == "density":
+        r_sum = oracle.run(d["q"], d["k"], d["v"], d["lam"], C, cfg.tau, init=init, outputs=False,
+                           final_states=False, nthreads=oracle_threads())
+        assert any(a != b for a, b in zip(r["events"], r_sum["events"])), "the two rules agree on this input"
     dev = torch.device("cuda:0")
     say(f"batched decode B={B} H={H}: GPU")
     ti = torch.from_numpy(idx).to(dev)
@@ -126,7 +134,7 @@ def test_batched_decode_workload(B, H, n_unique, steps):
                info=torch.from_numpy(d["info"]).to(dev)[ti],
                count=torch.from_numpy(d["count"]).to(dev)[ti],
                start=torch.from_numpy(d["start"]).to(dev)[ti], t_seen=d["t_seen"])
-    cache = dla.Cache(B, H, C, dk, dv, device=dev, preload=pre)
+    cache = dla.Cache(B, H, C, dk, dv, device=dev, preload=pre, merge_rule=rule)
     del pre
     o, sc = _decode_steps(cache, d["q"][idx], d["k"][idx], d["v"][idx], d["lam"][idx], cfg.tau,
                           "bf16", B, H)

@@ -17,11 +17,11 @@ pytestmark = pytest.mark.gpu
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "schedule_cases.json")
 
 
-def _full_check(d, C, tau, io, label, B=None, H=None):
+def _full_check(d, C, tau, io, label, B=None, H=None, merge_rule="sum"):
     say(f"prefill {label}: S={d['k'].shape[0]} T={d['k'].shape[1]} dk={d['k'].shape[2]} "
-        f"dv={d['v'].shape[2]} C={C} tau={tau} io={io}")
-    o, sc, fin = gpu_prefill(d["q"], d["k"], d["v"], d["lam"], C, tau, io, B=B, H=H)
-    r = oracle.run(d["q"], d["k"], d["v"], d["lam"], C, tau, nthreads=oracle_threads())
+        f"dv={d['v'].shape[2]} C={C} tau={tau} io={io} merge={merge_rule}")
+    o, sc, fin = gpu_prefill(d["q"], d["k"], d["v"], d["lam"], C, tau, io, B=B, H=H, merge_rule=merge_rule)
+    r = oracle.run(d["q"], d["k"], d["v"], d["lam"], C, tau, nthreads=oracle_threads(), merge_rule=merge_rule)
     compare_schedule(r, sc, fin, label)
     compare_states(r, fin, label=label)
     err = compare_outputs(o, r["o"], TOL[io], label)
@@ -50,9 +50,11 @@ def test_hand_derived_schedules(io):
         v = workloads.round_bf16(rng.standard_normal((1, T, 16)).astype(np.float32) / 4)
         lam = workloads.round_bf16(rng.uniform(0.1, 1, (1, T, case["C"])).astype(np.float32))
         d = dict(q=q, k=k, v=v, lam=lam)
-        r = _full_check(d, case["C"], case["tau"], io, f"golden {case['name']} {io}")
+        rule = case.get("merge_rule", "sum")
+        r = _full_check(d, case["C"], case["tau"], io, f"golden {case['name']} {io}", merge_rule=rule)
         e = case["expect"]
         assert r["b"][0].tolist() == e["boundary"]
+        assert [list(x) for x in r["events"][0]] == e["events"]
 
 
 REDUCED = [
@@ -98,6 +100,28 @@ def test_dk64_bf16_many_chunks(C, prefill_path):
     d = workloads.prefill_inputs(cfg, streams=[0, 1], T=1000)
     r = _full_check(d, C, cfg.tau, "bf16", f"dk64 C={C}")
     assert r["n_ev"].min() > 0
+
+
+DENSITY = [
+    # (workload, streams, T, C, segment means)
+    ("mamba2_780m_bf16", [0, 1, 2], 1100, 16, (12, 90)),
+    ("gdn_1p3b_t32k_bf16", [0, 1], 2300, 32, (6, 40)),
+    ("long_t131k_bf16", [4], 900, 5, (8,)),
+]
+
+
+@pytest.mark.parametrize("name,streams,T,C,means", DENSITY)
+def test_density_merge_rule(name, streams, T, C, means, prefill_path):
+    """Merging the pair of lowest information density: the GPU schedule equals
+    the oracle's bit for bit, and it is not the summed rule's schedule."""
+    torch_mod()
+    cfg = dataclasses.replace(workloads.CONFIGS[name], C=C, seg_means=means)
+    d = workloads.prefill_inputs(cfg, streams=streams, T=T)
+    r = _full_check(d, C, cfg.tau, "bf16", f"density {name}", merge_rule="density")
+    r_sum = oracle.run(d["q"], d["k"], d["v"], d["lam"], C, cfg.tau, outputs=False, final_states=False,
+                       nthreads=oracle_threads())
+    assert r["n_ev"].min() > 0
+    assert any(a != b for a, b in zip(r["events"], r_sum["events"])), "the two rules agree on this input"
 
 
 def test_literal_noise_reading_every_token_opens(prefill_path):

@@ -20,7 +20,11 @@ Also reported on the same line:
   prefill_density_merge_rule
                 the same prefill with the capacity merges choosing the pair
                 of lowest information density instead of smallest summed
-                information (--no-density skips it).
+                information (--no-density skips it);
+  decode_bf16_states
+                the same decode on caches storing closed states as bf16 (the
+                most recent one stays fp32), with its algorithmic bytes
+                (--no-bf16-states skips it).
 
 roofline.traffic is the kernel's HBM bytes per launch from the hardware
 counters FETCH_SIZE and WRITE_SIZE (two rocprofv3 --pmc passes over this
@@ -224,7 +228,9 @@ def decode_inputs_device(torch, cfg, steps, dev):
                 q=Q, k=K, v=V, lam=L)
 
 
-def decode_bench(args, torch, dla, workloads):
+def decode_bench(args, torch, dla, workloads, state_dtype="f32"):
+    """Batched decode on preloaded full caches: every state fp32 ("f32"), or
+    closed states bf16 and the most recent fp32 ("bf16")."""
     cfg = workloads.CONFIGS[args.decode_workload]
     B, H, C, dk, dv = cfg.B, cfg.H, cfg.C, cfg.dk, cfg.dv
     BH = B * H
@@ -232,7 +238,7 @@ def decode_bench(args, torch, dla, workloads):
     S, W = args.decode_steps, args.decode_warmup
     t0 = time.time()
     d = decode_inputs_device(torch, cfg, S + W, dev)
-    cache = dla.Cache(B, H, C, dk, dv, device=dev,
+    cache = dla.Cache(B, H, C, dk, dv, device=dev, state_dtype=state_dtype,
                       preload=dict(m0=C, states=d["states"], info=d["info"], count=d["count"],
                                    start=d["start"], t_seen=d["t_seen"]))
     del d["states"]
@@ -261,34 +267,46 @@ def decode_bench(args, torch, dla, workloads):
     wall = time.perf_counter() - w0
     kern = [a.elapsed_time(b) for a, b in evs]
     kern_avg = sum(kern) / S
-    # algorithmic bytes: every live state read once; states written (1, or 2
-    # for a merge away from the newest pair); q, k, v, lam in, o out (bf16);
-    # the stream's metadata read and written
+    # algorithmic bytes: every live state read once, the states a step changes
+    # written once; q, k, v, lam in, o out (bf16); the stream's metadata read
+    # and written
     b_ = bnd[W:].to(torch.int64)
     e_ = evi[W:].to(torch.int64)
     m_prev = torch.cat([mt[W - 1:W] if W > 0 else torch.full((1, BH), C, dtype=torch.int32, device=dev),
                         mt[W:-1]], 0).to(torch.int64)
-    writes = torch.where((b_ == 1) & (e_ >= 0) & (e_ < m_prev - 1), 2, 1)
-    st_bytes = dk * dv * 4
+    D2 = dk * dv
+    if state_dtype == "f32":
+        # fp32 states: one written, or two for a merge away from the newest pair
+        writes = torch.where((b_ == 1) & (e_ >= 0) & (e_ < m_prev - 1), 2, 1)
+        st_bytes = (m_prev * 4 + writes * 4) * D2
+    else:
+        # m - 1 closed bf16 states and the fp32 active one read; written: the
+        # active one (4 B) always, plus the closing active state (2 B) when a
+        # new state opens without absorbing the token, plus a merged pair's
+        # result (2 B) when the merge is not into the active state
+        closes = (b_ == 1) & ((e_ < 0) | (e_ < m_prev - 2))
+        merged = (b_ == 1) & (e_ >= 0) & (e_ < m_prev - 1)
+        st_bytes = ((m_prev - 1) * 2 + 4 + 4 + 2 * closes.to(torch.int64) + 2 * merged.to(torch.int64)) * D2
     meta_rw = 2 * (32 + 64 + 20 * m_prev + 4 * dk)
     io_bytes = 2 * (2 * dk + dv + C + dv)
-    total = (m_prev * st_bytes + writes * st_bytes + meta_rw + io_bytes).sum().item()
+    total = (st_bytes + meta_rw + io_bytes).sum().item()
     bytes_per_step = total / S
     achieved = bytes_per_step / (kern_avg * 1e-3) / 1e9
     res = dict(
         workload=f"{args.decode_workload}", B=B, H=H, d_k=dk, d_v=dv, C=C, steps=S, warmup=W,
+        state_dtype=state_dtype,
         steps_per_s=S / wall, ms_per_step=wall * 1e3 / S, tokens_per_s=BH * S / wall,
         boundaries_per_stream=float(b_.sum().item()) / BH,
         merges_per_stream=float((e_ >= 0).sum().item()) / BH,
         roofline=dict(bound="hbm", achieved=achieved, peak=PEAK_HBM_GBS, unit="GB/s",
                       frac=achieved / PEAK_HBM_GBS,
-                      traffic=measured_traffic(f"k_decode_{args.decode_workload}_hbm_traffic.txt",
-                                               "k_decode"),
+                      traffic=measured_traffic(f"k_decode_{args.decode_workload}_hbm_traffic.txt", "k_decode")
+                      if state_dtype == "f32" else None,
                       kernel="k_decode",
                       kernel_ms=kern_avg, algorithmic_bytes_per_launch=bytes_per_step),
         inputs="drawn on the device with torch's seeded generator, same recipe",
     )
-    log(f"decode: {res['steps_per_s']:.1f} steps/s, kernel {kern_avg:.3f} ms, "
+    log(f"decode ({state_dtype} states): {res['steps_per_s']:.1f} steps/s, kernel {kern_avg:.3f} ms, "
         f"{achieved:.0f} GB/s algorithmic ({100 * achieved / PEAK_HBM_GBS:.1f}% of HBM peak)")
     return res
 
@@ -346,6 +364,8 @@ def main():
     ap.add_argument("--decode-warmup", type=int, default=8)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-bf16-states", action="store_true",
+                    help="skip the second decode measurement on a cache with bf16 closed states")
     ap.add_argument("--no-density", action="store_true",
                     help="skip the second prefill measurement under the information-density merge rule")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -371,6 +391,9 @@ def main():
     pre, sample, cfg = prefill_bench(args, torch, dla, workloads)
     copy_probe(torch, args.copy_probe_mib)
     dec = None if args.no_decode else decode_bench(args, torch, dla, workloads)
+    torch.cuda.empty_cache()
+    dec_bf = None if (args.no_decode or args.no_bf16_states) else \
+        decode_bench(args, torch, dla, workloads, state_dtype="bf16")
     cpu = None if args.no_cpu else cpu_baseline(args, sample, cfg)
     out = {
         "metric": METRIC, "value": pre["value"], "unit": "tokens/s", "n_gpus": 1,
@@ -380,6 +403,7 @@ def main():
         "cpu_baseline": cpu, "decode": dec, "schedule": pre["schedule"],
         "token_heads_per_s": pre["token_heads_per_s"],
         "prefill_density_merge_rule": pre["density_rule"],
+        "decode_bf16_states": dec_bf,
     }
     print(json.dumps(out), flush=True)
 

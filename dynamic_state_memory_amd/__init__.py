@@ -45,12 +45,12 @@ _STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace", 4: 
 
 class dla_cache(C.Structure):
     _fields_ = [("B", C.c_int32), ("H", C.c_int32), ("C", C.c_int32), ("d_k", C.c_int32),
-                ("d_v", C.c_int32), ("merge_rule", C.c_int32), ("base", C.c_void_p),
-                ("bytes", C.c_uint64)]
+                ("d_v", C.c_int32), ("merge_rule", C.c_int32), ("state_dtype", C.c_int32),
+                ("reserved", C.c_int32), ("base", C.c_void_p), ("bytes", C.c_uint64)]
 
 
 class dla_cache_layout_t(C.Structure):
-    _fields_ = [("states_offset", C.c_uint64), ("meta_offset", C.c_uint64),
+    _fields_ = [("states_offset", C.c_uint64), ("active_offset", C.c_uint64), ("meta_offset", C.c_uint64),
                 ("meta_stride", C.c_uint64), ("off_m", C.c_uint32), ("off_has_prev", C.c_uint32),
                 ("off_s_prev", C.c_uint32), ("off_t_seen", C.c_uint32), ("off_order", C.c_uint32),
                 ("off_info", C.c_uint32), ("off_count", C.c_uint32), ("off_start", C.c_uint32),
@@ -91,12 +91,12 @@ def load():
     lib.dla_abi_version.restype = i32
     lib.dla_abi_version.argtypes = []
     lib.dla_cache_bytes.restype = u64
-    lib.dla_cache_bytes.argtypes = [i32] * 5
+    lib.dla_cache_bytes.argtypes = [i32] * 5 + [C.c_int]
     lib.dla_cache_layout.restype = C.c_int
-    lib.dla_cache_layout.argtypes = [i32] * 5 + [C.POINTER(dla_cache_layout_t)]
+    lib.dla_cache_layout.argtypes = [i32] * 5 + [C.c_int, C.POINTER(dla_cache_layout_t)]
     lib.dla_cache_init.restype = C.c_int
     lib.dla_cache_init.argtypes = [C.POINTER(dla_cache), vp, u64] + [i32] * 5 + \
-        [C.POINTER(dla_cache_preload), vp]
+        [C.c_int, C.POINTER(dla_cache_preload), vp]
     lib.dla_cache_set_merge_rule.restype = C.c_int
     lib.dla_cache_set_merge_rule.argtypes = [C.POINTER(dla_cache), i32]
     lib.dla_prefill_workspace_bytes.restype = u64
@@ -125,19 +125,19 @@ def dla_abi_version() -> int:
     return load().dla_abi_version()
 
 
-def dla_cache_bytes(B, H, C_, d_k, d_v) -> int:
-    return load().dla_cache_bytes(B, H, C_, d_k, d_v)
+def dla_cache_bytes(B, H, C_, d_k, d_v, state_dtype=DLA_F32) -> int:
+    return load().dla_cache_bytes(B, H, C_, d_k, d_v, state_dtype)
 
 
-def dla_cache_layout(B, H, C_, d_k, d_v) -> dla_cache_layout_t:
+def dla_cache_layout(B, H, C_, d_k, d_v, state_dtype=DLA_F32) -> dla_cache_layout_t:
     out = dla_cache_layout_t()
-    _check(load().dla_cache_layout(B, H, C_, d_k, d_v, C.byref(out)))
+    _check(load().dla_cache_layout(B, H, C_, d_k, d_v, state_dtype, C.byref(out)))
     return out
 
 
-def dla_cache_init(cache: dla_cache, base: int, nbytes: int, B, H, C_, d_k, d_v,
+def dla_cache_init(cache: dla_cache, base: int, nbytes: int, B, H, C_, d_k, d_v, state_dtype,
                    preload: dla_cache_preload | None, stream: int) -> int:
-    return load().dla_cache_init(C.byref(cache), base, nbytes, B, H, C_, d_k, d_v,
+    return load().dla_cache_init(C.byref(cache), base, nbytes, B, H, C_, d_k, d_v, state_dtype,
                                  C.byref(preload) if preload is not None else None, stream)
 
 
@@ -221,18 +221,24 @@ class Cache:
     """A device cache for B*H streams (torch uint8 buffer + dla_cache view).
 
     ``merge_rule``: "sum" (smallest summed information, the default) or
-    "density" (lowest information density) for the capacity merges."""
+    "density" (lowest information density) for the capacity merges.
+    ``state_dtype``: "f32" (every state float32) or "bf16" (closed states
+    bfloat16, the most recent one float32)."""
 
     def __init__(self, B, H, C_, d_k, d_v, device="cuda", preload: dict | None = None,
-                 merge_rule: str = "sum"):
+                 merge_rule: str = "sum", state_dtype: str = "f32"):
         torch = _torch()
-        nbytes = dla_cache_bytes(B, H, C_, d_k, d_v)
+        if state_dtype not in ("f32", "bf16"):
+            raise DLAError(DLA_ERR_ARG, f"unknown state dtype {state_dtype!r}")
+        sdt = DLA_BF16 if state_dtype == "bf16" else DLA_F32
+        nbytes = dla_cache_bytes(B, H, C_, d_k, d_v, sdt)
         if nbytes == 0:
             raise DLAError(DLA_ERR_ARG, f"invalid cache shape {(B, H, C_, d_k, d_v)}")
         self.buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
         self.shape = (B, H, C_, d_k, d_v)
+        self.state_dtype = state_dtype
         self.view = dla_cache()
-        self.layout = dla_cache_layout(B, H, C_, d_k, d_v)
+        self.layout = dla_cache_layout(B, H, C_, d_k, d_v, sdt)
         pre = None
         self._keep = []
         if preload is not None:
@@ -244,7 +250,7 @@ class Cache:
             self._keep = [st, inf, cnt, sta]
             pre = dla_cache_preload(m0, 0, st.data_ptr(), inf.data_ptr(), cnt.data_ptr(),
                                     sta.data_ptr(), int(preload.get("t_seen", 0)))
-        _check(dla_cache_init(self.view, self.buf.data_ptr(), nbytes, B, H, C_, d_k, d_v, pre,
+        _check(dla_cache_init(self.view, self.buf.data_ptr(), nbytes, B, H, C_, d_k, d_v, sdt, pre,
                               _stream(self.buf.device)))
         if merge_rule not in MERGE_RULES:
             raise DLAError(DLA_ERR_ARG, f"unknown merge rule {merge_rule!r}")
@@ -262,8 +268,16 @@ class Cache:
         BH = B * H
         raw = self.buf.cpu().numpy()
         L = self.layout
-        states = raw[L.states_offset:L.states_offset + 4 * BH * C_ * dv * dk].view(np.float32)
-        states = states.reshape(BH, C_, dv, dk)
+        bf = self.state_dtype == "bf16"
+        if bf:
+            # closed states: bf16 bits widened to float32; the active ones: float32 region
+            u16 = raw[L.states_offset:L.states_offset + 2 * BH * C_ * dv * dk].view(np.uint16)
+            states = (u16.astype(np.uint32) << 16).view(np.float32).reshape(BH, C_, dv, dk)
+            active = raw[L.active_offset:L.active_offset + 4 * BH * dv * dk].view(np.float32)
+            active = active.reshape(BH, dv, dk)
+        else:
+            states = raw[L.states_offset:L.states_offset + 4 * BH * C_ * dv * dk].view(np.float32)
+            states = states.reshape(BH, C_, dv, dk)
         meta = raw[L.meta_offset:L.meta_offset + BH * L.meta_stride].reshape(BH, L.meta_stride)
 
         def field(off, dt, n):
@@ -281,8 +295,9 @@ class Cache:
                    k_prev=field(L.off_k_prev, np.float32, dk).copy())
         S = np.zeros((BH, C_, dv, dk), np.float32)
         for bh in range(BH):
-            for i in range(int(m[bh])):
-                S[bh, i] = states[bh, order[bh, i]]
+            mm = int(m[bh])
+            for i in range(mm):
+                S[bh, i] = active[bh] if (bf and i == mm - 1) else states[bh, order[bh, i]]
         out["S"] = S
         return out
 

@@ -98,7 +98,24 @@ Workspace carve(void *base, const Sizes &z)
     return w;
 }
 
-uint64_t states_bytes(int64_t BH, int64_t C, int64_t dk, int64_t dv) { return 4ull * BH * C * dv * dk; }
+// Offsets of a cache buffer's parts: the slots (fp32, or bf16 closed states),
+// the fp32 active-state region (bf16 storage only; empty otherwise) and the
+// per-stream metadata.
+struct CacheOffsets {
+    uint64_t states, active, meta, total;
+};
+
+CacheOffsets cache_offsets(int64_t BH, int64_t C, int64_t dk, int64_t dv, bool bf16)
+{
+    CacheOffsets o;
+    o.states = 0;
+    o.active = align_up((bf16 ? 2ull : 4ull) * BH * C * dv * dk, 256);
+    o.meta = align_up(o.active + (bf16 ? 4ull * BH * dv * dk : 0ull), 256);
+    o.total = o.meta + BH * meta_stride_bytes(dk);
+    return o;
+}
+
+bool valid_state_dtype(int d) { return d == DLA_F32 || d == DLA_BF16; }
 
 dla_status check_cache(const dla_cache *c)
 {
@@ -106,7 +123,8 @@ dla_status check_cache(const dla_cache *c)
     dla_status s = check_shape(c->B, c->H, c->C, c->d_k, c->d_v);
     if (s != DLA_OK) return s;
     if (!c->base || !aligned(c->base, 256)) return fail(DLA_ERR_ARG, "cache base is NULL or not 256-byte aligned");
-    if (c->bytes < dla_cache_bytes(c->B, c->H, c->C, c->d_k, c->d_v))
+    if (!valid_state_dtype(c->state_dtype)) return fail(DLA_ERR_ARG, "unknown state dtype %d", c->state_dtype);
+    if (c->bytes < dla_cache_bytes(c->B, c->H, c->C, c->d_k, c->d_v, static_cast<dla_dtype>(c->state_dtype)))
         return fail(DLA_ERR_ARG, "cache buffer too small (%llu bytes)", static_cast<unsigned long long>(c->bytes));
     if (c->merge_rule != DLA_MERGE_SUM && c->merge_rule != DLA_MERGE_DENSITY)
         return fail(DLA_ERR_ARG, "unknown merge rule %d", c->merge_rule);
@@ -117,6 +135,7 @@ CacheGeom geom(const dla_cache *c)
 {
     CacheGeom g;
     g.B = c->B; g.H = c->H; g.C = c->C; g.dk = c->d_k; g.dv = c->d_v;
+    g.state_bf16 = c->state_dtype == DLA_BF16;
     g.meta_stride = meta_stride_bytes(c->d_k);
     return g;
 }
@@ -176,25 +195,27 @@ extern "C" {
 
 int32_t dla_abi_version(void) { return DLA_ABI_VERSION; }
 
-uint64_t dla_cache_bytes(int32_t B, int32_t H, int32_t C, int32_t d_k, int32_t d_v)
+uint64_t dla_cache_bytes(int32_t B, int32_t H, int32_t C, int32_t d_k, int32_t d_v, dla_dtype state_dtype)
 {
     char saved[sizeof(g_err)];
     std::memcpy(saved, g_err, sizeof(g_err));
-    const bool bad = check_shape(B, H, C, d_k, d_v) != DLA_OK;
+    const bool bad = check_shape(B, H, C, d_k, d_v) != DLA_OK || !valid_state_dtype(state_dtype);
     std::memcpy(g_err, saved, sizeof(g_err));
     if (bad) return 0;
-    const int64_t BH = static_cast<int64_t>(B) * H;
-    return align_up(states_bytes(BH, C, d_k, d_v), 256) + BH * meta_stride_bytes(d_k);
+    return cache_offsets(static_cast<int64_t>(B) * H, C, d_k, d_v, state_dtype == DLA_BF16).total;
 }
 
-dla_status dla_cache_layout(int32_t B, int32_t H, int32_t C, int32_t d_k, int32_t d_v, dla_cache_layout_t *out)
+dla_status dla_cache_layout(int32_t B, int32_t H, int32_t C, int32_t d_k, int32_t d_v, dla_dtype state_dtype,
+                            dla_cache_layout_t *out)
 {
     dla_status s = check_shape(B, H, C, d_k, d_v);
     if (s != DLA_OK) return s;
+    if (!valid_state_dtype(state_dtype)) return fail(DLA_ERR_ARG, "unknown state dtype %d", static_cast<int>(state_dtype));
     if (!out) return fail(DLA_ERR_ARG, "out is NULL");
-    const int64_t BH = static_cast<int64_t>(B) * H;
-    out->states_offset = 0;
-    out->meta_offset = align_up(states_bytes(BH, C, d_k, d_v), 256);
+    const CacheOffsets co = cache_offsets(static_cast<int64_t>(B) * H, C, d_k, d_v, state_dtype == DLA_BF16);
+    out->states_offset = co.states;
+    out->active_offset = co.active;
+    out->meta_offset = co.meta;
     out->meta_stride = meta_stride_bytes(d_k);
     out->off_m = kOffM;
     out->off_has_prev = kOffHasPrev;
@@ -209,13 +230,15 @@ dla_status dla_cache_layout(int32_t B, int32_t H, int32_t C, int32_t d_k, int32_
 }
 
 dla_status dla_cache_init(dla_cache *cache, void *base, uint64_t bytes, int32_t B, int32_t H, int32_t C,
-                          int32_t d_k, int32_t d_v, const dla_cache_preload *preload, void *stream)
+                          int32_t d_k, int32_t d_v, dla_dtype state_dtype, const dla_cache_preload *preload,
+                          void *stream)
 {
     if (!cache) return fail(DLA_ERR_ARG, "cache is NULL");
     dla_status s = check_shape(B, H, C, d_k, d_v);
     if (s != DLA_OK) return s;
+    if (!valid_state_dtype(state_dtype)) return fail(DLA_ERR_ARG, "unknown state dtype %d", static_cast<int>(state_dtype));
     if (!base || !aligned(base, 256)) return fail(DLA_ERR_ARG, "base is NULL or not 256-byte aligned");
-    if (bytes < dla_cache_bytes(B, H, C, d_k, d_v))
+    if (bytes < dla_cache_bytes(B, H, C, d_k, d_v, state_dtype))
         return fail(DLA_ERR_ARG, "buffer of %llu bytes is smaller than dla_cache_bytes",
                     static_cast<unsigned long long>(bytes));
     PreloadArgs pre = {0, nullptr, nullptr, nullptr, nullptr, 0};
@@ -238,14 +261,17 @@ dla_status dla_cache_init(dla_cache *cache, void *base, uint64_t bytes, int32_t 
     }
     cache->B = B; cache->H = H; cache->C = C; cache->d_k = d_k; cache->d_v = d_v;
     cache->merge_rule = DLA_MERGE_SUM;
+    cache->state_dtype = state_dtype;
+    cache->reserved = 0;
     cache->base = base;
     cache->bytes = bytes;
     const CacheGeom g = geom(cache);
-    const int64_t BH = static_cast<int64_t>(B) * H;
+    const CacheOffsets co = cache_offsets(static_cast<int64_t>(B) * H, C, d_k, d_v, g.state_bf16);
     uint8_t *b8 = static_cast<uint8_t *>(base);
-    float *states = reinterpret_cast<float *>(b8);
-    uint8_t *meta = b8 + align_up(states_bytes(BH, C, d_k, d_v), 256);
-    return hip_status(launch_cache_init(states, meta, g, pre, static_cast<hipStream_t>(stream)),
+    float *states = reinterpret_cast<float *>(b8 + co.states);
+    float *active = g.state_bf16 ? reinterpret_cast<float *>(b8 + co.active) : nullptr;
+    uint8_t *meta = b8 + co.meta;
+    return hip_status(launch_cache_init(states, active, meta, g, pre, static_cast<hipStream_t>(stream)),
                       "cache init launch");
 }
 
@@ -302,9 +328,14 @@ dla_status dla_prefill(const void *q, const void *k, const void *v, const void *
     if (plan.lds > 160 * 1024)
         return fail(DLA_ERR_UNSUPPORTED, "shape needs more LDS than a compute unit has");
     a.g = geom(cache);
+    if (a.g.state_bf16 && !a.register_resident)
+        return fail(DLA_ERR_UNSUPPORTED, "bfloat16 state storage needs bfloat16 io and C <= 32 "
+                                         "(the register-resident prefill)");
+    const CacheOffsets co = cache_offsets(BH, cache->C, cache->d_k, cache->d_v, a.g.state_bf16);
     uint8_t *b8 = static_cast<uint8_t *>(cache->base);
-    a.states = reinterpret_cast<float *>(b8);
-    a.meta = b8 + align_up(states_bytes(BH, cache->C, cache->d_k, cache->d_v), 256);
+    a.states = reinterpret_cast<float *>(b8 + co.states);
+    a.active = a.g.state_bf16 ? reinterpret_cast<float *>(b8 + co.active) : nullptr;
+    a.meta = b8 + co.meta;
     a.ws = carve(workspace, z);
     a.ev_before = g_ev_before;
     a.ev_after = g_ev_after;
@@ -356,9 +387,11 @@ dla_status dla_decode_step(const void *q, const void *k, const void *v, const vo
     a.merge_rule = cache->merge_rule;
     a.g = geom(cache);
     const int64_t BH = static_cast<int64_t>(cache->B) * cache->H;
+    const CacheOffsets co = cache_offsets(BH, cache->C, cache->d_k, cache->d_v, a.g.state_bf16);
     uint8_t *b8 = static_cast<uint8_t *>(cache->base);
-    a.states = reinterpret_cast<float *>(b8);
-    a.meta = b8 + align_up(states_bytes(BH, cache->C, cache->d_k, cache->d_v), 256);
+    a.states = reinterpret_cast<float *>(b8 + co.states);
+    a.active = a.g.state_bf16 ? reinterpret_cast<float *>(b8 + co.active) : nullptr;
+    a.meta = b8 + co.meta;
     a.sched.s = sched ? sched->s : nullptr;
     a.sched.boundary = sched ? sched->boundary : nullptr;
     a.sched.m_t = sched ? sched->m_t : nullptr;

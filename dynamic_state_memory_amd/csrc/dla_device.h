@@ -193,6 +193,22 @@ __device__ __forceinline__ void read_frag_from(Frag<float> &f, const float *p, i
 
 __device__ __forceinline__ int64_t min_i64(int64_t a, int64_t b) { return b < a ? b : a; }
 
+// Four floats rounded to bf16 (nearest even), packed little-end first, and back.
+__device__ __forceinline__ uint2 pack_bf16x4(float4 v)
+{
+    const __bf16 a = static_cast<__bf16>(v.x), b = static_cast<__bf16>(v.y);
+    const __bf16 c = static_cast<__bf16>(v.z), d = static_cast<__bf16>(v.w);
+    return make_uint2(static_cast<uint32_t>(__builtin_bit_cast(uint16_t, a)) |
+                          (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b)) << 16),
+                      static_cast<uint32_t>(__builtin_bit_cast(uint16_t, c)) |
+                          (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, d)) << 16));
+}
+__device__ __forceinline__ float4 unpack_bf16x4(uint2 u)
+{
+    return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                       __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+}
+
 // Lane holding the smallest of the fractions num / den (num >= 0, den >= 1)
 // over the lanes with ok set, the lowest such lane on ties; the same in every
 // lane (64 if no lane is ok).  a / b < c / d is decided as a d < c b in

@@ -39,6 +39,7 @@ inline uint64_t meta_stride_bytes(int dk) { return align_up(kOffKprev + 4ull * d
 
 struct CacheGeom {
     int B, H, C, dk, dv;
+    int state_bf16;     // closed states bf16 in their slots, the active one fp32 in its own region
     size_t meta_stride;
 };
 
@@ -91,7 +92,8 @@ struct PrefillArgs {
     int merge_rule;                   // DLA_MERGE_SUM or DLA_MERGE_DENSITY
     int dvt;
     CacheGeom g;
-    float *states;
+    float *states;                    // slots (bf16 data when g.state_bf16)
+    float *active;                    // [BH][dv][dk] fp32 active states (g.state_bf16), else NULL
     uint8_t *meta;
     Workspace ws;
     dla_schedule_out sched;
@@ -113,13 +115,14 @@ struct DecodeArgs {
     int io_bf16;
     int merge_rule;                   // DLA_MERGE_SUM or DLA_MERGE_DENSITY
     CacheGeom g;
-    float *states;
+    float *states;                    // slots (bf16 data when g.state_bf16)
+    float *active;                    // [BH][dv][dk] fp32 active states (g.state_bf16), else NULL
     uint8_t *meta;
     DecodeSched sched;
 };
 
-hipError_t launch_cache_init(float *states, uint8_t *meta, const CacheGeom &g, const PreloadArgs &pre,
-                             hipStream_t stream);
+hipError_t launch_cache_init(float *states, float *active, uint8_t *meta, const CacheGeom &g,
+                             const PreloadArgs &pre, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 size_t prefill_smem_bytes(int io_bf16, int dk, int dvt);

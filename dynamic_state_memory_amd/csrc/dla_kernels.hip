@@ -26,7 +26,7 @@ namespace dla {
 // ------------------------------------------------------------ cache init
 
 // One block per stream: metadata reset, optional preload of the first m0 states.
-__global__ __launch_bounds__(256) void k_cache_init(float *__restrict__ states,
+__global__ __launch_bounds__(256) void k_cache_init(float *__restrict__ states, float *__restrict__ active,
                                                      uint8_t *__restrict__ meta_base,
                                                      CacheGeom g, PreloadArgs pre)
 {
@@ -56,12 +56,21 @@ __global__ __launch_bounds__(256) void k_cache_init(float *__restrict__ states,
         start[tid] = live ? pre.start[static_cast<size_t>(bh) * m0 + tid] : 0;
     }
     for (int i = tid; i < g.dk; i += blockDim.x) kprev[i] = 0.0f;
-    if (m0 > 0) {
+    if (m0 > 0 && !g.state_bf16) {
         const size_t n4 = static_cast<size_t>(m0) * g.dv * g.dk / 4;
         const float4 *src = reinterpret_cast<const float4 *>(pre.states) + bh * n4;
         float4 *dst = reinterpret_cast<float4 *>(states) +
                       static_cast<size_t>(bh) * g.C * g.dv * g.dk / 4;
         for (size_t i = tid; i < n4; i += blockDim.x) dst[i] = src[i];
+    } else if (m0 > 0) {
+        // closed states (all but the most recent) rounded to bf16 into slots
+        // 0 .. m0 - 2; the most recent one stays fp32 in the active region
+        const size_t ss4 = static_cast<size_t>(g.dv) * g.dk / 4;     // one state, in float4
+        const float4 *src = reinterpret_cast<const float4 *>(pre.states) + bh * m0 * ss4;
+        uint2 *dst = reinterpret_cast<uint2 *>(states) + static_cast<size_t>(bh) * g.C * ss4;
+        for (size_t i = tid; i < (m0 - 1) * ss4; i += blockDim.x) dst[i] = pack_bf16x4(src[i]);
+        float4 *act = reinterpret_cast<float4 *>(active) + static_cast<size_t>(bh) * ss4;
+        for (size_t i = tid; i < ss4; i += blockDim.x) act[i] = src[(m0 - 1) * ss4 + i];
     }
 }
 
@@ -759,11 +768,12 @@ __global__ __launch_bounds__(256, 1) void k_prefill(
 // and applying a capacity merge S_a += S_b while the data passes through.
 // The states are read and written with nontemporal hints: a step touches
 // each of them once, so they should not displace other data in the caches.
-template <typename TIO, int D>
+template <typename TIO, int D, bool BF>
 __global__ __launch_bounds__(256) void k_decode(const TIO *__restrict__ Qg, const TIO *__restrict__ Kg,
                                                 const TIO *__restrict__ Vg, const TIO *__restrict__ Lg,
                                                 TIO *__restrict__ Og, float tau, int C,
-                                                float *__restrict__ states, uint8_t *__restrict__ meta_base,
+                                                float *__restrict__ states, float *__restrict__ active,
+                                                uint8_t *__restrict__ meta_base,
                                                 size_t meta_stride, DecodeSched sched, int merge_rule)
 {
     constexpr int G = D / 4;          // threads per state row (float4 each)
@@ -902,48 +912,129 @@ __global__ __launch_bounds__(256) void k_decode(const TIO *__restrict__ Qg, cons
     float acc[P];
 #pragma unroll
     for (int j = 0; j < P; ++j) acc[j] = 0.0f;
-    float *sb = states + static_cast<size_t>(bh) * C * D * D;
-    for (int i = 0; i < m; ++i) {
-        const int p = order_s[i];
-        const float w = wlog[i];
-        float4 *sp = reinterpret_cast<float4 *>(sb + static_cast<size_t>(p) * D * D);
-        float4 x[P];
-#pragma unroll
-        for (int j = 0; j < P; ++j) {
-            const floatx4 t = __builtin_nontemporal_load(reinterpret_cast<const floatx4 *>(sp) + ((row0 + R * j) * D + col) / 4);
-            x[j] = make_float4(t[0], t[1], t[2], t[3]);
+    if constexpr (!BF) {
+        float *sb = states + static_cast<size_t>(bh) * C * D * D;
+        for (int i = 0; i < m; ++i) {
+            const int p = order_s[i];
+            const float w = wlog[i];
+            float4 *sp = reinterpret_cast<float4 *>(sb + static_cast<size_t>(p) * D * D);
+            float4 x[P];
+    #pragma unroll
+            for (int j = 0; j < P; ++j) {
+                const floatx4 t = __builtin_nontemporal_load(reinterpret_cast<const floatx4 *>(sp) + ((row0 + R * j) * D + col) / 4);
+                x[j] = make_float4(t[0], t[1], t[2], t[3]);
+            }
+    #pragma unroll
+            for (int j = 0; j < P; ++j)
+                acc[j] += w * (x[j].x * q4.x + x[j].y * q4.y + x[j].z * q4.z + x[j].w * q4.w);
+            if (p == add_slot) {
+    #pragma unroll
+                for (int j = 0; j < P; ++j) {
+                    const float vr = vs[row0 + R * j];
+                    float4 y = x[j];
+                    y.x += vr * k4.x; y.y += vr * k4.y; y.z += vr * k4.z; y.w += vr * k4.w;
+                    __builtin_nontemporal_store(floatx4{y.x, y.y, y.z, y.w},
+                                                reinterpret_cast<floatx4 *>(sp) + ((row0 + R * j) * D + col) / 4);
+                }
+            }
+            if (mode == 2 && i == merge_i + 1) {
+                float4 *dp = reinterpret_cast<float4 *>(sb + static_cast<size_t>(order_s[merge_i]) * D * D);
+    #pragma unroll
+                for (int j = 0; j < P; ++j) {
+                    const int idx = ((row0 + R * j) * D + col) / 4;
+                    float4 a = dp[idx];
+                    a.x += x[j].x; a.y += x[j].y; a.z += x[j].z; a.w += x[j].w;
+                    __builtin_nontemporal_store(floatx4{a.x, a.y, a.z, a.w}, reinterpret_cast<floatx4 *>(dp) + idx);
+                }
+            }
         }
-#pragma unroll
-        for (int j = 0; j < P; ++j)
-            acc[j] += w * (x[j].x * q4.x + x[j].y * q4.y + x[j].z * q4.z + x[j].w * q4.w);
-        if (p == add_slot) {
-#pragma unroll
+        if (set_slot >= 0) {
+            float4 *sp = reinterpret_cast<float4 *>(sb + static_cast<size_t>(set_slot) * D * D);
+    #pragma unroll
             for (int j = 0; j < P; ++j) {
                 const float vr = vs[row0 + R * j];
-                float4 y = x[j];
-                y.x += vr * k4.x; y.y += vr * k4.y; y.z += vr * k4.z; y.w += vr * k4.w;
-                __builtin_nontemporal_store(floatx4{y.x, y.y, y.z, y.w},
+                __builtin_nontemporal_store(floatx4{vr * k4.x, vr * k4.y, vr * k4.z, vr * k4.w},
                                             reinterpret_cast<floatx4 *>(sp) + ((row0 + R * j) * D + col) / 4);
             }
         }
-        if (mode == 2 && i == merge_i + 1) {
-            float4 *dp = reinterpret_cast<float4 *>(sb + static_cast<size_t>(order_s[merge_i]) * D * D);
+    } else {
+        // closed states bf16 in their slots, the active one (chronological
+        // index m - 1) fp32 in the stream's active region; each state is read
+        // once, and every change is applied while it passes
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        const int act_i = m - 1;
+        floatx4 *ab = reinterpret_cast<floatx4 *>(active + static_cast<size_t>(bh) * D * D);
+        u32x2 *sb = reinterpret_cast<u32x2 *>(states) + static_cast<size_t>(bh) * C * D * D / 4;
+        for (int i = 0; i < m; ++i) {
+            const int p = order_s[i];
+            const float w = wlog[i];
+            float4 x[P];
+            if (i == act_i) {
 #pragma unroll
-            for (int j = 0; j < P; ++j) {
-                const int idx = ((row0 + R * j) * D + col) / 4;
-                float4 a = dp[idx];
-                a.x += x[j].x; a.y += x[j].y; a.z += x[j].z; a.w += x[j].w;
-                __builtin_nontemporal_store(floatx4{a.x, a.y, a.z, a.w}, reinterpret_cast<floatx4 *>(dp) + idx);
+                for (int j = 0; j < P; ++j) {
+                    const floatx4 t = __builtin_nontemporal_load(ab + ((row0 + R * j) * D + col) / 4);
+                    x[j] = make_float4(t[0], t[1], t[2], t[3]);
+                }
+            } else {
+                const u32x2 *sp = sb + static_cast<size_t>(p) * D * D / 4;
+#pragma unroll
+                for (int j = 0; j < P; ++j) {
+                    const u32x2 t = __builtin_nontemporal_load(sp + ((row0 + R * j) * D + col) / 4);
+                    x[j] = unpack_bf16x4(make_uint2(t[0], t[1]));
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < P; ++j)
+                acc[j] += w * (x[j].x * q4.x + x[j].y * q4.y + x[j].z * q4.z + x[j].w * q4.w);
+            // where a bf16 result goes: the active state closing into its own
+            // slot, or the state merging away added into the slot of merge_i
+            int dst_slot = -1;
+            bool add_into = false;
+            if (i == act_i) {
+                if (mode == 0 || mode == 3) {
+                    // the token joins the active state
+#pragma unroll
+                    for (int j = 0; j < P; ++j) {
+                        const float vr = vs[row0 + R * j];
+                        const float4 y = x[j];
+                        __builtin_nontemporal_store(floatx4{y.x + vr * k4.x, y.y + vr * k4.y, y.z + vr * k4.z,
+                                                            y.w + vr * k4.w},
+                                                    ab + ((row0 + R * j) * D + col) / 4);
+                    }
+                } else if (mode == 2 && merge_i + 1 == act_i) {
+                    dst_slot = order_s[merge_i];       // merged into the closed state before it
+                    add_into = true;
+                } else {
+                    dst_slot = p;                      // closes: a new state becomes the active one
+                }
+            } else if (mode == 2 && i == merge_i + 1) {
+                dst_slot = order_s[merge_i];
+                add_into = true;
+            }
+            if (dst_slot >= 0) {
+                u32x2 *dp = sb + static_cast<size_t>(dst_slot) * D * D / 4;
+#pragma unroll
+                for (int j = 0; j < P; ++j) {
+                    const int idx = ((row0 + R * j) * D + col) / 4;
+                    float4 y = x[j];
+                    if (add_into) {
+                        const u32x2 t = dp[idx];
+                        const float4 a4 = unpack_bf16x4(make_uint2(t[0], t[1]));
+                        y.x += a4.x; y.y += a4.y; y.z += a4.z; y.w += a4.w;
+                    }
+                    const uint2 u = pack_bf16x4(y);
+                    __builtin_nontemporal_store(u32x2{u.x, u.y}, dp + idx);
+                }
             }
         }
-    }
-    if (set_slot >= 0) {
-        float4 *sp = reinterpret_cast<float4 *>(sb + static_cast<size_t>(set_slot) * D * D);
+        if (mode == 1 || mode == 2) {
+            // the new state v k^T is the active one now
 #pragma unroll
-        for (int j = 0; j < P; ++j) {
-            const float vr = vs[row0 + R * j];
-            __builtin_nontemporal_store(floatx4{vr * k4.x, vr * k4.y, vr * k4.z, vr * k4.w},
-                                        reinterpret_cast<floatx4 *>(sp) + ((row0 + R * j) * D + col) / 4);
+            for (int j = 0; j < P; ++j) {
+                const float vr = vs[row0 + R * j];
+                __builtin_nontemporal_store(floatx4{vr * k4.x, vr * k4.y, vr * k4.z, vr * k4.w},
+                                            ab + ((row0 + R * j) * D + col) / 4);
+            }
         }
     }
     (void)mode;
@@ -960,10 +1051,10 @@ __global__ __launch_bounds__(256) void k_decode(const TIO *__restrict__ Qg, cons
 
 // ------------------------------------------------------------ launchers
 
-hipError_t launch_cache_init(float *states, uint8_t *meta, const CacheGeom &g, const PreloadArgs &pre,
-                             hipStream_t stream)
+hipError_t launch_cache_init(float *states, float *active, uint8_t *meta, const CacheGeom &g,
+                             const PreloadArgs &pre, hipStream_t stream)
 {
-    hipLaunchKernelGGL(k_cache_init, dim3(g.B * g.H), dim3(256), 0, stream, states, meta, g, pre);
+    hipLaunchKernelGGL(k_cache_init, dim3(g.B * g.H), dim3(256), 0, stream, states, active, meta, g, pre);
     return hipGetLastError();
 }
 
@@ -1057,12 +1148,17 @@ static hipError_t decode_typed(const DecodeArgs &a, hipStream_t stream)
     const TIO *q = static_cast<const TIO *>(a.q), *k = static_cast<const TIO *>(a.k);
     const TIO *v = static_cast<const TIO *>(a.v), *l = static_cast<const TIO *>(a.lam);
     TIO *o = static_cast<TIO *>(a.o);
-    if (a.g.dk == 128)
-        hipLaunchKernelGGL((k_decode<TIO, 128>), dim3(BH), dim3(256), 0, stream, q, k, v, l, o, a.tau,
-                           a.g.C, a.states, a.meta, a.g.meta_stride, a.sched, a.merge_rule);
-    else
-        hipLaunchKernelGGL((k_decode<TIO, 64>), dim3(BH), dim3(256), 0, stream, q, k, v, l, o, a.tau,
-                           a.g.C, a.states, a.meta, a.g.meta_stride, a.sched, a.merge_rule);
+#define DLA_DECODE(D_, BF_)                                                                           \
+    hipLaunchKernelGGL((k_decode<TIO, D_, BF_>), dim3(BH), dim3(256), 0, stream, q, k, v, l, o, a.tau, a.g.C, \
+                       a.states, a.active, a.meta, a.g.meta_stride, a.sched, a.merge_rule)
+    if (a.g.dk == 128) {
+        if (a.g.state_bf16) DLA_DECODE(128, true);
+        else DLA_DECODE(128, false);
+    } else {
+        if (a.g.state_bf16) DLA_DECODE(64, true);
+        else DLA_DECODE(64, false);
+    }
+#undef DLA_DECODE
     return hipGetLastError();
 }
 

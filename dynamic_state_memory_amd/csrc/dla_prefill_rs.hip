@@ -425,6 +425,24 @@ struct RsCarry {
     uint32_t closed;                             // physical slots of the closed states (uniform)
 };
 
+// Four consecutive values of a state in the cache at element offset e of a
+// stream's slice: fp32, or bf16 for the closed states of a bf16 cache
+// (rounded to nearest even when stored).
+template <bool SBF>
+__device__ __forceinline__ float4 cache_load4(const void *base, size_t e)
+{
+    if constexpr (SBF) return unpack_bf16x4(*reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(base) + e));
+    else return *reinterpret_cast<const float4 *>(static_cast<const float *>(base) + e);
+}
+template <bool SBF>
+__device__ __forceinline__ void cache_store4(void *base, size_t e, float4 v)
+{
+    if constexpr (SBF)
+        *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(base) + e) = pack_bf16x4(v);
+    else
+        *reinterpret_cast<float4 *>(static_cast<float *>(base) + e) = v;
+}
+
 // Per-lane byte offsets, recomputed at each use from an opaque copy of the
 // thread index (kept live anyway) rather than held, or spilled, across chunks:
 // thread tid's V piece (token tid % 64, columns 8 (tid / 64) ..) within a
@@ -455,7 +473,8 @@ struct RsParams {
     int bh, dv0, tid, lane, wave, lr, lg, NCH, vr, vc;
     bool v_mover;
     size_t tok0, slot_stride;
-    float *st_base;
+    void *st_base;              // the stream's slice of the slots (fp32, or bf16 closed states)
+    float *act_base;            // its slice of the fp32 active-state region (bf16 cache), else NULL
 };
 
 // One chunk of the sweep: its part A operands are in X, its part B operands
@@ -466,7 +485,7 @@ struct RsParams {
 // (closed states in registers), holds d_k rows 32 (w - AW) .. + 31 of the
 // active state (d_k = 128: every wave), and reduces and stores the outputs of
 // tokens 16 w .. 16 w + 15.
-template <int DK, int DVT, int SPW>
+template <int DK, int DVT, int SPW, bool SBF>
 __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB<DK> &Y,
                                          RsSmem<DK, DVT, kRsWaves * SPW> &S, const RsParams &A,
                                          RsCarry<DK, DVT, SPW> &c)
@@ -482,7 +501,6 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
     const int bh = A.bh, dv0 = A.dv0, tid = A.tid, lane = A.lane, wave = A.wave, lr = A.lr, lg = A.lg;
     const int NCH = A.NCH, vr = A.vr, vc = A.vc;
     const size_t tok0 = A.tok0, slot_stride = A.slot_stride;
-    float *st_base = A.st_base;
     auto &stk = c.stk;
     auto &am = c.am;
     auto &af = c.af;
@@ -802,12 +820,11 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
 #pragma unroll
                     for (int nt = 0; nt < NTV; ++nt) acc[kt][nt] += actbuf[(kt * NTV + nt) * 64 + lane];
             } else {
-                const float *src = st_base + q * slot_stride;
 #pragma unroll
                 for (int kt = 0; kt < DK / 16; ++kt)
 #pragma unroll
                     for (int nt = 0; nt < NTV; ++nt) {
-                        const float4 v = *reinterpret_cast<const float4 *>(src + (16 * nt + lr) * DK + 16 * kt + 4 * lg);
+                        const float4 v = cache_load4<SBF>(A.st_base, q * slot_stride + (16 * nt + lr) * DK + 16 * kt + 4 * lg);
                         acc[kt][nt] += floatx4{v.x, v.y, v.z, v.w};
                     }
             }
@@ -841,7 +858,6 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
         // state merged away in this chunk, which another wave may still be
         // reading: new states are written after the next barrier), normalised
         // fp16 copy into the registers
-        float *dst = st_base + p * slot_stride;
         float mx = 0.0f;
 #pragma unroll
         for (int kt = 0; kt < DK / 16; ++kt)
@@ -849,8 +865,8 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
             for (int nt = 0; nt < NTV; ++nt) {
                 const floatx4 v = acc[kt][nt];
                 if (jbase)
-                    *reinterpret_cast<float4 *>(dst + (16 * nt + lr) * DK + 16 * kt + 4 * lg) =
-                        make_float4(v[0], v[1], v[2], v[3]);
+                    cache_store4<SBF>(A.st_base, p * slot_stride + (16 * nt + lr) * DK + 16 * kt + 4 * lg,
+                                 make_float4(v[0], v[1], v[2], v[3]));
                 mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
             }
         const int e = f16_exponent(wave_max(mx));
@@ -895,13 +911,12 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
                 for (int nt = 0; nt < NTV; ++nt) mma32(acc[kt][nt], a, b[nt]);
             }
         }
-        float *dst = st_base + p * slot_stride;
 #pragma unroll
         for (int kt = 0; kt < DK / 16; ++kt)
 #pragma unroll
             for (int nt = 0; nt < NTV; ++nt)
-                *reinterpret_cast<float4 *>(dst + (16 * nt + lr) * DK + 16 * kt + 4 * lg) =
-                    make_float4(acc[kt][nt][0], acc[kt][nt][1], acc[kt][nt][2], acc[kt][nt][3]);
+                cache_store4<SBF>(A.st_base, p * slot_stride + (16 * nt + lr) * DK + 16 * kt + 4 * lg,
+                             make_float4(acc[kt][nt][0], acc[kt][nt][1], acc[kt][nt][2], acc[kt][nt][3]));
     }
     // the new active state into the accumulators
     if (act_wave) {
@@ -956,10 +971,10 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
     c.ewin += nev;
 }
 
-template <int DK, int DVT, int SPW>
+template <int DK, int DVT, int SPW, bool SBF>
 __global__ __launch_bounds__(kRsThreads, 2) void k_prefill_rs(
     const __bf16 *__restrict__ V, __bf16 *__restrict__ O, int T, int C, int DV, int nblk_dv,
-    float *__restrict__ states, const int2 *__restrict__ events,
+    float *__restrict__ states, float *__restrict__ active, const int2 *__restrict__ events,
     const int32_t *__restrict__ chunk_ev, const uint8_t *__restrict__ rec,
     uint8_t *__restrict__ meta_base, size_t meta_stride)
 {
@@ -993,7 +1008,13 @@ __global__ __launch_bounds__(kRsThreads, 2) void k_prefill_rs(
     A.v_mover = A.tid < kChunk * DVT / 8;
     A.tok0 = static_cast<size_t>(A.bh) * T;
     A.slot_stride = static_cast<size_t>(DV) * DK;
-    A.st_base = states + static_cast<size_t>(A.bh) * C * DV * DK + static_cast<size_t>(A.dv0) * DK;
+    {
+        const size_t off = static_cast<size_t>(A.bh) * C * DV * DK + static_cast<size_t>(A.dv0) * DK;
+        A.st_base = SBF ? static_cast<void *>(reinterpret_cast<uint16_t *>(states) + off)
+                        : static_cast<void *>(states + off);
+        A.act_base = SBF ? active + static_cast<size_t>(A.bh) * DV * DK + static_cast<size_t>(A.dv0) * DK
+                         : nullptr;
+    }
     A.evtot = chunk_ev[static_cast<size_t>(A.bh) * (A.NCH + 1) + A.NCH];
     const int tid = A.tid, wave = A.wave, lr = A.lr, lg = A.lg, NCH = A.NCH;
 
@@ -1027,12 +1048,13 @@ __global__ __launch_bounds__(kRsThreads, 2) void k_prefill_rs(
     c.evnext = make_int2(0x7fffffff, -1);
     if (wave == 0 && A.lane < A.evtot) c.evnext = events[A.tok0 + A.lane];
 
-    for (int ch = 0; ch < NCH; ++ch) rs_chunk<DK, DVT, SPW>(ch, stA, stB, S, A, c);
+    for (int ch = 0; ch < NCH; ++ch) rs_chunk<DK, DVT, SPW, SBF>(ch, stA, stB, S, A, c);
 
     // the active state's accumulators are the last state of the final cache
     const int kb = wave - (kRsWaves - KS);
     if (c.act >= 0 && kb >= 0) {
-        float *dst = A.st_base + c.act * A.slot_stride;
+        // (fp32 in its slot, or in the active-state region of a bf16 cache)
+        float *dst = SBF ? A.act_base : static_cast<float *>(A.st_base) + c.act * A.slot_stride;
 #pragma unroll
         for (int nt = 0; nt < NTV; ++nt)
 #pragma unroll
@@ -1063,9 +1085,16 @@ static hipError_t launch_rs(const PrefillArgs &a, hipStream_t stream)
         hipError_t e = hipEventRecord(a.ev_before, stream);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((k_prefill_rs<DK, DVT, SPW>), dim3(BH * nblk_dv), dim3(kRsThreads), 0, stream,
-                       static_cast<const __bf16 *>(a.v), static_cast<__bf16 *>(a.o), a.T, a.g.C, a.g.dv,
-                       nblk_dv, a.states, a.ws.events, a.ws.chunk_ev, static_cast<const uint8_t *>(a.ws.rec), a.meta, a.g.meta_stride);
+    if (a.g.state_bf16)
+        hipLaunchKernelGGL((k_prefill_rs<DK, DVT, SPW, true>), dim3(BH * nblk_dv), dim3(kRsThreads), 0, stream,
+                           static_cast<const __bf16 *>(a.v), static_cast<__bf16 *>(a.o), a.T, a.g.C, a.g.dv,
+                           nblk_dv, a.states, a.active, a.ws.events, a.ws.chunk_ev,
+                           static_cast<const uint8_t *>(a.ws.rec), a.meta, a.g.meta_stride);
+    else
+        hipLaunchKernelGGL((k_prefill_rs<DK, DVT, SPW, false>), dim3(BH * nblk_dv), dim3(kRsThreads), 0, stream,
+                           static_cast<const __bf16 *>(a.v), static_cast<__bf16 *>(a.o), a.T, a.g.C, a.g.dv,
+                           nblk_dv, a.states, a.active, a.ws.events, a.ws.chunk_ev,
+                           static_cast<const uint8_t *>(a.ws.rec), a.meta, a.g.meta_stride);
     hipError_t e = hipGetLastError();
     if (e == hipSuccess && a.ev_after) e = hipEventRecord(a.ev_after, stream);
     return e;

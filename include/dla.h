@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define DLA_ABI_VERSION 2
+#define DLA_ABI_VERSION 3
 #define DLA_MAX_C 64        /* largest supported cache capacity */
 #define DLA_CHUNK 64        /* tokens per prefill chunk */
 
@@ -81,11 +81,20 @@ typedef enum dla_merge_rule {
 
 /*
  * Cache: caller-owned device memory holding, for every stream (b, h), up to
- * C fp32 states in physical slots plus the stream's metadata.  The struct is
- * a plain view; dla_cache_init fills it.
+ * C states in physical slots plus the stream's metadata.  The struct is a
+ * plain view; dla_cache_init fills it.
+ *
+ * State storage (the cache's state dtype):
+ *   DLA_F32   every state is float32 in its physical slot;
+ *   DLA_BF16  the closed states (all but the most recent) are bfloat16 in
+ *             their physical slots, and the most recent ("active") state,
+ *             the one tokens are added to, is float32 in a separate region
+ *             of one state per stream (its slot's bfloat16 copy is written
+ *             when it closes).  About half the bytes a decode step streams.
  *
  * Buffer layout (offsets from dla_cache_layout):
- *   states  at states_offset: [B*H][C][d_v][d_k] float32, physical slots;
+ *   states  at states_offset: [B*H][C][d_v][d_k] in the state dtype, physical slots;
+ *   active  at active_offset (DLA_BF16 only): [B*H][d_v][d_k] float32;
  *   meta    at meta_offset + bh * meta_stride, per stream:
  *     int32  m            live states (0..C)
  *     int32  has_prev     1 once the stream has seen a key
@@ -100,13 +109,16 @@ typedef enum dla_merge_rule {
  */
 typedef struct dla_cache {
     int32_t B, H, C, d_k, d_v;
-    int32_t merge_rule;  /* a dla_merge_rule; dla_cache_init sets DLA_MERGE_SUM */
-    void *base;          /* device pointer */
+    int32_t merge_rule;   /* a dla_merge_rule; dla_cache_init sets DLA_MERGE_SUM */
+    int32_t state_dtype;  /* DLA_F32 or DLA_BF16 (set by dla_cache_init) */
+    int32_t reserved;
+    void *base;           /* device pointer */
     uint64_t bytes;
 } dla_cache;
 
 typedef struct dla_cache_layout_t {
     uint64_t states_offset;
+    uint64_t active_offset;   /* DLA_BF16 state dtype; equal to meta_offset for DLA_F32 (no region) */
     uint64_t meta_offset;
     uint64_t meta_stride;
     uint32_t off_m, off_has_prev, off_s_prev, off_t_seen;
@@ -150,21 +162,24 @@ typedef struct dla_schedule_out {
 /* Version of this ABI (DLA_ABI_VERSION). */
 int32_t dla_abi_version(void);
 
-/* Bytes of a cache for the given shape; 0 if the shape is invalid. */
-uint64_t dla_cache_bytes(int32_t B, int32_t H, int32_t C, int32_t d_k, int32_t d_v);
+/* Bytes of a cache for the given shape and state dtype; 0 if either is invalid. */
+uint64_t dla_cache_bytes(int32_t B, int32_t H, int32_t C, int32_t d_k, int32_t d_v,
+                         dla_dtype state_dtype);
 
-/* Offsets of the cache buffer's parts (see dla_cache).  DLA_ERR_ARG on a bad shape. */
+/* Offsets of the cache buffer's parts (see dla_cache).  DLA_ERR_ARG on a bad shape or dtype. */
 dla_status dla_cache_layout(int32_t B, int32_t H, int32_t C, int32_t d_k, int32_t d_v,
-                            dla_cache_layout_t *out);
+                            dla_dtype state_dtype, dla_cache_layout_t *out);
 
 /*
- * Make `base` (device, >= dla_cache_bytes bytes, 256-byte aligned) an empty
- * cache, or one holding `preload` (may be NULL), and fill *cache.
- * Supported: C in [1, 64], d_k in {64, 128}, d_v a positive multiple of 16.
+ * Make `base` (device, >= dla_cache_bytes bytes for the same state dtype,
+ * 256-byte aligned) an empty cache, or one holding `preload` (may be NULL),
+ * and fill *cache.  Supported: C in [1, 64], d_k in {64, 128}, d_v a positive
+ * multiple of 16, state_dtype DLA_F32 or DLA_BF16 (preloaded closed states
+ * are rounded to bfloat16, to nearest even; the most recent stays float32).
  * A preloaded stream has no previous key, so its next token has s = 1.
  */
 dla_status dla_cache_init(dla_cache *cache, void *base, uint64_t bytes, int32_t B,
-                          int32_t H, int32_t C, int32_t d_k, int32_t d_v,
+                          int32_t H, int32_t C, int32_t d_k, int32_t d_v, dla_dtype state_dtype,
                           const dla_cache_preload *preload, void *stream);
 
 /*
@@ -194,7 +209,9 @@ uint64_t dla_prefill_workspace_bytes(int32_t B, int32_t H, int32_t T, int32_t C,
  *   workspace  device, >= dla_prefill_workspace_bytes, 256-byte aligned;
  *              scratch owned by the call until the stream work completes
  *   sched   optional schedule export, may be NULL
- * T must be in [1, 2^24].
+ * T must be in [1, 2^24].  A cache with bfloat16 state storage needs the
+ * register-resident sweep (bfloat16 io, C <= 32); other prefills of such a
+ * cache return DLA_ERR_UNSUPPORTED.
  */
 dla_status dla_prefill(const void *q, const void *k, const void *v, const void *lam,
                        void *o, int32_t T, float tau, dla_dtype io, const dla_cache *cache,

@@ -11,6 +11,12 @@ from tests.helpers import mat_rel_err, row_rel_err
 
 TOL = {"f32": 1e-4, "bf16": 2e-2}
 STATE_TOL = 1e-4
+# final states of a cache storing closed states in bf16: the gate of a bf16
+# configuration per state matrix (max |diff| / max |ref|), the same 2e-2 as its
+# outputs.  Each bf16 write rounds relative 2^-9, and a state that absorbs k
+# merges is rounded k times (worst seen: 1.05e-2 after a 1200-token prefill and
+# 300 decode steps under the density rule)
+STATE_TOL_BF16_STORAGE = 2e-2
 
 
 def say(msg: str):
@@ -30,7 +36,7 @@ def oracle_threads() -> int:
     return min(os.cpu_count() or 1, 16)
 
 
-def gpu_prefill(q, k, v, lam, C, tau, io, B=None, H=None, repeats=1, merge_rule="sum"):
+def gpu_prefill(q, k, v, lam, C, tau, io, B=None, H=None, repeats=1, merge_rule="sum", state_dtype="f32"):
     """q,k [S,T,dk] ... float32 numpy (already bf16-valued for bf16).  Returns
     o (float32 numpy [S,T,dv]), schedule dict, final cache dict."""
     torch = torch_mod()
@@ -54,7 +60,7 @@ def gpu_prefill(q, k, v, lam, C, tau, io, B=None, H=None, repeats=1, merge_rule=
                  ev_t=torch.empty(BH, T, dtype=torch.int32, device=dev),
                  ev_i=torch.empty(BH, T, dtype=torch.int32, device=dev),
                  n_ev=torch.empty(BH, dtype=torch.int32, device=dev))
-    cache = dla.Cache(B, H, C, dk, dv, device=dev, merge_rule=merge_rule)
+    cache = dla.Cache(B, H, C, dk, dv, device=dev, merge_rule=merge_rule, state_dtype=state_dtype)
     ws = dla.prefill_workspace(B, H, T, C, dk, dv, dev)
     outs = []
     for _ in range(repeats):

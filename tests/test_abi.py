@@ -23,7 +23,7 @@ def test_library_exports_every_declared_symbol():
     assert {"dla_prefill", "dla_decode_step", "dla_cache_init"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert dla.dla_abi_version() == 2
+    assert dla.dla_abi_version() == 3
 
 
 def test_sizes_and_layout():
@@ -100,18 +100,46 @@ def test_bad_arguments_are_rejected_on_the_host():
         == dla.DLA_ERR_UNSUPPORTED
     # cache init
     cc = dla.dla_cache()
-    assert dla.dla_cache_init(cc, 0, 1 << 20, 1, 1, 8, 64, 64, None, None) == dla.DLA_ERR_ARG
-    assert dla.dla_cache_init(cc, p, 16, 1, 1, 8, 64, 64, None, None) == dla.DLA_ERR_ARG
+    f32 = dla.DLA_F32
+    assert dla.dla_cache_init(cc, 0, 1 << 20, 1, 1, 8, 64, 64, f32, None, None) == dla.DLA_ERR_ARG
+    assert dla.dla_cache_init(cc, p, 16, 1, 1, 8, 64, 64, f32, None, None) == dla.DLA_ERR_ARG
     pre = dla.dla_cache_preload(9, 0, p, p, p, p, 0)
-    assert dla.dla_cache_init(cc, p, 1 << 30, 1, 1, 8, 64, 64, pre, None) == dla.DLA_ERR_ARG
+    assert dla.dla_cache_init(cc, p, 1 << 30, 1, 1, 8, 64, 64, f32, pre, None) == dla.DLA_ERR_ARG
     pre = dla.dla_cache_preload(2, 0, None, p, p, p, 0)
-    assert dla.dla_cache_init(cc, p, 1 << 30, 1, 1, 8, 64, 64, pre, None) == dla.DLA_ERR_ARG
+    assert dla.dla_cache_init(cc, p, 1 << 30, 1, 1, 8, 64, 64, f32, pre, None) == dla.DLA_ERR_ARG
+
+
+def test_bf16_state_storage_layout_and_checks():
+    B, H, C_, dk, dv = 2, 3, 32, 128, 256
+    L32 = dla.dla_cache_layout(B, H, C_, dk, dv, dla.DLA_F32)
+    L16 = dla.dla_cache_layout(B, H, C_, dk, dv, dla.DLA_BF16)
+    n_states = B * H * C_ * dv * dk
+    # fp32: no active region; bf16: half-size slots, then one fp32 state per stream
+    assert L32.active_offset == L32.meta_offset and L32.meta_offset >= 4 * n_states
+    assert L16.active_offset >= 2 * n_states and L16.active_offset % 256 == 0
+    assert L16.meta_offset >= L16.active_offset + 4 * B * H * dv * dk and L16.meta_offset % 256 == 0
+    assert L16.meta_offset < L32.meta_offset
+    assert dla.dla_cache_bytes(B, H, C_, dk, dv, dla.DLA_BF16) == L16.meta_offset + B * H * L16.meta_stride
+    assert dla.dla_cache_bytes(B, H, C_, dk, dv, 7) == 0
+    p = 0x100000
+    cc = dla.dla_cache()
+    assert dla.dla_cache_init(cc, p, 1 << 30, 1, 1, 8, 64, 64, 7, None, None) == dla.DLA_ERR_ARG
+    assert "state dtype" in dla.dla_last_error()
+    # a bf16 cache needs the register-resident prefill: fp32 io is refused on the host
+    c = _cache()
+    c.state_dtype = dla.DLA_BF16
+    c.bytes = dla.dla_cache_bytes(1, 1, 8, 64, 64, dla.DLA_BF16)
+    ws = dla.dla_prefill_workspace_bytes(1, 1, 100, 8, 64, 64)
+    assert dla.dla_prefill(p, p, p, p, p, 100, 0.3, dla.DLA_F32, c, p, ws, None, None) == dla.DLA_ERR_UNSUPPORTED
+    c.state_dtype = 3
+    assert dla.dla_prefill(p, p, p, p, p, 100, 0.3, dla.DLA_BF16, c, p, ws, None, None) == dla.DLA_ERR_ARG
 
 
 def test_merge_rule_is_validated_on_the_host():
     p = 0x100000
     # the view's layout: the rule sits where the header puts it
-    assert C.sizeof(dla.dla_cache) == 40 and dla.dla_cache.merge_rule.offset == 20
+    assert C.sizeof(dla.dla_cache) == 48 and dla.dla_cache.merge_rule.offset == 20
+    assert dla.dla_cache.state_dtype.offset == 24 and dla.dla_cache.base.offset == 32
     c = _cache()
     assert c.merge_rule == dla.DLA_MERGE_SUM
     assert dla.load().dla_cache_set_merge_rule(C.byref(c), 2) == dla.DLA_ERR_ARG

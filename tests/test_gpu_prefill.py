@@ -9,9 +9,9 @@ import pytest
 
 import oracle
 import workloads
-from tests.gpu_common import (TOL, compare_outputs, compare_schedule, compare_states, gpu_prefill,
-                              oracle_threads, say, torch_mod)
-from tests.helpers import keys_for_scores, row_rel_err
+from tests.gpu_common import (STATE_TOL_BF16_STORAGE, TOL, compare_outputs, compare_schedule, compare_states,
+                              gpu_prefill, oracle_threads, say, torch_mod)
+from tests.helpers import keys_for_scores, mat_rel_err, row_rel_err
 
 pytestmark = pytest.mark.gpu
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "schedule_cases.json")
@@ -122,6 +122,38 @@ def test_density_merge_rule(name, streams, T, C, means, prefill_path):
                        nthreads=oracle_threads())
     assert r["n_ev"].min() > 0
     assert any(a != b for a, b in zip(r["events"], r_sum["events"])), "the two rules agree on this input"
+
+
+BF16_STORAGE = [
+    # (workload, streams, T, C, segment means)
+    ("mamba2_780m_bf16", [0, 1, 2], 1300, 16, (12, 90)),
+    ("gdn_1p3b_t32k_bf16", [0, 1], 2100, 32, (6, 40)),
+    ("long_t131k_bf16", [3], 800, 5, (8,)),
+]
+
+
+@pytest.mark.parametrize("rule", ["sum", "density"])
+@pytest.mark.parametrize("name,streams,T,C,means", BF16_STORAGE)
+def test_bf16_state_storage(name, streams, T, C, means, rule):
+    """A cache storing its closed states in bf16: the schedule is the oracle's
+    bit for bit, outputs are within the bf16 tolerance, the active state is
+    fp32-exact, the closed ones within bf16 storage rounding."""
+    torch_mod()
+    cfg = dataclasses.replace(workloads.CONFIGS[name], C=C, **({} if means is None else dict(seg_means=means)))
+    d = workloads.prefill_inputs(cfg, streams=streams, T=T)
+    label = f"bf16 storage {name} {rule}"
+    say(f"prefill {label}: S={len(streams)} T={T} C={C}")
+    o, sc, fin = gpu_prefill(d["q"], d["k"], d["v"], d["lam"], C, cfg.tau, "bf16", merge_rule=rule,
+                             state_dtype="bf16")
+    r = oracle.run(d["q"], d["k"], d["v"], d["lam"], C, cfg.tau, nthreads=oracle_threads(), merge_rule=rule)
+    compare_schedule(r, sc, fin, label)
+    compare_outputs(o, r["o"], TOL["bf16"], label)
+    worst = compare_states(r, fin, tol=STATE_TOL_BF16_STORAGE, label=label)
+    for i in range(len(streams)):
+        m = int(r["fin_m"][i])
+        assert mat_rel_err(fin["S"][i, m - 1:m], r["fin_S"][i, m - 1:m]) <= 1e-4, f"{label}: active state ({i})"
+    assert r["n_ev"].min() > 0
+    say(f"prefill {label}: ok, worst closed-state error {worst:.2e}")
 
 
 def test_literal_noise_reading_every_token_opens(prefill_path):

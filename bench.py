@@ -301,7 +301,9 @@ def decode_bench(args, torch, dla, workloads, state_dtype="f32"):
         roofline=dict(bound="hbm", achieved=achieved, peak=PEAK_HBM_GBS, unit="GB/s",
                       frac=achieved / PEAK_HBM_GBS,
                       traffic=measured_traffic(f"k_decode_{args.decode_workload}_hbm_traffic.txt", "k_decode")
-                      if state_dtype == "f32" else None,
+                      if state_dtype == "f32" else
+                      measured_traffic(f"k_decode_bf16_states_{args.decode_workload}_hbm_traffic.txt",
+                                       "k_decode(bf16 states)"),
                       kernel="k_decode",
                       kernel_ms=kern_avg, algorithmic_bytes_per_launch=bytes_per_step),
         inputs="drawn on the device with torch's seeded generator, same recipe",

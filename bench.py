@@ -128,12 +128,15 @@ def prefill_bench(args, torch, dla, workloads):
         dla.prefill(q, k, v, lam, cfg.tau, cache, o=o, workspace=ws,
                     sched=dict(m_t=m_t, boundary=bnd, n_ev=n_ev))
         torch.cuda.synchronize()
+        # (a prefill continues what the cache holds: every step below starts
+        # from an empty cache, and the reset is part of the timed step)
         m_sum = int(m_t.sum(dtype=torch.int64).item())
         flops = 2.0 * (m_sum + BH * T) * dk * dv
         stats = dict(mean_live_states=m_sum / (BH * T),
                      boundaries_per_stream=float(bnd.sum(dtype=torch.int64).item()) / BH,
                      merges_per_stream=float(n_ev.sum(dtype=torch.int64).item()) / BH)
         for _ in range(args.warmup):
+            cache.reset()
             dla.prefill(q, k, v, lam, cfg.tau, cache, o=o, workspace=ws)
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(args.steps)]
@@ -143,6 +146,7 @@ def prefill_bench(args, torch, dla, workloads):
         torch.cuda.synchronize()
         w0 = time.perf_counter()
         for a, b in evs:
+            cache.reset()
             dla.dla_set_prefill_events(a.cuda_event, b.cuda_event)
             dla.prefill(q, k, v, lam, cfg.tau, cache, o=o, workspace=ws)
         torch.cuda.synchronize()

@@ -256,6 +256,16 @@ class Cache:
             raise DLAError(DLA_ERR_ARG, f"unknown merge rule {merge_rule!r}")
         dla_cache_set_merge_rule(self.view, MERGE_RULES[merge_rule])
 
+    def reset(self):
+        """Make every stream empty again (same buffer, shape, merge rule and
+        state dtype), so that the next prefill starts afresh."""
+        B, H, C_, d_k, d_v = self.shape
+        rule = self.view.merge_rule
+        sdt = DLA_BF16 if self.state_dtype == "bf16" else DLA_F32
+        _check(dla_cache_init(self.view, self.buf.data_ptr(), self.buf.numel(), B, H, C_, d_k, d_v, sdt, None,
+                              _stream(self.buf.device)))
+        dla_cache_set_merge_rule(self.view, rule)
+
     @property
     def device(self):
         return self.buf.device

@@ -49,7 +49,7 @@ dla_status check_shape(int32_t B, int32_t H, int32_t C, int32_t dk, int32_t dv)
 }
 
 struct Sizes {
-    uint64_t s, qs, flag, tile_cnt, tile_sum, seg_t, seg_P, seg_q0, nseg, events, chunk_ev, shadow;
+    uint64_t s, qs, flag, tile_cnt, tile_sum, seg_t, seg_P, seg_q0, nseg, events, chunk_ev, init_m, init_order, shadow;
     uint64_t rec;
     uint64_t total;
 };
@@ -70,10 +70,12 @@ Sizes workspace_sizes(int64_t BH, int64_t T, int64_t C, int64_t dk, int64_t dv)
     z.nseg = align_up(4ull * BH, 256);
     z.events = align_up(8ull * BH * T, 256);
     z.chunk_ev = align_up(4ull * BH * (NCH + 1), 256);
+    z.init_m = align_up(4ull * BH, 256);
+    z.init_order = align_up(64ull * BH, 256);
     z.shadow = align_up(2ull * BH * C * dv * dk, 256);
     z.rec = align_up(static_cast<uint64_t>(BH) * NCH * rs_record_bytes(dk), 256);
     z.total = z.s + z.qs + z.flag + z.tile_cnt + z.tile_sum + z.seg_t + z.seg_P + z.seg_q0 + z.nseg +
-              z.events + z.chunk_ev + z.shadow + z.rec;
+              z.events + z.chunk_ev + z.init_m + z.init_order + z.shadow + z.rec;
     return z;
 }
 
@@ -92,6 +94,8 @@ Workspace carve(void *base, const Sizes &z)
     w.nseg = reinterpret_cast<int32_t *>(p); p += z.nseg;
     w.events = reinterpret_cast<int2 *>(p); p += z.events;
     w.chunk_ev = reinterpret_cast<int32_t *>(p); p += z.chunk_ev;
+    w.init_m = reinterpret_cast<int32_t *>(p); p += z.init_m;
+    w.init_order = p; p += z.init_order;
     w.shadow = p; p += z.shadow;
     w.rec = p; p += z.rec;
     (void)p;

@@ -65,6 +65,8 @@ struct Workspace {
     int32_t *nseg;       // [BH]
     int2 *events;        // [BH][T] (token, state merged away or -1)
     int32_t *chunk_ev;   // [BH][NCH+1] first event of each chunk
+    int32_t *init_m;     // [BH] live states when the call starts (saved by the greedy scan)
+    uint8_t *init_order; // [BH][64] their physical slots, oldest first
     void *shadow;        // [BH][C][dv][dk] fp16 copy of the states (bf16 io)
     // per-chunk operands built by the chunk pre-pass (register-resident path)
     // [BH][NCH] chunk records of the register-resident prefill, each

@@ -85,7 +85,8 @@ __global__ __launch_bounds__(256) void k_score(const TIO *__restrict__ K, int T,
                                                int64_t *__restrict__ qs_out,
                                                uint8_t *__restrict__ flag_out,
                                                int32_t *__restrict__ tile_cnt,
-                                               int64_t *__restrict__ tile_sum, int NT)
+                                               int64_t *__restrict__ tile_sum, int NT,
+                                               const uint8_t *__restrict__ meta_base, size_t meta_stride)
 {
     constexpr int G = DK / 8;        // lanes per token, 8 elements each
     constexpr int TPW = 64 / G;      // tokens per wave pass
@@ -97,6 +98,14 @@ __global__ __launch_bounds__(256) void k_score(const TIO *__restrict__ K, int T,
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int gi = lane / G, gl = lane % G;
     const TIO *Kb = K + static_cast<size_t>(bh) * T * DK;
+    // the stream as the cache leaves it: token 0 is scored against its last
+    // key (if it has seen one) and is a boundary only by the usual rule
+    // unless the cache is empty
+    const uint8_t *meta = meta_base + static_cast<size_t>(bh) * meta_stride;
+    const MetaHead *head = reinterpret_cast<const MetaHead *>(meta);
+    const float *kprev = reinterpret_cast<const float *>(meta + kOffKprev);
+    const int has_prev = head->has_prev, m_init = head->m;
+    const float s_prev = head->s_prev;
 
     // j indexes tokens t0 - 1 .. t0 + 255
     for (int base = wave * TPW; base < kScoreTile + 1; base += 4 * TPW) {
@@ -115,11 +124,22 @@ __global__ __launch_bounds__(256) void k_score(const TIO *__restrict__ K, int T,
                 a += x * x;
                 b += y * y;
             }
+        } else if (valid && has_prev) {
+            // token 0 of the call against the last key the cache kept
+            const TIO *kt = Kb + gl * 8;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const double x = to_f(kt[e]);
+                const double y = kprev[gl * 8 + e];
+                d += x * y;
+                a += x * x;
+                b += y * y;
+            }
         }
         d = group_sum_dpp<G>(d);
         a = group_sum_dpp<G>(a);
         b = group_sum_dpp<G>(b);
-        if (valid && gl == 0) s_lds[j] = (t == 0) ? 1.0f : cosine_distance(d, a, b);
+        if (valid && gl == 0) s_lds[j] = (t == 0 && !has_prev) ? 1.0f : cosine_distance(d, a, b);
     }
     __syncthreads();
 
@@ -128,8 +148,8 @@ __global__ __launch_bounds__(256) void k_score(const TIO *__restrict__ K, int T,
     int64_t q = 0;
     if (t < T) {
         const float s = s_lds[tid + 1];
-        const float sp = (t == 0) ? 1.0f : s_lds[tid];
-        const int bnd = (t == 0) || !((s < tau) && (sp < tau));
+        const float sp = (t == 0) ? s_prev : s_lds[tid];
+        const int bnd = (t == 0 && m_init == 0) || !((s < tau) && (sp < tau));
         q = fixed_point(s);
         const size_t row = static_cast<size_t>(bh) * T + t;
         s_out[row] = s;
@@ -239,15 +259,36 @@ __global__ __launch_bounds__(64) void k_greedy(int T, int C, int NCH,
                                                uint8_t *__restrict__ meta_base, size_t meta_stride,
                                                int32_t *__restrict__ ev_t_out,
                                                int32_t *__restrict__ ev_i_out,
-                                               int32_t *__restrict__ n_ev_out, int merge_rule)
+                                               int32_t *__restrict__ n_ev_out, int merge_rule,
+                                               int32_t *__restrict__ init_m_out,
+                                               uint8_t *__restrict__ init_order_out)
 {
     const int bh = blockIdx.x;
     const int lane = threadIdx.x;
     const size_t sbase = static_cast<size_t>(bh) * (T + 1);
     const int nseg = nseg_arr[bh];
-    int64_t I = 0;
-    int32_t n = 0, st = 0, oi = -1;
-    int m = 0, cur_chunk = -1, nev = 0, nmerge = 0;
+    uint8_t *meta = meta_base + static_cast<size_t>(bh) * meta_stride;
+    MetaHead *head = reinterpret_cast<MetaHead *>(meta);
+    int64_t *info = reinterpret_cast<int64_t *>(meta + kOffInfo);
+    int32_t *count = reinterpret_cast<int32_t *>(meta + kOffCount);
+    int64_t *start = reinterpret_cast<int64_t *>(meta + kOffStart);
+    // the stream as the cache leaves it (states with absolute token starts);
+    // the live count and slots are kept for the chunk kernels, since the
+    // metadata is rewritten at the end
+    const int m_init = head->m;
+    const int64_t t_seen = head->t_seen;
+    int64_t I = lane < m_init ? info[lane] : 0;
+    int32_t n = lane < m_init ? count[lane] : 0;
+    int64_t st = lane < m_init ? start[lane] : 0;
+    int32_t oi = -1;
+    int m = m_init, cur_chunk = -1, nev = 0, nmerge = 0;
+    if (lane == 0) init_m_out[bh] = m_init;
+    init_order_out[static_cast<size_t>(bh) * kMaxC + lane] = meta[kOffOrder + lane];
+    // the tokens before the call's first boundary join the most recent state
+    if (m_init > 0 && lane == m_init - 1) {
+        I += seg_P[sbase];
+        n += seg_t[sbase];
+    }
 
     for (int b0 = 0; b0 < nseg; b0 += 64) {
         const int j = b0 + lane;
@@ -277,17 +318,17 @@ __global__ __launch_bounds__(64) void k_greedy(int T, int C, int NCH,
             }
             int dead = -1, istar = -1;
             if (m < C) {
-                if (lane == m) { I = qj; n = 1; st = t; oi = -1; }
+                if (lane == m) { I = qj; n = 1; st = t_seen + t; oi = -1; }
                 ++m;
             } else {
                 const int64_t I_nx = __shfl_down(I, 1);
                 const int32_t n_nx = __shfl_down(n, 1);
-                const int32_t st_nx = __shfl_down(st, 1);
+                const int64_t st_nx = __shfl_down(st, 1);
                 const int32_t oi_nx = __shfl_down(oi, 1);
                 const bool inside = lane + 1 < m;
                 const int64_t pI = inside ? I_nx : qj;
                 const int32_t pn = inside ? n_nx : 1;
-                const int32_t pst = inside ? st_nx : t;
+                const int64_t pst = inside ? st_nx : t_seen + t;
                 const int32_t poi = inside ? oi_nx : -1;
                 if (merge_rule == DLA_MERGE_DENSITY) {
                     // lowest information density (I_i + I_{i+1}) / (n_i + n_{i+1})
@@ -299,8 +340,8 @@ __global__ __launch_bounds__(64) void k_greedy(int T, int C, int NCH,
                     istar = __ffsll(static_cast<unsigned long long>(hit)) - 1;
                 }
                 const int32_t d_oi = readlane_any(poi, istar);
-                const int32_t d_st = readlane_any(pst, istar);
-                dead = d_oi >= 0 ? d_oi : 64 + (d_st - cur_chunk * kChunk);
+                const int64_t d_st = readlane_any(pst, istar);
+                dead = d_oi >= 0 ? d_oi : 64 + static_cast<int>(d_st - t_seen - cur_chunk * kChunk);
                 if (lane == istar) { I += pI; n += pn; }
                 else if (lane > istar && lane < m) { I = pI; n = pn; st = pst; oi = poi; }
             }
@@ -320,20 +361,15 @@ __global__ __launch_bounds__(64) void k_greedy(int T, int C, int NCH,
         chunk_ev[static_cast<size_t>(bh) * (NCH + 1) + kk] = nev;
     if (n_ev_out && lane == 0) n_ev_out[bh] = nmerge;
 
-    uint8_t *meta = meta_base + static_cast<size_t>(bh) * meta_stride;
-    MetaHead *head = reinterpret_cast<MetaHead *>(meta);
-    int64_t *info = reinterpret_cast<int64_t *>(meta + kOffInfo);
-    int32_t *count = reinterpret_cast<int32_t *>(meta + kOffCount);
-    int64_t *start = reinterpret_cast<int64_t *>(meta + kOffStart);
     info[lane] = lane < m ? I : 0;
     count[lane] = lane < m ? n : 0;
-    start[lane] = lane < m ? static_cast<int64_t>(st) : 0;
+    start[lane] = lane < m ? st : 0;
     if (lane == 0) {
         head->m = m;
         head->has_prev = 1;
         head->s_prev = s_all[static_cast<size_t>(bh) * T + T - 1];
         head->pad0 = 0;
-        head->t_seen = T;
+        head->t_seen = t_seen + T;
         head->pad1 = 0;
     }
 }
@@ -396,13 +432,46 @@ struct PrefillSmem {
 // query chunk scaled by a power of two; both exponents are folded into the
 // read weights.  The intra-chunk product and the state updates multiply the
 // exact bf16 inputs (fp32 accumulation).  With fp32 inputs everything is fp32.
+// The fp16 operand copy of the state in physical slot `slot` (this block's
+// d_v slice), normalised by a power of two kept in S.shexp: a block-wide
+// maximum, then the scaled copy.  Every thread of the block takes part.
+template <int DK, int DVT, typename Smem, typename RT>
+__device__ void shadow_state(Smem &S, int slot, const float *st_base, RT *shadow_base, size_t slot_stride,
+                             int tid, int lane, int wave)
+{
+    const float4 *src = reinterpret_cast<const float4 *>(st_base + slot * slot_stride);
+    float mx = 0.0f;
+    for (int idx = tid; idx < DVT * DK / 4; idx += 256) {
+        const float4 a = src[idx];
+        mx = fmaxf(mx, fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))));
+    }
+    mx = wave_max(mx);
+    __syncthreads();
+    if (lane == 0) S.red[wave] = mx;
+    __syncthreads();
+    const int e = f16_exponent(fmaxf(fmaxf(S.red[0], S.red[1]), fmaxf(S.red[2], S.red[3])));
+    RT *dst = shadow_base + slot * slot_stride;
+    for (int idx = tid; idx < DVT * DK / 8; idx += 256) {
+        const float4 a = src[2 * idx];
+        const float4 b = src[2 * idx + 1];
+        f16x8 o;
+        o[0] = static_cast<_Float16>(ldexpf(a.x, -e)); o[1] = static_cast<_Float16>(ldexpf(a.y, -e));
+        o[2] = static_cast<_Float16>(ldexpf(a.z, -e)); o[3] = static_cast<_Float16>(ldexpf(a.w, -e));
+        o[4] = static_cast<_Float16>(ldexpf(b.x, -e)); o[5] = static_cast<_Float16>(ldexpf(b.y, -e));
+        o[6] = static_cast<_Float16>(ldexpf(b.z, -e)); o[7] = static_cast<_Float16>(ldexpf(b.w, -e));
+        reinterpret_cast<f16x8 *>(dst)[idx] = o;
+    }
+    if (tid == 0) S.shexp[slot] = e;
+}
+
 template <typename TIO, int DK, int DVT>
 __global__ __launch_bounds__(256, 1) void k_prefill(
     const TIO *__restrict__ Q, const TIO *__restrict__ K, const TIO *__restrict__ V,
     const TIO *__restrict__ LAM, TIO *__restrict__ O, int T, int C, int DV, int nblk_dv,
     float *__restrict__ states, typename ReadT<TIO>::type *__restrict__ shadow,
     const int2 *__restrict__ events, const int32_t *__restrict__ chunk_ev,
-    uint8_t *__restrict__ meta_base, size_t meta_stride, int32_t *__restrict__ m_t_out)
+    uint8_t *__restrict__ meta_base, size_t meta_stride, int32_t *__restrict__ m_t_out,
+    const int32_t *__restrict__ init_m, const uint8_t *__restrict__ init_order)
 {
     constexpr int KS = DK / 32;     // reduction steps over d_k
     constexpr int NTV = DVT / 16;   // 16-wide tiles over the d_v slice
@@ -436,6 +505,17 @@ __global__ __launch_bounds__(256, 1) void k_prefill(
 
     int m0 = 0;
     if (tid < kMaxC) { S.order[tid] = tid; S.shexp[tid] = 0; }
+    // the states the cache holds when the call starts (their fp32 values are
+    // in the cache already; with bf16 io their fp16 operand copies are made here)
+    const int m_init = init_m[bh];
+    if (tid < m_init) S.order[tid] = init_order[static_cast<size_t>(bh) * kMaxC + tid];
+    m0 = m_init;
+    if constexpr (kHalfRead) {
+        __syncthreads();
+        for (int i = 0; i < m_init; ++i)
+            shadow_state<DK, DVT>(S, S.order[i], st_base, shadow + static_cast<size_t>(bh) * C * DV * DK +
+                                  static_cast<size_t>(dv0) * DK, slot_stride, tid, lane, wave);
+    }
 
     for (int ch = 0; ch < NCH; ++ch) {
         const int c0 = ch * kChunk;
@@ -720,33 +800,9 @@ __global__ __launch_bounds__(256, 1) void k_prefill(
         __syncthreads();
         if constexpr (kHalfRead) {
             // fp16 operand copies of the changed states, normalised per state
-            for (int c = 0; c < S.n_changed; ++c) {
-                const int slot = S.changed[c];
-                const float4 *src = reinterpret_cast<const float4 *>(st_base + slot * slot_stride);
-                float mx = 0.0f;
-                for (int idx = tid; idx < DVT * DK / 4; idx += 256) {
-                    const float4 a = src[idx];
-                    mx = fmaxf(mx, fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))));
-                }
-                mx = wave_max(mx);
-                __syncthreads();
-                if (lane == 0) S.red[wave] = mx;
-                __syncthreads();
-                const int e = f16_exponent(fmaxf(fmaxf(S.red[0], S.red[1]), fmaxf(S.red[2], S.red[3])));
-                RT *dst = shadow + static_cast<size_t>(bh) * C * DV * DK + slot * slot_stride +
-                          static_cast<size_t>(dv0) * DK;
-                for (int idx = tid; idx < DVT * DK / 8; idx += 256) {
-                    const float4 a = src[2 * idx];
-                    const float4 b = src[2 * idx + 1];
-                    f16x8 o;
-                    o[0] = static_cast<_Float16>(ldexpf(a.x, -e)); o[1] = static_cast<_Float16>(ldexpf(a.y, -e));
-                    o[2] = static_cast<_Float16>(ldexpf(a.z, -e)); o[3] = static_cast<_Float16>(ldexpf(a.w, -e));
-                    o[4] = static_cast<_Float16>(ldexpf(b.x, -e)); o[5] = static_cast<_Float16>(ldexpf(b.y, -e));
-                    o[6] = static_cast<_Float16>(ldexpf(b.z, -e)); o[7] = static_cast<_Float16>(ldexpf(b.w, -e));
-                    reinterpret_cast<f16x8 *>(dst)[idx] = o;
-                }
-                if (tid == 0) S.shexp[slot] = e;
-            }
+            for (int c = 0; c < S.n_changed; ++c)
+                shadow_state<DK, DVT>(S, S.changed[c], st_base, shadow + static_cast<size_t>(bh) * C * DV * DK +
+                                      static_cast<size_t>(dv0) * DK, slot_stride, tid, lane, wave);
         }
         __syncthreads();
         if (tid < kMaxC) S.order[tid] = tid < S.m_new ? S.new_order[tid] : 0;
@@ -1066,13 +1122,13 @@ static hipError_t prefill_schedule(const PrefillArgs &a, hipStream_t stream)
     const int NCH = (T + kChunk - 1) / kChunk;
     const TIO *K = static_cast<const TIO *>(a.k);
     hipLaunchKernelGGL((k_score<TIO, DK>), dim3(NT, BH), dim3(256), 0, stream, K, T, a.tau, a.ws.s,
-                       a.ws.qs, a.ws.flag, a.ws.tile_cnt, a.ws.tile_sum, NT);
+                       a.ws.qs, a.ws.flag, a.ws.tile_cnt, a.ws.tile_sum, NT, a.meta, a.g.meta_stride);
     hipLaunchKernelGGL(k_compact, dim3(NT, BH), dim3(256), 0, stream, T, NT, a.ws.flag, a.ws.qs,
                        a.ws.tile_cnt, a.ws.tile_sum, a.ws.seg_t, a.ws.seg_P, a.ws.seg_q0, a.ws.nseg,
                        a.sched.seg_id);
     hipLaunchKernelGGL(k_greedy, dim3(BH), dim3(64), 0, stream, T, a.g.C, NCH, a.ws.seg_t, a.ws.seg_P,
                        a.ws.seg_q0, a.ws.nseg, a.ws.events, a.ws.chunk_ev, a.ws.s, a.meta, a.g.meta_stride,
-                       a.sched.ev_t, a.sched.ev_i, a.sched.n_ev, a.merge_rule);
+                       a.sched.ev_t, a.sched.ev_i, a.sched.n_ev, a.merge_rule, a.ws.init_m, a.ws.init_order);
     hipLaunchKernelGGL((k_store_kprev<TIO>), dim3(BH), dim3(128), 0, stream, K, T, DK, a.meta,
                        a.g.meta_stride);
     return hipGetLastError();
@@ -1101,7 +1157,7 @@ static hipError_t prefill_main(const PrefillArgs &a, hipStream_t stream)
                        static_cast<const TIO *>(a.v), static_cast<const TIO *>(a.lam),
                        static_cast<TIO *>(a.o), a.T, a.g.C, a.g.dv, nblk_dv, a.states,
                        static_cast<typename ReadT<TIO>::type *>(a.ws.shadow), a.ws.events, a.ws.chunk_ev, a.meta,
-                       a.g.meta_stride, a.sched.m_t);
+                       a.g.meta_stride, a.sched.m_t, a.ws.init_m, a.ws.init_order);
     hipError_t e = hipGetLastError();
     if (e == hipSuccess && a.ev_after) e = hipEventRecord(a.ev_after, stream);
     return e;

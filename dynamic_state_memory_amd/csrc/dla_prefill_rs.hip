@@ -88,7 +88,7 @@ template <int DK>
 __global__ __launch_bounds__(256) void k_chunk_prep(
     const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, const __bf16 *__restrict__ LAM, int T, int C,
     const int2 *__restrict__ events, const int32_t *__restrict__ chunk_ev, uint8_t *__restrict__ rec,
-    int32_t *__restrict__ m_t_out)
+    int32_t *__restrict__ m_t_out, const int32_t *__restrict__ init_m)
 {
     constexpr int KS = DK / 32;
     // 40 KB of LDS: four blocks per compute unit.  The weighted scores P
@@ -146,9 +146,9 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
     }
     const int e0 = chunk_ev[static_cast<size_t>(bh) * (NCH + 1) + ch];
     const int nev = chunk_ev[static_cast<size_t>(bh) * (NCH + 1) + ch + 1] - e0;
-    // states live at the chunk start: the cache starts empty, every boundary
-    // opens a state and a merge keeps the count at C
-    const int m0 = min(C, e0);
+    // states live at the chunk start: those the cache held when the call
+    // started, plus one per boundary before the chunk, capped at C by the merges
+    const int m0 = min(C, init_m[bh] + e0);
     if (tid < nev) evs[tid] = events[tok0 + e0 + tid];
     qmax = wave_max(qmax);
     if (lane == 0) red[wave] = qmax;
@@ -473,6 +473,8 @@ struct RsParams {
     int bh, dv0, tid, lane, wave, lr, lg, NCH, vr, vc;
     bool v_mover;
     size_t tok0, slot_stride;
+    int m_init;                 // states the cache held when the call started
+    const uint8_t *init_order;  // their physical slots, oldest first
     void *st_base;              // the stream's slice of the slots (fp32, or bf16 closed states)
     float *act_base;            // its slice of the fp32 active-state region (bf16 cache), else NULL
 };
@@ -485,7 +487,7 @@ struct RsParams {
 // (closed states in registers), holds d_k rows 32 (w - AW) .. + 31 of the
 // active state (d_k = 128: every wave), and reduces and stores the outputs of
 // tokens 16 w .. 16 w + 15.
-template <int DK, int DVT, int SPW, bool SBF>
+template <int DK, int DVT, int SPW, bool SBF, bool CONT>
 __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB<DK> &Y,
                                          RsSmem<DK, DVT, kRsWaves * SPW> &S, const RsParams &A,
                                          RsCarry<DK, DVT, SPW> &c)
@@ -508,12 +510,16 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
     const bool act_wave = wave >= AW;
     const int kb = wave - AW;                    // the active wave's 32-row d_k block
 
+    // chunk -1 (a call starting from a non-empty cache) has no tokens and
+    // stores nothing: it runs on chunk 0's operands, and only its event
+    // path matters, which loads the closed states the cache holds
+    const bool virt = CONT && ch < 0;
     const int c0 = ch * kChunk;
-    const int nvalid = min(kChunk, T - c0);
+    const int nvalid = virt ? 0 : min(kChunk, T - c0);
     const u32x4 vcur = c.vnext;
     const int2 evcur = c.evnext;
     const bool more = ch + 1 < NCH;
-    const size_t cb = static_cast<size_t>(bh) * NCH + ch;
+    const size_t cb = static_cast<size_t>(bh) * NCH + (virt ? 0 : ch);
     // part A of chunk ch has landed (every wave's share) and every wave is
     // done with chunk ch - 1 (so part B may be overwritten)
     wait_vmem();
@@ -606,10 +612,10 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
     wait_vmem();
     __syncthreads();
     const int nev = __builtin_amdgcn_readfirstlane(S.nev);
-    const bool has_ev = nev > 0;
+    const bool has_ev = virt || nev > 0;
     // ---- part A of the next chunk; its V, events and query exponent into registers
     if (more) {
-        stage_a<DK>(X, A.rec, cb + 1, tid, wave);
+        stage_a<DK>(X, A.rec, cb + (virt ? 0 : 1), tid, wave);
         const int c0n = c0 + kChunk;
         c.vnext = u32x4{0u, 0u, 0u, 0u};
         if (A.v_mover && vr < min(kChunk, T - c0n))
@@ -695,7 +701,32 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
     floatx4 *anbuf = &S.ored[0][0][0][0];                           // [DK / 16][NTV][64]
     static_assert((DK / 16) * NTV * 64 * sizeof(floatx4) <= sizeof(S.W), "the active state fits the weight table");
     static_assert((DK / 16) * NTV * 64 <= NW * MT * NTV * 64, "a state slice fits the partial-read buffer");
-    if (wave == 0) {
+    if (wave == 0 && virt) {
+        // chunk -1: each closed state the cache holds is a job that keeps its
+        // own value (read from the cache into its owner's registers); the
+        // most recent one, already in the accumulators, stays the active state
+        const int mi = A.m_init;
+        const int ord = lane < mi ? A.init_order[lane] : 255;
+        uint32_t jobs = 0;
+        for (int i = 0; i + 1 < mi; ++i) jobs |= 1u << __builtin_amdgcn_readlane(ord, i);
+        const int an = __builtin_amdgcn_readlane(ord, mi - 1);
+        if (lane < mi) S.new_order[lane] = ord;
+        if (lane + 1 < mi) {
+            S.jbase[ord] = 1;
+            S.jsrc[ord] = 0;
+            S.jlo[ord] = 0;
+            S.jhi[ord] = 0;
+        }
+        if (lane == 0) {
+            S.jlo[an] = 0;
+            S.jhi[an] = 0;
+            S.jobs = jobs;
+            S.closed_new = jobs;
+            S.m_new = mi;
+            S.act_new = an;
+            S.an_case = 0;
+        }
+    } else if (wave == 0) {
         // the chunk's events are in the registers of lanes 0 .. nev - 1: the
         // live states at its end (bit i of oa: old state i, bit p of na: the
         // state opened at chunk position p) and the slots the old ones keep
@@ -971,12 +1002,13 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
     c.ewin += nev;
 }
 
-template <int DK, int DVT, int SPW, bool SBF>
+template <int DK, int DVT, int SPW, bool SBF, bool CONT>
 __global__ __launch_bounds__(kRsThreads, 2) void k_prefill_rs(
     const __bf16 *__restrict__ V, __bf16 *__restrict__ O, int T, int C, int DV, int nblk_dv,
     float *__restrict__ states, float *__restrict__ active, const int2 *__restrict__ events,
     const int32_t *__restrict__ chunk_ev, const uint8_t *__restrict__ rec,
-    uint8_t *__restrict__ meta_base, size_t meta_stride)
+    uint8_t *__restrict__ meta_base, size_t meta_stride, const int32_t *__restrict__ init_m,
+    const uint8_t *__restrict__ init_order)
 {
     constexpr int KS = DK / 32;
     constexpr int NTV = DVT / 16;
@@ -1038,6 +1070,40 @@ __global__ __launch_bounds__(kRsThreads, 2) void k_prefill_rs(
     c.closed = 0;
     if (tid < kMaxC) { S.order[tid] = tid; S.shexp[tid] = 0; }
 
+    // the states the cache holds when the call starts (oldest first, in the
+    // physical slots the greedy scan recorded): the closed ones into their
+    // owner waves' fp16 operand registers, the most recent one into the
+    // active-state accumulators
+    // the states the cache holds when the call starts: the most recent one
+    // into the active-state accumulators here, the closed ones through the
+    // event path of a chunk -1 (which loads each from the cache into its
+    // owner wave's registers)
+    A.m_init = init_m[A.bh];
+    A.init_order = init_order + static_cast<size_t>(A.bh) * kMaxC;
+    // two instances are launched: CONT for streams whose cache holds states,
+    // the other for empty ones (the sweep without the start-up code); a block
+    // of the other kind leaves at once (the whole block: no barrier is met)
+    if ((A.m_init > 0) != CONT) return;
+    if (CONT) {
+        c.act = A.init_order[A.m_init - 1];
+        if (A.m_init == 1) {
+            c.m0 = 1;
+            if (tid == 0) S.order[0] = c.act;
+        }
+        const int kb = wave - (kRsWaves - KS);
+        if (kb >= 0) {
+            const float *src = SBF ? A.act_base : static_cast<const float *>(A.st_base) + c.act * A.slot_stride;
+#pragma unroll
+            for (int nt = 0; nt < NTV; ++nt)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const float4 v = *reinterpret_cast<const float4 *>(src + (16 * nt + lr) * DK + 32 * kb + 16 * h + 4 * lg);
+                    c.am[nt][h] = floatx4{v.x, v.y, v.z, v.w};
+                }
+            c.ea = refresh_active<NTV>(c.am, c.af);
+        }
+    }
+
     // chunk 0: part A into LDS, V and events into registers
     stage_a<DK>(stA, rec, static_cast<size_t>(A.bh) * NCH, tid, wave);
     c.vnext = u32x4{0u, 0u, 0u, 0u};
@@ -1048,7 +1114,8 @@ __global__ __launch_bounds__(kRsThreads, 2) void k_prefill_rs(
     c.evnext = make_int2(0x7fffffff, -1);
     if (wave == 0 && A.lane < A.evtot) c.evnext = events[A.tok0 + A.lane];
 
-    for (int ch = 0; ch < NCH; ++ch) rs_chunk<DK, DVT, SPW, SBF>(ch, stA, stB, S, A, c);
+    for (int ch = (CONT && A.m_init > 1) ? -1 : 0; ch < NCH; ++ch)
+        rs_chunk<DK, DVT, SPW, SBF, CONT>(ch, stA, stB, S, A, c);
 
     // the active state's accumulators are the last state of the final cache
     const int kb = wave - (kRsWaves - KS);
@@ -1078,23 +1145,27 @@ static hipError_t launch_rs(const PrefillArgs &a, hipStream_t stream)
     hipLaunchKernelGGL((k_chunk_prep<DK>), dim3(NCH, BH), dim3(256), 0, stream,
                        static_cast<const __bf16 *>(a.q), static_cast<const __bf16 *>(a.k),
                        static_cast<const __bf16 *>(a.lam), a.T, a.g.C, a.ws.events, a.ws.chunk_ev,
-                       static_cast<uint8_t *>(a.ws.rec), a.sched.m_t);
+                       static_cast<uint8_t *>(a.ws.rec), a.sched.m_t, a.ws.init_m);
     hipError_t e0 = hipGetLastError();
     if (e0 != hipSuccess) return e0;
     if (a.ev_before) {
         hipError_t e = hipEventRecord(a.ev_before, stream);
         if (e != hipSuccess) return e;
     }
-    if (a.g.state_bf16)
-        hipLaunchKernelGGL((k_prefill_rs<DK, DVT, SPW, true>), dim3(BH * nblk_dv), dim3(kRsThreads), 0, stream,
-                           static_cast<const __bf16 *>(a.v), static_cast<__bf16 *>(a.o), a.T, a.g.C, a.g.dv,
-                           nblk_dv, a.states, a.active, a.ws.events, a.ws.chunk_ev,
-                           static_cast<const uint8_t *>(a.ws.rec), a.meta, a.g.meta_stride);
-    else
-        hipLaunchKernelGGL((k_prefill_rs<DK, DVT, SPW, false>), dim3(BH * nblk_dv), dim3(kRsThreads), 0, stream,
-                           static_cast<const __bf16 *>(a.v), static_cast<__bf16 *>(a.o), a.T, a.g.C, a.g.dv,
-                           nblk_dv, a.states, a.active, a.ws.events, a.ws.chunk_ev,
-                           static_cast<const uint8_t *>(a.ws.rec), a.meta, a.g.meta_stride);
+#define DLA_RS_LAUNCH(SBF_, CONT_)                                                                          \
+    hipLaunchKernelGGL((k_prefill_rs<DK, DVT, SPW, SBF_, CONT_>), dim3(BH * nblk_dv), dim3(kRsThreads), 0, stream, \
+                       static_cast<const __bf16 *>(a.v), static_cast<__bf16 *>(a.o), a.T, a.g.C, a.g.dv, nblk_dv,    \
+                       a.states, a.active, a.ws.events, a.ws.chunk_ev, static_cast<const uint8_t *>(a.ws.rec),      \
+                       a.meta, a.g.meta_stride, a.ws.init_m, a.ws.init_order)
+    // streams starting from an empty cache, then those continuing one
+    if (a.g.state_bf16) {
+        DLA_RS_LAUNCH(true, false);
+        DLA_RS_LAUNCH(true, true);
+    } else {
+        DLA_RS_LAUNCH(false, false);
+        DLA_RS_LAUNCH(false, true);
+    }
+#undef DLA_RS_LAUNCH
     hipError_t e = hipGetLastError();
     if (e == hipSuccess && a.ev_after) e = hipEventRecord(a.ev_after, stream);
     return e;

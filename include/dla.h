@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define DLA_ABI_VERSION 3
+#define DLA_ABI_VERSION 4
 #define DLA_MAX_C 64        /* largest supported cache capacity */
 #define DLA_CHUNK 64        /* tokens per prefill chunk */
 
@@ -198,9 +198,14 @@ uint64_t dla_prefill_workspace_bytes(int32_t B, int32_t H, int32_t T, int32_t C,
                                      int32_t d_k, int32_t d_v);
 
 /*
- * Prefill: consume T tokens of every stream, starting each stream afresh
- * (whatever the cache held is discarded), write o for every token and leave
- * the final states and metadata in the cache, ready for dla_decode_step.
+ * Prefill: consume T tokens of every stream on top of what the cache holds
+ * (an empty cache from dla_cache_init, or the states, metadata and last key
+ * that earlier prefill and decode calls or a preload left), write o for every
+ * token and leave the final states and metadata in the cache, ready for
+ * dla_decode_step or another prefill.  The result is the one a single call
+ * over all the tokens so far would give (reading notes, section 5: the cache
+ * is the running state of an online stream).  To start a stream afresh,
+ * initialise the cache again.
  *   q, k    [B*H][T][d_k]   io dtype, device
  *   v, o    [B*H][T][d_v]   io dtype, device
  *   lam     [B*H][T][C]     io dtype, device; lam[.][t][j] weights slot j

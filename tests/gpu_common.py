@@ -63,7 +63,9 @@ def gpu_prefill(q, k, v, lam, C, tau, io, B=None, H=None, repeats=1, merge_rule=
     cache = dla.Cache(B, H, C, dk, dv, device=dev, merge_rule=merge_rule, state_dtype=state_dtype)
     ws = dla.prefill_workspace(B, H, T, C, dk, dv, dev)
     outs = []
-    for _ in range(repeats):
+    for rep in range(repeats):
+        if rep:
+            cache.reset()        # a prefill continues the cache: start afresh each time
         o = dla.prefill(tq, tk, tv, tl, tau, cache, workspace=ws, sched=sched)
         torch.cuda.synchronize()
         outs.append(o.float().cpu().numpy().reshape(S, T, dv))
@@ -72,6 +74,38 @@ def gpu_prefill(q, k, v, lam, C, tau, io, B=None, H=None, repeats=1, merge_rule=
     if repeats == 1:
         return outs[0], sc, fin
     return outs, sc, fin
+
+
+def gpu_prefill_pieces(q, k, v, lam, C, tau, io, ends, merge_rule="sum", state_dtype="f32"):
+    """Prefill the tokens [0, ends[0]), [ends[0], ends[1]), ... of every
+    stream with one dla_prefill call each, on one cache.  Returns the outputs
+    (float32 [S,T,dv]), per-piece schedule dicts and the final cache dict."""
+    torch = torch_mod()
+    import dynamic_state_memory_amd as dla
+    S, T, dk = k.shape
+    dv = v.shape[2]
+    dt = torch.bfloat16 if io == "bf16" else torch.float32
+    dev = torch.device("cuda:0")
+    cache = dla.Cache(1, S, C, dk, dv, device=dev, merge_rule=merge_rule, state_dtype=state_dtype)
+    outs, scheds, lo = [], [], 0
+    for hi in ends:
+        n = hi - lo
+
+        def up(a, d):
+            return torch.from_numpy(np.ascontiguousarray(a[:, lo:hi])).to(dev).to(dt).reshape(1, S, n, d)
+
+        sched = dict(s=torch.empty(S, n, dtype=torch.float32, device=dev),
+                     boundary=torch.empty(S, n, dtype=torch.uint8, device=dev),
+                     m_t=torch.empty(S, n, dtype=torch.int32, device=dev),
+                     ev_t=torch.empty(S, n, dtype=torch.int32, device=dev),
+                     ev_i=torch.empty(S, n, dtype=torch.int32, device=dev),
+                     n_ev=torch.empty(S, dtype=torch.int32, device=dev))
+        o = dla.prefill(up(q, dk), up(k, dk), up(v, dv), up(lam, C), tau, cache, sched=sched)
+        torch.cuda.synchronize()
+        outs.append(o.float().cpu().numpy().reshape(S, n, dv))
+        scheds.append({kk: vv.cpu().numpy() for kk, vv in sched.items()})
+        lo = hi
+    return np.concatenate(outs, 1), scheds, cache.read()
 
 
 def compare_schedule(r, sc, fin, label=""):

@@ -23,7 +23,7 @@ def test_library_exports_every_declared_symbol():
     assert {"dla_prefill", "dla_decode_step", "dla_cache_init"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert dla.dla_abi_version() == 3
+    assert dla.dla_abi_version() == 4
 
 
 def test_sizes_and_layout():

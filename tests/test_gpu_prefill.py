@@ -10,7 +10,7 @@ import pytest
 import oracle
 import workloads
 from tests.gpu_common import (STATE_TOL_BF16_STORAGE, TOL, compare_outputs, compare_schedule, compare_states,
-                              gpu_prefill, oracle_threads, say, torch_mod)
+                              gpu_prefill, gpu_prefill_pieces, oracle_threads, say, torch_mod)
 from tests.helpers import keys_for_scores, mat_rel_err, row_rel_err
 
 pytestmark = pytest.mark.gpu
@@ -154,6 +154,56 @@ def test_bf16_state_storage(name, streams, T, C, means, rule):
         assert mat_rel_err(fin["S"][i, m - 1:m], r["fin_S"][i, m - 1:m]) <= 1e-4, f"{label}: active state ({i})"
     assert r["n_ev"].min() > 0
     say(f"prefill {label}: ok, worst closed-state error {worst:.2e}")
+
+
+CONTINUE = [
+    # (workload, streams, piece ends, C, segment means, io)
+    ("mamba2_780m_bf16", [0, 1], (300, 710, 1200), 16, (12, 90), "bf16"),
+    ("gdn_1p3b_t32k_bf16", [0, 1], (64, 129, 130, 700), 32, (6, 40), "bf16"),
+    ("long_t131k_bf16", [2], (1, 77, 500), 5, (8,), "bf16"),
+    ("tiny_fp32", [0], (100, 257, 512), 8, None, "f32"),
+]
+
+
+@pytest.mark.parametrize("state_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("rule", ["sum", "density"])
+@pytest.mark.parametrize("name,streams,ends,C,means,io", CONTINUE)
+def test_prefill_continues_the_cache(name, streams, ends, C, means, io, rule, state_dtype, prefill_path):
+    """Prefill in pieces on one cache equals one pass over all the tokens:
+    outputs, every piece's schedule and the final cache against the oracle."""
+    torch_mod()
+    if state_dtype == "bf16" and (prefill_path == "streamed" or io == "f32"):
+        pytest.skip("a bf16-state cache is prefilled by the register-resident kernel only")
+    cfg = dataclasses.replace(workloads.CONFIGS[name], C=C, **({} if means is None else dict(seg_means=means)))
+    T = ends[-1]
+    d = workloads.prefill_inputs(cfg, streams=streams, T=T)
+    label = f"pieces {ends} {name} {rule} {state_dtype} states"
+    say(f"prefill {label}: S={len(streams)} T={T} C={C} io={io}")
+    o, scheds, fin = gpu_prefill_pieces(d["q"], d["k"], d["v"], d["lam"], C, cfg.tau, io, ends,
+                                        merge_rule=rule, state_dtype=state_dtype)
+    r = oracle.run(d["q"], d["k"], d["v"], d["lam"], C, cfg.tau, nthreads=oracle_threads(), merge_rule=rule)
+    lo = 0
+    for hi, sc in zip(ends, scheds):
+        assert np.array_equal(sc["s"].view(np.uint32), r["s"][:, lo:hi].view(np.uint32)), f"{label}: s [{lo},{hi})"
+        assert np.array_equal(sc["boundary"], r["b"][:, lo:hi]), f"{label}: boundaries [{lo},{hi})"
+        assert np.array_equal(sc["m_t"], r["m_t"][:, lo:hi]), f"{label}: m_t [{lo},{hi})"
+        for i in range(len(streams)):
+            want = [(t - lo, e) for t, e in r["events"][i] if lo <= t < hi]
+            n = int(sc["n_ev"][i])
+            got = list(zip(sc["ev_t"][i, :n].tolist(), sc["ev_i"][i, :n].tolist()))
+            assert got == want, f"{label}: merges of piece [{lo},{hi}) stream {i}"
+        lo = hi
+    compare_outputs(o, r["o"], TOL[io], label)
+    assert np.array_equal(fin["m"], r["fin_m"])
+    tol = STATE_TOL_BF16_STORAGE if state_dtype == "bf16" else 1e-4
+    for i in range(len(streams)):
+        m = int(r["fin_m"][i])
+        assert fin["start"][i, :m].tolist() == r["fin_start"][i, :m].tolist(), f"{label}: starts ({i})"
+        assert fin["info"][i, :m].tolist() == r["fin_I"][i, :m].tolist(), f"{label}: information ({i})"
+        assert fin["count"][i, :m].tolist() == r["fin_n"][i, :m].tolist(), f"{label}: counts ({i})"
+        assert int(fin["t_seen"][i]) == T
+        assert mat_rel_err(fin["S"][i, :m], r["fin_S"][i, :m]) <= tol, f"{label}: states ({i})"
+    say(f"prefill {label}: ok, merges {int(r['n_ev'].sum())}")
 
 
 def test_literal_noise_reading_every_token_opens(prefill_path):

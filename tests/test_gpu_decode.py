@@ -102,6 +102,50 @@ def test_prefill_then_decode_equals_one_prefill(name, io, T, j, means, rule, sdt
     say(f"decode equivalence {name}: ok")
 
 
+@pytest.mark.parametrize("sdt", ["f32", "bf16"])
+@pytest.mark.parametrize("rule", ["sum", "density"])
+def test_prefill_decode_prefill_is_one_stream(rule, sdt):
+    """Prefill, decode steps, then another prefill on the same cache: the
+    outputs and final cache equal one pass over all the tokens (oracle)."""
+    torch = torch_mod()
+    import dynamic_state_memory_amd as dla
+    cfg = dataclasses.replace(workloads.CONFIGS["long_t131k_bf16"], C=16, seg_means=(7,))
+    T1, T2, T3 = 330, 57, 401
+    T = T1 + T2 + T3
+    d = workloads.prefill_inputs(cfg, streams=[0, 1, 2], T=T)
+    S = 3
+    say(f"prefill {T1} + decode {T2} + prefill {T3} ({rule} rule, {sdt} states)")
+    r = oracle.run(d["q"], d["k"], d["v"], d["lam"], cfg.C, cfg.tau, nthreads=oracle_threads(), merge_rule=rule)
+    dev = torch.device("cuda:0")
+    cache = dla.Cache(1, S, cfg.C, cfg.dk, cfg.dv, device=dev, merge_rule=rule, state_dtype=sdt)
+
+    def up(a, lo, hi, d_):
+        return torch.from_numpy(np.ascontiguousarray(a[:, lo:hi])).to(dev).to(torch.bfloat16).reshape(1, S, hi - lo, d_)
+
+    def pre(lo, hi):
+        o = dla.prefill(up(d["q"], lo, hi, cfg.dk), up(d["k"], lo, hi, cfg.dk), up(d["v"], lo, hi, cfg.dv),
+                        up(d["lam"], lo, hi, cfg.C), cfg.tau, cache)
+        torch.cuda.synchronize()
+        return o.float().cpu().numpy().reshape(S, hi - lo, cfg.dv)
+
+    o1 = pre(0, T1)
+    o2, _ = _decode_steps(cache, d["q"][:, T1:T1 + T2], d["k"][:, T1:T1 + T2], d["v"][:, T1:T1 + T2],
+                          d["lam"][:, T1:T1 + T2], cfg.tau, "bf16", 1, S)
+    o3 = pre(T1 + T2, T)
+    compare_outputs(np.concatenate([o1, o2, o3], 1), r["o"], TOL["bf16"], "prefill-decode-prefill")
+    fin = cache.read()
+    assert np.array_equal(fin["m"], r["fin_m"]) and np.array_equal(fin["t_seen"], r["fin_t_seen"])
+    tol = STATE_TOL_BF16_STORAGE if sdt == "bf16" else 1e-4
+    for i in range(S):
+        m = int(r["fin_m"][i])
+        assert fin["start"][i, :m].tolist() == r["fin_start"][i, :m].tolist()
+        assert fin["info"][i, :m].tolist() == r["fin_I"][i, :m].tolist()
+        assert fin["count"][i, :m].tolist() == r["fin_n"][i, :m].tolist()
+        assert mat_rel_err(fin["S"][i, :m], r["fin_S"][i, :m]) <= tol
+    assert r["n_ev"].min() > 0
+    say("prefill-decode-prefill: ok")
+
+
 def _decode_workload(n_unique, steps, B, H):
     """The batched-decode workload: n_unique distinct caches tiled over B*H."""
     d = workloads.decode_inputs(caches=range(n_unique), steps=steps)

@@ -24,7 +24,14 @@ Also reported on the same line:
   decode_bf16_states
                 the same decode on caches storing closed states as bf16 (the
                 most recent one stays fp32), with its algorithmic bytes
-                (--no-bf16-states skips it).
+                (--no-bf16-states skips it);
+  prefill_fenwick_schedule
+                the same prefill under the Log-Linear fixed schedule (Fenwick
+                buckets, lam = the first 16 columns, one weight per level),
+                the comparison the pages draw between the two methods; its
+                algorithmic flops count 2 (popcount(t) + 2) d_k d_v per
+                token-head, the buckets read plus the update (--no-fenwick
+                skips it).
 
 roofline.traffic is the kernel's HBM bytes per launch from the hardware
 counters FETCH_SIZE and WRITE_SIZE (two rocprofv3 --pmc passes over this
@@ -168,6 +175,9 @@ def prefill_bench(args, torch, dla, workloads):
         log(f"prefill, density merge rule: {d_ms:.3f} ms/step, chunk kernel {d_kern:.3f} ms, "
             f"{100 * d_ach / PEAK_BF16_TFLOPS:.1f}% of bf16 peak, mean live states "
             f"{d_stats['mean_live_states']:.2f}, merges/stream {d_stats['merges_per_stream']:.1f}")
+    fenwick = None
+    if not args.no_fenwick:
+        fenwick = fenwick_leg(args, torch, dla, cfg, q, k, v, lam, o, ws, ms_per_step)
     kernel = dla.dla_prefill_kernel(dla.DLA_BF16 if cfg.io == "bf16" else dla.DLA_F32, B, H, C, dk, dv)
     traffic = measured_traffic(f"{_kernel_file(kernel)}_{args.workload}_hbm_traffic.txt", kernel)
     res = dict(
@@ -181,6 +191,7 @@ def prefill_bench(args, torch, dla, workloads):
         schedule=stats,
         token_heads_per_s=BH * T / (ms_per_step * 1e-3),
         density_rule=density,
+        fenwick=fenwick,
     )
     log(f"prefill: {ms_per_step:.3f} ms/step, chunk kernel {kern_avg:.3f} ms, "
         f"{achieved:.1f} TFLOP/s algorithmic ({100 * achieved / PEAK_BF16_TFLOPS:.1f}% of bf16 peak), "
@@ -188,6 +199,43 @@ def prefill_bench(args, torch, dla, workloads):
     del q, k, v, lam, o, ws
     torch.cuda.empty_cache()
     return res, sample, cfg
+
+
+def fenwick_leg(args, torch, dla, cfg, q, k, v, lam, o, ws, dla_ms):
+    """The same tokens under the Log-Linear fixed schedule: L = bit_length(T-1)+1
+    level weights (the first L columns of the workload's lam), a cache of C = L
+    slots.  Every such prefill starts afresh, so no reset is needed."""
+    B, H, T, dk, dv = cfg.B, cfg.H, cfg.T, cfg.dk, cfg.dv
+    L = (T - 1).bit_length() + 1
+    lamL = lam[..., :L].contiguous()
+    cache = dla.Cache(B, H, L, dk, dv, device=q.device, merge_rule="fenwick")
+    for _ in range(max(args.warmup, 1)):
+        dla.prefill(q, k, v, lamL, 0.0, cache, o=o, workspace=ws)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, b in evs:
+        a.record()
+        b.record()
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for a, b in evs:
+        dla.dla_set_prefill_events(a.cuda_event, b.cuda_event)
+        dla.prefill(q, k, v, lamL, 0.0, cache, o=o, workspace=ws)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - w0) * 1e3 / args.steps
+    dla.dla_set_prefill_events(None, None)
+    kern = sum(a.elapsed_time(b) for a, b in evs) / len(evs)
+    read = sum(bin(t).count("1") + 1 for t in range(T))        # buckets read per stream
+    flops = 2.0 * B * H * (read + T) * dk * dv
+    ach = flops / (kern * 1e-3) / 1e12
+    kernel = dla.dla_prefill_kernel(dla.DLA_BF16, B, H, L, dk, dv)
+    log(f"prefill, Log-Linear fixed schedule (C = L = {L}): {ms:.3f} ms/step, chunk kernel {kern:.3f} ms, "
+        f"{100 * ach / PEAK_BF16_TFLOPS:.1f}% of bf16 peak, buckets read per token {read / T:.2f}, "
+        f"DLA/Log-Linear time {dla_ms / ms:.2f}")
+    del cache
+    return dict(schedule="Log-Linear fixed (Fenwick)", value=B * T / (ms * 1e-3), unit="tokens/s",
+                ms_per_step=ms, kernel=kernel, kernel_ms=kern, C=L, achieved=ach, unit_achieved="TFLOP/s",
+                frac=ach / PEAK_BF16_TFLOPS, algorithmic_flop_per_launch=flops,
+                buckets_read_per_token=read / T, dla_over_fenwick_time=dla_ms / ms)
 
 
 def decode_inputs_device(torch, cfg, steps, dev):
@@ -374,6 +422,8 @@ def main():
                     help="skip the second decode measurement on a cache with bf16 closed states")
     ap.add_argument("--no-density", action="store_true",
                     help="skip the second prefill measurement under the information-density merge rule")
+    ap.add_argument("--no-fenwick", action="store_true",
+                    help="skip the prefill measurement under the Log-Linear fixed schedule")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--cpu-streams", type=int, default=16)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -410,6 +460,7 @@ def main():
         "token_heads_per_s": pre["token_heads_per_s"],
         "prefill_density_merge_rule": pre["density_rule"],
         "decode_bf16_states": dec_bf,
+        "prefill_fenwick_schedule": pre["fenwick"],
     }
     print(json.dumps(out), flush=True)
 

@@ -24,8 +24,8 @@ __all__ = [
 
 DLA_OK, DLA_ERR_ARG, DLA_ERR_UNSUPPORTED, DLA_ERR_WORKSPACE, DLA_ERR_HIP = 0, 1, 2, 3, 4
 DLA_F32, DLA_BF16 = 0, 1
-DLA_MERGE_SUM, DLA_MERGE_DENSITY = 0, 1
-MERGE_RULES = {"sum": DLA_MERGE_SUM, "density": DLA_MERGE_DENSITY}
+DLA_MERGE_SUM, DLA_MERGE_DENSITY, DLA_FENWICK = 0, 1, 2
+MERGE_RULES = {"sum": DLA_MERGE_SUM, "density": DLA_MERGE_DENSITY, "fenwick": DLA_FENWICK}
 DLA_MAX_C = 64
 DLA_CHUNK = 64
 
@@ -221,7 +221,9 @@ class Cache:
     """A device cache for B*H streams (torch uint8 buffer + dla_cache view).
 
     ``merge_rule``: "sum" (smallest summed information, the default) or
-    "density" (lowest information density) for the capacity merges.
+    "density" (lowest information density) for the capacity merges, or
+    "fenwick" for the Log-Linear fixed schedule (prefill only: lam weights
+    levels, C >= bit_length(T - 1) + 1, every prefill starts afresh).
     ``state_dtype``: "f32" (every state float32) or "bf16" (closed states
     bfloat16, the most recent one float32)."""
 

@@ -36,6 +36,8 @@ dla_status ok()
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+int bit_length(int64_t x) { int n = 0; for (; x > 0; x >>= 1) ++n; return n; }
+
 // Shape check shared by every entry point.  Returns DLA_OK or a status and message.
 dla_status check_shape(int32_t B, int32_t H, int32_t C, int32_t dk, int32_t dv)
 {
@@ -130,7 +132,7 @@ dla_status check_cache(const dla_cache *c)
     if (!valid_state_dtype(c->state_dtype)) return fail(DLA_ERR_ARG, "unknown state dtype %d", c->state_dtype);
     if (c->bytes < dla_cache_bytes(c->B, c->H, c->C, c->d_k, c->d_v, static_cast<dla_dtype>(c->state_dtype)))
         return fail(DLA_ERR_ARG, "cache buffer too small (%llu bytes)", static_cast<unsigned long long>(c->bytes));
-    if (c->merge_rule != DLA_MERGE_SUM && c->merge_rule != DLA_MERGE_DENSITY)
+    if (c->merge_rule != DLA_MERGE_SUM && c->merge_rule != DLA_MERGE_DENSITY && c->merge_rule != DLA_FENWICK)
         return fail(DLA_ERR_ARG, "unknown merge rule %d", c->merge_rule);
     return DLA_OK;
 }
@@ -282,7 +284,7 @@ dla_status dla_cache_init(dla_cache *cache, void *base, uint64_t bytes, int32_t 
 dla_status dla_cache_set_merge_rule(dla_cache *cache, int32_t rule)
 {
     if (!cache) return fail(DLA_ERR_ARG, "cache is NULL");
-    if (rule != DLA_MERGE_SUM && rule != DLA_MERGE_DENSITY)
+    if (rule != DLA_MERGE_SUM && rule != DLA_MERGE_DENSITY && rule != DLA_FENWICK)
         return fail(DLA_ERR_ARG, "unknown merge rule %d", rule);
     cache->merge_rule = rule;
     return ok();
@@ -335,6 +337,23 @@ dla_status dla_prefill(const void *q, const void *k, const void *v, const void *
     if (a.g.state_bf16 && !a.register_resident)
         return fail(DLA_ERR_UNSUPPORTED, "bfloat16 state storage needs bfloat16 io and C <= 32 "
                                          "(the register-resident prefill)");
+    if (a.merge_rule == DLA_FENWICK) {
+        const int levels = bit_length(T - 1) + 1;
+        if (cache->C < levels)
+            return fail(DLA_ERR_ARG, "the fixed schedule over %d tokens needs C >= %d levels (C = %d)", T, levels,
+                        cache->C);
+        if (!a.register_resident)
+            return fail(DLA_ERR_UNSUPPORTED, "the fixed schedule needs bfloat16 io and C <= 32 "
+                                             "(the register-resident prefill)");
+        // every bucket is built by a cascade of merges, and with bf16 storage
+        // each one re-rounds the closed values it reads: about one rounding per
+        // carry level, past the bf16 output gate already at T ~ 1500
+        if (a.g.state_bf16)
+            return fail(DLA_ERR_UNSUPPORTED, "the fixed schedule needs float32 state storage");
+        if (sched && (sched->s || sched->boundary || sched->seg_id || sched->m_t || sched->ev_t || sched->ev_i ||
+                      sched->n_ev))
+            return fail(DLA_ERR_UNSUPPORTED, "no schedule export for the fixed schedule");
+    }
     const CacheOffsets co = cache_offsets(BH, cache->C, cache->d_k, cache->d_v, a.g.state_bf16);
     uint8_t *b8 = static_cast<uint8_t *>(cache->base);
     a.states = reinterpret_cast<float *>(b8 + co.states);
@@ -383,6 +402,8 @@ dla_status dla_decode_step(const void *q, const void *k, const void *v, const vo
         return fail(DLA_ERR_ARG, "q, k, v, lam and o must be 16-byte aligned");
     if (io != DLA_F32 && io != DLA_BF16) return fail(DLA_ERR_ARG, "unknown io dtype %d", static_cast<int>(io));
     if (cache->d_k != cache->d_v) return fail(DLA_ERR_UNSUPPORTED, "decode needs d_k == d_v");
+    if (cache->merge_rule == DLA_FENWICK)
+        return fail(DLA_ERR_UNSUPPORTED, "the fixed schedule is prefill only");
     if (tau != tau) return fail(DLA_ERR_ARG, "tau is NaN");
     DecodeArgs a;
     a.q = q; a.k = k; a.v = v; a.lam = lam; a.o = o;

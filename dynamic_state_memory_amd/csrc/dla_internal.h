@@ -91,7 +91,7 @@ struct PrefillArgs {
     int T;
     float tau;
     int io_bf16;
-    int merge_rule;                   // DLA_MERGE_SUM or DLA_MERGE_DENSITY
+    int merge_rule;                   // DLA_MERGE_SUM, DLA_MERGE_DENSITY or DLA_FENWICK
     int dvt;
     CacheGeom g;
     float *states;                    // slots (bf16 data when g.state_bf16)

@@ -385,6 +385,132 @@ __global__ void k_store_kprev(const TIO *__restrict__ K, int T, int dk, uint8_t 
     for (int i = threadIdx.x; i < dk; i += blockDim.x) kp[i] = to_f(src[i]);
 }
 
+// ------------------------------------------------------------ Log-Linear fixed schedule
+//
+// The Log-Linear form quoted in "Dynamic Linear Attention | Chlience Paper
+// Archive", section 2: the prefix seen by query t is split into Fenwick-tree
+// buckets and o_t = sum_l lam_t^(l) S_t^(l) q_t.  Reading: the token itself is
+// level 0 and the rest of the prefix is the binary decomposition of t, oldest
+// (largest) bucket first; key s < t is at level 1 + (highest bit in which s
+// and t differ).
+//
+// The chunk kernels see this schedule as chunk-level events in the greedy
+// scan's encoding.  Within a chunk the reads take their weights from the
+// pre-pass (a formula of the positions), so the events only have to say what
+// the states are at each chunk end: whole chunks, each piece inside one
+// bucket of every later token.  A chunk with an even index opens a state at
+// its first token and merges the older pieces that have become one bucket
+// (several events on one token: one boundary, several merges); a chunk with
+// an odd index joins the state of the chunk before it (no event).  The last
+// chunk leaves the buckets of the whole prefix: a full last chunk with an odd
+// index opens a state and merges it and the carried pieces away; a partial one
+// opens a state at the start of each of its buckets.
+
+// Pieces live at the start of chunk c (before its events).
+__device__ __forceinline__ int fen_m0(int c) { return c == 0 ? 0 : __popc((c & 1) ? c : c - 1); }
+
+// Events of chunk c, written at ev when ev is not NULL; returns their number.
+__device__ int fen_chunk_events(int c, int T, int NCH, int2 *ev)
+{
+    const int c0 = c * kChunk, n = min(kChunk, T - c0), m0 = fen_m0(c);
+    const bool last = c == NCH - 1;
+    int cnt = 0;
+    auto put = [&](int p, int d) {
+        if (ev) ev[cnt] = make_int2(p, d);
+        ++cnt;
+    };
+    if (last && n == kChunk && (c & 1)) {
+        // the chunk and the z pieces it completes become one bucket
+        const int z = __ffs(c + 1) - 1;
+        for (int d = m0 - z + 1; d < m0; ++d) put(c0, d);
+        put(c0, 64);
+        return cnt;
+    }
+    if ((c & 1) && !(last && n < kChunk)) return 0;
+    if (c >= 2 && !(c & 1)) {
+        // the z most recent pieces (a chunk pair and its carries) are one bucket now
+        const int z = __ffs(c) - 1;
+        for (int d = m0 - z + 1; d < m0; ++d) put(c0, d);
+    }
+    if (cnt == 0) put(c0, -1);
+    if (last && n < kChunk) {
+        int p = 0;
+        for (int b = 5; b >= 0; --b)
+            if ((n >> b) & 1) {
+                if (p > 0) put(c0 + p, -1);
+                p += 1 << b;
+            }
+    }
+    return cnt;
+}
+
+// One block per stream: the events and per-chunk event offsets of the whole
+// stream (a block-wide scan over the chunks), and the metadata of the final
+// cache, the buckets of [0, T).  A call with this schedule starts the stream
+// afresh: nothing the cache held before is kept.
+__global__ __launch_bounds__(256) void k_fenwick_schedule(int T, int NCH, int dk, int2 *__restrict__ events,
+                                                          int32_t *__restrict__ chunk_ev,
+                                                          uint8_t *__restrict__ meta_base, size_t meta_stride,
+                                                          int32_t *__restrict__ init_m_out,
+                                                          uint8_t *__restrict__ init_order_out)
+{
+    const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    __shared__ int wsum[4];
+    int carry = 0;
+    for (int base = 0; base < NCH; base += 256) {
+        const int c = base + tid;
+        const int cnt = c < NCH ? fen_chunk_events(c, T, NCH, nullptr) : 0;
+        int x = cnt;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int y = __shfl_up(x, off);
+            if (lane >= off) x += y;
+        }
+        if (lane == 63) wsum[wave] = x;
+        __syncthreads();
+        int before = carry;
+        for (int w = 0; w < wave; ++w) before += wsum[w];
+        const int total = carry + wsum[0] + wsum[1] + wsum[2] + wsum[3];
+        if (c < NCH) {
+            const int e0 = before + x - cnt;
+            chunk_ev[static_cast<size_t>(bh) * (NCH + 1) + c] = e0;
+            fen_chunk_events(c, T, NCH, events + static_cast<size_t>(bh) * T + e0);
+        }
+        __syncthreads();
+        carry = total;
+    }
+    if (tid == 0) chunk_ev[static_cast<size_t>(bh) * (NCH + 1) + NCH] = carry;
+
+    uint8_t *meta = meta_base + static_cast<size_t>(bh) * meta_stride;
+    if (tid < kMaxC) {
+        // bucket tid: the tid-th set bit of T from the top
+        int64_t st = 0, cnt = 0;
+        int seen = 0;
+        for (int b = 30; b >= 0; --b)
+            if ((T >> b) & 1) {
+                if (seen == tid) cnt = 1ll << b;
+                if (seen < tid) st += 1ll << b;
+                ++seen;
+            }
+        if (tid >= seen) st = 0;
+        reinterpret_cast<int64_t *>(meta + kOffInfo)[tid] = 0;
+        reinterpret_cast<int32_t *>(meta + kOffCount)[tid] = static_cast<int32_t>(cnt);
+        reinterpret_cast<int64_t *>(meta + kOffStart)[tid] = st;
+        init_order_out[static_cast<size_t>(bh) * kMaxC + tid] = 0xFF;
+    }
+    for (int i = tid; i < dk; i += blockDim.x) reinterpret_cast<float *>(meta + kOffKprev)[i] = 0.0f;
+    if (tid == 0) {
+        MetaHead *head = reinterpret_cast<MetaHead *>(meta);
+        head->m = __popc(T);
+        head->has_prev = 0;
+        head->s_prev = 0.0f;
+        head->pad0 = 0;
+        head->t_seen = T;
+        head->pad1 = 0;
+        init_m_out[bh] = 0;
+    }
+}
+
 // ------------------------------------------------------------ prefill
 
 template <typename TIO, int DK, int DVT>
@@ -1184,8 +1310,15 @@ static hipError_t prefill_typed(const PrefillArgs &a, hipStream_t stream)
 
 static hipError_t prefill_register_resident(const PrefillArgs &a, hipStream_t stream)
 {
-    hipError_t e = a.g.dk == 128 ? prefill_schedule<__bf16, 128>(a, stream)
-                                 : prefill_schedule<__bf16, 64>(a, stream);
+    hipError_t e;
+    if (a.merge_rule == DLA_FENWICK) {
+        const int NCH = (a.T + kChunk - 1) / kChunk;
+        hipLaunchKernelGGL(k_fenwick_schedule, dim3(a.g.B * a.g.H), dim3(256), 0, stream, a.T, NCH, a.g.dk,
+                           a.ws.events, a.ws.chunk_ev, a.meta, a.g.meta_stride, a.ws.init_m, a.ws.init_order);
+        e = hipGetLastError();
+    } else {
+        e = a.g.dk == 128 ? prefill_schedule<__bf16, 128>(a, stream) : prefill_schedule<__bf16, 64>(a, stream);
+    }
     if (e != hipSuccess) return e;
     return launch_prefill_rs(a, stream);
 }

@@ -84,7 +84,11 @@ __device__ __forceinline__ int refresh_active(const floatx4 (&am)[NTV][2], Frag<
 
 // ------------------------------------------------------------ chunk pre-pass
 
-template <int DK>
+// FEN: the Log-Linear fixed schedule (the schedule kernel's chunk events);
+// key s is read by query t with lam_t[level], level 0 for s = t and
+// 1 + (highest bit in which s and t differ) otherwise, the same for every key
+// of a piece live at the chunk start.
+template <int DK, bool FEN>
 __global__ __launch_bounds__(256) void k_chunk_prep(
     const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, const __bf16 *__restrict__ LAM, int T, int C,
     const int2 *__restrict__ events, const int32_t *__restrict__ chunk_ev, uint8_t *__restrict__ rec,
@@ -148,13 +152,13 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
     const int nev = chunk_ev[static_cast<size_t>(bh) * (NCH + 1) + ch + 1] - e0;
     // states live at the chunk start: those the cache held when the call
     // started, plus one per boundary before the chunk, capped at C by the merges
-    const int m0 = min(C, init_m[bh] + e0);
-    if (tid < nev) evs[tid] = events[tok0 + e0 + tid];
+    const int m0 = FEN ? (ch == 0 ? 0 : __popc((ch & 1) ? ch : ch - 1)) : min(C, init_m[bh] + e0);
+    if (!FEN && tid < nev) evs[tid] = events[tok0 + e0 + tid];
     qmax = wave_max(qmax);
     if (lane == 0) red[wave] = qmax;
     __syncthreads();
     const int qexp = f16_exponent(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
-    if (tid < kChunk) {
+    if (!FEN && tid < kChunk) {
         // bit i of o: the state with chronological index i at the chunk start
         // is live after token tid; bit p of m: the state opened at chunk
         // position p is live after token tid
@@ -221,7 +225,10 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
                 const int t = 16 * w + 4 * lg + r;
                 const int s = 16 * nt + lr;
                 float val = 0.0f;
-                if (s <= t) val = A[r] * static_cast<float>(lam[t][__popcll(shr64(nm[t], s + 1))]);
+                if (s <= t) {
+                    const int col = FEN ? (s == t ? 0 : 32 - __clz(t ^ s)) : __popcll(shr64(nm[t], s + 1));
+                    val = A[r] * static_cast<float>(lam[t][col]);
+                }
                 pw[t][s] = static_cast<__bf16>(val);
             }
         }
@@ -243,7 +250,23 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
         const int idx = tid + 256 * j;
         const int t = idx & (kChunk - 1), i = idx / kChunk;
         float w = 0.0f;
-        if (i < m0) w = ldexpf(static_cast<float>(lam[t][__popcll(shr64(om[t], i + 1)) + __popcll(nm[t])]), qexp);
+        if (FEN && i < m0 && t < nvalid) {
+            // (rows past the stream's end keep weight 0: their level could
+            // exceed the last column)
+            // piece i: the bucket of the i-th set bit (from the top) of the
+            // chunk count it was formed for; its first chunk has the bits above
+            const int cp = (ch & 1) ? ch : ch - 1;
+            int seen = 0, first = 0;
+            for (int b = 30; b >= 0; --b)
+                if ((cp >> b) & 1) {
+                    if (seen == i) first = cp & ~((2 << b) - 1);
+                    ++seen;
+                }
+            const int col = 32 - __clz((c0 + t) ^ (first * kChunk));
+            w = ldexpf(static_cast<float>(lam[t][col]), qexp);
+        } else if (i < m0) {
+            w = ldexpf(static_cast<float>(lam[t][__popcll(shr64(om[t], i + 1)) + __popcll(nm[t])]), qexp);
+        }
         wrow[i * kChunk + (t % 16) * (kChunk / 16) + t / 16] = static_cast<__bf16>(w);
     }
 }
@@ -1142,10 +1165,14 @@ static hipError_t launch_rs(const PrefillArgs &a, hipStream_t stream)
     const int BH = a.g.B * a.g.H;
     const int nblk_dv = a.g.dv / DVT;
     const int NCH = (a.T + kChunk - 1) / kChunk;
-    hipLaunchKernelGGL((k_chunk_prep<DK>), dim3(NCH, BH), dim3(256), 0, stream,
-                       static_cast<const __bf16 *>(a.q), static_cast<const __bf16 *>(a.k),
-                       static_cast<const __bf16 *>(a.lam), a.T, a.g.C, a.ws.events, a.ws.chunk_ev,
-                       static_cast<uint8_t *>(a.ws.rec), a.sched.m_t, a.ws.init_m);
+#define DLA_PREP_LAUNCH(FEN_)                                                                               \
+    hipLaunchKernelGGL((k_chunk_prep<DK, FEN_>), dim3(NCH, BH), dim3(256), 0, stream,                      \
+                       static_cast<const __bf16 *>(a.q), static_cast<const __bf16 *>(a.k),                  \
+                       static_cast<const __bf16 *>(a.lam), a.T, a.g.C, a.ws.events, a.ws.chunk_ev,          \
+                       static_cast<uint8_t *>(a.ws.rec), a.sched.m_t, a.ws.init_m)
+    if (a.merge_rule == DLA_FENWICK) DLA_PREP_LAUNCH(true);
+    else DLA_PREP_LAUNCH(false);
+#undef DLA_PREP_LAUNCH
     hipError_t e0 = hipGetLastError();
     if (e0 != hipSuccess) return e0;
     if (a.ev_before) {

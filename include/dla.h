@@ -34,6 +34,20 @@
  *   - o_t is read after the update and any merge;
  *   - lam is indexed by cache slot, slot 0 = most recent state.
  *
+ * The Log-Linear fixed schedule (a cache set to DLA_FENWICK).  The reading
+ * notes quote Log-Linear Attention in section 2 as the multi-state method
+ * whose buckets come from a Fenwick-tree decomposition of the prefix, with
+ * o_t = sum_l lam_t^(l) S_t^(l) q_t, and contrast it with DLA in section 5.4
+ * (buckets by position: recent tokens fine, old ones coarse).  The pages do
+ * not spell out the buckets; this library takes the binary decomposition:
+ *   - level 0 is token t itself; level l >= 1 is the bucket of the 2^(l-1)
+ *     earlier tokens that agree with t above bit l-1 and have bit l-1 clear
+ *     where t has it set (empty if bit l-1 of t is clear), i.e. key s < t
+ *     sits at level 1 + (highest bit in which s and t differ);
+ *   - lam_t[l] weights level l (not a slot), so lam needs
+ *     L(T) = bit_length(T - 1) + 1 columns: C >= L(T);
+ *   - no token information is computed and tau is ignored.
+ *
  * Conventions for every entry point
  *   - Pointers named as device pointers must point to device memory the
  *     caller allocated; the library never allocates, frees or synchronises.
@@ -56,7 +70,7 @@
 extern "C" {
 #endif
 
-#define DLA_ABI_VERSION 4
+#define DLA_ABI_VERSION 5
 #define DLA_MAX_C 64        /* largest supported cache capacity */
 #define DLA_CHUNK 64        /* tokens per prefill chunk */
 
@@ -76,7 +90,8 @@ typedef enum dla_dtype {
 /* Which adjacent pair a capacity merge joins. */
 typedef enum dla_merge_rule {
     DLA_MERGE_SUM = 0,       /* smallest summed information I_i + I_{i+1} (the default) */
-    DLA_MERGE_DENSITY = 1    /* lowest information density (I_i + I_{i+1}) / (n_i + n_{i+1}) */
+    DLA_MERGE_DENSITY = 1,   /* lowest information density (I_i + I_{i+1}) / (n_i + n_{i+1}) */
+    DLA_FENWICK = 2          /* the Log-Linear fixed schedule (dla_prefill), no information rule */
 } dla_merge_rule;
 
 /*
@@ -186,7 +201,8 @@ dla_status dla_cache_init(dla_cache *cache, void *base, uint64_t bytes, int32_t 
  * Merge rule of the cache's streams from the next prefill or decode call on:
  * DLA_MERGE_SUM or DLA_MERGE_DENSITY (reading notes "Dynamic Linear Attention
  * | Chlience Paper Archive", section 5.2: the pair of lowest information
- * density is merged).  Host only: it sets cache->merge_rule, which a caller
+ * density is merged), or DLA_FENWICK, the Log-Linear fixed schedule
+ * (sections 2 and 5.4; see the top of this header).  Host only: it sets cache->merge_rule, which a caller
  * may also set directly; prefill and decode reject any other value with
  * DLA_ERR_ARG.  DLA_ERR_ARG for a NULL cache or an unknown rule (the cache is
  * then unchanged).
@@ -217,6 +233,17 @@ uint64_t dla_prefill_workspace_bytes(int32_t B, int32_t H, int32_t T, int32_t C,
  * T must be in [1, 2^24].  A cache with bfloat16 state storage needs the
  * register-resident sweep (bfloat16 io, C <= 32); other prefills of such a
  * cache return DLA_ERR_UNSUPPORTED.
+ *
+ * With the cache's rule DLA_FENWICK the call follows the Log-Linear fixed
+ * schedule (top of this header) and starts every stream afresh at position 0:
+ * whatever the cache held is discarded.  lam[.][t][l] weights level l, and C
+ * must be at least bit_length(T - 1) + 1 (DLA_ERR_ARG otherwise).  Supported
+ * on the register-resident sweep only (bfloat16 io, C <= 32) and with float32
+ * state storage (each bucket is built by a cascade of merges, which bfloat16
+ * storage would round once per carry level); tau is ignored, and a sched with any non-NULL field returns DLA_ERR_UNSUPPORTED
+ * (the export describes the information schedule).  The final cache holds the
+ * buckets of the prefix [0, T), oldest first: popcount(T) states with their
+ * starts and counts, information 0, no previous key, t_seen = T.
  */
 dla_status dla_prefill(const void *q, const void *k, const void *v, const void *lam,
                        void *o, int32_t T, float tau, dla_dtype io, const dla_cache *cache,
@@ -236,7 +263,8 @@ const char *dla_prefill_kernel(dla_dtype io, int32_t B, int32_t H, int32_t C, in
 /*
  * Decode step: consume one token of every stream on top of the cache and
  * write o.  q, k [B*H][d_k]; v, o [B*H][d_v]; lam [B*H][C]; io dtype, device.
- * Supported: d_k = d_v = 128 or d_k = d_v = 64, any io dtype.
+ * Supported: d_k = d_v = 128 or d_k = d_v = 64, any io dtype.  A cache set to
+ * DLA_FENWICK returns DLA_ERR_UNSUPPORTED (the fixed schedule is prefill only).
  */
 dla_status dla_decode_step(const void *q, const void *k, const void *v, const void *lam,
                            void *o, float tau, dla_dtype io, const dla_cache *cache,

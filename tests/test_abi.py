@@ -23,7 +23,7 @@ def test_library_exports_every_declared_symbol():
     assert {"dla_prefill", "dla_decode_step", "dla_cache_init"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert dla.dla_abi_version() == 4
+    assert dla.dla_abi_version() == 5
 
 
 def test_sizes_and_layout():
@@ -142,7 +142,7 @@ def test_merge_rule_is_validated_on_the_host():
     assert dla.dla_cache.state_dtype.offset == 24 and dla.dla_cache.base.offset == 32
     c = _cache()
     assert c.merge_rule == dla.DLA_MERGE_SUM
-    assert dla.load().dla_cache_set_merge_rule(C.byref(c), 2) == dla.DLA_ERR_ARG
+    assert dla.load().dla_cache_set_merge_rule(C.byref(c), 3) == dla.DLA_ERR_ARG
     assert "merge rule" in dla.dla_last_error() and c.merge_rule == dla.DLA_MERGE_SUM
     assert dla.load().dla_cache_set_merge_rule(None, 1) == dla.DLA_ERR_ARG
     dla.dla_cache_set_merge_rule(c, dla.DLA_MERGE_DENSITY)
@@ -153,6 +153,39 @@ def test_merge_rule_is_validated_on_the_host():
     assert dla.dla_prefill(p, p, p, p, p, 100, 0.3, dla.DLA_F32, c, p, ws, None, None) == dla.DLA_ERR_ARG
     assert "merge rule" in dla.dla_last_error()
     assert dla.dla_decode_step(p, p, p, p, p, 0.3, dla.DLA_BF16, c, None, None) == dla.DLA_ERR_ARG
+
+
+def test_fenwick_rule_checks_on_the_host(monkeypatch):
+    monkeypatch.delenv("DLA_PREFILL_PATH", raising=False)
+    p = 0x100000
+    c = _cache()                      # C = 8: levels 0 .. 7, enough for T <= 128
+    dla.dla_cache_set_merge_rule(c, dla.DLA_FENWICK)
+    assert c.merge_rule == dla.DLA_FENWICK
+
+    def pre(T, io=dla.DLA_BF16, sched=None, cache=c):
+        ws = dla.dla_prefill_workspace_bytes(1, 1, T, 8, 64, 64)
+        return dla.dla_prefill(p, p, p, p, p, T, 0.3, io, cache, p, ws, sched, None)
+
+    # 129 tokens need 9 level weights
+    assert pre(129) == dla.DLA_ERR_ARG and "levels" in dla.dla_last_error()
+    # only on the register-resident sweep
+    assert pre(128, io=dla.DLA_F32) == dla.DLA_ERR_UNSUPPORTED
+    monkeypatch.setenv("DLA_PREFILL_PATH", "streamed")
+    assert pre(100) == dla.DLA_ERR_UNSUPPORTED
+    monkeypatch.delenv("DLA_PREFILL_PATH")
+    # float32 state storage only
+    cb = _cache()
+    cb.state_dtype = dla.DLA_BF16
+    cb.bytes = dla.dla_cache_bytes(1, 1, 8, 64, 64, dla.DLA_BF16)
+    dla.dla_cache_set_merge_rule(cb, dla.DLA_FENWICK)
+    assert pre(100, cache=cb) == dla.DLA_ERR_UNSUPPORTED and "float32 state" in dla.dla_last_error()
+    # no schedule export
+    sc = dla.dla_schedule_out()
+    sc.m_t = p
+    assert pre(100, sched=sc) == dla.DLA_ERR_UNSUPPORTED and "export" in dla.dla_last_error()
+    # prefill only
+    assert dla.dla_decode_step(p, p, p, p, p, 0.3, dla.DLA_BF16, c, None, None) == dla.DLA_ERR_UNSUPPORTED
+    assert "prefill only" in dla.dla_last_error()
 
 
 def test_gpu_package_never_imports_the_oracle():

@@ -1,0 +1,132 @@
+"""Parity of the Log-Linear fixed (Fenwick) schedule on the GPU with its oracle
+(oracle/fenwick.py): outputs within the bf16 gate, final cache -- the buckets
+of the prefix -- exact in its metadata and within the state gate in its
+matrices.  Inputs come from the seeded workload generator with lam holding one
+weight per level."""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import oracle.fenwick as FEN
+import workloads
+from tests.gpu_common import STATE_TOL, TOL, compare_outputs, say, torch_mod
+from tests.helpers import mat_rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(T, streams, C, dk=128, dv=64, base="gdn_1p3b_t32k_bf16"):
+    cfg = dataclasses.replace(workloads.CONFIGS[base], C=C, dk=dk, dv=dv)
+    return workloads.prefill_inputs(cfg, streams=streams, T=T)
+
+
+def _run(d, C, B=1, H=None, cache=None):
+    torch = torch_mod()
+    import dynamic_state_memory_amd as dla
+    q, k, v, lam = d["q"], d["k"], d["v"], d["lam"]
+    S, T, dk = k.shape
+    dv = v.shape[2]
+    H = S // B if H is None else H
+    dev = torch.device("cuda:0")
+
+    def up(a, n):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(torch.bfloat16).reshape(B, H, T, n)
+
+    if cache is None:
+        cache = dla.Cache(B, H, C, dk, dv, device=dev, merge_rule="fenwick")
+    ws = dla.prefill_workspace(B, H, T, C, dk, dv, dev)
+    o = dla.prefill(up(q, dk), up(k, dk), up(v, dv), up(lam, C), 0.0, cache, workspace=ws)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy().reshape(S, T, dv), cache.read()
+
+
+def _check_cache(fin, k, v, T, label, state_streams=None):
+    """Metadata of every stream exact; each state matrix (of the streams in
+    state_streams, default all) within the state gate."""
+    S = k.shape[0]
+    m = bin(T).count("1")
+    assert (fin["m"] == m).all(), f"{label}: live states {fin['m']} != popcount({T}) = {m}"
+    assert (fin["t_seen"] == T).all() and (fin["has_prev"] == 0).all(), label
+    C = fin["order"].shape[1]
+    bk = FEN.buckets(T)
+    for x in range(S):
+        assert list(fin["start"][x, :m]) == [a for a, _, _ in bk], f"{label}: starts of stream {x}"
+        assert list(fin["count"][x, :m]) == [n for _, n, _ in bk], f"{label}: counts of stream {x}"
+        assert (fin["info"][x, :m] == 0).all(), label
+        order = list(fin["order"][x, :m])
+        assert len(set(order)) == m and all(0 <= p < C for p in order), f"{label}: slots {order}"
+    for x in (range(S) if state_streams is None else state_streams):
+        ref = FEN.final_states(k[x:x + 1], v[x:x + 1], T)[0]
+        for i, (_, _, R) in enumerate(ref):
+            err = mat_rel_err(fin["S"][x, i], R)
+            assert err <= STATE_TOL, f"{label}: stream {x} state {i} rel err {err:.2e} > {STATE_TOL}"
+
+
+# T spans: a single token, partial first chunks, exact chunk multiples with
+# odd and even last chunks (the carried merges at the end), ragged tails after
+# odd and even chunks, and carries across 2, 4, 8 and 16 chunks
+TS = [1, 2, 5, 63, 64, 65, 127, 128, 129, 192, 256, 300, 511, 512, 513, 777, 1024, 1100, 2256, 4160]
+
+
+@pytest.mark.parametrize("T", TS)
+def test_fenwick_prefill_matches_oracle(T):
+    say(f"fenwick T={T}")
+    d = _inputs(T, [0, 1, 2], 16)
+    o, fin = _run(d, 16)
+    ref = FEN.outputs(d["q"], d["k"], d["v"], d["lam"])
+    compare_outputs(o, ref, TOL["bf16"], f"fenwick T={T}")
+    _check_cache(fin, d["k"], d["v"], T, f"fenwick T={T}")
+
+
+@pytest.mark.parametrize("dk,dv,C,T", [(64, 32, 8, 128), (64, 32, 12, 700), (128, 64, 32, 1500),
+                                       (64, 16, 32, 64 * 17 + 9), (128, 128, 13, 4096)])
+def test_fenwick_shapes_and_capacities(dk, dv, C, T):
+    say(f"fenwick dk={dk} dv={dv} C={C} T={T}")
+    d = _inputs(T, [3, 4], C, dk=dk, dv=dv)
+    o, fin = _run(d, C, B=2, H=1)
+    compare_outputs(o, FEN.outputs(d["q"], d["k"], d["v"], d["lam"]), TOL["bf16"], f"dk={dk} C={C} T={T}")
+    _check_cache(fin, d["k"], d["v"], T, f"dk={dk} C={C} T={T}")
+
+
+def test_fenwick_discards_what_the_cache_held():
+    """A prefill under the fixed schedule starts afresh: on a cache that an
+    information-driven prefill filled, it gives what it gives on an empty one,
+    bit for bit."""
+    torch = torch_mod()
+    import dynamic_state_memory_amd as dla
+    say("fenwick on a used cache")
+    T = 777
+    first = _inputs(500, [7, 8], 16)
+    d = _inputs(T, [9, 10], 16)
+    dev = torch.device("cuda:0")
+    used = dla.Cache(1, 2, 16, 128, 64, device=dev, merge_rule="sum")
+    _run(first, 16, cache=used)                   # an information-driven prefill
+    dla.dla_cache_set_merge_rule(used.view, dla.DLA_FENWICK)
+    o1, fin1 = _run(d, 16, cache=used)
+    o2, fin2 = _run(d, 16)
+    assert np.array_equal(o1, o2)
+    for key in ("m", "t_seen", "has_prev", "start", "count", "info"):
+        assert np.array_equal(fin1[key], fin2[key]), key
+    assert np.array_equal(fin1["S"], fin2["S"])
+
+
+def test_fenwick_full_size_sampled():
+    """The full Gated-DeltaNet-1.3B-shaped layer (B=2, H=16, T=32768, d_k=128,
+    d_v=256) with 16 level weights, in the benchmark's launch configuration:
+    outputs at sampled tokens of every stream within the bf16 gate, metadata of
+    every stream exact, the final state (one bucket of all 32768 tokens) of
+    four streams within the state gate."""
+    say("fenwick full size: generating inputs")
+    cfg = dataclasses.replace(workloads.CONFIGS["gdn_1p3b_t32k_bf16"], C=16)
+    d = workloads.prefill_inputs(cfg)
+    S, T = d["k"].shape[:2]
+    say("fenwick full size: GPU prefill")
+    o, fin = _run(d, 16, B=cfg.B, H=cfg.H)
+    rng = np.random.default_rng(7)
+    rows = sorted(set(rng.choice(T, 20, replace=False).tolist()) | {0, 1, 63, 64, 4095, 4096, 16383, T - 1})
+    say(f"fenwick full size: oracle rows ({len(rows)} per stream)")
+    ref = FEN.output_rows(d["q"], d["k"], d["v"], d["lam"], rows)
+    err = compare_outputs(o[:, rows], ref, TOL["bf16"], "fenwick full size")
+    _check_cache(fin, d["k"], d["v"], T, "fenwick full size", state_streams=[0, 9, 17, 31])
+    say(f"fenwick full size: ok, sampled max row rel err {err:.2e}")

@@ -31,7 +31,13 @@ Also reported on the same line:
                 the comparison the pages draw between the two methods; its
                 algorithmic flops count 2 (popcount(t) + 2) d_k d_v per
                 token-head, the buckets read plus the update (--no-fenwick
-                skips it).
+                skips it);
+  decode_fenwick_schedule
+                batched decode (B=256, H=16, d=128, C=32) under the same
+                schedule, from position 2^20 (the cache preloaded with the one
+                bucket of the first 2^20 tokens), with its algorithmic bytes:
+                the popcount(t) buckets read, the token's bucket written
+                (--no-fenwick skips it).
 
 roofline.traffic is the kernel's HBM bytes per launch from the hardware
 counters FETCH_SIZE and WRITE_SIZE (two rocprofv3 --pmc passes over this
@@ -365,6 +371,63 @@ def decode_bench(args, torch, dla, workloads, state_dtype="f32"):
     return res
 
 
+def fenwick_decode_bench(args, torch, dla, workloads):
+    """Batched decode under the Log-Linear fixed schedule: the decode workload's
+    shapes and token draws (lam = the level weights), caches preloaded with the
+    one bucket of positions [0, 2^20), then S + W steps from there."""
+    cfg = workloads.CONFIGS[args.decode_workload]
+    B, H, C, dk, dv = cfg.B, cfg.H, cfg.C, cfg.dk, cfg.dv
+    BH = B * H
+    dev = torch.device("cuda:0")
+    S, W = args.decode_steps, args.decode_warmup
+    t0 = 1 << 20
+    d = decode_inputs_device(torch, cfg, S + W, dev)
+    first = d.pop("states")[:, :1].contiguous()
+    cache = dla.Cache(B, H, C, dk, dv, device=dev, merge_rule="fenwick",
+                      preload=dict(m0=1, states=first, info=torch.zeros(BH, 1, dtype=torch.int64, device=dev),
+                                   count=torch.full((BH, 1), t0, dtype=torch.int32, device=dev),
+                                   start=torch.zeros(BH, 1, dtype=torch.int64, device=dev), t_seen=t0))
+    del first
+    torch.cuda.synchronize()
+    o = torch.empty(B, H, dv, dtype=torch.bfloat16, device=dev)
+
+    def step(j):
+        dla.decode_step(d["q"][j].view(B, H, dk), d["k"][j].view(B, H, dk), d["v"][j].view(B, H, dv),
+                        d["lam"][j].view(B, H, C), 0.0, cache, o=o)
+
+    for j in range(W):
+        step(j)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(S)]
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for i, (a, b) in enumerate(evs):
+        a.record()
+        step(W + i)
+        b.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    kern_avg = sum(a.elapsed_time(b) for a, b in evs) / S
+    # algorithmic bytes per stream-step at position t: the popcount(t) buckets
+    # read and the token's bucket written (fp32), the metadata read and
+    # written, q, k, v, lam in and o out (bf16)
+    m_sum = sum(bin(t0 + W + i).count("1") for i in range(S))
+    D2 = dk * dv
+    per_stream = 4 * D2 * (m_sum + S) + 2 * (96 * S + 20 * m_sum) + 2 * (2 * dk + dv + C + dv) * S
+    bytes_per_step = BH * per_stream / S
+    achieved = bytes_per_step / (kern_avg * 1e-3) / 1e9
+    res = dict(workload=f"{args.decode_workload}, Log-Linear fixed schedule from position 2^20",
+               B=B, H=H, d_k=dk, d_v=dv, C=C, steps=S, warmup=W, steps_per_s=S / wall,
+               ms_per_step=wall * 1e3 / S, tokens_per_s=BH * S / wall, mean_live_states=m_sum / S,
+               roofline=dict(bound="hbm", achieved=achieved, peak=PEAK_HBM_GBS, unit="GB/s",
+                             frac=achieved / PEAK_HBM_GBS, kernel="k_decode_fenwick", kernel_ms=kern_avg,
+                             algorithmic_bytes_per_launch=bytes_per_step))
+    log(f"decode, Log-Linear fixed schedule: {res['steps_per_s']:.1f} steps/s, kernel {kern_avg:.3f} ms, "
+        f"{achieved:.0f} GB/s algorithmic ({100 * achieved / PEAK_HBM_GBS:.1f}% of HBM peak), "
+        f"mean buckets read {m_sum / S:.2f}")
+    del d, cache
+    return res
+
+
 def _kernel_file(kernel: str) -> str:
     """k_prefill_rs<128,16,8> -> k_prefill_rs_128_16_8 (a file-name form)."""
     return kernel.replace("<", "_").replace(">", "").replace(",", "_")
@@ -450,6 +513,8 @@ def main():
     torch.cuda.empty_cache()
     dec_bf = None if (args.no_decode or args.no_bf16_states) else \
         decode_bench(args, torch, dla, workloads, state_dtype="bf16")
+    torch.cuda.empty_cache()
+    dec_fen = None if (args.no_decode or args.no_fenwick) else fenwick_decode_bench(args, torch, dla, workloads)
     cpu = None if args.no_cpu else cpu_baseline(args, sample, cfg)
     out = {
         "metric": METRIC, "value": pre["value"], "unit": "tokens/s", "n_gpus": 1,
@@ -461,6 +526,7 @@ def main():
         "prefill_density_merge_rule": pre["density_rule"],
         "decode_bf16_states": dec_bf,
         "prefill_fenwick_schedule": pre["fenwick"],
+        "decode_fenwick_schedule": dec_fen,
     }
     print(json.dumps(out), flush=True)
 

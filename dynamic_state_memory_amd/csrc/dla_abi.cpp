@@ -402,8 +402,12 @@ dla_status dla_decode_step(const void *q, const void *k, const void *v, const vo
         return fail(DLA_ERR_ARG, "q, k, v, lam and o must be 16-byte aligned");
     if (io != DLA_F32 && io != DLA_BF16) return fail(DLA_ERR_ARG, "unknown io dtype %d", static_cast<int>(io));
     if (cache->d_k != cache->d_v) return fail(DLA_ERR_UNSUPPORTED, "decode needs d_k == d_v");
-    if (cache->merge_rule == DLA_FENWICK)
-        return fail(DLA_ERR_UNSUPPORTED, "the fixed schedule is prefill only");
+    if (cache->merge_rule == DLA_FENWICK) {
+        if (cache->state_dtype != DLA_F32)
+            return fail(DLA_ERR_UNSUPPORTED, "the fixed schedule needs float32 state storage");
+        if (sched && (sched->s || sched->boundary || sched->m_t || sched->ev_i))
+            return fail(DLA_ERR_UNSUPPORTED, "no schedule export for the fixed schedule");
+    }
     if (tau != tau) return fail(DLA_ERR_ARG, "tau is NaN");
     DecodeArgs a;
     a.q = q; a.k = k; a.v = v; a.lam = lam; a.o = o;

@@ -1231,6 +1231,160 @@ __global__ __launch_bounds__(256) void k_decode(const TIO *__restrict__ Qg, cons
     if (tid < D) Og[static_cast<size_t>(bh) * D + tid] = from_f<TIO>(orow[tid] + sc_kq * vs[tid]);
 }
 
+// ------------------------------------------------------------ decode, fixed schedule
+//
+// One token of every stream under the Log-Linear fixed schedule (the Fenwick
+// buckets described at k_fenwick_schedule).  The cache holds the buckets of
+// [0, t), t = t_seen, oldest first.  Token t is read at level 0 and bucket i
+// at level 1 + (highest bit in which its start and t differ); then the token
+// joins the buckets its carry completes: with z trailing ones in t, the last
+// z buckets and the token become one bucket (z = 0: the token opens a state).
+// Each state is read once; the ones that merge are summed in registers on
+// the way and the sum is written once, into the slot of the oldest of them.
+// A stream at t >= 2^(C-1) would need a level weight the cache does not
+// have: its output row is NaN and its cache is left as it was.
+template <typename TIO, int D>
+__global__ __launch_bounds__(256) void k_decode_fenwick(const TIO *__restrict__ Qg, const TIO *__restrict__ Kg,
+                                                        const TIO *__restrict__ Vg, const TIO *__restrict__ Lg,
+                                                        TIO *__restrict__ Og, int C, float *__restrict__ states,
+                                                        uint8_t *__restrict__ meta_base, size_t meta_stride)
+{
+    constexpr int G = D / 4;          // threads per state row (float4 each)
+    constexpr int R = 256 / G;        // rows per pass
+    constexpr int P = D / R;          // passes per state
+    __shared__ float qs[D], ks[D], vs[D], lw[kMaxC];
+    __shared__ float wlog[kMaxC];
+    __shared__ int32_t order_s[kMaxC];
+    __shared__ double red[4];
+    __shared__ float orow[D];
+    __shared__ int32_t ctl[4];        // m, first merging index, destination slot, refused
+    __shared__ float sc_kq;
+
+    const int bh = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    uint8_t *meta = meta_base + static_cast<size_t>(bh) * meta_stride;
+    MetaHead *head = reinterpret_cast<MetaHead *>(meta);
+    uint8_t *order = meta + kOffOrder;
+    int64_t *info = reinterpret_cast<int64_t *>(meta + kOffInfo);
+    int32_t *count = reinterpret_cast<int32_t *>(meta + kOffCount);
+    int64_t *start = reinterpret_cast<int64_t *>(meta + kOffStart);
+
+    if (tid < D) {
+        qs[tid] = to_f(Qg[static_cast<size_t>(bh) * D + tid]);
+        ks[tid] = to_f(Kg[static_cast<size_t>(bh) * D + tid]);
+        vs[tid] = to_f(Vg[static_cast<size_t>(bh) * D + tid]);
+    }
+    if (tid < C) lw[tid] = to_f(Lg[static_cast<size_t>(bh) * C + tid]);
+    __syncthreads();
+    {
+        double kq = tid < D ? static_cast<double>(ks[tid]) * static_cast<double>(qs[tid]) : 0.0;
+        kq = wave_sum(kq);
+        if (lane == 0) red[wave] = kq;
+    }
+    __syncthreads();
+    if (wave == 0) {
+        const double kq = red[0] + red[1] + red[2] + red[3];
+        const int m = head->m;
+        const int64_t t = head->t_seen;
+        int32_t n = lane < m ? count[lane] : 0;
+        int64_t stt = lane < m ? start[lane] : 0;
+        int32_t ord = lane < m ? static_cast<int32_t>(order[lane]) : 0;
+        if (lane < m) {
+            const int lv = 64 - __clzll(static_cast<unsigned long long>(t ^ stt));
+            wlog[lane] = lv < C ? lw[lv] : 0.0f;
+            order_s[lane] = ord;
+        }
+        uint64_t usedmask = 0;
+        for (int i = 0; i < m; ++i) usedmask |= 1ull << __shfl(ord, i);
+        const int z = __ffsll(static_cast<unsigned long long>(~t)) - 1;       // trailing ones of t
+        const int first = z == 0 ? m : max(m - z, 0);
+        // (a cache that no fixed-schedule call left -- too many states for a
+        // new one -- is refused the same way, so no slot past C is written)
+        const bool refused = t >= (1ll << (C - 1)) || m > C || (first == m && m >= C);
+        int dst, m_new;
+        if (first == m) {
+            dst = __ffsll(static_cast<unsigned long long>(~usedmask)) - 1;  // lowest free slot
+            m_new = m + 1;
+            if (lane == m) { n = 1; stt = t; ord = dst; }
+        } else {
+            dst = __shfl(ord, first);
+            m_new = first + 1;
+            const int32_t tot = wave_sum<int32_t>(lane >= first && lane < m ? n : 0);
+            if (lane == first) n = tot + 1;
+        }
+        if (lane == 0) {
+            ctl[0] = m; ctl[1] = first; ctl[2] = dst; ctl[3] = refused;
+            sc_kq = static_cast<float>(kq) * lw[0];
+        }
+        if (!refused) {
+            if (lane < kMaxC) {
+                info[lane] = 0;
+                count[lane] = lane < m_new ? n : 0;
+                start[lane] = lane < m_new ? stt : 0;
+                order[lane] = static_cast<uint8_t>(lane < m_new ? ord : 0xFF);
+            }
+            if (lane == 0) {
+                head->m = m_new;
+                head->has_prev = 0;
+                head->s_prev = 0.0f;
+                head->t_seen = t + 1;
+            }
+        }
+    }
+    __syncthreads();
+    const int m = ctl[0], first = ctl[1], dst = ctl[2];
+    if (ctl[3]) {
+        if (tid < D) Og[static_cast<size_t>(bh) * D + tid] = from_f<TIO>(__builtin_nanf(""));
+        return;
+    }
+    const int col = (tid % G) * 4, row0 = tid / G;
+    const float4 q4 = *reinterpret_cast<const float4 *>(&qs[col]);
+    const float4 k4 = *reinterpret_cast<const float4 *>(&ks[col]);
+    float acc[P];
+    float4 sum[P];
+#pragma unroll
+    for (int j = 0; j < P; ++j) {
+        acc[j] = 0.0f;
+        const float vr = vs[row0 + R * j];
+        sum[j] = make_float4(vr * k4.x, vr * k4.y, vr * k4.z, vr * k4.w);
+    }
+    float *sb = states + static_cast<size_t>(bh) * C * D * D;
+    for (int i = 0; i < m; ++i) {
+        const int p = order_s[i];
+        const float w = wlog[i];
+        const floatx4 *sp = reinterpret_cast<const floatx4 *>(sb + static_cast<size_t>(p) * D * D);
+        float4 x[P];
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+            const floatx4 u = __builtin_nontemporal_load(sp + ((row0 + R * j) * D + col) / 4);
+            x[j] = make_float4(u[0], u[1], u[2], u[3]);
+        }
+#pragma unroll
+        for (int j = 0; j < P; ++j)
+            acc[j] += w * (x[j].x * q4.x + x[j].y * q4.y + x[j].z * q4.z + x[j].w * q4.w);
+        if (i >= first) {
+#pragma unroll
+            for (int j = 0; j < P; ++j) {
+                sum[j].x += x[j].x; sum[j].y += x[j].y; sum[j].z += x[j].z; sum[j].w += x[j].w;
+            }
+        }
+    }
+    // the token's bucket (its own slot was read above by the same threads)
+    floatx4 *dp = reinterpret_cast<floatx4 *>(sb + static_cast<size_t>(dst) * D * D);
+#pragma unroll
+    for (int j = 0; j < P; ++j)
+        __builtin_nontemporal_store(floatx4{sum[j].x, sum[j].y, sum[j].z, sum[j].w}, dp + ((row0 + R * j) * D + col) / 4);
+#pragma unroll
+    for (int j = 0; j < P; ++j) {
+        float x = acc[j];
+#pragma unroll
+        for (int off = G / 2; off > 0; off >>= 1) x += __shfl_xor(x, off);
+        if (tid % G == 0) orow[row0 + R * j] = x;
+    }
+    __syncthreads();
+    if (tid < D) Og[static_cast<size_t>(bh) * D + tid] = from_f<TIO>(orow[tid] + sc_kq * vs[tid]);
+}
+
 // ------------------------------------------------------------ launchers
 
 hipError_t launch_cache_init(float *states, float *active, uint8_t *meta, const CacheGeom &g,
@@ -1337,6 +1491,15 @@ static hipError_t decode_typed(const DecodeArgs &a, hipStream_t stream)
     const TIO *q = static_cast<const TIO *>(a.q), *k = static_cast<const TIO *>(a.k);
     const TIO *v = static_cast<const TIO *>(a.v), *l = static_cast<const TIO *>(a.lam);
     TIO *o = static_cast<TIO *>(a.o);
+    if (a.merge_rule == DLA_FENWICK) {
+        if (a.g.dk == 128)
+            hipLaunchKernelGGL((k_decode_fenwick<TIO, 128>), dim3(BH), dim3(256), 0, stream, q, k, v, l, o, a.g.C,
+                               a.states, a.meta, a.g.meta_stride);
+        else
+            hipLaunchKernelGGL((k_decode_fenwick<TIO, 64>), dim3(BH), dim3(256), 0, stream, q, k, v, l, o, a.g.C,
+                               a.states, a.meta, a.g.meta_stride);
+        return hipGetLastError();
+    }
 #define DLA_DECODE(D_, BF_)                                                                           \
     hipLaunchKernelGGL((k_decode<TIO, D_, BF_>), dim3(BH), dim3(256), 0, stream, q, k, v, l, o, a.tau, a.g.C, \
                        a.states, a.active, a.meta, a.g.meta_stride, a.sched, a.merge_rule)

@@ -46,7 +46,8 @@
  *     sits at level 1 + (highest bit in which s and t differ);
  *   - lam_t[l] weights level l (not a slot), so lam needs
  *     L(T) = bit_length(T - 1) + 1 columns: C >= L(T);
- *   - no token information is computed and tau is ignored.
+ *   - no token information is computed and tau is ignored;
+ *   - dla_prefill starts the streams afresh; dla_decode_step continues them.
  *
  * Conventions for every entry point
  *   - Pointers named as device pointers must point to device memory the
@@ -263,8 +264,18 @@ const char *dla_prefill_kernel(dla_dtype io, int32_t B, int32_t H, int32_t C, in
 /*
  * Decode step: consume one token of every stream on top of the cache and
  * write o.  q, k [B*H][d_k]; v, o [B*H][d_v]; lam [B*H][C]; io dtype, device.
- * Supported: d_k = d_v = 128 or d_k = d_v = 64, any io dtype.  A cache set to
- * DLA_FENWICK returns DLA_ERR_UNSUPPORTED (the fixed schedule is prefill only).
+ * Supported: d_k = d_v = 128 or d_k = d_v = 64, any io dtype.
+ *
+ * With the cache's rule DLA_FENWICK the step follows the Log-Linear fixed
+ * schedule (top of this header) on a cache that fixed-schedule calls left (or
+ * an empty one): token t = t_seen is read at level 0 and each bucket of
+ * [0, t) at its level, with lam[.][l] the weight of level l; then the token
+ * joins the buckets its carry completes (with z trailing ones in t, the last
+ * z buckets and the token become one state; z = 0 opens a state).  float32
+ * state storage only and no schedule export (DLA_ERR_UNSUPPORTED); tau is
+ * ignored.  A stream at t >= 2^(C-1) needs a level weight the cache does not
+ * have, and so does a cache no fixed-schedule call left that has no free
+ * slot: that stream's output row is NaN and its cache is left unchanged.
  */
 dla_status dla_decode_step(const void *q, const void *k, const void *v, const void *lam,
                            void *o, float tau, dla_dtype io, const dla_cache *cache,

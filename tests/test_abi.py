@@ -183,9 +183,13 @@ def test_fenwick_rule_checks_on_the_host(monkeypatch):
     sc = dla.dla_schedule_out()
     sc.m_t = p
     assert pre(100, sched=sc) == dla.DLA_ERR_UNSUPPORTED and "export" in dla.dla_last_error()
-    # prefill only
-    assert dla.dla_decode_step(p, p, p, p, p, 0.3, dla.DLA_BF16, c, None, None) == dla.DLA_ERR_UNSUPPORTED
-    assert "prefill only" in dla.dla_last_error()
+    # decode: float32 state storage and no schedule export either
+    c64 = _cache(dk=64, dv=64)
+    dla.dla_cache_set_merge_rule(c64, dla.DLA_FENWICK)
+    assert dla.dla_decode_step(p, p, p, p, p, 0.3, dla.DLA_BF16, c64, sc, None) == dla.DLA_ERR_UNSUPPORTED
+    assert "export" in dla.dla_last_error()
+    assert dla.dla_decode_step(p, p, p, p, p, 0.3, dla.DLA_BF16, cb, None, None) == dla.DLA_ERR_UNSUPPORTED
+    assert "float32 state" in dla.dla_last_error()
 
 
 def test_gpu_package_never_imports_the_oracle():

@@ -1,8 +1,9 @@
 """Parity of the Log-Linear fixed (Fenwick) schedule on the GPU with its oracle
-(oracle/fenwick.py): outputs within the bf16 gate, final cache -- the buckets
-of the prefix -- exact in its metadata and within the state gate in its
-matrices.  Inputs come from the seeded workload generator with lam holding one
-weight per level."""
+(oracle/fenwick.py): outputs within the gate of their io dtype, final cache --
+the buckets of the prefix -- exact in its metadata and within the state gate in
+its matrices.  A prefill followed by decode steps must give what the oracle
+gives over all the tokens at once.  Inputs come from the seeded workload
+generator with lam holding one weight per level."""
 import dataclasses
 
 import numpy as np
@@ -130,3 +131,63 @@ def test_fenwick_full_size_sampled():
     err = compare_outputs(o[:, rows], ref, TOL["bf16"], "fenwick full size")
     _check_cache(fin, d["k"], d["v"], T, "fenwick full size", state_streams=[0, 9, 17, 31])
     say(f"fenwick full size: ok, sampled max row rel err {err:.2e}")
+
+
+def _decode_steps(d, lo, hi, cache, io):
+    """Decode tokens lo .. hi-1 of every stream one dla_decode_step at a time."""
+    torch = torch_mod()
+    import dynamic_state_memory_amd as dla
+    B, H, C, dk, dv = cache.shape
+    dt = torch.bfloat16 if io == "bf16" else torch.float32
+    dev = cache.device
+    outs = []
+    for t in range(lo, hi):
+        def one(a, n):
+            return torch.from_numpy(np.ascontiguousarray(a[:, t])).to(dev).to(dt).reshape(B, H, n)
+        o = dla.decode_step(one(d["q"], dk), one(d["k"], dk), one(d["v"], dv), one(d["lam"], C), 0.0, cache)
+        outs.append(o.float().cpu().numpy().reshape(B * H, 1, dv))
+    torch.cuda.synchronize()
+    return np.concatenate(outs, 1) if outs else np.zeros((B * H, 0, dv), np.float32)
+
+
+@pytest.mark.parametrize("T0,k,dd,io", [(0, 70, 64, "f32"), (0, 40, 128, "bf16"), (1, 66, 128, "bf16"),
+                                        (64, 70, 64, "bf16"), (100, 60, 128, "bf16"), (255, 70, 64, "bf16"),
+                                        (512, 33, 128, "bf16"), (1000, 50, 64, "bf16")])
+def test_fenwick_decode_continues_the_stream(T0, k, dd, io):
+    """Prefill T0 tokens (none: decode from an empty cache), then k decode
+    steps: outputs and final cache as one pass of the oracle over T0 + k."""
+    torch = torch_mod()
+    import dynamic_state_memory_amd as dla
+    say(f"fenwick decode T0={T0} k={k} d={dd} io={io}")
+    T = T0 + k
+    d = _inputs(T, [11, 12], 16, dk=dd, dv=dd)
+    cache = dla.Cache(1, 2, 16, dd, dd, device=torch.device("cuda:0"), merge_rule="fenwick")
+    parts = []
+    if T0:
+        pre = {x: d[x][:, :T0] for x in ("q", "k", "v", "lam")}
+        o_pre, _ = _run(pre, 16, cache=cache)
+        parts.append(o_pre)
+    parts.append(_decode_steps(d, T0, T, cache, io))
+    o = np.concatenate(parts, 1)
+    ref = FEN.outputs(d["q"], d["k"], d["v"], d["lam"])
+    compare_outputs(o, ref, TOL[io], f"prefill {T0} + decode {k}")
+    _check_cache(cache.read(), d["k"], d["v"], T, f"prefill {T0} + decode {k}")
+
+
+def test_fenwick_decode_position_limit():
+    """C = 4 level weights cover positions 0 .. 7; the step at position 8 is
+    refused on the device: NaN outputs, the cache as it was."""
+    torch = torch_mod()
+    import dynamic_state_memory_amd as dla
+    say("fenwick decode position limit")
+    d = _inputs(9, [13], 4, dk=64, dv=64)
+    cache = dla.Cache(1, 1, 4, 64, 64, device=torch.device("cuda:0"), merge_rule="fenwick")
+    o = _decode_steps(d, 0, 8, cache, "f32")
+    ref = FEN.outputs(*(d[x][:, :8] for x in ("q", "k", "v", "lam")))
+    compare_outputs(o, ref, TOL["f32"], "positions 0 .. 7")
+    before = cache.read()
+    o8 = _decode_steps(d, 8, 9, cache, "f32")
+    assert np.isnan(o8).all()
+    after = cache.read()
+    for key in ("m", "t_seen", "order", "start", "count", "S"):
+        assert np.array_equal(before[key], after[key]), key

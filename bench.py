@@ -32,6 +32,10 @@ Also reported on the same line:
                 algorithmic flops count 2 (popcount(t) + 2) d_k d_v per
                 token-head, the buckets read plus the update (--no-fenwick
                 skips it);
+  prefill_context_sweep
+                DLA and the fixed schedule on the first T' tokens of the same
+                streams, T' = 4096 .. 32768 (the pages compare the two
+                methods' prefill over context lengths); --no-fenwick skips it;
   decode_fenwick_schedule
                 batched decode (B=256, H=16, d=128, C=32) under the same
                 schedule, from position 2^20 (the cache preloaded with the one
@@ -181,9 +185,10 @@ def prefill_bench(args, torch, dla, workloads):
         log(f"prefill, density merge rule: {d_ms:.3f} ms/step, chunk kernel {d_kern:.3f} ms, "
             f"{100 * d_ach / PEAK_BF16_TFLOPS:.1f}% of bf16 peak, mean live states "
             f"{d_stats['mean_live_states']:.2f}, merges/stream {d_stats['merges_per_stream']:.1f}")
-    fenwick = None
+    fenwick = sweep = None
     if not args.no_fenwick:
         fenwick = fenwick_leg(args, torch, dla, cfg, q, k, v, lam, o, ws, ms_per_step)
+        sweep = context_sweep(torch, dla, cfg, q, k, v, lam, ws)
     kernel = dla.dla_prefill_kernel(dla.DLA_BF16 if cfg.io == "bf16" else dla.DLA_F32, B, H, C, dk, dv)
     traffic = measured_traffic(f"{_kernel_file(kernel)}_{args.workload}_hbm_traffic.txt", kernel)
     res = dict(
@@ -198,6 +203,7 @@ def prefill_bench(args, torch, dla, workloads):
         token_heads_per_s=BH * T / (ms_per_step * 1e-3),
         density_rule=density,
         fenwick=fenwick,
+        context_sweep=sweep,
     )
     log(f"prefill: {ms_per_step:.3f} ms/step, chunk kernel {kern_avg:.3f} ms, "
         f"{achieved:.1f} TFLOP/s algorithmic ({100 * achieved / PEAK_BF16_TFLOPS:.1f}% of bf16 peak), "
@@ -242,6 +248,47 @@ def fenwick_leg(args, torch, dla, cfg, q, k, v, lam, o, ws, dla_ms):
                 ms_per_step=ms, kernel=kernel, kernel_ms=kern, C=L, achieved=ach, unit_achieved="TFLOP/s",
                 frac=ach / PEAK_BF16_TFLOPS, algorithmic_flop_per_launch=flops,
                 buckets_read_per_token=read / T, dla_over_fenwick_time=dla_ms / ms)
+
+
+def context_sweep(torch, dla, cfg, q, k, v, lam, ws, lengths=(4096, 8192, 16384, 32768), steps=5):
+    """Prefill tokens/s of DLA (summed-information merges, C = cfg.C) and of the
+    Log-Linear fixed schedule (C = L(T')) on the first T' tokens of the
+    workload's streams: wall time over `steps` calls after one warmup call."""
+    B, H, dk, dv = cfg.B, cfg.H, cfg.dk, cfg.dv
+    out = []
+    for Tn in lengths:
+        if Tn > cfg.T:
+            continue
+        L = (Tn - 1).bit_length() + 1
+        qn, kn, vn = (x[:, :, :Tn].contiguous() for x in (q, k, v))
+        lam_d = lam[:, :, :Tn].contiguous()
+        lam_f = lam[:, :, :Tn, :L].contiguous()
+        on = torch.empty(B, H, Tn, dv, dtype=q.dtype, device=q.device)
+        res = dict(T=Tn)
+        for name, rule, C, ln in (("dla", "sum", cfg.C, lam_d), ("fenwick", "fenwick", L, lam_f)):
+            cache = dla.Cache(B, H, C, dk, dv, device=q.device, merge_rule=rule)
+            wsn = dla.prefill_workspace(B, H, Tn, C, dk, dv, q.device)
+
+            def call():
+                if rule != "fenwick":
+                    cache.reset()
+                dla.prefill(qn, kn, vn, ln, cfg.tau, cache, o=on, workspace=wsn)
+
+            call()
+            torch.cuda.synchronize()
+            w0 = time.perf_counter()
+            for _ in range(steps):
+                call()
+            torch.cuda.synchronize()
+            ms = (time.perf_counter() - w0) * 1e3 / steps
+            res[f"{name}_ms_per_step"] = ms
+            res[f"{name}_tokens_per_s"] = B * Tn / (ms * 1e-3)
+            del cache, wsn
+        res["dla_over_fenwick_time"] = res["dla_ms_per_step"] / res["fenwick_ms_per_step"]
+        out.append(res)
+        log(f"context sweep T={Tn}: DLA {res['dla_ms_per_step']:.3f} ms, Log-Linear fixed schedule "
+            f"{res['fenwick_ms_per_step']:.3f} ms, ratio {res['dla_over_fenwick_time']:.2f}")
+    return out
 
 
 def decode_inputs_device(torch, cfg, steps, dev):
@@ -526,6 +573,7 @@ def main():
         "prefill_density_merge_rule": pre["density_rule"],
         "decode_bf16_states": dec_bf,
         "prefill_fenwick_schedule": pre["fenwick"],
+        "prefill_context_sweep": pre["context_sweep"],
         "decode_fenwick_schedule": dec_fen,
     }
     print(json.dumps(out), flush=True)

@@ -112,25 +112,27 @@ def test_fenwick_discards_what_the_cache_held():
     assert np.array_equal(fin1["S"], fin2["S"])
 
 
-def test_fenwick_full_size_sampled():
-    """The full Gated-DeltaNet-1.3B-shaped layer (B=2, H=16, T=32768, d_k=128,
-    d_v=256) with 16 level weights, in the benchmark's launch configuration:
-    outputs at sampled tokens of every stream within the bf16 gate, metadata of
-    every stream exact, the final state (one bucket of all 32768 tokens) of
-    four streams within the state gate."""
-    say("fenwick full size: generating inputs")
-    cfg = dataclasses.replace(workloads.CONFIGS["gdn_1p3b_t32k_bf16"], C=16)
-    d = workloads.prefill_inputs(cfg)
+@pytest.mark.parametrize("name,C,T", [("gdn_1p3b_t32k_bf16", 16, None), ("long_t131k_bf16", 18, 131072 - 77)])
+def test_fenwick_full_size_sampled(name, C, T):
+    """Full-size layers in the benchmark's launch configuration: the
+    Gated-DeltaNet-1.3B-shaped one (B=2, H=16, T=32768, d_k=128, d_v=256) with
+    16 level weights, and the long-context one (B=1, H=16, d=128) over 131072 -
+    77 tokens with 18 (a ragged last chunk after 2047 full ones).  Outputs at
+    sampled tokens of every stream within the bf16 gate, metadata of every
+    stream exact, the final states of four streams within the state gate."""
+    say(f"fenwick full size {name}: generating inputs")
+    cfg = dataclasses.replace(workloads.CONFIGS[name], C=C)
+    d = workloads.prefill_inputs(cfg, T=T)
     S, T = d["k"].shape[:2]
-    say("fenwick full size: GPU prefill")
-    o, fin = _run(d, 16, B=cfg.B, H=cfg.H)
+    say(f"fenwick full size {name}: GPU prefill")
+    o, fin = _run(d, C, B=cfg.B, H=cfg.H)
     rng = np.random.default_rng(7)
     rows = sorted(set(rng.choice(T, 20, replace=False).tolist()) | {0, 1, 63, 64, 4095, 4096, 16383, T - 1})
-    say(f"fenwick full size: oracle rows ({len(rows)} per stream)")
+    say(f"fenwick full size {name}: oracle rows ({len(rows)} per stream)")
     ref = FEN.output_rows(d["q"], d["k"], d["v"], d["lam"], rows)
-    err = compare_outputs(o[:, rows], ref, TOL["bf16"], "fenwick full size")
-    _check_cache(fin, d["k"], d["v"], T, "fenwick full size", state_streams=[0, 9, 17, 31])
-    say(f"fenwick full size: ok, sampled max row rel err {err:.2e}")
+    err = compare_outputs(o[:, rows], ref, TOL["bf16"], f"fenwick full size {name}")
+    _check_cache(fin, d["k"], d["v"], T, f"fenwick full size {name}", state_streams=[0, 5, 9, S - 1])
+    say(f"fenwick full size {name}: ok, sampled max row rel err {err:.2e}")
 
 
 def _decode_steps(d, lo, hi, cache, io):

@@ -32,6 +32,10 @@ Also reported on the same line:
                 algorithmic flops count 2 (popcount(t) + 2) d_k d_v per
                 token-head, the buckets read plus the update (--no-fenwick
                 skips it);
+  prefill_literal_reading
+                the same prefill on the literal reading of the key noise
+                (0.2 N(0, I) per coordinate: every token opens a state, so
+                every chunk merges), 5 timed steps (--no-literal skips it);
   prefill_context_sweep
                 DLA and the fixed schedule on the first T' tokens of the same
                 streams, T' = 4096 .. 32768 (the pages compare the two
@@ -126,6 +130,7 @@ def prefill_bench(args, torch, dla, workloads):
         return torch.from_numpy(a).to(dev).to(dt).view(B, H, T, dd)
 
     q, k, v, lam = up(d["q"], dk), up(d["k"], dk), up(d["v"], dv), up(d["lam"], C)
+    q_, k_, v_, lam_ = q, k, v, lam
     sample = None
     if not args.no_cpu:
         S = min(BH, args.cpu_streams)
@@ -134,10 +139,13 @@ def prefill_bench(args, torch, dla, workloads):
     ws = dla.prefill_workspace(B, H, T, C, dk, dv, dev)
     o = torch.empty(B, H, T, dv, dtype=dt, device=dev)
 
-    def timed(rule):
+    def timed(rule, steps=None, x=None):
         """One untimed call exporting the schedule (m_t gives the algorithmic
-        flops), the warmup, then args.steps timed calls: wall time per step and
-        the chunk kernel's HIP-event time."""
+        flops), the warmup, then `steps` (default args.steps) timed calls on
+        the inputs x (default the workload's): wall time per step and the
+        chunk kernel's HIP-event time."""
+        steps = args.steps if steps is None else steps
+        q, k, v, lam = (q_, k_, v_, lam_) if x is None else x
         cache = dla.Cache(B, H, C, dk, dv, device=dev, merge_rule=rule)
         m_t = torch.empty(BH, T, dtype=torch.int32, device=dev)
         bnd = torch.empty(BH, T, dtype=torch.uint8, device=dev)
@@ -156,7 +164,7 @@ def prefill_bench(args, torch, dla, workloads):
             cache.reset()
             dla.prefill(q, k, v, lam, cfg.tau, cache, o=o, workspace=ws)
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.steps)]
+               for _ in range(steps)]
         for a, b in evs:          # materialise the event handles
             a.record()
             b.record()
@@ -170,7 +178,7 @@ def prefill_bench(args, torch, dla, workloads):
         wall = time.perf_counter() - w0
         dla.dla_set_prefill_events(None, None)
         kern_ms = [a.elapsed_time(b) for a, b in evs]
-        return wall * 1e3 / args.steps, sum(kern_ms) / len(kern_ms), flops, stats
+        return wall * 1e3 / steps, sum(kern_ms) / len(kern_ms), flops, stats
 
     ms_per_step, kern_avg, flops, stats = timed("sum")
     tokens = B * T
@@ -185,6 +193,21 @@ def prefill_bench(args, torch, dla, workloads):
         log(f"prefill, density merge rule: {d_ms:.3f} ms/step, chunk kernel {d_kern:.3f} ms, "
             f"{100 * d_ach / PEAK_BF16_TFLOPS:.1f}% of bf16 peak, mean live states "
             f"{d_stats['mean_live_states']:.2f}, merges/stream {d_stats['merges_per_stream']:.1f}")
+    literal = None
+    if args.reading == "relative" and not args.no_literal:
+        # the literal reading of the key noise: every token opens a state
+        dl = workloads.prefill_inputs(cfg, reading="literal")
+        xl = (up(dl["q"], dk), up(dl["k"], dk), up(dl["v"], dv), up(dl["lam"], C))
+        del dl
+        l_ms, l_kern, l_flops, l_stats = timed("sum", steps=5, x=xl)
+        del xl
+        l_ach = l_flops / (l_kern * 1e-3) / 1e12
+        literal = dict(reading="literal", value=tokens / (l_ms * 1e-3), unit="tokens/s", steps=5,
+                       ms_per_step=l_ms, kernel_ms=l_kern, achieved=l_ach, unit_achieved="TFLOP/s",
+                       frac=l_ach / PEAK_BF16_TFLOPS, algorithmic_flop_per_launch=l_flops, schedule=l_stats)
+        log(f"prefill, literal noise reading: {l_ms:.3f} ms/step, chunk kernel {l_kern:.3f} ms, "
+            f"{100 * l_ach / PEAK_BF16_TFLOPS:.1f}% of bf16 peak, boundaries/stream "
+            f"{l_stats['boundaries_per_stream']:.0f}, merges/stream {l_stats['merges_per_stream']:.0f}")
     fenwick = sweep = None
     if not args.no_fenwick:
         fenwick = fenwick_leg(args, torch, dla, cfg, q, k, v, lam, o, ws, ms_per_step)
@@ -204,6 +227,7 @@ def prefill_bench(args, torch, dla, workloads):
         density_rule=density,
         fenwick=fenwick,
         context_sweep=sweep,
+        literal=literal,
     )
     log(f"prefill: {ms_per_step:.3f} ms/step, chunk kernel {kern_avg:.3f} ms, "
         f"{achieved:.1f} TFLOP/s algorithmic ({100 * achieved / PEAK_BF16_TFLOPS:.1f}% of bf16 peak), "
@@ -532,6 +556,8 @@ def main():
                     help="skip the second decode measurement on a cache with bf16 closed states")
     ap.add_argument("--no-density", action="store_true",
                     help="skip the second prefill measurement under the information-density merge rule")
+    ap.add_argument("--no-literal", action="store_true",
+                    help="skip the prefill measurement on the literal reading of the key noise")
     ap.add_argument("--no-fenwick", action="store_true",
                     help="skip the prefill measurement under the Log-Linear fixed schedule")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -572,6 +598,7 @@ def main():
         "token_heads_per_s": pre["token_heads_per_s"],
         "prefill_density_merge_rule": pre["density_rule"],
         "decode_bf16_states": dec_bf,
+        "prefill_literal_reading": pre["literal"],
         "prefill_fenwick_schedule": pre["fenwick"],
         "prefill_context_sweep": pre["context_sweep"],
         "decode_fenwick_schedule": dec_fen,

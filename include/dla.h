@@ -78,7 +78,7 @@ extern "C" {
 typedef enum dla_status {
     DLA_OK = 0,
     DLA_ERR_ARG = 1,          /* bad pointer, size, alignment or mismatch */
-    DLA_ERR_UNSUPPORTED = 2,  /* valid request outside what this build supports */
+    DLA_ERR_UNSUPPORTED = 2,  /* valid request outside what this library supports */
     DLA_ERR_WORKSPACE = 3,    /* workspace missing or too small */
     DLA_ERR_HIP = 4           /* a HIP launch failed; see dla_last_error() */
 } dla_status;

@@ -116,6 +116,21 @@ constexpr int kDppXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
 constexpr int kDppHalfMirror = 0x141; // row_half_mirror
 constexpr int kDppMirror = 0x140;     // row_mirror
 
+// Lane l reads lane l + 1 across the whole wave (DPP wave_shl:1, registers
+// only); lane 63 reads 0.  Callers use the value only where lane l + 1 holds
+// data.
+constexpr int kDppWaveShl1 = 0x130;
+template <typename T> __device__ __forceinline__ T lane_down1(T x) {
+    if constexpr (sizeof(T) == 8) {
+        const uint64_t u = __builtin_bit_cast(uint64_t, x);
+        const uint32_t lo = dpp32<kDppWaveShl1>(static_cast<uint32_t>(u));
+        const uint32_t hi = dpp32<kDppWaveShl1>(static_cast<uint32_t>(u >> 32));
+        return __builtin_bit_cast(T, (static_cast<uint64_t>(hi) << 32) | lo);
+    } else {
+        return __builtin_bit_cast(T, dpp32<kDppWaveShl1>(__builtin_bit_cast(uint32_t, x)));
+    }
+}
+
 template <int CTRL> __device__ __forceinline__ float dpp_move(float x) {
     return __builtin_bit_cast(float, dpp32<CTRL>(__builtin_bit_cast(uint32_t, x)));
 }

@@ -321,10 +321,10 @@ __global__ __launch_bounds__(64) void k_greedy(int T, int C, int NCH,
                 if (lane == m) { I = qj; n = 1; st = t_seen + t; oi = -1; }
                 ++m;
             } else {
-                const int64_t I_nx = __shfl_down(I, 1);
-                const int32_t n_nx = __shfl_down(n, 1);
-                const int64_t st_nx = __shfl_down(st, 1);
-                const int32_t oi_nx = __shfl_down(oi, 1);
+                const int64_t I_nx = lane_down1(I);
+                const int32_t n_nx = lane_down1(n);
+                const int64_t st_nx = lane_down1(st);
+                const int32_t oi_nx = lane_down1(oi);
                 const bool inside = lane + 1 < m;
                 const int64_t pI = inside ? I_nx : qj;
                 const int32_t pn = inside ? n_nx : 1;
@@ -1029,12 +1029,12 @@ __global__ __launch_bounds__(256) void k_decode(const TIO *__restrict__ Qg, cons
             if (lane == m) { I = qv; n = 1; stt = t_seen; ord = set_slot; }
             m_new = m + 1;
         } else {
-            const int64_t I_nx = __shfl_down(I, 1);
+            const int64_t I_nx = lane_down1(I);
             const bool inside = lane + 1 < m;
             const int64_t pI = inside ? I_nx : qv;
             if (merge_rule == DLA_MERGE_DENSITY) {
                 // lowest information density (I_i + I_{i+1}) / (n_i + n_{i+1})
-                const int32_t n_down = __shfl_down(n, 1);
+                const int32_t n_down = lane_down1(n);
                 const int64_t pn = inside ? n_down : 1;
                 merge_i = wave_argmin_frac(I + pI, static_cast<int64_t>(n) + pn, lane < m);
             } else {
@@ -1051,9 +1051,9 @@ __global__ __launch_bounds__(256) void k_decode(const TIO *__restrict__ Qg, cons
                 mode = 2;                              // merge (i, i+1), new state into the freed slot
                 const int32_t freed = __shfl(ord, merge_i + 1);
                 set_slot = freed;
-                const int32_t n_nx = __shfl_down(n, 1);
-                const int64_t st_nx = __shfl_down(stt, 1);
-                const int32_t ord_nx = __shfl_down(ord, 1);
+                const int32_t n_nx = lane_down1(n);
+                const int64_t st_nx = lane_down1(stt);
+                const int32_t ord_nx = lane_down1(ord);
                 if (lane == merge_i) { I += I_nx; n += n_nx; }
                 else if (lane > merge_i && lane < m - 1) { I = I_nx; n = n_nx; stt = st_nx; ord = ord_nx; }
                 else if (lane == m - 1) { I = qv; n = 1; stt = t_seen; ord = freed; }

@@ -39,7 +39,8 @@ Also reported on the same line:
   prefill_context_sweep
                 DLA and the fixed schedule on the first T' tokens of the same
                 streams, T' = 4096 .. 32768 (the pages compare the two
-                methods' prefill over context lengths); --no-fenwick skips it;
+                methods' prefill over context lengths); --no-sweep or
+                --no-fenwick skips it;
   decode_fenwick_schedule
                 batched decode (B=256, H=16, d=128, C=32) under the same
                 schedule, from position 2^20 (the cache preloaded with the one
@@ -211,7 +212,8 @@ def prefill_bench(args, torch, dla, workloads):
     fenwick = sweep = None
     if not args.no_fenwick:
         fenwick = fenwick_leg(args, torch, dla, cfg, q, k, v, lam, o, ws, ms_per_step)
-        sweep = context_sweep(torch, dla, cfg, q, k, v, lam, ws)
+        if not args.no_sweep:
+            sweep = context_sweep(torch, dla, cfg, q, k, v, lam, ws)
     kernel = dla.dla_prefill_kernel(dla.DLA_BF16 if cfg.io == "bf16" else dla.DLA_F32, B, H, C, dk, dv)
     traffic = measured_traffic(f"{_kernel_file(kernel)}_{args.workload}_hbm_traffic.txt", kernel)
     res = dict(
@@ -558,6 +560,8 @@ def main():
                     help="skip the second prefill measurement under the information-density merge rule")
     ap.add_argument("--no-literal", action="store_true",
                     help="skip the prefill measurement on the literal reading of the key noise")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the DLA vs Log-Linear context sweep")
     ap.add_argument("--no-fenwick", action="store_true",
                     help="skip the prefill measurement under the Log-Linear fixed schedule")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)

@@ -1300,7 +1300,7 @@ __global__ __launch_bounds__(256) void k_decode_fenwick(const TIO *__restrict__ 
         const int first = z == 0 ? m : max(m - z, 0);
         // (a cache that no fixed-schedule call left -- too many states for a
         // new one -- is refused the same way, so no slot past C is written)
-        const bool refused = t >= (1ll << (C - 1)) || m > C || (first == m && m >= C);
+        const bool refused = (C < 64 && t >= (1ll << (C - 1))) || m > C || (first == m && m >= C);
         int dst, m_new;
         if (first == m) {
             dst = __ffsll(static_cast<unsigned long long>(~usedmask)) - 1;  // lowest free slot

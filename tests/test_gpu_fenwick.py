@@ -176,6 +176,19 @@ def test_fenwick_decode_continues_the_stream(T0, k, dd, io):
     _check_cache(cache.read(), d["k"], d["v"], T, f"prefill {T0} + decode {k}")
 
 
+def test_fenwick_decode_full_capacity():
+    """C = 64, the largest capacity (no position limit within reach): decode
+    from an empty cache as one pass of the oracle."""
+    torch = torch_mod()
+    import dynamic_state_memory_amd as dla
+    say("fenwick decode C=64")
+    d = _inputs(100, [14, 15], 64, dk=64, dv=64)
+    cache = dla.Cache(1, 2, 64, 64, 64, device=torch.device("cuda:0"), merge_rule="fenwick")
+    o = _decode_steps(d, 0, 100, cache, "f32")
+    compare_outputs(o, FEN.outputs(d["q"], d["k"], d["v"], d["lam"]), TOL["f32"], "C=64")
+    _check_cache(cache.read(), d["k"], d["v"], 100, "C=64")
+
+
 def test_fenwick_decode_position_limit():
     """C = 4 level weights cover positions 0 .. 7; the step at position 8 is
     refused on the device: NaN outputs, the cache as it was."""

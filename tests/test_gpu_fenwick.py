@@ -90,6 +90,32 @@ def test_fenwick_shapes_and_capacities(dk, dv, C, T):
     _check_cache(fin, d["k"], d["v"], T, f"dk={dk} C={C} T={T}")
 
 
+def _random_shapes(n, seed=2024):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        T = int(rng.integers(1, 3000))
+        dk = int(rng.choice([64, 128]))
+        dv = int(16 * rng.integers(1, 17))
+        L = FEN.levels_needed(T)
+        C = int(rng.integers(L, 33))
+        S = int(rng.integers(1, 7))
+        out.append((T, dk, dv, C, S))
+    return out
+
+
+@pytest.mark.parametrize("T,dk,dv,C,S", _random_shapes(12))
+def test_fenwick_random_shapes(T, dk, dv, C, S):
+    """Seeded random shapes within the supported ranges: T in [1, 3000), d_k in
+    {64, 128}, d_v a multiple of 16 up to 256, C from the level count to 32,
+    1 to 6 streams."""
+    say(f"fenwick random T={T} dk={dk} dv={dv} C={C} S={S}")
+    d = _inputs(T, list(range(S)), C, dk=dk, dv=dv)
+    o, fin = _run(d, C, B=1, H=S)
+    compare_outputs(o, FEN.outputs(d["q"], d["k"], d["v"], d["lam"]), TOL["bf16"], f"T={T} dk={dk} dv={dv} C={C}")
+    _check_cache(fin, d["k"], d["v"], T, f"T={T} dk={dk} dv={dv} C={C}")
+
+
 def test_fenwick_discards_what_the_cache_held():
     """A prefill under the fixed schedule starts afresh: on a cache that an
     information-driven prefill filled, it gives what it gives on an empty one,

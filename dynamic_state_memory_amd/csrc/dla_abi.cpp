@@ -4,6 +4,7 @@
 // synchronises.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -75,7 +76,9 @@ Sizes workspace_sizes(int64_t BH, int64_t T, int64_t C, int64_t dk, int64_t dv)
     z.init_m = align_up(4ull * BH, 256);
     z.init_order = align_up(64ull * BH, 256);
     z.shadow = align_up(2ull * BH * C * dv * dk, 256);
-    z.rec = align_up(static_cast<uint64_t>(BH) * NCH * rs_record_bytes(dk), 256);
+    // chunk records (register-resident path), or the fp32 working copy of a
+    // bf16-state cache's states (streamed path)
+    z.rec = align_up(std::max<uint64_t>(static_cast<uint64_t>(BH) * NCH * rs_record_bytes(dk), 4ull * BH * C * dv * dk), 256);
     z.total = z.s + z.qs + z.flag + z.tile_cnt + z.tile_sum + z.seg_t + z.seg_P + z.seg_q0 + z.nseg +
               z.events + z.chunk_ev + z.init_m + z.init_order + z.shadow + z.rec;
     return z;
@@ -99,7 +102,9 @@ Workspace carve(void *base, const Sizes &z)
     w.init_m = reinterpret_cast<int32_t *>(p); p += z.init_m;
     w.init_order = p; p += z.init_order;
     w.shadow = p; p += z.shadow;
-    w.rec = p; p += z.rec;
+    w.rec = p;
+    w.work = reinterpret_cast<float *>(p);
+    p += z.rec;
     (void)p;
     return w;
 }
@@ -334,9 +339,6 @@ dla_status dla_prefill(const void *q, const void *k, const void *v, const void *
     if (plan.lds > 160 * 1024)
         return fail(DLA_ERR_UNSUPPORTED, "shape needs more LDS than a compute unit has");
     a.g = geom(cache);
-    if (a.g.state_bf16 && !a.register_resident)
-        return fail(DLA_ERR_UNSUPPORTED, "bfloat16 state storage needs bfloat16 io and C <= 32 "
-                                         "(the register-resident prefill)");
     if (a.merge_rule == DLA_FENWICK) {
         const int levels = bit_length(T - 1) + 1;
         if (cache->C < levels)

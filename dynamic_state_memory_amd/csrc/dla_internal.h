@@ -76,6 +76,9 @@ struct Workspace {
     // times 2^e for the query scaling 2^-e of the fragments), bf16 fragments
     // of (Q K^T) o W [4][2][64][8], bf16 fragments of K^T [DK/16][2][64][8]
     void *rec;
+    // streamed path on a cache with bf16 closed states: the fp32 working copy
+    // of the states [BH][C][dv][dk], in the same bytes as rec (unused there)
+    float *work;
 };
 constexpr int kPrepCmax = 32;   // read-weight rows kept per chunk by the pre-pass
 // chunk record of the register-resident prefill: query fragments, read weights,

@@ -16,6 +16,8 @@
 // timestamp.  The fixed choices (cosine score, summed-information key,
 // slot-indexed lam) are listed in include/dla.h.
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 #include <stdint.h>
 
 #include "dla_device.h"
@@ -1443,6 +1445,50 @@ static hipError_t prefill_main(const PrefillArgs &a, hipStream_t stream)
     return e;
 }
 
+// A cache with bf16 closed states on the streamed prefill: the live states are
+// widened into an fp32 working copy (closed ones from their bf16 slots, the
+// most recent from the fp32 active region), the streamed kernels run on the
+// copy, and the final live states are narrowed back: the closed ones rounded
+// once to bf16 (nearest even) into their slots, the most recent into the
+// active region.  Grid (element blocks, slot, stream); a block whose slot
+// holds no live state does nothing.
+template <bool NARROW>
+__global__ __launch_bounds__(256) void k_state_copy(uint16_t *__restrict__ slots, float *__restrict__ active,
+                                                    float *__restrict__ work, const uint8_t *__restrict__ meta_base,
+                                                    size_t meta_stride, int C, int D2)
+{
+    const int p = blockIdx.y, bh = blockIdx.z;
+    const uint8_t *meta = meta_base + static_cast<size_t>(bh) * meta_stride;
+    const int m = reinterpret_cast<const MetaHead *>(meta)->m;
+    int idx = -1;                    // chronological index of the state in slot p
+    for (int i = 0; i < m; ++i)
+        if (meta[kOffOrder + i] == p) idx = i;
+    if (idx < 0) return;
+    const bool last = idx == m - 1;
+    float4 *w4 = reinterpret_cast<float4 *>(work + (static_cast<size_t>(bh) * C + p) * D2);
+    uint2 *s4 = reinterpret_cast<uint2 *>(slots + (static_cast<size_t>(bh) * C + p) * D2);
+    float4 *a4 = reinterpret_cast<float4 *>(active + static_cast<size_t>(bh) * D2);
+    for (int e = blockIdx.x * 256 + threadIdx.x; e < D2 / 4; e += gridDim.x * 256) {
+        if constexpr (NARROW) {
+            if (last) a4[e] = w4[e];
+            else s4[e] = pack_bf16x4(w4[e]);
+        } else {
+            w4[e] = last ? a4[e] : unpack_bf16x4(s4[e]);
+        }
+    }
+}
+
+template <bool NARROW>
+static hipError_t state_copy(const PrefillArgs &a, hipStream_t stream)
+{
+    const int D2 = a.g.dv * a.g.dk;
+    const int gx = std::min((D2 / 4 + 255) / 256, 16);
+    hipLaunchKernelGGL(k_state_copy<NARROW>, dim3(gx, a.g.C, a.g.B * a.g.H), dim3(256), 0, stream,
+                       reinterpret_cast<uint16_t *>(a.states), a.active, a.ws.work, a.meta, a.g.meta_stride, a.g.C,
+                       D2);
+    return hipGetLastError();
+}
+
 template <typename TIO>
 static hipError_t prefill_typed(const PrefillArgs &a, hipStream_t stream)
 {
@@ -1480,6 +1526,16 @@ static hipError_t prefill_register_resident(const PrefillArgs &a, hipStream_t st
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream)
 {
     if (a.register_resident) return prefill_register_resident(a, stream);
+    if (a.g.state_bf16) {
+        // the streamed kernels on an fp32 working copy of the states
+        hipError_t e = state_copy<false>(a, stream);
+        if (e != hipSuccess) return e;
+        PrefillArgs b = a;
+        b.states = a.ws.work;
+        e = b.io_bf16 ? prefill_typed<__bf16>(b, stream) : prefill_typed<float>(b, stream);
+        if (e != hipSuccess) return e;
+        return state_copy<true>(a, stream);
+    }
     if (a.io_bf16) return prefill_typed<__bf16>(a, stream);
     return prefill_typed<float>(a, stream);
 }

@@ -231,9 +231,11 @@ uint64_t dla_prefill_workspace_bytes(int32_t B, int32_t H, int32_t T, int32_t C,
  *   workspace  device, >= dla_prefill_workspace_bytes, 256-byte aligned;
  *              scratch owned by the call until the stream work completes
  *   sched   optional schedule export, may be NULL
- * T must be in [1, 2^24].  A cache with bfloat16 state storage needs the
- * register-resident sweep (bfloat16 io, C <= 32); other prefills of such a
- * cache return DLA_ERR_UNSUPPORTED.
+ * T must be in [1, 2^24].  On a cache with bfloat16 state storage the
+ * register-resident sweep (bfloat16 io, C <= 32) rounds each closed state to
+ * bfloat16 when it closes or takes a merge; the streamed kernel (float32 io,
+ * or C > 32) widens the live states into the workspace, runs in float32 and
+ * rounds each closed state once at the end of the call.
  *
  * With the cache's rule DLA_FENWICK the call follows the Log-Linear fixed
  * schedule (top of this header) and starts every stream afresh at position 0:

@@ -125,12 +125,14 @@ def test_bf16_state_storage_layout_and_checks():
     cc = dla.dla_cache()
     assert dla.dla_cache_init(cc, p, 1 << 30, 1, 1, 8, 64, 64, 7, None, None) == dla.DLA_ERR_ARG
     assert "state dtype" in dla.dla_last_error()
-    # a bf16 cache needs the register-resident prefill: fp32 io is refused on the host
+    # the workspace holds an fp32 copy of every state (the streamed path on a
+    # bf16 cache), even when the chunk records are smaller
+    assert dla.dla_prefill_workspace_bytes(1, 1, 64, 64, 128, 512) >= 4 * 64 * 128 * 512
     c = _cache()
     c.state_dtype = dla.DLA_BF16
     c.bytes = dla.dla_cache_bytes(1, 1, 8, 64, 64, dla.DLA_BF16)
     ws = dla.dla_prefill_workspace_bytes(1, 1, 100, 8, 64, 64)
-    assert dla.dla_prefill(p, p, p, p, p, 100, 0.3, dla.DLA_F32, c, p, ws, None, None) == dla.DLA_ERR_UNSUPPORTED
+    assert dla.dla_prefill(p, p, p, p, p, 100, 0.3, dla.DLA_F32, c, p, ws - 1, None, None) == dla.DLA_ERR_WORKSPACE
     c.state_dtype = 3
     assert dla.dla_prefill(p, p, p, p, p, 100, 0.3, dla.DLA_BF16, c, p, ws, None, None) == dla.DLA_ERR_ARG
 

@@ -242,12 +242,13 @@ def prefill_bench(args, torch, dla, workloads):
 def fenwick_leg(args, torch, dla, cfg, q, k, v, lam, o, ws, dla_ms):
     """The same tokens under the Log-Linear fixed schedule: L = bit_length(T-1)+1
     level weights (the first L columns of the workload's lam), a cache of C = L
-    slots.  Every such prefill starts afresh, so no reset is needed."""
+    slots, reset before every call (a prefill continues the cache)."""
     B, H, T, dk, dv = cfg.B, cfg.H, cfg.T, cfg.dk, cfg.dv
     L = (T - 1).bit_length() + 1
     lamL = lam[..., :L].contiguous()
     cache = dla.Cache(B, H, L, dk, dv, device=q.device, merge_rule="fenwick")
     for _ in range(max(args.warmup, 1)):
+        cache.reset()
         dla.prefill(q, k, v, lamL, 0.0, cache, o=o, workspace=ws)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     for a, b in evs:
@@ -256,6 +257,7 @@ def fenwick_leg(args, torch, dla, cfg, q, k, v, lam, o, ws, dla_ms):
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     for a, b in evs:
+        cache.reset()
         dla.dla_set_prefill_events(a.cuda_event, b.cuda_event)
         dla.prefill(q, k, v, lamL, 0.0, cache, o=o, workspace=ws)
     torch.cuda.synchronize()
@@ -296,8 +298,7 @@ def context_sweep(torch, dla, cfg, q, k, v, lam, ws, lengths=(4096, 8192, 16384,
             wsn = dla.prefill_workspace(B, H, Tn, C, dk, dv, q.device)
 
             def call():
-                if rule != "fenwick":
-                    cache.reset()
+                cache.reset()
                 dla.prefill(qn, kn, vn, ln, cfg.tau, cache, o=on, workspace=wsn)
 
             call()

@@ -222,8 +222,8 @@ class Cache:
 
     ``merge_rule``: "sum" (smallest summed information, the default) or
     "density" (lowest information density) for the capacity merges, or
-    "fenwick" for the Log-Linear fixed schedule (prefill only: lam weights
-    levels, C >= bit_length(T - 1) + 1, every prefill starts afresh).
+    "fenwick" for the Log-Linear fixed schedule (lam weights levels, C at
+    least the level count bit_length(t - 1) + 1 of the positions reached).
     ``state_dtype``: "f32" (every state float32) or "bf16" (closed states
     bfloat16, the most recent one float32)."""
 

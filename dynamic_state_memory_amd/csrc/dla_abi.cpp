@@ -52,7 +52,9 @@ dla_status check_shape(int32_t B, int32_t H, int32_t C, int32_t dk, int32_t dv)
 }
 
 struct Sizes {
-    uint64_t s, qs, flag, tile_cnt, tile_sum, seg_t, seg_P, seg_q0, nseg, events, chunk_ev, init_m, init_order, shadow;
+    uint64_t s, qs, flag, tile_cnt, tile_sum, seg_t, seg_P, seg_q0, nseg, events, chunk_ev, init_m, init_order, init_t,
+        shadow;
+    uint64_t ev_stride;
     uint64_t rec;
     uint64_t total;
 };
@@ -71,16 +73,18 @@ Sizes workspace_sizes(int64_t BH, int64_t T, int64_t C, int64_t dk, int64_t dv)
     z.seg_P = align_up(8ull * BH * (T + 1), 256);
     z.seg_q0 = align_up(8ull * BH * T, 256);
     z.nseg = align_up(4ull * BH, 256);
-    z.events = align_up(8ull * BH * T, 256);
+    z.ev_stride = static_cast<uint64_t>(std::max<int64_t>(T, kChunk));
+    z.events = align_up(8ull * BH * z.ev_stride, 256);
     z.chunk_ev = align_up(4ull * BH * (NCH + 1), 256);
     z.init_m = align_up(4ull * BH, 256);
     z.init_order = align_up(64ull * BH, 256);
+    z.init_t = align_up(8ull * BH, 256);
     z.shadow = align_up(2ull * BH * C * dv * dk, 256);
     // chunk records (register-resident path), or the fp32 working copy of a
     // bf16-state cache's states (streamed path)
     z.rec = align_up(std::max<uint64_t>(static_cast<uint64_t>(BH) * NCH * rs_record_bytes(dk), 4ull * BH * C * dv * dk), 256);
     z.total = z.s + z.qs + z.flag + z.tile_cnt + z.tile_sum + z.seg_t + z.seg_P + z.seg_q0 + z.nseg +
-              z.events + z.chunk_ev + z.init_m + z.init_order + z.shadow + z.rec;
+              z.events + z.chunk_ev + z.init_m + z.init_order + z.init_t + z.shadow + z.rec;
     return z;
 }
 
@@ -101,6 +105,8 @@ Workspace carve(void *base, const Sizes &z)
     w.chunk_ev = reinterpret_cast<int32_t *>(p); p += z.chunk_ev;
     w.init_m = reinterpret_cast<int32_t *>(p); p += z.init_m;
     w.init_order = p; p += z.init_order;
+    w.init_t = reinterpret_cast<int64_t *>(p); p += z.init_t;
+    w.ev_stride = z.ev_stride;
     w.shadow = p; p += z.shadow;
     w.rec = p;
     w.work = reinterpret_cast<float *>(p);

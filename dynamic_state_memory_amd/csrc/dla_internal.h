@@ -63,10 +63,12 @@ struct Workspace {
     int64_t *seg_P;      // [BH][T+1] information before each boundary (+ total)
     int64_t *seg_q0;     // [BH][T] information of each boundary token
     int32_t *nseg;       // [BH]
-    int2 *events;        // [BH][T] (token, state merged away or -1)
+    int2 *events;        // [BH][ev_stride] (token, state merged away or -1)
+    size_t ev_stride;    // events per stream: max(T, 64) (fixed-schedule calls can have more events than tokens)
     int32_t *chunk_ev;   // [BH][NCH+1] first event of each chunk
     int32_t *init_m;     // [BH] live states when the call starts (saved by the greedy scan)
     uint8_t *init_order; // [BH][64] their physical slots, oldest first
+    int64_t *init_t;     // [BH] position the call starts at (fixed schedule)
     void *shadow;        // [BH][C][dv][dk] fp16 copy of the states (bf16 io)
     // per-chunk operands built by the chunk pre-pass (register-resident path)
     // [BH][NCH] chunk records of the register-resident prefill, each

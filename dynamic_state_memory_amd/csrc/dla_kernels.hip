@@ -446,22 +446,90 @@ __device__ int fen_chunk_events(int c, int T, int NCH, int2 *ev)
     return cnt;
 }
 
+// A call continuing a stream at position t0 > 0 keeps the pieces exactly the
+// buckets of [0, t) at every chunk end (its chunks are not aligned to the
+// bucket sizes).  Call chunk c goes from the buckets of ts = t0 + 64 c to
+// those of te: the two share their buckets above bit h, the highest bit in
+// which ts and te differ; te's bucket of bit h starts where ts's buckets below
+// h start, so those merge into the oldest of them and the chunk's first tokens
+// join it (or, if ts has no bucket below h, the chunk opens it); te's buckets
+// below h lie inside the chunk and each opens a state.  Merges ride on the
+// first boundary; with no boundary they ride on one at the chunk start whose
+// own state is merged away last.
+__device__ int fen_cont_events(int64_t t0, int c, int T, int2 *ev)
+{
+    const int c0 = c * kChunk;
+    const int64_t ts = t0 + c0, te = ts + min(kChunk, T - c0);
+    const int m0 = __popcll(ts);
+    const int h = 63 - __clzll(static_cast<unsigned long long>(ts ^ te));
+    const int k = __popcll(ts >> (h + 1));
+    const bool below = (ts & ((1ll << h) - 1)) != 0;
+    int cnt = 0;
+    auto put = [&](int p, int d) {
+        if (ev) ev[cnt] = make_int2(p, d);
+        ++cnt;
+    };
+    // boundaries: te's bucket of bit h when ts has nothing below h, then te's
+    // buckets below h (positions within the chunk, increasing)
+    int first = -1;
+    if (!below) first = 0;
+    else
+        for (int b = h - 1; b >= 0; --b)
+            if ((te >> b) & 1) {
+                first = static_cast<int>((te & ~((2ll << b) - 1)) - ts);
+                break;
+            }
+    if (first >= 0) {
+        if (below && k + 1 < m0)
+            for (int d = k + 1; d < m0; ++d) put(c0 + first, d);
+        else
+            put(c0 + first, -1);
+        for (int b = h - 1; b >= 0; --b)
+            if ((te >> b) & 1) {
+                const int p = static_cast<int>((te & ~((2ll << b) - 1)) - ts);
+                if (p > first) put(c0 + p, -1);
+            }
+    } else if (k + 1 < m0) {
+        for (int d = k + 1; d < m0; ++d) put(c0, d);
+        put(c0, 64);
+    }
+    return cnt;
+}
+
 // One block per stream: the events and per-chunk event offsets of the whole
 // stream (a block-wide scan over the chunks), and the metadata of the final
-// cache, the buckets of [0, T).  A call with this schedule starts the stream
-// afresh: nothing the cache held before is kept.
-__global__ __launch_bounds__(256) void k_fenwick_schedule(int T, int NCH, int dk, int2 *__restrict__ events,
-                                                          int32_t *__restrict__ chunk_ev,
+// cache, the buckets of [0, t0 + T).  The stream continues from t0 = t_seen
+// with the pieces the cache holds (the buckets of [0, t0), as fixed-schedule
+// calls leave them).  A stream that would need a level weight past column
+// C - 1 is refused: init_m = -1 marks it for the chunk kernels, which then
+// leave its cache as it was and its outputs NaN.
+__global__ __launch_bounds__(256) void k_fenwick_schedule(int T, int NCH, int C, int dk, size_t ev_stride,
+                                                          int2 *__restrict__ events, int32_t *__restrict__ chunk_ev,
                                                           uint8_t *__restrict__ meta_base, size_t meta_stride,
                                                           int32_t *__restrict__ init_m_out,
-                                                          uint8_t *__restrict__ init_order_out)
+                                                          uint8_t *__restrict__ init_order_out,
+                                                          int64_t *__restrict__ t0_out)
 {
     const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     __shared__ int wsum[4];
+    uint8_t *meta = meta_base + static_cast<size_t>(bh) * meta_stride;
+    MetaHead *head = reinterpret_cast<MetaHead *>(meta);
+    const int64_t t0 = head->t_seen;
+    const int m_init = head->m;
+    const int64_t tend = t0 + T;
+    // levels 0 .. bit_length(tend - 1) must have a column
+    const bool refused = C < 64 && tend - 1 >= (1ll << (C - 1));
+    __syncthreads();          // every thread has read the head before it changes
+    if (tid == 0) t0_out[bh] = t0;
+    if (refused) {
+        for (int c = tid; c <= NCH; c += 256) chunk_ev[static_cast<size_t>(bh) * (NCH + 1) + c] = 0;
+        if (tid == 0) init_m_out[bh] = -1;
+        return;
+    }
     int carry = 0;
     for (int base = 0; base < NCH; base += 256) {
         const int c = base + tid;
-        const int cnt = c < NCH ? fen_chunk_events(c, T, NCH, nullptr) : 0;
+        const int cnt = c >= NCH ? 0 : t0 > 0 ? fen_cont_events(t0, c, T, nullptr) : fen_chunk_events(c, T, NCH, nullptr);
         int x = cnt;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
@@ -476,20 +544,25 @@ __global__ __launch_bounds__(256) void k_fenwick_schedule(int T, int NCH, int dk
         if (c < NCH) {
             const int e0 = before + x - cnt;
             chunk_ev[static_cast<size_t>(bh) * (NCH + 1) + c] = e0;
-            fen_chunk_events(c, T, NCH, events + static_cast<size_t>(bh) * T + e0);
+            int2 *ev = events + static_cast<size_t>(bh) * ev_stride + e0;
+            if (t0 > 0) fen_cont_events(t0, c, T, ev);
+            else fen_chunk_events(c, T, NCH, ev);
         }
         __syncthreads();
         carry = total;
     }
     if (tid == 0) chunk_ev[static_cast<size_t>(bh) * (NCH + 1) + NCH] = carry;
 
-    uint8_t *meta = meta_base + static_cast<size_t>(bh) * meta_stride;
+    // the pieces the call starts from (their slots are kept for the sweep,
+    // which rewrites the order)
+    if (tid < kMaxC) init_order_out[static_cast<size_t>(bh) * kMaxC + tid] = meta[kOffOrder + tid];
+    __syncthreads();
     if (tid < kMaxC) {
-        // bucket tid: the tid-th set bit of T from the top
+        // bucket tid of [0, tend): the tid-th set bit of tend from the top
         int64_t st = 0, cnt = 0;
         int seen = 0;
-        for (int b = 30; b >= 0; --b)
-            if ((T >> b) & 1) {
+        for (int b = 62; b >= 0; --b)
+            if ((tend >> b) & 1) {
                 if (seen == tid) cnt = 1ll << b;
                 if (seen < tid) st += 1ll << b;
                 ++seen;
@@ -498,18 +571,16 @@ __global__ __launch_bounds__(256) void k_fenwick_schedule(int T, int NCH, int dk
         reinterpret_cast<int64_t *>(meta + kOffInfo)[tid] = 0;
         reinterpret_cast<int32_t *>(meta + kOffCount)[tid] = static_cast<int32_t>(cnt);
         reinterpret_cast<int64_t *>(meta + kOffStart)[tid] = st;
-        init_order_out[static_cast<size_t>(bh) * kMaxC + tid] = 0xFF;
     }
     for (int i = tid; i < dk; i += blockDim.x) reinterpret_cast<float *>(meta + kOffKprev)[i] = 0.0f;
     if (tid == 0) {
-        MetaHead *head = reinterpret_cast<MetaHead *>(meta);
-        head->m = __popc(T);
+        head->m = __popcll(tend);
         head->has_prev = 0;
         head->s_prev = 0.0f;
         head->pad0 = 0;
-        head->t_seen = T;
+        head->t_seen = tend;
         head->pad1 = 0;
-        init_m_out[bh] = 0;
+        init_m_out[bh] = m_init;
     }
 }
 
@@ -1513,8 +1584,9 @@ static hipError_t prefill_register_resident(const PrefillArgs &a, hipStream_t st
     hipError_t e;
     if (a.merge_rule == DLA_FENWICK) {
         const int NCH = (a.T + kChunk - 1) / kChunk;
-        hipLaunchKernelGGL(k_fenwick_schedule, dim3(a.g.B * a.g.H), dim3(256), 0, stream, a.T, NCH, a.g.dk,
-                           a.ws.events, a.ws.chunk_ev, a.meta, a.g.meta_stride, a.ws.init_m, a.ws.init_order);
+        hipLaunchKernelGGL(k_fenwick_schedule, dim3(a.g.B * a.g.H), dim3(256), 0, stream, a.T, NCH, a.g.C, a.g.dk,
+                           a.ws.ev_stride, a.ws.events, a.ws.chunk_ev, a.meta, a.g.meta_stride, a.ws.init_m,
+                           a.ws.init_order, a.ws.init_t);
         e = hipGetLastError();
     } else {
         e = a.g.dk == 128 ? prefill_schedule<__bf16, 128>(a, stream) : prefill_schedule<__bf16, 64>(a, stream);

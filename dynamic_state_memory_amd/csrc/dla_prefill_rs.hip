@@ -39,6 +39,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "dla_device.h"
@@ -92,7 +93,7 @@ template <int DK, bool FEN>
 __global__ __launch_bounds__(256) void k_chunk_prep(
     const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, const __bf16 *__restrict__ LAM, int T, int C,
     const int2 *__restrict__ events, const int32_t *__restrict__ chunk_ev, uint8_t *__restrict__ rec,
-    int32_t *__restrict__ m_t_out, const int32_t *__restrict__ init_m)
+    int32_t *__restrict__ m_t_out, const int32_t *__restrict__ init_m, const int64_t *__restrict__ init_t)
 {
     constexpr int KS = DK / 32;
     // 40 KB of LDS: four blocks per compute unit.  The weighted scores P
@@ -124,6 +125,14 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
     bf16x8 *pwf = reinterpret_cast<bf16x8 *>(rb + rs_rec_a_bytes(DK));
     bf16x8 *ktf = reinterpret_cast<bf16x8 *>(rb + rs_rec_a_bytes(DK) + 2 * kChunk * kChunk);
     const int lr = lane & 15, lg = lane >> 4;
+    // fixed schedule: the position the call starts at (a refused stream is
+    // left alone: its outputs are set apart and its records never read)
+    int64_t t0 = 0;
+    if constexpr (FEN) {
+        if (init_m[bh] < 0) return;
+        t0 = init_t[bh];
+    }
+    const int64_t ts = t0 + c0;         // absolute position of the chunk's first token
 
     float qmax = 0.0f;
 #pragma unroll
@@ -152,7 +161,10 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
     const int nev = chunk_ev[static_cast<size_t>(bh) * (NCH + 1) + ch + 1] - e0;
     // states live at the chunk start: those the cache held when the call
     // started, plus one per boundary before the chunk, capped at C by the merges
-    const int m0 = FEN ? (ch == 0 ? 0 : __popc((ch & 1) ? ch : ch - 1)) : min(C, init_m[bh] + e0);
+    // (fixed schedule from position 0: the chunk-level pieces; from t0 > 0:
+    // the buckets of [0, ts))
+    const int m0 = FEN ? (t0 > 0 ? __popcll(ts) : ch == 0 ? 0 : __popc((ch & 1) ? ch : ch - 1))
+                       : min(C, init_m[bh] + e0);
     if (!FEN && tid < nev) evs[tid] = events[tok0 + e0 + tid];
     qmax = wave_max(qmax);
     if (lane == 0) red[wave] = qmax;
@@ -226,7 +238,12 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
                 const int s = 16 * nt + lr;
                 float val = 0.0f;
                 if (s <= t) {
-                    const int col = FEN ? (s == t ? 0 : 32 - __clz(t ^ s)) : __popcll(shr64(nm[t], s + 1));
+                    // (fixed schedule: the level of absolute positions; rows
+                    // past the stream's end hold zero scores, read column 0)
+                    const int col = !FEN ? __popcll(shr64(nm[t], s + 1))
+                                         : (s == t || t >= nvalid) ? 0
+                                                                   : 64 - __clzll(static_cast<unsigned long long>(
+                                                                              (ts + t) ^ (ts + s)));
                     val = A[r] * static_cast<float>(lam[t][col]);
                 }
                 pw[t][s] = static_cast<__bf16>(val);
@@ -253,16 +270,18 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
         if (FEN && i < m0 && t < nvalid) {
             // (rows past the stream's end keep weight 0: their level could
             // exceed the last column)
-            // piece i: the bucket of the i-th set bit (from the top) of the
-            // chunk count it was formed for; its first chunk has the bits above
-            const int cp = (ch & 1) ? ch : ch - 1;
-            int seen = 0, first = 0;
-            for (int b = 30; b >= 0; --b)
+            // piece i: from position 0, the bucket of the i-th set bit (from
+            // the top) of the chunk count it was formed for, its first chunk
+            // the bits above; from t0 > 0, the i-th bucket of [0, ts)
+            const int64_t cp = t0 > 0 ? ts : static_cast<int64_t>((ch & 1) ? ch : ch - 1) * kChunk;
+            int seen = 0;
+            int64_t first = 0;
+            for (int b = 62; b >= 0; --b)
                 if ((cp >> b) & 1) {
-                    if (seen == i) first = cp & ~((2 << b) - 1);
+                    if (seen == i) first = cp & ~((2ll << b) - 1);
                     ++seen;
                 }
-            const int col = 32 - __clz((c0 + t) ^ (first * kChunk));
+            const int col = 64 - __clzll(static_cast<unsigned long long>((ts + t) ^ first));
             w = ldexpf(static_cast<float>(lam[t][col]), qexp);
         } else if (i < m0) {
             w = ldexpf(static_cast<float>(lam[t][__popcll(shr64(om[t], i + 1)) + __popcll(nm[t])]), qexp);
@@ -490,7 +509,7 @@ struct RsParams {
     const __bf16 *V;
     __bf16 *O;
     int T, C, DV;
-    const int2 *events;
+    const int2 *events;         // the stream's events
     int evtot;                  // events of the stream
     const uint8_t *rec;         // chunk records
     int bh, dv0, tid, lane, wave, lr, lg, NCH, vr, vc;
@@ -649,7 +668,7 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
         // value would wait for the load here)
         c.evnext = make_int2(0x7fffffff, -1);
         const int en = c.ewin + nev;
-        if (wave == 0 && en + lane < A.evtot) c.evnext = *at_bytes(A.events + tok0 + en, 8u * lane);
+        if (wave == 0 && en + lane < A.evtot) c.evnext = *at_bytes(A.events + en, 8u * lane);
     }
     // ---- reduce the partial reads of rows 16 w .., add P V
     {
@@ -1028,7 +1047,7 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
 template <int DK, int DVT, int SPW, bool SBF, bool CONT>
 __global__ __launch_bounds__(kRsThreads, 2) void k_prefill_rs(
     const __bf16 *__restrict__ V, __bf16 *__restrict__ O, int T, int C, int DV, int nblk_dv,
-    float *__restrict__ states, float *__restrict__ active, const int2 *__restrict__ events,
+    float *__restrict__ states, float *__restrict__ active, const int2 *__restrict__ events, size_t ev_stride,
     const int32_t *__restrict__ chunk_ev, const uint8_t *__restrict__ rec,
     uint8_t *__restrict__ meta_base, size_t meta_stride, const int32_t *__restrict__ init_m,
     const uint8_t *__restrict__ init_order)
@@ -1048,8 +1067,9 @@ __global__ __launch_bounds__(kRsThreads, 2) void k_prefill_rs(
     if ((nblk & 7) == 0) lin = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
     RsParams A;
     A.V = V; A.O = O; A.T = T; A.C = C; A.DV = DV;
-    A.events = events; A.rec = rec;
+    A.rec = rec;
     A.bh = lin / nblk_dv;
+    A.events = events + static_cast<size_t>(A.bh) * ev_stride;
     A.dv0 = (lin % nblk_dv) * DVT;
     A.tid = threadIdx.x;
     A.lane = A.tid & 63;
@@ -1106,7 +1126,8 @@ __global__ __launch_bounds__(kRsThreads, 2) void k_prefill_rs(
     // two instances are launched: CONT for streams whose cache holds states,
     // the other for empty ones (the sweep without the start-up code); a block
     // of the other kind leaves at once (the whole block: no barrier is met)
-    if ((A.m_init > 0) != CONT) return;
+    // (a stream the fixed schedule refused, m_init < 0, is left to a later kernel)
+    if (A.m_init < 0 || (A.m_init > 0) != CONT) return;
     if (CONT) {
         c.act = A.init_order[A.m_init - 1];
         if (A.m_init == 1) {
@@ -1135,7 +1156,7 @@ __global__ __launch_bounds__(kRsThreads, 2) void k_prefill_rs(
     // wave 0: the window of chunk 0 (the stream's first 64 events)
     c.ewin = 0;
     c.evnext = make_int2(0x7fffffff, -1);
-    if (wave == 0 && A.lane < A.evtot) c.evnext = events[A.tok0 + A.lane];
+    if (wave == 0 && A.lane < A.evtot) c.evnext = A.events[A.lane];
 
     for (int ch = (CONT && A.m_init > 1) ? -1 : 0; ch < NCH; ++ch)
         rs_chunk<DK, DVT, SPW, SBF, CONT>(ch, stA, stB, S, A, c);
@@ -1159,17 +1180,34 @@ __global__ __launch_bounds__(kRsThreads, 2) void k_prefill_rs(
     }
 }
 
+// The outputs of streams the fixed schedule refused (a level weight past
+// column C - 1 would be needed; marked init_m < 0): NaN, as the decode step
+// reports the same condition.  Their caches were left as they were.
+__global__ __launch_bounds__(256) void k_fen_refused(__bf16 *__restrict__ O, int T, int DV,
+                                                     const int32_t *__restrict__ init_m)
+{
+    const int bh = blockIdx.y;
+    if (init_m[bh] >= 0) return;
+    const size_t n = static_cast<size_t>(T) * DV;
+    __bf16 *o = O + static_cast<size_t>(bh) * n;
+    for (size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x; i < n; i += static_cast<size_t>(gridDim.x) * 256)
+        o[i] = static_cast<__bf16>(__builtin_nanf(""));
+}
+
 template <int DK, int DVT, int SPW>
 static hipError_t launch_rs(const PrefillArgs &a, hipStream_t stream)
 {
     const int BH = a.g.B * a.g.H;
+    // the greedy scan writes T events per stream at most, the fixed schedule
+    // up to max(T, 64)
+    const size_t ev_stride = a.merge_rule == DLA_FENWICK ? a.ws.ev_stride : static_cast<size_t>(a.T);
     const int nblk_dv = a.g.dv / DVT;
     const int NCH = (a.T + kChunk - 1) / kChunk;
 #define DLA_PREP_LAUNCH(FEN_)                                                                               \
     hipLaunchKernelGGL((k_chunk_prep<DK, FEN_>), dim3(NCH, BH), dim3(256), 0, stream,                      \
                        static_cast<const __bf16 *>(a.q), static_cast<const __bf16 *>(a.k),                  \
                        static_cast<const __bf16 *>(a.lam), a.T, a.g.C, a.ws.events, a.ws.chunk_ev,          \
-                       static_cast<uint8_t *>(a.ws.rec), a.sched.m_t, a.ws.init_m)
+                       static_cast<uint8_t *>(a.ws.rec), a.sched.m_t, a.ws.init_m, a.ws.init_t)
     if (a.merge_rule == DLA_FENWICK) DLA_PREP_LAUNCH(true);
     else DLA_PREP_LAUNCH(false);
 #undef DLA_PREP_LAUNCH
@@ -1182,8 +1220,8 @@ static hipError_t launch_rs(const PrefillArgs &a, hipStream_t stream)
 #define DLA_RS_LAUNCH(SBF_, CONT_)                                                                          \
     hipLaunchKernelGGL((k_prefill_rs<DK, DVT, SPW, SBF_, CONT_>), dim3(BH * nblk_dv), dim3(kRsThreads), 0, stream, \
                        static_cast<const __bf16 *>(a.v), static_cast<__bf16 *>(a.o), a.T, a.g.C, a.g.dv, nblk_dv,    \
-                       a.states, a.active, a.ws.events, a.ws.chunk_ev, static_cast<const uint8_t *>(a.ws.rec),      \
-                       a.meta, a.g.meta_stride, a.ws.init_m, a.ws.init_order)
+                       a.states, a.active, a.ws.events, ev_stride, a.ws.chunk_ev,                                   \
+                       static_cast<const uint8_t *>(a.ws.rec), a.meta, a.g.meta_stride, a.ws.init_m, a.ws.init_order)
     // streams starting from an empty cache, then those continuing one
     if (a.g.state_bf16) {
         DLA_RS_LAUNCH(true, false);
@@ -1195,6 +1233,12 @@ static hipError_t launch_rs(const PrefillArgs &a, hipStream_t stream)
 #undef DLA_RS_LAUNCH
     hipError_t e = hipGetLastError();
     if (e == hipSuccess && a.ev_after) e = hipEventRecord(a.ev_after, stream);
+    if (e == hipSuccess && a.merge_rule == DLA_FENWICK) {
+        const int gx = static_cast<int>(std::min<int64_t>((static_cast<int64_t>(a.T) * a.g.dv + 255) / 256, 64));
+        hipLaunchKernelGGL(k_fen_refused, dim3(gx, BH), dim3(256), 0, stream, static_cast<__bf16 *>(a.o), a.T, a.g.dv,
+                           a.ws.init_m);
+        e = hipGetLastError();
+    }
     return e;
 }
 

@@ -47,7 +47,8 @@
  *   - lam_t[l] weights level l (not a slot), so lam needs
  *     L(T) = bit_length(T - 1) + 1 columns: C >= L(T);
  *   - no token information is computed and tau is ignored;
- *   - dla_prefill starts the streams afresh; dla_decode_step continues them.
+ *   - dla_prefill and dla_decode_step continue the streams from t_seen, on
+ *     a cache that fixed-schedule calls left (or an empty one).
  *
  * Conventions for every entry point
  *   - Pointers named as device pointers must point to device memory the
@@ -238,15 +239,18 @@ uint64_t dla_prefill_workspace_bytes(int32_t B, int32_t H, int32_t T, int32_t C,
  * rounds each closed state once at the end of the call.
  *
  * With the cache's rule DLA_FENWICK the call follows the Log-Linear fixed
- * schedule (top of this header) and starts every stream afresh at position 0:
- * whatever the cache held is discarded.  lam[.][t][l] weights level l, and C
- * must be at least bit_length(T - 1) + 1 (DLA_ERR_ARG otherwise).  Supported
+ * schedule (top of this header), continuing each stream from t0 = t_seen on a
+ * cache that fixed-schedule calls left (or an empty one).  lam[.][t][l]
+ * weights level l.  C must be at least bit_length(T - 1) + 1 (DLA_ERR_ARG
+ * otherwise); a stream whose positions need more, bit_length(t0 + T - 1) + 1
+ * > C, is refused on the device: its outputs are NaN and its cache is left
+ * unchanged.  Supported
  * on the register-resident sweep only (bfloat16 io, C <= 32) and with float32
  * state storage (each bucket is built by a cascade of merges, which bfloat16
  * storage would round once per carry level); tau is ignored, and a sched with any non-NULL field returns DLA_ERR_UNSUPPORTED
  * (the export describes the information schedule).  The final cache holds the
- * buckets of the prefix [0, T), oldest first: popcount(T) states with their
- * starts and counts, information 0, no previous key, t_seen = T.
+ * buckets of the prefix [0, t0 + T), oldest first: popcount(t0 + T) states
+ * with their starts and counts, information 0, no previous key.
  */
 dla_status dla_prefill(const void *q, const void *k, const void *v, const void *lam,
                        void *o, int32_t T, float tau, dla_dtype io, const dla_cache *cache,

@@ -116,26 +116,64 @@ def test_fenwick_random_shapes(T, dk, dv, C, S):
     _check_cache(fin, d["k"], d["v"], T, f"T={T} dk={dk} dv={dv} C={C}")
 
 
-def test_fenwick_discards_what_the_cache_held():
-    """A prefill under the fixed schedule starts afresh: on a cache that an
-    information-driven prefill filled, it gives what it gives on an empty one,
-    bit for bit."""
+@pytest.mark.parametrize("ends", [(100, 300), (64, 128, 192), (1, 2, 3, 70), (63, 127, 1000), (500, 501, 1300),
+                                  (777, 2100)])
+def test_fenwick_prefill_continues_the_cache(ends):
+    """Prefill in pieces on one cache (chunks of later pieces not aligned to
+    the buckets) equals one pass of the oracle over all the tokens."""
     torch = torch_mod()
     import dynamic_state_memory_amd as dla
-    say("fenwick on a used cache")
-    T = 777
-    first = _inputs(500, [7, 8], 16)
-    d = _inputs(T, [9, 10], 16)
-    dev = torch.device("cuda:0")
-    used = dla.Cache(1, 2, 16, 128, 64, device=dev, merge_rule="sum")
-    _run(first, 16, cache=used)                   # an information-driven prefill
-    dla.dla_cache_set_merge_rule(used.view, dla.DLA_FENWICK)
-    o1, fin1 = _run(d, 16, cache=used)
-    o2, fin2 = _run(d, 16)
-    assert np.array_equal(o1, o2)
-    for key in ("m", "t_seen", "has_prev", "start", "count", "info"):
-        assert np.array_equal(fin1[key], fin2[key]), key
-    assert np.array_equal(fin1["S"], fin2["S"])
+    say(f"fenwick pieces {ends}")
+    T = ends[-1]
+    d = _inputs(T, [16, 17], 16)
+    cache = dla.Cache(1, 2, 16, 128, 64, device=torch.device("cuda:0"), merge_rule="fenwick")
+    outs, lo = [], 0
+    for hi in ends:
+        o, _ = _run({x: d[x][:, lo:hi] for x in ("q", "k", "v", "lam")}, 16, cache=cache)
+        outs.append(o)
+        lo = hi
+    compare_outputs(np.concatenate(outs, 1), FEN.outputs(d["q"], d["k"], d["v"], d["lam"]), TOL["bf16"],
+                    f"pieces {ends}")
+    _check_cache(cache.read(), d["k"], d["v"], T, f"pieces {ends}")
+
+
+def test_fenwick_prefill_decode_prefill():
+    """Prefill 300, decode 37 steps, prefill 500 more: one pass of the oracle."""
+    torch = torch_mod()
+    import dynamic_state_memory_amd as dla
+    say("fenwick prefill + decode + prefill")
+    T1, T2, T3 = 300, 37, 500
+    T = T1 + T2 + T3
+    d = _inputs(T, [18, 19], 16, dk=128, dv=128)
+    cache = dla.Cache(1, 2, 16, 128, 128, device=torch.device("cuda:0"), merge_rule="fenwick")
+    o1, _ = _run({x: d[x][:, :T1] for x in ("q", "k", "v", "lam")}, 16, cache=cache)
+    o2 = _decode_steps(d, T1, T1 + T2, cache, "bf16")
+    o3, _ = _run({x: d[x][:, T1 + T2:] for x in ("q", "k", "v", "lam")}, 16, cache=cache)
+    compare_outputs(np.concatenate([o1, o2, o3], 1), FEN.outputs(d["q"], d["k"], d["v"], d["lam"]), TOL["bf16"],
+                    "prefill + decode + prefill")
+    _check_cache(cache.read(), d["k"], d["v"], T, "prefill + decode + prefill")
+
+
+def test_fenwick_prefill_position_limit():
+    """C = 4 level weights cover positions 0 .. 7: a prefill of 5 tokens on a
+    stream at position 5 is refused on the device (NaN outputs, the cache as it
+    was); the same prefill of 3 tokens is not."""
+    torch = torch_mod()
+    import dynamic_state_memory_amd as dla
+    say("fenwick prefill position limit")
+    d = _inputs(10, [20], 4, dk=64, dv=16)
+    cache = dla.Cache(1, 1, 4, 64, 16, device=torch.device("cuda:0"), merge_rule="fenwick")
+    part = lambda lo, hi: {x: d[x][:, lo:hi] for x in ("q", "k", "v", "lam")}
+    _run(part(0, 5), 4, cache=cache)
+    before = cache.read()
+    o, after = _run(part(5, 10), 4, cache=cache)
+    assert np.isnan(o).all()
+    for key in ("m", "t_seen", "order", "start", "count", "S"):
+        assert np.array_equal(before[key], after[key]), key
+    o, fin = _run(part(5, 8), 4, cache=cache)
+    ref = FEN.outputs(*(d[x][:, :8] for x in ("q", "k", "v", "lam")))
+    compare_outputs(o, ref[:, 5:8], TOL["bf16"], "positions 5 .. 7")
+    _check_cache(fin, d["k"], d["v"], 8, "positions 0 .. 7")
 
 
 @pytest.mark.parametrize("name,C,T", [("gdn_1p3b_t32k_bf16", 16, None), ("long_t131k_bf16", 18, 131072 - 77)])

@@ -207,6 +207,35 @@ def test_prefill_continues_the_cache(name, streams, ends, C, means, io, rule, st
     say(f"prefill {label}: ok, merges {int(r['n_ev'].sum())}")
 
 
+def _random_cases(n, seed=7):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        io = str(rng.choice(["bf16", "bf16", "f32"]))
+        dk = 64 if io == "f32" else int(rng.choice([64, 128]))
+        dv = int(16 * rng.integers(1, 17))
+        T = int(rng.integers(1, 3000))
+        C = int(rng.integers(1, 65))
+        tau = float(rng.choice([0.1, 0.3, 0.6]))
+        means = tuple(int(x) for x in rng.choice([3, 12, 60, 400], size=int(rng.integers(1, 3)), replace=False))
+        rule = str(rng.choice(["sum", "density"]))
+        S = int(rng.integers(1, 5))
+        out.append((T, dk, dv, C, tau, means, io, rule, S if io == "bf16" else 1))   # (the fp32 workload has one stream)
+    return out
+
+
+@pytest.mark.parametrize("T,dk,dv,C,tau,means,io,rule,S", _random_cases(12))
+def test_random_shapes(T, dk, dv, C, tau, means, io, rule, S):
+    """Seeded random shapes across the supported ranges (C from 1 to 64, so
+    both prefill kernels; fp32 io at d_k = 64): schedule bit-exact, outputs and
+    final states within their gates."""
+    torch_mod()
+    base = "tiny_fp32" if io == "f32" else "gdn_1p3b_t32k_bf16"
+    cfg = dataclasses.replace(workloads.CONFIGS[base], dk=dk, dv=dv, C=C, seg_means=means)
+    d = workloads.prefill_inputs(cfg, streams=list(range(S)), T=T)
+    _full_check(d, C, tau, io, f"random T={T} dk={dk} dv={dv} C={C} tau={tau} means={means}", merge_rule=rule)
+
+
 def test_literal_noise_reading_every_token_opens(prefill_path):
     torch_mod()
     cfg = workloads.CONFIGS["gdn_1p3b_t32k_bf16"]

@@ -350,9 +350,6 @@ dla_status dla_prefill(const void *q, const void *k, const void *v, const void *
         if (cache->C < levels)
             return fail(DLA_ERR_ARG, "the fixed schedule over %d tokens needs C >= %d levels (C = %d)", T, levels,
                         cache->C);
-        if (!a.register_resident)
-            return fail(DLA_ERR_UNSUPPORTED, "the fixed schedule needs bfloat16 io and C <= 32 "
-                                             "(the register-resident prefill)");
         // every bucket is built by a cascade of merges, and with bf16 storage
         // each one re-rounds the closed values it reads: about one rounding per
         // carry level, past the bf16 output gate already at T ~ 1500

@@ -134,6 +134,8 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 size_t prefill_smem_bytes(int io_bf16, int dk, int dvt);
 hipError_t launch_prefill_rs(const PrefillArgs &a, hipStream_t stream);
+hipError_t launch_fenwick_schedule(const PrefillArgs &a, hipStream_t stream);
+hipError_t launch_fen_refused(const PrefillArgs &a, hipStream_t stream);   // NaN outputs of refused streams
 size_t prefill_rs_smem_bytes(int dk, int dvt, int C);
 int prefill_rs_dvt(int dk, int C, int dvt_wanted);
 int prefill_rs_spw(int C);      // closed-state slots per wave of the register-resident sweep

@@ -670,7 +670,8 @@ __global__ __launch_bounds__(256, 1) void k_prefill(
     float *__restrict__ states, typename ReadT<TIO>::type *__restrict__ shadow,
     const int2 *__restrict__ events, const int32_t *__restrict__ chunk_ev,
     uint8_t *__restrict__ meta_base, size_t meta_stride, int32_t *__restrict__ m_t_out,
-    const int32_t *__restrict__ init_m, const uint8_t *__restrict__ init_order)
+    const int32_t *__restrict__ init_m, const uint8_t *__restrict__ init_order, int fen, size_t ev_stride,
+    const int64_t *__restrict__ init_t)
 {
     constexpr int KS = DK / 32;     // reduction steps over d_k
     constexpr int NTV = DVT / 16;   // 16-wide tiles over the d_v slice
@@ -707,6 +708,11 @@ __global__ __launch_bounds__(256, 1) void k_prefill(
     // the states the cache holds when the call starts (their fp32 values are
     // in the cache already; with bf16 io their fp16 operand copies are made here)
     const int m_init = init_m[bh];
+    // fixed schedule (fen): a refused stream is left as it was (its outputs are
+    // set apart later); the position the call starts at
+    if (m_init < 0) return;
+    const int64_t t0 = fen ? init_t[bh] : 0;
+    const int2 *ev_s = events + static_cast<size_t>(bh) * ev_stride;
     if (tid < m_init) S.order[tid] = init_order[static_cast<size_t>(bh) * kMaxC + tid];
     m0 = m_init;
     if constexpr (kHalfRead) {
@@ -756,7 +762,7 @@ __global__ __launch_bounds__(256, 1) void k_prefill(
             const int e1 = chunk_ev[static_cast<size_t>(bh) * (NCH + 1) + ch + 1];
             uint64_t om = low_bits(m0), nm = 0;
             for (int e = e0; e < e1; ++e) {
-                const int2 ev = events[tok0 + e];
+                const int2 ev = ev_s[e];
                 const int pos = ev.x - c0;
                 if (tid >= pos) {
                     nm |= 1ull << pos;
@@ -773,10 +779,27 @@ __global__ __launch_bounds__(256, 1) void k_prefill(
         if (lane == 0) S.red[wave] = qmax;
         __syncthreads();
         const int qexp = kHalfRead ? f16_exponent(fmaxf(fmaxf(S.red[0], S.red[1]), fmaxf(S.red[2], S.red[3]))) : 0;
+        const int64_t ts = t0 + c0;         // absolute position of the chunk's first token
         for (int idx = tid; idx < m0 * kChunk; idx += 256) {
             const int i = idx / kChunk, t = idx % kChunk;
-            const int slot = __popcll(shr64(S.om[t], i + 1)) + __popcll(S.nm[t]);
-            const float w = S.lam[t][slot];
+            float w;
+            if (fen) {
+                // piece i of the fixed schedule (as in the register path's
+                // pre-pass): the i-th bucket of the chunk count it was formed
+                // for (from position 0) or of [0, ts) (continuing), read at
+                // its level; rows past the stream's end weigh 0
+                const int64_t cp = t0 > 0 ? ts : static_cast<int64_t>((ch & 1) ? ch : ch - 1) * kChunk;
+                int seen = 0;
+                int64_t first = 0;
+                for (int b = 62; b >= 0; --b)
+                    if ((cp >> b) & 1) {
+                        if (seen == i) first = cp & ~((2ll << b) - 1);
+                        ++seen;
+                    }
+                w = t < nvalid ? S.lam[t][64 - __clzll(static_cast<unsigned long long>((ts + t) ^ first))] : 0.0f;
+            } else {
+                w = S.lam[t][__popcll(shr64(S.om[t], i + 1)) + __popcll(S.nm[t])];
+            }
             S.wold[i][t] = kHalfRead ? ldexpf(w, S.shexp[S.order[i]] + qexp) : w;
         }
         // Q fragments of the whole chunk (A operand of the inter-chunk read)
@@ -871,7 +894,10 @@ __global__ __launch_bounds__(256, 1) void k_prefill(
                     const int s = 16 * nt + lr;
                     float val = 0.0f;
                     if (s <= t) {
-                        const int slot = __popcll(shr64(S.nm[t], s + 1));
+                        const int slot = !fen ? __popcll(shr64(S.nm[t], s + 1))
+                                              : (s == t || t >= nvalid) ? 0
+                                                                        : 64 - __clzll(static_cast<unsigned long long>(
+                                                                                   (ts + t) ^ (ts + s)));
                         val = A[r] * S.lam[t][slot];
                     }
                     S.pw[t][s] = from_f<TIO>(val);
@@ -1510,7 +1536,8 @@ static hipError_t prefill_main(const PrefillArgs &a, hipStream_t stream)
                        static_cast<const TIO *>(a.v), static_cast<const TIO *>(a.lam),
                        static_cast<TIO *>(a.o), a.T, a.g.C, a.g.dv, nblk_dv, a.states,
                        static_cast<typename ReadT<TIO>::type *>(a.ws.shadow), a.ws.events, a.ws.chunk_ev, a.meta,
-                       a.g.meta_stride, a.sched.m_t, a.ws.init_m, a.ws.init_order);
+                       a.g.meta_stride, a.sched.m_t, a.ws.init_m, a.ws.init_order, a.merge_rule == DLA_FENWICK ? 1 : 0,
+                       a.merge_rule == DLA_FENWICK ? a.ws.ev_stride : static_cast<size_t>(a.T), a.ws.init_t);
     hipError_t e = hipGetLastError();
     if (e == hipSuccess && a.ev_after) e = hipEventRecord(a.ev_after, stream);
     return e;
@@ -1560,10 +1587,60 @@ static hipError_t state_copy(const PrefillArgs &a, hipStream_t stream)
     return hipGetLastError();
 }
 
+// The outputs of streams the fixed schedule refused (a level weight past
+// column C - 1 would be needed; marked init_m < 0): NaN, as the decode step
+// reports the same condition.  Their caches were left as they were.
+template <typename TIO>
+__global__ __launch_bounds__(256) void k_fen_refused(TIO *__restrict__ O, int T, int DV,
+                                                     const int32_t *__restrict__ init_m)
+{
+    const int bh = blockIdx.y;
+    if (init_m[bh] >= 0) return;
+    const size_t n = static_cast<size_t>(T) * DV;
+    TIO *o = O + static_cast<size_t>(bh) * n;
+    for (size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x; i < n; i += static_cast<size_t>(gridDim.x) * 256)
+        o[i] = from_f<TIO>(__builtin_nanf(""));
+}
+
+hipError_t launch_fen_refused(const PrefillArgs &a, hipStream_t stream)
+{
+    const int gx = static_cast<int>(std::min<int64_t>((static_cast<int64_t>(a.T) * a.g.dv + 255) / 256, 64));
+    const dim3 grid(gx, a.g.B * a.g.H);
+    if (a.io_bf16)
+        hipLaunchKernelGGL(k_fen_refused<__bf16>, grid, dim3(256), 0, stream, static_cast<__bf16 *>(a.o), a.T, a.g.dv,
+                           a.ws.init_m);
+    else
+        hipLaunchKernelGGL(k_fen_refused<float>, grid, dim3(256), 0, stream, static_cast<float *>(a.o), a.T, a.g.dv,
+                           a.ws.init_m);
+    return hipGetLastError();
+}
+
+hipError_t launch_fenwick_schedule(const PrefillArgs &a, hipStream_t stream)
+{
+    const int NCH = (a.T + kChunk - 1) / kChunk;
+    hipLaunchKernelGGL(k_fenwick_schedule, dim3(a.g.B * a.g.H), dim3(256), 0, stream, a.T, NCH, a.g.C, a.g.dk,
+                       a.ws.ev_stride, a.ws.events, a.ws.chunk_ev, a.meta, a.g.meta_stride, a.ws.init_m,
+                       a.ws.init_order, a.ws.init_t);
+    return hipGetLastError();
+}
+
 template <typename TIO>
 static hipError_t prefill_typed(const PrefillArgs &a, hipStream_t stream)
 {
     hipError_t e;
+    const bool fen = a.merge_rule == DLA_FENWICK;
+    if (fen) {
+        e = launch_fenwick_schedule(a, stream);
+        if (e != hipSuccess) return e;
+        if (a.g.dk == 64)
+            e = a.dvt == 32 ? prefill_main<TIO, 64, 32>(a, stream) : prefill_main<TIO, 64, 16>(a, stream);
+        else if constexpr (sizeof(TIO) == 2)
+            e = a.dvt == 32 ? prefill_main<TIO, 128, 32>(a, stream) : prefill_main<TIO, 128, 16>(a, stream);
+        else
+            return hipErrorInvalidValue;
+        if (e != hipSuccess) return e;
+        return launch_fen_refused(a, stream);
+    }
     if (a.g.dk == 64) {
         e = prefill_schedule<TIO, 64>(a, stream);
         if (e != hipSuccess) return e;
@@ -1583,11 +1660,7 @@ static hipError_t prefill_register_resident(const PrefillArgs &a, hipStream_t st
 {
     hipError_t e;
     if (a.merge_rule == DLA_FENWICK) {
-        const int NCH = (a.T + kChunk - 1) / kChunk;
-        hipLaunchKernelGGL(k_fenwick_schedule, dim3(a.g.B * a.g.H), dim3(256), 0, stream, a.T, NCH, a.g.C, a.g.dk,
-                           a.ws.ev_stride, a.ws.events, a.ws.chunk_ev, a.meta, a.g.meta_stride, a.ws.init_m,
-                           a.ws.init_order, a.ws.init_t);
-        e = hipGetLastError();
+        e = launch_fenwick_schedule(a, stream);
     } else {
         e = a.g.dk == 128 ? prefill_schedule<__bf16, 128>(a, stream) : prefill_schedule<__bf16, 64>(a, stream);
     }

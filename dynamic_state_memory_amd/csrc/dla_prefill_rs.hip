@@ -1180,20 +1180,6 @@ __global__ __launch_bounds__(kRsThreads, 2) void k_prefill_rs(
     }
 }
 
-// The outputs of streams the fixed schedule refused (a level weight past
-// column C - 1 would be needed; marked init_m < 0): NaN, as the decode step
-// reports the same condition.  Their caches were left as they were.
-__global__ __launch_bounds__(256) void k_fen_refused(__bf16 *__restrict__ O, int T, int DV,
-                                                     const int32_t *__restrict__ init_m)
-{
-    const int bh = blockIdx.y;
-    if (init_m[bh] >= 0) return;
-    const size_t n = static_cast<size_t>(T) * DV;
-    __bf16 *o = O + static_cast<size_t>(bh) * n;
-    for (size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x; i < n; i += static_cast<size_t>(gridDim.x) * 256)
-        o[i] = static_cast<__bf16>(__builtin_nanf(""));
-}
-
 template <int DK, int DVT, int SPW>
 static hipError_t launch_rs(const PrefillArgs &a, hipStream_t stream)
 {
@@ -1233,12 +1219,7 @@ static hipError_t launch_rs(const PrefillArgs &a, hipStream_t stream)
 #undef DLA_RS_LAUNCH
     hipError_t e = hipGetLastError();
     if (e == hipSuccess && a.ev_after) e = hipEventRecord(a.ev_after, stream);
-    if (e == hipSuccess && a.merge_rule == DLA_FENWICK) {
-        const int gx = static_cast<int>(std::min<int64_t>((static_cast<int64_t>(a.T) * a.g.dv + 255) / 256, 64));
-        hipLaunchKernelGGL(k_fen_refused, dim3(gx, BH), dim3(256), 0, stream, static_cast<__bf16 *>(a.o), a.T, a.g.dv,
-                           a.ws.init_m);
-        e = hipGetLastError();
-    }
+    if (e == hipSuccess && a.merge_rule == DLA_FENWICK) e = launch_fen_refused(a, stream);
     return e;
 }
 

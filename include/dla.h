@@ -244,10 +244,9 @@ uint64_t dla_prefill_workspace_bytes(int32_t B, int32_t H, int32_t T, int32_t C,
  * weights level l.  C must be at least bit_length(T - 1) + 1 (DLA_ERR_ARG
  * otherwise); a stream whose positions need more, bit_length(t0 + T - 1) + 1
  * > C, is refused on the device: its outputs are NaN and its cache is left
- * unchanged.  Supported
- * on the register-resident sweep only (bfloat16 io, C <= 32) and with float32
- * state storage (each bucket is built by a cascade of merges, which bfloat16
- * storage would round once per carry level); tau is ignored, and a sched with any non-NULL field returns DLA_ERR_UNSUPPORTED
+ * unchanged.  float32 state storage only (each bucket is built by a cascade
+ * of merges, which bfloat16 storage would round once per carry level); tau is
+ * ignored, and a sched with any non-NULL field returns DLA_ERR_UNSUPPORTED
  * (the export describes the information schedule).  The final cache holds the
  * buckets of the prefix [0, t0 + T), oldest first: popcount(t0 + T) states
  * with their starts and counts, information 0, no previous key.

@@ -170,11 +170,6 @@ def test_fenwick_rule_checks_on_the_host(monkeypatch):
 
     # 129 tokens need 9 level weights
     assert pre(129) == dla.DLA_ERR_ARG and "levels" in dla.dla_last_error()
-    # only on the register-resident sweep
-    assert pre(128, io=dla.DLA_F32) == dla.DLA_ERR_UNSUPPORTED
-    monkeypatch.setenv("DLA_PREFILL_PATH", "streamed")
-    assert pre(100) == dla.DLA_ERR_UNSUPPORTED
-    monkeypatch.delenv("DLA_PREFILL_PATH")
     # float32 state storage only
     cb = _cache()
     cb.state_dtype = dla.DLA_BF16

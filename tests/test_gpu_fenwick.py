@@ -154,6 +154,34 @@ def test_fenwick_prefill_decode_prefill():
     _check_cache(cache.read(), d["k"], d["v"], T, "prefill + decode + prefill")
 
 
+@pytest.mark.parametrize("io,dk,ends", [("f32", 64, (300,)), ("f32", 64, (100, 613, 1000)),
+                                        ("bf16", 128, (700,)), ("bf16", 64, (65, 400, 1100))])
+def test_fenwick_streamed_kernel(io, dk, ends, monkeypatch):
+    """The fixed schedule on the streamed prefill kernel (fp32 io; bf16 io
+    forced there): from position 0 and continuing, one pass of the oracle."""
+    torch = torch_mod()
+    import dynamic_state_memory_amd as dla
+    monkeypatch.setenv("DLA_PREFILL_PATH", "streamed")
+    say(f"fenwick streamed io={io} dk={dk} ends={ends}")
+    T = ends[-1]
+    d = _inputs(T, [21, 22], 16, dk=dk, dv=32)
+    dev = torch.device("cuda:0")
+    dt = torch.float32 if io == "f32" else torch.bfloat16
+    cache = dla.Cache(1, 2, 16, dk, 32, device=dev, merge_rule="fenwick")
+    outs, lo = [], 0
+    for hi in ends:
+        def up(a, n):
+            return torch.from_numpy(np.ascontiguousarray(a[:, lo:hi])).to(dev).to(dt).reshape(1, 2, hi - lo, n)
+        ws = dla.prefill_workspace(1, 2, hi - lo, 16, dk, 32, dev)
+        o = dla.prefill(up(d["q"], dk), up(d["k"], dk), up(d["v"], 32), up(d["lam"], 16), 0.0, cache, workspace=ws)
+        outs.append(o.float().cpu().numpy().reshape(2, hi - lo, 32))
+        lo = hi
+    torch.cuda.synchronize()
+    compare_outputs(np.concatenate(outs, 1), FEN.outputs(d["q"], d["k"], d["v"], d["lam"]), TOL[io],
+                    f"streamed {io} {ends}")
+    _check_cache(cache.read(), d["k"], d["v"], T, f"streamed {io} {ends}")
+
+
 def test_fenwick_prefill_position_limit():
     """C = 4 level weights cover positions 0 .. 7: a prefill of 5 tokens on a
     stream at position 5 is refused on the device (NaN outputs, the cache as it

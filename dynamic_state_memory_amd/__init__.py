@@ -16,10 +16,10 @@ import numpy as np
 __all__ = [
     "DLA_OK", "DLA_F32", "DLA_BF16", "DLAError", "lib_path", "load",
     "dla_abi_version", "dla_cache_bytes", "dla_cache_layout", "dla_cache_init",
-    "dla_prefill_workspace_bytes", "dla_prefill", "dla_decode_step",
+    "dla_prefill_workspace_bytes", "dla_prefill", "dla_prefill_noalloc", "dla_decode_step",
     "dla_status_str", "dla_last_error", "dla_set_prefill_events", "Cache", "prefill",
     "decode_step",
-    "prefill_workspace", "DLA_MAX_C", "DLA_CHUNK",
+    "prefill_workspace", "prefill_noalloc", "DLA_MAX_C", "DLA_CHUNK", "DLA_NOALLOC_SCRATCH_BYTES",
 ]
 
 DLA_OK, DLA_ERR_ARG, DLA_ERR_UNSUPPORTED, DLA_ERR_WORKSPACE, DLA_ERR_HIP = 0, 1, 2, 3, 4
@@ -28,6 +28,7 @@ DLA_MERGE_SUM, DLA_MERGE_DENSITY, DLA_FENWICK = 0, 1, 2
 MERGE_RULES = {"sum": DLA_MERGE_SUM, "density": DLA_MERGE_DENSITY, "fenwick": DLA_FENWICK}
 DLA_MAX_C = 64
 DLA_CHUNK = 64
+DLA_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB = os.path.join(_PKG, "_build", "libdla.so")
@@ -104,6 +105,9 @@ def load():
     lib.dla_prefill.restype = C.c_int
     lib.dla_prefill.argtypes = [vp, vp, vp, vp, vp, i32, f32, C.c_int, C.POINTER(dla_cache), vp,
                                 u64, C.POINTER(dla_schedule_out), vp]
+    lib.dla_prefill_noalloc.restype = C.c_int
+    lib.dla_prefill_noalloc.argtypes = [vp, vp, vp, vp, vp, i32, f32, C.c_int, C.POINTER(dla_cache),
+                                        C.POINTER(dla_schedule_out), vp]
     lib.dla_decode_step.restype = C.c_int
     lib.dla_decode_step.argtypes = [vp, vp, vp, vp, vp, f32, C.c_int, C.POINTER(dla_cache),
                                     C.POINTER(dla_schedule_out), vp]
@@ -154,6 +158,12 @@ def dla_prefill(q, k, v, lam, o, T, tau, io, cache: dla_cache, workspace, worksp
     return load().dla_prefill(q, k, v, lam, o, T, tau, io, C.byref(cache), workspace,
                               workspace_bytes, C.byref(sched) if sched is not None else None,
                               stream)
+
+
+def dla_prefill_noalloc(q, k, v, lam, o, T, tau, io, cache: dla_cache,
+                        sched: dla_schedule_out | None, stream) -> int:
+    return load().dla_prefill_noalloc(q, k, v, lam, o, T, tau, io, C.byref(cache),
+                                      C.byref(sched) if sched is not None else None, stream)
 
 
 def dla_decode_step(q, k, v, lam, o, tau, io, cache: dla_cache,
@@ -345,6 +355,25 @@ def prefill(q, k, v, lam, tau: float, cache: Cache, o=None, workspace=None, sche
         workspace = prefill_workspace(B, H, T, C_, dk, dv, q.device)
     _check(dla_prefill(*args, T, float(tau), io, cache.view, workspace.data_ptr(),
                        workspace.numel(), _sched_struct(sched), _stream(q.device)))
+    return o
+
+
+def prefill_noalloc(q, k, v, lam, tau: float, cache: Cache, o=None, sched: dict | None = None):
+    """dla_prefill_noalloc on torch tensors (as ``prefill``; the library's
+    static scratch replaces the workspace, so nothing is allocated but ``o``
+    when it is not given)."""
+    torch = _torch()
+    B, H, C_, dk, dv = cache.shape
+    T = q.shape[2]
+    io = _io_of(q)
+    dt = q.dtype
+    args = [_dev(q, "q", (B, H, T, dk), dt), _dev(k, "k", (B, H, T, dk), dt),
+            _dev(v, "v", (B, H, T, dv), dt), _dev(lam, "lam", (B, H, T, C_), dt)]
+    if o is None:
+        o = torch.empty((B, H, T, dv), dtype=dt, device=q.device)
+    args.append(_dev(o, "o", (B, H, T, dv), dt))
+    _check(dla_prefill_noalloc(*args, T, float(tau), io, cache.view, _sched_struct(sched),
+                               _stream(q.device)))
     return o
 
 

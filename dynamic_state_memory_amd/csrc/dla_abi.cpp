@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "dla.h"
 #include "dla_internal.h"
@@ -206,6 +207,45 @@ PrefillPlan plan_prefill(bool io_bf16, int64_t BH, int C, int dk, int dv)
 
 thread_local char g_kernel_name[48];
 
+// Static scratch of dla_prefill_noalloc: the prefill workspace for callers
+// that cannot allocate.  One copy per device, held from the library's load on
+// that device until the process ends.  Host code never passes the array's
+// name to a kernel (on the host it is only a stand-in for the symbol): it uses
+// the device address that hipGetSymbolAddress returns, looked up once per
+// device with that device current.
+static __device__ __align__(256) uint8_t scratch[DLA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// The scratch address of the device current on this thread, which must be
+// the device of `stream`.
+dla_status device_scratch(hipStream_t stream, void **out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(DLA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(DLA_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+    if (stream) {
+        hipDevice_t sdev = -1;
+        e = hipStreamGetDevice(stream, &sdev);
+        if (e != hipSuccess) return fail(DLA_ERR_HIP, "hipStreamGetDevice: %s", hipGetErrorString(e));
+        if (sdev != dev)
+            return fail(DLA_ERR_ARG, "the stream belongs to device %d, the current device is %d", sdev, dev);
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(DLA_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return DLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -311,9 +351,17 @@ uint64_t dla_prefill_workspace_bytes(int32_t B, int32_t H, int32_t T, int32_t C,
     return workspace_sizes(static_cast<int64_t>(B) * H, T, C, d_k, d_v).total;
 }
 
-dla_status dla_prefill(const void *q, const void *k, const void *v, const void *lam, void *o, int32_t T,
-                       float tau, dla_dtype io, const dla_cache *cache, void *workspace,
-                       uint64_t workspace_bytes, const dla_schedule_out *sched, void *stream)
+}  // extern "C"
+
+namespace {
+
+// Every check of a prefill call, then the launches.  With `scratch_only` the
+// workspace is the library's static scratch of the stream's device (the
+// arguments workspace and workspace_bytes are ignored): the call allocates
+// nothing.
+dla_status prefill_call(const void *q, const void *k, const void *v, const void *lam, void *o, int32_t T, float tau,
+                        dla_dtype io, const dla_cache *cache, void *workspace, uint64_t workspace_bytes,
+                        const dla_schedule_out *sched, void *stream, bool scratch_only)
 {
     dla_status s = check_cache(cache);
     if (s != DLA_OK) return s;
@@ -329,10 +377,20 @@ dla_status dla_prefill(const void *q, const void *k, const void *v, const void *
         return fail(DLA_ERR_ARG, "schedule export: ev_t and ev_i go together");
     const int64_t BH = static_cast<int64_t>(cache->B) * cache->H;
     const Sizes z = workspace_sizes(BH, T, cache->C, cache->d_k, cache->d_v);
-    if (!workspace || !aligned(workspace, 256)) return fail(DLA_ERR_WORKSPACE, "workspace NULL or not 256-byte aligned");
-    if (workspace_bytes < z.total)
-        return fail(DLA_ERR_WORKSPACE, "workspace of %llu bytes, %llu needed",
-                    static_cast<unsigned long long>(workspace_bytes), static_cast<unsigned long long>(z.total));
+    if (scratch_only) {
+        if (z.total > DLA_NOALLOC_SCRATCH_BYTES)
+            return fail(DLA_ERR_WORKSPACE,
+                        "this call needs %llu bytes of scratch; the static scratch holds %llu (use dla_prefill "
+                        "with a workspace)",
+                        static_cast<unsigned long long>(z.total),
+                        static_cast<unsigned long long>(DLA_NOALLOC_SCRATCH_BYTES));
+    } else {
+        if (!workspace || !aligned(workspace, 256))
+            return fail(DLA_ERR_WORKSPACE, "workspace NULL or not 256-byte aligned");
+        if (workspace_bytes < z.total)
+            return fail(DLA_ERR_WORKSPACE, "workspace of %llu bytes, %llu needed",
+                        static_cast<unsigned long long>(workspace_bytes), static_cast<unsigned long long>(z.total));
+    }
     PrefillArgs a;
     a.q = q; a.k = k; a.v = v; a.lam = lam; a.o = o;
     a.T = T;
@@ -364,6 +422,11 @@ dla_status dla_prefill(const void *q, const void *k, const void *v, const void *
     a.states = reinterpret_cast<float *>(b8 + co.states);
     a.active = a.g.state_bf16 ? reinterpret_cast<float *>(b8 + co.active) : nullptr;
     a.meta = b8 + co.meta;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (scratch_only) {
+        dla_status ss = device_scratch(st, &workspace);
+        if (ss != DLA_OK) return ss;
+    }
     a.ws = carve(workspace, z);
     a.ev_before = g_ev_before;
     a.ev_after = g_ev_after;
@@ -371,7 +434,6 @@ dla_status dla_prefill(const void *q, const void *k, const void *v, const void *
     else std::memset(&a.sched, 0, sizeof(a.sched));
     // schedule fields the prefill kernels never fill are ignored; s and boundary
     // are copied from the workspace afterwards
-    hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e = launch_prefill(a, st);
     if (e != hipSuccess) return hip_status(e, "prefill launch");
     if (sched && sched->s) {
@@ -383,6 +445,24 @@ dla_status dla_prefill(const void *q, const void *k, const void *v, const void *
         if (e != hipSuccess) return hip_status(e, "schedule copy");
     }
     return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+dla_status dla_prefill(const void *q, const void *k, const void *v, const void *lam, void *o, int32_t T,
+                       float tau, dla_dtype io, const dla_cache *cache, void *workspace,
+                       uint64_t workspace_bytes, const dla_schedule_out *sched, void *stream)
+{
+    return prefill_call(q, k, v, lam, o, T, tau, io, cache, workspace, workspace_bytes, sched, stream, false);
+}
+
+dla_status dla_prefill_noalloc(const void *q, const void *k, const void *v, const void *lam, void *o, int32_t T,
+                               float tau, dla_dtype io, const dla_cache *cache, const dla_schedule_out *sched,
+                               void *stream)
+{
+    return prefill_call(q, k, v, lam, o, T, tau, io, cache, nullptr, 0, sched, stream, true);
 }
 
 const char *dla_prefill_kernel(dla_dtype io, int32_t B, int32_t H, int32_t C, int32_t d_k, int32_t d_v)

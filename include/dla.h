@@ -75,6 +75,8 @@ extern "C" {
 #define DLA_ABI_VERSION 5
 #define DLA_MAX_C 64        /* largest supported cache capacity */
 #define DLA_CHUNK 64        /* tokens per prefill chunk */
+/* bytes of the static per-device scratch of dla_prefill_noalloc (64 MiB) */
+#define DLA_NOALLOC_SCRATCH_BYTES (64ull << 20)
 
 typedef enum dla_status {
     DLA_OK = 0,
@@ -255,6 +257,28 @@ dla_status dla_prefill(const void *q, const void *k, const void *v, const void *
                        void *o, int32_t T, float tau, dla_dtype io, const dla_cache *cache,
                        void *workspace, uint64_t workspace_bytes,
                        const dla_schedule_out *sched, void *stream);
+
+/*
+ * dla_prefill without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same computation, arguments and results as
+ * dla_prefill, with the workspace taken from a static scratch array of
+ * DLA_NOALLOC_SCRATCH_BYTES bytes that the library holds on each device it
+ * runs on, from its load there until the process ends.  The call allocates
+ * and frees nothing.
+ *   - The scratch is the one of the device current on the calling thread;
+ *     `stream` must belong to that device (DLA_ERR_ARG otherwise).
+ *   - A call whose dla_prefill_workspace_bytes exceeds
+ *     DLA_NOALLOC_SCRATCH_BYTES returns DLA_ERR_WORKSPACE with nothing
+ *     enqueued (use dla_prefill with a workspace then).
+ *   - Every call on a device shares that device's scratch, which keeps the
+ *     last call's contents (nothing in it needs to start at zero): calls that
+ *     overlap on one device race, so calls on different streams of one device
+ *     must be ordered by the caller.
+ */
+dla_status dla_prefill_noalloc(const void *q, const void *k, const void *v, const void *lam,
+                               void *o, int32_t T, float tau, dla_dtype io, const dla_cache *cache,
+                               const dla_schedule_out *sched, void *stream);
 
 /*
  * Name of the chunk kernel (the MFMA sweep after the schedule kernels) that

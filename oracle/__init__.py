@@ -74,10 +74,12 @@ class _Args(C.Structure):
         ("fin_m", _p), ("fin_S", _p), ("fin_I", _p), ("fin_n", _p), ("fin_start", _p),
         ("fin_has_prev", _p), ("fin_s_prev", _p), ("fin_k_prev", _p),
         ("fin_t_seen", _p), ("nthreads", C.c_int32), ("merge_rule", C.c_int32),
+        ("score_rule", C.c_int32),
     ]
 
 
 MERGE_RULES = {"sum": 0, "density": 1}
+SCORE_RULES = {"cosine": 0, "state": 1}
 
 
 def _ptr(a):
@@ -90,11 +92,19 @@ def _c(a, dt):
 
 def run(q, k, v, lam, C_: int, tau: float, init: dict | None = None,
         want=None, outputs: bool = True, final_states: bool = True,
-        nthreads: int | None = None, lib=None, merge_rule: str = "sum") -> dict:
+        nthreads: int | None = None, lib=None, merge_rule: str = "sum",
+        score_rule: str = "cosine") -> dict:
     """Run the oracle on float32 inputs q,k [S,T,dk], v [S,T,dv], lam [S,T,C].
 
     ``merge_rule``: "sum" merges the adjacent pair of smallest summed
     information, "density" the pair of lowest (I_i + I_{i+1}) / (n_i + n_{i+1}).
+    ``score_rule``: "cosine" scores a token by 1 - cos(k_t, k_{t-1}) and opens
+    a state unless it and the token before are both below tau; "state" scores
+    it by the state information score against the current state (the
+    per-token state v k^T and the most recent state, each RMS-normalised,
+    Frobenius distance over the normalised current state's norm + 1e-6) and
+    opens a state when the score is at least tau.  The ``s`` output holds the
+    score either way.
 
     ``init``: optional starting cache, dict with m [S], S [S,C,dv,dk] (float64
     or float32), I [S,C] int64, n [S,C] int32, start [S,C] int64, has_prev [S],
@@ -155,6 +165,7 @@ def run(q, k, v, lam, C_: int, tau: float, init: dict | None = None,
     out("fin_t_seen", (S_,), np.int64, "fin_t_seen")
     a.nthreads = int(nthreads or os.environ.get("DLA_ORACLE_THREADS", 0) or os.cpu_count() or 1)
     a.merge_rule = MERGE_RULES[merge_rule]
+    a.score_rule = SCORE_RULES[score_rule]
     rc = (lib or _load()).dlao_run(C.byref(a))
     if rc != 0:
         raise RuntimeError(f"dlao_run failed with code {rc}")
@@ -217,7 +228,7 @@ def brute_force(q, k, v, lam, sets, rows=None) -> np.ndarray:
 
 
 def check_schedule(s, tau: float, C_: int, boundaries, events, m_t=None,
-                   init=None, merge_rule: str = "sum") -> None:
+                   init=None, merge_rule: str = "sum", score_rule: str = "cosine") -> None:
     """Assert that a schedule is exactly what the greedy rule produces from s.
 
     Re-derives from the float32 token information ``s`` alone: every boundary
@@ -227,7 +238,9 @@ def check_schedule(s, tau: float, C_: int, boundaries, events, m_t=None,
     are recomputed from the token ranges it covers, and the merged pair must
     be the earliest adjacent pair of minimal summed information ("sum") or of
     minimal information density, (I_i + I_{i+1}) / (n_i + n_{i+1}) as an exact
-    fraction ("density").  ``init`` (optional) is a starting cache: dict with
+    fraction ("density").  With ``score_rule="state"`` the boundary rule is
+    the single-token one, s_t >= tau (or an empty cache).  ``init`` (optional)
+    is a starting cache: dict with
     starts (list, oldest first, relative to this call's token 0), infos (int64
     list), counts (int list; needed by "density") and s_prev (float) /
     has_prev.
@@ -261,9 +274,13 @@ def check_schedule(s, tau: float, C_: int, boundaries, events, m_t=None,
         lo = max(a, 0)
         return max(b_end - lo, 0) + sum(int(x) for p, x in base_count.items() if a <= p < b_end)
 
+    assert score_rule in ("cosine", "state")
     for t in range(T):
-        low = (s[t] < tau32) and (prev < tau32)
-        expect_b = (len(starts) == 0) or (not low)
+        if score_rule == "state":
+            expect_b = (len(starts) == 0) or bool(s[t] >= tau32)
+        else:
+            low = (s[t] < tau32) and (prev < tau32)
+            expect_b = (len(starts) == 0) or (not low)
         assert bool(boundaries[t]) == expect_b, f"boundary mismatch at token {t}"
         if expect_b:
             starts.append(t)
@@ -287,3 +304,44 @@ def check_schedule(s, tau: float, C_: int, boundaries, events, m_t=None,
         if m_t is not None:
             assert int(m_t[t]) == len(starts), f"m_t mismatch at token {t}"
         prev = s[t]
+
+
+def state_scores_closed_form(v, k, sets, init_last=None, eps: float = 1e-6) -> np.ndarray:
+    """State information scores of one stream recomputed from a schedule.
+
+    For token t the current state is the most recent state after token t-1,
+    the sum of v_s k_s^T over its tokens [a, t) with a the largest start in
+    ``sets[t-1]``; ``init_last`` = (start, S) gives the most recent state of a
+    starting cache (its start < 0), the current state of token 0.  With
+    c = <v_t k_t^T, S>_F / (|v_t k_t^T|_F |S|_F) = v_t^T S k_t / (|v_t| |k_t| |S|_F),
+    each RMS-normalised matrix has Frobenius norm sqrt(D) (D = d_v d_k) and
+    |N(a) - N(S)|_F^2 = 2 D (1 - c), so the score is
+    sqrt(2 D (1 - c)) / (sqrt(D) + eps); 2 without a current state or for a
+    zero matrix.  float64; the current state is summed afresh from its token
+    range, not taken from the oracle's bookkeeping.
+    """
+    v = np.asarray(v, np.float64)
+    k = np.asarray(k, np.float64)
+    T, dv = v.shape
+    D = float(dv * k.shape[1])
+    out = np.zeros(T)
+    a, S = (None, None) if init_last is None else (init_last[0], np.array(init_last[1], np.float64))
+    for t in range(T):
+        if t > 0:
+            a_new = max(sets[t - 1])
+            if a_new == a:
+                S = S + np.outer(v[t - 1], k[t - 1])
+            else:
+                assert a_new >= 0, "a state older than the call cannot become the most recent one"
+                S = v[a_new:t].T @ k[a_new:t]
+                a = a_new
+        if S is None:
+            out[t] = 2.0
+            continue
+        nv, nk, ns = np.linalg.norm(v[t]), np.linalg.norm(k[t]), np.linalg.norm(S)
+        if nv * nk == 0.0 or ns == 0.0:
+            out[t] = 2.0
+        else:
+            c = float(v[t] @ S @ k[t]) / (nv * nk * ns)
+            out[t] = np.sqrt(max(0.0, 2.0 * D * (1.0 - c))) / (np.sqrt(D) + eps)
+    return out

@@ -81,6 +81,7 @@ typedef struct {
     int64_t *fin_t_seen;            /* [BH] */
     int32_t nthreads;
     int32_t merge_rule;             /* 0: smallest summed information; 1: lowest density */
+    int32_t score_rule;             /* 0: cosine of consecutive keys; 1: state information score */
 } dlao_args;
 
 /* s_t = 1 - cos(k_t, k_prev), rounded once to float. */
@@ -95,6 +96,39 @@ static float token_information(const float *kt, const float *kp, int dk)
     double ab = a * b;
     if (ab == 0.0) return 1.0f;
     return (float)(1.0 - d / sqrt(ab));
+}
+
+/* State Information Score (reading notes, section 5.1): the per-token state
+ * a = v_t k_t^T is compared with the current state Sc, the most recent state
+ * of the cache after token t-1; both are first divided by their root mean
+ * square (RMSNorm with unit gain), and
+ *     I_t = ||N(a) - N(Sc)||_F / (||N(Sc)||_F + eps),   eps = 1e-6,
+ * rounded once to float.  Without a current state (empty cache), or when a
+ * or Sc is the zero matrix (its normalisation is undefined), I_t = 2, the
+ * largest value the score takes otherwise. */
+static float state_information(const float *vt, const float *kt, const double *Sc, int dv, int dk)
+{
+    if (!Sc) return 2.0f;
+    const double D = (double)dv * (double)dk;
+    double a2 = 0.0, c2 = 0.0;
+    for (int r = 0; r < dv; ++r)
+        for (int c = 0; c < dk; ++c) {
+            const double x = (double)vt[r] * (double)kt[c];
+            const double y = Sc[(size_t)r * dk + c];
+            a2 += x * x;
+            c2 += y * y;
+        }
+    if (a2 == 0.0 || c2 == 0.0) return 2.0f;
+    const double ra = sqrt(a2 / D), rc = sqrt(c2 / D);
+    double diff = 0.0, nc = 0.0;
+    for (int r = 0; r < dv; ++r)
+        for (int c = 0; c < dk; ++c) {
+            const double na = (double)vt[r] * (double)kt[c] / ra;
+            const double ns = Sc[(size_t)r * dk + c] / rc;
+            diff += (na - ns) * (na - ns);
+            nc += ns * ns;
+        }
+    return (float)(sqrt(diff) / (sqrt(nc) + 1e-6));
 }
 
 static void run_stream(const dlao_args *A, int bh, double *S, int64_t *I,
@@ -128,10 +162,19 @@ static void run_stream(const dlao_args *A, int bh, double *S, int64_t *I,
         const float *vt = A->v + row * dv;
         const float *lt = A->lam + row * C;
 
-        /* 1. token information */
-        float s = has_prev ? token_information(kt, kprev, dk) : 1.0f;
-        /* 2. boundary: open a state unless this and the previous token are both low */
-        int bnd = (m == 0) || !((s < tau) && (s_prev < tau));
+        /* 1. token information: the cosine score of consecutive keys, or
+         * (score_rule 1) the state information score against the current state */
+        float s;
+        int bnd;
+        if (A->score_rule == 1) {
+            s = state_information(vt, kt, m > 0 ? S + (size_t)(m - 1) * SS : NULL, dv, dk);
+            /* 2'. boundary indicator b_t = [I_t >= tau] (section 5.1) */
+            bnd = (m == 0) || (s >= tau);
+        } else {
+            s = has_prev ? token_information(kt, kprev, dk) : 1.0f;
+            /* 2. boundary: open a state unless this and the previous token are both low */
+            bnd = (m == 0) || !((s < tau) && (s_prev < tau));
+        }
         int64_t qs = llrint(ldexp((double)s, 32));
 
         if (bnd) {
@@ -245,6 +288,7 @@ int dlao_run(const dlao_args *A)
                       !A->init_t_seen)) return -1;
     if (A->ev_t && (!A->ev_i || !A->n_ev)) return -1;
     if (A->merge_rule != 0 && A->merge_rule != 1) return -1;
+    if (A->score_rule != 0 && A->score_rule != 1) return -1;
     if (A->init_m)
         for (int bh = 0; bh < A->BH; ++bh)
             if (A->init_m[bh] < 0 || A->init_m[bh] > A->C) return -1;

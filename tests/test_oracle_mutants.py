@@ -10,6 +10,7 @@ import pytest
 
 import oracle
 from tests import test_oracle as P
+from tests import test_oracle_state_score as Q
 
 SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "dla_oracle.c")
 
@@ -75,6 +76,28 @@ MUTANTS = [
      "den = (__int128)n[i] + n[i + 1];", "den = (__int128)n[i];"),
     ("density rule ignored",
      "if (A->merge_rule == 1) {", "if (0) {"),
+    # the state information score
+    ("state score without the normalisation",
+     "const double ra = sqrt(a2 / D), rc = sqrt(c2 / D);", "const double ra = 1.0, rc = 1.0;"),
+    ("state score against the oldest state",
+     "m > 0 ? S + (size_t)(m - 1) * SS : NULL", "m > 0 ? S : NULL"),
+    ("state score drops the current state from the numerator",
+     "diff += (na - ns) * (na - ns);", "diff += na * na;"),
+    ("state score with a reversed key index",
+     "const double na = (double)vt[r] * (double)kt[c] / ra;",
+     "const double na = (double)vt[r] * (double)kt[dk - 1 - c] / ra;"),
+    ("state score with eps = 1",
+     "return (float)(sqrt(diff) / (sqrt(nc) + 1e-6));", "return (float)(sqrt(diff) / (sqrt(nc) + 1.0));"),
+    ("state score of an empty cache is 1",
+     "if (!Sc) return 2.0f;", "if (!Sc) return 1.0f;"),
+    ("state score of a zero matrix is 0",
+     "if (a2 == 0.0 || c2 == 0.0) return 2.0f;", "if (a2 == 0.0 || c2 == 0.0) return 0.0f;"),
+    ("state boundary at equality treated as low",
+     "bnd = (m == 0) || (s >= tau);", "bnd = (m == 0) || (s > tau);"),
+    ("state rule keeps the two-low boundary rule",
+     "bnd = (m == 0) || (s >= tau);", "bnd = (m == 0) || !((s < tau) && (s_prev < tau));"),
+    ("state rule ignored",
+     "if (A->score_rule == 1) {", "if (0) {"),
 ]
 
 
@@ -94,6 +117,12 @@ def _battery():
     out.append(("single state", lambda lib: P.pin_single_state(0.3, lib)))
     out.append(("dense slot weighted", P.pin_dense_slot_weighted))
     out.append(("prefix sum", P.pin_prefix_sum))
+    for args in [(120, 4, 3, 3, 0.3, 1), (100, 6, 6, 2, 0.3, 2), (80, 8, 5, 5, 0.15, 3)]:
+        out.append((f"state score closed form {args}", lambda lib, a=args: Q.pin_state_closed_form(*a, lib=lib)))
+    out.append(("state score special cases", Q.pin_state_special_cases))
+    for case in Q._golden():
+        out.append((f"state golden {case['name']}", lambda lib, c=case: Q.pin_state_golden(c, lib)))
+    out.append(("state continuation", Q.pin_state_continuation))
     return out
 
 

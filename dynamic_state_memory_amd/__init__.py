@@ -17,7 +17,7 @@ __all__ = [
     "DLA_OK", "DLA_F32", "DLA_BF16", "DLAError", "lib_path", "load",
     "dla_abi_version", "dla_cache_bytes", "dla_cache_layout", "dla_cache_init",
     "dla_prefill_workspace_bytes", "dla_prefill", "dla_prefill_noalloc", "dla_decode_step",
-    "dla_status_str", "dla_last_error", "dla_set_prefill_events", "Cache", "prefill",
+    "dla_status_str", "dla_last_error", "dla_set_prefill_events", "dla_set_prefill_path", "Cache", "prefill",
     "decode_step",
     "prefill_workspace", "prefill_noalloc", "DLA_MAX_C", "DLA_CHUNK", "DLA_NOALLOC_SCRATCH_BYTES",
 ]
@@ -25,6 +25,7 @@ __all__ = [
 DLA_OK, DLA_ERR_ARG, DLA_ERR_UNSUPPORTED, DLA_ERR_WORKSPACE, DLA_ERR_HIP = 0, 1, 2, 3, 4
 DLA_F32, DLA_BF16 = 0, 1
 DLA_MERGE_SUM, DLA_MERGE_DENSITY, DLA_FENWICK = 0, 1, 2
+DLA_PATH_AUTO, DLA_PATH_STREAMED = 0, 1
 MERGE_RULES = {"sum": DLA_MERGE_SUM, "density": DLA_MERGE_DENSITY, "fenwick": DLA_FENWICK}
 DLA_MAX_C = 64
 DLA_CHUNK = 64
@@ -111,6 +112,8 @@ def load():
     lib.dla_decode_step.restype = C.c_int
     lib.dla_decode_step.argtypes = [vp, vp, vp, vp, vp, f32, C.c_int, C.POINTER(dla_cache),
                                     C.POINTER(dla_schedule_out), vp]
+    lib.dla_set_prefill_path.restype = C.c_int
+    lib.dla_set_prefill_path.argtypes = [i32, i32]
     lib.dla_set_prefill_events.restype = C.c_int
     lib.dla_set_prefill_events.argtypes = [vp, vp]
     lib.dla_prefill_kernel.restype = C.c_char_p
@@ -170,6 +173,10 @@ def dla_decode_step(q, k, v, lam, o, tau, io, cache: dla_cache,
                     sched: dla_schedule_out | None, stream) -> int:
     return load().dla_decode_step(q, k, v, lam, o, tau, io, C.byref(cache),
                                   C.byref(sched) if sched is not None else None, stream)
+
+
+def dla_set_prefill_path(path: int, value_columns: int = 0) -> int:
+    return load().dla_set_prefill_path(path, value_columns)
 
 
 def dla_set_prefill_events(before, after) -> int:
@@ -282,29 +289,37 @@ class Cache:
     def device(self):
         return self.buf.device
 
-    def read(self) -> dict:
-        """Copy the cache to the host: states in chronological order, metadata."""
+    def read(self, streams=None) -> dict:
+        """Copy the cache to the host: states in chronological order, metadata.
+
+        ``streams``: flat stream indices (b * H + h) to copy, in that order
+        (default every stream); only their bytes leave the device."""
         torch = _torch()
         torch.cuda.synchronize(self.buf.device)
         B, H, C_, dk, dv = self.shape
         BH = B * H
-        raw = self.buf.cpu().numpy()
+        sel = list(range(BH)) if streams is None else [int(x) for x in streams]
+        n = len(sel)
         L = self.layout
         bf = self.state_dtype == "bf16"
+        ti = torch.tensor(sel, dtype=torch.int64, device=self.buf.device)
+        esz = 2 if bf else 4
+        slots = self.buf[L.states_offset:L.states_offset + esz * BH * C_ * dv * dk].view(BH, -1)
+        slots = slots.index_select(0, ti).cpu().numpy()
         if bf:
             # closed states: bf16 bits widened to float32; the active ones: float32 region
-            u16 = raw[L.states_offset:L.states_offset + 2 * BH * C_ * dv * dk].view(np.uint16)
-            states = (u16.astype(np.uint32) << 16).view(np.float32).reshape(BH, C_, dv, dk)
-            active = raw[L.active_offset:L.active_offset + 4 * BH * dv * dk].view(np.float32)
-            active = active.reshape(BH, dv, dk)
+            u16 = slots.view(np.uint16).reshape(n, C_, dv, dk)
+            states = (u16.astype(np.uint32) << 16).view(np.float32)
+            act = self.buf[L.active_offset:L.active_offset + 4 * BH * dv * dk].view(BH, -1)
+            active = act.index_select(0, ti).cpu().numpy().view(np.float32).reshape(n, dv, dk)
         else:
-            states = raw[L.states_offset:L.states_offset + 4 * BH * C_ * dv * dk].view(np.float32)
-            states = states.reshape(BH, C_, dv, dk)
-        meta = raw[L.meta_offset:L.meta_offset + BH * L.meta_stride].reshape(BH, L.meta_stride)
+            states = slots.view(np.float32).reshape(n, C_, dv, dk)
+        meta = self.buf[L.meta_offset:L.meta_offset + BH * L.meta_stride].view(BH, L.meta_stride)
+        meta = meta.index_select(0, ti).cpu().numpy()
 
-        def field(off, dt, n):
+        def field(off, dt, k):
             w = np.dtype(dt).itemsize
-            return np.ascontiguousarray(meta[:, off:off + w * n]).view(dt).reshape(BH, n)
+            return np.ascontiguousarray(meta[:, off:off + w * k]).view(dt).reshape(n, k)
 
         m = field(L.off_m, np.int32, 1)[:, 0]
         order = field(L.off_order, np.uint8, 64)[:, :C_].astype(np.int64)
@@ -315,11 +330,11 @@ class Cache:
                    count=field(L.off_count, np.int32, 64)[:, :C_].copy(),
                    start=field(L.off_start, np.int64, 64)[:, :C_].copy(),
                    k_prev=field(L.off_k_prev, np.float32, dk).copy())
-        S = np.zeros((BH, C_, dv, dk), np.float32)
-        for bh in range(BH):
-            mm = int(m[bh])
+        S = np.zeros((n, C_, dv, dk), np.float32)
+        for j in range(n):
+            mm = int(m[j])
             for i in range(mm):
-                S[bh, i] = active[bh] if (bf and i == mm - 1) else states[bh, order[bh, i]]
+                S[j, i] = active[j] if (bf and i == mm - 1) else states[j, order[j, i]]
         out["S"] = S
         return out
 

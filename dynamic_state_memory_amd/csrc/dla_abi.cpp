@@ -20,6 +20,8 @@ namespace {
 
 thread_local char g_err[512] = "";
 thread_local hipEvent_t g_ev_before = nullptr, g_ev_after = nullptr;
+// testing and profiling override of the chunk-kernel choice (dla_set_prefill_path)
+thread_local int g_path_override = DLA_PATH_AUTO, g_dvt_override = 0;
 
 dla_status fail(dla_status s, const char *fmt, ...)
 {
@@ -38,6 +40,8 @@ dla_status ok()
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+constexpr size_t kLdsBytes = 160 * 1024;    // LDS of one compute unit
+
 int bit_length(int64_t x) { int n = 0; for (; x > 0; x >>= 1) ++n; return n; }
 
 // Shape check shared by every entry point.  Returns DLA_OK or a status and message.
@@ -46,7 +50,8 @@ dla_status check_shape(int32_t B, int32_t H, int32_t C, int32_t dk, int32_t dv)
     if (B < 1 || H < 1) return fail(DLA_ERR_ARG, "B and H must be >= 1 (got %d, %d)", B, H);
     if (static_cast<int64_t>(B) * H > (1 << 24)) return fail(DLA_ERR_ARG, "B*H too large");
     if (C < 1 || C > DLA_MAX_C) return fail(DLA_ERR_ARG, "C must be in [1, %d] (got %d)", DLA_MAX_C, C);
-    if (dk != 64 && dk != 128) return fail(DLA_ERR_UNSUPPORTED, "d_k must be 64 or 128 (got %d)", dk);
+    if (dk != 64 && dk != 128 && dk != 256)
+        return fail(DLA_ERR_UNSUPPORTED, "d_k must be 64, 128 or 256 (got %d)", dk);
     if (dv < 16 || dv % 16 != 0 || dv > 4096)
         return fail(DLA_ERR_UNSUPPORTED, "d_v must be a multiple of 16 in [16, 4096] (got %d)", dv);
     return DLA_OK;
@@ -166,20 +171,17 @@ dla_status hip_status(hipError_t e, const char *what)
 
 int choose_dvt(int64_t BH, int dv)
 {
-    const char *env = std::getenv("DLA_PREFILL_DVT");
-    if (env) {
-        const int v = std::atoi(env);
-        if ((v == 16 || v == 32) && dv % v == 0) return v;
-    }
+    if (g_dvt_override != 0 && dv % g_dvt_override == 0) return g_dvt_override;
     if (dv % 32 != 0) return 16;
     // prefer the wider slice when it still gives about one block per compute unit
     return BH * (dv / 32) >= 200 ? 32 : 16;
 }
 
 // Which chunk kernel a prefill of this shape runs, with its value-column
-// slice width and LDS need.  bf16 inputs with C <= 32 keep the state stack in
-// registers; the streamed kernel covers the rest (DLA_PREFILL_PATH=streamed
-// forces it).
+// slice width and LDS need.  bf16 inputs with C <= 32 and d_k <= 128 keep the
+// state stack in registers; the streamed kernel covers the rest (or every
+// shape while dla_set_prefill_path asks for it on this thread).  The streamed
+// kernel takes 32-column slices only where their LDS fits a compute unit.
 struct PrefillPlan {
     int register_resident;
     int dvt;
@@ -191,14 +193,14 @@ PrefillPlan plan_prefill(bool io_bf16, int64_t BH, int C, int dk, int dv)
 {
     PrefillPlan p;
     p.dvt = choose_dvt(BH, dv);
-    const char *path = std::getenv("DLA_PREFILL_PATH");
-    p.register_resident = io_bf16 && C <= 32 && !(path && std::strcmp(path, "streamed") == 0);
+    p.register_resident = io_bf16 && C <= 32 && dk <= 128 && g_path_override != DLA_PATH_STREAMED;
     if (p.register_resident) {
         p.dvt = prefill_rs_dvt(dk, C, p.dvt);
         p.lds = prefill_rs_smem_bytes(dk, p.dvt, C);
         const int spw = prefill_rs_spw(C);
         std::snprintf(p.name, sizeof(p.name), "k_prefill_rs<%d,%d,%d>", dk, p.dvt, spw);
     } else {
+        if (p.dvt == 32 && prefill_smem_bytes(io_bf16, dk, 32) > kLdsBytes) p.dvt = 16;
         p.lds = prefill_smem_bytes(io_bf16, dk, p.dvt);
         std::snprintf(p.name, sizeof(p.name), "k_prefill<%s,%d,%d>", io_bf16 ? "bf16" : "f32", dk, p.dvt);
     }
@@ -370,8 +372,11 @@ dla_status prefill_call(const void *q, const void *k, const void *v, const void 
         return fail(DLA_ERR_ARG, "q, k, v, lam and o must be 16-byte aligned");
     if (T < 1 || T > (1 << 24)) return fail(DLA_ERR_ARG, "T must be in [1, 2^24] (got %d)", T);
     if (io != DLA_F32 && io != DLA_BF16) return fail(DLA_ERR_ARG, "unknown io dtype %d", static_cast<int>(io));
-    if (io == DLA_F32 && cache->d_k != 64)
-        return fail(DLA_ERR_UNSUPPORTED, "float32 prefill supports d_k = 64 only");
+    if (io == DLA_F32 && cache->d_k > 128)
+        return fail(DLA_ERR_UNSUPPORTED,
+                    "float32 prefill supports d_k in {64, 128} (the streamed kernel's chunk operands at d_k = 256 "
+                    "need %zu bytes of LDS, a compute unit has %zu)",
+                    prefill_smem_bytes(0, 256, 16), kLdsBytes);
     if (tau != tau) return fail(DLA_ERR_ARG, "tau is NaN");
     if (sched && ((sched->ev_t == nullptr) != (sched->ev_i == nullptr)))
         return fail(DLA_ERR_ARG, "schedule export: ev_t and ev_i go together");
@@ -400,7 +405,7 @@ dla_status prefill_call(const void *q, const void *k, const void *v, const void 
     const PrefillPlan plan = plan_prefill(a.io_bf16, BH, cache->C, cache->d_k, cache->d_v);
     a.dvt = plan.dvt;
     a.register_resident = plan.register_resident;
-    if (plan.lds > 160 * 1024)
+    if (plan.lds > kLdsBytes)
         return fail(DLA_ERR_UNSUPPORTED, "shape needs more LDS than a compute unit has");
     a.g = geom(cache);
     if (a.merge_rule == DLA_FENWICK) {
@@ -486,7 +491,8 @@ dla_status dla_decode_step(const void *q, const void *k, const void *v, const vo
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(lam, 16) || !aligned(o, 16))
         return fail(DLA_ERR_ARG, "q, k, v, lam and o must be 16-byte aligned");
     if (io != DLA_F32 && io != DLA_BF16) return fail(DLA_ERR_ARG, "unknown io dtype %d", static_cast<int>(io));
-    if (cache->d_k != cache->d_v) return fail(DLA_ERR_UNSUPPORTED, "decode needs d_k == d_v");
+    if (cache->d_v != 64 && cache->d_v != 128 && cache->d_v != 256)
+        return fail(DLA_ERR_UNSUPPORTED, "decode supports d_v in {64, 128, 256} (got %d)", cache->d_v);
     if (cache->merge_rule == DLA_FENWICK) {
         if (cache->state_dtype != DLA_F32)
             return fail(DLA_ERR_UNSUPPORTED, "the fixed schedule needs float32 state storage");
@@ -511,6 +517,16 @@ dla_status dla_decode_step(const void *q, const void *k, const void *v, const vo
     a.sched.m_t = sched ? sched->m_t : nullptr;
     a.sched.ev_i = sched ? sched->ev_i : nullptr;
     return hip_status(launch_decode(a, static_cast<hipStream_t>(stream)), "decode launch");
+}
+
+dla_status dla_set_prefill_path(int32_t path, int32_t value_columns)
+{
+    if (path != DLA_PATH_AUTO && path != DLA_PATH_STREAMED) return fail(DLA_ERR_ARG, "unknown prefill path %d", path);
+    if (value_columns != 0 && value_columns != 16 && value_columns != 32)
+        return fail(DLA_ERR_ARG, "value_columns must be 0, 16 or 32 (got %d)", value_columns);
+    g_path_override = path;
+    g_dvt_override = value_columns;
+    return ok();
 }
 
 dla_status dla_set_prefill_events(void *before, void *after)

@@ -160,14 +160,16 @@ template <typename T> __device__ __forceinline__ T readlane_any(T x, int l) {
     }
 }
 
-// Sum over aligned groups of G lanes (G = 8 or 16), in every lane of the
-// group: DPP steps within the group only.
+// Sum over aligned groups of G lanes (G = 8, 16 or 32), in every lane of the
+// group: DPP steps within a row of 16, then (G = 32) one exchange between
+// the two rows of the group.
 template <int G, typename T> __device__ __forceinline__ T group_sum_dpp(T x) {
-    static_assert(G == 8 || G == 16, "groups of 8 or 16 lanes");
+    static_assert(G == 8 || G == 16 || G == 32, "groups of 8, 16 or 32 lanes");
     x += dpp_move<kDppXor1>(x);
     x += dpp_move<kDppXor2>(x);
     x += dpp_move<kDppHalfMirror>(x);
-    if constexpr (G == 16) x += dpp_move<kDppMirror>(x);
+    if constexpr (G >= 16) x += dpp_move<kDppMirror>(x);
+    if constexpr (G == 32) x += __shfl_xor(x, 16);
     return x;
 }
 

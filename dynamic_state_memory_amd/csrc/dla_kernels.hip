@@ -595,8 +595,13 @@ struct PrefillSmem {
     TIO vt[DVT][kChunk + PAD];
     TIO pw[kChunk][kChunk + PAD];
     float lam[kChunk][kMaxC];
-    float wold[kMaxC][kChunk];
-    float ored[4][kChunk][DVT];
+    // the read weights of the states live at the chunk start, used only by
+    // the inter-chunk read, and the four waves' partial reads written after
+    // it (a barrier between): one region
+    union {
+        float wold[kMaxC][kChunk];
+        float ored[4][kChunk][DVT];
+    };
     uint64_t om[kChunk];
     uint64_t nm[kChunk];
     int32_t order[kMaxC];
@@ -864,6 +869,7 @@ __global__ __launch_bounds__(256, 1) void k_prefill(
                     for (int nt = 0; nt < NTV; ++nt) bc[ks][nt] = bn[ks][nt];
             }
         }
+        __syncthreads();          // every wave is done with the read weights
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -1049,7 +1055,21 @@ __global__ __launch_bounds__(256, 1) void k_prefill(
 // and applying a capacity merge S_a += S_b while the data passes through.
 // The states are read and written with nontemporal hints: a step touches
 // each of them once, so they should not displace other data in the caches.
-template <typename TIO, int D, bool BF>
+//
+// Thread tid owns columns 4 (tid % G) .. + 3 of the rows tid / G + R j of
+// every state (G = DK / 4 threads per row, R rows per pass, P passes); the
+// passes go in batches of at most 16 loads per thread, batch by batch over
+// all the states, so that large states do not need more registers.
+template <int DK, int DV>
+struct DecodeShape {
+    static constexpr int G = DK / 4;          // threads per state row (float4 each)
+    static constexpr int R = 256 / G;         // rows per pass
+    static constexpr int P = DV / R;          // passes per state
+    static constexpr int PB = P < 16 ? P : 16; // passes per batch
+    static_assert(DV % R == 0 && P % PB == 0, "whole passes and batches");
+};
+
+template <typename TIO, int DK, int DV, bool BF>
 __global__ __launch_bounds__(256) void k_decode(const TIO *__restrict__ Qg, const TIO *__restrict__ Kg,
                                                 const TIO *__restrict__ Vg, const TIO *__restrict__ Lg,
                                                 TIO *__restrict__ Og, float tau, int C,
@@ -1057,14 +1077,16 @@ __global__ __launch_bounds__(256) void k_decode(const TIO *__restrict__ Qg, cons
                                                 uint8_t *__restrict__ meta_base,
                                                 size_t meta_stride, DecodeSched sched, int merge_rule)
 {
-    constexpr int G = D / 4;          // threads per state row (float4 each)
-    constexpr int R = 256 / G;        // rows per pass
-    constexpr int P = D / R;          // passes per state
-    __shared__ float qs[D], ks[D], vs[D], kp[D], lw[kMaxC];
+    typedef DecodeShape<DK, DV> Sh;
+    constexpr int G = Sh::G, R = Sh::R, P = Sh::P, PB = Sh::PB;
+    constexpr size_t SS = static_cast<size_t>(DK) * DV;   // elements per state
+    __shared__ __align__(16) float qs[DK];
+    __shared__ __align__(16) float ks[DK];
+    __shared__ float kp[DK], vs[DV], lw[kMaxC];
     __shared__ float wlog[kMaxC];
     __shared__ int32_t order_s[kMaxC];
     __shared__ double red[4][4];
-    __shared__ float orow[D];
+    __shared__ float orow[DV];
     __shared__ int32_t ctl[8];        // mode, add_slot, set_slot, merge_i, m, ...
     __shared__ float sc_kq;
 
@@ -1078,17 +1100,17 @@ __global__ __launch_bounds__(256) void k_decode(const TIO *__restrict__ Qg, cons
     int64_t *start = reinterpret_cast<int64_t *>(meta + kOffStart);
     float *kprev = reinterpret_cast<float *>(meta + kOffKprev);
 
-    if (tid < D) {
-        qs[tid] = to_f(Qg[static_cast<size_t>(bh) * D + tid]);
-        ks[tid] = to_f(Kg[static_cast<size_t>(bh) * D + tid]);
-        vs[tid] = to_f(Vg[static_cast<size_t>(bh) * D + tid]);
+    if (tid < DK) {
+        qs[tid] = to_f(Qg[static_cast<size_t>(bh) * DK + tid]);
+        ks[tid] = to_f(Kg[static_cast<size_t>(bh) * DK + tid]);
         kp[tid] = kprev[tid];
     }
+    if (tid < DV) vs[tid] = to_f(Vg[static_cast<size_t>(bh) * DV + tid]);
     if (tid < C) lw[tid] = to_f(Lg[static_cast<size_t>(bh) * C + tid]);
     __syncthreads();
     {
         double d = 0.0, a = 0.0, b = 0.0, kq = 0.0;
-        if (tid < D) {
+        if (tid < DK) {
             const double x = ks[tid], y = kp[tid];
             d = x * y; a = x * x; b = y * y;
             kq = x * static_cast<double>(qs[tid]);
@@ -1185,7 +1207,7 @@ __global__ __launch_bounds__(256) void k_decode(const TIO *__restrict__ Qg, cons
         }
     }
     __syncthreads();
-    if (tid < D) kprev[tid] = ks[tid];
+    if (tid < DK) kprev[tid] = ks[tid];
     const int mode = ctl[0], add_slot = ctl[1], set_slot = ctl[2], merge_i = ctl[3], m = ctl[4];
     const int col = (tid % G) * 4, row0 = tid / G;
     const float4 q4 = *reinterpret_cast<const float4 *>(&qs[col]);
@@ -1194,48 +1216,52 @@ __global__ __launch_bounds__(256) void k_decode(const TIO *__restrict__ Qg, cons
 #pragma unroll
     for (int j = 0; j < P; ++j) acc[j] = 0.0f;
     if constexpr (!BF) {
-        float *sb = states + static_cast<size_t>(bh) * C * D * D;
-        for (int i = 0; i < m; ++i) {
-            const int p = order_s[i];
-            const float w = wlog[i];
-            float4 *sp = reinterpret_cast<float4 *>(sb + static_cast<size_t>(p) * D * D);
-            float4 x[P];
-    #pragma unroll
-            for (int j = 0; j < P; ++j) {
-                const floatx4 t = __builtin_nontemporal_load(reinterpret_cast<const floatx4 *>(sp) + ((row0 + R * j) * D + col) / 4);
-                x[j] = make_float4(t[0], t[1], t[2], t[3]);
-            }
-    #pragma unroll
-            for (int j = 0; j < P; ++j)
-                acc[j] += w * (x[j].x * q4.x + x[j].y * q4.y + x[j].z * q4.z + x[j].w * q4.w);
-            if (p == add_slot) {
-    #pragma unroll
-                for (int j = 0; j < P; ++j) {
-                    const float vr = vs[row0 + R * j];
-                    float4 y = x[j];
-                    y.x += vr * k4.x; y.y += vr * k4.y; y.z += vr * k4.z; y.w += vr * k4.w;
-                    __builtin_nontemporal_store(floatx4{y.x, y.y, y.z, y.w},
-                                                reinterpret_cast<floatx4 *>(sp) + ((row0 + R * j) * D + col) / 4);
+        float *sb = states + static_cast<size_t>(bh) * C * SS;
+#pragma unroll 1
+        for (int b = 0; b < P; b += PB) {
+            for (int i = 0; i < m; ++i) {
+                const int p = order_s[i];
+                const float w = wlog[i];
+                float4 *sp = reinterpret_cast<float4 *>(sb + static_cast<size_t>(p) * SS);
+                float4 x[PB];
+#pragma unroll
+                for (int j = 0; j < PB; ++j) {
+                    const floatx4 t = __builtin_nontemporal_load(reinterpret_cast<const floatx4 *>(sp) +
+                                                                 ((row0 + R * (b + j)) * DK + col) / 4);
+                    x[j] = make_float4(t[0], t[1], t[2], t[3]);
+                }
+#pragma unroll
+                for (int j = 0; j < PB; ++j)
+                    acc[b + j] += w * (x[j].x * q4.x + x[j].y * q4.y + x[j].z * q4.z + x[j].w * q4.w);
+                if (p == add_slot) {
+#pragma unroll
+                    for (int j = 0; j < PB; ++j) {
+                        const float vr = vs[row0 + R * (b + j)];
+                        float4 y = x[j];
+                        y.x += vr * k4.x; y.y += vr * k4.y; y.z += vr * k4.z; y.w += vr * k4.w;
+                        __builtin_nontemporal_store(floatx4{y.x, y.y, y.z, y.w},
+                                                    reinterpret_cast<floatx4 *>(sp) + ((row0 + R * (b + j)) * DK + col) / 4);
+                    }
+                }
+                if (mode == 2 && i == merge_i + 1) {
+                    float4 *dp = reinterpret_cast<float4 *>(sb + static_cast<size_t>(order_s[merge_i]) * SS);
+#pragma unroll
+                    for (int j = 0; j < PB; ++j) {
+                        const int idx = ((row0 + R * (b + j)) * DK + col) / 4;
+                        float4 a = dp[idx];
+                        a.x += x[j].x; a.y += x[j].y; a.z += x[j].z; a.w += x[j].w;
+                        __builtin_nontemporal_store(floatx4{a.x, a.y, a.z, a.w}, reinterpret_cast<floatx4 *>(dp) + idx);
+                    }
                 }
             }
-            if (mode == 2 && i == merge_i + 1) {
-                float4 *dp = reinterpret_cast<float4 *>(sb + static_cast<size_t>(order_s[merge_i]) * D * D);
-    #pragma unroll
-                for (int j = 0; j < P; ++j) {
-                    const int idx = ((row0 + R * j) * D + col) / 4;
-                    float4 a = dp[idx];
-                    a.x += x[j].x; a.y += x[j].y; a.z += x[j].z; a.w += x[j].w;
-                    __builtin_nontemporal_store(floatx4{a.x, a.y, a.z, a.w}, reinterpret_cast<floatx4 *>(dp) + idx);
+            if (set_slot >= 0) {
+                float4 *sp = reinterpret_cast<float4 *>(sb + static_cast<size_t>(set_slot) * SS);
+#pragma unroll
+                for (int j = 0; j < PB; ++j) {
+                    const float vr = vs[row0 + R * (b + j)];
+                    __builtin_nontemporal_store(floatx4{vr * k4.x, vr * k4.y, vr * k4.z, vr * k4.w},
+                                                reinterpret_cast<floatx4 *>(sp) + ((row0 + R * (b + j)) * DK + col) / 4);
                 }
-            }
-        }
-        if (set_slot >= 0) {
-            float4 *sp = reinterpret_cast<float4 *>(sb + static_cast<size_t>(set_slot) * D * D);
-    #pragma unroll
-            for (int j = 0; j < P; ++j) {
-                const float vr = vs[row0 + R * j];
-                __builtin_nontemporal_store(floatx4{vr * k4.x, vr * k4.y, vr * k4.z, vr * k4.w},
-                                            reinterpret_cast<floatx4 *>(sp) + ((row0 + R * j) * D + col) / 4);
             }
         }
     } else {
@@ -1244,77 +1270,80 @@ __global__ __launch_bounds__(256) void k_decode(const TIO *__restrict__ Qg, cons
         // once, and every change is applied while it passes
         typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
         const int act_i = m - 1;
-        floatx4 *ab = reinterpret_cast<floatx4 *>(active + static_cast<size_t>(bh) * D * D);
-        u32x2 *sb = reinterpret_cast<u32x2 *>(states) + static_cast<size_t>(bh) * C * D * D / 4;
-        for (int i = 0; i < m; ++i) {
-            const int p = order_s[i];
-            const float w = wlog[i];
-            float4 x[P];
-            if (i == act_i) {
+        floatx4 *ab = reinterpret_cast<floatx4 *>(active + static_cast<size_t>(bh) * SS);
+        u32x2 *sb = reinterpret_cast<u32x2 *>(states) + static_cast<size_t>(bh) * C * SS / 4;
+#pragma unroll 1
+        for (int b = 0; b < P; b += PB) {
+            for (int i = 0; i < m; ++i) {
+                const int p = order_s[i];
+                const float w = wlog[i];
+                float4 x[PB];
+                if (i == act_i) {
 #pragma unroll
-                for (int j = 0; j < P; ++j) {
-                    const floatx4 t = __builtin_nontemporal_load(ab + ((row0 + R * j) * D + col) / 4);
-                    x[j] = make_float4(t[0], t[1], t[2], t[3]);
-                }
-            } else {
-                const u32x2 *sp = sb + static_cast<size_t>(p) * D * D / 4;
-#pragma unroll
-                for (int j = 0; j < P; ++j) {
-                    const u32x2 t = __builtin_nontemporal_load(sp + ((row0 + R * j) * D + col) / 4);
-                    x[j] = unpack_bf16x4(make_uint2(t[0], t[1]));
-                }
-            }
-#pragma unroll
-            for (int j = 0; j < P; ++j)
-                acc[j] += w * (x[j].x * q4.x + x[j].y * q4.y + x[j].z * q4.z + x[j].w * q4.w);
-            // where a bf16 result goes: the active state closing into its own
-            // slot, or the state merging away added into the slot of merge_i
-            int dst_slot = -1;
-            bool add_into = false;
-            if (i == act_i) {
-                if (mode == 0 || mode == 3) {
-                    // the token joins the active state
-#pragma unroll
-                    for (int j = 0; j < P; ++j) {
-                        const float vr = vs[row0 + R * j];
-                        const float4 y = x[j];
-                        __builtin_nontemporal_store(floatx4{y.x + vr * k4.x, y.y + vr * k4.y, y.z + vr * k4.z,
-                                                            y.w + vr * k4.w},
-                                                    ab + ((row0 + R * j) * D + col) / 4);
+                    for (int j = 0; j < PB; ++j) {
+                        const floatx4 t = __builtin_nontemporal_load(ab + ((row0 + R * (b + j)) * DK + col) / 4);
+                        x[j] = make_float4(t[0], t[1], t[2], t[3]);
                     }
-                } else if (mode == 2 && merge_i + 1 == act_i) {
-                    dst_slot = order_s[merge_i];       // merged into the closed state before it
-                    add_into = true;
                 } else {
-                    dst_slot = p;                      // closes: a new state becomes the active one
-                }
-            } else if (mode == 2 && i == merge_i + 1) {
-                dst_slot = order_s[merge_i];
-                add_into = true;
-            }
-            if (dst_slot >= 0) {
-                u32x2 *dp = sb + static_cast<size_t>(dst_slot) * D * D / 4;
+                    const u32x2 *sp = sb + static_cast<size_t>(p) * SS / 4;
 #pragma unroll
-                for (int j = 0; j < P; ++j) {
-                    const int idx = ((row0 + R * j) * D + col) / 4;
-                    float4 y = x[j];
-                    if (add_into) {
-                        const u32x2 t = dp[idx];
-                        const float4 a4 = unpack_bf16x4(make_uint2(t[0], t[1]));
-                        y.x += a4.x; y.y += a4.y; y.z += a4.z; y.w += a4.w;
+                    for (int j = 0; j < PB; ++j) {
+                        const u32x2 t = __builtin_nontemporal_load(sp + ((row0 + R * (b + j)) * DK + col) / 4);
+                        x[j] = unpack_bf16x4(make_uint2(t[0], t[1]));
                     }
-                    const uint2 u = pack_bf16x4(y);
-                    __builtin_nontemporal_store(u32x2{u.x, u.y}, dp + idx);
+                }
+#pragma unroll
+                for (int j = 0; j < PB; ++j)
+                    acc[b + j] += w * (x[j].x * q4.x + x[j].y * q4.y + x[j].z * q4.z + x[j].w * q4.w);
+                // where a bf16 result goes: the active state closing into its own
+                // slot, or the state merging away added into the slot of merge_i
+                int dst_slot = -1;
+                bool add_into = false;
+                if (i == act_i) {
+                    if (mode == 0 || mode == 3) {
+                        // the token joins the active state
+#pragma unroll
+                        for (int j = 0; j < PB; ++j) {
+                            const float vr = vs[row0 + R * (b + j)];
+                            const float4 y = x[j];
+                            __builtin_nontemporal_store(floatx4{y.x + vr * k4.x, y.y + vr * k4.y, y.z + vr * k4.z,
+                                                                y.w + vr * k4.w},
+                                                        ab + ((row0 + R * (b + j)) * DK + col) / 4);
+                        }
+                    } else if (mode == 2 && merge_i + 1 == act_i) {
+                        dst_slot = order_s[merge_i];       // merged into the closed state before it
+                        add_into = true;
+                    } else {
+                        dst_slot = p;                      // closes: a new state becomes the active one
+                    }
+                } else if (mode == 2 && i == merge_i + 1) {
+                    dst_slot = order_s[merge_i];
+                    add_into = true;
+                }
+                if (dst_slot >= 0) {
+                    u32x2 *dp = sb + static_cast<size_t>(dst_slot) * SS / 4;
+#pragma unroll
+                    for (int j = 0; j < PB; ++j) {
+                        const int idx = ((row0 + R * (b + j)) * DK + col) / 4;
+                        float4 y = x[j];
+                        if (add_into) {
+                            const u32x2 t = dp[idx];
+                            const float4 a4 = unpack_bf16x4(make_uint2(t[0], t[1]));
+                            y.x += a4.x; y.y += a4.y; y.z += a4.z; y.w += a4.w;
+                        }
+                        const uint2 u = pack_bf16x4(y);
+                        __builtin_nontemporal_store(u32x2{u.x, u.y}, dp + idx);
+                    }
                 }
             }
-        }
-        if (mode == 1 || mode == 2) {
-            // the new state v k^T is the active one now
+            if (mode == 1 || mode == 2) {
+                // the new state v k^T is the active one now
 #pragma unroll
-            for (int j = 0; j < P; ++j) {
-                const float vr = vs[row0 + R * j];
-                __builtin_nontemporal_store(floatx4{vr * k4.x, vr * k4.y, vr * k4.z, vr * k4.w},
-                                            ab + ((row0 + R * j) * D + col) / 4);
+                for (int j = 0; j < PB; ++j) {
+                    const float vr = vs[row0 + R * (b + j)];
+                    __builtin_nontemporal_store(floatx4{vr * k4.x, vr * k4.y, vr * k4.z, vr * k4.w},
+                                                ab + ((row0 + R * (b + j)) * DK + col) / 4);
+                }
             }
         }
     }
@@ -1327,7 +1356,7 @@ __global__ __launch_bounds__(256) void k_decode(const TIO *__restrict__ Qg, cons
         if (tid % G == 0) orow[row0 + R * j] = x;
     }
     __syncthreads();
-    if (tid < D) Og[static_cast<size_t>(bh) * D + tid] = from_f<TIO>(orow[tid] + sc_kq * vs[tid]);
+    if (tid < DV) Og[static_cast<size_t>(bh) * DV + tid] = from_f<TIO>(orow[tid] + sc_kq * vs[tid]);
 }
 
 // ------------------------------------------------------------ decode, fixed schedule
@@ -1342,20 +1371,22 @@ __global__ __launch_bounds__(256) void k_decode(const TIO *__restrict__ Qg, cons
 // the way and the sum is written once, into the slot of the oldest of them.
 // A stream at t >= 2^(C-1) would need a level weight the cache does not
 // have: its output row is NaN and its cache is left as it was.
-template <typename TIO, int D>
+template <typename TIO, int DK, int DV>
 __global__ __launch_bounds__(256) void k_decode_fenwick(const TIO *__restrict__ Qg, const TIO *__restrict__ Kg,
                                                         const TIO *__restrict__ Vg, const TIO *__restrict__ Lg,
                                                         TIO *__restrict__ Og, int C, float *__restrict__ states,
                                                         uint8_t *__restrict__ meta_base, size_t meta_stride)
 {
-    constexpr int G = D / 4;          // threads per state row (float4 each)
-    constexpr int R = 256 / G;        // rows per pass
-    constexpr int P = D / R;          // passes per state
-    __shared__ float qs[D], ks[D], vs[D], lw[kMaxC];
+    typedef DecodeShape<DK, DV> Sh;
+    constexpr int G = Sh::G, R = Sh::R, P = Sh::P, PB = Sh::PB;
+    constexpr size_t SS = static_cast<size_t>(DK) * DV;
+    __shared__ __align__(16) float qs[DK];
+    __shared__ __align__(16) float ks[DK];
+    __shared__ float vs[DV], lw[kMaxC];
     __shared__ float wlog[kMaxC];
     __shared__ int32_t order_s[kMaxC];
     __shared__ double red[4];
-    __shared__ float orow[D];
+    __shared__ float orow[DV];
     __shared__ int32_t ctl[4];        // m, first merging index, destination slot, refused
     __shared__ float sc_kq;
 
@@ -1368,15 +1399,15 @@ __global__ __launch_bounds__(256) void k_decode_fenwick(const TIO *__restrict__ 
     int32_t *count = reinterpret_cast<int32_t *>(meta + kOffCount);
     int64_t *start = reinterpret_cast<int64_t *>(meta + kOffStart);
 
-    if (tid < D) {
-        qs[tid] = to_f(Qg[static_cast<size_t>(bh) * D + tid]);
-        ks[tid] = to_f(Kg[static_cast<size_t>(bh) * D + tid]);
-        vs[tid] = to_f(Vg[static_cast<size_t>(bh) * D + tid]);
+    if (tid < DK) {
+        qs[tid] = to_f(Qg[static_cast<size_t>(bh) * DK + tid]);
+        ks[tid] = to_f(Kg[static_cast<size_t>(bh) * DK + tid]);
     }
+    if (tid < DV) vs[tid] = to_f(Vg[static_cast<size_t>(bh) * DV + tid]);
     if (tid < C) lw[tid] = to_f(Lg[static_cast<size_t>(bh) * C + tid]);
     __syncthreads();
     {
-        double kq = tid < D ? static_cast<double>(ks[tid]) * static_cast<double>(qs[tid]) : 0.0;
+        double kq = tid < DK ? static_cast<double>(ks[tid]) * static_cast<double>(qs[tid]) : 0.0;
         kq = wave_sum(kq);
         if (lane == 0) red[wave] = kq;
     }
@@ -1433,46 +1464,56 @@ __global__ __launch_bounds__(256) void k_decode_fenwick(const TIO *__restrict__ 
     __syncthreads();
     const int m = ctl[0], first = ctl[1], dst = ctl[2];
     if (ctl[3]) {
-        if (tid < D) Og[static_cast<size_t>(bh) * D + tid] = from_f<TIO>(__builtin_nanf(""));
+        if (tid < DV) Og[static_cast<size_t>(bh) * DV + tid] = from_f<TIO>(__builtin_nanf(""));
         return;
     }
     const int col = (tid % G) * 4, row0 = tid / G;
     const float4 q4 = *reinterpret_cast<const float4 *>(&qs[col]);
     const float4 k4 = *reinterpret_cast<const float4 *>(&ks[col]);
     float acc[P];
-    float4 sum[P];
 #pragma unroll
-    for (int j = 0; j < P; ++j) {
-        acc[j] = 0.0f;
-        const float vr = vs[row0 + R * j];
-        sum[j] = make_float4(vr * k4.x, vr * k4.y, vr * k4.z, vr * k4.w);
-    }
-    float *sb = states + static_cast<size_t>(bh) * C * D * D;
-    for (int i = 0; i < m; ++i) {
-        const int p = order_s[i];
-        const float w = wlog[i];
-        const floatx4 *sp = reinterpret_cast<const floatx4 *>(sb + static_cast<size_t>(p) * D * D);
-        float4 x[P];
+    for (int j = 0; j < P; ++j) acc[j] = 0.0f;
+    float *sb = states + static_cast<size_t>(bh) * C * SS;
+    auto batch = [&](const int b) {
+        float4 sum[PB];
 #pragma unroll
-        for (int j = 0; j < P; ++j) {
-            const floatx4 u = __builtin_nontemporal_load(sp + ((row0 + R * j) * D + col) / 4);
-            x[j] = make_float4(u[0], u[1], u[2], u[3]);
+        for (int j = 0; j < PB; ++j) {
+            const float vr = vs[row0 + R * (b + j)];
+            sum[j] = make_float4(vr * k4.x, vr * k4.y, vr * k4.z, vr * k4.w);
         }
+        for (int i = 0; i < m; ++i) {
+            const int p = order_s[i];
+            const float w = wlog[i];
+            const floatx4 *sp = reinterpret_cast<const floatx4 *>(sb + static_cast<size_t>(p) * SS);
+            float4 x[PB];
 #pragma unroll
-        for (int j = 0; j < P; ++j)
-            acc[j] += w * (x[j].x * q4.x + x[j].y * q4.y + x[j].z * q4.z + x[j].w * q4.w);
-        if (i >= first) {
+            for (int j = 0; j < PB; ++j) {
+                const floatx4 u = __builtin_nontemporal_load(sp + ((row0 + R * (b + j)) * DK + col) / 4);
+                x[j] = make_float4(u[0], u[1], u[2], u[3]);
+            }
 #pragma unroll
-            for (int j = 0; j < P; ++j) {
-                sum[j].x += x[j].x; sum[j].y += x[j].y; sum[j].z += x[j].z; sum[j].w += x[j].w;
+            for (int j = 0; j < PB; ++j)
+                acc[b + j] += w * (x[j].x * q4.x + x[j].y * q4.y + x[j].z * q4.z + x[j].w * q4.w);
+            if (i >= first) {
+#pragma unroll
+                for (int j = 0; j < PB; ++j) {
+                    sum[j].x += x[j].x; sum[j].y += x[j].y; sum[j].z += x[j].z; sum[j].w += x[j].w;
+                }
             }
         }
-    }
-    // the token's bucket (its own slot was read above by the same threads)
-    floatx4 *dp = reinterpret_cast<floatx4 *>(sb + static_cast<size_t>(dst) * D * D);
+        // the token's bucket (its own slot was read above by the same threads)
+        floatx4 *dp = reinterpret_cast<floatx4 *>(sb + static_cast<size_t>(dst) * SS);
 #pragma unroll
-    for (int j = 0; j < P; ++j)
-        __builtin_nontemporal_store(floatx4{sum[j].x, sum[j].y, sum[j].z, sum[j].w}, dp + ((row0 + R * j) * D + col) / 4);
+        for (int j = 0; j < PB; ++j)
+            __builtin_nontemporal_store(floatx4{sum[j].x, sum[j].y, sum[j].z, sum[j].w},
+                                        dp + ((row0 + R * (b + j)) * DK + col) / 4);
+    };
+    if constexpr (P == PB) {
+        batch(0);
+    } else {
+#pragma unroll 1
+        for (int b = 0; b < P; b += PB) batch(b);
+    }
 #pragma unroll
     for (int j = 0; j < P; ++j) {
         float x = acc[j];
@@ -1481,7 +1522,7 @@ __global__ __launch_bounds__(256) void k_decode_fenwick(const TIO *__restrict__ 
         if (tid % G == 0) orow[row0 + R * j] = x;
     }
     __syncthreads();
-    if (tid < D) Og[static_cast<size_t>(bh) * D + tid] = from_f<TIO>(orow[tid] + sc_kq * vs[tid]);
+    if (tid < DV) Og[static_cast<size_t>(bh) * DV + tid] = from_f<TIO>(orow[tid] + sc_kq * vs[tid]);
 }
 
 // ------------------------------------------------------------ launchers
@@ -1624,36 +1665,32 @@ hipError_t launch_fenwick_schedule(const PrefillArgs &a, hipStream_t stream)
     return hipGetLastError();
 }
 
+// The streamed chunk kernel of key width DK, slice width a.dvt.
+template <typename TIO, int DK>
+static hipError_t prefill_main_dk(const PrefillArgs &a, hipStream_t stream)
+{
+    if constexpr (sizeof(PrefillSmem<TIO, DK, 32>) <= 160 * 1024)
+        if (a.dvt == 32) return prefill_main<TIO, DK, 32>(a, stream);
+    return prefill_main<TIO, DK, 16>(a, stream);
+}
+
 template <typename TIO>
 static hipError_t prefill_typed(const PrefillArgs &a, hipStream_t stream)
 {
     hipError_t e;
     const bool fen = a.merge_rule == DLA_FENWICK;
-    if (fen) {
-        e = launch_fenwick_schedule(a, stream);
-        if (e != hipSuccess) return e;
-        if (a.g.dk == 64)
-            e = a.dvt == 32 ? prefill_main<TIO, 64, 32>(a, stream) : prefill_main<TIO, 64, 16>(a, stream);
-        else if constexpr (sizeof(TIO) == 2)
-            e = a.dvt == 32 ? prefill_main<TIO, 128, 32>(a, stream) : prefill_main<TIO, 128, 16>(a, stream);
-        else
-            return hipErrorInvalidValue;
-        if (e != hipSuccess) return e;
-        return launch_fen_refused(a, stream);
-    }
-    if (a.g.dk == 64) {
-        e = prefill_schedule<TIO, 64>(a, stream);
-        if (e != hipSuccess) return e;
-        if (a.dvt == 32) return prefill_main<TIO, 64, 32>(a, stream);
-        return prefill_main<TIO, 64, 16>(a, stream);
-    }
-    if constexpr (sizeof(TIO) == 2) {
-        e = prefill_schedule<TIO, 128>(a, stream);
-        if (e != hipSuccess) return e;
-        if (a.dvt == 32) return prefill_main<TIO, 128, 32>(a, stream);
-        return prefill_main<TIO, 128, 16>(a, stream);
-    }
-    return hipErrorInvalidValue;
+    if (fen) e = launch_fenwick_schedule(a, stream);
+    else if (a.g.dk == 64) e = prefill_schedule<TIO, 64>(a, stream);
+    else if (a.g.dk == 128) e = prefill_schedule<TIO, 128>(a, stream);
+    else if constexpr (sizeof(TIO) == 2) e = prefill_schedule<TIO, 256>(a, stream);
+    else return hipErrorInvalidValue;
+    if (e != hipSuccess) return e;
+    if (a.g.dk == 64) e = prefill_main_dk<TIO, 64>(a, stream);
+    else if (a.g.dk == 128) e = prefill_main_dk<TIO, 128>(a, stream);
+    else if constexpr (sizeof(TIO) == 2) e = prefill_main_dk<TIO, 256>(a, stream);
+    else return hipErrorInvalidValue;
+    if (e != hipSuccess || !fen) return e;
+    return launch_fen_refused(a, stream);
 }
 
 static hipError_t prefill_register_resident(const PrefillArgs &a, hipStream_t stream)
@@ -1685,34 +1722,45 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream)
     return prefill_typed<float>(a, stream);
 }
 
-template <typename TIO>
-static hipError_t decode_typed(const DecodeArgs &a, hipStream_t stream)
+template <typename TIO, int DK, int DV>
+static void decode_launch(const DecodeArgs &a, hipStream_t stream)
 {
     const int BH = a.g.B * a.g.H;
     const TIO *q = static_cast<const TIO *>(a.q), *k = static_cast<const TIO *>(a.k);
     const TIO *v = static_cast<const TIO *>(a.v), *l = static_cast<const TIO *>(a.lam);
     TIO *o = static_cast<TIO *>(a.o);
-    if (a.merge_rule == DLA_FENWICK) {
-        if (a.g.dk == 128)
-            hipLaunchKernelGGL((k_decode_fenwick<TIO, 128>), dim3(BH), dim3(256), 0, stream, q, k, v, l, o, a.g.C,
-                               a.states, a.meta, a.g.meta_stride);
-        else
-            hipLaunchKernelGGL((k_decode_fenwick<TIO, 64>), dim3(BH), dim3(256), 0, stream, q, k, v, l, o, a.g.C,
-                               a.states, a.meta, a.g.meta_stride);
-        return hipGetLastError();
+    if (a.merge_rule == DLA_FENWICK)
+        hipLaunchKernelGGL((k_decode_fenwick<TIO, DK, DV>), dim3(BH), dim3(256), 0, stream, q, k, v, l, o, a.g.C,
+                           a.states, a.meta, a.g.meta_stride);
+    else if (a.g.state_bf16)
+        hipLaunchKernelGGL((k_decode<TIO, DK, DV, true>), dim3(BH), dim3(256), 0, stream, q, k, v, l, o, a.tau,
+                           a.g.C, a.states, a.active, a.meta, a.g.meta_stride, a.sched, a.merge_rule);
+    else
+        hipLaunchKernelGGL((k_decode<TIO, DK, DV, false>), dim3(BH), dim3(256), 0, stream, q, k, v, l, o, a.tau,
+                           a.g.C, a.states, a.active, a.meta, a.g.meta_stride, a.sched, a.merge_rule);
+}
+
+template <typename TIO, int DK>
+static hipError_t decode_dk(const DecodeArgs &a, hipStream_t stream)
+{
+    switch (a.g.dv) {
+    case 64: decode_launch<TIO, DK, 64>(a, stream); break;
+    case 128: decode_launch<TIO, DK, 128>(a, stream); break;
+    case 256: decode_launch<TIO, DK, 256>(a, stream); break;
+    default: return hipErrorInvalidValue;
     }
-#define DLA_DECODE(D_, BF_)                                                                           \
-    hipLaunchKernelGGL((k_decode<TIO, D_, BF_>), dim3(BH), dim3(256), 0, stream, q, k, v, l, o, a.tau, a.g.C, \
-                       a.states, a.active, a.meta, a.g.meta_stride, a.sched, a.merge_rule)
-    if (a.g.dk == 128) {
-        if (a.g.state_bf16) DLA_DECODE(128, true);
-        else DLA_DECODE(128, false);
-    } else {
-        if (a.g.state_bf16) DLA_DECODE(64, true);
-        else DLA_DECODE(64, false);
-    }
-#undef DLA_DECODE
     return hipGetLastError();
+}
+
+template <typename TIO>
+static hipError_t decode_typed(const DecodeArgs &a, hipStream_t stream)
+{
+    switch (a.g.dk) {
+    case 64: return decode_dk<TIO, 64>(a, stream);
+    case 128: return decode_dk<TIO, 128>(a, stream);
+    case 256: return decode_dk<TIO, 256>(a, stream);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream)
@@ -1725,9 +1773,12 @@ size_t prefill_smem_bytes(int io_bf16, int dk, int dvt)
 {
     if (io_bf16) {
         if (dk == 64) return dvt == 32 ? sizeof(PrefillSmem<__bf16, 64, 32>) : sizeof(PrefillSmem<__bf16, 64, 16>);
-        return dvt == 32 ? sizeof(PrefillSmem<__bf16, 128, 32>) : sizeof(PrefillSmem<__bf16, 128, 16>);
+        if (dk == 128) return dvt == 32 ? sizeof(PrefillSmem<__bf16, 128, 32>) : sizeof(PrefillSmem<__bf16, 128, 16>);
+        return dvt == 32 ? sizeof(PrefillSmem<__bf16, 256, 32>) : sizeof(PrefillSmem<__bf16, 256, 16>);
     }
-    return dvt == 32 ? sizeof(PrefillSmem<float, 64, 32>) : sizeof(PrefillSmem<float, 64, 16>);
+    if (dk == 64) return dvt == 32 ? sizeof(PrefillSmem<float, 64, 32>) : sizeof(PrefillSmem<float, 64, 16>);
+    if (dk == 128) return dvt == 32 ? sizeof(PrefillSmem<float, 128, 32>) : sizeof(PrefillSmem<float, 128, 16>);
+    return dvt == 32 ? sizeof(PrefillSmem<float, 256, 32>) : sizeof(PrefillSmem<float, 256, 16>);
 }
 
 }  // namespace dla

@@ -72,11 +72,15 @@
 extern "C" {
 #endif
 
-#define DLA_ABI_VERSION 5
+#define DLA_ABI_VERSION 6
 #define DLA_MAX_C 64        /* largest supported cache capacity */
 #define DLA_CHUNK 64        /* tokens per prefill chunk */
 /* bytes of the static per-device scratch of dla_prefill_noalloc (64 MiB) */
 #define DLA_NOALLOC_SCRATCH_BYTES (64ull << 20)
+
+/* Chunk-kernel choice of dla_set_prefill_path (testing and profiling). */
+#define DLA_PATH_AUTO 0       /* the library's choice (the default) */
+#define DLA_PATH_STREAMED 1   /* the streamed chunk kernel for every shape */
 
 typedef enum dla_status {
     DLA_OK = 0,
@@ -181,21 +185,38 @@ typedef struct dla_schedule_out {
 /* Version of this ABI (DLA_ABI_VERSION). */
 int32_t dla_abi_version(void);
 
-/* Bytes of a cache for the given shape and state dtype; 0 if either is invalid. */
+/*
+ * Bytes of a cache for the given shape and state dtype; 0 if either is
+ * invalid (then dla_last_error is left as it was).  The cache is the
+ * fixed-capacity state set M = {(S_i, n_i, I_i)}, m <= C, of the reading
+ * notes' section 5.2 (capacity-bounded memory), one per stream, with the
+ * metadata an online stream carries from call to call (ai-feeds.com summary,
+ * method section).  Host only.
+ */
 uint64_t dla_cache_bytes(int32_t B, int32_t H, int32_t C, int32_t d_k, int32_t d_v,
                          dla_dtype state_dtype);
 
-/* Offsets of the cache buffer's parts (see dla_cache).  DLA_ERR_ARG on a bad shape or dtype. */
+/* Offsets of the cache buffer's parts (the layout of dla_cache above, the
+ * state set of section 5.2).  Host only.  DLA_ERR_ARG on a bad shape or dtype
+ * or a NULL out. */
 dla_status dla_cache_layout(int32_t B, int32_t H, int32_t C, int32_t d_k, int32_t d_v,
                             dla_dtype state_dtype, dla_cache_layout_t *out);
 
 /*
  * Make `base` (device, >= dla_cache_bytes bytes for the same state dtype,
  * 256-byte aligned) an empty cache, or one holding `preload` (may be NULL),
- * and fill *cache.  Supported: C in [1, 64], d_k in {64, 128}, d_v a positive
- * multiple of 16, state_dtype DLA_F32 or DLA_BF16 (preloaded closed states
- * are rounded to bfloat16, to nearest even; the most recent stays float32).
- * A preloaded stream has no previous key, so its next token has s = 1.
+ * and fill *cache: the empty state set the layer starts from, or a given one
+ * (reading notes, section 5.2: the cache M of at most C states, each with its
+ * token count n_i and information sum I_i; ai-feeds.com summary, method
+ * section: the state set handed on to decoding).  Supported: C in [1, 64],
+ * d_k in {64, 128, 256}, d_v a positive multiple of 16 up to 4096,
+ * state_dtype DLA_F32 or DLA_BF16 (preloaded closed states are rounded to
+ * bfloat16, to nearest even; the most recent stays float32).  A preloaded
+ * stream has no previous key, so its next token has s = 1.  Enqueues one
+ * kernel on `stream`; the preload buffers must stay alive until it ran.
+ * DLA_ERR_ARG on a NULL cache, bad shape, misaligned or short buffer, bad
+ * preload (m0 outside [0, C], NULL or misaligned pointers); DLA_ERR_HIP when
+ * the launch fails.
  */
 dla_status dla_cache_init(dla_cache *cache, void *base, uint64_t bytes, int32_t B,
                           int32_t H, int32_t C, int32_t d_k, int32_t d_v, dla_dtype state_dtype,
@@ -213,7 +234,9 @@ dla_status dla_cache_init(dla_cache *cache, void *base, uint64_t bytes, int32_t 
  */
 dla_status dla_cache_set_merge_rule(dla_cache *cache, int32_t rule);
 
-/* Workspace bytes dla_prefill needs for this shape; 0 if the shape is invalid. */
+/* Workspace bytes dla_prefill needs for this shape (the schedule of section
+ * 5.1-5.2 and the chunk operands of the section 5.3 read); 0 if the shape is
+ * invalid.  Host only. */
 uint64_t dla_prefill_workspace_bytes(int32_t B, int32_t H, int32_t T, int32_t C,
                                      int32_t d_k, int32_t d_v);
 
@@ -230,7 +253,7 @@ uint64_t dla_prefill_workspace_bytes(int32_t B, int32_t H, int32_t T, int32_t C,
  *   v, o    [B*H][T][d_v]   io dtype, device
  *   lam     [B*H][T][C]     io dtype, device; lam[.][t][j] weights slot j
  *   tau     boundary threshold
- *   io      DLA_F32 (d_k = 64 only) or DLA_BF16 (d_k in {64, 128})
+ *   io      DLA_F32 (d_k in {64, 128}) or DLA_BF16 (d_k in {64, 128, 256})
  *   workspace  device, >= dla_prefill_workspace_bytes, 256-byte aligned;
  *              scratch owned by the call until the stream work completes
  *   sched   optional schedule export, may be NULL
@@ -281,10 +304,11 @@ dla_status dla_prefill_noalloc(const void *q, const void *k, const void *v, cons
                                const dla_schedule_out *sched, void *stream);
 
 /*
- * Name of the chunk kernel (the MFMA sweep after the schedule kernels) that
- * dla_prefill launches for this shape and io dtype under the current
- * environment, e.g. "k_prefill_rs<128,16,8>" (template arguments d_k, value
- * columns per block, state slots per wave).  For profilers and benchmarks.
+ * Name of the chunk kernel (the MFMA sweep of the section 5.3 read after the
+ * schedule kernels) that dla_prefill launches for this shape and io dtype on
+ * this thread (see dla_set_prefill_path), e.g. "k_prefill_rs<128,16,8>"
+ * (template arguments d_k, value columns per block, state slots per wave).
+ * For profilers and benchmarks; host only.
  * The string is thread-local and valid until the next call on this thread;
  * NULL for a shape dla_prefill would reject.
  */
@@ -293,7 +317,14 @@ const char *dla_prefill_kernel(dla_dtype io, int32_t B, int32_t H, int32_t C, in
 /*
  * Decode step: consume one token of every stream on top of the cache and
  * write o.  q, k [B*H][d_k]; v, o [B*H][d_v]; lam [B*H][C]; io dtype, device.
- * Supported: d_k = d_v = 128 or d_k = d_v = 64, any io dtype.
+ * Supported: d_k and d_v each in {64, 128, 256}, any io dtype
+ * (DLA_ERR_UNSUPPORTED for another d_v).  The step is the layer's online
+ * form: the token's information and boundary (reading notes, section 5.1),
+ * the capacity merge (section 5.2), the read o = sum_j lam[j] S_(j) q after
+ * the update (sections 5.3 and 1); the updated state set stays in the cache
+ * for the next step (ai-feeds.com summary, method section).  Enqueues one
+ * kernel on `stream`; DLA_ERR_ARG on a bad cache, NULL or misaligned
+ * pointers or a NaN tau, DLA_ERR_HIP when the launch fails.
  *
  * With the cache's rule DLA_FENWICK the step follows the Log-Linear fixed
  * schedule (top of this header) on a cache that fixed-schedule calls left (or
@@ -311,6 +342,19 @@ dla_status dla_decode_step(const void *q, const void *k, const void *v, const vo
                            const dla_schedule_out *sched, void *stream);
 
 /*
+ * Testing and profiling hook: which chunk kernel the dla_prefill calls made
+ * on this thread launch.  DLA_PATH_AUTO (the default) lets the library
+ * choose (the register-resident sweep for bfloat16 io, C <= 32 and
+ * d_k <= 128, the streamed kernel otherwise); DLA_PATH_STREAMED runs the
+ * streamed kernel for every shape.  value_columns = 0 lets the library choose
+ * the streamed kernel's d_v slice width, 16 or 32 forces it where d_v allows
+ * and its LDS fits.  Both kernels compute the same layer (reading notes,
+ * sections 5.1-5.3); production callers never need this.  Host only;
+ * DLA_ERR_ARG for an unknown path or width (nothing changes then).
+ */
+dla_status dla_set_prefill_path(int32_t path, int32_t value_columns);
+
+/*
  * Benchmark hook.  While set, every dla_prefill call made on this thread
  * records the event `before` right before its chunk kernel (the MFMA
  * prefill sweep, after the schedule kernels) and `after` right after it, on
@@ -319,10 +363,11 @@ dla_status dla_decode_step(const void *q, const void *k, const void *v, const vo
  */
 dla_status dla_set_prefill_events(void *before, void *after);
 
-/* Static text for a status code. */
+/* Static text for a status code (host only). */
 const char *dla_status_str(dla_status s);
 
-/* Detail of the last non-OK status returned on this thread ("" if none). */
+/* Detail of the last non-OK status returned on this thread ("" if none;
+ * host only).  The string is thread-local and valid until the next call. */
 const char *dla_last_error(void);
 
 #ifdef __cplusplus

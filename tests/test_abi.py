@@ -23,7 +23,7 @@ def test_library_exports_every_declared_symbol():
     assert {"dla_prefill", "dla_decode_step", "dla_cache_init"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert dla.dla_abi_version() == 5
+    assert dla.dla_abi_version() == 6
 
 
 def test_sizes_and_layout():
@@ -31,6 +31,8 @@ def test_sizes_and_layout():
     assert dla.dla_cache_bytes(1, 1, 0, 64, 64) == 0
     assert dla.dla_cache_bytes(1, 1, 65, 64, 64) == 0
     assert dla.dla_cache_bytes(1, 1, 8, 96, 64) == 0
+    assert dla.dla_cache_bytes(1, 1, 8, 512, 64) == 0
+    assert dla.dla_cache_bytes(1, 1, 8, 256, 64) > 8 * 256 * 64 * 4
     assert dla.dla_cache_bytes(1, 1, 8, 64, 24) == 0
     L = dla.dla_cache_layout(2, 3, 32, 128, 256)
     assert L.meta_offset >= 6 * 32 * 128 * 256 * 4 and L.meta_offset % 256 == 0
@@ -43,15 +45,30 @@ def test_sizes_and_layout():
 
 
 def test_prefill_kernel_choice(monkeypatch):
-    monkeypatch.delenv("DLA_PREFILL_PATH", raising=False)
-    monkeypatch.delenv("DLA_PREFILL_DVT", raising=False)
+    # the environment never changes the choice; only the explicit hook does
+    monkeypatch.setenv("DLA_PREFILL_PATH", "streamed")
+    monkeypatch.setenv("DLA_PREFILL_DVT", "32")
     assert dla.dla_prefill_kernel(dla.DLA_BF16, 2, 16, 32, 128, 256) == "k_prefill_rs<128,16,8>"
     assert dla.dla_prefill_kernel(dla.DLA_BF16, 4, 24, 16, 128, 64) == "k_prefill_rs<128,16,4>"
     assert dla.dla_prefill_kernel(dla.DLA_F32, 1, 1, 8, 64, 64) == "k_prefill<f32,64,16>"
+    assert dla.dla_prefill_kernel(dla.DLA_F32, 1, 1, 8, 128, 64) == "k_prefill<f32,128,16>"
     assert dla.dla_prefill_kernel(dla.DLA_BF16, 1, 1, 48, 64, 64) == "k_prefill<bf16,64,16>"
+    assert dla.dla_prefill_kernel(dla.DLA_BF16, 1, 1, 8, 256, 64) == "k_prefill<bf16,256,16>"
+    # d_k = 256 and fp32 d_k = 128 keep 16-column slices (32 would not fit the LDS)
+    assert dla.dla_prefill_kernel(dla.DLA_BF16, 8, 32, 8, 256, 256) == "k_prefill<bf16,256,16>"
     assert dla.dla_prefill_kernel(dla.DLA_BF16, 1, 1, 8, 96, 64) is None
-    monkeypatch.setenv("DLA_PREFILL_PATH", "streamed")
-    assert dla.dla_prefill_kernel(dla.DLA_BF16, 2, 16, 32, 128, 256) == "k_prefill<bf16,128,32>"
+    try:
+        assert dla.dla_set_prefill_path(dla.DLA_PATH_STREAMED, 0) == dla.DLA_OK
+        assert dla.dla_prefill_kernel(dla.DLA_BF16, 2, 16, 32, 128, 256) == "k_prefill<bf16,128,32>"
+        assert dla.dla_set_prefill_path(dla.DLA_PATH_STREAMED, 16) == dla.DLA_OK
+        assert dla.dla_prefill_kernel(dla.DLA_BF16, 2, 16, 32, 128, 256) == "k_prefill<bf16,128,16>"
+        assert dla.dla_set_prefill_path(7, 0) == dla.DLA_ERR_ARG
+        assert dla.dla_set_prefill_path(dla.DLA_PATH_AUTO, 24) == dla.DLA_ERR_ARG
+        # (a refused call changes nothing)
+        assert dla.dla_prefill_kernel(dla.DLA_BF16, 2, 16, 32, 128, 256) == "k_prefill<bf16,128,16>"
+    finally:
+        dla.dla_set_prefill_path(dla.DLA_PATH_AUTO, 0)
+    assert dla.dla_prefill_kernel(dla.DLA_BF16, 2, 16, 32, 128, 256) == "k_prefill_rs<128,16,8>"
 
 
 def _cache(B=1, H=1, C_=8, dk=64, dv=64, base=0x10000):
@@ -91,12 +108,16 @@ def test_bad_arguments_are_rejected_on_the_host():
     c_small = _cache()
     c_small.bytes -= 1
     assert call(cache=c_small) == dla.DLA_ERR_ARG
-    assert call(cache=_cache(dk=128, dv=64), io=dla.DLA_F32,
-                workspace_bytes=dla.dla_prefill_workspace_bytes(1, 1, 100, 8, 128, 64)) \
+    # fp32 io stops at d_k = 128 (the streamed kernel's LDS at d_k = 256)
+    assert call(cache=_cache(dk=256, dv=64), io=dla.DLA_F32,
+                workspace_bytes=dla.dla_prefill_workspace_bytes(1, 1, 100, 8, 256, 64)) \
         == dla.DLA_ERR_UNSUPPORTED
-    # decode
+    assert "LDS" in dla.dla_last_error()
+    # decode: d_v outside {64, 128, 256}
     assert dla.dla_decode_step(p, p, p, p, None, 0.3, dla.DLA_BF16, c, None, None) == dla.DLA_ERR_ARG
-    assert dla.dla_decode_step(p, p, p, p, p, 0.3, dla.DLA_BF16, _cache(dk=64, dv=128), None, None) \
+    assert dla.dla_decode_step(p, p, p, p, p, 0.3, dla.DLA_BF16, _cache(dk=64, dv=96), None, None) \
+        == dla.DLA_ERR_UNSUPPORTED
+    assert dla.dla_decode_step(p, p, p, p, p, 0.3, dla.DLA_BF16, _cache(dk=64, dv=512), None, None) \
         == dla.DLA_ERR_UNSUPPORTED
     # cache init
     cc = dla.dla_cache()
@@ -157,8 +178,7 @@ def test_merge_rule_is_validated_on_the_host():
     assert dla.dla_decode_step(p, p, p, p, p, 0.3, dla.DLA_BF16, c, None, None) == dla.DLA_ERR_ARG
 
 
-def test_fenwick_rule_checks_on_the_host(monkeypatch):
-    monkeypatch.delenv("DLA_PREFILL_PATH", raising=False)
+def test_fenwick_rule_checks_on_the_host():
     p = 0x100000
     c = _cache()                      # C = 8: levels 0 .. 7, enough for T <= 128
     dla.dla_cache_set_merge_rule(c, dla.DLA_FENWICK)

@@ -154,32 +154,73 @@ def test_fenwick_prefill_decode_prefill():
     _check_cache(cache.read(), d["k"], d["v"], T, "prefill + decode + prefill")
 
 
-@pytest.mark.parametrize("io,dk,ends", [("f32", 64, (300,)), ("f32", 64, (100, 613, 1000)),
-                                        ("bf16", 128, (700,)), ("bf16", 64, (65, 400, 1100))])
-def test_fenwick_streamed_kernel(io, dk, ends, monkeypatch):
-    """The fixed schedule on the streamed prefill kernel (fp32 io; bf16 io
-    forced there): from position 0 and continuing, one pass of the oracle."""
+@pytest.fixture
+def streamed_path():
+    import dynamic_state_memory_amd as dla
+    dla.dla_set_prefill_path(dla.DLA_PATH_STREAMED, 0)
+    yield
+    dla.dla_set_prefill_path(dla.DLA_PATH_AUTO, 0)
+
+
+def _streamed_prefill_pieces(d, ends, C, dk, dv, io, cache):
     torch = torch_mod()
     import dynamic_state_memory_amd as dla
-    monkeypatch.setenv("DLA_PREFILL_PATH", "streamed")
-    say(f"fenwick streamed io={io} dk={dk} ends={ends}")
-    T = ends[-1]
-    d = _inputs(T, [21, 22], 16, dk=dk, dv=32)
     dev = torch.device("cuda:0")
     dt = torch.float32 if io == "f32" else torch.bfloat16
-    cache = dla.Cache(1, 2, 16, dk, 32, device=dev, merge_rule="fenwick")
+    S = d["k"].shape[0]
     outs, lo = [], 0
     for hi in ends:
         def up(a, n):
-            return torch.from_numpy(np.ascontiguousarray(a[:, lo:hi])).to(dev).to(dt).reshape(1, 2, hi - lo, n)
-        ws = dla.prefill_workspace(1, 2, hi - lo, 16, dk, 32, dev)
-        o = dla.prefill(up(d["q"], dk), up(d["k"], dk), up(d["v"], 32), up(d["lam"], 16), 0.0, cache, workspace=ws)
-        outs.append(o.float().cpu().numpy().reshape(2, hi - lo, 32))
+            return torch.from_numpy(np.ascontiguousarray(a[:, lo:hi])).to(dev).to(dt).reshape(1, S, hi - lo, n)
+        ws = dla.prefill_workspace(1, S, hi - lo, C, dk, dv, dev)
+        o = dla.prefill(up(d["q"], dk), up(d["k"], dk), up(d["v"], dv), up(d["lam"], C), 0.0, cache, workspace=ws)
+        outs.append(o.float().cpu().numpy().reshape(S, hi - lo, dv))
         lo = hi
     torch.cuda.synchronize()
-    compare_outputs(np.concatenate(outs, 1), FEN.outputs(d["q"], d["k"], d["v"], d["lam"]), TOL[io],
-                    f"streamed {io} {ends}")
+    return np.concatenate(outs, 1)
+
+
+@pytest.mark.parametrize("io,dk,ends,C", [("f32", 64, (300,), 16), ("f32", 64, (100, 613, 1000), 16),
+                                          ("bf16", 128, (700,), 16), ("bf16", 64, (65, 400, 1100), 16),
+                                          ("f32", 64, (200, 900), 48), ("bf16", 128, (500, 1300), 64),
+                                          ("f32", 128, (130, 800), 16), ("bf16", 256, (90, 600), 24)])
+def test_fenwick_streamed_kernel(io, dk, ends, C, streamed_path):
+    """The fixed schedule on the streamed prefill kernel (fp32 io, C > 32 or
+    d_k = 256; bf16 io forced there): from position 0 and continuing, one pass
+    of the oracle."""
+    torch = torch_mod()
+    import dynamic_state_memory_amd as dla
+    say(f"fenwick streamed io={io} dk={dk} ends={ends} C={C}")
+    T = ends[-1]
+    d = _inputs(T, [21, 22], C, dk=dk, dv=32)
+    cache = dla.Cache(1, 2, C, dk, 32, device=torch.device("cuda:0"), merge_rule="fenwick")
+    o = _streamed_prefill_pieces(d, ends, C, dk, 32, io, cache)
+    compare_outputs(o, FEN.outputs(d["q"], d["k"], d["v"], d["lam"]), TOL[io], f"streamed {io} {ends}")
     _check_cache(cache.read(), d["k"], d["v"], T, f"streamed {io} {ends}")
+
+
+def test_fenwick_streamed_position_limit(streamed_path):
+    """The position limit on the streamed kernel with fp32 io: C = 4 level
+    weights cover positions 0 .. 7, so 5 tokens at position 5 are refused on
+    the device (NaN outputs, the cache as it was); 3 tokens are not."""
+    torch = torch_mod()
+    import dynamic_state_memory_amd as dla
+    say("fenwick streamed prefill position limit (f32)")
+    d = _inputs(10, [20], 4, dk=64, dv=16)
+    cache = dla.Cache(1, 1, 4, 64, 16, device=torch.device("cuda:0"), merge_rule="fenwick")
+    _streamed_prefill_pieces(d, (5,), 4, 64, 16, "f32", cache)
+    before = cache.read()
+    part = {x: d[x][:, 5:10] for x in ("q", "k", "v", "lam")}
+    o = _streamed_prefill_pieces(part, (5,), 4, 64, 16, "f32", cache)
+    assert np.isnan(o).all()
+    after = cache.read()
+    for key in ("m", "t_seen", "order", "start", "count", "S"):
+        assert np.array_equal(before[key], after[key]), key
+    part = {x: d[x][:, 5:8] for x in ("q", "k", "v", "lam")}
+    o = _streamed_prefill_pieces(part, (3,), 4, 64, 16, "f32", cache)
+    ref = FEN.outputs(*(d[x][:, :8] for x in ("q", "k", "v", "lam")))
+    compare_outputs(o, ref[:, 5:8], TOL["f32"], "positions 5 .. 7")
+    _check_cache(cache.read(), d["k"], d["v"], 8, "positions 0 .. 7")
 
 
 def test_fenwick_prefill_position_limit():
@@ -244,18 +285,23 @@ def _decode_steps(d, lo, hi, cache, io):
     return np.concatenate(outs, 1) if outs else np.zeros((B * H, 0, dv), np.float32)
 
 
-@pytest.mark.parametrize("T0,k,dd,io", [(0, 70, 64, "f32"), (0, 40, 128, "bf16"), (1, 66, 128, "bf16"),
-                                        (64, 70, 64, "bf16"), (100, 60, 128, "bf16"), (255, 70, 64, "bf16"),
-                                        (512, 33, 128, "bf16"), (1000, 50, 64, "bf16")])
-def test_fenwick_decode_continues_the_stream(T0, k, dd, io):
+@pytest.mark.parametrize("T0,k,dd,io,dv", [(0, 70, 64, "f32", 64), (0, 40, 128, "bf16", 128),
+                                           (1, 66, 128, "bf16", 128), (64, 70, 64, "bf16", 64),
+                                           (100, 60, 128, "bf16", 128), (255, 70, 64, "bf16", 64),
+                                           (512, 33, 128, "bf16", 128), (1000, 50, 64, "bf16", 64),
+                                           (300, 40, 128, "bf16", 64), (200, 50, 128, "bf16", 256),
+                                           (0, 60, 256, "bf16", 128), (150, 30, 64, "bf16", 256),
+                                           (200, 20, 256, "bf16", 64)])
+def test_fenwick_decode_continues_the_stream(T0, k, dd, io, dv):
     """Prefill T0 tokens (none: decode from an empty cache), then k decode
-    steps: outputs and final cache as one pass of the oracle over T0 + k."""
+    steps: outputs and final cache as one pass of the oracle over T0 + k
+    (d_k = dd, and d_v = dv, equal or not)."""
     torch = torch_mod()
     import dynamic_state_memory_amd as dla
-    say(f"fenwick decode T0={T0} k={k} d={dd} io={io}")
+    say(f"fenwick decode T0={T0} k={k} d_k={dd} d_v={dv} io={io}")
     T = T0 + k
-    d = _inputs(T, [11, 12], 16, dk=dd, dv=dd)
-    cache = dla.Cache(1, 2, 16, dd, dd, device=torch.device("cuda:0"), merge_rule="fenwick")
+    d = _inputs(T, [11, 12], 16, dk=dd, dv=dv)
+    cache = dla.Cache(1, 2, 16, dd, dv, device=torch.device("cuda:0"), merge_rule="fenwick")
     parts = []
     if T0:
         pre = {x: d[x][:, :T0] for x in ("q", "k", "v", "lam")}

@@ -69,14 +69,13 @@ REDUCED = [
 
 
 @pytest.fixture(params=["register", "streamed"])
-def prefill_path(request, monkeypatch):
+def prefill_path(request):
     """Both prefill kernels: states held in registers (the default for bf16
     inputs and C <= 32) and states streamed from the cache."""
-    if request.param == "streamed":
-        monkeypatch.setenv("DLA_PREFILL_PATH", "streamed")
-    else:
-        monkeypatch.delenv("DLA_PREFILL_PATH", raising=False)
-    return request.param
+    import dynamic_state_memory_amd as dla
+    dla.dla_set_prefill_path(dla.DLA_PATH_STREAMED if request.param == "streamed" else dla.DLA_PATH_AUTO, 0)
+    yield request.param
+    dla.dla_set_prefill_path(dla.DLA_PATH_AUTO, 0)
 
 
 @pytest.mark.parametrize("name,streams,T,means", REDUCED)
@@ -234,6 +233,20 @@ def test_random_shapes(T, dk, dv, C, tau, means, io, rule, S):
     cfg = dataclasses.replace(workloads.CONFIGS[base], dk=dk, dv=dv, C=C, seg_means=means)
     d = workloads.prefill_inputs(cfg, streams=list(range(S)), T=T)
     _full_check(d, C, tau, io, f"random T={T} dk={dk} dv={dv} C={C} tau={tau} means={means}", merge_rule=rule)
+
+
+@pytest.mark.parametrize("io,dk,dv,C,T,means", [("bf16", 256, 64, 16, 900, (15,)), ("bf16", 256, 128, 40, 700, (10,)),
+                                               ("f32", 128, 64, 8, 1000, (25,)), ("f32", 128, 48, 48, 600, (8,)),
+                                               ("f32", 128, 256, 12, 400, (12,))])
+def test_wider_key_shapes(io, dk, dv, C, T, means):
+    """d_k = 256 with bf16 io and d_k = 128 with fp32 io (the streamed
+    kernel): schedule bit-exact, final states and outputs within their gates."""
+    torch_mod()
+    base = "tiny_fp32" if io == "f32" else "long_t131k_bf16"
+    cfg = dataclasses.replace(workloads.CONFIGS[base], H=2, dk=dk, dv=dv, C=C, seg_means=means)
+    d = workloads.prefill_inputs(cfg, streams=[0, 1], T=T)
+    r = _full_check(d, C, cfg.tau, io, f"wider keys io={io} dk={dk} dv={dv} C={C}")
+    assert r["n_ev"].min() > 0
 
 
 def test_literal_noise_reading_every_token_opens(prefill_path):

@@ -26,6 +26,8 @@ DLA_OK, DLA_ERR_ARG, DLA_ERR_UNSUPPORTED, DLA_ERR_WORKSPACE, DLA_ERR_HIP = 0, 1,
 DLA_F32, DLA_BF16 = 0, 1
 DLA_MERGE_SUM, DLA_MERGE_DENSITY, DLA_FENWICK = 0, 1, 2
 DLA_PATH_AUTO, DLA_PATH_STREAMED = 0, 1
+DLA_SCORE_COSINE, DLA_SCORE_STATE = 0, 1
+SCORE_RULES = {"cosine": DLA_SCORE_COSINE, "state": DLA_SCORE_STATE}
 MERGE_RULES = {"sum": DLA_MERGE_SUM, "density": DLA_MERGE_DENSITY, "fenwick": DLA_FENWICK}
 DLA_MAX_C = 64
 DLA_CHUNK = 64
@@ -48,7 +50,7 @@ _STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace", 4: 
 class dla_cache(C.Structure):
     _fields_ = [("B", C.c_int32), ("H", C.c_int32), ("C", C.c_int32), ("d_k", C.c_int32),
                 ("d_v", C.c_int32), ("merge_rule", C.c_int32), ("state_dtype", C.c_int32),
-                ("reserved", C.c_int32), ("base", C.c_void_p), ("bytes", C.c_uint64)]
+                ("score_rule", C.c_int32), ("base", C.c_void_p), ("bytes", C.c_uint64)]
 
 
 class dla_cache_layout_t(C.Structure):
@@ -101,6 +103,8 @@ def load():
         [C.c_int, C.POINTER(dla_cache_preload), vp]
     lib.dla_cache_set_merge_rule.restype = C.c_int
     lib.dla_cache_set_merge_rule.argtypes = [C.POINTER(dla_cache), i32]
+    lib.dla_cache_set_score_rule.restype = C.c_int
+    lib.dla_cache_set_score_rule.argtypes = [C.POINTER(dla_cache), i32]
     lib.dla_prefill_workspace_bytes.restype = u64
     lib.dla_prefill_workspace_bytes.argtypes = [i32] * 6
     lib.dla_prefill.restype = C.c_int
@@ -150,6 +154,10 @@ def dla_cache_init(cache: dla_cache, base: int, nbytes: int, B, H, C_, d_k, d_v,
 
 def dla_cache_set_merge_rule(cache: dla_cache, rule: int) -> int:
     return _check(load().dla_cache_set_merge_rule(C.byref(cache), rule))
+
+
+def dla_cache_set_score_rule(cache: dla_cache, rule: int) -> int:
+    return _check(load().dla_cache_set_score_rule(C.byref(cache), rule))
 
 
 def dla_prefill_workspace_bytes(B, H, T, C_, d_k, d_v) -> int:
@@ -242,10 +250,12 @@ class Cache:
     "fenwick" for the Log-Linear fixed schedule (lam weights levels, C at
     least the level count bit_length(t - 1) + 1 of the positions reached).
     ``state_dtype``: "f32" (every state float32) or "bf16" (closed states
-    bfloat16, the most recent one float32)."""
+    bfloat16, the most recent one float32).
+    ``score_rule``: "cosine" (cosine of consecutive keys, the default) or
+    "state" (the state information score against the current state)."""
 
     def __init__(self, B, H, C_, d_k, d_v, device="cuda", preload: dict | None = None,
-                 merge_rule: str = "sum", state_dtype: str = "f32"):
+                 merge_rule: str = "sum", state_dtype: str = "f32", score_rule: str = "cosine"):
         torch = _torch()
         if state_dtype not in ("f32", "bf16"):
             raise DLAError(DLA_ERR_ARG, f"unknown state dtype {state_dtype!r}")
@@ -274,16 +284,20 @@ class Cache:
         if merge_rule not in MERGE_RULES:
             raise DLAError(DLA_ERR_ARG, f"unknown merge rule {merge_rule!r}")
         dla_cache_set_merge_rule(self.view, MERGE_RULES[merge_rule])
+        if score_rule not in SCORE_RULES:
+            raise DLAError(DLA_ERR_ARG, f"unknown score rule {score_rule!r}")
+        dla_cache_set_score_rule(self.view, SCORE_RULES[score_rule])
 
     def reset(self):
         """Make every stream empty again (same buffer, shape, merge rule and
         state dtype), so that the next prefill starts afresh."""
         B, H, C_, d_k, d_v = self.shape
-        rule = self.view.merge_rule
+        rule, score = self.view.merge_rule, self.view.score_rule
         sdt = DLA_BF16 if self.state_dtype == "bf16" else DLA_F32
         _check(dla_cache_init(self.view, self.buf.data_ptr(), self.buf.numel(), B, H, C_, d_k, d_v, sdt, None,
                               _stream(self.buf.device)))
         dla_cache_set_merge_rule(self.view, rule)
+        dla_cache_set_score_rule(self.view, score)
 
     @property
     def device(self):

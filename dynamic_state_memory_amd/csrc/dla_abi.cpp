@@ -151,6 +151,24 @@ dla_status check_cache(const dla_cache *c)
         return fail(DLA_ERR_ARG, "cache buffer too small (%llu bytes)", static_cast<unsigned long long>(c->bytes));
     if (c->merge_rule != DLA_MERGE_SUM && c->merge_rule != DLA_MERGE_DENSITY && c->merge_rule != DLA_FENWICK)
         return fail(DLA_ERR_ARG, "unknown merge rule %d", c->merge_rule);
+    if (c->score_rule != DLA_SCORE_COSINE && c->score_rule != DLA_SCORE_STATE)
+        return fail(DLA_ERR_ARG, "unknown score rule %d", c->score_rule);
+    return DLA_OK;
+}
+
+// Shapes the state information score supports (its schedule kernel holds a
+// stream's current state in registers and the chunk in LDS).
+dla_status check_state_score(const dla_cache *c, bool io_bf16)
+{
+    if (c->score_rule != DLA_SCORE_STATE || c->merge_rule == DLA_FENWICK) return DLA_OK;
+    const bool w = (c->d_v == 64 || c->d_v == 128 || c->d_v == 256);
+    if (!w) return fail(DLA_ERR_UNSUPPORTED, "the state score supports d_v in {64, 128, 256} (got %d)", c->d_v);
+    if (!io_bf16 && (c->d_k > 128 || c->d_v > 128))
+        return fail(DLA_ERR_UNSUPPORTED, "the state score with float32 io supports d_k, d_v in {64, 128}");
+    if (c->d_k == 256 && c->d_v == 256)
+        return fail(DLA_ERR_UNSUPPORTED,
+                    "the state score at d_k = d_v = 256 is not supported (the current state, 64 K floats, held by "
+                    "one block's registers, would spill)");
     return DLA_OK;
 }
 
@@ -321,7 +339,7 @@ dla_status dla_cache_init(dla_cache *cache, void *base, uint64_t bytes, int32_t 
     cache->B = B; cache->H = H; cache->C = C; cache->d_k = d_k; cache->d_v = d_v;
     cache->merge_rule = DLA_MERGE_SUM;
     cache->state_dtype = state_dtype;
-    cache->reserved = 0;
+    cache->score_rule = DLA_SCORE_COSINE;
     cache->base = base;
     cache->bytes = bytes;
     const CacheGeom g = geom(cache);
@@ -402,6 +420,11 @@ dla_status prefill_call(const void *q, const void *k, const void *v, const void 
     a.tau = tau;
     a.io_bf16 = io == DLA_BF16;
     a.merge_rule = cache->merge_rule;
+    a.score_rule = cache->merge_rule == DLA_FENWICK ? DLA_SCORE_COSINE : cache->score_rule;
+    s = check_state_score(cache, a.io_bf16);
+    if (s != DLA_OK) return s;
+    if (a.score_rule == DLA_SCORE_STATE && state_score_smem_bytes(a.io_bf16, cache->d_k, cache->d_v) > kLdsBytes)
+        return fail(DLA_ERR_UNSUPPORTED, "the state score's chunk operands at this shape need more LDS than a compute unit has");
     const PrefillPlan plan = plan_prefill(a.io_bf16, BH, cache->C, cache->d_k, cache->d_v);
     a.dvt = plan.dvt;
     a.register_resident = plan.register_resident;
@@ -505,6 +528,9 @@ dla_status dla_decode_step(const void *q, const void *k, const void *v, const vo
     a.tau = tau;
     a.io_bf16 = io == DLA_BF16;
     a.merge_rule = cache->merge_rule;
+    a.score_rule = cache->merge_rule == DLA_FENWICK ? DLA_SCORE_COSINE : cache->score_rule;
+    s = check_state_score(cache, a.io_bf16);
+    if (s != DLA_OK) return s;
     a.g = geom(cache);
     const int64_t BH = static_cast<int64_t>(cache->B) * cache->H;
     const CacheOffsets co = cache_offsets(BH, cache->C, cache->d_k, cache->d_v, a.g.state_bf16);
@@ -517,6 +543,14 @@ dla_status dla_decode_step(const void *q, const void *k, const void *v, const vo
     a.sched.m_t = sched ? sched->m_t : nullptr;
     a.sched.ev_i = sched ? sched->ev_i : nullptr;
     return hip_status(launch_decode(a, static_cast<hipStream_t>(stream)), "decode launch");
+}
+
+dla_status dla_cache_set_score_rule(dla_cache *cache, int32_t rule)
+{
+    if (!cache) return fail(DLA_ERR_ARG, "cache is NULL");
+    if (rule != DLA_SCORE_COSINE && rule != DLA_SCORE_STATE) return fail(DLA_ERR_ARG, "unknown score rule %d", rule);
+    cache->score_rule = rule;
+    return ok();
 }
 
 dla_status dla_set_prefill_path(int32_t path, int32_t value_columns)

@@ -97,6 +97,7 @@ struct PrefillArgs {
     float tau;
     int io_bf16;
     int merge_rule;                   // DLA_MERGE_SUM, DLA_MERGE_DENSITY or DLA_FENWICK
+    int score_rule;                   // DLA_SCORE_COSINE or DLA_SCORE_STATE
     int dvt;
     CacheGeom g;
     float *states;                    // slots (bf16 data when g.state_bf16)
@@ -121,6 +122,7 @@ struct DecodeArgs {
     float tau;
     int io_bf16;
     int merge_rule;                   // DLA_MERGE_SUM or DLA_MERGE_DENSITY
+    int score_rule;                   // DLA_SCORE_COSINE or DLA_SCORE_STATE
     CacheGeom g;
     float *states;                    // slots (bf16 data when g.state_bf16)
     float *active;                    // [BH][dv][dk] fp32 active states (g.state_bf16), else NULL
@@ -137,6 +139,8 @@ hipError_t launch_prefill_rs(const PrefillArgs &a, hipStream_t stream);
 hipError_t launch_fenwick_schedule(const PrefillArgs &a, hipStream_t stream);
 hipError_t launch_fen_refused(const PrefillArgs &a, hipStream_t stream);   // NaN outputs of refused streams
 size_t prefill_rs_smem_bytes(int dk, int dvt, int C);
+hipError_t launch_state_score(const PrefillArgs &a, hipStream_t stream);   // scores of the state rule
+size_t state_score_smem_bytes(int io_bf16, int dk, int dv);
 int prefill_rs_dvt(int dk, int C, int dvt_wanted);
 int prefill_rs_spw(int C);      // closed-state slots per wave of the register-resident sweep
 

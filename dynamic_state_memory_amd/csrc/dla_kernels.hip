@@ -1075,7 +1075,8 @@ __global__ __launch_bounds__(256) void k_decode(const TIO *__restrict__ Qg, cons
                                                 TIO *__restrict__ Og, float tau, int C,
                                                 float *__restrict__ states, float *__restrict__ active,
                                                 uint8_t *__restrict__ meta_base,
-                                                size_t meta_stride, DecodeSched sched, int merge_rule)
+                                                size_t meta_stride, DecodeSched sched, int merge_rule,
+                                                int score_rule)
 {
     typedef DecodeShape<DK, DV> Sh;
     constexpr int G = Sh::G, R = Sh::R, P = Sh::P, PB = Sh::PB;
@@ -1086,6 +1087,7 @@ __global__ __launch_bounds__(256) void k_decode(const TIO *__restrict__ Qg, cons
     __shared__ float wlog[kMaxC];
     __shared__ int32_t order_s[kMaxC];
     __shared__ double red[4][4];
+    __shared__ double fsq[4];
     __shared__ float orow[DV];
     __shared__ int32_t ctl[8];        // mode, add_slot, set_slot, merge_i, m, ...
     __shared__ float sc_kq;
@@ -1108,6 +1110,7 @@ __global__ __launch_bounds__(256) void k_decode(const TIO *__restrict__ Qg, cons
     if (tid < DV) vs[tid] = to_f(Vg[static_cast<size_t>(bh) * DV + tid]);
     if (tid < C) lw[tid] = to_f(Lg[static_cast<size_t>(bh) * C + tid]);
     __syncthreads();
+    const bool state_score = score_rule == DLA_SCORE_STATE;
     {
         double d = 0.0, a = 0.0, b = 0.0, kq = 0.0;
         if (tid < DK) {
@@ -1115,8 +1118,37 @@ __global__ __launch_bounds__(256) void k_decode(const TIO *__restrict__ Qg, cons
             d = x * y; a = x * x; b = y * y;
             kq = x * static_cast<double>(qs[tid]);
         }
-        d = wave_sum(d); a = wave_sum(a); b = wave_sum(b); kq = wave_sum(kq);
-        if (lane == 0) { red[wave][0] = d; red[wave][1] = a; red[wave][2] = b; red[wave][3] = kq; }
+        if (state_score) {
+            // the state information score needs x = v^T S k and |S|_F^2 of the
+            // current (most recent) state, read once before the step; a and b
+            // then carry |k|^2 and |v|^2
+            const int m0 = head->m;
+            d = 0.0;
+            a = tid < DK ? static_cast<double>(ks[tid]) * ks[tid] : 0.0;
+            b = tid < DV ? static_cast<double>(vs[tid]) * vs[tid] : 0.0;
+            double f = 0.0;
+            if (m0 > 0) {
+                const int col = (tid % G) * 4, row0 = tid / G;
+                const float4 k4 = *reinterpret_cast<const float4 *>(&ks[col]);
+                const float *src;
+                if constexpr (BF) src = active + static_cast<size_t>(bh) * SS;
+                else src = states + (static_cast<size_t>(bh) * C + order[m0 - 1]) * SS;
+#pragma unroll 4
+                for (int j = 0; j < P; ++j) {
+                    const int row = row0 + R * j;
+                    const float4 x = *reinterpret_cast<const float4 *>(src + static_cast<size_t>(row) * DK + col);
+                    d += static_cast<double>(vs[row]) * (static_cast<double>(x.x) * k4.x + static_cast<double>(x.y) * k4.y +
+                                                         static_cast<double>(x.z) * k4.z + static_cast<double>(x.w) * k4.w);
+                    f += static_cast<double>(x.x) * x.x + static_cast<double>(x.y) * x.y +
+                         static_cast<double>(x.z) * x.z + static_cast<double>(x.w) * x.w;
+                }
+            }
+            d = wave_sum(d); a = wave_sum(a); b = wave_sum(b); kq = wave_sum(kq); f = wave_sum(f);
+            if (lane == 0) { red[wave][0] = d; red[wave][1] = a; red[wave][2] = b; red[wave][3] = kq; fsq[wave] = f; }
+        } else {
+            d = wave_sum(d); a = wave_sum(a); b = wave_sum(b); kq = wave_sum(kq);
+            if (lane == 0) { red[wave][0] = d; red[wave][1] = a; red[wave][2] = b; red[wave][3] = kq; }
+        }
     }
     __syncthreads();
     if (wave == 0) {
@@ -1128,8 +1160,19 @@ __global__ __launch_bounds__(256) void k_decode(const TIO *__restrict__ Qg, cons
         const int has_prev = head->has_prev;
         const float s_prev = head->s_prev;
         const int64_t t_seen = head->t_seen;
-        const float s = has_prev ? cosine_distance(d, a, b) : 1.0f;
-        const int bnd = (m == 0) || !((s < tau) && (s_prev < tau));
+        float s;
+        int bnd;
+        if (state_score) {
+            // I = sqrt(2 D (1 - c)) / (sqrt(D) + 1e-6), c = x / (|v| |k| |S|_F)
+            const double F = fsq[0] + fsq[1] + fsq[2] + fsq[3];
+            const double nn = a * b, Dd = static_cast<double>(DK) * DV;
+            if (m == 0 || nn == 0.0 || F <= 0.0) s = 2.0f;
+            else s = static_cast<float>(sqrt(fmax(0.0, 2.0 * Dd * (1.0 - d / sqrt(nn * F)))) / (sqrt(Dd) + 1e-6));
+            bnd = (m == 0) || (s >= tau);
+        } else {
+            s = has_prev ? cosine_distance(d, a, b) : 1.0f;
+            bnd = (m == 0) || !((s < tau) && (s_prev < tau));
+        }
         const int64_t qv = fixed_point(s);
         int64_t I = lane < m ? info[lane] : 0;
         int32_t n = lane < m ? count[lane] : 0;
@@ -1541,8 +1584,13 @@ static hipError_t prefill_schedule(const PrefillArgs &a, hipStream_t stream)
     const int NT = (T + kScoreTile - 1) / kScoreTile;
     const int NCH = (T + kChunk - 1) / kChunk;
     const TIO *K = static_cast<const TIO *>(a.k);
-    hipLaunchKernelGGL((k_score<TIO, DK>), dim3(NT, BH), dim3(256), 0, stream, K, T, a.tau, a.ws.s,
-                       a.ws.qs, a.ws.flag, a.ws.tile_cnt, a.ws.tile_sum, NT, a.meta, a.g.meta_stride);
+    if (a.score_rule == DLA_SCORE_STATE) {
+        hipError_t e = launch_state_score(a, stream);
+        if (e != hipSuccess) return e;
+    } else {
+        hipLaunchKernelGGL((k_score<TIO, DK>), dim3(NT, BH), dim3(256), 0, stream, K, T, a.tau, a.ws.s,
+                           a.ws.qs, a.ws.flag, a.ws.tile_cnt, a.ws.tile_sum, NT, a.meta, a.g.meta_stride);
+    }
     hipLaunchKernelGGL(k_compact, dim3(NT, BH), dim3(256), 0, stream, T, NT, a.ws.flag, a.ws.qs,
                        a.ws.tile_cnt, a.ws.tile_sum, a.ws.seg_t, a.ws.seg_P, a.ws.seg_q0, a.ws.nseg,
                        a.sched.seg_id);
@@ -1734,10 +1782,10 @@ static void decode_launch(const DecodeArgs &a, hipStream_t stream)
                            a.states, a.meta, a.g.meta_stride);
     else if (a.g.state_bf16)
         hipLaunchKernelGGL((k_decode<TIO, DK, DV, true>), dim3(BH), dim3(256), 0, stream, q, k, v, l, o, a.tau,
-                           a.g.C, a.states, a.active, a.meta, a.g.meta_stride, a.sched, a.merge_rule);
+                           a.g.C, a.states, a.active, a.meta, a.g.meta_stride, a.sched, a.merge_rule, a.score_rule);
     else
         hipLaunchKernelGGL((k_decode<TIO, DK, DV, false>), dim3(BH), dim3(256), 0, stream, q, k, v, l, o, a.tau,
-                           a.g.C, a.states, a.active, a.meta, a.g.meta_stride, a.sched, a.merge_rule);
+                           a.g.C, a.states, a.active, a.meta, a.g.meta_stride, a.sched, a.merge_rule, a.score_rule);
 }
 
 template <typename TIO, int DK>

@@ -1,0 +1,491 @@
+// dla_state_score.hip -- the state information score of the DLA prefill
+// (a cache whose score rule is DLA_SCORE_STATE).
+//
+// Reading notes "Dynamic Linear Attention | Chlience Paper Archive", section
+// 5.1: each token builds its per-token state v_t k_t^T and compares it with
+// the current (most recent) memory state S; both are RMS-normalised, and
+//     I_t = ||N(v_t k_t^T) - N(S)||_F / (||N(S)||_F + eps),   eps = 1e-6;
+// the token opens a new state when I_t >= tau (an empty cache always does).
+// With both matrices non-zero each normalised matrix has Frobenius norm
+// sqrt(D), D = d_k d_v, so
+//     I_t = sqrt(2 D (1 - c)) / (sqrt(D) + eps),
+//     c = <v_t k_t^T, S>_F / (|v_t| |k_t| |S|_F) = x / sqrt(nn F),
+// with x = v_t^T S k_t, nn = |v_t|^2 |k_t|^2 and F = |S|_F^2; a zero matrix or
+// an empty cache gives I_t = 2.
+//
+// The score depends on the current state, and which state is current depends
+// on the earlier boundaries and capacity merges (section 5.2): a token that
+// joins, or whose new state the capacity merge joins to the state before it,
+// extends the current state; any other boundary restarts it at the token.
+// The current state is therefore always a suffix [a, t) of the stream.  One
+// block per stream sweeps the 64-token chunks in order, with the part of the
+// current state that precedes the chunk, S_pre = sum over [a, c0) of v k^T,
+// held as fp32 MFMA accumulators:
+//   1. u_t = v_t^T S_pre k_t for the chunk's tokens: Y = S_pre K^T on MFMA,
+//      S_pre split into two fp16 halves (22 significant bits) and K exact in
+//      fp16 (bf16 inputs) or split as well (fp32 inputs), then u_t = v_t . Y_t;
+//   2. the chunk's Gram products H[t][s] = (v_t . v_s)(k_t . k_s) on MFMA and
+//      their row prefix sums in fp64, so that the part of x_t inside the chunk
+//      is one difference;
+//   3. one wave scans the tokens: x_t, the score, the boundary, and at a
+//      boundary over capacity the greedy merge decision (same rule and
+//      arithmetic as the greedy scan kernel) -- only to know whether the
+//      current state restarts; F is kept in fp64 (F' = F + 2 x + nn when the
+//      token joins);
+//   4. S_pre of the next chunk: the tokens of the chunk from the current
+//      state's start on are added (the accumulators are cleared first if the
+//      current state restarted inside the chunk).
+// The kernel writes what the cosine score kernel writes (scores, their 2^-32
+// fixed-point values, boundary flags, per-tile boundary counts and sums); the
+// boundary compaction and the greedy scan then build the schedule exactly as
+// for the cosine score.  It reads the cache (the states it holds when the
+// call starts) and writes nothing into it.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dla_device.h"
+#include "dla_internal.h"
+
+namespace dla {
+
+namespace {
+
+constexpr int kSsThreads = 256;
+constexpr int kPreEntries = kChunk * (kChunk + 1) / 2;   // packed lower triangle, diagonal included
+
+// Row-prefix index of (t, s), s <= t: entry = sum of H[t][s'] over s' < s.
+__device__ __forceinline__ int pre_idx(int t, int s) { return t * (t + 1) / 2 + s; }
+
+template <typename TIO, int DK, int DV>
+struct SsSmem {
+    static constexpr int PAD = 16 / sizeof(TIO);
+    TIO kr[kChunk][DK + PAD];       // K of the chunk, row-major
+    TIO vr[kChunk][DV + PAD];       // V of the chunk, row-major
+    TIO kt[DK][kChunk + PAD];       // K transposed
+    TIO vt[DV][kChunk + PAD];       // V transposed
+    union {
+        float H[kChunk][kChunk + 1];  // Gram products (lower triangle)
+        double pre[kPreEntries];      // their row prefix sums
+    };
+    float upart[4][kChunk];         // partial u_t of the four waves
+    float nn[kChunk];               // |v_t|^2 |k_t|^2
+    float s_c[kChunk];              // scores of the chunk
+    uint8_t f_c[kChunk];            // boundary flags of the chunk
+    float red[4], kred[4];
+    double dred[4];
+    int64_t a_s;                    // start of the current state after the chunk (from the scan)
+};
+
+// fp16 halves of x * 2^-e: hi = fp16(x'), lo = fp16(x' - hi).
+__device__ __forceinline__ void split16(float x, int e, _Float16 &hi, _Float16 &lo)
+{
+    const float y = ldexpf(x, -e);
+    hi = static_cast<_Float16>(y);
+    lo = static_cast<_Float16>(y - static_cast<float>(hi));
+}
+
+template <typename TIO, int DK, int DV>
+__global__ __launch_bounds__(kSsThreads, 1) void k_state_score(
+    const TIO *__restrict__ K, const TIO *__restrict__ V, int T, float tau, int C, int merge_rule,
+    const float *__restrict__ states, const float *__restrict__ active, int state_bf16,
+    const uint8_t *__restrict__ meta_base, size_t meta_stride,
+    float *__restrict__ s_out, int64_t *__restrict__ qs_out, uint8_t *__restrict__ flag_out,
+    int32_t *__restrict__ tile_cnt, int64_t *__restrict__ tile_sum, int NT)
+{
+    constexpr int NIT = DV / 16;                 // 16-row tiles of d_v
+    constexpr int NJT = DK / 16;                 // 16-column tiles of d_k
+    constexpr int IPW = NIT / 4;                 // d_v tiles per wave: wave + 4 ii
+    constexpr bool kF32 = sizeof(TIO) == 4;
+    static_assert(NIT % 4 == 0, "d_v tiles spread evenly over the waves");
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    typedef SsSmem<TIO, DK, DV> Smem;
+    Smem &S = *reinterpret_cast<Smem *>(smem_raw);
+
+    const int bh = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lr = lane & 15, lg = lane >> 4;
+    const int NCH = (T + kChunk - 1) / kChunk;
+    const size_t tok0 = static_cast<size_t>(bh) * T;
+    const double D = static_cast<double>(DK) * DV;
+    const double sqD = sqrt(D);
+
+    // the stream as the cache holds it: its states' information and counts
+    // (the greedy lanes) and its most recent state (the current one)
+    const uint8_t *meta = meta_base + static_cast<size_t>(bh) * meta_stride;
+    const MetaHead *head = reinterpret_cast<const MetaHead *>(meta);
+    const int m_init = head->m;
+    int64_t I = 0;
+    int32_t n = 0;
+    if (wave == 0 && lane < m_init) {
+        I = reinterpret_cast<const int64_t *>(meta + kOffInfo)[lane];
+        n = reinterpret_cast<const int32_t *>(meta + kOffCount)[lane];
+    }
+    int m = m_init;
+    // S_pre^T accumulators: tile (jt, it) holds S[16 it + lr][16 jt + 4 lg + r]
+    floatx4 acc[IPW][NJT];
+#pragma unroll
+    for (int ii = 0; ii < IPW; ++ii)
+#pragma unroll
+        for (int jt = 0; jt < NJT; ++jt) acc[ii][jt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    double F = 0.0;          // |S_cur|_F^2 (wave 0)
+    int64_t a = 0;           // start of the current state (absolute token of this call; < 0: before it)
+    if (m_init > 0) {
+        // (m_init is the same for the whole block)
+        const int slot = meta[kOffOrder + m_init - 1];
+        const float *src = state_bf16 ? active + static_cast<size_t>(bh) * DV * DK
+                                      : states + (static_cast<size_t>(bh) * C + slot) * DV * DK;
+        double sqd = 0.0;
+#pragma unroll
+        for (int ii = 0; ii < IPW; ++ii)
+#pragma unroll
+            for (int jt = 0; jt < NJT; ++jt) {
+                const int i = 16 * (wave + 4 * ii) + lr;
+                const float4 x = *reinterpret_cast<const float4 *>(src + static_cast<size_t>(i) * DK + 16 * jt + 4 * lg);
+                acc[ii][jt] = floatx4{x.x, x.y, x.z, x.w};
+                sqd += static_cast<double>(x.x) * x.x + static_cast<double>(x.y) * x.y +
+                       static_cast<double>(x.z) * x.z + static_cast<double>(x.w) * x.w;
+            }
+        sqd = wave_sum(sqd);
+        if (lane == 0) S.dred[wave] = sqd;
+        __syncthreads();
+        F = S.dred[0] + S.dred[1] + S.dred[2] + S.dred[3];
+        a = -1;
+    }
+    int32_t tcnt = 0;
+    int64_t tsum = 0;
+
+    for (int ch = 0; ch < NCH; ++ch) {
+        const int c0 = ch * kChunk;
+        const int nvalid = min(kChunk, T - c0);
+        __syncthreads();
+        // ---- 1. stage the chunk (zero rows past the stream's end)
+        constexpr int EPV = 16 / sizeof(TIO);
+        float kmax = 0.0f;
+        for (int idx = tid; idx < kChunk * DK / EPV; idx += kSsThreads) {
+            const int r = idx / (DK / EPV), cv = (idx % (DK / EPV)) * EPV;
+            uint4 x = make_uint4(0, 0, 0, 0);
+            if (r < nvalid) x = *reinterpret_cast<const uint4 *>(K + (tok0 + c0 + r) * DK + cv);
+            *reinterpret_cast<uint4 *>(&S.kr[r][cv]) = x;
+            const TIO *e = reinterpret_cast<const TIO *>(&x);
+#pragma unroll
+            for (int j = 0; j < EPV; ++j) {
+                S.kt[cv + j][r] = e[j];
+                kmax = fmaxf(kmax, fabsf(to_f(e[j])));
+            }
+        }
+        for (int idx = tid; idx < kChunk * DV / EPV; idx += kSsThreads) {
+            const int r = idx / (DV / EPV), cv = (idx % (DV / EPV)) * EPV;
+            uint4 x = make_uint4(0, 0, 0, 0);
+            if (r < nvalid) x = *reinterpret_cast<const uint4 *>(V + (tok0 + c0 + r) * DV + cv);
+            *reinterpret_cast<uint4 *>(&S.vr[r][cv]) = x;
+            const TIO *e = reinterpret_cast<const TIO *>(&x);
+#pragma unroll
+            for (int j = 0; j < EPV; ++j) S.vt[cv + j][r] = e[j];
+        }
+        // scale of S_pre's fp16 halves and of K's
+        float smax = 0.0f;
+#pragma unroll
+        for (int ii = 0; ii < IPW; ++ii)
+#pragma unroll
+            for (int jt = 0; jt < NJT; ++jt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) smax = fmaxf(smax, fabsf(acc[ii][jt][r]));
+        smax = wave_max(smax);
+        kmax = wave_max(kmax);
+        if (lane == 0) {
+            S.red[wave] = smax;
+            S.kred[wave] = kmax;
+        }
+        __syncthreads();
+        const int es = f16_exponent(fmaxf(fmaxf(S.red[0], S.red[1]), fmaxf(S.red[2], S.red[3])));
+        const int ek = f16_exponent(fmaxf(fmaxf(S.kred[0], S.kred[1]), fmaxf(S.kred[2], S.kred[3])));
+        const bool pre_live = a < c0;   // the current state began before this chunk
+
+        // ---- 2. u_t = v_t^T S_pre k_t (wave w: its d_v tiles, every token)
+        if (pre_live) {
+            floatx4 Y[IPW][4];
+#pragma unroll
+            for (int ii = 0; ii < IPW; ++ii)
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) Y[ii][tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int jp = 0; jp < NJT / 2; ++jp) {
+                // S rows 16 it + lr at columns {32 jp + 4 lg + r, 32 jp + 16 + 4 lg + r}
+                f16x8 sh[IPW], sl[IPW];
+#pragma unroll
+                for (int ii = 0; ii < IPW; ++ii)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        _Float16 h, l;
+                        split16(acc[ii][2 * jp][r], es, h, l);
+                        sh[ii][r] = h; sl[ii][r] = l;
+                        split16(acc[ii][2 * jp + 1][r], es, h, l);
+                        sh[ii][4 + r] = h; sl[ii][4 + r] = l;
+                    }
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) {
+                    // K of token 16 tt + lr at the same columns
+                    f16x8 kh, kl;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        _Float16 h, l;
+                        split16(to_f(S.kr[16 * tt + lr][32 * jp + 4 * lg + r]), ek, h, l);
+                        kh[r] = h; kl[r] = l;
+                        split16(to_f(S.kr[16 * tt + lr][32 * jp + 16 + 4 * lg + r]), ek, h, l);
+                        kh[4 + r] = h; kl[4 + r] = l;
+                    }
+#pragma unroll
+                    for (int ii = 0; ii < IPW; ++ii) {
+                        Y[ii][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(sh[ii], kh, Y[ii][tt], 0, 0, 0);
+                        Y[ii][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(sl[ii], kh, Y[ii][tt], 0, 0, 0);
+                        if constexpr (kF32)
+                            Y[ii][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(sh[ii], kl, Y[ii][tt], 0, 0, 0);
+                    }
+                    (void)kl;
+                }
+            }
+            // Y[ii][tt] holds (S K^T) at rows 16 it + 4 lg + r, token 16 tt + lr
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+                float x = 0.0f;
+#pragma unroll
+                for (int ii = 0; ii < IPW; ++ii)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        x += to_f(S.vr[16 * tt + lr][16 * (wave + 4 * ii) + 4 * lg + r]) * Y[ii][tt][r];
+                x += __shfl_xor(x, 16);
+                x += __shfl_xor(x, 32);
+                if (lg == 0) S.upart[wave][16 * tt + lr] = ldexpf(x, es + ek);
+            }
+        } else {
+            S.upart[wave][lane] = 0.0f;
+        }
+        // ---- 3. Gram products H = (V V^T) o (K K^T), lower-triangle tiles
+        for (int tile = wave; tile < 10; tile += 4) {
+            int tt = 0, st = tile;
+            while (st > tt) { st -= tt + 1; ++tt; }   // tile -> (tt, st), st <= tt
+            floatx4 gk = floatx4{0.f, 0.f, 0.f, 0.f}, gv = gk;
+#pragma unroll
+            for (int ks = 0; ks < DK / 32; ++ks) {
+                Frag<TIO> x, y;
+                load_frag(x, &S.kr[16 * tt + lr][32 * ks + 8 * lg]);
+                load_frag(y, &S.kr[16 * st + lr][32 * ks + 8 * lg]);
+                mma32(gk, x, y);
+            }
+#pragma unroll
+            for (int ks = 0; ks < DV / 32; ++ks) {
+                Frag<TIO> x, y;
+                load_frag(x, &S.vr[16 * tt + lr][32 * ks + 8 * lg]);
+                load_frag(y, &S.vr[16 * st + lr][32 * ks + 8 * lg]);
+                mma32(gv, x, y);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) S.H[16 * tt + 4 * lg + r][16 * st + lr] = gk[r] * gv[r];
+        }
+        __syncthreads();
+        // ---- row prefix sums of H in fp64 (wave 0: lane t owns row t); the
+        // whole row is read before any lane writes the prefix array, which
+        // shares the bytes
+        if (wave == 0) {
+            float row[kChunk];
+#pragma unroll
+            for (int s = 0; s < kChunk; ++s) row[s] = s <= lane ? S.H[lane][s] : 0.0f;
+            const float diag = row[lane];
+            __builtin_amdgcn_wave_barrier();
+            double run = 0.0;
+#pragma unroll
+            for (int s = 0; s < kChunk; ++s)
+                if (s <= lane) {
+                    S.pre[pre_idx(lane, s)] = run;
+                    run += static_cast<double>(row[s]);
+                }
+            S.nn[lane] = diag;
+        }
+        __syncthreads();
+        // ---- 4. the scan (wave 0)
+        if (wave == 0) {
+            for (int t = 0; t < nvalid; ++t) {
+                const int64_t tok = c0 + t;
+                const double nn = S.nn[t];
+                float sc;
+                bool bnd;
+                double x = 0.0;
+                if (m == 0) {
+                    sc = 2.0f;
+                    bnd = true;
+                } else {
+                    const int lo = a > c0 ? static_cast<int>(a - c0) : 0;
+                    x = S.pre[pre_idx(t, t)] - S.pre[pre_idx(t, lo)];
+                    if (a < c0)
+                        x += static_cast<double>(S.upart[0][t]) + S.upart[1][t] + S.upart[2][t] + S.upart[3][t];
+                    if (nn == 0.0 || F <= 0.0) {
+                        sc = 2.0f;
+                    } else {
+                        const double c = x / sqrt(nn * F);
+                        sc = static_cast<float>(sqrt(fmax(0.0, 2.0 * D * (1.0 - c))) / (sqD + 1e-6));
+                    }
+                    bnd = sc >= tau;
+                }
+                const int64_t qv = fixed_point(sc);
+                bool extend = !bnd;             // the token extends the current state
+                if (bnd) {
+                    if (m < C) {
+                        if (lane == m) { I = qv; n = 1; }
+                        ++m;
+                    } else {
+                        // the greedy merge of the state set (as the greedy scan
+                        // kernel decides it): only whether it joins the newest
+                        // pair matters here
+                        const int64_t I_nx = lane_down1(I);
+                        const int32_t n_nx = lane_down1(n);
+                        const bool inside = lane + 1 < m;
+                        const int64_t pI = inside ? I_nx : qv;
+                        const int32_t pn = inside ? n_nx : 1;
+                        int istar;
+                        if (merge_rule == DLA_MERGE_DENSITY) {
+                            istar = wave_argmin_frac(I + pI, static_cast<int64_t>(n) + pn, lane < m);
+                        } else {
+                            const int64_t key = lane < m ? I + pI : INT64_MAX;
+                            const int64_t kmin = wave_min_i64(key);
+                            istar = __ffsll(static_cast<unsigned long long>(__ballot(key == kmin))) - 1;
+                        }
+                        if (lane == istar) { I += pI; n += pn; }
+                        else if (lane > istar && lane < m) { I = pI; n = pn; }
+                        extend = istar == m - 1;
+                    }
+                } else {
+                    if (lane == m - 1) { I += qv; n += 1; }
+                }
+                if (extend) {
+                    F += 2.0 * x + nn;
+                } else {
+                    F = nn;
+                    a = tok;
+                }
+                if (lane == 0) {
+                    S.s_c[t] = sc;
+                    S.f_c[t] = static_cast<uint8_t>(bnd);
+                }
+                tcnt += bnd ? 1 : 0;
+                tsum += qv;
+            }
+            if (lane == 0) S.a_s = a;
+            // per-tile boundary count and information sum for the compaction
+            const int tile = c0 / kScoreTile;
+            const bool tile_end = (c0 + nvalid) % kScoreTile == 0 || ch == NCH - 1;
+            if (tile_end) {
+                if (lane == 0) {
+                    tile_cnt[static_cast<size_t>(bh) * NT + tile] = tcnt;
+                    tile_sum[static_cast<size_t>(bh) * NT + tile] = tsum;
+                }
+                tcnt = 0;
+                tsum = 0;
+            }
+        }
+        __syncthreads();
+        a = S.a_s;
+        // chunk outputs
+        if (tid < nvalid) {
+            const float sc = S.s_c[tid];
+            s_out[tok0 + c0 + tid] = sc;
+            qs_out[tok0 + c0 + tid] = fixed_point(sc);
+            flag_out[tok0 + c0 + tid] = S.f_c[tid];
+        }
+        // ---- 5. S_pre of the next chunk: the current state's tokens of this
+        // chunk added, after clearing when the state began inside it
+        if (ch + 1 < NCH) {
+            const int lo = a > c0 ? static_cast<int>(a - c0) : 0;
+            if (a >= c0) {
+#pragma unroll
+                for (int ii = 0; ii < IPW; ++ii)
+#pragma unroll
+                    for (int jt = 0; jt < NJT; ++jt) acc[ii][jt] = floatx4{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+            for (int ks = 0; ks < kChunk / 32; ++ks) {
+                if (32 * ks + 32 <= lo) continue;
+#pragma unroll
+                for (int jt = 0; jt < NJT; ++jt) {
+                    Frag<TIO> x;
+                    load_frag(x, &S.kt[16 * jt + lr][32 * ks + 8 * lg]);
+                    mask_frag(x, 32 * ks + 8 * lg, lo, kChunk);
+#pragma unroll
+                    for (int ii = 0; ii < IPW; ++ii) {
+                        Frag<TIO> y;
+                        load_frag(y, &S.vt[16 * (wave + 4 * ii) + lr][32 * ks + 8 * lg]);
+                        mma32(acc[ii][jt], x, y);
+                    }
+                }
+            }
+        }
+    }
+}
+
+}  // namespace
+
+template <typename TIO, int DK, int DV>
+static hipError_t ss_launch(const PrefillArgs &a, hipStream_t stream)
+{
+    const int BH = a.g.B * a.g.H, T = a.T;
+    const int NT = (T + kScoreTile - 1) / kScoreTile;
+    const size_t smem = sizeof(SsSmem<TIO, DK, DV>);
+    static bool attr_set = false;   // idempotent; a race only repeats the same call
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_state_score<TIO, DK, DV>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    hipLaunchKernelGGL((k_state_score<TIO, DK, DV>), dim3(BH), dim3(kSsThreads), smem, stream,
+                       static_cast<const TIO *>(a.k), static_cast<const TIO *>(a.v), T, a.tau, a.g.C, a.merge_rule,
+                       a.states, a.active, a.g.state_bf16, a.meta, a.g.meta_stride, a.ws.s, a.ws.qs, a.ws.flag,
+                       a.ws.tile_cnt, a.ws.tile_sum, NT);
+    return hipGetLastError();
+}
+
+template <typename TIO, int DK>
+static hipError_t ss_dv(const PrefillArgs &a, hipStream_t stream)
+{
+    switch (a.g.dv) {
+    case 64: return ss_launch<TIO, DK, 64>(a, stream);
+    case 128: return ss_launch<TIO, DK, 128>(a, stream);
+    case 256:
+        // (d_k = d_v = 256: the current state alone would take every register of the block)
+        if constexpr (DK < 256 && sizeof(SsSmem<TIO, DK, 256>) <= 160 * 1024) return ss_launch<TIO, DK, 256>(a, stream);
+        return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_state_score(const PrefillArgs &a, hipStream_t stream)
+{
+    if (a.io_bf16) {
+        switch (a.g.dk) {
+        case 64: return ss_dv<__bf16, 64>(a, stream);
+        case 128: return ss_dv<__bf16, 128>(a, stream);
+        case 256: return ss_dv<__bf16, 256>(a, stream);
+        default: return hipErrorInvalidValue;
+        }
+    }
+    switch (a.g.dk) {
+    case 64: return ss_dv<float, 64>(a, stream);
+    case 128: return ss_dv<float, 128>(a, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+size_t state_score_smem_bytes(int io_bf16, int dk, int dv)
+{
+    auto pick = [&](auto tio) -> size_t {
+        typedef decltype(tio) TIO;
+        if (dk == 64) return dv == 64 ? sizeof(SsSmem<TIO, 64, 64>) : dv == 128 ? sizeof(SsSmem<TIO, 64, 128>)
+                                                                                 : sizeof(SsSmem<TIO, 64, 256>);
+        if (dk == 128) return dv == 64 ? sizeof(SsSmem<TIO, 128, 64>) : dv == 128 ? sizeof(SsSmem<TIO, 128, 128>)
+                                                                                   : sizeof(SsSmem<TIO, 128, 256>);
+        return dv == 64 ? sizeof(SsSmem<TIO, 256, 64>) : dv == 128 ? sizeof(SsSmem<TIO, 256, 128>)
+                                                                    : sizeof(SsSmem<TIO, 256, 256>);
+    };
+    return io_bf16 ? pick(__bf16{}) : pick(float{});
+}
+
+}  // namespace dla

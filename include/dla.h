@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define DLA_ABI_VERSION 6
+#define DLA_ABI_VERSION 7
 #define DLA_MAX_C 64        /* largest supported cache capacity */
 #define DLA_CHUNK 64        /* tokens per prefill chunk */
 /* bytes of the static per-device scratch of dla_prefill_noalloc (64 MiB) */
@@ -101,6 +101,12 @@ typedef enum dla_merge_rule {
     DLA_MERGE_DENSITY = 1,   /* lowest information density (I_i + I_{i+1}) / (n_i + n_{i+1}) */
     DLA_FENWICK = 2          /* the Log-Linear fixed schedule (dla_prefill), no information rule */
 } dla_merge_rule;
+
+/* How a token's information is scored, and so where boundaries fall. */
+typedef enum dla_score_rule {
+    DLA_SCORE_COSINE = 0,    /* s_t = 1 - cos(k_t, k_{t-1}); a state opens unless s_t and s_{t-1} are both below tau (the default) */
+    DLA_SCORE_STATE = 1      /* the state information score I_t (reading notes, section 5.1); a state opens when I_t >= tau */
+} dla_score_rule;
 
 /*
  * Cache: caller-owned device memory holding, for every stream (b, h), up to
@@ -134,7 +140,7 @@ typedef struct dla_cache {
     int32_t B, H, C, d_k, d_v;
     int32_t merge_rule;   /* a dla_merge_rule; dla_cache_init sets DLA_MERGE_SUM */
     int32_t state_dtype;  /* DLA_F32 or DLA_BF16 (set by dla_cache_init) */
-    int32_t reserved;
+    int32_t score_rule;   /* a dla_score_rule; dla_cache_init sets DLA_SCORE_COSINE */
     void *base;           /* device pointer */
     uint64_t bytes;
 } dla_cache;
@@ -233,6 +239,25 @@ dla_status dla_cache_init(dla_cache *cache, void *base, uint64_t bytes, int32_t 
  * then unchanged).
  */
 dla_status dla_cache_set_merge_rule(dla_cache *cache, int32_t rule);
+
+/*
+ * Score rule of the cache's streams from the next prefill or decode call on.
+ * DLA_SCORE_COSINE (the default) is the cosine score of consecutive keys with
+ * the two-low-tokens boundary rule (top of this header).  DLA_SCORE_STATE is
+ * the State Information Score of the reading notes, section 5.1: the
+ * per-token state v_t k_t^T is compared with the current (most recent) state
+ * S of the cache, both divided by their root mean square (RMSNorm with unit
+ * gain), I_t = ||N(v_t k_t^T) - N(S)||_F / (||N(S)||_F + 1e-6), rounded to
+ * float, and token t opens a new state when I_t >= tau (b_t = [I_t >= tau],
+ * same section); I_t = 2 without a current state or for a zero matrix.  The
+ * information sums and capacity merges are those of the merge rule, with I_t
+ * in place of s_t.  Supported with DLA_SCORE_STATE: d_k and d_v in
+ * {64, 128, 256}, not both 256, with bfloat16 io, d_k and d_v in {64, 128}
+ * with float32 io (prefill and decode return DLA_ERR_UNSUPPORTED otherwise).  The fixed
+ * schedule computes no score and ignores the rule.  Host only: it sets
+ * cache->score_rule; DLA_ERR_ARG for a NULL cache or an unknown rule.
+ */
+dla_status dla_cache_set_score_rule(dla_cache *cache, int32_t rule);
 
 /* Workspace bytes dla_prefill needs for this shape (the schedule of section
  * 5.1-5.2 and the chunk operands of the section 5.3 read); 0 if the shape is

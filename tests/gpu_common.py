@@ -36,7 +36,8 @@ def oracle_threads() -> int:
     return min(os.cpu_count() or 1, 16)
 
 
-def gpu_prefill(q, k, v, lam, C, tau, io, B=None, H=None, repeats=1, merge_rule="sum", state_dtype="f32"):
+def gpu_prefill(q, k, v, lam, C, tau, io, B=None, H=None, repeats=1, merge_rule="sum", state_dtype="f32",
+                score_rule="cosine"):
     """q,k [S,T,dk] ... float32 numpy (already bf16-valued for bf16).  Returns
     o (float32 numpy [S,T,dv]), schedule dict, final cache dict."""
     torch = torch_mod()
@@ -60,7 +61,8 @@ def gpu_prefill(q, k, v, lam, C, tau, io, B=None, H=None, repeats=1, merge_rule=
                  ev_t=torch.empty(BH, T, dtype=torch.int32, device=dev),
                  ev_i=torch.empty(BH, T, dtype=torch.int32, device=dev),
                  n_ev=torch.empty(BH, dtype=torch.int32, device=dev))
-    cache = dla.Cache(B, H, C, dk, dv, device=dev, merge_rule=merge_rule, state_dtype=state_dtype)
+    cache = dla.Cache(B, H, C, dk, dv, device=dev, merge_rule=merge_rule, state_dtype=state_dtype,
+                      score_rule=score_rule)
     ws = dla.prefill_workspace(B, H, T, C, dk, dv, dev)
     outs = []
     for rep in range(repeats):
@@ -76,7 +78,7 @@ def gpu_prefill(q, k, v, lam, C, tau, io, B=None, H=None, repeats=1, merge_rule=
     return outs, sc, fin
 
 
-def gpu_prefill_pieces(q, k, v, lam, C, tau, io, ends, merge_rule="sum", state_dtype="f32"):
+def gpu_prefill_pieces(q, k, v, lam, C, tau, io, ends, merge_rule="sum", state_dtype="f32", score_rule="cosine"):
     """Prefill the tokens [0, ends[0]), [ends[0], ends[1]), ... of every
     stream with one dla_prefill call each, on one cache.  Returns the outputs
     (float32 [S,T,dv]), per-piece schedule dicts and the final cache dict."""
@@ -86,7 +88,8 @@ def gpu_prefill_pieces(q, k, v, lam, C, tau, io, ends, merge_rule="sum", state_d
     dv = v.shape[2]
     dt = torch.bfloat16 if io == "bf16" else torch.float32
     dev = torch.device("cuda:0")
-    cache = dla.Cache(1, S, C, dk, dv, device=dev, merge_rule=merge_rule, state_dtype=state_dtype)
+    cache = dla.Cache(1, S, C, dk, dv, device=dev, merge_rule=merge_rule, state_dtype=state_dtype,
+                      score_rule=score_rule)
     outs, scheds, lo = [], [], 0
     for hi in ends:
         n = hi - lo
@@ -108,12 +111,19 @@ def gpu_prefill_pieces(q, k, v, lam, C, tau, io, ends, merge_rule="sum", state_d
     return np.concatenate(outs, 1), scheds, cache.read()
 
 
-def compare_schedule(r, sc, fin, label=""):
-    """Bit-exact comparison of a GPU prefill schedule and final metadata with the oracle."""
+def compare_schedule(r, sc, fin, label="", s_tol=None):
+    """Bit-exact comparison of a GPU prefill schedule and final metadata with
+    the oracle.  With s_tol the token scores may differ by that much (the
+    state score: the GPU reads the states in a different precision and order),
+    the rest of the schedule stays exact."""
     S = r["s"].shape[0]
-    bad_s = np.flatnonzero(r["s"].view(np.uint32) != sc["s"].view(np.uint32))
-    assert len(bad_s) == 0, (f"{label}: {len(bad_s)} token scores differ, first at "
-                            f"{np.unravel_index(bad_s[0], r['s'].shape)}")
+    if s_tol is None:
+        bad_s = np.flatnonzero(r["s"].view(np.uint32) != sc["s"].view(np.uint32))
+        assert len(bad_s) == 0, (f"{label}: {len(bad_s)} token scores differ, first at "
+                                f"{np.unravel_index(bad_s[0], r['s'].shape)}")
+    else:
+        ds = np.abs(r["s"].astype(np.float64) - sc["s"])
+        assert ds.max() <= s_tol, f"{label}: token scores differ by up to {ds.max():.3e} > {s_tol}"
     assert np.array_equal(r["b"], sc["boundary"]), f"{label}: boundaries differ"
     assert np.array_equal(r["seg"], sc["seg_id"]), f"{label}: segment ids differ"
     assert np.array_equal(r["m_t"], sc["m_t"]), f"{label}: state counts differ"
@@ -125,12 +135,20 @@ def compare_schedule(r, sc, fin, label=""):
     assert np.array_equal(r["fin_m"], fin["m"]), f"{label}: final m differs"
     for i in range(S):
         m = int(r["fin_m"][i])
-        assert np.array_equal(r["fin_I"][i, :m], fin["info"][i, :m]), f"{label}: info differs ({i})"
+        if s_tol is None:
+            assert np.array_equal(r["fin_I"][i, :m], fin["info"][i, :m]), f"{label}: info differs ({i})"
+        else:
+            # sums of scores that may each differ by s_tol (units of 2^-32)
+            bound = (np.asarray(r["fin_n"][i, :m], np.float64) * s_tol + 1e-9) * 2.0 ** 32
+            assert np.all(np.abs(r["fin_I"][i, :m] - fin["info"][i, :m]) <= bound), f"{label}: info differs ({i})"
         assert np.array_equal(r["fin_n"][i, :m], fin["count"][i, :m]), f"{label}: counts differ ({i})"
         assert np.array_equal(r["fin_start"][i, :m], fin["start"][i, :m]), f"{label}: starts differ ({i})"
         assert sorted(fin["order"][i, :m].tolist()) == sorted(set(fin["order"][i, :m].tolist())), \
             f"{label}: physical slots repeat ({i})"
-    assert np.array_equal(r["fin_s_prev"], fin["s_prev"]), f"{label}: s_prev differs"
+    if s_tol is None:
+        assert np.array_equal(r["fin_s_prev"], fin["s_prev"]), f"{label}: s_prev differs"
+    else:
+        assert np.abs(r["fin_s_prev"] - fin["s_prev"]).max() <= s_tol, f"{label}: s_prev differs"
     assert np.array_equal(r["fin_k_prev"], fin["k_prev"]), f"{label}: k_prev differs"
     assert np.array_equal(r["fin_t_seen"], fin["t_seen"]), f"{label}: t_seen differs"
 

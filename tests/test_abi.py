@@ -23,7 +23,7 @@ def test_library_exports_every_declared_symbol():
     assert {"dla_prefill", "dla_decode_step", "dla_cache_init"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert dla.dla_abi_version() == 6
+    assert dla.dla_abi_version() == 7
 
 
 def test_sizes_and_layout():
@@ -162,6 +162,7 @@ def test_merge_rule_is_validated_on_the_host():
     p = 0x100000
     # the view's layout: the rule sits where the header puts it
     assert C.sizeof(dla.dla_cache) == 48 and dla.dla_cache.merge_rule.offset == 20
+    assert dla.dla_cache.score_rule.offset == 28
     assert dla.dla_cache.state_dtype.offset == 24 and dla.dla_cache.base.offset == 32
     c = _cache()
     assert c.merge_rule == dla.DLA_MERGE_SUM
@@ -216,3 +217,34 @@ def test_gpu_package_never_imports_the_oracle():
             if f.endswith((".py", ".hip", ".cpp", ".h")):
                 txt = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in txt.lower(), f
+
+
+def test_score_rule_is_validated_on_the_host():
+    p = 0x100000
+    c = _cache(dk=128, dv=128)
+    assert c.score_rule == dla.DLA_SCORE_COSINE
+    assert dla.load().dla_cache_set_score_rule(C.byref(c), 2) == dla.DLA_ERR_ARG
+    assert "score rule" in dla.dla_last_error() and c.score_rule == dla.DLA_SCORE_COSINE
+    assert dla.load().dla_cache_set_score_rule(None, 1) == dla.DLA_ERR_ARG
+    dla.dla_cache_set_score_rule(c, dla.DLA_SCORE_STATE)
+    assert c.score_rule == dla.DLA_SCORE_STATE
+
+    def pre(cache, io=dla.DLA_BF16, T=100):
+        ws = dla.dla_prefill_workspace_bytes(cache.B, cache.H, T, cache.C, cache.d_k, cache.d_v)
+        return dla.dla_prefill(p, p, p, p, p, T, 0.6, io, cache, p, ws, None, None)
+
+    def dec(cache, io=dla.DLA_BF16):
+        return dla.dla_decode_step(p, p, p, p, p, 0.6, io, cache, None, None)
+
+    # shapes the state score does not take, refused before any launch
+    for dk, dv, io in [(128, 96, dla.DLA_BF16), (256, 256, dla.DLA_BF16), (128, 256, dla.DLA_F32),
+                       (256, 64, dla.DLA_F32)]:
+        cc = _cache(dk=dk, dv=dv)
+        dla.dla_cache_set_score_rule(cc, dla.DLA_SCORE_STATE)
+        assert pre(cc, io) == dla.DLA_ERR_UNSUPPORTED, (dk, dv, io)
+        if dv in (64, 128, 256):
+            assert dec(cc, io) == dla.DLA_ERR_UNSUPPORTED, (dk, dv, io)
+    # a cache view with an unknown rule written into it
+    c.score_rule = 5
+    assert pre(c) == dla.DLA_ERR_ARG and "score rule" in dla.dla_last_error()
+    assert dec(c) == dla.DLA_ERR_ARG

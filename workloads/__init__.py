@@ -12,7 +12,10 @@ Workload recipe (one stream = one (batch, head) pair):
   * noise, "relative" reading (default): 0.2 * N(0, I / d_k), i.e. a noise
     vector of norm about 0.2 around a unit centroid;
     noise, "literal" reading: 0.2 * N(0, I) per coordinate (norm 0.2*sqrt(d_k));
-  * q ~ N(0, I / d_k), v ~ N(0, I / d_v);
+  * q ~ N(0, I / d_k), v ~ N(0, I / d_v); with values="regime" the values
+    follow the key segments instead: a unit N(0, I) centroid per segment
+    plus 0.2 * N(0, I / d_v) noise (a workload on which a score of the
+    states, not only of the keys, sees the segments);
   * lambda = sigmoid(N(0, 1)), one value per (token, cache slot);
   * bf16 workloads round every fp32 draw once to bf16 (round to nearest even)
     and hand back the rounded values as float32 arrays.
@@ -123,11 +126,19 @@ def _sigmoid(x):
     return (1.0 / (1.0 + np.exp(-x.astype(np.float64)))).astype(np.float32)
 
 
-def _stream(seed_seq, T, dk, dv, C, means, reading, io):
+def _stream(seed_seq, T, dk, dv, C, means, reading, io, values="random"):
     rng = np.random.default_rng(seed_seq)
     k, lens = _keys(rng, T, dk, means, reading)
     q = rng.standard_normal((T, dk), dtype=np.float32) * np.float32(1.0 / np.sqrt(dk))
-    v = rng.standard_normal((T, dv), dtype=np.float32) * np.float32(1.0 / np.sqrt(dv))
+    if values == "regime":
+        vc = rng.standard_normal((len(lens), dv), dtype=np.float32)
+        vc /= np.linalg.norm(vc, axis=1, keepdims=True)
+        v = (np.repeat(vc, lens, axis=0) +
+             rng.standard_normal((T, dv), dtype=np.float32) * np.float32(0.2 / np.sqrt(dv))).astype(np.float32)
+    elif values == "random":
+        v = rng.standard_normal((T, dv), dtype=np.float32) * np.float32(1.0 / np.sqrt(dv))
+    else:
+        raise ValueError(f"unknown values {values!r}")
     lam = _sigmoid(rng.standard_normal((T, C), dtype=np.float32))
     if io == "bf16":
         q, k, v, lam = (round_bf16(a) for a in (q, k, v, lam))
@@ -139,7 +150,7 @@ def _workers(n):
 
 
 def prefill_inputs(cfg: Config | str, reading: str = "relative", streams=None,
-                   T: int | None = None, seed: int | None = None) -> dict:
+                   T: int | None = None, seed: int | None = None, values: str = "random") -> dict:
     """Inputs of one prefill workload.
 
     Returns float32 arrays q,k [S,T,dk], v [S,T,dv], lam [S,T,C] where S is the
@@ -164,13 +175,13 @@ def prefill_inputs(cfg: Config | str, reading: str = "relative", streams=None,
 
     def one(j):
         qq, kk, vv, ll, ln = _stream(children[idx[j]], T, cfg.dk, cfg.dv, cfg.C,
-                                     cfg.seg_means, reading, cfg.io)
+                                     cfg.seg_means, reading, cfg.io, values)
         q[j], k[j], v[j], lam[j], lens[j] = qq, kk, vv, ll, ln
 
     with _cf.ThreadPoolExecutor(_workers(S)) as ex:
         list(ex.map(one, range(S)))
     return dict(q=q, k=k, v=v, lam=lam, seg_lens=lens, streams=idx, T=T, cfg=cfg,
-                reading=reading)
+                reading=reading, values=values)
 
 
 def decode_inputs(cfg: Config | str = "decode_b256_bf16", reading: str = "relative",

@@ -8,19 +8,36 @@ greedy capacity merges, chunked MFMA read/update).  Inputs are synthetic
 (seeded piecewise-regime keys) and resident in HBM before timing starts.
 
 Also reported on the same line:
-  roofline      the chunk kernel's algorithmic flops (sum over token-heads of
-                2 (m_t + 1) d_k d_v, m_t from the run's own schedule) per
-                launch over its HIP-event-timed duration, against the dense
-                bf16 MFMA peak;
+  roofline      the algorithmic flops of the prefill (sum over token-heads of
+                2 (m_t + 1) d_k d_v, m_t from the run's own schedule) over the
+                whole prefill's HIP-event time (every kernel of the call, from
+                the score to the sweep), against the dense bf16 MFMA peak;
+                kernel_* fields give the same for the chunk kernel (the
+                sweep) alone, and mfma_ops_ratio / mfma_busy_frac its MFMA
+                counters (issued MFMA flops over the algorithmic flops, share
+                of SIMD cycles the matrix cores were busy), from the counter
+                summary committed under profiles/;
   decode        batched decode (B=256, H=16, d=128, C=32 full fp32 caches):
                 steps/s over a loop of dla_decode_step calls and the decode
                 kernel's algorithmic HBM bytes per launch over its duration,
-                against the HBM peak;
-  cpu_baseline  the CPU oracle on a bounded sample of the prefill workload;
+                against the HBM peak; inputs from the tested recipe
+                (workloads.decode_inputs), distinct caches tiled over the
+                streams;
+  cpu_baseline  the CPU oracle on a bounded sample of the prefill workload, on
+                the CPU threads the process is granted;
   prefill_density_merge_rule
                 the same prefill with the capacity merges choosing the pair
                 of lowest information density instead of smallest summed
                 information (--no-density skips it);
+  prefill_streamed_kernel
+                the same prefill on the streamed chunk kernel (the kernel of
+                fp32 io and C > 32; --no-streamed skips it);
+  prefill_workloads
+                the other prefill workloads in their full launch
+                configurations: Mamba-2-780M-shaped, long context (T=131072),
+                Mamba-2-shaped with C=64, tiny fp32, and the state information
+                score on the Mamba-2-shaped layer with values that follow the
+                key segments (--no-other skips them);
   decode_bf16_states
                 the same decode on caches storing closed states as bf16 (the
                 most recent one stays fp32), with its algorithmic bytes
@@ -60,10 +77,11 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
-import math
 import os
 import sys
 import time
+
+import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
@@ -101,6 +119,31 @@ def measured_traffic(summary: str, kernel: str):
         return None
 
 
+def measured_mfma(summary: str, kernel: str):
+    """MFMA counters of `kernel` from a committed counter summary: the MFMA
+    flops it issues per launch and the share of SIMD cycles its matrix cores
+    were busy; None when the summary is absent, names another kernel, or was
+    taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", summary)
+    try:
+        kv = {}
+        for line in open(path):
+            if ":" in line and not line.startswith("#"):
+                key, val = line.split(":", 1)
+                kv[key.strip()] = val.strip()
+        if kv.get("kernel") != kernel:
+            return None
+        h = hashlib.sha256()
+        for f in kv["sources"].split():
+            h.update(open(os.path.join(ROOT, f), "rb").read())
+        if h.hexdigest() != kv["sources_sha256"]:
+            return None
+        return dict(mfma_flop_per_launch=float(kv["mfma_flop_per_launch"]),
+                    mfma_busy_frac=float(kv["mfma_busy_frac"]))
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def copy_probe(torch, mib):
     """A plain device-to-device copy of mib MiB, three times: the counter
     passes scale FETCH_SIZE and WRITE_SIZE by what they read for it."""
@@ -117,6 +160,90 @@ def copy_probe(torch, mib):
     torch.cuda.empty_cache()
 
 
+def upload(torch, d, cfg, dev, T=None):
+    """q, k, v, lam of a workload draw as device tensors [B, H, T, d] in the io dtype."""
+    T = cfg.T if T is None else T
+    dt = torch.bfloat16 if cfg.io == "bf16" else torch.float32
+
+    def up(a, dd):
+        return torch.from_numpy(a).to(dev).to(dt).view(cfg.B, cfg.H, T, dd)
+
+    return up(d["q"], cfg.dk), up(d["k"], cfg.dk), up(d["v"], cfg.dv), up(d["lam"], cfg.C)
+
+
+def prefill_leg(args, torch, dla, cfg, x, steps=None, rule="sum", score_rule="cosine", tau=None, path=None):
+    """One prefill workload timed: an untimed call exporting the schedule (its
+    m_t gives the algorithmic flops), the warmup, then `steps` timed calls.
+    Each timed step resets the cache (a prefill continues what the cache
+    holds) and runs dla_prefill; HIP events on the call's stream bracket the
+    whole prefill (every kernel from the score to the sweep, not the reset),
+    and the library's hook brackets the chunk kernel (the sweep)."""
+    steps = args.steps if steps is None else steps
+    tau = cfg.tau if tau is None else tau
+    B, H, T, dk, dv, C = cfg.B, cfg.H, x[0].shape[2], cfg.dk, cfg.dv, cfg.C
+    BH = B * H
+    dev = x[0].device
+    q, k, v, lam = x
+    if path is not None:
+        dla.dla_set_prefill_path(path, 0)
+    try:
+        cache = dla.Cache(B, H, C, dk, dv, device=dev, merge_rule=rule, score_rule=score_rule)
+        ws = dla.prefill_workspace(B, H, T, C, dk, dv, dev)
+        o = torch.empty(B, H, T, dv, dtype=q.dtype, device=dev)
+        m_t = torch.empty(BH, T, dtype=torch.int32, device=dev)
+        bnd = torch.empty(BH, T, dtype=torch.uint8, device=dev)
+        n_ev = torch.empty(BH, dtype=torch.int32, device=dev)
+        dla.prefill(q, k, v, lam, tau, cache, o=o, workspace=ws, sched=dict(m_t=m_t, boundary=bnd, n_ev=n_ev))
+        torch.cuda.synchronize()
+        m_sum = int(m_t.sum(dtype=torch.int64).item())
+        flops = 2.0 * (m_sum + BH * T) * dk * dv
+        stats = dict(mean_live_states=m_sum / (BH * T),
+                     boundaries_per_stream=float(bnd.sum(dtype=torch.int64).item()) / BH,
+                     merges_per_stream=float(n_ev.sum(dtype=torch.int64).item()) / BH)
+        del m_t, bnd, n_ev
+        for _ in range(args.warmup):
+            cache.reset()
+            dla.prefill(q, k, v, lam, tau, cache, o=o, workspace=ws)
+        ev = lambda: torch.cuda.Event(enable_timing=True)
+        whole = [(ev(), ev()) for _ in range(steps)]
+        sweep = [(ev(), ev()) for _ in range(steps)]
+        for pair in whole + sweep:          # materialise the event handles
+            pair[0].record()
+            pair[1].record()
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
+        for (a, b), (c, e) in zip(whole, sweep):
+            cache.reset()
+            dla.dla_set_prefill_events(c.cuda_event, e.cuda_event)
+            a.record()
+            dla.prefill(q, k, v, lam, tau, cache, o=o, workspace=ws)
+            b.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - w0
+        dla.dla_set_prefill_events(None, None)
+        kernel = dla.dla_prefill_kernel(dla.DLA_BF16 if q.dtype == torch.bfloat16 else dla.DLA_F32, B, H, C, dk, dv)
+    finally:
+        if path is not None:
+            dla.dla_set_prefill_path(dla.DLA_PATH_AUTO, 0)
+    whole_ms = sum(a.elapsed_time(b) for a, b in whole) / steps
+    sweep_ms = sum(a.elapsed_time(b) for a, b in sweep) / steps
+    ach = flops / (whole_ms * 1e-3) / 1e12
+    sweep_ach = flops / (sweep_ms * 1e-3) / 1e12
+    del cache, ws, o
+    return dict(value=B * T / (wall * 1e-3 / steps), unit="tokens/s", steps=steps, ms_per_step=wall * 1e3 / steps,
+                prefill_ms=whole_ms, achieved=ach, unit_achieved="TFLOP/s", frac=ach / PEAK_BF16_TFLOPS,
+                kernel=kernel, kernel_ms=sweep_ms, kernel_achieved=sweep_ach,
+                kernel_frac=sweep_ach / PEAK_BF16_TFLOPS, algorithmic_flop_per_launch=flops, schedule=stats)
+
+
+def _leg_log(name, r):
+    log(f"{name}: {r['ms_per_step']:.3f} ms/step, prefill {r['prefill_ms']:.3f} ms "
+        f"({100 * r['frac']:.1f}% of bf16 peak), chunk kernel {r['kernel']} {r['kernel_ms']:.3f} ms "
+        f"({100 * r['kernel_frac']:.1f}%), mean live states {r['schedule']['mean_live_states']:.2f}, "
+        f"boundaries/stream {r['schedule']['boundaries_per_stream']:.1f}, merges/stream "
+        f"{r['schedule']['merges_per_stream']:.1f}")
+
+
 def prefill_bench(args, torch, dla, workloads):
     cfg = workloads.CONFIGS[args.workload]
     B, H, T, dk, dv, C = cfg.B, cfg.H, cfg.T, cfg.dk, cfg.dv, cfg.C
@@ -125,118 +252,108 @@ def prefill_bench(args, torch, dla, workloads):
     t0 = time.time()
     d = workloads.prefill_inputs(cfg, reading=args.reading)
     log(f"prefill inputs {args.workload} ({args.reading}) generated in {time.time() - t0:.1f}s")
-    dt = torch.bfloat16 if cfg.io == "bf16" else torch.float32
-
-    def up(a, dd):
-        return torch.from_numpy(a).to(dev).to(dt).view(B, H, T, dd)
-
-    q, k, v, lam = up(d["q"], dk), up(d["k"], dk), up(d["v"], dv), up(d["lam"], C)
-    q_, k_, v_, lam_ = q, k, v, lam
+    q, k, v, lam = upload(torch, d, cfg, dev)
     sample = None
     if not args.no_cpu:
         S = min(BH, args.cpu_streams)
         sample = {x: d[x][:S].copy() for x in ("q", "k", "v", "lam")}
     del d
-    ws = dla.prefill_workspace(B, H, T, C, dk, dv, dev)
-    o = torch.empty(B, H, T, dv, dtype=dt, device=dev)
-
-    def timed(rule, steps=None, x=None):
-        """One untimed call exporting the schedule (m_t gives the algorithmic
-        flops), the warmup, then `steps` (default args.steps) timed calls on
-        the inputs x (default the workload's): wall time per step and the
-        chunk kernel's HIP-event time."""
-        steps = args.steps if steps is None else steps
-        q, k, v, lam = (q_, k_, v_, lam_) if x is None else x
-        cache = dla.Cache(B, H, C, dk, dv, device=dev, merge_rule=rule)
-        m_t = torch.empty(BH, T, dtype=torch.int32, device=dev)
-        bnd = torch.empty(BH, T, dtype=torch.uint8, device=dev)
-        n_ev = torch.empty(BH, dtype=torch.int32, device=dev)
-        dla.prefill(q, k, v, lam, cfg.tau, cache, o=o, workspace=ws,
-                    sched=dict(m_t=m_t, boundary=bnd, n_ev=n_ev))
-        torch.cuda.synchronize()
-        # (a prefill continues what the cache holds: every step below starts
-        # from an empty cache, and the reset is part of the timed step)
-        m_sum = int(m_t.sum(dtype=torch.int64).item())
-        flops = 2.0 * (m_sum + BH * T) * dk * dv
-        stats = dict(mean_live_states=m_sum / (BH * T),
-                     boundaries_per_stream=float(bnd.sum(dtype=torch.int64).item()) / BH,
-                     merges_per_stream=float(n_ev.sum(dtype=torch.int64).item()) / BH)
-        for _ in range(args.warmup):
-            cache.reset()
-            dla.prefill(q, k, v, lam, cfg.tau, cache, o=o, workspace=ws)
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(steps)]
-        for a, b in evs:          # materialise the event handles
-            a.record()
-            b.record()
-        torch.cuda.synchronize()
-        w0 = time.perf_counter()
-        for a, b in evs:
-            cache.reset()
-            dla.dla_set_prefill_events(a.cuda_event, b.cuda_event)
-            dla.prefill(q, k, v, lam, cfg.tau, cache, o=o, workspace=ws)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - w0
-        dla.dla_set_prefill_events(None, None)
-        kern_ms = [a.elapsed_time(b) for a, b in evs]
-        return wall * 1e3 / steps, sum(kern_ms) / len(kern_ms), flops, stats
-
-    ms_per_step, kern_avg, flops, stats = timed("sum")
+    head = prefill_leg(args, torch, dla, cfg, (q, k, v, lam))
+    _leg_log("prefill", head)
     tokens = B * T
-    achieved = flops / (kern_avg * 1e-3) / 1e12
     density = None
     if not args.no_density:
-        d_ms, d_kern, d_flops, d_stats = timed("density")
-        d_ach = d_flops / (d_kern * 1e-3) / 1e12
-        density = dict(merge_rule="density", value=tokens / (d_ms * 1e-3), unit="tokens/s",
-                       ms_per_step=d_ms, kernel_ms=d_kern, achieved=d_ach, unit_achieved="TFLOP/s",
-                       frac=d_ach / PEAK_BF16_TFLOPS, algorithmic_flop_per_launch=d_flops, schedule=d_stats)
-        log(f"prefill, density merge rule: {d_ms:.3f} ms/step, chunk kernel {d_kern:.3f} ms, "
-            f"{100 * d_ach / PEAK_BF16_TFLOPS:.1f}% of bf16 peak, mean live states "
-            f"{d_stats['mean_live_states']:.2f}, merges/stream {d_stats['merges_per_stream']:.1f}")
+        density = prefill_leg(args, torch, dla, cfg, (q, k, v, lam), rule="density")
+        density["merge_rule"] = "density"
+        _leg_log("prefill, density merge rule", density)
     literal = None
     if args.reading == "relative" and not args.no_literal:
         # the literal reading of the key noise: every token opens a state
         dl = workloads.prefill_inputs(cfg, reading="literal")
-        xl = (up(dl["q"], dk), up(dl["k"], dk), up(dl["v"], dv), up(dl["lam"], C))
+        xl = upload(torch, dl, cfg, dev)
         del dl
-        l_ms, l_kern, l_flops, l_stats = timed("sum", steps=5, x=xl)
+        literal = prefill_leg(args, torch, dla, cfg, xl, steps=5)
+        literal["reading"] = "literal"
         del xl
-        l_ach = l_flops / (l_kern * 1e-3) / 1e12
-        literal = dict(reading="literal", value=tokens / (l_ms * 1e-3), unit="tokens/s", steps=5,
-                       ms_per_step=l_ms, kernel_ms=l_kern, achieved=l_ach, unit_achieved="TFLOP/s",
-                       frac=l_ach / PEAK_BF16_TFLOPS, algorithmic_flop_per_launch=l_flops, schedule=l_stats)
-        log(f"prefill, literal noise reading: {l_ms:.3f} ms/step, chunk kernel {l_kern:.3f} ms, "
-            f"{100 * l_ach / PEAK_BF16_TFLOPS:.1f}% of bf16 peak, boundaries/stream "
-            f"{l_stats['boundaries_per_stream']:.0f}, merges/stream {l_stats['merges_per_stream']:.0f}")
+        _leg_log("prefill, literal noise reading", literal)
+    streamed = None
+    if not args.no_streamed:
+        # the streamed chunk kernel (states read from the cache every chunk) on
+        # the same workload: the kernel fp32 io and C > 32 take
+        streamed = prefill_leg(args, torch, dla, cfg, (q, k, v, lam), steps=5, path=dla.DLA_PATH_STREAMED)
+        streamed["path"] = "streamed"
+        _leg_log("prefill, streamed kernel", streamed)
     fenwick = sweep = None
     if not args.no_fenwick:
-        fenwick = fenwick_leg(args, torch, dla, cfg, q, k, v, lam, o, ws, ms_per_step)
+        o = torch.empty(B, H, T, dv, dtype=q.dtype, device=dev)
+        ws = dla.prefill_workspace(B, H, T, C, dk, dv, dev)
+        fenwick = fenwick_leg(args, torch, dla, cfg, q, k, v, lam, o, ws, head["ms_per_step"])
+        del o, ws
         if not args.no_sweep:
-            sweep = context_sweep(torch, dla, cfg, q, k, v, lam, ws)
-    kernel = dla.dla_prefill_kernel(dla.DLA_BF16 if cfg.io == "bf16" else dla.DLA_F32, B, H, C, dk, dv)
+            sweep = context_sweep(torch, dla, cfg, q, k, v, lam)
+    kernel = head["kernel"]
     traffic = measured_traffic(f"{_kernel_file(kernel)}_{args.workload}_hbm_traffic.txt", kernel)
+    mfma = measured_mfma(f"{_kernel_file(kernel)}_{args.workload}_mfma.txt", kernel)
+    roof = dict(bound="mfma", achieved=head["achieved"], peak=PEAK_BF16_TFLOPS, unit="TFLOP/s", frac=head["frac"],
+                traffic=traffic, scope="whole prefill (score, compaction, greedy scan, pre-pass, sweep)",
+                prefill_ms=head["prefill_ms"], kernel=kernel, kernel_ms=head["kernel_ms"],
+                kernel_achieved=head["kernel_achieved"], kernel_frac=head["kernel_frac"],
+                algorithmic_flop_per_launch=head["algorithmic_flop_per_launch"])
+    if mfma is not None:
+        # counters of the sweep kernel: MFMA flops issued over the algorithmic
+        # flops, and the share of SIMD cycles the matrix cores were busy
+        roof["mfma_ops_ratio"] = mfma["mfma_flop_per_launch"] / head["algorithmic_flop_per_launch"]
+        roof["mfma_busy_frac"] = mfma["mfma_busy_frac"]
+    else:
+        roof["mfma_ops_ratio"] = roof["mfma_busy_frac"] = None
     res = dict(
-        value=tokens / (ms_per_step * 1e-3), ms_per_step=ms_per_step,
+        value=tokens / (head["ms_per_step"] * 1e-3), ms_per_step=head["ms_per_step"],
         config=dict(workload=f"{args.workload} prefill", B=B, H=H, T=T, d_k=dk, d_v=dv, C=C,
                     tau=cfg.tau, io=cfg.io, keys=f"piecewise-regime, {args.reading} noise",
                     segment_means=list(cfg.seg_means)),
-        roofline=dict(bound="mfma", achieved=achieved, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                      frac=achieved / PEAK_BF16_TFLOPS, traffic=traffic,
-                      kernel=kernel, kernel_ms=kern_avg, algorithmic_flop_per_launch=flops),
-        schedule=stats,
-        token_heads_per_s=BH * T / (ms_per_step * 1e-3),
-        density_rule=density,
-        fenwick=fenwick,
-        context_sweep=sweep,
-        literal=literal,
+        roofline=roof, schedule=head["schedule"],
+        token_heads_per_s=BH * T / (head["ms_per_step"] * 1e-3),
+        density_rule=density, fenwick=fenwick, context_sweep=sweep, literal=literal, streamed=streamed,
     )
-    log(f"prefill: {ms_per_step:.3f} ms/step, chunk kernel {kern_avg:.3f} ms, "
-        f"{achieved:.1f} TFLOP/s algorithmic ({100 * achieved / PEAK_BF16_TFLOPS:.1f}% of bf16 peak), "
-        f"mean live states {stats['mean_live_states']:.2f}")
-    del q, k, v, lam, o, ws
+    del q, k, v, lam
     torch.cuda.empty_cache()
     return res, sample, cfg
+
+
+def other_prefill_legs(args, torch, dla, workloads):
+    """The other prefill workloads, each in its own full launch configuration:
+    the Mamba-2-780M-shaped layer (B=4, H=24, T=8192, d_k=128, d_v=64, C=16),
+    the long-context one (B=1, H=16, T=131072, d=128, C=32), the same
+    Mamba-2-shaped tokens with C=64 (the streamed kernel), the tiny fp32 layer
+    (the streamed kernel in fp32), and the state information score on the
+    Mamba-2-shaped layer with values that follow the key segments."""
+    dev = torch.device("cuda:0")
+    out = {}
+    import dataclasses
+    legs = [("mamba2_780m_bf16", "mamba2_780m_bf16", {}, {}),
+            ("long_t131k_bf16", "long_t131k_bf16", {}, {}),
+            ("mamba2_780m_bf16_c64", "mamba2_780m_bf16", dict(C=64), {}),
+            ("tiny_fp32", "tiny_fp32", {}, {}),
+            ("mamba2_780m_bf16_state_score", "mamba2_780m_bf16", {}, dict(score_rule="state", tau=0.6))]
+    for name, base, repl, kw in legs:
+        cfg = dataclasses.replace(workloads.CONFIGS[base], **repl)
+        t0 = time.time()
+        d = workloads.prefill_inputs(cfg, values="regime" if kw.get("score_rule") == "state" else "random")
+        x = upload(torch, d, cfg, dev)
+        del d
+        log(f"{name}: inputs generated in {time.time() - t0:.1f}s")
+        r = prefill_leg(args, torch, dla, cfg, x, steps=10 if cfg.T >= 4096 else 50, **kw)
+        r["config"] = dict(workload=name, B=cfg.B, H=cfg.H, T=cfg.T, d_k=cfg.dk, d_v=cfg.dv, C=cfg.C,
+                           tau=kw.get("tau", cfg.tau), io=cfg.io, score_rule=kw.get("score_rule", "cosine"),
+                           values="regime" if kw.get("score_rule") == "state" else "random",
+                           segment_means=list(cfg.seg_means))
+        kernel = r["kernel"]
+        r["traffic"] = measured_traffic(f"{_kernel_file(kernel)}_{name}_hbm_traffic.txt", kernel)
+        _leg_log(name, r)
+        out[name] = r
+        del x
+        torch.cuda.empty_cache()
+    return out
 
 
 def fenwick_leg(args, torch, dla, cfg, q, k, v, lam, o, ws, dla_ms):
@@ -278,7 +395,7 @@ def fenwick_leg(args, torch, dla, cfg, q, k, v, lam, o, ws, dla_ms):
                 buckets_read_per_token=read / T, dla_over_fenwick_time=dla_ms / ms)
 
 
-def context_sweep(torch, dla, cfg, q, k, v, lam, ws, lengths=(4096, 8192, 16384, 32768), steps=5):
+def context_sweep(torch, dla, cfg, q, k, v, lam, lengths=(4096, 8192, 16384, 32768), steps=5):
     """Prefill tokens/s of DLA (summed-information merges, C = cfg.C) and of the
     Log-Linear fixed schedule (C = L(T')) on the first T' tokens of the
     workload's streams: wall time over `steps` calls after one warmup call."""
@@ -318,46 +435,24 @@ def context_sweep(torch, dla, cfg, q, k, v, lam, ws, lengths=(4096, 8192, 16384,
     return out
 
 
-def decode_inputs_device(torch, cfg, steps, dev):
-    """The batched-decode workload drawn on the device with torch's seeded
-    generator (same recipe as workloads.decode_inputs, different generator)."""
-    g = torch.Generator(device=dev)
-    g.manual_seed(cfg.seed)
-    BH, C, dk, dv, n0 = cfg.B * cfg.H, cfg.C, cfg.dk, cfg.dv, cfg.init_tokens
-    bf = torch.bfloat16
-    states = torch.empty(BH, C, dv, dk, dtype=torch.float32, device=dev)
-    step = 128
-    for c0 in range(0, BH, step):
-        n = min(step, BH - c0)
-        U = (torch.randn(n * C, dv, n0, generator=g, device=dev) / math.sqrt(dv)).to(bf).float()
-        W = (torch.randn(n * C, n0, dk, generator=g, device=dev) / math.sqrt(dk)).to(bf).float()
-        states[c0:c0 + n] = torch.bmm(U, W.contiguous()).view(n, C, dv, dk)
-    e = torch.empty(BH, C, dtype=torch.float64, device=dev).exponential_(1.0, generator=g)
-    info = torch.round(e * 2.0 ** 32).to(torch.int64)
-    count = torch.full((BH, C), n0, dtype=torch.int32, device=dev)
-    start = (torch.arange(C, device=dev, dtype=torch.int64) * n0).expand(BH, C).contiguous()
-    # keys: a new regime starts at each step with probability 1/mean (Geometric lengths)
-    mu = cfg.seg_means[0]
-    newseg = torch.rand(BH, steps, generator=g, device=dev) < (1.0 / mu)
-    seg = torch.cumsum(newseg.to(torch.int32), 1)
-    nseg = int(seg.max().item()) + 1
-    cent = torch.randn(BH, nseg, dk, generator=g, device=dev)
-    cent = cent / cent.norm(dim=2, keepdim=True)
-    K = torch.empty(steps, BH, dk, dtype=bf, device=dev)
-    Q = torch.empty(steps, BH, dk, dtype=bf, device=dev)
-    V = torch.empty(steps, BH, dv, dtype=bf, device=dev)
-    L = torch.empty(steps, BH, C, dtype=bf, device=dev)
-    for s0 in range(0, steps, 256):
-        n = min(256, steps - s0)
-        sg = seg[:, s0:s0 + n].long()
-        kk = torch.gather(cent, 1, sg.unsqueeze(2).expand(BH, n, dk)) + \
-            (0.2 / math.sqrt(dk)) * torch.randn(BH, n, dk, generator=g, device=dev)
-        K[s0:s0 + n] = kk.transpose(0, 1).to(bf)
-        Q[s0:s0 + n] = (torch.randn(n, BH, dk, generator=g, device=dev) / math.sqrt(dk)).to(bf)
-        V[s0:s0 + n] = (torch.randn(n, BH, dv, generator=g, device=dev) / math.sqrt(dv)).to(bf)
-        L[s0:s0 + n] = torch.sigmoid(torch.randn(n, BH, C, generator=g, device=dev)).to(bf)
-    return dict(states=states, info=info, count=count, start=start, t_seen=C * n0,
-                q=Q, k=K, v=V, lam=L)
+def decode_inputs_tiled(torch, workloads, cfg, steps, dev, distinct):
+    """The batched-decode workload from workloads.decode_inputs (the recipe the
+    parity tests check): `distinct` caches and their step inputs drawn on the
+    host, tiled over the B*H streams on the device (stream i gets draw
+    i mod distinct); step inputs as [steps, B*H, d] bf16."""
+    BH = cfg.B * cfg.H
+    d = workloads.decode_inputs(cfg, caches=range(distinct), steps=steps)
+    ti = torch.arange(BH, device=dev) % distinct
+
+    def tile(a):          # [distinct, steps, n] -> [steps, B*H, n] bf16
+        return torch.from_numpy(np.ascontiguousarray(np.swapaxes(a, 0, 1))).to(dev).to(torch.bfloat16)[:, ti]
+
+    out = dict(states=torch.from_numpy(d["states"]).to(dev)[ti], info=torch.from_numpy(d["info"]).to(dev)[ti],
+               count=torch.from_numpy(d["count"]).to(dev)[ti], start=torch.from_numpy(d["start"]).to(dev)[ti],
+               t_seen=d["t_seen"])
+    for x in ("q", "k", "v", "lam"):
+        out[x] = tile(d[x])
+    return out
 
 
 def decode_bench(args, torch, dla, workloads, state_dtype="f32"):
@@ -369,7 +464,7 @@ def decode_bench(args, torch, dla, workloads, state_dtype="f32"):
     dev = torch.device("cuda:0")
     S, W = args.decode_steps, args.decode_warmup
     t0 = time.time()
-    d = decode_inputs_device(torch, cfg, S + W, dev)
+    d = decode_inputs_tiled(torch, workloads, cfg, S + W, dev, args.decode_distinct)
     cache = dla.Cache(B, H, C, dk, dv, device=dev, state_dtype=state_dtype,
                       preload=dict(m0=C, states=d["states"], info=d["info"], count=d["count"],
                                    start=d["start"], t_seen=d["t_seen"]))
@@ -438,7 +533,8 @@ def decode_bench(args, torch, dla, workloads, state_dtype="f32"):
                                        "k_decode(bf16 states)"),
                       kernel="k_decode",
                       kernel_ms=kern_avg, algorithmic_bytes_per_launch=bytes_per_step),
-        inputs="drawn on the device with torch's seeded generator, same recipe",
+        inputs=f"workloads.decode_inputs: {args.decode_distinct} distinct caches and step inputs tiled over the "
+               f"{BH} streams",
     )
     log(f"decode ({state_dtype} states): {res['steps_per_s']:.1f} steps/s, kernel {kern_avg:.3f} ms, "
         f"{achieved:.0f} GB/s algorithmic ({100 * achieved / PEAK_HBM_GBS:.1f}% of HBM peak)")
@@ -455,7 +551,7 @@ def fenwick_decode_bench(args, torch, dla, workloads):
     dev = torch.device("cuda:0")
     S, W = args.decode_steps, args.decode_warmup
     t0 = 1 << 20
-    d = decode_inputs_device(torch, cfg, S + W, dev)
+    d = decode_inputs_tiled(torch, workloads, cfg, S + W, dev, args.decode_distinct)
     first = d.pop("states")[:, :1].contiguous()
     cache = dla.Cache(B, H, C, dk, dv, device=dev, merge_rule="fenwick",
                       preload=dict(m0=1, states=first, info=torch.zeros(BH, 1, dtype=torch.int64, device=dev),
@@ -508,12 +604,14 @@ def _kernel_file(kernel: str) -> str:
 
 
 def cpu_baseline(args, sample, cfg):
-    """The oracle as it stands on S streams x the first Ts tokens; Ts doubles
-    from 512 until one run takes a third of the time budget, and that run is
-    reported."""
+    """The oracle as it stands on S streams x the first Ts tokens, one stream
+    per thread on every CPU thread the process is granted (OMP_NUM_THREADS
+    where it is set, else all host threads); Ts doubles from 512 until one run
+    takes a third of the time budget, and that run is reported."""
     import oracle
     S = sample["k"].shape[0]
-    cores = min(S, os.cpu_count() or 1)
+    granted = int(os.environ.get("OMP_NUM_THREADS") or 0) or (os.cpu_count() or 1)
+    cores = min(S, granted)
     Ts = 512
     while True:
         t0 = time.perf_counter()
@@ -525,12 +623,13 @@ def cpu_baseline(args, sample, cfg):
         Ts = min(cfg.T, 2 * Ts)
     # a token of the layer is d_k x d_v work in each of the H heads
     val = S * Ts / dt / cfg.H
-    log(f"cpu oracle: {S} streams x {Ts} tokens in {dt:.1f}s on {cores} threads")
+    log(f"cpu oracle: {S} streams x {Ts} tokens in {dt:.1f}s on {cores} threads "
+        f"(host threads {os.cpu_count()}, granted {granted})")
     return dict(value=val, unit="tokens/s", cores=cores, kind="oracle",
                 sample=f"{S} of {cfg.B * cfg.H} streams x first {Ts} of {cfg.T} tokens of the "
                        f"prefill workload (schedule, states and every output, float64), "
                        f"{dt:.1f} s; value = stream-tokens/s / H",
-                host_cpu=_cpu_model())
+                host_threads=os.cpu_count(), granted_threads=granted, host_cpu=_cpu_model())
 
 
 def _cpu_model():
@@ -566,7 +665,13 @@ def main():
     ap.add_argument("--no-fenwick", action="store_true",
                     help="skip the prefill measurement under the Log-Linear fixed schedule")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--cpu-streams", type=int, default=16)
+    ap.add_argument("--cpu-streams", type=int, default=32)
+    ap.add_argument("--decode-distinct", type=int, default=128,
+                    help="distinct decode caches drawn on the host and tiled over the B*H streams")
+    ap.add_argument("--no-streamed", action="store_true",
+                    help="skip the prefill measurement on the streamed chunk kernel")
+    ap.add_argument("--no-other", action="store_true",
+                    help="skip the other prefill workloads (Mamba-2-shaped, long context, C=64, fp32, state score)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the prefill, copy this many MiB three times (counter calibration)")
     args = ap.parse_args()
@@ -586,6 +691,7 @@ def main():
         sys.exit(1)
     dla.load()
     pre, sample, cfg = prefill_bench(args, torch, dla, workloads)
+    other = None if args.no_other else other_prefill_legs(args, torch, dla, workloads)
     copy_probe(torch, args.copy_probe_mib)
     dec = None if args.no_decode else decode_bench(args, torch, dla, workloads)
     torch.cuda.empty_cache()
@@ -606,6 +712,8 @@ def main():
         "prefill_literal_reading": pre["literal"],
         "prefill_fenwick_schedule": pre["fenwick"],
         "prefill_context_sweep": pre["context_sweep"],
+        "prefill_streamed_kernel": pre["streamed"],
+        "prefill_workloads": other,
         "decode_fenwick_schedule": dec_fen,
     }
     print(json.dumps(out), flush=True)

@@ -230,7 +230,7 @@ def prefill_leg(args, torch, dla, cfg, x, steps=None, rule="sum", score_rule="co
     ach = flops / (whole_ms * 1e-3) / 1e12
     sweep_ach = flops / (sweep_ms * 1e-3) / 1e12
     del cache, ws, o
-    return dict(value=B * T / (wall * 1e-3 / steps), unit="tokens/s", steps=steps, ms_per_step=wall * 1e3 / steps,
+    return dict(value=B * T * steps / wall, unit="tokens/s", steps=steps, ms_per_step=wall * 1e3 / steps,
                 prefill_ms=whole_ms, achieved=ach, unit_achieved="TFLOP/s", frac=ach / PEAK_BF16_TFLOPS,
                 kernel=kernel, kernel_ms=sweep_ms, kernel_achieved=sweep_ach,
                 kernel_frac=sweep_ach / PEAK_BF16_TFLOPS, algorithmic_flop_per_launch=flops, schedule=stats)

@@ -63,6 +63,9 @@ struct SsSmem {
     TIO vr[kChunk][DV + PAD];       // V of the chunk, row-major
     TIO kt[DK][kChunk + PAD];       // K transposed
     TIO vt[DV][kChunk + PAD];       // V transposed
+    // K of the chunk scaled by 2^-ek in fp16 (bf16 inputs: exact while within
+    // fp16's normal range of the chunk's largest element), the operand of u_t
+    _Float16 kh[sizeof(TIO) == 2 ? kChunk : 1][DK + 8];
     union {
         float H[kChunk][kChunk + 1];  // Gram products (lower triangle)
         double pre[kPreEntries];      // their row prefix sums
@@ -153,34 +156,67 @@ __global__ __launch_bounds__(kSsThreads, 1) void k_state_score(
     }
     int32_t tcnt = 0;
     int64_t tsum = 0;
+    // the chunk's K and V rows as 16-byte pieces: lane l holds token l's
+    // pieces wave + 4 i (so that the transposed LDS writes of a wave touch 64
+    // consecutive tokens of one row of K^T or V^T)
+    constexpr int EPV = 16 / sizeof(TIO);
+    constexpr int NKP = kChunk * DK / EPV / kSsThreads;
+    constexpr int NVP = kChunk * DV / EPV / kSsThreads;
+    static_assert(NKP * kSsThreads * EPV == kChunk * DK && NVP * kSsThreads * EPV == kChunk * DV && kChunk == 64,
+                  "whole pieces, one token per lane");
+    constexpr bool kPrefetch = NKP + NVP <= 8;
+    uint4 kp[NKP], vp[NVP];
+    auto load_chunk = [&](int c, uint4 (&kq)[NKP], uint4 (&vq)[NVP]) {
+        const int cbase = c * kChunk, nv = min(kChunk, T - cbase);
+        // (rows past the stream's end load its last row and are zeroed when
+        // staged: a select here would wait for the load)
+        const size_t row = tok0 + cbase + min(lane, nv - 1);
+#pragma unroll
+        for (int i = 0; i < NKP; ++i) kq[i] = *reinterpret_cast<const uint4 *>(K + row * DK + EPV * (wave + 4 * i));
+#pragma unroll
+        for (int i = 0; i < NVP; ++i) vq[i] = *reinterpret_cast<const uint4 *>(V + row * DV + EPV * (wave + 4 * i));
+    };
+    if constexpr (kPrefetch) load_chunk(0, kp, vp);
 
+    // (the waves exchange only LDS data inside the chunk loop: its barriers
+    // leave the global loads of the next chunk in flight)
     for (int ch = 0; ch < NCH; ++ch) {
         const int c0 = ch * kChunk;
         const int nvalid = min(kChunk, T - c0);
-        __syncthreads();
-        // ---- 1. stage the chunk (zero rows past the stream's end)
-        constexpr int EPV = 16 / sizeof(TIO);
+        lds_barrier();
+        // ---- 1. stage the chunk (zero rows past the stream's end): rows into
+        // LDS row-major and transposed; where the registers allow, the pieces
+        // were loaded during the previous chunk and the next chunk's are
+        // loaded now
         float kmax = 0.0f;
-        for (int idx = tid; idx < kChunk * DK / EPV; idx += kSsThreads) {
-            const int r = idx / (DK / EPV), cv = (idx % (DK / EPV)) * EPV;
-            uint4 x = make_uint4(0, 0, 0, 0);
-            if (r < nvalid) x = *reinterpret_cast<const uint4 *>(K + (tok0 + c0 + r) * DK + cv);
-            *reinterpret_cast<uint4 *>(&S.kr[r][cv]) = x;
-            const TIO *e = reinterpret_cast<const TIO *>(&x);
+        if constexpr (!kPrefetch) load_chunk(ch, kp, vp);
+        if (lane >= nvalid) {
+#pragma unroll
+            for (int i = 0; i < NKP; ++i) kp[i] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < NVP; ++i) vp[i] = make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < NKP; ++i) {
+            const int r = lane, cv = EPV * (wave + 4 * i);
+            *reinterpret_cast<uint4 *>(&S.kr[r][cv]) = kp[i];
+            const TIO *e = reinterpret_cast<const TIO *>(&kp[i]);
 #pragma unroll
             for (int j = 0; j < EPV; ++j) {
                 S.kt[cv + j][r] = e[j];
                 kmax = fmaxf(kmax, fabsf(to_f(e[j])));
             }
         }
-        for (int idx = tid; idx < kChunk * DV / EPV; idx += kSsThreads) {
-            const int r = idx / (DV / EPV), cv = (idx % (DV / EPV)) * EPV;
-            uint4 x = make_uint4(0, 0, 0, 0);
-            if (r < nvalid) x = *reinterpret_cast<const uint4 *>(V + (tok0 + c0 + r) * DV + cv);
-            *reinterpret_cast<uint4 *>(&S.vr[r][cv]) = x;
-            const TIO *e = reinterpret_cast<const TIO *>(&x);
+#pragma unroll
+        for (int i = 0; i < NVP; ++i) {
+            const int r = lane, cv = EPV * (wave + 4 * i);
+            *reinterpret_cast<uint4 *>(&S.vr[r][cv]) = vp[i];
+            const TIO *e = reinterpret_cast<const TIO *>(&vp[i]);
 #pragma unroll
             for (int j = 0; j < EPV; ++j) S.vt[cv + j][r] = e[j];
+        }
+        if constexpr (kPrefetch) {
+            if (ch + 1 < NCH) load_chunk(ch + 1, kp, vp);
         }
         // scale of S_pre's fp16 halves and of K's
         float smax = 0.0f;
@@ -196,13 +232,26 @@ __global__ __launch_bounds__(kSsThreads, 1) void k_state_score(
             S.red[wave] = smax;
             S.kred[wave] = kmax;
         }
-        __syncthreads();
+        lds_barrier();
         const int es = f16_exponent(fmaxf(fmaxf(S.red[0], S.red[1]), fmaxf(S.red[2], S.red[3])));
         const int ek = f16_exponent(fmaxf(fmaxf(S.kred[0], S.kred[1]), fmaxf(S.kred[2], S.kred[3])));
         const bool pre_live = a < c0;   // the current state began before this chunk
 
         // ---- 2. u_t = v_t^T S_pre k_t (wave w: its d_v tiles, every token)
         if (pre_live) {
+            if constexpr (!kF32) {
+                // (every wave reads every token's K: converted once, by all threads)
+                for (int idx = tid; idx < kChunk * DK / 8; idx += kSsThreads) {
+                    const int r = idx / (DK / 8), cv = (idx % (DK / 8)) * 8;
+                    const uint4 x = *reinterpret_cast<const uint4 *>(&S.kr[r][cv]);
+                    const TIO *e = reinterpret_cast<const TIO *>(&x);
+                    f16x8 h;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) h[j] = static_cast<_Float16>(ldexpf(to_f(e[j]), -ek));
+                    *reinterpret_cast<f16x8 *>(&S.kh[r][cv]) = h;
+                }
+                lds_barrier();
+            }
             floatx4 Y[IPW][4];
 #pragma unroll
             for (int ii = 0; ii < IPW; ++ii)
@@ -226,13 +275,21 @@ __global__ __launch_bounds__(kSsThreads, 1) void k_state_score(
                 for (int tt = 0; tt < 4; ++tt) {
                     // K of token 16 tt + lr at the same columns
                     f16x8 kh, kl;
+                    if constexpr (kF32) {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        _Float16 h, l;
-                        split16(to_f(S.kr[16 * tt + lr][32 * jp + 4 * lg + r]), ek, h, l);
-                        kh[r] = h; kl[r] = l;
-                        split16(to_f(S.kr[16 * tt + lr][32 * jp + 16 + 4 * lg + r]), ek, h, l);
-                        kh[4 + r] = h; kl[4 + r] = l;
+                        for (int r = 0; r < 4; ++r) {
+                            _Float16 h, l;
+                            split16(to_f(S.kr[16 * tt + lr][32 * jp + 4 * lg + r]), ek, h, l);
+                            kh[r] = h; kl[r] = l;
+                            split16(to_f(S.kr[16 * tt + lr][32 * jp + 16 + 4 * lg + r]), ek, h, l);
+                            kh[4 + r] = h; kl[4 + r] = l;
+                        }
+                    } else {
+                        typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+                        const f16x4 a0 = *reinterpret_cast<const f16x4 *>(&S.kh[16 * tt + lr][32 * jp + 4 * lg]);
+                        const f16x4 a1 = *reinterpret_cast<const f16x4 *>(&S.kh[16 * tt + lr][32 * jp + 16 + 4 * lg]);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) { kh[r] = a0[r]; kh[4 + r] = a1[r]; }
                     }
 #pragma unroll
                     for (int ii = 0; ii < IPW; ++ii) {
@@ -282,55 +339,148 @@ __global__ __launch_bounds__(kSsThreads, 1) void k_state_score(
 #pragma unroll
             for (int r = 0; r < 4; ++r) S.H[16 * tt + 4 * lg + r][16 * st + lr] = gk[r] * gv[r];
         }
-        __syncthreads();
-        // ---- row prefix sums of H in fp64 (wave 0: lane t owns row t); the
-        // whole row is read before any lane writes the prefix array, which
-        // shares the bytes
-        if (wave == 0) {
-            float row[kChunk];
+        lds_barrier();
+        // ---- row prefix sums of H in fp64: four threads per row t (lanes 4t'
+        // .. 4t' + 3 of a wave), each a 16-column segment, offset by the sums
+        // of the segments before it; the rows are read whole before any
+        // thread writes the prefix array, which shares their bytes
+        {
+            const int t = tid >> 2, g = tid & 3;
+            float seg[16];
 #pragma unroll
-            for (int s = 0; s < kChunk; ++s) row[s] = s <= lane ? S.H[lane][s] : 0.0f;
-            const float diag = row[lane];
-            __builtin_amdgcn_wave_barrier();
-            double run = 0.0;
+            for (int j = 0; j < 16; ++j) seg[j] = 16 * g + j <= t ? S.H[t][16 * g + j] : 0.0f;
+            const float diag = S.H[t][t];
+            lds_barrier();
+            double tot = 0.0;
 #pragma unroll
-            for (int s = 0; s < kChunk; ++s)
-                if (s <= lane) {
-                    S.pre[pre_idx(lane, s)] = run;
-                    run += static_cast<double>(row[s]);
+            for (int j = 0; j < 16; ++j) tot += static_cast<double>(seg[j]);
+            double inc = tot;
+            double y = __shfl_up(inc, 1, 4);
+            if (g >= 1) inc += y;
+            y = __shfl_up(inc, 2, 4);
+            if (g >= 2) inc += y;
+            double run = __shfl_up(inc, 1, 4);
+            if (g == 0) run = 0.0;
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                if (16 * g + j <= t) {
+                    S.pre[pre_idx(t, 16 * g + j)] = run;
+                    run += static_cast<double>(seg[j]);
                 }
-            S.nn[lane] = diag;
+            if (g == 0) S.nn[t] = diag;
         }
-        __syncthreads();
-        // ---- 4. the scan (wave 0)
+        lds_barrier();
+        // ---- 4. the scan (wave 0, lane t = token t).  A pass scores every
+        // token from pos on against the current state as it stands (the one
+        // that began at a), as if none of them restarted it: x_t from the
+        // Gram prefix sums (and u_t while the state began before the chunk),
+        // |S|_F^2 as F plus the prefix sum of 2 x_j + |v_j|^2 |k_j|^2.  Then
+        // the pass's boundaries are taken in order; the tokens before one join
+        // the current state, and at the boundary the greedy merge decides: a
+        // new state that stays apart restarts the current state at the
+        // boundary token, and the next pass scores from the token after it.
         if (wave == 0) {
-            for (int t = 0; t < nvalid; ++t) {
-                const int64_t tok = c0 + t;
-                const double nn = S.nn[t];
-                float sc;
-                bool bnd;
-                double x = 0.0;
+            const int t = lane;
+            const bool valid = t < nvalid;
+            const double nn_t = valid ? static_cast<double>(S.nn[t]) : 0.0;
+            const double pre_tt = valid ? S.pre[pre_idx(t, t)] : 0.0;
+            double u_t = 0.0;
+            if (valid && a < c0)
+                u_t = static_cast<double>(S.upart[0][t]) + S.upart[1][t] + S.upart[2][t] + S.upart[3][t];
+            float sc_fin = 0.0f;            // the token's final score and boundary flag
+            bool bnd_fin = false;
+            int pos = 0;
+            while (pos < nvalid) {
                 if (m == 0) {
-                    sc = 2.0f;
-                    bnd = true;
-                } else {
-                    const int lo = a > c0 ? static_cast<int>(a - c0) : 0;
-                    x = S.pre[pre_idx(t, t)] - S.pre[pre_idx(t, lo)];
-                    if (a < c0)
-                        x += static_cast<double>(S.upart[0][t]) + S.upart[1][t] + S.upart[2][t] + S.upart[3][t];
-                    if (nn == 0.0 || F <= 0.0) {
+                    // an empty cache: the token opens the first state
+                    if (t == pos) { sc_fin = 2.0f; bnd_fin = true; }
+                    if (lane == 0) { I = fixed_point(2.0f); n = 1; }
+                    m = 1;
+                    F = readlane_any(nn_t, pos);
+                    a = c0 + pos;
+                    ++pos;
+                    continue;
+                }
+                const int lo = a > c0 ? static_cast<int>(a - c0) : 0;
+                const bool live = valid && t >= pos;
+                double x = 0.0, d = 0.0;
+                if (live) {
+                    x = pre_tt - S.pre[pre_idx(t, lo)];
+                    if (a < c0) x += u_t;
+                    d = 2.0 * x + nn_t;
+                }
+                const double dsum = wave_incl_scan(d, lane);
+                double dex = __shfl_up(dsum, 1);
+                if (lane == 0) dex = 0.0;
+                const double Fin = F + dsum;    // |S|_F^2 after token t joins
+                const double Fx = F + dex;      // before it
+                float sc = 0.0f;
+                if (live) {
+                    if (nn_t == 0.0 || Fx <= 0.0) {
                         sc = 2.0f;
                     } else {
-                        const double c = x / sqrt(nn * F);
+                        const double c = x / sqrt(nn_t * Fx);
                         sc = static_cast<float>(sqrt(fmax(0.0, 2.0 * D * (1.0 - c))) / (sqD + 1e-6));
                     }
-                    bnd = sc >= tau;
                 }
-                const int64_t qv = fixed_point(sc);
-                bool extend = !bnd;             // the token extends the current state
-                if (bnd) {
+                const bool b_t = live && sc >= tau;
+                const int64_t qv = live ? fixed_point(sc) : 0;
+                uint64_t bm = __ballot(b_t);
+                bool restart = false;
+                while (!restart) {
+                    if (m == C && merge_rule != DLA_MERGE_DENSITY && bm) {
+                        // A full cache under the summed key: a boundary b merges
+                        // into the newest pair (the current state and b itself)
+                        // when that pair's key, I_last + q_b, is below the key of
+                        // the pair before it (q_b < I_{m-2}) and below every older
+                        // pair's key (their minimum M, which such merges leave
+                        // alone), I_last grown by every token from pos to b.  The
+                        // run of such boundaries is taken at once, up to the first
+                        // boundary whose merge lands elsewhere.
+                        const int64_t Iprev = m >= 2 ? readlane_any(I, m - 2) : INT64_MAX;
+                        const int64_t Ilast = readlane_any(I, m - 1);
+                        // (the neighbour's value is moved by every lane before the
+                        // select: a lane-to-lane move reads nothing from a lane
+                        // that a branch has switched off)
+                        const int64_t I_nx = lane_down1(I);
+                        const int64_t M = wave_min_i64(lane + 2 < m ? I + I_nx : INT64_MAX);
+                        const int64_t qa = t >= pos ? qv : int64_t{0};
+                        const int64_t Qin = wave_incl_scan(qa, lane);
+                        const bool joins_newest = qa < Iprev && Ilast + Qin < M;
+                        const uint64_t stop = bm & __ballot(!joins_newest);
+                        const int bs = stop ? __builtin_ctzll(stop) : nvalid;
+                        if (bs > pos) {
+                            const int64_t q_run = readlane_any(Qin, bs - 1);
+                            if (lane == m - 1) { I += q_run; n += bs - pos; }
+                            if (t >= pos && t < bs) { sc_fin = sc; bnd_fin = b_t; }
+                            bm &= ~low_bits(bs);
+                            pos = bs;
+                        }
+                        if (bs >= nvalid) {
+                            F = readlane_any(Fin, nvalid - 1);
+                            pos = nvalid;
+                            break;
+                        }
+                        // (boundary bs is taken below, one step of the greedy merge)
+                    }
+                    const int b = bm ? __builtin_ctzll(bm) : nvalid;
+                    // tokens pos .. b - 1 join the current state
+                    if (b > pos) {
+                        const int64_t q_join = wave_sum((t >= pos && t < b) ? qv : int64_t{0});
+                        if (lane == m - 1) { I += q_join; n += b - pos; }
+                        if (t >= pos && t < b) { sc_fin = sc; bnd_fin = false; }
+                    }
+                    if (b >= nvalid) {
+                        F = readlane_any(Fin, nvalid - 1);
+                        pos = nvalid;
+                        break;
+                    }
+                    // the boundary token b
+                    if (t == b) { sc_fin = sc; bnd_fin = true; }
+                    const int64_t qb = readlane_any(qv, b);
+                    bool extend = false;
                     if (m < C) {
-                        if (lane == m) { I = qv; n = 1; }
+                        if (lane == m) { I = qb; n = 1; }
                         ++m;
                     } else {
                         // the greedy merge of the state set (as the greedy scan
@@ -339,7 +489,7 @@ __global__ __launch_bounds__(kSsThreads, 1) void k_state_score(
                         const int64_t I_nx = lane_down1(I);
                         const int32_t n_nx = lane_down1(n);
                         const bool inside = lane + 1 < m;
-                        const int64_t pI = inside ? I_nx : qv;
+                        const int64_t pI = inside ? I_nx : qb;
                         const int32_t pn = inside ? n_nx : 1;
                         int istar;
                         if (merge_rule == DLA_MERGE_DENSITY) {
@@ -353,22 +503,23 @@ __global__ __launch_bounds__(kSsThreads, 1) void k_state_score(
                         else if (lane > istar && lane < m) { I = pI; n = pn; }
                         extend = istar == m - 1;
                     }
-                } else {
-                    if (lane == m - 1) { I += qv; n += 1; }
+                    pos = b + 1;
+                    bm &= bm - 1;
+                    if (!extend) {
+                        // a new current state, of the boundary token alone
+                        F = readlane_any(nn_t, b);
+                        a = c0 + b;
+                        restart = true;
+                    }
+                    // (joined: the pass's scores of the later tokens stand)
                 }
-                if (extend) {
-                    F += 2.0 * x + nn;
-                } else {
-                    F = nn;
-                    a = tok;
-                }
-                if (lane == 0) {
-                    S.s_c[t] = sc;
-                    S.f_c[t] = static_cast<uint8_t>(bnd);
-                }
-                tcnt += bnd ? 1 : 0;
-                tsum += qv;
             }
+            if (valid) {
+                S.s_c[t] = sc_fin;
+                S.f_c[t] = static_cast<uint8_t>(bnd_fin);
+            }
+            tcnt += __popcll(__ballot(valid && bnd_fin));
+            tsum += wave_sum(valid ? fixed_point(sc_fin) : int64_t{0});
             if (lane == 0) S.a_s = a;
             // per-tile boundary count and information sum for the compaction
             const int tile = c0 / kScoreTile;
@@ -382,7 +533,7 @@ __global__ __launch_bounds__(kSsThreads, 1) void k_state_score(
                 tsum = 0;
             }
         }
-        __syncthreads();
+        lds_barrier();
         a = S.a_s;
         // chunk outputs
         if (tid < nvalid) {

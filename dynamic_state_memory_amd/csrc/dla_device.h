@@ -149,6 +149,37 @@ template <int CTRL> __device__ __forceinline__ int64_t dpp_move(int64_t x) {
     return static_cast<int64_t>(dpp_move64<CTRL>(static_cast<uint64_t>(x)));
 }
 
+// DPP move that reads 0 in every lane outside the rows set in ROWS (bit r:
+// lanes 16 r .. 16 r + 15) and in every lane whose source lies outside the wave
+// or its row: row_shr:n (0x110 + n), row_bcast:15 (0x142), row_bcast:31
+// (0x143) and wave_shr:1 (0x138).
+template <int CTRL, int ROWS> __device__ __forceinline__ uint32_t dpp32_rows(uint32_t x) {
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), CTRL, ROWS, 0xF, false));
+}
+template <int CTRL, int ROWS, typename T> __device__ __forceinline__ T dpp_rows(T x) {
+    static_assert(sizeof(T) == 8, "64-bit values");
+    const uint64_t u = __builtin_bit_cast(uint64_t, x);
+    const uint32_t lo = dpp32_rows<CTRL, ROWS>(static_cast<uint32_t>(u));
+    const uint32_t hi = dpp32_rows<CTRL, ROWS>(static_cast<uint32_t>(u >> 32));
+    return __builtin_bit_cast(T, (static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave by DPP: shifts by 1, 2, 4
+// and 8 lanes within each row of 16, then the last lane of row 0 (2) added
+// into row 1 (3), then the last lane of row 1 into rows 2 and 3.  The whole
+// wave must be active.
+template <typename T> __device__ __forceinline__ T wave_incl_scan_dpp(T x) {
+    x += dpp_rows<0x111, 0xF>(x);
+    x += dpp_rows<0x112, 0xF>(x);
+    x += dpp_rows<0x114, 0xF>(x);
+    x += dpp_rows<0x118, 0xF>(x);
+    x += dpp_rows<0x142, 0xA>(x);
+    x += dpp_rows<0x143, 0xC>(x);
+    return x;
+}
+// The value of the lane below (lane 0 reads 0).
+template <typename T> __device__ __forceinline__ T lane_up1(T x) { return dpp_rows<0x138, 0xF>(x); }
+
 template <typename T> __device__ __forceinline__ T readlane_any(T x, int l) {
     if constexpr (sizeof(T) == 8) {
         const uint64_t u = __builtin_bit_cast(uint64_t, x);

@@ -25,13 +25,17 @@
 //      S_pre split into two fp16 halves (22 significant bits) and K exact in
 //      fp16 (bf16 inputs) or split as well (fp32 inputs), then u_t = v_t . Y_t;
 //   2. the chunk's Gram products H[t][s] = (v_t . v_s)(k_t . k_s) on MFMA and
-//      their row prefix sums in fp64, so that the part of x_t inside the chunk
-//      is one difference;
-//   3. one wave scans the tokens: x_t, the score, the boundary, and at a
-//      boundary over capacity the greedy merge decision (same rule and
-//      arithmetic as the greedy scan kernel) -- only to know whether the
-//      current state restarts; F is kept in fp64 (F' = F + 2 x + nn when the
-//      token joins);
+//      their row sums in fp64 (the part of x_t inside the chunk while the
+//      current state began before it);
+//   3. one wave scores the tokens in passes, a lane per token: a pass scores
+//      every token against the current state as if none restarted it (x_t
+//      from the row sums, or from the Gram row from the state's start when it
+//      began inside the chunk; |S|_F^2 as a prefix sum of 2 x + |v|^2 |k|^2),
+//      then walks the boundaries in order with the greedy merge decision
+//      (same rule and arithmetic as the greedy scan kernel): a boundary
+//      merged into the newest pair keeps the pass going, any other restarts
+//      the current state at the boundary token and the next pass begins after
+//      it;
 //   4. S_pre of the next chunk: the tokens of the chunk from the current
 //      state's start on are added (the accumulators are cleared first if the
 //      current state restarted inside the chunk).
@@ -51,10 +55,6 @@ namespace dla {
 namespace {
 
 constexpr int kSsThreads = 256;
-constexpr int kPreEntries = kChunk * (kChunk + 1) / 2;   // packed lower triangle, diagonal included
-
-// Row-prefix index of (t, s), s <= t: entry = sum of H[t][s'] over s' < s.
-__device__ __forceinline__ int pre_idx(int t, int s) { return t * (t + 1) / 2 + s; }
 
 template <typename TIO, int DK, int DV>
 struct SsSmem {
@@ -66,10 +66,8 @@ struct SsSmem {
     // K of the chunk scaled by 2^-ek in fp16 (bf16 inputs: exact while within
     // fp16's normal range of the chunk's largest element), the operand of u_t
     _Float16 kh[sizeof(TIO) == 2 ? kChunk : 1][DK + 8];
-    union {
-        float H[kChunk][kChunk + 1];  // Gram products (lower triangle)
-        double pre[kPreEntries];      // their row prefix sums
-    };
+    float H[kChunk][kChunk + 1];    // Gram products (lower triangle)
+    double rowsum[kChunk];          // sum of H[t][s] over s < t
     float upart[4][kChunk];         // partial u_t of the four waves
     float nn[kChunk];               // |v_t|^2 |k_t|^2
     float s_c[kChunk];              // scores of the chunk
@@ -340,34 +338,20 @@ __global__ __launch_bounds__(kSsThreads, 1) void k_state_score(
             for (int r = 0; r < 4; ++r) S.H[16 * tt + 4 * lg + r][16 * st + lr] = gk[r] * gv[r];
         }
         lds_barrier();
-        // ---- row prefix sums of H in fp64: four threads per row t (lanes 4t'
-        // .. 4t' + 3 of a wave), each a 16-column segment, offset by the sums
-        // of the segments before it; the rows are read whole before any
-        // thread writes the prefix array, which shares their bytes
+        // ---- row sums of H in fp64 below the diagonal: four threads per row t
+        // (lanes 4t' .. 4t' + 3 of a wave), a 16-column segment each
         {
             const int t = tid >> 2, g = tid & 3;
-            float seg[16];
-#pragma unroll
-            for (int j = 0; j < 16; ++j) seg[j] = 16 * g + j <= t ? S.H[t][16 * g + j] : 0.0f;
-            const float diag = S.H[t][t];
-            lds_barrier();
             double tot = 0.0;
 #pragma unroll
-            for (int j = 0; j < 16; ++j) tot += static_cast<double>(seg[j]);
-            double inc = tot;
-            double y = __shfl_up(inc, 1, 4);
-            if (g >= 1) inc += y;
-            y = __shfl_up(inc, 2, 4);
-            if (g >= 2) inc += y;
-            double run = __shfl_up(inc, 1, 4);
-            if (g == 0) run = 0.0;
-#pragma unroll
             for (int j = 0; j < 16; ++j)
-                if (16 * g + j <= t) {
-                    S.pre[pre_idx(t, 16 * g + j)] = run;
-                    run += static_cast<double>(seg[j]);
-                }
-            if (g == 0) S.nn[t] = diag;
+                if (16 * g + j < t) tot += static_cast<double>(S.H[t][16 * g + j]);
+            tot += __shfl_xor(tot, 1, 4);
+            tot += __shfl_xor(tot, 2, 4);
+            if (g == 0) {
+                S.rowsum[t] = tot;
+                S.nn[t] = S.H[t][t];
+            }
         }
         lds_barrier();
         // ---- 4. the scan (wave 0, lane t = token t).  A pass scores every
@@ -383,7 +367,7 @@ __global__ __launch_bounds__(kSsThreads, 1) void k_state_score(
             const int t = lane;
             const bool valid = t < nvalid;
             const double nn_t = valid ? static_cast<double>(S.nn[t]) : 0.0;
-            const double pre_tt = valid ? S.pre[pre_idx(t, t)] : 0.0;
+            const double rs_t = valid ? S.rowsum[t] : 0.0;
             double u_t = 0.0;
             if (valid && a < c0)
                 u_t = static_cast<double>(S.upart[0][t]) + S.upart[1][t] + S.upart[2][t] + S.upart[3][t];
@@ -405,13 +389,17 @@ __global__ __launch_bounds__(kSsThreads, 1) void k_state_score(
                 const bool live = valid && t >= pos;
                 double x = 0.0, d = 0.0;
                 if (live) {
-                    x = pre_tt - S.pre[pre_idx(t, lo)];
+                    if (lo == 0) {
+                        x = rs_t;
+                    } else {
+                        // the state began at chunk token lo: the Gram row from lo
+                        for (int s2 = lo; s2 < t; ++s2) x += static_cast<double>(S.H[t][s2]);
+                    }
                     if (a < c0) x += u_t;
                     d = 2.0 * x + nn_t;
                 }
-                const double dsum = wave_incl_scan(d, lane);
-                double dex = __shfl_up(dsum, 1);
-                if (lane == 0) dex = 0.0;
+                const double dsum = wave_incl_scan_dpp(d);
+                const double dex = lane_up1(dsum);
                 const double Fin = F + dsum;    // |S|_F^2 after token t joins
                 const double Fx = F + dex;      // before it
                 float sc = 0.0f;
@@ -445,7 +433,7 @@ __global__ __launch_bounds__(kSsThreads, 1) void k_state_score(
                         const int64_t I_nx = lane_down1(I);
                         const int64_t M = wave_min_i64(lane + 2 < m ? I + I_nx : INT64_MAX);
                         const int64_t qa = t >= pos ? qv : int64_t{0};
-                        const int64_t Qin = wave_incl_scan(qa, lane);
+                        const int64_t Qin = wave_incl_scan_dpp(qa);
                         const bool joins_newest = qa < Iprev && Ilast + Qin < M;
                         const uint64_t stop = bm & __ballot(!joins_newest);
                         const int bs = stop ? __builtin_ctzll(stop) : nvalid;

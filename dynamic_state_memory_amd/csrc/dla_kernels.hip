@@ -305,6 +305,57 @@ __global__ __launch_bounds__(64) void k_greedy(int T, int C, int NCH,
         }
         const int cnt = min(64, nseg - b0);
         for (int jj = 0; jj < cnt; ++jj) {
+            if (m == C && merge_rule != DLA_MERGE_DENSITY) {
+                // A full cache under the summed key: the boundary of segment j
+                // merges into the newest pair (the most recent state and its
+                // own new state) when that pair's key is below the key of the
+                // pair before it (q_j < I_{m-2}) and below every older pair's
+                // key (their minimum M, which such merges leave alone), the most
+                // recent state grown by every segment since jj.  The run of such
+                // segments is taken at once: each merges its new state away at
+                // once, so the state list keeps its shape and only the most
+                // recent state's information and count grow.
+                const int64_t Iprev = m >= 2 ? readlane_any(I, m - 2) : INT64_MAX;
+                const int64_t Ilast = readlane_any(I, m - 1);
+                const int64_t I_nx = lane_down1(I);
+                const int64_t M = wave_min_i64(lane + 2 < m ? I + I_nx : INT64_MAX);
+                const int64_t Pfirst = readlane_any(Pj, jj);
+                const bool in = lane >= jj && lane < cnt;
+                const bool joins = q0 < Iprev && Ilast + (Pj - Pfirst) + q0 < M;
+                const uint64_t stop = __ballot(in && !joins);
+                const int je = stop ? __builtin_ctzll(stop) : cnt;
+                if (je > jj) {
+                    // lane j of the run: its event (the state opened at t_j,
+                    // merged away at once: 64 + its offset in the chunk), its
+                    // merge for the schedule export, and the first event of
+                    // every chunk from the one after the previous segment's on
+                    const int tprev = static_cast<int>(dpp32_rows<0x138, 0xF>(static_cast<uint32_t>(tj)));
+                    if (in && lane < je) {
+                        const int cj = tj / kChunk;
+                        const int k = lane - jj;
+                        events[static_cast<size_t>(bh) * T + nev + k] = make_int2(tj, 64 + tj - cj * kChunk);
+                        if (ev_t_out) {
+                            ev_t_out[static_cast<size_t>(bh) * T + nmerge + k] = tj;
+                            ev_i_out[static_cast<size_t>(bh) * T + nmerge + k] = m - 1;
+                        }
+                        for (int kk = (lane == jj ? cur_chunk : tprev / kChunk) + 1; kk <= cj; ++kk)
+                            chunk_ev[static_cast<size_t>(bh) * (NCH + 1) + kk] = nev + k;
+                    }
+                    const int last_chunk = readlane_any(tj, je - 1) / kChunk;
+                    if (last_chunk != cur_chunk) {
+                        oi = lane < m ? lane : -1;
+                        cur_chunk = last_chunk;
+                    }
+                    const int64_t addI = readlane_any(Pn, je - 1) - Pfirst;
+                    const int addn = readlane_any(tn, je - 1) - readlane_any(tj, jj);
+                    if (lane == m - 1) { I += addI; n += addn; }
+                    nev += je - jj;
+                    nmerge += je - jj;
+                    jj = je;
+                    if (jj >= cnt) break;
+                }
+                // (segment jj, whose merge lands elsewhere, takes the step below)
+            }
             // segment jj of this batch, broadcast from its lane (jj is uniform)
             const int t = readlane_any(tj, jj);
             const int tnext = readlane_any(tn, jj);

@@ -249,7 +249,10 @@ __global__ __launch_bounds__(256) void k_compact(int T, int NT, const uint8_t *_
 // segment joins the most recent state.  Emits one event per boundary for the
 // prefill kernel: (token, identity of the state merged away or -1), where the
 // identity is its index among the states alive at its chunk's start, or
-// 64 + its start offset within the chunk when it was opened in that chunk.
+// 64 + its start offset within the chunk when it was opened in that chunk --
+// except for a boundary whose new state the merge joins at once to the state
+// before it (the newest pair): for the chunk kernels that is the token
+// joining the most recent state, as a token without a boundary does.
 __global__ __launch_bounds__(64) void k_greedy(int T, int C, int NCH,
                                                const int32_t *__restrict__ seg_t,
                                                const int64_t *__restrict__ seg_P,
@@ -325,21 +328,19 @@ __global__ __launch_bounds__(64) void k_greedy(int T, int C, int NCH,
                 const uint64_t stop = __ballot(in && !joins);
                 const int je = stop ? __builtin_ctzll(stop) : cnt;
                 if (je > jj) {
-                    // lane j of the run: its event (the state opened at t_j,
-                    // merged away at once: 64 + its offset in the chunk), its
-                    // merge for the schedule export, and the first event of
-                    // every chunk from the one after the previous segment's on
+                    // lane j of the run: its merge for the schedule export, and
+                    // the event offset of every chunk from the one after the
+                    // previous segment's on (a run emits no event: see below)
                     const int tprev = static_cast<int>(dpp32_rows<0x138, 0xF>(static_cast<uint32_t>(tj)));
                     if (in && lane < je) {
                         const int cj = tj / kChunk;
                         const int k = lane - jj;
-                        events[static_cast<size_t>(bh) * T + nev + k] = make_int2(tj, 64 + tj - cj * kChunk);
                         if (ev_t_out) {
                             ev_t_out[static_cast<size_t>(bh) * T + nmerge + k] = tj;
                             ev_i_out[static_cast<size_t>(bh) * T + nmerge + k] = m - 1;
                         }
                         for (int kk = (lane == jj ? cur_chunk : tprev / kChunk) + 1; kk <= cj; ++kk)
-                            chunk_ev[static_cast<size_t>(bh) * (NCH + 1) + kk] = nev + k;
+                            chunk_ev[static_cast<size_t>(bh) * (NCH + 1) + kk] = nev;
                     }
                     const int last_chunk = readlane_any(tj, je - 1) / kChunk;
                     if (last_chunk != cur_chunk) {
@@ -349,7 +350,6 @@ __global__ __launch_bounds__(64) void k_greedy(int T, int C, int NCH,
                     const int64_t addI = readlane_any(Pn, je - 1) - Pfirst;
                     const int addn = readlane_any(tn, je - 1) - readlane_any(tj, jj);
                     if (lane == m - 1) { I += addI; n += addn; }
-                    nev += je - jj;
                     nmerge += je - jj;
                     jj = je;
                     if (jj >= cnt) break;
@@ -398,14 +398,18 @@ __global__ __launch_bounds__(64) void k_greedy(int T, int C, int NCH,
                 if (lane == istar) { I += pI; n += pn; }
                 else if (lane > istar && lane < m) { I = pI; n = pn; st = pst; oi = poi; }
             }
+            // (a new state merged at once into the state before it -- the
+            // newest pair -- is the token joining the most recent state: the
+            // chunk kernels get no event for it)
+            const bool joined = istar >= 0 && istar == m - 1;
             if (lane == 0) {
-                events[static_cast<size_t>(bh) * T + nev] = make_int2(t, dead);
+                if (!joined) events[static_cast<size_t>(bh) * T + nev] = make_int2(t, dead);
                 if (ev_t_out && istar >= 0) {
                     ev_t_out[static_cast<size_t>(bh) * T + nmerge] = t;
                     ev_i_out[static_cast<size_t>(bh) * T + nmerge] = istar;
                 }
             }
-            ++nev;
+            if (!joined) ++nev;
             if (istar >= 0) ++nmerge;
             if (lane == m - 1) { I += remI; n += remn; }
         }

@@ -257,6 +257,21 @@ def test_literal_noise_reading_every_token_opens(prefill_path):
     assert r["b"].mean() > 0.99 and r["n_ev"].min() >= 777 - cfg.C - 5
 
 
+@pytest.mark.parametrize("rule", ["sum", "density"])
+@pytest.mark.parametrize("C", [1, 2, 3, 4])
+def test_every_token_a_boundary_small_capacity(C, rule, prefill_path):
+    """Every token opens a state (literal key noise) at capacities 1 to 4: the
+    greedy scan's runs of merges into the newest pair at their edge cases (one
+    or two states, no older pair), across chunks and 64-segment batches, and
+    the boundaries whose new state is merged at once (no chunk-kernel event);
+    schedule bit-exact, outputs and final states within their gates."""
+    torch_mod()
+    cfg = dataclasses.replace(workloads.CONFIGS["gdn_1p3b_t32k_bf16"], C=C)
+    d = workloads.prefill_inputs(cfg, reading="literal", streams=[0, 1], T=700)
+    r = _full_check(d, C, cfg.tau, "bf16", f"literal C={C} {rule}", merge_rule=rule)
+    assert r["b"].mean() > 0.99 and r["n_ev"].min() >= 700 - C - 5
+
+
 @pytest.mark.parametrize("tau,C", [(-1.0, 64), (-1.0, 5), (3.0, 8), (0.3, 1), (0.9, 63), (-1.0, 32),
                                    (0.3, 17)])
 def test_threshold_and_capacity_extremes(tau, C):

@@ -78,7 +78,8 @@ def _first_unpinned(r, tau, C, merge_rule):
                     else:
                         keys = [Fraction(I[j] + I[j + 1], n[j] + n[j + 1]) for j in range(len(I) - 1)]
                     order = sorted(range(len(keys)), key=lambda j: (keys[j], j))
-                    if float(keys[order[1]] - keys[order[0]]) <= MARGIN * float(keys[order[0]]):
+                    # (with C = 1 there is one pair: no tie)
+                    if len(keys) > 1 and float(keys[order[1]] - keys[order[0]]) <= MARGIN * float(keys[order[0]]):
                         out[i] = t
                         break
                     del starts[order[0] + 1]
@@ -163,6 +164,11 @@ CASES = [
     ("long_t131k_bf16", 64, 128, 4, 999, (15,), "sum", "f32"),
     ("long_t131k_bf16", 256, 64, 6, 777, (18,), "density", "f32"),
     ("gdn_1p3b_t32k_bf16", 64, 256, 7, 640, (20,), "sum", "f32"),
+    # capacities 1 to 3: the scan's runs of merges into the newest pair with
+    # one state (no pair before it) and two (no older pair)
+    ("long_t131k_bf16", 128, 128, 1, 900, (12,), "sum", "f32"),
+    ("mamba2_780m_bf16", 128, 64, 2, 1100, (15,), "sum", "f32"),
+    ("mamba2_780m_bf16", 128, 64, 3, 1000, (10,), "sum", "f32"),
 ]
 
 

@@ -54,7 +54,29 @@ namespace dla {
 
 namespace {
 
-constexpr int kSsThreads = 256;
+constexpr int kSsMaxWaves = 8;
+
+// Waves per block: eight (two per SIMD, 256 registers each) where the
+// per-wave state fits, four (512 registers each) for the larger shapes.
+template <typename TIO, int DK, int DV>
+constexpr int ss_waves()
+{
+    return (sizeof(TIO) == 2 ? (DK * DV <= 128 * 64 || (DK == 256 && DV == 64)) : DK * DV <= 64 * 128) ? 8 : 4;
+}
+
+// The d_v x d_k tiles of S_pre over the NW waves: JW waves along d_k, IW along
+// d_v; wave w holds the tiles (d_v tile iw + IW i, d_k tile jw + JW j) with
+// jw = w % JW, iw = w / JW.  Eight waves split d_k first, so that each wave
+// reads the key columns of its own d_k tiles only; four waves (the larger
+// shapes, whose registers are the limit) split d_v.
+template <int DK, int DV, int NW>
+struct SsSplit {
+    static constexpr int NJT = DK / 16, NIT = DV / 16;
+    static constexpr int JW = NW == 4 ? 1 : (NJT < NW ? NJT : NW);
+    static constexpr int IW = NW / JW;
+    static constexpr int JPW = NJT / JW, IPW = NIT / IW;
+    static_assert(JW * IW == NW && JPW * JW == NJT && IPW * IW == NIT, "whole tiles per wave");
+};
 
 template <typename TIO, int DK, int DV>
 struct SsSmem {
@@ -68,12 +90,12 @@ struct SsSmem {
     _Float16 kh[sizeof(TIO) == 2 ? kChunk : 1][DK + 8];
     float H[kChunk][kChunk + 1];    // Gram products (lower triangle)
     double rowsum[kChunk];          // sum of H[t][s] over s < t
-    float upart[4][kChunk];         // partial u_t of the four waves
+    float upart[kSsMaxWaves][kChunk];   // partial u_t of the waves
     float nn[kChunk];               // |v_t|^2 |k_t|^2
     float s_c[kChunk];              // scores of the chunk
     uint8_t f_c[kChunk];            // boundary flags of the chunk
-    float red[4], kred[4];
-    double dred[4];
+    float red[kSsMaxWaves], kred[kSsMaxWaves];
+    double dred[kSsMaxWaves];
     int64_t a_s;                    // start of the current state after the chunk (from the scan)
 };
 
@@ -86,18 +108,18 @@ __device__ __forceinline__ void split16(float x, int e, _Float16 &hi, _Float16 &
 }
 
 template <typename TIO, int DK, int DV>
-__global__ __launch_bounds__(kSsThreads, 1) void k_state_score(
+__global__ __launch_bounds__((64 * ss_waves<TIO, DK, DV>()), 1) void k_state_score(
     const TIO *__restrict__ K, const TIO *__restrict__ V, int T, float tau, int C, int merge_rule,
     const float *__restrict__ states, const float *__restrict__ active, int state_bf16,
     const uint8_t *__restrict__ meta_base, size_t meta_stride,
     float *__restrict__ s_out, int64_t *__restrict__ qs_out, uint8_t *__restrict__ flag_out,
     int32_t *__restrict__ tile_cnt, int64_t *__restrict__ tile_sum, int NT)
 {
-    constexpr int NIT = DV / 16;                 // 16-row tiles of d_v
-    constexpr int NJT = DK / 16;                 // 16-column tiles of d_k
-    constexpr int IPW = NIT / 4;                 // d_v tiles per wave: wave + 4 ii
+    constexpr int NW = ss_waves<TIO, DK, DV>();
+    constexpr int kSsThreads = 64 * NW;
+    typedef SsSplit<DK, DV, NW> Sp;
+    constexpr int IPW = Sp::IPW, JPW = Sp::JPW, IW = Sp::IW, JW = Sp::JW;
     constexpr bool kF32 = sizeof(TIO) == 4;
-    static_assert(NIT % 4 == 0, "d_v tiles spread evenly over the waves");
     extern __shared__ __align__(16) unsigned char smem_raw[];
     typedef SsSmem<TIO, DK, DV> Smem;
     Smem &S = *reinterpret_cast<Smem *>(smem_raw);
@@ -105,6 +127,7 @@ __global__ __launch_bounds__(kSsThreads, 1) void k_state_score(
     const int bh = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 15, lg = lane >> 4;
+    const int jw = wave % JW, iw = wave / JW;
     const int NCH = (T + kChunk - 1) / kChunk;
     const size_t tok0 = static_cast<size_t>(bh) * T;
     const double D = static_cast<double>(DK) * DV;
@@ -122,12 +145,13 @@ __global__ __launch_bounds__(kSsThreads, 1) void k_state_score(
         n = reinterpret_cast<const int32_t *>(meta + kOffCount)[lane];
     }
     int m = m_init;
-    // S_pre^T accumulators: tile (jt, it) holds S[16 it + lr][16 jt + 4 lg + r]
-    floatx4 acc[IPW][NJT];
+    // S_pre accumulators: acc[i][j], the tile of d_v tile it = iw + IW i and
+    // d_k tile jt = jw + JW j, holds S[16 it + lr][16 jt + 4 lg + r]
+    floatx4 acc[IPW][JPW];
 #pragma unroll
-    for (int ii = 0; ii < IPW; ++ii)
+    for (int i = 0; i < IPW; ++i)
 #pragma unroll
-        for (int jt = 0; jt < NJT; ++jt) acc[ii][jt] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < JPW; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
     double F = 0.0;          // |S_cur|_F^2 (wave 0)
     int64_t a = 0;           // start of the current state (absolute token of this call; < 0: before it)
     if (m_init > 0) {
@@ -137,25 +161,27 @@ __global__ __launch_bounds__(kSsThreads, 1) void k_state_score(
                                       : states + (static_cast<size_t>(bh) * C + slot) * DV * DK;
         double sqd = 0.0;
 #pragma unroll
-        for (int ii = 0; ii < IPW; ++ii)
+        for (int i = 0; i < IPW; ++i)
 #pragma unroll
-            for (int jt = 0; jt < NJT; ++jt) {
-                const int i = 16 * (wave + 4 * ii) + lr;
-                const float4 x = *reinterpret_cast<const float4 *>(src + static_cast<size_t>(i) * DK + 16 * jt + 4 * lg);
-                acc[ii][jt] = floatx4{x.x, x.y, x.z, x.w};
+            for (int j = 0; j < JPW; ++j) {
+                const int row = 16 * (iw + IW * i) + lr, jt = jw + JW * j;
+                const float4 x = *reinterpret_cast<const float4 *>(src + static_cast<size_t>(row) * DK + 16 * jt + 4 * lg);
+                acc[i][j] = floatx4{x.x, x.y, x.z, x.w};
                 sqd += static_cast<double>(x.x) * x.x + static_cast<double>(x.y) * x.y +
                        static_cast<double>(x.z) * x.z + static_cast<double>(x.w) * x.w;
             }
         sqd = wave_sum(sqd);
         if (lane == 0) S.dred[wave] = sqd;
         __syncthreads();
-        F = S.dred[0] + S.dred[1] + S.dred[2] + S.dred[3];
+        F = 0.0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) F += S.dred[w];
         a = -1;
     }
     int32_t tcnt = 0;
     int64_t tsum = 0;
     // the chunk's K and V rows as 16-byte pieces: lane l holds token l's
-    // pieces wave + 4 i (so that the transposed LDS writes of a wave touch 64
+    // pieces wave + 8 i (so that the transposed LDS writes of a wave touch 64
     // consecutive tokens of one row of K^T or V^T)
     constexpr int EPV = 16 / sizeof(TIO);
     constexpr int NKP = kChunk * DK / EPV / kSsThreads;
@@ -170,9 +196,11 @@ __global__ __launch_bounds__(kSsThreads, 1) void k_state_score(
         // staged: a select here would wait for the load)
         const size_t row = tok0 + cbase + min(lane, nv - 1);
 #pragma unroll
-        for (int i = 0; i < NKP; ++i) kq[i] = *reinterpret_cast<const uint4 *>(K + row * DK + EPV * (wave + 4 * i));
+        for (int i = 0; i < NKP; ++i)
+            kq[i] = *reinterpret_cast<const uint4 *>(K + row * DK + EPV * (wave + NW * i));
 #pragma unroll
-        for (int i = 0; i < NVP; ++i) vq[i] = *reinterpret_cast<const uint4 *>(V + row * DV + EPV * (wave + 4 * i));
+        for (int i = 0; i < NVP; ++i)
+            vq[i] = *reinterpret_cast<const uint4 *>(V + row * DV + EPV * (wave + NW * i));
     };
     if constexpr (kPrefetch) load_chunk(0, kp, vp);
 
@@ -196,7 +224,7 @@ __global__ __launch_bounds__(kSsThreads, 1) void k_state_score(
         }
 #pragma unroll
         for (int i = 0; i < NKP; ++i) {
-            const int r = lane, cv = EPV * (wave + 4 * i);
+            const int r = lane, cv = EPV * (wave + NW * i);
             *reinterpret_cast<uint4 *>(&S.kr[r][cv]) = kp[i];
             const TIO *e = reinterpret_cast<const TIO *>(&kp[i]);
 #pragma unroll
@@ -207,7 +235,7 @@ __global__ __launch_bounds__(kSsThreads, 1) void k_state_score(
         }
 #pragma unroll
         for (int i = 0; i < NVP; ++i) {
-            const int r = lane, cv = EPV * (wave + 4 * i);
+            const int r = lane, cv = EPV * (wave + NW * i);
             *reinterpret_cast<uint4 *>(&S.vr[r][cv]) = vp[i];
             const TIO *e = reinterpret_cast<const TIO *>(&vp[i]);
 #pragma unroll
@@ -219,11 +247,11 @@ __global__ __launch_bounds__(kSsThreads, 1) void k_state_score(
         // scale of S_pre's fp16 halves and of K's
         float smax = 0.0f;
 #pragma unroll
-        for (int ii = 0; ii < IPW; ++ii)
+        for (int i = 0; i < IPW; ++i)
 #pragma unroll
-            for (int jt = 0; jt < NJT; ++jt)
+            for (int j = 0; j < JPW; ++j)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) smax = fmaxf(smax, fabsf(acc[ii][jt][r]));
+                for (int r = 0; r < 4; ++r) smax = fmaxf(smax, fabsf(acc[i][j][r]));
         smax = wave_max(smax);
         kmax = wave_max(kmax);
         if (lane == 0) {
@@ -231,14 +259,23 @@ __global__ __launch_bounds__(kSsThreads, 1) void k_state_score(
             S.kred[wave] = kmax;
         }
         lds_barrier();
-        const int es = f16_exponent(fmaxf(fmaxf(S.red[0], S.red[1]), fmaxf(S.red[2], S.red[3])));
-        const int ek = f16_exponent(fmaxf(fmaxf(S.kred[0], S.kred[1]), fmaxf(S.kred[2], S.kred[3])));
+        float smx = 0.0f, kmx = 0.0f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            smx = fmaxf(smx, S.red[w]);
+            kmx = fmaxf(kmx, S.kred[w]);
+        }
+        const int es = f16_exponent(smx);
+        const int ek = f16_exponent(kmx);
         const bool pre_live = a < c0;   // the current state began before this chunk
 
         // ---- 2. u_t = v_t^T S_pre k_t (wave w: its d_v tiles, every token)
         if (pre_live) {
-            if constexpr (!kF32) {
-                // (every wave reads every token's K: converted once, by all threads)
+            // (with the d_v split every wave reads every token's K: converted
+            // to fp16 once, by all threads; with the d_k split each wave
+            // converts its own columns in registers below)
+            constexpr bool kShared = !kF32 && JW == 1;
+            if constexpr (kShared) {
                 for (int idx = tid; idx < kChunk * DK / 8; idx += kSsThreads) {
                     const int r = idx / (DK / 8), cv = (idx % (DK / 8)) * 8;
                     const uint4 x = *reinterpret_cast<const uint4 *>(&S.kr[r][cv]);
@@ -250,64 +287,71 @@ __global__ __launch_bounds__(kSsThreads, 1) void k_state_score(
                 }
                 lds_barrier();
             }
-            floatx4 Y[IPW][4];
+            // per d_v tile of the wave: Y = S K^T over the wave's d_k tiles
+            // (16x16x16 products: the accumulator tile is the first operand as
+            // it stands, K's four columns of the tile the second), then the
+            // dot product with v_t of the tile's rows
+            typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+            // K of token 16 tt + lr at columns 16 jt + 4 lg + r of the wave's
+            // d_k tiles (fp16 halves for fp32 io), the same for every d_v tile
+            f16x4 khf[JPW][4], klf[JPW][4];
 #pragma unroll
-            for (int ii = 0; ii < IPW; ++ii)
-#pragma unroll
-                for (int tt = 0; tt < 4; ++tt) Y[ii][tt] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int jp = 0; jp < NJT / 2; ++jp) {
-                // S rows 16 it + lr at columns {32 jp + 4 lg + r, 32 jp + 16 + 4 lg + r}
-                f16x8 sh[IPW], sl[IPW];
-#pragma unroll
-                for (int ii = 0; ii < IPW; ++ii)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        _Float16 h, l;
-                        split16(acc[ii][2 * jp][r], es, h, l);
-                        sh[ii][r] = h; sl[ii][r] = l;
-                        split16(acc[ii][2 * jp + 1][r], es, h, l);
-                        sh[ii][4 + r] = h; sl[ii][4 + r] = l;
-                    }
+            for (int j = 0; j < JPW; ++j)
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt) {
-                    // K of token 16 tt + lr at the same columns
-                    f16x8 kh, kl;
-                    if constexpr (kF32) {
+                    const int jt = jw + JW * j;
+                    if constexpr (kShared) {
+                        khf[j][tt] = *reinterpret_cast<const f16x4 *>(&S.kh[16 * tt + lr][16 * jt + 4 * lg]);
+                        klf[j][tt] = khf[j][tt];
+                    } else {
+                        TIO kv[4];
+                        __builtin_memcpy(kv, &S.kr[16 * tt + lr][16 * jt + 4 * lg], sizeof(kv));
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
                             _Float16 h, l;
-                            split16(to_f(S.kr[16 * tt + lr][32 * jp + 4 * lg + r]), ek, h, l);
-                            kh[r] = h; kl[r] = l;
-                            split16(to_f(S.kr[16 * tt + lr][32 * jp + 16 + 4 * lg + r]), ek, h, l);
-                            kh[4 + r] = h; kl[4 + r] = l;
+                            split16(to_f(kv[r]), ek, h, l);
+                            khf[j][tt][r] = h; klf[j][tt][r] = l;
                         }
-                    } else {
-                        typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-                        const f16x4 a0 = *reinterpret_cast<const f16x4 *>(&S.kh[16 * tt + lr][32 * jp + 4 * lg]);
-                        const f16x4 a1 = *reinterpret_cast<const f16x4 *>(&S.kh[16 * tt + lr][32 * jp + 16 + 4 * lg]);
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) { kh[r] = a0[r]; kh[4 + r] = a1[r]; }
                     }
-#pragma unroll
-                    for (int ii = 0; ii < IPW; ++ii) {
-                        Y[ii][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(sh[ii], kh, Y[ii][tt], 0, 0, 0);
-                        Y[ii][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(sl[ii], kh, Y[ii][tt], 0, 0, 0);
-                        if constexpr (kF32)
-                            Y[ii][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(sh[ii], kl, Y[ii][tt], 0, 0, 0);
-                    }
-                    (void)kl;
                 }
+            float xacc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int i = 0; i < IPW; ++i) {
+                const int it = iw + IW * i;
+                floatx4 Y[4];
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) Y[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int j = 0; j < JPW; ++j) {
+                    f16x4 sh, sl;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        _Float16 h, l;
+                        split16(acc[i][j][r], es, h, l);
+                        sh[r] = h; sl[r] = l;
+                    }
+#pragma unroll
+                    for (int tt = 0; tt < 4; ++tt) {
+                        Y[tt] = __builtin_amdgcn_mfma_f32_16x16x16f16(sh, khf[j][tt], Y[tt], 0, 0, 0);
+                        Y[tt] = __builtin_amdgcn_mfma_f32_16x16x16f16(sl, khf[j][tt], Y[tt], 0, 0, 0);
+                        if constexpr (kF32) Y[tt] = __builtin_amdgcn_mfma_f32_16x16x16f16(sh, klf[j][tt], Y[tt], 0, 0, 0);
+                    }
+                }
+                // Y[tt] holds (S K^T) at rows 16 it + 4 lg + r, token 16 tt + lr
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) {
+                    TIO vv[4];
+                    __builtin_memcpy(vv, &S.vr[16 * tt + lr][16 * it + 4 * lg], sizeof(vv));
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) xacc[tt] += to_f(vv[r]) * Y[tt][r];
+                }
+                // (one d_v tile at a time: the next tile's loads are not
+                // hoisted over this one, which would keep them all live)
+                asm volatile("" ::: "memory");
             }
-            // Y[ii][tt] holds (S K^T) at rows 16 it + 4 lg + r, token 16 tt + lr
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt) {
-                float x = 0.0f;
-#pragma unroll
-                for (int ii = 0; ii < IPW; ++ii)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        x += to_f(S.vr[16 * tt + lr][16 * (wave + 4 * ii) + 4 * lg + r]) * Y[ii][tt][r];
+                float x = xacc[tt];
                 x += __shfl_xor(x, 16);
                 x += __shfl_xor(x, 32);
                 if (lg == 0) S.upart[wave][16 * tt + lr] = ldexpf(x, es + ek);
@@ -316,7 +360,7 @@ __global__ __launch_bounds__(kSsThreads, 1) void k_state_score(
             S.upart[wave][lane] = 0.0f;
         }
         // ---- 3. Gram products H = (V V^T) o (K K^T), lower-triangle tiles
-        for (int tile = wave; tile < 10; tile += 4) {
+        for (int tile = wave; tile < 10; tile += NW) {
             int tt = 0, st = tile;
             while (st > tt) { st -= tt + 1; ++tt; }   // tile -> (tt, st), st <= tt
             floatx4 gk = floatx4{0.f, 0.f, 0.f, 0.f}, gv = gk;
@@ -338,16 +382,17 @@ __global__ __launch_bounds__(kSsThreads, 1) void k_state_score(
             for (int r = 0; r < 4; ++r) S.H[16 * tt + 4 * lg + r][16 * st + lr] = gk[r] * gv[r];
         }
         lds_barrier();
-        // ---- row sums of H in fp64 below the diagonal: four threads per row t
-        // (lanes 4t' .. 4t' + 3 of a wave), a 16-column segment each
+        // ---- row sums of H in fp64 below the diagonal: NW threads per row t
+        // (adjacent lanes of a wave), a segment of 64 / NW columns each
         {
-            const int t = tid >> 2, g = tid & 3;
+            constexpr int SEG = kChunk / NW;
+            const int t = tid / NW, g = tid % NW;
             double tot = 0.0;
 #pragma unroll
-            for (int j = 0; j < 16; ++j)
-                if (16 * g + j < t) tot += static_cast<double>(S.H[t][16 * g + j]);
-            tot += __shfl_xor(tot, 1, 4);
-            tot += __shfl_xor(tot, 2, 4);
+            for (int j = 0; j < SEG; ++j)
+                if (SEG * g + j < t) tot += static_cast<double>(S.H[t][SEG * g + j]);
+#pragma unroll
+            for (int o = 1; o < NW; o <<= 1) tot += __shfl_xor(tot, o, NW);
             if (g == 0) {
                 S.rowsum[t] = tot;
                 S.nn[t] = S.H[t][t];
@@ -369,8 +414,10 @@ __global__ __launch_bounds__(kSsThreads, 1) void k_state_score(
             const double nn_t = valid ? static_cast<double>(S.nn[t]) : 0.0;
             const double rs_t = valid ? S.rowsum[t] : 0.0;
             double u_t = 0.0;
-            if (valid && a < c0)
-                u_t = static_cast<double>(S.upart[0][t]) + S.upart[1][t] + S.upart[2][t] + S.upart[3][t];
+            if (valid && a < c0) {
+#pragma unroll
+                for (int w = 0; w < NW; ++w) u_t += static_cast<double>(S.upart[w][t]);
+            }
             float sc_fin = 0.0f;            // the token's final score and boundary flag
             bool bnd_fin = false;
             int pos = 0;
@@ -536,23 +583,23 @@ __global__ __launch_bounds__(kSsThreads, 1) void k_state_score(
             const int lo = a > c0 ? static_cast<int>(a - c0) : 0;
             if (a >= c0) {
 #pragma unroll
-                for (int ii = 0; ii < IPW; ++ii)
+                for (int i = 0; i < IPW; ++i)
 #pragma unroll
-                    for (int jt = 0; jt < NJT; ++jt) acc[ii][jt] = floatx4{0.f, 0.f, 0.f, 0.f};
+                    for (int j = 0; j < JPW; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
             }
 #pragma unroll
             for (int ks = 0; ks < kChunk / 32; ++ks) {
                 if (32 * ks + 32 <= lo) continue;
 #pragma unroll
-                for (int jt = 0; jt < NJT; ++jt) {
+                for (int j = 0; j < JPW; ++j) {
                     Frag<TIO> x;
-                    load_frag(x, &S.kt[16 * jt + lr][32 * ks + 8 * lg]);
+                    load_frag(x, &S.kt[16 * (jw + JW * j) + lr][32 * ks + 8 * lg]);
                     mask_frag(x, 32 * ks + 8 * lg, lo, kChunk);
 #pragma unroll
-                    for (int ii = 0; ii < IPW; ++ii) {
+                    for (int i = 0; i < IPW; ++i) {
                         Frag<TIO> y;
-                        load_frag(y, &S.vt[16 * (wave + 4 * ii) + lr][32 * ks + 8 * lg]);
-                        mma32(acc[ii][jt], x, y);
+                        load_frag(y, &S.vt[16 * (iw + IW * i) + lr][32 * ks + 8 * lg]);
+                        mma32(acc[i][j], x, y);
                     }
                 }
             }
@@ -575,7 +622,7 @@ static hipError_t ss_launch(const PrefillArgs &a, hipStream_t stream)
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    hipLaunchKernelGGL((k_state_score<TIO, DK, DV>), dim3(BH), dim3(kSsThreads), smem, stream,
+    hipLaunchKernelGGL((k_state_score<TIO, DK, DV>), dim3(BH), dim3((64 * ss_waves<TIO, DK, DV>())), smem, stream,
                        static_cast<const TIO *>(a.k), static_cast<const TIO *>(a.v), T, a.tau, a.g.C, a.merge_rule,
                        a.states, a.active, a.g.state_bf16, a.meta, a.g.meta_stride, a.ws.s, a.ws.qs, a.ws.flag,
                        a.ws.tile_cnt, a.ws.tile_sum, NT);

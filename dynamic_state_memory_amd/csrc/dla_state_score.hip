@@ -20,10 +20,13 @@
 // The current state is therefore always a suffix [a, t) of the stream.  One
 // block per stream sweeps the 64-token chunks in order, with the part of the
 // current state that precedes the chunk, S_pre = sum over [a, c0) of v k^T,
-// held as fp32 MFMA accumulators:
+// held as fp32 MFMA accumulators, its 16 x 16 tiles spread over the block's
+// waves (eight waves by key columns, or four by value rows for the larger
+// shapes):
 //   1. u_t = v_t^T S_pre k_t for the chunk's tokens: Y = S_pre K^T on MFMA,
 //      S_pre split into two fp16 halves (22 significant bits) and K exact in
-//      fp16 (bf16 inputs) or split as well (fp32 inputs), then u_t = v_t . Y_t;
+//      fp16 (bf16 inputs) or split as well (fp32 inputs), then u_t = v_t . Y_t
+//      (each wave's part over its tiles, summed in the scan);
 //   2. the chunk's Gram products H[t][s] = (v_t . v_s)(k_t . k_s) on MFMA and
 //      their row sums in fp64 (the part of x_t inside the chunk while the
 //      current state began before it);
@@ -33,9 +36,9 @@
 //      began inside the chunk; |S|_F^2 as a prefix sum of 2 x + |v|^2 |k|^2),
 //      then walks the boundaries in order with the greedy merge decision
 //      (same rule and arithmetic as the greedy scan kernel): a boundary
-//      merged into the newest pair keeps the pass going, any other restarts
-//      the current state at the boundary token and the next pass begins after
-//      it;
+//      merged into the newest pair keeps the pass going (a run of them is
+//      taken at once), any other restarts the current state at the boundary
+//      token and the next pass begins after it;
 //   4. S_pre of the next chunk: the tokens of the chunk from the current
 //      state's start on are added (the accumulators are cleared first if the
 //      current state restarted inside the chunk).

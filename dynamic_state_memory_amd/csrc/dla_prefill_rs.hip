@@ -323,9 +323,8 @@ static_assert(sizeof(RsStageA<128>) == rs_rec_a_bytes(128) && sizeof(RsStageB<12
 template <int DK, int DVT, int CMAX>
 struct RsSmem {
     __bf16 vt[DVT][kChunk + 8];                  // V slice of the chunk, transposed
-    // closed-state read weights by physical slot (owner wave's rows); in a
-    // chunk with events, after the read, the active state passes through it
-    float W[CMAX < 32 ? 32 : CMAX][kChunk];
+    // in a chunk with events, after the read, the active state passes through it
+    floatx4 abuf[(DK / 16) * (DVT / 16) * 64];
     floatx4 ored[kRsWaves][kChunk / 16][DVT / 16][64];  // partial reads: wave, row tile, column tile, lane
     int32_t order[kMaxC];       // physical slot of each live state, oldest first
     int32_t new_order[kMaxC];
@@ -340,7 +339,8 @@ struct RsSmem {
     // read weights of physical slot p: row jrow[p] of the chunk's weight table
     // (the chronological index of its state) times wsc[p] = 2^(state
     // exponent); 0 for a slot without a closed state (rewritten after every
-    // chunk with events)
+    // chunk with events, when each owner wave copies its slots' values into
+    // registers)
     int32_t jrow[CMAX];
     float wsc[CMAX];
     int32_t nev;                // events of the chunk
@@ -362,6 +362,16 @@ __device__ __forceinline__ void load_to_lds16(const void *g, void *lds_wave)
 }
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// A constant made in registers where it is used: with the register file full
+// the compiler would otherwise keep such a value in scratch memory and reload
+// it, and the reload waits for every vector memory load in flight (the loads
+// of the next chunk's operands included).
+__device__ __forceinline__ int fresh_i32(int v)
+{
+    asm volatile("" : "+v"(v));
+    return v;
+}
 
 // base (the same for the whole wave) plus a per-lane byte offset: the form
 // the global instructions take as an SGPR base and a 32-bit VGPR offset.  The
@@ -407,7 +417,8 @@ __device__ __forceinline__ void stage_b(RsStageB<DK> &Y, const uint8_t *rec, siz
 // The closed-state part of the inter-chunk read over the wave's first NP slot
 // pairs: one 16-token row tile at a time (a quarter of the query fragments
 // live), two independent product chains per pair, each product weighted per
-// token with the slot's read weights (row NW r + wave of W).  Straight-line
+// token with the slot's read weight: row wrow[r] of the chunk's weight table
+// times wscl[r] (0 for a slot without a closed state).  Straight-line
 // code: the products of one pair overlap the weighting of the previous one.
 // The products are formed transposed, state fragment times query fragment
 // (the two operand layouts of the 16x16x32 product are the same), so lane
@@ -416,7 +427,7 @@ __device__ __forceinline__ void stage_b(RsStageB<DK> &Y, const uint8_t *rec, siz
 template <int DK, int DVT, int SPW, int NP>
 __device__ __forceinline__ void rs_read_closed(floatx4 (&Oi)[kChunk / 16][DVT / 16],
                                                const Frag<_Float16> (&stk)[SPW][DK / 32][DVT / 16],
-                                               const RsStageA<DK> &X, const float (*W)[kChunk], int wave, int lane,
+                                               const RsStageA<DK> &X, const int (&wrow)[SPW], const float (&wscl)[SPW], int wave, int lane,
                                                int lr)
 {
     constexpr int KS = DK / 32;
@@ -443,8 +454,8 @@ __device__ __forceinline__ void rs_read_closed(floatx4 (&Oi)[kChunk / 16][DVT / 
                     mma32(P0[nt], stk[r2][ks][nt], qf[ks]);
                     mma32(P1[nt], stk[r2 + 1][ks][nt], qf[ks]);
                 }
-            const float w0 = W[NW * r2 + wave][(kChunk / 16) * lr + mt];
-            const float w1 = W[NW * (r2 + 1) + wave][(kChunk / 16) * lr + mt];
+            const float w0 = static_cast<float>(X.wr[wrow[r2]][(kChunk / 16) * lr + mt]) * wscl[r2];
+            const float w1 = static_cast<float>(X.wr[wrow[r2 + 1]][(kChunk / 16) * lr + mt]) * wscl[r2 + 1];
 #pragma unroll
             for (int nt = 0; nt < NTV; ++nt)
 #pragma unroll
@@ -459,6 +470,8 @@ struct RsCarry {
     Frag<_Float16> stk[SPW][DK / 32][DVT / 16];  // closed states of the wave's slots (fp16, normalised)
     floatx4 am[DVT / 16][2];                     // active state, d_k rows 32 kb .. 32 kb + 31 (fp32)
     Frag<_Float16> af[DVT / 16];                 // its fp16 operand copy
+    int wrow[SPW];                               // read-weight rows of the wave's slots (uniform)
+    float wscl[SPW];                             // and their scales (uniform)
     u32x4 vnext;                                 // next chunk's V piece
     int2 evnext;                                 // event lane of the next chunk's window (wave 0)
     int ea;                                      // exponent of this wave's active-state operand
@@ -580,24 +593,6 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
 #pragma unroll
         for (int e = 0; e < 8; ++e) S.vt[vc + e][vr] = ve[e];
     }
-    // read weights: closed states by slot, from the row of their
-    // chronological index (wsc is 0 for a slot without a closed state); the
-    // active state is the most recent one (each wave writes and reads only
-    // its own rows)
-    // (every load before the first store: the stores into S.W could alias the
-    // row indices and scales as far as the compiler knows, so interleaving
-    // them would serialise the loads)
-    int wrow[SPW];
-    float wscl[SPW], wv[SPW];
-#pragma unroll
-    for (int r = 0; r < SPW; ++r) {
-        wrow[r] = S.jrow[NW * r + wave];
-        wscl[r] = S.wsc[NW * r + wave];
-    }
-#pragma unroll
-    for (int r = 0; r < SPW; ++r) wv[r] = static_cast<float>(X.wr[wrow[r]][lane]) * wscl[r];
-#pragma unroll
-    for (int r = 0; r < SPW; ++r) S.W[NW * r + wave][lane] = wv[r];
     // ---- inter-chunk read: closed states from registers, then the active state
     floatx4 Oi[MT][NTV];
 #pragma unroll
@@ -621,10 +616,10 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
     __builtin_amdgcn_s_setprio(0);
     switch (npair) {
     case 0: break;
-    case 1: rs_read_closed<DK, DVT, SPW, 1>(Oi, stk, X, S.W, wave, lane, lr); break;
-    case 2: rs_read_closed<DK, DVT, SPW, (SPW >= 4 ? 2 : 1)>(Oi, stk, X, S.W, wave, lane, lr); break;
-    case 3: rs_read_closed<DK, DVT, SPW, (SPW >= 6 ? 3 : 1)>(Oi, stk, X, S.W, wave, lane, lr); break;
-    default: rs_read_closed<DK, DVT, SPW, SPW / 2>(Oi, stk, X, S.W, wave, lane, lr); break;
+    case 1: rs_read_closed<DK, DVT, SPW, 1>(Oi, stk, X, c.wrow, c.wscl, wave, lane, lr); break;
+    case 2: rs_read_closed<DK, DVT, SPW, (SPW >= 4 ? 2 : 1)>(Oi, stk, X, c.wrow, c.wscl, wave, lane, lr); break;
+    case 3: rs_read_closed<DK, DVT, SPW, (SPW >= 6 ? 3 : 1)>(Oi, stk, X, c.wrow, c.wscl, wave, lane, lr); break;
+    default: rs_read_closed<DK, DVT, SPW, SPW / 2>(Oi, stk, X, c.wrow, c.wscl, wave, lane, lr); break;
     }
     __builtin_amdgcn_s_setprio(2);
     if (c.act >= 0 && act_wave) {
@@ -659,14 +654,17 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
     if (more) {
         stage_a<DK>(X, A.rec, cb + (virt ? 0 : 1), tid, wave);
         const int c0n = c0 + kChunk;
-        c.vnext = u32x4{0u, 0u, 0u, 0u};
+        {
+            const uint32_t z = static_cast<uint32_t>(fresh_i32(0));
+            c.vnext = u32x4{z, z, z, z};
+        }
         if (A.v_mover && vr < min(kChunk, T - c0n))
             c.vnext = *at_bytes(reinterpret_cast<const u32x4 *>(A.V + (tok0 + c0n) * DV + dv0), v_offset(tid, DV));
         // wave 0: the window of the next chunk (past the stream's last event a
         // lane holds a token no chunk reaches)
         // (the sentinel is the destination's old value: a select on the loaded
         // value would wait for the load here)
-        c.evnext = make_int2(0x7fffffff, -1);
+        c.evnext = make_int2(fresh_i32(0x7fffffff), fresh_i32(-1));
         const int en = c.ewin + nev;
         if (wave == 0 && en + lane < A.evtot) c.evnext = *at_bytes(A.events + en, 8u * lane);
     }
@@ -735,13 +733,11 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
     // V^T K of its tokens), writes it to the cache and converts it into its
     // fp16 operand copy, and the active-state waves form the new active state.
     const int m0 = c.m0, act = c.act;
-    // the active state (d_k rows in 16-row tiles) passes through the read
-    // weights, which no wave reads after the inter-chunk read; a new active
-    // state built by an owner wave (rare) through the partial reads, which it
-    // writes only after the barrier that follows every wave's reduce
-    floatx4 *actbuf = reinterpret_cast<floatx4 *>(&S.W[0][0]);     // [DK / 16][NTV][64]
+    // the active state (d_k rows in 16-row tiles) passes through abuf; a new
+    // active state built by an owner wave (rare) through the partial reads,
+    // which it writes only after the barrier that follows every wave's reduce
+    floatx4 *actbuf = S.abuf;                                       // [DK / 16][NTV][64]
     floatx4 *anbuf = &S.ored[0][0][0][0];                           // [DK / 16][NTV][64]
-    static_assert((DK / 16) * NTV * 64 * sizeof(floatx4) <= sizeof(S.W), "the active state fits the weight table");
     static_assert((DK / 16) * NTV * 64 <= NW * MT * NTV * 64, "a state slice fits the partial-read buffer");
     if (wave == 0 && virt) {
         // chunk -1: each closed state the cache holds is a job that keeps its
@@ -1038,6 +1034,13 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
         S.jrow[p] = closed ? tid : 0;
         S.wsc[p] = closed ? ldexpf(1.0f, S.shexp[p]) : 0.0f;
     }
+    // every owner wave takes its slots' read weights into registers
+    lds_barrier();
+#pragma unroll
+    for (int r = 0; r < SPW; ++r) {
+        c.wrow[r] = __builtin_amdgcn_readfirstlane(S.jrow[NW * r + wave]);
+        c.wscl[r] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(S.wsc[NW * r + wave])));
+    }
     c.m0 = mnew;
     c.act = an;
     c.closed = cl;
@@ -1107,6 +1110,11 @@ __global__ __launch_bounds__(kRsThreads, 2) void k_prefill_rs(
         zero_frag(c.af[nt]);
     }
     if (tid < CMAX) { S.jrow[tid] = 0; S.wsc[tid] = 0.0f; }
+#pragma unroll
+    for (int r = 0; r < SPW; ++r) {
+        c.wrow[r] = 0;
+        c.wscl[r] = 0.0f;
+    }
     c.ea = 0;
     c.m0 = 0;
     c.act = -1;

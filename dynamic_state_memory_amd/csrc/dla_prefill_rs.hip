@@ -317,12 +317,18 @@ static_assert(sizeof(RsStageA<128>) == rs_rec_a_bytes(128) && sizeof(RsStageB<12
                   sizeof(RsStageA<64>) == rs_rec_a_bytes(64) && sizeof(RsStageB<64>) == rs_rec_b_bytes(64),
               "the LDS stages mirror the two parts of a chunk record");
 
+// The chunk's V slice, row-major (token, column), copied into LDS by
+// global->LDS loads at the chunk start and read after the middle barrier.
+template <int DVT>
+struct RsStageV {
+    __bf16 v[kChunk][DVT];
+};
+
 // Everything else the sweep keeps in LDS.  The stages are separate __shared__
 // variables so that the compiler can tell that loads in flight into one never
 // touch the other.
 template <int DK, int DVT, int CMAX>
 struct RsSmem {
-    __bf16 vt[DVT][kChunk + 8];                  // V slice of the chunk, transposed
     // in a chunk with events, after the read, the active state passes through it
     floatx4 abuf[(DK / 16) * (DVT / 16) * 64];
     floatx4 ored[kRsWaves][kChunk / 16][DVT / 16][64];  // partial reads: wave, row tile, column tile, lane
@@ -414,6 +420,44 @@ __device__ __forceinline__ void stage_b(RsStageB<DK> &Y, const uint8_t *rec, siz
         reinterpret_cast<u32x4 *>(&Y), tid, wave);
 }
 
+// The V slice of the chunk starting at token c0 into LDS: 16-byte piece p
+// (row p / (DVT / 8), columns 8 (p % (DVT / 8)) ..) from thread p; rows past
+// the end of the stream repeat its last row (their products meet zero keys
+// and zero intra-chunk weights).
+template <int DVT>
+__device__ __forceinline__ void stage_v(RsStageV<DVT> &Vs, const __bf16 *V, size_t tok0, int c0, int T, int DV,
+                                        int dv0, int tid, int wave)
+{
+    constexpr int PPR = DVT / 8;                 // pieces per row
+    static_assert(kChunk * PPR <= kRsThreads, "one piece per thread");
+    if (tid < kChunk * PPR) {
+        const int r = min(tid / PPR, T - 1 - c0);
+        const uint32_t off = 2u * (static_cast<uint32_t>(r) * static_cast<uint32_t>(DV) + 8u * (tid % PPR));
+        load_to_lds16(at_bytes(V + (tok0 + c0) * DV + dv0, off), reinterpret_cast<char *>(&Vs) + 1024 * wave);
+    }
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// Lane (g, i) = (lane / 16, lane % 16)'s operand of token step kk (32 tokens)
+// and column tile nt of the V slice held row-major in LDS: V[32 kk + 8 g + j]
+// [16 nt + i], j = 0..7, the B operand of P V and the update.  Two transposed
+// 8-byte reads: in each 16-lane group, lane i receives element i % 4 of the
+// reads of lanes 4 k + i / 4 (k = 0..3), so lane q reads row 32 kk + 8 g +
+// q / 4 (+ 4 in the second read), columns 16 nt + 4 (q % 4) .. + 3.
+template <int DVT>
+__device__ __forceinline__ Frag<__bf16> v_frag(const RsStageV<DVT> &Vs, int nt, int kk, int lane)
+{
+    const int g = lane >> 4, q = lane & 15;
+    const __bf16 *p0 = &Vs.v[32 * kk + 8 * g + (q >> 2)][16 * nt + 4 * (q & 3)];
+    const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p0));
+    const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p0 + 4 * DVT));
+    Frag<__bf16> f;
+    f.v = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+    return f;
+}
+
 // The closed-state part of the inter-chunk read over the wave's first NP slot
 // pairs: one 16-token row tile at a time (a quarter of the query fragments
 // live), two independent product chains per pair, each product weighted per
@@ -472,7 +516,6 @@ struct RsCarry {
     Frag<_Float16> af[DVT / 16];                 // its fp16 operand copy
     int wrow[SPW];                               // read-weight rows of the wave's slots (uniform)
     float wscl[SPW];                             // and their scales (uniform)
-    u32x4 vnext;                                 // next chunk's V piece
     int2 evnext;                                 // event lane of the next chunk's window (wave 0)
     int ea;                                      // exponent of this wave's active-state operand
     int m0, act;                                 // live states, the active state's slot (uniform)
@@ -498,17 +541,10 @@ __device__ __forceinline__ void cache_store4(void *base, size_t e, float4 v)
         *reinterpret_cast<float4 *>(static_cast<float *>(base) + e) = v;
 }
 
-// Per-lane byte offsets, recomputed at each use from an opaque copy of the
+// Per-lane byte offset, recomputed at each use from an opaque copy of the
 // thread index (kept live anyway) rather than held, or spilled, across chunks:
-// thread tid's V piece (token tid % 64, columns 8 (tid / 64) ..) within a
-// chunk's rows, and lane (lr, lg) of wave w's output piece (token 16 w + lr,
-// columns 4 lg .. 4 lg + 3) within a chunk.
-__device__ __forceinline__ uint32_t v_offset(int tid, int DV)
-{
-    uint32_t t = static_cast<uint32_t>(tid);
-    asm volatile("" : "+v"(t));
-    return 2u * ((t & (kChunk - 1)) * static_cast<uint32_t>(DV) + (t / kChunk) * 8u);
-}
+// lane (lr, lg) of wave w's output piece (token 16 w + lr, columns
+// 4 lg .. 4 lg + 3) within a chunk.
 __device__ __forceinline__ uint32_t o_offset(int tid, int DV)
 {
     uint32_t t = static_cast<uint32_t>(tid);
@@ -525,8 +561,7 @@ struct RsParams {
     const int2 *events;         // the stream's events
     int evtot;                  // events of the stream
     const uint8_t *rec;         // chunk records
-    int bh, dv0, tid, lane, wave, lr, lg, NCH, vr, vc;
-    bool v_mover;
+    int bh, dv0, tid, lane, wave, lr, lg, NCH;
     size_t tok0, slot_stride;
     int m_init;                 // states the cache held when the call started
     const uint8_t *init_order;  // their physical slots, oldest first
@@ -543,7 +578,7 @@ struct RsParams {
 // active state (d_k = 128: every wave), and reduces and stores the outputs of
 // tokens 16 w .. 16 w + 15.
 template <int DK, int DVT, int SPW, bool SBF, bool CONT>
-__device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB<DK> &Y,
+__device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB<DK> &Y, RsStageV<DVT> &Vs,
                                          RsSmem<DK, DVT, kRsWaves * SPW> &S, const RsParams &A,
                                          RsCarry<DK, DVT, SPW> &c)
 {
@@ -556,7 +591,7 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
     __bf16 *O = A.O;
     const int T = A.T, DV = A.DV;
     const int bh = A.bh, dv0 = A.dv0, tid = A.tid, lane = A.lane, wave = A.wave, lr = A.lr, lg = A.lg;
-    const int NCH = A.NCH, vr = A.vr, vc = A.vc;
+    const int NCH = A.NCH;
     const size_t tok0 = A.tok0, slot_stride = A.slot_stride;
     auto &stk = c.stk;
     auto &am = c.am;
@@ -571,7 +606,6 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
     const bool virt = CONT && ch < 0;
     const int c0 = ch * kChunk;
     const int nvalid = virt ? 0 : min(kChunk, T - c0);
-    const u32x4 vcur = c.vnext;
     const int2 evcur = c.evnext;
     const bool more = ch + 1 < NCH;
     const size_t cb = static_cast<size_t>(bh) * NCH + (virt ? 0 : ch);
@@ -588,11 +622,7 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
         if (lane == 0) S.nev = n;
     }
     // ---- this chunk's V (transposed) and events into LDS
-    if (A.v_mover) {
-        const __bf16 *ve = reinterpret_cast<const __bf16 *>(&vcur);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) S.vt[vc + e][vr] = ve[e];
-    }
+    stage_v<DVT>(Vs, A.V, tok0, virt ? 0 : c0, T, DV, dv0, tid, wave);
     // ---- inter-chunk read: closed states from registers, then the active state
     floatx4 Oi[MT][NTV];
 #pragma unroll
@@ -650,16 +680,9 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
     __syncthreads();
     const int nev = __builtin_amdgcn_readfirstlane(S.nev);
     const bool has_ev = virt || nev > 0;
-    // ---- part A of the next chunk; its V, events and query exponent into registers
+    // ---- part A of the next chunk; its events into registers
     if (more) {
         stage_a<DK>(X, A.rec, cb + (virt ? 0 : 1), tid, wave);
-        const int c0n = c0 + kChunk;
-        {
-            const uint32_t z = static_cast<uint32_t>(fresh_i32(0));
-            c.vnext = u32x4{z, z, z, z};
-        }
-        if (A.v_mover && vr < min(kChunk, T - c0n))
-            c.vnext = *at_bytes(reinterpret_cast<const u32x4 *>(A.V + (tok0 + c0n) * DV + dv0), v_offset(tid, DV));
         // wave 0: the window of the next chunk (past the stream's last event a
         // lane holds a token no chunk reaches)
         // (the sentinel is the destination's old value: a select on the loaded
@@ -686,7 +709,7 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
 #pragma unroll
                 for (int nt = 0; nt < NTV; ++nt) {
                     Frag<__bf16> b;
-                    load_frag(b, &S.vt[16 * nt + lr][32 * ks + 8 * lg]);
+                    b = v_frag<DVT>(Vs, nt, ks, lane);
                     mma32(Oprev[nt], b, a);
                 }
             }
@@ -716,7 +739,7 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
 #pragma unroll
                     for (int nt = 0; nt < NTV; ++nt) {
                         Frag<__bf16> b;
-                        load_frag(b, &S.vt[16 * nt + lr][32 * kk + 8 * lg]);
+                        b = v_frag<DVT>(Vs, nt, kk, lane);
                         mma32(am[nt][h], a, b);
                     }
                 }
@@ -904,7 +927,7 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
                 if (32 * kk >= hi || 32 * kk + 32 <= lo) continue;
                 Frag<__bf16> b[NTV];
 #pragma unroll
-                for (int nt = 0; nt < NTV; ++nt) load_frag(b[nt], &S.vt[16 * nt + lr][32 * kk + 8 * lg]);
+                for (int nt = 0; nt < NTV; ++nt) b[nt] = v_frag<DVT>(Vs, nt, kk, lane);
 #pragma unroll
                 for (int kt = 0; kt < DK / 16; ++kt) {
                     Frag<__bf16> a;
@@ -970,7 +993,7 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
             if (32 * kk >= hi || 32 * kk + 32 <= lo) continue;
             Frag<__bf16> b[NTV];
 #pragma unroll
-            for (int nt = 0; nt < NTV; ++nt) load_frag(b[nt], &S.vt[16 * nt + lr][32 * kk + 8 * lg]);
+            for (int nt = 0; nt < NTV; ++nt) b[nt] = v_frag<DVT>(Vs, nt, kk, lane);
 #pragma unroll
             for (int kt = 0; kt < DK / 16; ++kt) {
                 Frag<__bf16> a;
@@ -1014,7 +1037,7 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
 #pragma unroll
                     for (int nt = 0; nt < NTV; ++nt) {
                         Frag<__bf16> b;
-                        load_frag(b, &S.vt[16 * nt + lr][32 * kk + 8 * lg]);
+                        b = v_frag<DVT>(Vs, nt, kk, lane);
                         mma32(am[nt][h], a, b);
                     }
                 }
@@ -1063,6 +1086,7 @@ __global__ __launch_bounds__(kRsThreads, 2) void k_prefill_rs(
     static_assert(CMAX <= kPrepCmax, "a chunk record holds lam for 32 slots");
     __shared__ RsStageA<DK> stA;
     __shared__ RsStageB<DK> stB;
+    __shared__ RsStageV<DVT> stV;
     __shared__ RsSmem<DK, DVT, CMAX> S;
 
     const int nblk = gridDim.x;
@@ -1080,10 +1104,6 @@ __global__ __launch_bounds__(kRsThreads, 2) void k_prefill_rs(
     A.lr = A.lane & 15;
     A.lg = A.lane >> 4;
     A.NCH = (T + kChunk - 1) / kChunk;
-    // thread tid < 8 DVT moves V piece (token tid % 64, columns 8 (tid / 64) ..)
-    A.vr = A.tid & (kChunk - 1);
-    A.vc = (A.tid / kChunk) * 8;
-    A.v_mover = A.tid < kChunk * DVT / 8;
     A.tok0 = static_cast<size_t>(A.bh) * T;
     A.slot_stride = static_cast<size_t>(DV) * DK;
     {
@@ -1156,18 +1176,15 @@ __global__ __launch_bounds__(kRsThreads, 2) void k_prefill_rs(
         }
     }
 
-    // chunk 0: part A into LDS, V and events into registers
+    // chunk 0: part A into LDS, events into registers
     stage_a<DK>(stA, rec, static_cast<size_t>(A.bh) * NCH, tid, wave);
-    c.vnext = u32x4{0u, 0u, 0u, 0u};
-    if (A.v_mover && A.vr < min(kChunk, T))
-        c.vnext = *reinterpret_cast<const u32x4 *>(V + (A.tok0 + A.vr) * DV + A.dv0 + A.vc);
     // wave 0: the window of chunk 0 (the stream's first 64 events)
     c.ewin = 0;
     c.evnext = make_int2(0x7fffffff, -1);
     if (wave == 0 && A.lane < A.evtot) c.evnext = A.events[A.lane];
 
     for (int ch = (CONT && A.m_init > 1) ? -1 : 0; ch < NCH; ++ch)
-        rs_chunk<DK, DVT, SPW, SBF, CONT>(ch, stA, stB, S, A, c);
+        rs_chunk<DK, DVT, SPW, SBF, CONT>(ch, stA, stB, stV, S, A, c);
 
     // the active state's accumulators are the last state of the final cache
     const int kb = wave - (kRsWaves - KS);
@@ -1256,7 +1273,7 @@ hipError_t launch_prefill_rs(const PrefillArgs &a, hipStream_t stream)
 template <int DK, int DVT, int CMAX>
 constexpr size_t rs_lds_bytes()
 {
-    return sizeof(RsStageA<DK>) + sizeof(RsStageB<DK>) + sizeof(RsSmem<DK, DVT, CMAX>);
+    return sizeof(RsStageA<DK>) + sizeof(RsStageB<DK>) + sizeof(RsStageV<DVT>) + sizeof(RsSmem<DK, DVT, CMAX>);
 }
 
 size_t prefill_rs_smem_bytes(int dk, int, int C)

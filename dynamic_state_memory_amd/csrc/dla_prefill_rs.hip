@@ -83,6 +83,10 @@ __device__ __forceinline__ int refresh_active(const floatx4 (&am)[NTV][2], Frag<
     return e;
 }
 
+// Four 16-bit elements, the result of a transposed 8-byte LDS read.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
 // ------------------------------------------------------------ chunk pre-pass
 
 // FEN: the Log-Linear fixed schedule (the schedule kernel's chunk events);
@@ -203,16 +207,20 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
         }
         __builtin_nontemporal_store(h, &q16f[f]);
     }
-    // K^T fragments: d_k rows of a 16-tile, 8 consecutive tokens per lane
+    // K^T fragments: d_k rows of a 16-tile, 8 consecutive tokens per lane, by
+    // two transposed 8-byte LDS reads (each wave one (tile, kk) pair per step:
+    // in a 16-lane group, lane i receives element i % 4 of the reads of lanes
+    // 4 k + i / 4, so lane q reads row t0 + q / 4, columns 16 tile + 4 (q % 4) ..)
 #pragma unroll
     for (int j = 0; j < DK / 32; ++j) {
         const int f = tid + 256 * j;                   // (tile, kk, lane)
         const int l = f & 63, kk = (f >> 6) & 1, tile = f >> 7;
-        const int dk = 16 * tile + (l & 15), t0 = 32 * kk + 8 * (l >> 4);
-        bf16x8 h;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) h[e] = k[t0 + e][dk];
-        __builtin_nontemporal_store(h, &ktf[f]);
+        const int q = l & 15, t0 = 32 * kk + 8 * (l >> 4);
+        const __bf16 *p0 = &k[t0 + (q >> 2)][16 * tile + 4 * (q & 3)];
+        const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p0));
+        const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p0 + 4 * (DK + 8)));
+        __builtin_nontemporal_store(__builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7)),
+                                    &ktf[f]);
     }
     __syncthreads();
     // P = (Q K^T) o W on the causal triangle (wave w: rows 16w..16w+15)
@@ -437,8 +445,6 @@ __device__ __forceinline__ void stage_v(RsStageV<DVT> &Vs, const __bf16 *V, size
     }
 }
 
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 // Lane (g, i) = (lane / 16, lane % 16)'s operand of token step kk (32 tokens)
 // and column tile nt of the V slice held row-major in LDS: V[32 kk + 8 g + j]

@@ -249,6 +249,19 @@ def test_wider_key_shapes(io, dk, dv, C, T, means):
     assert r["n_ev"].min() > 0
 
 
+@pytest.mark.parametrize("T", [1, 2, 63, 64, 65, 127, 130])
+def test_short_streams_register_path(T):
+    """Streams shorter than a chunk, exactly one or two chunks, and a ragged
+    second chunk, on the register-resident kernel at the headline's head
+    shape (its V slice and records are staged per chunk; the rows past a
+    stream's end must add nothing): schedule bit-exact, outputs and final
+    states within their gates."""
+    torch_mod()
+    cfg = dataclasses.replace(workloads.CONFIGS["gdn_1p3b_t32k_bf16"], H=2, seg_means=(6,))
+    d = workloads.prefill_inputs(cfg, streams=[0, 1], T=T)
+    _full_check(d, cfg.C, cfg.tau, "bf16", f"short stream T={T}")
+
+
 def test_literal_noise_reading_every_token_opens(prefill_path):
     torch_mod()
     cfg = workloads.CONFIGS["gdn_1p3b_t32k_bf16"]

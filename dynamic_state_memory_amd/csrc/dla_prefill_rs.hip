@@ -439,8 +439,11 @@ __device__ __forceinline__ void stage_v(RsStageV<DVT> &Vs, const __bf16 *V, size
     constexpr int PPR = DVT / 8;                 // pieces per row
     static_assert(kChunk * PPR <= kRsThreads, "one piece per thread");
     if (tid < kChunk * PPR) {
-        const int r = min(tid / PPR, T - 1 - c0);
-        const uint32_t off = 2u * (static_cast<uint32_t>(r) * static_cast<uint32_t>(DV) + 8u * (tid % PPR));
+        // (the thread index made opaque here: no per-lane 64-bit address is
+        // formed once and held, or spilled, across the chunk loop)
+        const int t = fresh_i32(tid);
+        const int r = min(t / PPR, T - 1 - c0);
+        const uint32_t off = 2u * (static_cast<uint32_t>(r) * static_cast<uint32_t>(DV) + 8u * (t % PPR));
         load_to_lds16(at_bytes(V + (tok0 + c0) * DV + dv0, off), reinterpret_cast<char *>(&Vs) + 1024 * wave);
     }
 }
@@ -484,11 +487,15 @@ __device__ __forceinline__ void rs_read_closed(floatx4 (&Oi)[kChunk / 16][DVT / 
     constexpr int NTV = DVT / 16;
     constexpr int NW = kRsWaves;
     static_assert(2 * NP <= SPW, "pairs of the wave's slots");
+    // the query fragments of a row tile rotate through one set of registers:
+    // the last pair of a tile loads each fragment of the next tile as soon as
+    // its own products with that fragment have issued, so the next tile's
+    // loads are in flight under the tile's last products and weighting
+    Frag<_Float16> qf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) load_frag(qf[ks], X.qf[0][ks][lane]);
 #pragma unroll
     for (int mt = 0; mt < kChunk / 16; ++mt) {
-        Frag<_Float16> qf[KS];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) load_frag(qf[ks], X.qf[mt][ks][lane]);
 #pragma unroll
         for (int r2 = 0; r2 < 2 * NP; r2 += 2) {
             floatx4 P0[NTV], P1[NTV];
@@ -498,12 +505,14 @@ __device__ __forceinline__ void rs_read_closed(floatx4 (&Oi)[kChunk / 16][DVT / 
                 P1[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
             }
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
+            for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
                 for (int nt = 0; nt < NTV; ++nt) {
                     mma32(P0[nt], stk[r2][ks][nt], qf[ks]);
                     mma32(P1[nt], stk[r2 + 1][ks][nt], qf[ks]);
                 }
+                if (r2 + 2 == 2 * NP && mt + 1 < kChunk / 16) load_frag(qf[ks], X.qf[mt + 1][ks][lane]);
+            }
             const float w0 = static_cast<float>(X.wr[wrow[r2]][(kChunk / 16) * lr + mt]) * wscl[r2];
             const float w1 = static_cast<float>(X.wr[wrow[r2 + 1]][(kChunk / 16) * lr + mt]) * wscl[r2 + 1];
 #pragma unroll

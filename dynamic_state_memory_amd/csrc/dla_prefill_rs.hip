@@ -368,11 +368,21 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) const void glb_void_t;
 
-// One 16-byte piece per lane from global memory straight into LDS: lane l's
-// piece lands at lds_wave + 16 l (lds_wave is the same for the whole wave).
-__device__ __forceinline__ void load_to_lds16(const void *g, void *lds_wave)
+// One 16-byte piece per lane from global memory straight into LDS: lane l
+// reads base + off (base and lds_wave the same for the whole wave, off its
+// own) and its piece lands at lds_wave + 16 l.  Issued as a buffer load
+// (base in a buffer resource, off as the lane's offset) rather than a global
+// one: the compiler counts a global load into LDS as a possible LDS access
+// too, and while one is in flight it waits for every LDS read at once
+// (lgkmcnt 0) instead of for the one it needs; a buffer load into LDS is
+// counted as a vector memory load only.
+__device__ __forceinline__ void load_to_lds16(const void *base, uint32_t off, void *lds_wave)
 {
-    __builtin_amdgcn_global_load_lds((glb_void_t *)(g), (lds_void_t *)(lds_wave), 16, 0, 0);
+    // raw buffer, no stride, no range limit in practice (the offsets stay
+    // within the caller's buffers); word 3 as for gfx9 raw buffers
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), static_cast<short>(0), 0x7fffffff, 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)(lds_wave), 16, off, 0, 0, 0);
 }
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
@@ -406,10 +416,11 @@ __device__ __forceinline__ P *at_bytes(P *base, uint32_t off)
 template <int N>
 __device__ __forceinline__ void stage_array(const u32x4 *src, u32x4 *dst, int tid, int wave)
 {
+    const int wv = __builtin_amdgcn_readfirstlane(wave);   // (uniform: the buffer base is a scalar)
 #pragma unroll
     for (int j = 0; j < (N + kRsThreads - 1) / kRsThreads; ++j)
-        if (N % kRsThreads == 0 || 64 * wave + kRsThreads * j < N)
-            load_to_lds16(at_bytes(src + 64 * wave + kRsThreads * j, 16u * (tid & 63)), dst + 64 * wave + kRsThreads * j);
+        if (N % kRsThreads == 0 || 64 * wv + kRsThreads * j < N)
+            load_to_lds16(src + 64 * wv + kRsThreads * j, 16u * (fresh_i32(tid) & 63), dst + 64 * wv + kRsThreads * j);
 }
 
 // part A / part B of chunk record cb into the stages
@@ -444,7 +455,8 @@ __device__ __forceinline__ void stage_v(RsStageV<DVT> &Vs, const __bf16 *V, size
         const int t = fresh_i32(tid);
         const int r = min(t / PPR, T - 1 - c0);
         const uint32_t off = 2u * (static_cast<uint32_t>(r) * static_cast<uint32_t>(DV) + 8u * (t % PPR));
-        load_to_lds16(at_bytes(V + (tok0 + c0) * DV + dv0, off), reinterpret_cast<char *>(&Vs) + 1024 * wave);
+        load_to_lds16(V + (tok0 + c0) * DV + dv0, off,
+                      reinterpret_cast<char *>(&Vs) + 1024 * __builtin_amdgcn_readfirstlane(wave));
     }
 }
 
@@ -669,7 +681,7 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
     __builtin_amdgcn_s_setprio(2);
     if (c.act >= 0 && act_wave) {
         // the most recent state's weights of token 16 mt + lr, times 2^ea
-        const uint2 wb = *reinterpret_cast<const uint2 *>(&X.wr[c.m0 > 0 ? c.m0 - 1 : 0][(kChunk / 16) * lr]);
+        const uint2 wb = *reinterpret_cast<const uint2 *>(&X.wr[c.m0 > 0 ? c.m0 - 1 : 0][(kChunk / 16) * (fresh_i32(tid) & 15)]);
         const float wa[4] = {ldexpf(__uint_as_float(wb.x << 16), c.ea), ldexpf(__uint_as_float(wb.x & 0xffff0000u), c.ea),
                              ldexpf(__uint_as_float(wb.y << 16), c.ea), ldexpf(__uint_as_float(wb.y & 0xffff0000u), c.ea)};
         static_assert(MT == 4, "one weight per row tile in the lane's 8 bytes");
@@ -704,7 +716,7 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
         // value would wait for the load here)
         c.evnext = make_int2(fresh_i32(0x7fffffff), fresh_i32(-1));
         const int en = c.ewin + nev;
-        if (wave == 0 && en + lane < A.evtot) c.evnext = *at_bytes(A.events + en, 8u * lane);
+        if (wave == 0 && en + lane < A.evtot) c.evnext = *at_bytes(A.events + en, 8u * (fresh_i32(tid) & 63));
     }
     // ---- reduce the partial reads of rows 16 w .., add P V
     {
@@ -820,8 +832,9 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
             }
         }
         // old states still live keep their value and their order (lane i: old state i)
-        if (lane < m0 && ((oa >> lane) & 1ull)) {
-            const int p = S.order[lane];
+        const int ln = fresh_i32(tid) & 63;     // (= lane, formed here rather than held)
+        if (ln < m0 && ((oa >> ln) & 1ull)) {
+            const int p = S.order[ln];
             // (position: the live old states in lower lanes, counted by mbcnt)
             S.new_order[__builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(oa >> 32),
                                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(oa), 0u))] = p;

@@ -25,7 +25,7 @@ __all__ = [
 DLA_OK, DLA_ERR_ARG, DLA_ERR_UNSUPPORTED, DLA_ERR_WORKSPACE, DLA_ERR_HIP = 0, 1, 2, 3, 4
 DLA_F32, DLA_BF16 = 0, 1
 DLA_MERGE_SUM, DLA_MERGE_DENSITY, DLA_FENWICK = 0, 1, 2
-DLA_PATH_AUTO, DLA_PATH_STREAMED = 0, 1
+DLA_PATH_AUTO, DLA_PATH_STREAMED, DLA_PATH_UNSPLIT = 0, 1, 2
 DLA_SCORE_COSINE, DLA_SCORE_STATE = 0, 1
 SCORE_RULES = {"cosine": DLA_SCORE_COSINE, "state": DLA_SCORE_STATE}
 MERGE_RULES = {"sum": DLA_MERGE_SUM, "density": DLA_MERGE_DENSITY, "fenwick": DLA_FENWICK}

@@ -62,6 +62,7 @@ struct Sizes {
         shadow;
     uint64_t ev_stride;
     uint64_t rec;
+    uint64_t seg;
     uint64_t total;
 };
 
@@ -89,8 +90,13 @@ Sizes workspace_sizes(int64_t BH, int64_t T, int64_t C, int64_t dk, int64_t dv)
     // chunk records (register-resident path), or the fp32 working copy of a
     // bf16-state cache's states (streamed path)
     z.rec = align_up(std::max<uint64_t>(static_cast<uint64_t>(BH) * NCH * rs_record_bytes(dk), 4ull * BH * C * dv * dk), 256);
+    // slots of the block sets of a sweep split along the sequence: only for a
+    // grid of at most 256 blocks of the register-resident sweep (16 value
+    // columns per block)
+    z.seg = (C <= 32 && dk <= 128 && BH * ((dv + 15) / 16) <= 256) ? align_up(4ull * kSegScratch * BH * C * dv * dk, 256)
+                                                                 : 0;
     z.total = z.s + z.qs + z.flag + z.tile_cnt + z.tile_sum + z.seg_t + z.seg_P + z.seg_q0 + z.nseg +
-              z.events + z.chunk_ev + z.init_m + z.init_order + z.init_t + z.shadow + z.rec;
+              z.events + z.chunk_ev + z.init_m + z.init_order + z.init_t + z.shadow + z.rec + z.seg;
     return z;
 }
 
@@ -117,6 +123,8 @@ Workspace carve(void *base, const Sizes &z)
     w.rec = p;
     w.work = reinterpret_cast<float *>(p);
     p += z.rec;
+    w.seg_states = z.seg ? reinterpret_cast<float *>(p) : nullptr;
+    p += z.seg;
     (void)p;
     return w;
 }
@@ -238,6 +246,28 @@ static __device__ __align__(256) uint8_t scratch[DLA_NOALLOC_SCRATCH_BYTES];
 constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
 void *g_scratch_ptr[kMaxDevices];
+
+// Block slots of the sweep on the current device (two blocks per compute
+// unit), looked up once per device.
+int g_block_slots[kMaxDevices];
+
+dla_status device_block_slots(int *out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(DLA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(DLA_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_block_slots[dev]) {
+        int cus = 0;
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess || cus <= 0)
+            return fail(DLA_ERR_HIP, "hipDeviceGetAttribute(compute units): %s", hipGetErrorString(e));
+        g_block_slots[dev] = 2 * cus;
+    }
+    *out = g_block_slots[dev];
+    return DLA_OK;
+}
 
 // The scratch address of the device current on this thread, which must be
 // the device of `stream`.
@@ -456,6 +486,11 @@ dla_status prefill_call(const void *q, const void *k, const void *v, const void 
         if (ss != DLA_OK) return ss;
     }
     a.ws = carve(workspace, z);
+    a.seg_slots = 0;
+    if (a.register_resident && g_path_override != DLA_PATH_UNSPLIT) {
+        s = device_block_slots(&a.seg_slots);
+        if (s != DLA_OK) return s;
+    }
     a.ev_before = g_ev_before;
     a.ev_after = g_ev_after;
     if (sched) a.sched = *sched;
@@ -555,7 +590,8 @@ dla_status dla_cache_set_score_rule(dla_cache *cache, int32_t rule)
 
 dla_status dla_set_prefill_path(int32_t path, int32_t value_columns)
 {
-    if (path != DLA_PATH_AUTO && path != DLA_PATH_STREAMED) return fail(DLA_ERR_ARG, "unknown prefill path %d", path);
+    if (path != DLA_PATH_AUTO && path != DLA_PATH_STREAMED && path != DLA_PATH_UNSPLIT)
+        return fail(DLA_ERR_ARG, "unknown prefill path %d", path);
     if (value_columns != 0 && value_columns != 16 && value_columns != 32)
         return fail(DLA_ERR_ARG, "value_columns must be 0, 16 or 32 (got %d)", value_columns);
     g_path_override = path;

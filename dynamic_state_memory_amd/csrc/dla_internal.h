@@ -81,7 +81,12 @@ struct Workspace {
     // streamed path on a cache with bf16 closed states: the fp32 working copy
     // of the states [BH][C][dv][dk], in the same bytes as rec (unused there)
     float *work;
+    // register-resident sweep split along the sequence: the slots of every
+    // block set but the last [kSegScratch][BH][C][dv][dk] fp32 (NULL when the
+    // shape's grid is too large to be split)
+    float *seg_states;
 };
+constexpr int kSegScratch = 3;  // block sets with slots of their own (at most 4 sets)
 constexpr int kPrepCmax = 32;   // read-weight rows kept per chunk by the pre-pass
 // chunk record of the register-resident prefill: query fragments, read weights,
 // weighted-score fragments, key fragments (bytes; each part a multiple of 16)
@@ -107,6 +112,8 @@ struct PrefillArgs {
     dla_schedule_out sched;
     hipEvent_t ev_before, ev_after;   // optional, recorded around the chunk kernel
     int register_resident;            // 1: k_prefill_rs, 0: k_prefill (states streamed)
+    int seg_slots;                    // block slots of the device (two per compute unit) for
+                                      // splitting a small sweep grid along the sequence; 0: no split
 };
 
 struct DecodeSched {

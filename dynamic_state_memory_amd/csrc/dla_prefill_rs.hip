@@ -30,7 +30,15 @@
 //                 a chunk with events the wave owning each changed slot builds
 //                 its new fp32 value in registers (own value, merged-in
 //                 values, V_g^T K_g of its tokens), writes it to the fp32 cache
-//                 and converts it into its register copy.
+//                 and converts it into its register copy.  A grid that would
+//                 fill at most half of the device's block slots (few streams)
+//                 is split along the sequence into up to four block sets per
+//                 stream: set s takes the chunks before its range for their
+//                 state updates only (no reads, no outputs, only the key
+//                 operands staged) and then sweeps its range in full, in a
+//                 copy of the slots of its own (the last set in the cache).
+//                 The updates are the same in every set, so the results equal
+//                 the unsplit sweep's bit for bit.
 //
 // Operand order of the read: the reduction index d_k of a 32-wide step is
 // split over lane groups g = lane / 16 as {4g..4g+3, 16+4g..16+4g+3}, the
@@ -40,6 +48,8 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <cstddef>
+#include <cmath>
 #include <type_traits>
 
 #include "dla_device.h"
@@ -439,6 +449,16 @@ __device__ __forceinline__ void stage_b(RsStageB<DK> &Y, const uint8_t *rec, siz
         reinterpret_cast<u32x4 *>(&Y), tid, wave);
 }
 
+// only the K^T fragments of part B (a chunk taken for its updates only)
+template <int DK>
+__device__ __forceinline__ void stage_b_keys(RsStageB<DK> &Y, const uint8_t *rec, size_t cb, int tid, int wave)
+{
+    constexpr size_t kt = offsetof(RsStageB<DK>, ktf);
+    stage_array<(rs_rec_b_bytes(DK) - kt) / 16>(
+        reinterpret_cast<const u32x4 *>(rec + cb * rs_record_bytes(DK) + rs_rec_a_bytes(DK) + kt),
+        reinterpret_cast<u32x4 *>(reinterpret_cast<uint8_t *>(&Y) + kt), tid, wave);
+}
+
 // The V slice of the chunk starting at token c0 into LDS: 16-byte piece p
 // (row p / (DVT / 8), columns 8 (p % (DVT / 8)) ..) from thread p; rows past
 // the end of the stream repeat its last row (their products meet zero keys
@@ -580,6 +600,14 @@ __device__ __forceinline__ uint32_t o_offset(int tid, int DV)
     return 2u * ((16u * w + (l & 15u)) * static_cast<uint32_t>(DV) + 4u * (l >> 4));
 }
 
+// The chunk ranges of the block sets a stream's sweep is split into (see
+// k_prefill_rs): set s sweeps chunks [first[s], first[s + 1]) in full.
+constexpr int kMaxSeg = kSegScratch + 1;
+struct RsSegments {
+    int n;
+    int first[kMaxSeg + 1];
+};
+
 // Per-block constants of the sweep.
 struct RsParams {
     const __bf16 *V;
@@ -590,6 +618,7 @@ struct RsParams {
     const uint8_t *rec;         // chunk records
     int bh, dv0, tid, lane, wave, lr, lg, NCH;
     size_t tok0, slot_stride;
+    int c_begin, c_end;         // this block's chunks: [0, c_begin) update only, then [c_begin, c_end) in full
     int m_init;                 // states the cache held when the call started
     const uint8_t *init_order;  // their physical slots, oldest first
     void *st_base;              // the stream's slice of the slots (fp32, or bf16 closed states)
@@ -607,7 +636,7 @@ struct RsParams {
 template <int DK, int DVT, int SPW, bool SBF, bool CONT>
 __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB<DK> &Y, RsStageV<DVT> &Vs,
                                          RsSmem<DK, DVT, kRsWaves * SPW> &S, const RsParams &A,
-                                         RsCarry<DK, DVT, SPW> &c)
+                                         RsCarry<DK, DVT, SPW> &c, const bool upd)
 {
     constexpr int KS = DK / 32;
     constexpr int NTV = DVT / 16;
@@ -634,14 +663,15 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
     const int c0 = ch * kChunk;
     const int nvalid = virt ? 0 : min(kChunk, T - c0);
     const int2 evcur = c.evnext;
-    const bool more = ch + 1 < NCH;
+    const bool more = ch + 1 < A.c_end;
     const size_t cb = static_cast<size_t>(bh) * NCH + (virt ? 0 : ch);
     // part A of chunk ch has landed (every wave's share) and every wave is
     // done with chunk ch - 1 (so part B may be overwritten)
     wait_vmem();
     __syncthreads();
     // ---- part B of this chunk
-    stage_b<DK>(Y, A.rec, cb, tid, wave);
+    if (upd) stage_b_keys<DK>(Y, A.rec, cb, tid, wave);
+    else stage_b<DK>(Y, A.rec, cb, tid, wave);
     // the chunk's events: the lanes of wave 0's window (the next 64 events of
     // the stream, at most 64 per chunk) whose token lies in the chunk
     if (wave == 0) {
@@ -670,8 +700,9 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
     // priority, everything else at a higher one, so that one block's short
     // dependent phases take the issue slots they need while the other block
     // reads and the products fill the rest)
+    // (a chunk taken for its state updates only reads nothing: npair = 0)
     __builtin_amdgcn_s_setprio(0);
-    switch (npair) {
+    switch (upd ? 0 : npair) {
     case 0: break;
     case 1: rs_read_closed<DK, DVT, SPW, 1>(Oi, stk, X, c.wrow, c.wscl, wave, lane, lr); break;
     case 2: rs_read_closed<DK, DVT, SPW, (SPW >= 4 ? 2 : 1)>(Oi, stk, X, c.wrow, c.wscl, wave, lane, lr); break;
@@ -679,7 +710,7 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
     default: rs_read_closed<DK, DVT, SPW, SPW / 2>(Oi, stk, X, c.wrow, c.wscl, wave, lane, lr); break;
     }
     __builtin_amdgcn_s_setprio(2);
-    if (c.act >= 0 && act_wave) {
+    if (!upd && c.act >= 0 && act_wave) {
         // the most recent state's weights of token 16 mt + lr, times 2^ea
         const uint2 wb = *reinterpret_cast<const uint2 *>(&X.wr[c.m0 > 0 ? c.m0 - 1 : 0][(kChunk / 16) * (fresh_i32(tid) & 15)]);
         const float wa[4] = {ldexpf(__uint_as_float(wb.x << 16), c.ea), ldexpf(__uint_as_float(wb.x & 0xffff0000u), c.ea),
@@ -698,10 +729,12 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
             }
         }
     }
+    if (!upd) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < NTV; ++nt) S.ored[wave][mt][nt][lane] = Oi[mt][nt];
+            for (int nt = 0; nt < NTV; ++nt) S.ored[wave][mt][nt][lane] = Oi[mt][nt];
+    }
     // part B has landed and every wave is done with part A
     wait_vmem();
     __syncthreads();
@@ -709,7 +742,8 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
     const bool has_ev = virt || nev > 0;
     // ---- part A of the next chunk; its events into registers
     if (more) {
-        stage_a<DK>(X, A.rec, cb + (virt ? 0 : 1), tid, wave);
+        // (not for a next chunk that is taken for its updates only)
+        if (!(upd && ch + 1 < A.c_begin)) stage_a<DK>(X, A.rec, cb + (virt ? 0 : 1), tid, wave);
         // wave 0: the window of the next chunk (past the stream's last event a
         // lane holds a token no chunk reaches)
         // (the sentinel is the destination's old value: a select on the loaded
@@ -719,7 +753,7 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
         if (wave == 0 && en + lane < A.evtot) c.evnext = *at_bytes(A.events + en, 8u * (fresh_i32(tid) & 63));
     }
     // ---- reduce the partial reads of rows 16 w .., add P V
-    {
+    if (!upd) {
         const int w = wave;
 #pragma unroll
         for (int nt = 0; nt < NTV; ++nt) {
@@ -1104,7 +1138,7 @@ __global__ __launch_bounds__(kRsThreads, 2) void k_prefill_rs(
     float *__restrict__ states, float *__restrict__ active, const int2 *__restrict__ events, size_t ev_stride,
     const int32_t *__restrict__ chunk_ev, const uint8_t *__restrict__ rec,
     uint8_t *__restrict__ meta_base, size_t meta_stride, const int32_t *__restrict__ init_m,
-    const uint8_t *__restrict__ init_order)
+    const uint8_t *__restrict__ init_order, const RsSegments seg, float *__restrict__ seg_states)
 {
     constexpr int KS = DK / 32;
     constexpr int NTV = DVT / 16;
@@ -1120,6 +1154,10 @@ __global__ __launch_bounds__(kRsThreads, 2) void k_prefill_rs(
     const int nblk = gridDim.x;
     int lin = blockIdx.x;
     if ((nblk & 7) == 0) lin = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
+    // block lin: segment sg = lin / (BH nblk_dv) of stream (lin / nblk_dv) % BH
+    const int BHn = nblk / (seg.n * nblk_dv);
+    const int sg = lin / (BHn * nblk_dv);
+    lin -= sg * BHn * nblk_dv;
     RsParams A;
     A.V = V; A.O = O; A.T = T; A.C = C; A.DV = DV;
     A.rec = rec;
@@ -1184,6 +1222,19 @@ __global__ __launch_bounds__(kRsThreads, 2) void k_prefill_rs(
     // of the other kind leaves at once (the whole block: no barrier is met)
     // (a stream the fixed schedule refused, m_init < 0, is left to a later kernel)
     if (A.m_init < 0 || (A.m_init > 0) != CONT) return;
+    // segments (float32 state storage): a stream that starts from an empty
+    // cache is swept by seg.n block sets; set sg takes chunks [0, first[sg])
+    // for their state updates only (the same updates and merges, in the same
+    // order, as any set) and chunks [first[sg], first[sg + 1]) in full, into a
+    // copy of the slots of its own (the last set into the cache).  Any other
+    // stream is swept whole by the last set.
+    const bool split = !SBF && seg.n > 1 && A.m_init == 0;
+    const bool last_set = sg == seg.n - 1;
+    if (!split && !last_set) return;
+    A.c_begin = split ? seg.first[sg] : 0;
+    A.c_end = split ? seg.first[sg + 1] : NCH;
+    if (split && !last_set)
+        A.st_base = seg_states + (static_cast<size_t>(sg) * BHn + A.bh) * C * DV * DK + static_cast<size_t>(A.dv0) * DK;
     if (CONT) {
         c.act = A.init_order[A.m_init - 1];
         if (A.m_init == 1) {
@@ -1211,8 +1262,8 @@ __global__ __launch_bounds__(kRsThreads, 2) void k_prefill_rs(
     c.evnext = make_int2(0x7fffffff, -1);
     if (wave == 0 && A.lane < A.evtot) c.evnext = A.events[A.lane];
 
-    for (int ch = (CONT && A.m_init > 1) ? -1 : 0; ch < NCH; ++ch)
-        rs_chunk<DK, DVT, SPW, SBF, CONT>(ch, stA, stB, stV, S, A, c);
+    for (int ch = (CONT && A.m_init > 1) ? -1 : 0; ch < A.c_end; ++ch)
+        rs_chunk<DK, DVT, SPW, SBF, CONT>(ch, stA, stB, stV, S, A, c, ch >= 0 && ch < A.c_begin);
 
     // the active state's accumulators are the last state of the final cache
     const int kb = wave - (kRsWaves - KS);
@@ -1227,7 +1278,7 @@ __global__ __launch_bounds__(kRsThreads, 2) void k_prefill_rs(
                     make_float4(c.am[nt][h][0], c.am[nt][h][1], c.am[nt][h][2], c.am[nt][h][3]);
     }
     __syncthreads();
-    if (A.dv0 == 0 && tid < kMaxC) {
+    if (last_set && A.dv0 == 0 && tid < kMaxC) {
         uint8_t *order = meta_base + static_cast<size_t>(A.bh) * meta_stride + kOffOrder;
         order[tid] = static_cast<uint8_t>(tid < c.m0 ? S.order[tid] : 0xFF);
     }
@@ -1256,11 +1307,39 @@ static hipError_t launch_rs(const PrefillArgs &a, hipStream_t stream)
         hipError_t e = hipEventRecord(a.ev_before, stream);
         if (e != hipSuccess) return e;
     }
+    // A grid that fills at most half the block slots is split along the
+    // sequence into seg.n block sets (streams that start from an empty cache,
+    // float32 state storage, the information schedule).  Set s sweeps chunks
+    // [first[s], first[s + 1]) in full after chunks [0, first[s]) for their
+    // updates only, which cost a fraction x of a full chunk; the ranges are
+    // chosen so that every set has the same work: first[s] = tau (1 - (1 -
+    // x)^s) / x with tau = NCH x / (1 - (1 - x)^n).
+    RsSegments seg{};
+    seg.n = 1;
+    {
+        const int blocks = BH * nblk_dv;
+        int n = a.seg_slots > 0 ? std::min(kMaxSeg, a.seg_slots / blocks) : 1;
+        n = std::min(n, NCH / 8);
+        if (n >= 2 && a.ws.seg_states && !a.g.state_bf16 && a.merge_rule != DLA_FENWICK) {
+            constexpr double x = 0.3;
+            const double tau = NCH * x / (1.0 - std::pow(1.0 - x, n));
+            seg.n = n;
+            seg.first[0] = 0;
+            for (int k = 1; k < n; ++k) {
+                const int f = static_cast<int>(std::lround(tau * (1.0 - std::pow(1.0 - x, k)) / x));
+                seg.first[k] = std::min(std::max(f, seg.first[k - 1] + 1), NCH - (n - k));
+            }
+            seg.first[n] = NCH;
+        } else {
+            seg.first[1] = NCH;
+        }
+    }
 #define DLA_RS_LAUNCH(SBF_, CONT_)                                                                          \
-    hipLaunchKernelGGL((k_prefill_rs<DK, DVT, SPW, SBF_, CONT_>), dim3(BH * nblk_dv), dim3(kRsThreads), 0, stream, \
+    hipLaunchKernelGGL((k_prefill_rs<DK, DVT, SPW, SBF_, CONT_>), dim3(seg.n * BH * nblk_dv), dim3(kRsThreads), 0, stream, \
                        static_cast<const __bf16 *>(a.v), static_cast<__bf16 *>(a.o), a.T, a.g.C, a.g.dv, nblk_dv,    \
                        a.states, a.active, a.ws.events, ev_stride, a.ws.chunk_ev,                                   \
-                       static_cast<const uint8_t *>(a.ws.rec), a.meta, a.g.meta_stride, a.ws.init_m, a.ws.init_order)
+                       static_cast<const uint8_t *>(a.ws.rec), a.meta, a.g.meta_stride, a.ws.init_m, a.ws.init_order, \
+                       seg, a.ws.seg_states)
     // streams starting from an empty cache, then those continuing one
     if (a.g.state_bf16) {
         DLA_RS_LAUNCH(true, false);

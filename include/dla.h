@@ -81,6 +81,7 @@ extern "C" {
 /* Chunk-kernel choice of dla_set_prefill_path (testing and profiling). */
 #define DLA_PATH_AUTO 0       /* the library's choice (the default) */
 #define DLA_PATH_STREAMED 1   /* the streamed chunk kernel for every shape */
+#define DLA_PATH_UNSPLIT 2    /* the library's kernel, never split along the sequence */
 
 typedef enum dla_status {
     DLA_OK = 0,
@@ -371,7 +372,11 @@ dla_status dla_decode_step(const void *q, const void *k, const void *v, const vo
  * on this thread launch.  DLA_PATH_AUTO (the default) lets the library
  * choose (the register-resident sweep for bfloat16 io, C <= 32 and
  * d_k <= 128, the streamed kernel otherwise); DLA_PATH_STREAMED runs the
- * streamed kernel for every shape.  value_columns = 0 lets the library choose
+ * streamed kernel for every shape; DLA_PATH_UNSPLIT runs the library's
+ * choice but never splits the register-resident sweep along the sequence
+ * (which it does for streams starting from an empty cache with float32 state
+ * storage under the information schedule, when the sweep's grid would fill at
+ * most half of the device's block slots: the same results, bit for bit).  value_columns = 0 lets the library choose
  * the streamed kernel's d_v slice width, 16 or 32 forces it where d_v allows
  * and its LDS fits.  Both kernels compute the same layer (reading notes,
  * sections 5.1-5.3); production callers never need this.  Host only;

@@ -633,11 +633,13 @@ struct RsParams {
 // (closed states in registers), holds d_k rows 32 (w - AW) .. + 31 of the
 // active state (d_k = 128: every wave), and reduces and stores the outputs of
 // tokens 16 w .. 16 w + 15.
-template <int DK, int DVT, int SPW, bool SBF, bool CONT>
+template <int DK, int DVT, int SPW, bool SBF, bool CONT, bool MAYUPD>
 __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB<DK> &Y, RsStageV<DVT> &Vs,
                                          RsSmem<DK, DVT, kRsWaves * SPW> &S, const RsParams &A,
-                                         RsCarry<DK, DVT, SPW> &c, const bool upd)
+                                         RsCarry<DK, DVT, SPW> &c, const bool upd_chunk)
 {
+    // a chunk taken for its state updates only (the instance for split grids)
+    const bool upd = MAYUPD && upd_chunk;
     constexpr int KS = DK / 32;
     constexpr int NTV = DVT / 16;
     constexpr int MT = kChunk / 16;
@@ -1132,7 +1134,7 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
     c.ewin += nev;
 }
 
-template <int DK, int DVT, int SPW, bool SBF, bool CONT>
+template <int DK, int DVT, int SPW, bool SBF, bool CONT, bool SPLIT>
 __global__ __launch_bounds__(kRsThreads, 2) void k_prefill_rs(
     const __bf16 *__restrict__ V, __bf16 *__restrict__ O, int T, int C, int DV, int nblk_dv,
     float *__restrict__ states, float *__restrict__ active, const int2 *__restrict__ events, size_t ev_stride,
@@ -1228,7 +1230,7 @@ __global__ __launch_bounds__(kRsThreads, 2) void k_prefill_rs(
     // order, as any set) and chunks [first[sg], first[sg + 1]) in full, into a
     // copy of the slots of its own (the last set into the cache).  Any other
     // stream is swept whole by the last set.
-    const bool split = !SBF && seg.n > 1 && A.m_init == 0;
+    const bool split = SPLIT && !SBF && !CONT && seg.n > 1 && A.m_init == 0;
     const bool last_set = sg == seg.n - 1;
     if (!split && !last_set) return;
     A.c_begin = split ? seg.first[sg] : 0;
@@ -1262,8 +1264,12 @@ __global__ __launch_bounds__(kRsThreads, 2) void k_prefill_rs(
     c.evnext = make_int2(0x7fffffff, -1);
     if (wave == 0 && A.lane < A.evtot) c.evnext = A.events[A.lane];
 
+    // (a later block set first takes the chunks before its range for their
+    // updates only; only a stream that starts from an empty cache is split)
+    // (the update-only chunk code is in the instance launched for split grids
+    // only, so that it takes no registers from the other instances' sweep)
     for (int ch = (CONT && A.m_init > 1) ? -1 : 0; ch < A.c_end; ++ch)
-        rs_chunk<DK, DVT, SPW, SBF, CONT>(ch, stA, stB, stV, S, A, c, ch >= 0 && ch < A.c_begin);
+        rs_chunk<DK, DVT, SPW, SBF, CONT, SPLIT && !CONT>(ch, stA, stB, stV, S, A, c, ch < A.c_begin);
 
     // the active state's accumulators are the last state of the final cache
     const int kb = wave - (kRsWaves - KS);
@@ -1334,19 +1340,20 @@ static hipError_t launch_rs(const PrefillArgs &a, hipStream_t stream)
             seg.first[1] = NCH;
         }
     }
-#define DLA_RS_LAUNCH(SBF_, CONT_)                                                                          \
-    hipLaunchKernelGGL((k_prefill_rs<DK, DVT, SPW, SBF_, CONT_>), dim3(seg.n * BH * nblk_dv), dim3(kRsThreads), 0, stream, \
+#define DLA_RS_LAUNCH(SBF_, CONT_, SPLIT_)                                                                  \
+    hipLaunchKernelGGL((k_prefill_rs<DK, DVT, SPW, SBF_, CONT_, SPLIT_>), dim3(seg.n * BH * nblk_dv), dim3(kRsThreads), 0, stream, \
                        static_cast<const __bf16 *>(a.v), static_cast<__bf16 *>(a.o), a.T, a.g.C, a.g.dv, nblk_dv,    \
                        a.states, a.active, a.ws.events, ev_stride, a.ws.chunk_ev,                                   \
                        static_cast<const uint8_t *>(a.ws.rec), a.meta, a.g.meta_stride, a.ws.init_m, a.ws.init_order, \
                        seg, a.ws.seg_states)
     // streams starting from an empty cache, then those continuing one
     if (a.g.state_bf16) {
-        DLA_RS_LAUNCH(true, false);
-        DLA_RS_LAUNCH(true, true);
+        DLA_RS_LAUNCH(true, false, false);
+        DLA_RS_LAUNCH(true, true, false);
     } else {
-        DLA_RS_LAUNCH(false, false);
-        DLA_RS_LAUNCH(false, true);
+        if (seg.n > 1) DLA_RS_LAUNCH(false, false, true);
+        else DLA_RS_LAUNCH(false, false, false);
+        DLA_RS_LAUNCH(false, true, false);
     }
 #undef DLA_RS_LAUNCH
     hipError_t e = hipGetLastError();

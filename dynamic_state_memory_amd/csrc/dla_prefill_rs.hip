@@ -33,7 +33,8 @@
 //                 and converts it into its register copy.  A grid that would
 //                 fill at most half of the device's block slots (few streams)
 //                 is split along the sequence into up to four block sets per
-//                 stream: set s takes the chunks before its range for their
+//                 stream (float32 state storage, the information schedule):
+//                 set s takes the chunks before its range for their
 //                 state updates only (no reads, no outputs, only the key
 //                 operands staged) and then sweeps its range in full, in a
 //                 copy of the slots of its own (the last set in the cache).
@@ -1224,19 +1225,31 @@ __global__ __launch_bounds__(kRsThreads, 2) void k_prefill_rs(
     // of the other kind leaves at once (the whole block: no barrier is met)
     // (a stream the fixed schedule refused, m_init < 0, is left to a later kernel)
     if (A.m_init < 0 || (A.m_init > 0) != CONT) return;
-    // segments (float32 state storage): a stream that starts from an empty
-    // cache is swept by seg.n block sets; set sg takes chunks [0, first[sg])
-    // for their state updates only (the same updates and merges, in the same
-    // order, as any set) and chunks [first[sg], first[sg + 1]) in full, into a
-    // copy of the slots of its own (the last set into the cache).  Any other
-    // stream is swept whole by the last set.
-    const bool split = SPLIT && !SBF && !CONT && seg.n > 1 && A.m_init == 0;
+    // segments (float32 state storage): the stream is swept by seg.n block
+    // sets; set sg takes chunks [0, first[sg]) for their state updates only
+    // (the same updates and merges, in the same order, as any set) and chunks
+    // [first[sg], first[sg + 1]) in full, in slots of its own (the last set
+    // in the cache), which start as a copy of the cache's.
+    const bool split = SPLIT && !SBF && seg.n > 1;
     const bool last_set = sg == seg.n - 1;
     if (!split && !last_set) return;
     A.c_begin = split ? seg.first[sg] : 0;
     A.c_end = split ? seg.first[sg + 1] : NCH;
-    if (split && !last_set)
-        A.st_base = seg_states + (static_cast<size_t>(sg) * BHn + A.bh) * C * DV * DK + static_cast<size_t>(A.dv0) * DK;
+    if (split && !last_set) {
+        float *own = seg_states + (static_cast<size_t>(sg) * BHn + A.bh) * C * DV * DK + static_cast<size_t>(A.dv0) * DK;
+        if (CONT) {
+            // the states the cache holds: this block's rows of every slot
+            const float *from = static_cast<const float *>(A.st_base);
+            constexpr int PER = DVT * DK / 4;          // 16-byte pieces of a slot's rows
+            for (int i = tid; i < C * PER; i += kRsThreads) {
+                const int p = i / PER, e = i % PER;
+                reinterpret_cast<float4 *>(own + p * A.slot_stride)[e] =
+                    reinterpret_cast<const float4 *>(from + p * A.slot_stride)[e];
+            }
+            __syncthreads();
+        }
+        A.st_base = own;
+    }
     if (CONT) {
         c.act = A.init_order[A.m_init - 1];
         if (A.m_init == 1) {
@@ -1269,7 +1282,7 @@ __global__ __launch_bounds__(kRsThreads, 2) void k_prefill_rs(
     // (the update-only chunk code is in the instance launched for split grids
     // only, so that it takes no registers from the other instances' sweep)
     for (int ch = (CONT && A.m_init > 1) ? -1 : 0; ch < A.c_end; ++ch)
-        rs_chunk<DK, DVT, SPW, SBF, CONT, SPLIT && !CONT>(ch, stA, stB, stV, S, A, c, ch < A.c_begin);
+        rs_chunk<DK, DVT, SPW, SBF, CONT, SPLIT>(ch, stA, stB, stV, S, A, c, ch < A.c_begin);
 
     // the active state's accumulators are the last state of the final cache
     const int kb = wave - (kRsWaves - KS);
@@ -1314,8 +1327,8 @@ static hipError_t launch_rs(const PrefillArgs &a, hipStream_t stream)
         if (e != hipSuccess) return e;
     }
     // A grid that fills at most half the block slots is split along the
-    // sequence into seg.n block sets (streams that start from an empty cache,
-    // float32 state storage, the information schedule).  Set s sweeps chunks
+    // sequence into seg.n block sets (float32 state storage, the information
+    // schedule).  Set s sweeps chunks
     // [first[s], first[s + 1]) in full after chunks [0, first[s]) for their
     // updates only, which cost a fraction x of a full chunk; the ranges are
     // chosen so that every set has the same work: first[s] = tau (1 - (1 -
@@ -1351,9 +1364,13 @@ static hipError_t launch_rs(const PrefillArgs &a, hipStream_t stream)
         DLA_RS_LAUNCH(true, false, false);
         DLA_RS_LAUNCH(true, true, false);
     } else {
-        if (seg.n > 1) DLA_RS_LAUNCH(false, false, true);
-        else DLA_RS_LAUNCH(false, false, false);
-        DLA_RS_LAUNCH(false, true, false);
+        if (seg.n > 1) {
+            DLA_RS_LAUNCH(false, false, true);
+            DLA_RS_LAUNCH(false, true, true);
+        } else {
+            DLA_RS_LAUNCH(false, false, false);
+            DLA_RS_LAUNCH(false, true, false);
+        }
     }
 #undef DLA_RS_LAUNCH
     hipError_t e = hipGetLastError();

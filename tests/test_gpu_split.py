@@ -80,15 +80,28 @@ def test_split_sweep_state_score():
     _same(a, b, "split state score")
 
 
-def test_split_then_continue():
-    """A fresh stream's prefill is split; the call that continues it is not
-    (its cache holds states): together one pass of the oracle."""
+@pytest.mark.parametrize("ends,rule", [((2100, 3000), "sum"), ((700, 1400, 3000), "sum"), ((1025, 2600), "density")])
+def test_split_continuing_calls(ends, rule):
+    """Calls that continue a stream are split too (every block set starts
+    from a copy of the cache's states): each call equals the unsplit sweep
+    bit for bit, and together they are one pass of the oracle."""
+    import dynamic_state_memory_amd as dla
     torch_mod()
     cfg = dataclasses.replace(workloads.CONFIGS["long_t131k_bf16"], C=32, seg_means=(40,))
-    d = workloads.prefill_inputs(cfg, streams=[5, 6], T=3000)
-    ends = (2100, 3000)
-    o, scs, fin = gpu_prefill_pieces(d["q"], d["k"], d["v"], d["lam"], cfg.C, cfg.tau, "bf16", ends)
-    r = oracle.run(d["q"], d["k"], d["v"], d["lam"], cfg.C, cfg.tau, nthreads=oracle_threads())
-    compare_states(r, fin, label="split then continue")
-    err = compare_outputs(o, r["o"], TOL["bf16"], "split then continue")
-    say(f"split then continue: ok, max row rel err {err:.2e}")
+    d = workloads.prefill_inputs(cfg, streams=[5, 6], T=ends[-1])
+    label = f"split continuing calls {ends} {rule}"
+    say(label)
+    a = gpu_prefill_pieces(d["q"], d["k"], d["v"], d["lam"], cfg.C, cfg.tau, "bf16", ends, merge_rule=rule)
+    dla.dla_set_prefill_path(dla.DLA_PATH_UNSPLIT, 0)
+    try:
+        b = gpu_prefill_pieces(d["q"], d["k"], d["v"], d["lam"], cfg.C, cfg.tau, "bf16", ends, merge_rule=rule)
+    finally:
+        dla.dla_set_prefill_path(dla.DLA_PATH_AUTO, 0)
+    assert np.array_equal(a[0], b[0]), f"{label}: outputs differ from the unsplit sweep"
+    for key in a[2]:
+        assert np.array_equal(np.asarray(a[2][key]), np.asarray(b[2][key])), f"{label}: final cache {key} differs"
+    o, _, fin = a
+    r = oracle.run(d["q"], d["k"], d["v"], d["lam"], cfg.C, cfg.tau, nthreads=oracle_threads(), merge_rule=rule)
+    compare_states(r, fin, label=label)
+    err = compare_outputs(o, r["o"], TOL["bf16"], label)
+    say(f"{label}: ok, max row rel err {err:.2e}")

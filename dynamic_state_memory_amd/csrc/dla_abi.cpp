@@ -63,6 +63,7 @@ struct Sizes {
     uint64_t ev_stride;
     uint64_t rec;
     uint64_t seg;
+    int seg_sets;
     uint64_t total;
 };
 
@@ -90,17 +91,21 @@ Sizes workspace_sizes(int64_t BH, int64_t T, int64_t C, int64_t dk, int64_t dv)
     // chunk records (register-resident path), or the fp32 working copy of a
     // bf16-state cache's states (streamed path)
     z.rec = align_up(std::max<uint64_t>(static_cast<uint64_t>(BH) * NCH * rs_record_bytes(dk), 4ull * BH * C * dv * dk), 256);
-    // slots of the block sets of a sweep split along the sequence: only for a
-    // grid of at most 256 blocks of the register-resident sweep (16 value
-    // columns per block)
-    z.seg = (C <= 32 && dk <= 128 && BH * ((dv + 15) / 16) <= 256) ? align_up(4ull * kSegScratch * BH * C * dv * dk, 256)
-                                                                 : 0;
+    // slots of the block sets of a sweep split along the sequence (one per
+    // set but the last): only for a grid of at most 256 blocks of the
+    // register-resident sweep (16 value columns per block), at most one set
+    // per 8 chunks; last in the workspace, so that the allocation-free call
+    // can leave them out and run unsplit
+    z.seg_sets = (C <= 32 && dk <= 128 && BH * ((dv + 15) / 16) <= 256)
+                     ? static_cast<int>(std::min<int64_t>(kSegScratch, std::max<int64_t>(0, NCH / 8 - 1)))
+                     : 0;
+    z.seg = align_up(4ull * z.seg_sets * BH * C * dv * dk, 256);
     z.total = z.s + z.qs + z.flag + z.tile_cnt + z.tile_sum + z.seg_t + z.seg_P + z.seg_q0 + z.nseg +
               z.events + z.chunk_ev + z.init_m + z.init_order + z.init_t + z.shadow + z.rec + z.seg;
     return z;
 }
 
-Workspace carve(void *base, const Sizes &z)
+Workspace carve(void *base, const Sizes &z, bool with_seg)
 {
     uint8_t *p = static_cast<uint8_t *>(base);
     Workspace w;
@@ -123,7 +128,8 @@ Workspace carve(void *base, const Sizes &z)
     w.rec = p;
     w.work = reinterpret_cast<float *>(p);
     p += z.rec;
-    w.seg_states = z.seg ? reinterpret_cast<float *>(p) : nullptr;
+    w.seg_states = with_seg && z.seg ? reinterpret_cast<float *>(p) : nullptr;
+    w.seg_sets = with_seg ? z.seg_sets : 0;
     p += z.seg;
     (void)p;
     return w;
@@ -430,13 +436,17 @@ dla_status prefill_call(const void *q, const void *k, const void *v, const void 
         return fail(DLA_ERR_ARG, "schedule export: ev_t and ev_i go together");
     const int64_t BH = static_cast<int64_t>(cache->B) * cache->H;
     const Sizes z = workspace_sizes(BH, T, cache->C, cache->d_k, cache->d_v);
+    // (the allocation-free call runs the sweep unsplit when the split's slots
+    // do not fit its scratch)
+    bool with_seg = true;
     if (scratch_only) {
-        if (z.total > DLA_NOALLOC_SCRATCH_BYTES)
+        if (z.total - z.seg > DLA_NOALLOC_SCRATCH_BYTES)
             return fail(DLA_ERR_WORKSPACE,
                         "this call needs %llu bytes of scratch; the static scratch holds %llu (use dla_prefill "
                         "with a workspace)",
-                        static_cast<unsigned long long>(z.total),
+                        static_cast<unsigned long long>(z.total - z.seg),
                         static_cast<unsigned long long>(DLA_NOALLOC_SCRATCH_BYTES));
+        with_seg = z.total <= DLA_NOALLOC_SCRATCH_BYTES;
     } else {
         if (!workspace || !aligned(workspace, 256))
             return fail(DLA_ERR_WORKSPACE, "workspace NULL or not 256-byte aligned");
@@ -485,7 +495,7 @@ dla_status prefill_call(const void *q, const void *k, const void *v, const void 
         dla_status ss = device_scratch(st, &workspace);
         if (ss != DLA_OK) return ss;
     }
-    a.ws = carve(workspace, z);
+    a.ws = carve(workspace, z, with_seg);
     a.seg_slots = 0;
     if (a.register_resident && g_path_override != DLA_PATH_UNSPLIT) {
         s = device_block_slots(&a.seg_slots);

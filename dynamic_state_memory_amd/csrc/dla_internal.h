@@ -85,6 +85,7 @@ struct Workspace {
     // block set but the last [kSegScratch][BH][C][dv][dk] fp32 (NULL when the
     // shape's grid is too large to be split)
     float *seg_states;
+    int seg_sets;        // block sets with slots there (the split has at most one more)
 };
 constexpr int kSegScratch = 3;  // block sets with slots of their own (at most 4 sets)
 constexpr int kPrepCmax = 32;   // read-weight rows kept per chunk by the pre-pass

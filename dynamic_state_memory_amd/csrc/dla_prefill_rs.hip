@@ -1338,7 +1338,7 @@ static hipError_t launch_rs(const PrefillArgs &a, hipStream_t stream)
     {
         const int blocks = BH * nblk_dv;
         int n = a.seg_slots > 0 ? std::min(kMaxSeg, a.seg_slots / blocks) : 1;
-        n = std::min(n, NCH / 8);
+        n = std::min(std::min(n, NCH / 8), 1 + a.ws.seg_sets);
         if (n >= 2 && a.ws.seg_states && !a.g.state_bf16 && a.merge_rule != DLA_FENWICK) {
             constexpr double x = 0.3;
             const double tau = NCH * x / (1.0 - std::pow(1.0 - x, n));

@@ -261,8 +261,9 @@ dla_status dla_cache_set_merge_rule(dla_cache *cache, int32_t rule);
 dla_status dla_cache_set_score_rule(dla_cache *cache, int32_t rule);
 
 /* Workspace bytes dla_prefill needs for this shape (the schedule of section
- * 5.1-5.2 and the chunk operands of the section 5.3 read); 0 if the shape is
- * invalid.  Host only. */
+ * 5.1-5.2, the chunk operands of the section 5.3 read and, for a sweep grid
+ * small enough to be split along the sequence, the slots of its block sets);
+ * 0 if the shape is invalid.  Host only. */
 uint64_t dla_prefill_workspace_bytes(int32_t B, int32_t H, int32_t T, int32_t C,
                                      int32_t d_k, int32_t d_v);
 
@@ -317,9 +318,10 @@ dla_status dla_prefill(const void *q, const void *k, const void *v, const void *
  * and frees nothing.
  *   - The scratch is the one of the device current on the calling thread;
  *     `stream` must belong to that device (DLA_ERR_ARG otherwise).
- *   - A call whose dla_prefill_workspace_bytes exceeds
- *     DLA_NOALLOC_SCRATCH_BYTES returns DLA_ERR_WORKSPACE with nothing
- *     enqueued (use dla_prefill with a workspace then).
+ *   - A call whose dla_prefill_workspace_bytes, less the slots of a split
+ *     sweep (which the call then runs unsplit, with the same results),
+ *     exceeds DLA_NOALLOC_SCRATCH_BYTES returns DLA_ERR_WORKSPACE with
+ *     nothing enqueued (use dla_prefill with a workspace then).
  *   - Every call on a device shares that device's scratch, which keeps the
  *     last call's contents (nothing in it needs to start at zero): calls that
  *     overlap on one device race, so calls on different streams of one device

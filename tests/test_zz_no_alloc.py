@@ -1,6 +1,8 @@
 """dla_prefill_noalloc (the library's static scratch instead of a workspace)
 gives what dla_prefill gives on the same inputs, on two calls in a row, the
-second one smaller, through the C ABI; too large a call is refused on the host."""
+second one smaller, through the C ABI (also where only the workspace call
+has room to split its sweep along the sequence); too large a call is refused
+on the host."""
 import dataclasses
 
 import numpy as np
@@ -46,7 +48,7 @@ def _run(entry, q, k, v, lam, C, tau, dev, merge_rule="sum"):
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("case", ["bf16_register", "f32_streamed", "bf16_fenwick"])
+@pytest.mark.parametrize("case", ["bf16_register", "f32_streamed", "bf16_fenwick", "bf16_split_fallback"])
 def test_noalloc_matches_the_workspace_entry(case):
     torch = torch_mod()
     dev = torch.device("cuda:0")
@@ -54,8 +56,14 @@ def test_noalloc_matches_the_workspace_entry(case):
         cfg, H, sizes, rule = workloads.CONFIGS["mamba2_780m_bf16"], 4, (3000, 700), "sum"
     elif case == "f32_streamed":
         cfg, H, sizes, rule = dataclasses.replace(workloads.CONFIGS["tiny_fp32"], H=2), 2, (1500, 300), "sum"
-    else:
+    elif case == "bf16_fenwick":
         cfg, H, sizes, rule = workloads.CONFIGS["mamba2_780m_bf16"], 2, (2500, 600), "fenwick"
+    else:
+        # the workspace call splits its sweep along the sequence; the split's
+        # slots do not fit the static scratch, so the allocation-free call runs
+        # it unsplit (the same results, bit for bit)
+        cfg, H, sizes, rule = workloads.CONFIGS["long_t131k_bf16"], 16, (1100, 600), "sum"
+        assert dla.dla_prefill_workspace_bytes(1, H, sizes[0], cfg.C, cfg.dk, cfg.dv) > dla.DLA_NOALLOC_SCRATCH_BYTES
     dt = torch.bfloat16 if cfg.io == "bf16" else torch.float32
     C = cfg.C if rule != "fenwick" else 13
     for n, T in enumerate(sizes):

@@ -33,7 +33,7 @@
 //                 and converts it into its register copy.  A grid that would
 //                 fill at most half of the device's block slots (few streams)
 //                 is split along the sequence into up to four block sets per
-//                 stream (float32 state storage, the information schedule):
+//                 stream (float32 state storage):
 //                 set s takes the chunks before its range for their
 //                 state updates only (no reads, no outputs, only the key
 //                 operands staged) and then sweeps its range in full, in a
@@ -807,7 +807,9 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
                         mma32(am[nt][h], a, b);
                     }
                 }
-            c.ea = refresh_active<NTV>(am, af);
+            // (its fp16 copy serves the reads: in update-only chunks, only for
+            // the first full chunk after them)
+            if (!upd || ch + 1 >= A.c_begin) c.ea = refresh_active<NTV>(am, af);
         }
         c.ewin += nev;
         return;
@@ -1108,7 +1110,7 @@ __device__ __forceinline__ void rs_chunk(const int ch, RsStageA<DK> &X, RsStageB
                 }
             }
         }
-        c.ea = refresh_active<NTV>(am, af);
+        if (!upd || ch + 1 >= A.c_begin) c.ea = refresh_active<NTV>(am, af);
     }
     const int mnew = __builtin_amdgcn_readfirstlane(S.m_new);
     const uint32_t cl = __builtin_amdgcn_readfirstlane(S.closed_new);
@@ -1327,8 +1329,7 @@ static hipError_t launch_rs(const PrefillArgs &a, hipStream_t stream)
         if (e != hipSuccess) return e;
     }
     // A grid that fills at most half the block slots is split along the
-    // sequence into seg.n block sets (float32 state storage, the information
-    // schedule).  Set s sweeps chunks
+    // sequence into seg.n block sets (float32 state storage).  Set s sweeps chunks
     // [first[s], first[s + 1]) in full after chunks [0, first[s]) for their
     // updates only, which cost a fraction x of a full chunk; the ranges are
     // chosen so that every set has the same work: first[s] = tau (1 - (1 -
@@ -1339,7 +1340,7 @@ static hipError_t launch_rs(const PrefillArgs &a, hipStream_t stream)
         const int blocks = BH * nblk_dv;
         int n = a.seg_slots > 0 ? std::min(kMaxSeg, a.seg_slots / blocks) : 1;
         n = std::min(std::min(n, NCH / 8), 1 + a.ws.seg_sets);
-        if (n >= 2 && a.ws.seg_states && !a.g.state_bf16 && a.merge_rule != DLA_FENWICK) {
+        if (n >= 2 && a.ws.seg_states && !a.g.state_bf16) {
             constexpr double x = 0.3;
             const double tau = NCH * x / (1.0 - std::pow(1.0 - x, n));
             seg.n = n;

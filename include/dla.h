@@ -376,9 +376,8 @@ dla_status dla_decode_step(const void *q, const void *k, const void *v, const vo
  * d_k <= 128, the streamed kernel otherwise); DLA_PATH_STREAMED runs the
  * streamed kernel for every shape; DLA_PATH_UNSPLIT runs the library's
  * choice but never splits the register-resident sweep along the sequence
- * (which it does with float32 state storage under the information schedule,
- * when the sweep's grid would fill at most half of the device's block slots:
- * the same results, bit for bit).  value_columns = 0 lets the library choose
+ * (which it does with float32 state storage when the sweep's grid would fill
+ * at most half of the device's block slots: the same results, bit for bit).  value_columns = 0 lets the library choose
  * the streamed kernel's d_v slice width, 16 or 32 forces it where d_v allows
  * and its LDS fits.  Both kernels compute the same layer (reading notes,
  * sections 5.1-5.3); production callers never need this.  Host only;

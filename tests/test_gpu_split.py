@@ -105,3 +105,32 @@ def test_split_continuing_calls(ends, rule):
     compare_states(r, fin, label=label)
     err = compare_outputs(o, r["o"], TOL["bf16"], label)
     say(f"{label}: ok, max row rel err {err:.2e}")
+
+
+@pytest.mark.parametrize("ends", [(3000,), (1300, 3100)])
+def test_split_sweep_fixed_schedule(ends):
+    """The Log-Linear fixed schedule's sweep split the same way, from position
+    0 and continuing: equal to the unsplit sweep bit for bit."""
+    import dynamic_state_memory_amd as dla
+    torch = torch_mod()
+    from tests.test_gpu_fenwick import _inputs, _run
+    d = _inputs(ends[-1], [20, 21], 16)
+    dev = torch.device("cuda:0")
+    res = []
+    for path in (dla.DLA_PATH_AUTO, dla.DLA_PATH_UNSPLIT):
+        dla.dla_set_prefill_path(path, 0)
+        try:
+            cache = dla.Cache(1, 2, 16, 128, 64, device=dev, merge_rule="fenwick")
+            outs, lo = [], 0
+            for hi in ends:
+                o, _ = _run({x: d[x][:, lo:hi] for x in ("q", "k", "v", "lam")}, 16, cache=cache)
+                outs.append(o)
+                lo = hi
+            res.append((np.concatenate(outs, 1), cache.read()))
+        finally:
+            dla.dla_set_prefill_path(dla.DLA_PATH_AUTO, 0)
+    (o1, f1), (o2, f2) = res
+    assert np.array_equal(o1, o2), f"fixed schedule {ends}: outputs differ from the unsplit sweep"
+    for key in f1:
+        assert np.array_equal(np.asarray(f1[key]), np.asarray(f2[key])), f"fixed schedule {ends}: cache {key} differs"
+    say(f"split fixed schedule {ends}: equal to the unsplit sweep")

@@ -37,7 +37,12 @@ Also reported on the same line:
                 configurations: Mamba-2-780M-shaped, long context (T=131072),
                 Mamba-2-shaped with C=64, tiny fp32, and the state information
                 score on the Mamba-2-shaped layer with values that follow the
-                key segments (--no-other skips them);
+                key segments (--no-other skips them); the long-context one
+                also timed with its sweep unsplit (`unsplit`: its grid of 128
+                blocks is split along the sequence), and the Mamba-2-shaped
+                one over batch sizes 1, 2, 4 with the library's sweep and
+                unsplit (`batch_sweep`: the pages measure prefill over batch
+                sizes);
   decode_bf16_states
                 the same decode on caches storing closed states as bf16 (the
                 most recent one stays fp32), with its algorithmic bytes
@@ -343,6 +348,14 @@ def other_prefill_legs(args, torch, dla, workloads):
         del d
         log(f"{name}: inputs generated in {time.time() - t0:.1f}s")
         r = prefill_leg(args, torch, dla, cfg, x, steps=10 if cfg.T >= 4096 else 50, **kw)
+        if name == "long_t131k_bf16":
+            # its sweep grid (128 blocks) is split along the sequence; the same
+            # call with the split turned off, for comparison
+            u = prefill_leg(args, torch, dla, cfg, x, steps=5, path=dla.DLA_PATH_UNSPLIT, **kw)
+            r["unsplit"] = {kk: u[kk] for kk in ("ms_per_step", "prefill_ms", "kernel_ms", "frac", "kernel_frac")}
+            log(f"{name} unsplit: {u['ms_per_step']:.3f} ms/step, sweep {u['kernel_ms']:.3f} ms")
+        if name == "mamba2_780m_bf16":
+            r["batch_sweep"] = batch_sweep(torch, dla, cfg, x)
         r["config"] = dict(workload=name, B=cfg.B, H=cfg.H, T=cfg.T, d_k=cfg.dk, d_v=cfg.dv, C=cfg.C,
                            tau=kw.get("tau", cfg.tau), io=cfg.io, score_rule=kw.get("score_rule", "cosine"),
                            values="regime" if kw.get("score_rule") == "state" else "random",
@@ -393,6 +406,47 @@ def fenwick_leg(args, torch, dla, cfg, q, k, v, lam, o, ws, dla_ms):
                 ms_per_step=ms, kernel=kernel, kernel_ms=kern, C=L, achieved=ach, unit_achieved="TFLOP/s",
                 frac=ach / PEAK_BF16_TFLOPS, algorithmic_flop_per_launch=flops,
                 buckets_read_per_token=read / T, dla_over_fenwick_time=dla_ms / ms)
+
+
+def batch_sweep(torch, dla, cfg, x, batches=(1, 2, 4), steps=10):
+    """Prefill tokens/s of the workload's layer at batch sizes B' <= B (the
+    first B' sequences of its batch): the library's choice of sweep, which
+    splits a small grid along the sequence, and the same calls with the split
+    turned off.  Wall time over `steps` calls after one warmup call."""
+    q, k, v, lam = x
+    H, T, dk, dv, C = cfg.H, q.shape[2], cfg.dk, cfg.dv, cfg.C
+    out = []
+    for Bn in batches:
+        if Bn > cfg.B:
+            continue
+        xs = [t[:Bn].contiguous() for t in (q, k, v, lam)]
+        on = torch.empty(Bn, H, T, dv, dtype=q.dtype, device=q.device)
+        cache = dla.Cache(Bn, H, C, dk, dv, device=q.device)
+        wsn = dla.prefill_workspace(Bn, H, T, C, dk, dv, q.device)
+        res = dict(B=Bn, T=T)
+        for name, path in (("split", dla.DLA_PATH_AUTO), ("unsplit", dla.DLA_PATH_UNSPLIT)):
+            dla.dla_set_prefill_path(path, 0)
+            try:
+                def call():
+                    cache.reset()
+                    dla.prefill(*xs, cfg.tau, cache, o=on, workspace=wsn)
+
+                call()
+                torch.cuda.synchronize()
+                w0 = time.perf_counter()
+                for _ in range(steps):
+                    call()
+                torch.cuda.synchronize()
+                ms = (time.perf_counter() - w0) * 1e3 / steps
+            finally:
+                dla.dla_set_prefill_path(dla.DLA_PATH_AUTO, 0)
+            res[f"{name}_ms_per_step"] = ms
+            res[f"{name}_tokens_per_s"] = Bn * T / (ms * 1e-3)
+        del cache, wsn, on, xs
+        out.append(res)
+        log(f"batch sweep B={Bn}: {res['split_ms_per_step']:.3f} ms (library's sweep), "
+            f"{res['unsplit_ms_per_step']:.3f} ms unsplit")
+    return out
 
 
 def context_sweep(torch, dla, cfg, q, k, v, lam, lengths=(4096, 8192, 16384, 32768), steps=5):

@@ -63,12 +63,30 @@ def test_prefill_kernel_choice(monkeypatch):
         assert dla.dla_set_prefill_path(dla.DLA_PATH_STREAMED, 16) == dla.DLA_OK
         assert dla.dla_prefill_kernel(dla.DLA_BF16, 2, 16, 32, 128, 256) == "k_prefill<bf16,128,16>"
         assert dla.dla_set_prefill_path(7, 0) == dla.DLA_ERR_ARG
+        # the register-resident sweep without its split along the sequence:
+        # the same kernel
+        assert dla.dla_set_prefill_path(dla.DLA_PATH_UNSPLIT, 0) == dla.DLA_OK
+        assert dla.dla_prefill_kernel(dla.DLA_BF16, 1, 16, 32, 128, 128) == "k_prefill_rs<128,16,8>"
+        assert dla.dla_set_prefill_path(dla.DLA_PATH_STREAMED, 16) == dla.DLA_OK
         assert dla.dla_set_prefill_path(dla.DLA_PATH_AUTO, 24) == dla.DLA_ERR_ARG
         # (a refused call changes nothing)
         assert dla.dla_prefill_kernel(dla.DLA_BF16, 2, 16, 32, 128, 256) == "k_prefill<bf16,128,16>"
     finally:
         dla.dla_set_prefill_path(dla.DLA_PATH_AUTO, 0)
     assert dla.dla_prefill_kernel(dla.DLA_BF16, 2, 16, 32, 128, 256) == "k_prefill_rs<128,16,8>"
+
+
+def test_split_sweep_workspace():
+    """A sweep grid of at most 256 blocks may be split along the sequence:
+    its workspace holds the slots of up to three more block sets, one per 8
+    chunks beyond the first 8 (a larger grid's does not)."""
+    slot_bytes = 4 * 16 * 32 * 128 * 128            # B*H = 16 streams, C = 32, d_k = d_v = 128
+    ws = [dla.dla_prefill_workspace_bytes(1, 16, 64 * n, 32, 128, 128) for n in (8, 15, 16, 24, 32)]
+    per_chunk = ws[1] - ws[0]                       # no split slots below 16 chunks
+    assert ws[2] - ws[1] >= slot_bytes > ws[2] - ws[1] - 2 * per_chunk
+    assert ws[3] - ws[2] >= slot_bytes and ws[4] - ws[3] >= slot_bytes
+    big = [dla.dla_prefill_workspace_bytes(2, 16, 64 * n, 32, 128, 256) for n in (15, 16)]   # 512 blocks
+    assert big[1] - big[0] < slot_bytes
 
 
 def _cache(B=1, H=1, C_=8, dk=64, dv=64, base=0x10000):
